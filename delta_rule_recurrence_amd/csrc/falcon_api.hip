@@ -1,0 +1,196 @@
+// C ABI of the Falcon library: argument validation, status codes and
+// dispatch to the kernels.  Nothing here allocates or synchronises.
+#include <math.h>
+#include <string.h>
+
+#include "falcon.h"
+#include "falcon_launch.h"
+
+namespace {
+
+using falcon::DecodeArgs;
+using falcon::ProblemArgs;
+
+bool supported_width(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+  const void* p;
+  int64_t bytes;
+};
+
+bool overlap(Range a, Range b) {
+  if (!a.p || !b.p || a.bytes <= 0 || b.bytes <= 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + static_cast<uintptr_t>(b.bytes) && b0 < a0 + static_cast<uintptr_t>(a.bytes);
+}
+
+falcon_status check_problem(const falcon_problem* p) {
+  if (!p) return FALCON_ERR_NULL;
+  if (p->B < 0 || p->H < 0 || p->T < 0) return FALCON_ERR_SHAPE;
+  if (!supported_width(p->dk) || !supported_width(p->dv)) return FALCON_ERR_SHAPE;
+  if (p->variant < FALCON_1 || p->variant > FALCON_2A) return FALCON_ERR_VARIANT;
+  if (p->io_dtype != FALCON_F32 && p->io_dtype != FALCON_BF16) return FALCON_ERR_DTYPE;
+  if (!isfinite(p->eps) || p->eps < 0.0f) return FALCON_ERR_VALUE;
+  if (!(p->eps_gamma > 0.0f && p->eps_gamma < 1.0f)) return FALCON_ERR_VALUE;
+  const int64_t bh = int64_t(p->B) * p->H;
+  if (bh > (int64_t(1) << 30)) return FALCON_ERR_SHAPE;
+  return FALCON_OK;
+}
+
+bool per_column(int variant) { return variant == FALCON_2 || variant == FALCON_2A; }
+
+// Validates the arguments shared by the two forward entry points and fills
+// the launch arguments.
+falcon_status check_forward(const falcon_problem* p, const void* phi_k, const void* phi_q,
+                            const void* v, const float* beta, const float* lam, const float* S0,
+                            const void* k_prev, void* o, float* S_T, ProblemArgs* out) {
+  falcon_status s = check_problem(p);
+  if (s != FALCON_OK) return s;
+  const int64_t bh = int64_t(p->B) * p->H;
+  const int64_t es = p->io_dtype == FALCON_BF16 ? 2 : 4;
+  const bool work = bh > 0 && p->T > 0;
+  if (work && (!phi_k || !phi_q || !v || !beta || !lam || !o)) return FALCON_ERR_NULL;
+  const void* ptrs[] = {phi_k, phi_q, v, beta, lam, S0, k_prev, o, S_T};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return FALCON_ERR_ALIGN;
+  const int64_t nk = bh * p->T * p->dk, nv = bh * p->T * p->dv;
+  const Range ro{o, nv * es};
+  const Range inputs[] = {{phi_k, nk * es},
+                          {phi_q, nk * es},
+                          {v, nv * es},
+                          {beta, (per_column(p->variant) ? nv : bh * p->T) * 4},
+                          {lam, bh * p->T * 4},
+                          {S0, bh * p->dk * p->dv * 4},
+                          {k_prev, bh * p->dk * es},
+                          {S_T, bh * p->dk * p->dv * 4}};
+  for (const Range& r : inputs)
+    if (overlap(ro, r)) return FALCON_ERR_ALIAS;
+  // S_T may alias S0 exactly (in-place continuation) but not partially, and
+  // must not overlap any other input.
+  const Range rs{S_T, bh * p->dk * p->dv * 4};
+  if (S_T && S0 && S_T != S0 && overlap(rs, Range{S0, rs.bytes})) return FALCON_ERR_ALIAS;
+  for (int i = 0; i < 5; ++i)
+    if (overlap(rs, inputs[i])) return FALCON_ERR_ALIAS;
+  if (overlap(rs, inputs[6])) return FALCON_ERR_ALIAS;
+
+  *out = ProblemArgs{};
+  out->B = p->B; out->H = p->H; out->T = p->T; out->dk = p->dk; out->dv = p->dv;
+  out->variant = p->variant;
+  out->bf16 = p->io_dtype == FALCON_BF16;
+  out->eps = p->eps; out->eps_gamma = p->eps_gamma;
+  out->phi_k = phi_k; out->phi_q = phi_q; out->v = v; out->beta = beta; out->lam = lam;
+  out->S0 = S0; out->k_prev = k_prev; out->o = o; out->S_T = S_T;
+  return FALCON_OK;
+}
+
+falcon_status finish(hipError_t e) { return e == hipSuccess ? FALCON_OK : FALCON_ERR_HIP; }
+
+// With no token to process the result is just S_T = S_0.
+falcon_status empty_forward(const ProblemArgs& a, hipStream_t st) {
+  const int64_t n = int64_t(a.B) * a.H * a.dk * a.dv;
+  if (!a.S_T || n == 0) return FALCON_OK;
+  if (a.S_T == a.S0) return FALCON_OK;
+  (void)hipGetLastError();
+  return finish(falcon::launch_state_copy(a.S0, a.S_T, n, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t falcon_abi_version(void) { return FALCON_ABI_VERSION; }
+
+const char* falcon_status_string(int32_t s) {
+  switch (s) {
+    case FALCON_OK: return "FALCON_OK";
+    case FALCON_ERR_NULL: return "FALCON_ERR_NULL: a required pointer is NULL";
+    case FALCON_ERR_SHAPE: return "FALCON_ERR_SHAPE: unsupported or negative size";
+    case FALCON_ERR_DTYPE: return "FALCON_ERR_DTYPE: unknown io dtype";
+    case FALCON_ERR_CHUNK: return "FALCON_ERR_CHUNK: chunk size must be 16, 32 or 64";
+    case FALCON_ERR_ALIGN: return "FALCON_ERR_ALIGN: pointer not 16-byte aligned";
+    case FALCON_ERR_WORKSPACE: return "FALCON_ERR_WORKSPACE: workspace missing or too small";
+    case FALCON_ERR_VARIANT: return "FALCON_ERR_VARIANT: unknown variant";
+    case FALCON_ERR_HIP: return "FALCON_ERR_HIP: the HIP runtime reported a launch error";
+    case FALCON_ERR_VALUE: return "FALCON_ERR_VALUE: eps must be finite and >= 0, eps_gamma in (0,1)";
+    case FALCON_ERR_ALIAS: return "FALCON_ERR_ALIAS: an output overlaps an input";
+    default: return "unknown falcon_status";
+  }
+}
+
+falcon_status falcon_fwd_recurrent(const falcon_problem* p, const void* phi_k, const void* phi_q,
+                                   const void* v, const float* beta, const float* lam,
+                                   const float* S0, const void* k_prev, void* o, float* S_T,
+                                   hipStream_t stream) {
+  ProblemArgs a;
+  falcon_status s = check_forward(p, phi_k, phi_q, v, beta, lam, S0, k_prev, o, S_T, &a);
+  if (s != FALCON_OK) return s;
+  if (int64_t(a.B) * a.H == 0 || a.T == 0) return empty_forward(a, stream);
+  (void)hipGetLastError();
+  return finish(falcon::launch_recurrent(a, stream));
+}
+
+size_t falcon_workspace_bytes(const falcon_problem* p, int32_t C) {
+  if (check_problem(p) != FALCON_OK) return static_cast<size_t>(-1);
+  if (C != 16 && C != 32 && C != 64) return static_cast<size_t>(-1);
+  ProblemArgs a{};
+  a.B = p->B; a.H = p->H; a.T = p->T; a.dk = p->dk; a.dv = p->dv;
+  a.variant = p->variant; a.bf16 = p->io_dtype == FALCON_BF16; a.C = C;
+  return falcon::chunked_workspace_bytes(a);
+}
+
+falcon_status falcon_fwd_chunked(const falcon_problem* p, const void* phi_k, const void* phi_q,
+                                 const void* v, const float* beta, const float* lam,
+                                 const float* S0, const void* k_prev, void* o, float* S_T,
+                                 int32_t C, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+  ProblemArgs a;
+  falcon_status s = check_forward(p, phi_k, phi_q, v, beta, lam, S0, k_prev, o, S_T, &a);
+  if (s != FALCON_OK) return s;
+  if (C != 16 && C != 32 && C != 64) return FALCON_ERR_CHUNK;
+  a.C = C;
+  const size_t need = falcon::chunked_workspace_bytes(a);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return FALCON_ERR_WORKSPACE;
+  if (workspace && !aligned16(workspace)) return FALCON_ERR_ALIGN;
+  a.workspace = workspace;
+  a.workspace_bytes = workspace_bytes;
+  if (int64_t(a.B) * a.H == 0 || a.T == 0) return empty_forward(a, stream);
+  (void)hipGetLastError();
+  return finish(falcon::launch_chunked(a, stream));
+}
+
+falcon_status falcon_decode_step(const falcon_problem* p, const void* phi_k_prev,
+                                 const void* phi_q, const void* v, const float* beta,
+                                 const float* lam, float* S, const uint8_t* is_first, void* o,
+                                 hipStream_t stream) {
+  falcon_status s = check_problem(p);
+  if (s != FALCON_OK) return s;
+  const int64_t bh = int64_t(p->B) * p->H;
+  if (bh == 0) return FALCON_OK;
+  if (!phi_k_prev || !phi_q || !v || !beta || !lam || !S || !o) return FALCON_ERR_NULL;
+  const void* ptrs[] = {phi_k_prev, phi_q, v, beta, lam, S, o};
+  for (const void* q : ptrs)
+    if (!aligned16(q)) return FALCON_ERR_ALIGN;
+  const int64_t es = p->io_dtype == FALCON_BF16 ? 2 : 4;
+  const Range ro{o, bh * p->dv * es};
+  const Range rs{S, bh * p->dk * p->dv * 4};
+  const Range inputs[] = {{phi_k_prev, bh * p->dk * es},
+                          {phi_q, bh * p->dk * es},
+                          {v, bh * p->dv * es},
+                          {beta, (per_column(p->variant) ? bh * p->dv : bh) * 4},
+                          {lam, bh * 4},
+                          {is_first, is_first ? p->B : 0}};
+  for (const Range& r : inputs)
+    if (overlap(ro, r) || overlap(rs, r)) return FALCON_ERR_ALIAS;
+  if (overlap(ro, rs)) return FALCON_ERR_ALIAS;
+  DecodeArgs a{};
+  a.B = p->B; a.H = p->H; a.dk = p->dk; a.dv = p->dv; a.variant = p->variant;
+  a.bf16 = p->io_dtype == FALCON_BF16;
+  a.eps = p->eps; a.eps_gamma = p->eps_gamma;
+  a.x = phi_k_prev; a.q = phi_q; a.v = v; a.beta = beta; a.lam = lam; a.S = S;
+  a.is_first = is_first; a.o = o;
+  (void)hipGetLastError();
+  return finish(falcon::launch_decode(a, stream));
+}
+
+}  // extern "C"

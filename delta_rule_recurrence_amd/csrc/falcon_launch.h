@@ -1,0 +1,52 @@
+// Host-side launch interface between the C ABI layer and the kernels.
+// Arguments reaching these functions have already been validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace falcon {
+
+struct ProblemArgs {
+  int B, H, T, dk, dv;
+  int variant;
+  bool bf16;
+  float eps, eps_gamma;
+  const void* phi_k;
+  const void* phi_q;
+  const void* v;
+  const float* beta;
+  const float* lam;
+  const float* S0;       // may be null (zero state)
+  const void* k_prev;    // may be null (fresh start)
+  void* o;
+  float* S_T;            // may be null
+  int C;                 // chunk size (chunked path only)
+  void* workspace;
+  size_t workspace_bytes;
+};
+
+struct DecodeArgs {
+  int B, H, dk, dv;
+  int variant;
+  bool bf16;
+  float eps, eps_gamma;
+  const void* x;
+  const void* q;
+  const void* v;
+  const float* beta;
+  const float* lam;
+  float* S;
+  const uint8_t* is_first;
+  void* o;
+};
+
+hipError_t launch_recurrent(const ProblemArgs& a, hipStream_t st);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_chunked(const ProblemArgs& a, hipStream_t st);
+size_t chunked_workspace_bytes(const ProblemArgs& a);
+// Copy S0 (or zeros when S0 is null) to S_T; used when there is no token.
+hipError_t launch_state_copy(const float* S0, float* S_T, int64_t n, hipStream_t st);
+
+}  // namespace falcon

@@ -1,0 +1,159 @@
+"""Thin Python binding of libfalcon (ctypes).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/falcon.h``.  Tensors must be
+contiguous device tensors; outputs are allocated with torch when not given.
+There is no CPU fallback: without the built library, or without a GPU,
+these functions raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfalcon.so")
+
+VARIANTS = {"falcon1": 1, "falcon1a": 2, "falcon2": 3, "falcon2a": 4}
+DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+
+FALCON_OK = 0
+
+
+class FalconProblem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("T", ctypes.c_int32),
+                ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("variant", ctypes.c_int32),
+                ("io_dtype", ctypes.c_int32), ("eps", ctypes.c_float), ("eps_gamma", ctypes.c_float)]
+
+
+_P = ctypes.c_void_p
+_SIGNATURES = {
+    "falcon_abi_version": (ctypes.c_int32, []),
+    "falcon_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
+    "falcon_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(FalconProblem), ctypes.c_int32]),
+    "falcon_fwd_recurrent": (ctypes.c_int32, [ctypes.POINTER(FalconProblem), _P, _P, _P, _P, _P,
+                                              _P, _P, _P, _P, _P]),
+    "falcon_fwd_chunked": (ctypes.c_int32, [ctypes.POINTER(FalconProblem), _P, _P, _P, _P, _P, _P,
+                                            _P, _P, _P, ctypes.c_int32, _P, ctypes.c_size_t, _P]),
+    "falcon_decode_step": (ctypes.c_int32, [ctypes.POINTER(FalconProblem), _P, _P, _P, _P, _P,
+                                            _P, _P, _P, _P]),
+}
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfalcon.so (built by ``delta_rule_recurrence_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m delta_rule_recurrence_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+class FalconError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(falcon_status_string(status))
+
+
+def falcon_status_string(status: int) -> str:
+    return load_library().falcon_status_string(int(status)).decode()
+
+
+def falcon_abi_version() -> int:
+    return int(load_library().falcon_abi_version())
+
+
+def make_problem(B, H, T, dk, dv, *, variant="falcon1", io_dtype=torch.bfloat16, eps=1e-6,
+                 eps_gamma=1e-6) -> FalconProblem:
+    return FalconProblem(B, H, T, dk, dv, VARIANTS[variant], DTYPES[io_dtype], eps, eps_gamma)
+
+
+def falcon_workspace_bytes(problem: FalconProblem, C: int) -> int:
+    return int(load_library().falcon_workspace_bytes(ctypes.byref(problem), int(C)))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(status: int):
+    if status != FALCON_OK:
+        raise FalconError(status)
+
+
+def _forward_setup(phi_k, phi_q, v, beta, variant, o, S_T, return_state):
+    B, H, T, dk = phi_k.shape
+    dv = v.shape[-1]
+    if o is None:
+        o = torch.empty((B, H, T, dv), dtype=v.dtype, device=v.device)
+    if S_T is None and return_state:
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=v.device)
+    return B, H, T, dk, dv, o, S_T
+
+
+def falcon_fwd_recurrent(phi_k, phi_q, v, beta, lam, *, variant="falcon1", S0=None, k_prev=None,
+                         eps=1e-6, eps_gamma=1e-6, o=None, S_T=None, return_state=True,
+                         stream=None):
+    """Recurrent form; returns ``(o, S_T)``."""
+    B, H, T, dk, dv, o, S_T = _forward_setup(phi_k, phi_q, v, beta, variant, o, S_T, return_state)
+    p = make_problem(B, H, T, dk, dv, variant=variant, io_dtype=v.dtype, eps=eps, eps_gamma=eps_gamma)
+    _check(load_library().falcon_fwd_recurrent(
+        ctypes.byref(p), _ptr(phi_k), _ptr(phi_q), _ptr(v), _ptr(beta), _ptr(lam), _ptr(S0),
+        _ptr(k_prev), _ptr(o), _ptr(S_T), _stream(stream)))
+    return o, S_T
+
+
+def falcon_fwd_chunked(phi_k, phi_q, v, beta, lam, *, variant="falcon1", C=64, S0=None,
+                       k_prev=None, eps=1e-6, eps_gamma=1e-6, o=None, S_T=None, workspace=None,
+                       return_state=True, stream=None):
+    """Chunk-parallel form; returns ``(o, S_T)``."""
+    B, H, T, dk, dv, o, S_T = _forward_setup(phi_k, phi_q, v, beta, variant, o, S_T, return_state)
+    p = make_problem(B, H, T, dk, dv, variant=variant, io_dtype=v.dtype, eps=eps, eps_gamma=eps_gamma)
+    need = falcon_workspace_bytes(p, C)
+    if need == ctypes.c_size_t(-1).value:
+        raise FalconError(-2)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=v.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().falcon_fwd_chunked(
+        ctypes.byref(p), _ptr(phi_k), _ptr(phi_q), _ptr(v), _ptr(beta), _ptr(lam), _ptr(S0),
+        _ptr(k_prev), _ptr(o), _ptr(S_T), int(C), _ptr(workspace), wbytes, _stream(stream)))
+    return o, S_T
+
+
+def falcon_decode_step(phi_k_prev, phi_q, v, beta, lam, S, *, variant="falcon1", is_first=None,
+                       eps=1e-6, eps_gamma=1e-6, o=None, stream=None):
+    """One decode token; updates ``S`` in place and returns ``o``."""
+    B, H, dk = phi_k_prev.shape
+    dv = v.shape[-1]
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=v.dtype, device=v.device)
+    p = make_problem(B, H, 1, dk, dv, variant=variant, io_dtype=v.dtype, eps=eps, eps_gamma=eps_gamma)
+    _check(load_library().falcon_decode_step(
+        ctypes.byref(p), _ptr(phi_k_prev), _ptr(phi_q), _ptr(v), _ptr(beta), _ptr(lam), _ptr(S),
+        _ptr(is_first), _ptr(o), _stream(stream)))
+    return o

@@ -1,0 +1,172 @@
+/*
+ * falcon.h -- C ABI of the MI355X (gfx950) Falcon fast-weight library.
+ *
+ * The library computes the read-after-write, prefix-shifted, NLMS-normalised
+ * delta rule of "Fast Weight Attention for Continual Learning" (arXiv
+ * 2608.27763; section and equation numbers below are the paper's) and its
+ * inner-product and per-column relatives.  For every (batch b, head h) the
+ * fast state S in R^{dk x dv} evolves over t = 1..T as
+ *
+ *     x_t   = phi(k_{t-1})             x_1 = k_prev, or 0 on a fresh start
+ *     eta_t = beta_t / (||x_t||^2 + lam_t + eps)          (Eq. 3.4)
+ *             eta_t := 0 if the denominator is 0, and eta_1 := 0 on a fresh
+ *             start (Section 3, indexing and causality conventions)
+ *     alpha_t = min(eta_t lam_t, 1 - eps_gamma),  gamma_t = 1 - alpha_t
+ *             (Section 4.3, "Decay positivity"; applied in every entry point)
+ *     FALCON_1 : S_t = gamma_t S_{t-1} + eta_t x_t r_t^T, r_t = v_t - S_{t-1}^T x_t
+ *     FALCON_1A: S_t = gamma_t S_{t-1} + eta_t x_t v_t^T            (Section 4.3)
+ *     FALCON_2 : per-column gains beta_{t,j}: column j of S follows FALCON_1
+ *                with eta_{t,j}, gamma_{t,j}                       (Section 4.2)
+ *     FALCON_2A: per-column gains, additive write                  (Eq. 4.7)
+ *     o_t = S_t^T phi(q_t)              (read after write, Section 4 summary)
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers owned by the caller, contiguous
+ *    row-major with the last axis fastest, 16-byte aligned.  Layouts:
+ *      phi_k, phi_q : [B, H, T, dk]     io dtype
+ *      v, o         : [B, H, T, dv]     io dtype
+ *      beta         : [B, H, T] (FALCON_1, FALCON_1A) or [B, H, T, dv]
+ *                     (FALCON_2, FALCON_2A), float32
+ *      lam          : [B, H, T]         float32
+ *      S0, S_T, S   : [B, H, dk, dv]    float32 (dv fastest)
+ *      k_prev       : [B, H, dk]        io dtype
+ *  - Calls are asynchronous and stream-ordered on `stream` (a hipStream_t;
+ *    NULL means the legacy default stream).  The library never synchronises
+ *    the device, allocates no device memory in these entry points, and keeps
+ *    no global mutable state, so concurrent calls on different streams are
+ *    safe as long as their output buffers do not overlap.
+ *  - Every argument is validated before anything is launched; on error the
+ *    call returns a negative falcon_status and touches no memory.
+ *  - Launch failures reported by the HIP runtime return FALCON_ERR_HIP.
+ *  - Values outside the paper's domain (beta outside (0,2), lam < 0,
+ *    non-finite data) are not checked on the device: they propagate
+ *    arithmetically (NaN in, NaN out).
+ *  - Supported sizes: dk, dv in {16, 32, 64, 128}; chunk C in {16, 32, 64};
+ *    any T >= 0 (the last chunk may be ragged); B, H >= 0.
+ *  - Arithmetic: the state and every accumulation are float32.  With bf16
+ *    I/O the matrix products of the chunked path take bf16 operands with
+ *    float32 accumulation; with float32 I/O everything is float32.
+ */
+#ifndef FALCON_H_
+#define FALCON_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FALCON_ABI_VERSION 1
+
+typedef enum {
+  FALCON_OK = 0,
+  FALCON_ERR_NULL = -1,      /* a required pointer is NULL                    */
+  FALCON_ERR_SHAPE = -2,     /* B, H, T < 0, or dk / dv not supported         */
+  FALCON_ERR_DTYPE = -3,     /* io_dtype not a falcon_dtype                   */
+  FALCON_ERR_CHUNK = -4,     /* chunk size not supported                      */
+  FALCON_ERR_ALIGN = -5,     /* a pointer is not 16-byte aligned              */
+  FALCON_ERR_WORKSPACE = -6, /* workspace missing or smaller than required   */
+  FALCON_ERR_VARIANT = -7,   /* variant not a falcon_variant                  */
+  FALCON_ERR_HIP = -8,       /* the HIP runtime reported an error at launch  */
+  FALCON_ERR_VALUE = -9,     /* eps < 0 / not finite, eps_gamma not in (0,1) */
+  FALCON_ERR_ALIAS = -10     /* o overlaps an input                           */
+} falcon_status;
+
+typedef enum {
+  FALCON_1 = 1,   /* scalar NLMS regression rule (Section 4, Falcon-1)      */
+  FALCON_1A = 2,  /* scalar inner-product rule   (Section 4.3, Falcon-1A)   */
+  FALCON_2 = 3,   /* per-column regression rule  (Section 4.2, Falcon-2)    */
+  FALCON_2A = 4   /* per-column inner-product    (Section 4.3, Falcon-2A)   */
+} falcon_variant;
+
+typedef enum {
+  FALCON_F32 = 0,  /* float32 features, values and outputs */
+  FALCON_BF16 = 1  /* bfloat16 features, values and outputs (RNE on store) */
+} falcon_dtype;
+
+/* Problem description (plain int32 fields so that every language binds it
+ * the same way). */
+typedef struct {
+  int32_t B, H, T;      /* batch, heads, sequence length                    */
+  int32_t dk, dv;       /* key-feature and value widths                     */
+  int32_t variant;      /* a falcon_variant                                 */
+  int32_t io_dtype;     /* a falcon_dtype                                   */
+  float eps;            /* step-size stabiliser, >= 0 (Eq. 3.4)             */
+  float eps_gamma;      /* positive-decay clamp, in (0, 1) (Section 4.3);
+                           the pages give no value, 1e-6 is the default    */
+} falcon_problem;
+
+/* Version of this ABI (FALCON_ABI_VERSION of the built library). */
+int32_t falcon_abi_version(void);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* falcon_status_string(int32_t status);
+
+/*
+ * falcon_fwd_recurrent -- the recurrent form (paper, Section 4.6 and the
+ * complexity table of the juhoplayground post: O(N) sequential scan, O(1)
+ * state).  One pass over T per (b, h) with the state held on-chip.
+ *
+ *  S0      : initial state, or NULL for S_0 = 0.
+ *  k_prev  : phi(k_0), the key feature preceding token 1, for continuing a
+ *            sequence; NULL selects the fresh-start boundary x_1 = 0,
+ *            eta_1 = 0 (even when S0 is not NULL).
+ *  o       : output, must not overlap any input.
+ *  S_T     : final state, or NULL to skip; may alias S0 exactly.
+ */
+falcon_status falcon_fwd_recurrent(const falcon_problem* p,
+                                   const void* phi_k, const void* phi_q, const void* v,
+                                   const float* beta, const float* lam,
+                                   const float* S0, const void* k_prev,
+                                   void* o, float* S_T, hipStream_t stream);
+
+/*
+ * falcon_fwd_chunked -- the chunk-parallel form (paper, Section 4.2
+ * "Chunk-parallel implementation" and the SSD-style chunking of the
+ * rainbus review: intra-chunk work in parallel, only the fixed-size state
+ * passed between chunks).  Same arguments and result as
+ * falcon_fwd_recurrent up to float rounding, plus the chunk size C.
+ *
+ *  C         : chunk length, 16, 32 or 64.
+ *  workspace : device scratch of at least falcon_workspace_bytes(p, C)
+ *              bytes (may be NULL when that is 0).
+ */
+falcon_status falcon_fwd_chunked(const falcon_problem* p,
+                                 const void* phi_k, const void* phi_q, const void* v,
+                                 const float* beta, const float* lam,
+                                 const float* S0, const void* k_prev,
+                                 void* o, float* S_T,
+                                 int32_t C, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
+/* Device scratch needed by falcon_fwd_chunked for this problem and C;
+ * returns (size_t)-1 for an invalid problem. */
+size_t falcon_workspace_bytes(const falcon_problem* p, int32_t C);
+
+/*
+ * falcon_decode_step -- one read-after-write token for every (b, h) from a
+ * carried state (the recurrent form at inference).  p->T is ignored.
+ *
+ *  phi_k_prev : [B, H, dk] io dtype, the PREVIOUS token's key feature x_t.
+ *  phi_q, v   : [B, H, dk] / [B, H, dv] io dtype, this token's query, value.
+ *  beta       : [B, H] (FALCON_1, 1A) or [B, H, dv] (FALCON_2, 2A), float32.
+ *  lam        : [B, H] float32.
+ *  S          : [B, H, dk, dv] float32, updated IN PLACE to S_t.
+ *  is_first   : [B] bytes or NULL; a nonzero entry marks a sequence whose
+ *               current token is t = 1, where eta := 0 and gamma := 1.
+ *  o          : [B, H, dv] io dtype, o_t = S_t^T phi(q_t).
+ */
+falcon_status falcon_decode_step(const falcon_problem* p,
+                                 const void* phi_k_prev, const void* phi_q, const void* v,
+                                 const float* beta, const float* lam,
+                                 float* S, const uint8_t* is_first,
+                                 void* o, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FALCON_H_ */

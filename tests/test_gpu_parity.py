@@ -1,0 +1,179 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle on
+identical seeded inputs, element by element (relative L2 over the whole
+tensor, per the stated tolerances: 1e-4 for float32 I/O, 2e-2 for bf16 I/O
+with the float32 state)."""
+
+import numpy as np
+import pytest
+import torch
+
+from delta_rule_recurrence_amd import falcon as fb
+from delta_rule_recurrence_amd import inputs as I
+
+from gpu_utils import TOL, check, oracle_forward, rel_l2, to_dev
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def _run(entry, d, variant, C=64, S0=None, k_prev=None, **kw):
+    if entry == "recurrent":
+        return fb.falcon_fwd_recurrent(d["phi_k"], d["phi_q"], d["v"], d["beta"], d["lam"],
+                                       variant=variant, S0=S0, k_prev=k_prev, **kw)
+    return fb.falcon_fwd_chunked(d["phi_k"], d["phi_q"], d["v"], d["beta"], d["lam"],
+                                 variant=variant, C=C, S0=S0, k_prev=k_prev, **kw)
+
+
+# ---- the tiny float32 workload (1 x 1 x 64, d = 16, C = 16, seed 0) ---------
+
+@pytest.mark.parametrize("entry", ["recurrent", "chunked"])
+def test_tiny_f32_workload(entry):
+    w = I.WORKLOADS["f1_recurrent_tiny"]
+    d = I.workload_inputs(w)
+    O_ref, S_ref = oracle_forward(w.variant, d)
+    o, S_T = _run(entry, to_dev(d), w.variant, C=w.C)
+    torch.cuda.synchronize()
+    check(o, S_T, O_ref, S_ref, TOL["f32"], f"{entry} tiny")
+
+
+# ---- small shapes: every variant, dtype, width, chunk, ragged T -------------
+
+SMALL = [
+    # (variant, io, B, H, T, dk, dv, C)
+    ("falcon1", "f32", 2, 3, 100, 16, 16, 16),
+    ("falcon1", "f32", 1, 2, 77, 32, 64, 32),
+    ("falcon1", "f32", 2, 2, 130, 64, 64, 64),
+    ("falcon1", "bf16", 2, 2, 130, 64, 64, 64),
+    ("falcon1", "bf16", 1, 3, 200, 128, 128, 64),
+    ("falcon1", "bf16", 1, 2, 67, 128, 32, 16),
+    ("falcon1a", "f32", 2, 2, 90, 64, 64, 32),
+    ("falcon1a", "bf16", 2, 3, 150, 64, 64, 64),
+    ("falcon2", "f32", 2, 2, 90, 32, 32, 16),
+    ("falcon2", "bf16", 2, 3, 150, 64, 64, 64),
+    ("falcon2a", "f32", 1, 2, 70, 64, 16, 32),
+    ("falcon2a", "bf16", 2, 2, 65, 64, 64, 64),
+]
+
+
+@pytest.mark.parametrize("entry", ["recurrent", "chunked"])
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "-".join(map(str, c)))
+def test_small_shapes(entry, case):
+    variant, io, B, H, T, dk, dv, C = case
+    d = I.make_inputs(B, H, T, dk, dv, seed=100 + T, io_dtype=io,
+                      per_column_beta=variant in ("falcon2", "falcon2a"))
+    O_ref, S_ref = oracle_forward(variant, d)
+    o, S_T = _run(entry, to_dev(d), variant, C=C)
+    torch.cuda.synchronize()
+    check(o, S_T, O_ref, S_ref, TOL[io], f"{entry} {case}")
+
+
+@pytest.mark.parametrize("entry", ["recurrent", "chunked"])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_carried_state_and_continuation(entry, io):
+    """A run split at T1 with (S_T1, phi(k_T1)) handed over equals one run,
+    and a carried state without k_prev uses the fresh-start boundary."""
+    B, H, T, dk, dv, T1 = 2, 3, 150, 64, 64, 70
+    d = I.make_inputs(B, H, T, dk, dv, seed=7, io_dtype=io)
+    S0 = I.random_state((B, H, dk, dv), seed=8)
+    O_ref, S_ref = oracle_forward("falcon1", d, S0=S0)
+    dd = to_dev(d)
+    o, S_T = _run(entry, dd, "falcon1", S0=S0.cuda())
+    torch.cuda.synchronize()
+    check(o, S_T, O_ref, S_ref, TOL[io], f"{entry} carried S0")
+    first = {k: v[:, :, :T1].contiguous() for k, v in dd.items()}
+    second = {k: v[:, :, T1:].contiguous() for k, v in dd.items()}
+    o1, S1 = _run(entry, first, "falcon1", S0=S0.cuda())
+    kp = dd["phi_k"][:, :, T1 - 1].contiguous()
+    o2, S2 = _run(entry, second, "falcon1", S0=S1, k_prev=kp)
+    torch.cuda.synchronize()
+    check(torch.cat([o1, o2], dim=2), S2, O_ref, S_ref, TOL[io], f"{entry} split")
+
+
+@pytest.mark.parametrize("entry", ["recurrent", "chunked"])
+def test_state_in_place_and_optional_outputs(entry):
+    B, H, T, dk, dv = 1, 2, 40, 32, 32
+    d = to_dev(I.make_inputs(B, H, T, dk, dv, seed=9, io_dtype="f32"))
+    S = I.random_state((B, H, dk, dv), seed=10).cuda()
+    O_ref, S_ref = oracle_forward("falcon1", {k: v.cpu() for k, v in d.items()}, S0=S.cpu())
+    o, S_T = _run(entry, d, "falcon1", C=16, S0=S, S_T=S)   # S_T aliases S0
+    torch.cuda.synchronize()
+    check(o, S, O_ref, S_ref, TOL["f32"], f"{entry} in place")
+    o2, none = _run(entry, d, "falcon1", C=16, S0=None, return_state=False)
+    torch.cuda.synchronize()
+    assert none is None
+    O_ref2, _ = oracle_forward("falcon1", {k: v.cpu() for k, v in d.items()})
+    assert rel_l2(o2.cpu().numpy(), O_ref2) <= TOL["f32"]
+
+
+def test_empty_sequence_copies_state():
+    B, H, dk, dv = 2, 2, 16, 16
+    d = to_dev(I.make_inputs(B, H, 1, dk, dv, seed=11, io_dtype="f32"))
+    d = {k: v[:, :, :0].contiguous() for k, v in d.items()}
+    S0 = I.random_state((B, H, dk, dv), seed=12).cuda()
+    for entry in ("recurrent", "chunked"):
+        o, S_T = _run(entry, d, "falcon1", C=16, S0=S0)
+        torch.cuda.synchronize()
+        assert o.numel() == 0
+        assert torch.equal(S_T, S0)
+
+
+def test_chunk_size_invariance():
+    B, H, T, dk, dv = 2, 3, 256, 64, 64
+    d = to_dev(I.make_inputs(B, H, T, dk, dv, seed=13, io_dtype="f32"))
+    outs = [fb.falcon_fwd_chunked(d["phi_k"], d["phi_q"], d["v"], d["beta"], d["lam"], C=C)
+            for C in (16, 32, 64)]
+    torch.cuda.synchronize()
+    for o, s in outs[1:]:
+        assert rel_l2(o.cpu().numpy(), outs[0][0].cpu().numpy()) <= 1e-5
+        assert rel_l2(s.cpu().numpy(), outs[0][1].cpu().numpy()) <= 1e-5
+
+
+def test_clamp_active_stress():
+    """beta near 2, large lam and tiny keys: the positive-decay clamp and
+    gamma = eps_gamma are exercised on every path."""
+    B, H, T, dk, dv = 1, 2, 96, 32, 32
+    d = I.make_inputs(B, H, T, dk, dv, seed=14, io_dtype="f32", feature_scale=0.01)
+    d["beta"] = torch.full_like(d["beta"], 1.9)
+    d["lam"] = torch.full_like(d["lam"], 10.0)
+    O_ref, S_ref = oracle_forward("falcon1", d, eps_gamma=1e-3)
+    for entry in ("recurrent", "chunked"):
+        o, S_T = _run(entry, to_dev(d), "falcon1", C=32, eps_gamma=1e-3)
+        torch.cuda.synchronize()
+        check(o, S_T, O_ref, S_ref, TOL["f32"], f"{entry} clamp")
+
+
+def test_nan_propagates_without_hang():
+    B, H, T, dk, dv = 1, 1, 64, 16, 16
+    d = I.make_inputs(B, H, T, dk, dv, seed=15, io_dtype="f32")
+    d["lam"][0, 0, 20] = float("nan")
+    for entry in ("recurrent", "chunked"):
+        o, S_T = _run(entry, to_dev(d), "falcon1", C=16)
+        torch.cuda.synchronize()
+        assert torch.isnan(o[0, 0, 20:]).any()
+        assert torch.isfinite(o[0, 0, :20]).all()
+
+
+# ---- decode ------------------------------------------------------------------
+
+@pytest.mark.parametrize("variant", ["falcon1", "falcon1a", "falcon2", "falcon2a"])
+@pytest.mark.parametrize("io,dk,dv", [("f32", 16, 16), ("bf16", 64, 128), ("bf16", 128, 128),
+                                      ("f32", 128, 32)])
+def test_decode_steps_match_forward(variant, io, dk, dv):
+    B, H, T = 3, 2, 12
+    per_col = variant in ("falcon2", "falcon2a")
+    d = I.make_inputs(B, H, T, dk, dv, seed=16, io_dtype=io, per_column_beta=per_col)
+    O_ref, S_ref = oracle_forward(variant, d)
+    dd = to_dev(d)
+    S = torch.zeros((B, H, dk, dv), dtype=torch.float32, device="cuda")
+    first = torch.ones(B, dtype=torch.uint8, device="cuda")
+    outs = []
+    for t in range(T):
+        x = torch.zeros_like(dd["phi_k"][:, :, 0]) if t == 0 else dd["phi_k"][:, :, t - 1].contiguous()
+        beta = dd["beta"][:, :, t].contiguous()
+        outs.append(fb.falcon_decode_step(x, dd["phi_q"][:, :, t].contiguous(),
+                                          dd["v"][:, :, t].contiguous(), beta,
+                                          dd["lam"][:, :, t].contiguous(), S, variant=variant,
+                                          is_first=first if t == 0 else None))
+    torch.cuda.synchronize()
+    check(torch.stack(outs, dim=2), S, O_ref, S_ref, TOL[io], f"decode {variant}")
