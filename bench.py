@@ -1,0 +1,176 @@
+"""Benchmark of the Falcon-1 chunked forward on one MI355X.
+
+Workload: Falcon-1 chunk-parallel forward, B=8, H=12, T=2048, dk=dv=64,
+C=64, bf16 features/values/outputs, float32 gates and state, S_0 = 0,
+synthetic seeded inputs (seed 1).  One step = one falcon_fwd_chunked call
+over the whole batch.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tokens/sec + % MFMA peak, Falcon-1 chunked fwd B=8 H=12 T=2048 d=64 bf16"
+WORKLOAD = "f1_chunked_8x12x2048_d64"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "falcon1_chunked_mfma_8x12x2048_d64_pmc.md")
+KERNEL_SOURCES = ["delta_rule_recurrence_amd/csrc/falcon_chunked_mfma.hip",
+                  "delta_rule_recurrence_amd/csrc/falcon_chunked_generic.hip",
+                  "delta_rule_recurrence_amd/csrc/falcon_chunked.hip"]
+
+
+def algorithmic_bytes(B, H, T, dk, dv, io_bytes=2):
+    """Compulsory HBM bytes of one forward: read phi(k), phi(q), v once, beta
+    and lam once, write o once and S_T once (S_0 = 0 is not read)."""
+    th = B * H * T
+    return th * (2 * dk + dv) * io_bytes + th * 2 * 4 + th * dv * io_bytes + B * H * dk * dv * 4
+
+
+def algorithmic_flops(B, H, T, dk, dv, C):
+    """Falcon-1 chunked-form flops per token-head, triangles counted once:
+    W S, X^T R and Q S (2 dk dv each), the decayed Gram and Q X^T (C dk each),
+    the W and U factors (C (dk + dv)), the intra-chunk read (C dv) and the
+    triangular inverse (C^2 / 3)."""
+    per = 6 * dk * dv + 2 * C * dk + C * (dk + dv) + C * dv + C * C / 3
+    return B * H * T * per
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        p = os.path.join(ROOT, rel)
+        if os.path.exists(p):
+            h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, or None
+    when the kernel sources changed after the counters were taken."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    text = open(PMC_SUMMARY).read()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (m_hash and m_bytes) or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_baseline(d, w, o_gpu, S_gpu):
+    """The oracle as it stands, on the host, over a bounded sample: the first
+    T_s tokens of every (batch, head) sequence of the same workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from delta_rule_recurrence_amd import inputs as I
+    from oracle import falcon_oracle as orc
+
+    Ts = 1024
+    f = I.as_f64
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        O, S = orc.falcon_forward(w.variant, f(d["phi_k"][:, :, :Ts]), f(d["phi_q"][:, :, :Ts]),
+                                  f(d["v"][:, :, :Ts]), f(d["beta"][:, :, :Ts]),
+                                  f(d["lam"][:, :, :Ts]), eps=w.eps, eps_gamma=w.eps_gamma)
+        dt = time.perf_counter() - t0
+    ref = np.asarray(O)
+    got = o_gpu[:, :, :Ts].float().cpu().numpy()
+    rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    return {"value": w.B * w.H * Ts / dt / w.H, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"all {w.B}x{w.H} sequences, first {Ts} of {w.T} tokens (fp64 numpy, 1 thread)",
+            "seconds": round(dt, 3), "rel_l2_o_prefix": rel}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the Falcon forward "
+              "shards by (batch, head) with no communication, so there is no multi-GPU path here.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from delta_rule_recurrence_amd import falcon as fb
+    from delta_rule_recurrence_amd import inputs as I
+
+    w = I.WORKLOADS[WORKLOAD]
+    d = I.workload_inputs(w)
+    dev = {k: v.cuda() for k, v in d.items()}
+    o = torch.empty((w.B, w.H, w.T, w.dv), dtype=torch.bfloat16, device="cuda")
+    S_T = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    p = fb.make_problem(w.B, w.H, w.T, w.dk, w.dv, variant=w.variant, io_dtype=torch.bfloat16,
+                        eps=w.eps, eps_gamma=w.eps_gamma)
+    ws_bytes = fb.falcon_workspace_bytes(p, w.C)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+
+    def step():
+        fb.falcon_fwd_chunked(dev["phi_k"], dev["phi_q"], dev["v"], dev["beta"], dev["lam"],
+                              variant=w.variant, C=w.C, o=o, S_T=S_T, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = ev0.elapsed_time(ev1) / args.steps
+    ms_per_step = max(wall * 1e3 / args.steps, ev_ms)
+
+    tokens = w.B * w.T
+    bytes_alg = algorithmic_bytes(w.B, w.H, w.T, w.dk, w.dv)
+    flops_alg = algorithmic_flops(w.B, w.H, w.T, w.dk, w.dv, w.C)
+    # One kernel launch per step: its average duration is the event time.
+    achieved_gbs = bytes_alg / (ev_ms * 1e-3) / 1e9
+    traffic = measured_traffic()
+    line = {
+        "metric": METRIC,
+        "value": tokens / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1)/8 features and values, sigmoid/softplus gates)",
+        "config": {"workload": WORKLOAD, "variant": w.variant, "B": w.B, "H": w.H, "T": w.T,
+                   "dk": w.dk, "dv": w.dv, "C": w.C, "io": "bf16", "state": "f32"},
+        "mfma_pct_of_peak": 100.0 * flops_alg / (ev_ms * 1e-3) / (BF16_MFMA_PEAK_TFLOPS * 1e12),
+        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes": bytes_alg, "kernel_ms": ev_ms},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(d, w, o, S_T)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,15 +1,18 @@
-// Chunked-forward dispatch: the MFMA kernel where it applies, the general
-// float32 kernel otherwise.
+// Chunked-forward dispatch: the fused MFMA kernel where it applies (Falcon-1,
+// bf16 I/O, dk = dv = 64, C = 64), the general float32 kernel otherwise.
 #include "falcon_device.h"
 #include "falcon_launch.h"
 
 namespace falcon {
 
 hipError_t launch_chunked_generic(const ProblemArgs& a, hipStream_t st);
+bool chunked_mfma_applies(const ProblemArgs& a);
+hipError_t launch_chunked_mfma(const ProblemArgs& a, hipStream_t st);
 
 size_t chunked_workspace_bytes(const ProblemArgs&) { return 0; }
 
 hipError_t launch_chunked(const ProblemArgs& a, hipStream_t st) {
+  if (chunked_mfma_applies(a)) return launch_chunked_mfma(a, st);
   return launch_chunked_generic(a, st);
 }
 
