@@ -69,16 +69,73 @@ def measured_traffic():
     return float(m_bytes.group(1))
 
 
+def decode_bytes(B, H, dk, dv, io_bytes=2):
+    """Compulsory HBM bytes of one decode step: the float32 state read and
+    written once, x, q, v read, beta and lam read, o written."""
+    bh = B * H
+    return 2 * bh * dk * dv * 4 + bh * (2 * dk + dv) * io_bytes + bh * 2 * 4 + bh * dv * io_bytes
+
+
+def bench_decode(steps=50, warmup=5):
+    """Decode step at batch 512 x 12 heads, d = 128, float32 state (~384 MiB)
+    resident in HBM; inputs for 8 distinct steps are pre-staged and cycled."""
+    import torch
+
+    from delta_rule_recurrence_amd import falcon as fb
+    from delta_rule_recurrence_amd import inputs as I
+
+    D = I.DECODE
+    B, H, dk, dv = D["B"], D["H"], D["dk"], D["dv"]
+    S = I.random_state((B, H, dk, dv), seed=D["seed"], scale=0.05).cuda()
+    staged = [{k: v.cuda() for k, v in I.decode_step_inputs(s, B, H, dk, dv, seed=D["seed"]).items()}
+              for s in range(1, 9)]
+    o = torch.empty((B, H, dv), dtype=torch.bfloat16, device="cuda")
+
+    def step(i):
+        st = staged[i % 8]
+        fb.falcon_decode_step(staged[(i - 1) % 8]["phi_k"], st["phi_q"], st["v"], st["beta"], st["lam"],
+                              S, o=o, eps=D["eps"], eps_gamma=D["eps_gamma"])
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = decode_bytes(B, H, dk, dv)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": D["name"], "steps": steps, "us_per_step": ms * 1e3,
+            "tokens_per_s": B / (ms * 1e-3), "algorithmic_bytes": nbytes,
+            "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
+
+
+def calibrate_copy(nbytes=1 << 28, reps=5):
+    """A plain device copy of known size, for scaling rocprofv3 FETCH_SIZE /
+    WRITE_SIZE counters (each copy reads and writes nbytes once)."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_per_copy": nbytes, "copies": reps}))
+
+
 def cpu_baseline(d, w, o_gpu, S_gpu):
-    """The oracle as it stands, on the host, over a bounded sample: the first
-    T_s tokens of every (batch, head) sequence of the same workload."""
+    """The oracle as it stands, timed on the host over the same workload (all
+    sequences, all tokens; a few seconds of single-thread fp64 numpy)."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     from delta_rule_recurrence_amd import inputs as I
     from oracle import falcon_oracle as orc
 
-    Ts = 1024
+    Ts = w.T
     f = I.as_f64
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
@@ -89,8 +146,8 @@ def cpu_baseline(d, w, o_gpu, S_gpu):
     ref = np.asarray(O)
     got = o_gpu[:, :, :Ts].float().cpu().numpy()
     rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
-    return {"value": w.B * w.H * Ts / dt / w.H, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"all {w.B}x{w.H} sequences, first {Ts} of {w.T} tokens (fp64 numpy, 1 thread)",
+    return {"value": w.B * Ts / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"the whole workload: all {w.B}x{w.H} sequences x {Ts} tokens (fp64 numpy, 1 thread)",
             "seconds": round(dt, 3), "rel_l2_o_prefix": rel}
 
 
@@ -100,6 +157,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain copy of known size (for PMC counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the Falcon forward "
@@ -112,6 +172,9 @@ def main():
     from delta_rule_recurrence_amd import falcon as fb
     from delta_rule_recurrence_amd import inputs as I
 
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     w = I.WORKLOADS[WORKLOAD]
     d = I.workload_inputs(w)
     dev = {k: v.cuda() for k, v in d.items()}
@@ -167,6 +230,8 @@ def main():
                      "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes": bytes_alg, "kernel_ms": ev_ms},
     }
+    if not args.no_decode:
+        line["decode"] = bench_decode()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(d, w, o, S_T)
     print(json.dumps(line))
