@@ -1,46 +1,51 @@
 // Fused chunk-parallel Falcon-1 forward on MFMA (gfx950), bf16 I/O,
 // dk = dv = 64, chunk C = 64.
 //
-// One workgroup owns one (batch, head) sequence.  Its waves split into two
-// roles that run concurrently and meet in a ring of LDS slots:
+// One workgroup owns one (batch, head) sequence for its whole length.  Its
+// six waves split into two roles that run concurrently:
 //
-//  * three FACTOR waves, each building the state-independent factors of one
-//    chunk at a time (chunks f, f + 3, f + 6, ...), entirely from registers:
+//  * two CHAIN waves; wave w owns value columns 32w..32w+31 of the float32
+//    state S (kept in MFMA result registers for the whole sequence):
+//      a3  R = U - W S (rows eta_i r_i), S <- e^{g_63} S + (Diag(e^{g_63-g}) X)^T R;
+//      a4  O = Diag(e^g) Q S + M R, stored as bf16;
+//    they also stream the sequence's keys, queries and gates from HBM into
+//    an LDS ring two chunks ahead (direct global-to-LDS loads, 1 KiB per
+//    instruction, fully coalesced).
+//  * a FACTOR GROUP of four waves that builds the state-independent factors
+//    of the next chunk while the chain works on the current one:
 //      a1  x_i = phi(k_{t0+i-1}), E_i = ||x_i||^2, eta_i (Eq. 3.4 with the
 //          fresh-start sentinel), log gamma_i = log1p(-min(eta_i lam_i,
-//          1 - eps_gamma)) (Section 4.3) and the chunk-local prefix g_i
-//          (log-space renormalisation of Section 4.4 applied per chunk);
+//          1 - eps_gamma)) (Section 4.3) and the chunk-local prefix g_i (the
+//          log-space renormalisation of Section 4.4 applied per chunk);
 //      a2  the decayed strictly-lower Gram matrix
-//          A_{i,s} = eta_i e^{g_{i-1}-g_s} (x_i . x_s), T = (I + A)^{-1} by
-//          blocked forward substitution (16x16 diagonal blocks by column
-//          elimination in registers, off-diagonal blocks on MFMA), the
-//          factor W = T Diag(eta e^{g_{s-1}}) X ("one multi-RHS TriSolve per
-//          chunk" of the WY form), the decayed read mask
-//          M_{i,s} = e^{g_i-g_s} (q_i . x_s) (s <= i, read after write) and
-//          the decayed keys (Diag(e^{g_63-g}) X)^T;
-//  * four CHAIN waves, wave w owning value columns 16w..16w+15 of the
-//    float32 state S for the whole sequence:
-//      a2  U = T Diag(eta) V for its columns;
-//      a3  R = U - W S (rows eta_i r_i), S <- e^{g_63} S + (Diag(e^{g_63-g}) X)^T R;
-//      a4  O = Diag(e^g) Q S + M R, stored as bf16.
+//          A_{i,s} = eta_i e^{g_{i-1}-g_s} (x_i . x_s), T = (I + A)^{-1}
+//          (16x16 diagonal blocks by column elimination in registers with
+//          DPP broadcasts, off-diagonal blocks by MFMA block products),
+//          W = T Diag(eta e^{g_{s-1}}) X and U = T Diag(eta) V ("one
+//          multi-RHS TriSolve per chunk" of the WY form), the decayed read
+//          mask M_{i,s} = e^{g_i-g_s} (q_i . x_s) for s <= i (read after
+//          write) and the decayed keys (Diag(e^{g_63-g}) X)^T.
+//    Wave f0 carries the inverse (the critical path); f1..f3 share the mask,
+//    the key/value transposes and the W and U products.
 //
-// A slot is handed over with LDS flags (release/acquire at workgroup scope):
-// full[slot] = chunk index when its factors are written, consumed[slot]
-// counts chain waves done with it.  Every wait is bounded.
-//
-// Every input byte is read from HBM once (the chain waves re-read Q and V
-// tiles that the factor waves touched moments before, from L2) and every
-// output byte is written once.
+// Hand-over is through LDS: a 3-entry input ring, 2 factor slots and a pair
+// of T buffers, each guarded by counters with workgroup-scope
+// release/acquire.  Every wait is bounded (spin limit + abort flag), so no
+// schedule can hang.  Every input byte is read from HBM once (values by the
+// U waves, the rest by the chain's ring loads) and every output byte is
+// written once.
 //
 // MFMA operand convention.  v_mfma_f32_16x16x32_bf16 takes, in lane l, row
 // (l & 15) of A and column (l & 15) of B with eight k-values each; the
-// result holds column (l & 15), rows 4 (l >> 4) .. +3.  Every product here
-// feeds lane group g = l >> 4 the k-values {4g..4g+3, 16+4g..16+4g+3} of a
-// 32-wide k block (the same for A and B, so the sum is unchanged).  With
-// that choice two stacked result tiles are exactly the operand fragment of
-// the next product, which keeps S and R in registers, and a product with
-// the identity turns token-major rows into the feature-major fragments that
-// contract over tokens.
+// result holds column (l & 15), rows 4 (l >> 4) .. +3.  Products whose two
+// operands are rows of the inputs give lane group g = l >> 4 the eight
+// contiguous k-values 8g..8g+7 of a 32-wide block (one 16-byte read).
+// Products that consume results feed lane group g the k-values
+// {4g..4g+3, 16+4g..16+4g+3}: then two stacked result tiles are exactly
+// the next operand fragment, which keeps S and R in registers, and a
+// product with a selection matrix turns token-major rows into the
+// feature-major fragments that contract over tokens.  Either way A and B
+// use the same order, so every sum is unchanged.
 
 #include "falcon_device.h"
 #include "falcon_launch.h"
@@ -52,43 +57,61 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kC = 64;            // chunk length
 constexpr int kD = 64;            // dk = dv
 constexpr int kP = 72;            // bf16 row pitch of T in LDS (elements)
-constexpr int kNF = 3;            // factor waves
-constexpr int kNS = 4;            // ring slots
-constexpr int kThreads = 64 * (4 + kNF);
+constexpr int kNI = 3;            // input ring entries
+constexpr int kNS = 2;            // factor slots
+constexpr int kChain = 2;         // chain waves
+constexpr int kFactor = 4;        // factor waves
+constexpr int kThreads = 64 * (kChain + kFactor);
 constexpr int kSpinLimit = 1 << 22;
+
+// Rows of one chunk as loaded from HBM: 64 rows of 128 bytes, the 16-byte
+// segment q of row r stored at position q ^ ((r >> 1) & 7) (conflict-free
+// reads of 16 consecutive rows).
+struct InputEntry {
+  uint16_t x[kC * kD];            // keys phi(k_{t0+r-1})
+  uint16_t q[kC * kD];            // queries phi(q_{t0+r})
+  float beta[kC];
+  float lam[kC];
+};
 
 // Factors of one chunk, as consumed by the chain waves.
 struct Slot {
   uint16_t wf[4 * 2 * 64 * 8];    // -W, A fragments [ib][m][lane][8]
   uint16_t mf[4 * 2 * 64 * 8];    // M^T, B fragments [ib][m][lane][8]
   uint16_t xh[4 * 2 * 64 * 8];    // (Diag(e^{g_63-g}) X)^T, A fragments [fb][m][lane][8]
-  uint16_t tb[kC * kP];           // T = (I + A)^{-1}, row-major
-  float eta[kC];                  // eta_s, token order
+  uint16_t uf[4 * 4 * 64 * 4];    // U result tiles [ib][cb][lane][4], bf16
   float gexp_t[kC];               // e^{g_i} at [c16 * 4 + ib] for i = 16 ib + c16
   float glast[4];                 // e^{g_63}
 };
 
-// Per factor wave: the chunk's gates in the orders its lanes read them, and
-// the diagonal 16x16 blocks of A.
-struct FactorPrivate {
-  float abt[4][16][16];           // [b][s][i] = A[16b+i][16b+s]
+// Gates of the chunk in the orders a factor wave reads them back.
+struct Gates {
   float graw[kC];                 // g_s, token order
   float sxg[kC];                  // eta_s e^{g_{s-1}}
   float sxh[kC];                  // e^{g_63 - g_s}
+  float eta[kC];                  // eta_s, token order
   float eta_t[kC];                // eta_i at [c16 * 4 + ib]
   float gprev_t[kC];              // g_{i-1} at [c16 * 4 + ib]
   float graw_t[kC];               // g_i at [c16 * 4 + ib]
 };
 
 struct Smem {
+  InputEntry in[kNI];
   Slot slot[kNS];
-  FactorPrivate fp[kNF];
-  int full[kNS];
-  int consumed[kNS];
+  uint16_t tb[2][kC * kP];        // T = (I + A)^{-1}, row-major, by chunk parity
+  float abt[4][16][16];           // diagonal blocks of A: [b][s][i] = A[16b+i][16b+s]
+  Gates gates[kFactor];
+  int in_ready[kNI];              // +1 per chain wave when its half of an entry landed
+  int in_free[kNI];               // +1 per chain wave when done with an entry
+  int slot_full[kNS];             // +1 per factor wave when its part is written
+  int slot_free[kNS];             // +1 per chain wave when it has read a slot
+  int t_ready[2];                 // chunk + 1 whose T is complete in tb[parity]
+  int t_used[2];                  // +1 per factor wave 1..3 done reading tb[parity]
   int abort_flag;
 };
 
@@ -101,25 +124,31 @@ __device__ __forceinline__ f32x4 mfma16(s16x4 a, s16x4 b, f32x4 c) {
 __device__ __forceinline__ uint16_t bf(float f) { return f32_to_bf16(f); }
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
-// k offset (within a 32-wide block) of fragment element e of lane group g.
+// k offset (within a 32-wide block) of element e of lane group g in the
+// result-compatible order.
 __device__ __forceinline__ int kperm(int g, int e) { return e < 4 ? 4 * g + e : 12 + 4 * g + e; }
 
-// Fragment of a bf16 row: k = kbase + kperm(g, 0..7).
+__device__ __forceinline__ int seg_pos(int r, int q) { return q ^ ((r >> 1) & 7); }
+
+// Contiguous-order fragment: k = 32m + 8g .. +7 of row r of a ring matrix.
+__device__ __forceinline__ bf16x8 ring_frag_c(const uint16_t* mat, int r, int m, int g) {
+  const uint4 v = *reinterpret_cast<const uint4*>(mat + r * kD + 8 * seg_pos(r, 4 * m + g));
+  return __builtin_bit_cast(bf16x8, v);
+}
+// Result-compatible fragment: k = 32m + kperm(g, 0..7) of row r of a ring matrix.
+__device__ __forceinline__ bf16x8 ring_frag_p(const uint16_t* mat, int r, int m, int g) {
+  const int off = 4 * (g & 1);
+  const uint2 a = *reinterpret_cast<const uint2*>(mat + r * kD + 8 * seg_pos(r, 4 * m + (g >> 1)) + off);
+  const uint2 b = *reinterpret_cast<const uint2*>(mat + r * kD + 8 * seg_pos(r, 4 * m + 2 + (g >> 1)) + off);
+  return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
+}
+// Result-compatible fragment of a bf16 row in a padded row-major array.
 __device__ __forceinline__ bf16x8 frag_lds(const uint16_t* row, int kbase, int g) {
   const uint2 a = *reinterpret_cast<const uint2*>(row + kbase + 4 * g);
   const uint2 b = *reinterpret_cast<const uint2*>(row + kbase + 16 + 4 * g);
   return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
 }
-// Same from global memory, or zeros when the row does not exist.
-__device__ __forceinline__ bf16x8 frag_global(const bf16_t* row, int kbase, int g, bool valid) {
-  uint2 a = make_uint2(0, 0), b = make_uint2(0, 0);
-  if (valid) {
-    a = *reinterpret_cast<const uint2*>(row + kbase + 4 * g);
-    b = *reinterpret_cast<const uint2*>(row + kbase + 16 + 4 * g);
-  }
-  return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
-}
-// Two stacked result tiles (k rows 0-15 and 16-31 of a block), scaled, as a fragment.
+// Two stacked result tiles (k rows 0-15 and 16-31 of a block) as a fragment.
 __device__ __forceinline__ bf16x8 frag_acc(f32x4 lo, f32x4 hi) {
   bf16x8 r;
 #pragma unroll
@@ -140,6 +169,11 @@ __device__ __forceinline__ void store_half(uint16_t* p, f32x4 v) {
   const uint32_t b = uint32_t(bf(v[2])) | (uint32_t(bf(v[3])) << 16);
   *reinterpret_cast<uint2*>(p) = make_uint2(a, b);
 }
+__device__ __forceinline__ f32x4 load_half(const uint16_t* p) {
+  const uint2 v = *reinterpret_cast<const uint2*>(p);
+  return f32x4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+               __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u)};
+}
 __device__ __forceinline__ s16x4 s16_acc(f32x4 v) {
   s16x4 r;
 #pragma unroll
@@ -150,12 +184,12 @@ __device__ __forceinline__ f32x4 ld4(const float* p) {
   const float4 v = *reinterpret_cast<const float4*>(p);
   return f32x4{v.x, v.y, v.z, v.w};
 }
-// B fragment of the 32x16 selection matrix picking columns 16h..16h+15 of a
-// 32-wide k block (a product with it transposes a tile into the result layout).
-__device__ __forceinline__ bf16x8 identity_frag(int h, int g, int c16) {
+// Contiguous-order B fragment of the selection matrix picking columns
+// 16h..16h+15 of a 32-wide block (a product with it transposes a tile).
+__device__ __forceinline__ bf16x8 select_frag(int h, int g, int c16) {
   bf16x8 r;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = static_cast<__bf16>(kperm(g, e) == 16 * h + c16 ? 1.0f : 0.0f);
+  for (int e = 0; e < 8; ++e) r[e] = static_cast<__bf16>(8 * g + e == 16 * h + c16 ? 1.0f : 0.0f);
   return r;
 }
 
@@ -195,8 +229,14 @@ __device__ __forceinline__ bool wait_at_least(int* flag, int target, int* abort_
   __hip_atomic_store(abort_flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   return false;
 }
+__device__ __forceinline__ void signal_add(int* flag, int l) {
+  if (l == 0) __hip_atomic_fetch_add(flag, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ bool aborted(int* abort_flag) {
+  return __hip_atomic_load(abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0;
+}
 
-// Lower 16x16 tiles (ib >= sb) of a 64x64 matrix.
+// Lower 16x16 tiles (ib >= sb) of a 64x64 matrix, n = 0..9.
 __device__ __forceinline__ void lower_tile(int n, int& ib, int& sb) {
   ib = n < 1 ? 0 : n < 3 ? 1 : n < 6 ? 2 : 3;
   sb = n - (ib * (ib + 1)) / 2;
@@ -213,43 +253,72 @@ struct Seq {
 };
 
 // ---------------------------------------------------------------------------
-// Factor wave: builds the slot of chunk c.
+// Ring loads (chain waves): half h of the entry of chunk c.  h = 0 loads the
+// keys and the gates, h = 1 the queries.  Rows past the sequence are loaded
+// from a valid row (their step size is 0, so their finite values never
+// reach a result); so is the fresh-start key row -1 (eta_1 = 0).
 // ---------------------------------------------------------------------------
-struct FactorLoads {
-  bf16x8 x[4][2];   // X rows, fragments [row block][k step]
-  bf16x8 q[4][2];   // Q rows
-  float beta, lam;
-};
-
-__device__ __forceinline__ void factor_load(FactorLoads& L, const Seq& sq, int c, int l) {
-  const int g = l >> 4, c16 = l & 15;
+__device__ __forceinline__ void ring_load(InputEntry& E, const Seq& sq, int c, int h, int l) {
   const int t0 = c * kC;
+  const int T = sq.T;
 #pragma unroll
-  for (int ib = 0; ib < 4; ++ib) {
-    const int tok = t0 + 16 * ib + c16;
-    const int kt = tok - 1;                               // x_i = phi(k_{t-1})
-    const bool xv = (kt >= 0 && kt < sq.T) || (kt == -1 && sq.k_prev);
-    const bf16_t* xrow = kt >= 0 ? sq.K + int64_t(kt) * kD : sq.k_prev;
-    const bool qv = tok < sq.T;
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      L.x[ib][m] = frag_global(xrow, 32 * m, g, xv);
-      L.q[ib][m] = frag_global(sq.Q + int64_t(tok) * kD, 32 * m, g, qv);
+  for (int j = 0; j < 8; ++j) {
+    const int r = 8 * j + (l >> 3);
+    const int q = (l & 7) ^ ((r >> 1) & 7);          // logical segment stored at position l & 7
+    const bf16_t* src;
+    if (h == 0) {
+      const int kt = t0 + r - 1;
+      if (kt < 0) src = sq.k_prev ? sq.k_prev : sq.K;
+      else src = sq.K + int64_t(kt < T ? kt : T - 1) * kD;
+    } else {
+      const int tok = t0 + r;
+      src = sq.Q + int64_t(tok < T ? tok : T - 1) * kD;
     }
+    uint16_t* dst = (h == 0 ? E.x : E.q) + j * 512;  // 8 rows of 64 bf16
+    __builtin_amdgcn_global_load_lds(src + 8 * q, (lds_void*)(dst), 16, 0, 0);
   }
-  const int tok = t0 + l;
-  L.beta = tok < sq.T ? sq.beta[tok] : 0.0f;
-  L.lam = tok < sq.T ? sq.lam[tok] : 0.0f;
+  if (h == 0) {
+    const int tok = t0 + l < T ? t0 + l : T - 1;
+    __builtin_amdgcn_global_load_lds(sq.beta + tok, (lds_void*)(E.beta), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(sq.lam + tok, (lds_void*)(E.lam), 4, 0, 0);
+  }
 }
 
-__device__ void factor_chunk(Smem& sm, FactorLoads& L, const Seq& sq, int c, int fw, int l,
+// ---------------------------------------------------------------------------
+// Factor group: wave fw of the four builds its share of the slot of chunk c.
+// ---------------------------------------------------------------------------
+struct ValueFrags {
+  bf16x8 v[4];      // V rows of the four row blocks, k block 32*vk .. +31 (contiguous order)
+};
+
+__device__ __forceinline__ void load_values(ValueFrags& L, const Seq& sq, int c, int vk, int l) {
+  const int g = l >> 4, c16 = l & 15;
+#pragma unroll
+  for (int sb = 0; sb < 4; ++sb) {
+    int tok = c * kC + 16 * sb + c16;
+    tok = tok < sq.T ? tok : sq.T - 1;
+    L.v[sb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(sq.V + int64_t(tok) * kD + 32 * vk + 8 * g));
+  }
+}
+
+// kRole: 0 for wave f0, 1 for f1, 2 for f2 and f3 (fw tells them apart).
+template <int kRole>
+__device__ bool factor_chunk(Smem& sm, ValueFrags& VF, const Seq& sq, int c, int fw, int l,
                              float eps, float eps_gamma, bool fresh, int nchunks) {
   const int g = l >> 4, c16 = l & 15;
   const int t0 = c * kC;
+  const InputEntry& E = sm.in[c % kNI];
   Slot& S = sm.slot[c % kNS];
-  FactorPrivate& P = sm.fp[fw];
+  uint16_t* tb = sm.tb[c & 1];
+  Gates& G = sm.gates[fw];
+  if (!wait_at_least(&sm.in_ready[c % kNI], 2 * (c / kNI + 1), &sm.abort_flag)) return false;
 
-  // ---- a1: energies, step sizes, chunk-local log decays -------------------
+  // ---- a1: energies, step sizes, chunk-local log decays (every wave) -------
+  bf16x8 xf[4][2];
+#pragma unroll
+  for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+    for (int m = 0; m < 2; ++m) xf[ib][m] = ring_frag_c(E.x, 16 * ib + c16, m, g);
   float part[4];
 #pragma unroll
   for (int ib = 0; ib < 4; ++ib) {
@@ -258,7 +327,7 @@ __device__ void factor_chunk(Smem& sm, FactorLoads& L, const Seq& sq, int c, int
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const float xv = static_cast<float>(L.x[ib][m][k]);
+        const float xv = static_cast<float>(xf[ib][m][k]);
         e = fmaf(xv, xv, e);
       }
     part[ib] = e;
@@ -268,14 +337,15 @@ __device__ void factor_chunk(Smem& sm, FactorLoads& L, const Seq& sq, int c, int
 #pragma unroll
   for (int ib = 0; ib < 4; ++ib) part[ib] += __shfl_xor(part[ib], 32);
   const float energy = g == 0 ? part[0] : g == 1 ? part[1] : g == 2 ? part[2] : part[3];
-  const int tok = t0 + l;                                  // this lane's row is l
+  const int tok = t0 + l;                                    // this lane's row is l
   float eta = 0.f, lg = 0.f;
   if (tok < sq.T) {
-    eta = nlms_eta(L.beta, energy, L.lam, eps, fresh && tok == 0);
-    lg = clamped_log_gamma(eta, L.lam, eps_gamma);
+    const float bt = E.beta[l], lt = E.lam[l];
+    eta = nlms_eta(bt, energy, lt, eps, fresh && tok == 0);
+    lg = clamped_log_gamma(eta, lt, eps_gamma);
   }
-  // inclusive prefix over the 64 rows: within 16-lane rows by DPP shifts,
-  // then the row totals carried across rows
+  // inclusive prefix over the 64 rows: DPP shifts within 16-lane rows, then
+  // the row totals carried across rows
   float gi = lg;
   gi += row_shr<1>(gi);
   gi += row_shr<2>(gi);
@@ -286,258 +356,269 @@ __device__ void factor_chunk(Smem& sm, FactorLoads& L, const Seq& sq, int c, int
     gi += (g >= 1 ? r0 : 0.0f) + (g >= 2 ? r1 : 0.0f) + (g >= 3 ? r2 : 0.0f);
   }
   float gprev = row_shr<1>(gi);
-  if (c16 == 0) {
+  {
     const float e15 = lane_value(gi, 15), e31 = lane_value(gi, 31), e47 = lane_value(gi, 47);
-    gprev = g == 0 ? 0.0f : g == 1 ? e15 : g == 2 ? e31 : e47;
+    if (c16 == 0) gprev = g == 0 ? 0.0f : g == 1 ? e15 : g == 2 ? e31 : e47;
   }
   const float glast = lane_value(gi, 63);
+  G.graw[l] = gi;
+  G.sxg[l] = eta * __expf(gprev);
+  G.sxh[l] = __expf(glast - gi);
+  G.eta[l] = eta;
+  G.eta_t[c16 * 4 + g] = eta;
+  G.gprev_t[c16 * 4 + g] = gprev;
+  G.graw_t[c16 * 4 + g] = gi;
 
-  // Gates in the orders the lanes read them back.
-  P.graw[l] = gi;
-  P.sxg[l] = eta * __expf(gprev);
-  P.sxh[l] = __expf(glast - gi);
-  P.eta_t[c16 * 4 + g] = eta;
-  P.gprev_t[c16 * 4 + g] = gprev;
-  P.graw_t[c16 * 4 + g] = gi;
-  // i-role values (i = 16 ib + c16) and s-role values (s = 16 sb + 4 g + r)
-  const f32x4 eta_i = ld4(&P.eta_t[c16 * 4]);
-  const f32x4 gpv_i = ld4(&P.gprev_t[c16 * 4]);
-  const f32x4 gra_i = ld4(&P.graw_t[c16 * 4]);
-  f32x4 gs_s[4];
+  if constexpr (kRole == 0) {
+    // ---- decayed Gram: A^T tile (sb, ib) = X_sb X_ib^T, scaled ------------
+    const f32x4 eta_i = ld4(&G.eta_t[c16 * 4]);
+    const f32x4 gpv_i = ld4(&G.gprev_t[c16 * 4]);
+    f32x4 gs_s[4];                                           // g_s for s = 16 sb + 4 g + r
 #pragma unroll
-  for (int sb = 0; sb < 4; ++sb) gs_s[sb] = ld4(&P.graw[16 * sb + 4 * g]);
+    for (int sb = 0; sb < 4; ++sb) gs_s[sb] = ld4(&G.graw[16 * sb + 4 * g]);
+    s16x4 a10, a32;      // A blocks (1,0) and (3,2) as K=16 A fragments
+    bf16x8 a2lo, a3lo;   // A rows 32-47 / 48-63, columns 0-31, as K=32 A fragments
+    {
+      f32x4 a_off[6];
+#pragma unroll
+      for (int n = 0; n < 10; ++n) {
+        int ib, sb;
+        lower_tile(n, ib, sb);
+        f32x4 acc = mfma32(xf[sb][0], xf[ib][0], zero4());
+        acc = mfma32(xf[sb][1], xf[ib][1], acc);
+        const int i = 16 * ib + c16;
+        f32x4 a;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int s_ = 16 * sb + 4 * g + r;
+          a[r] = s_ < i ? eta_i[ib] * __expf(gpv_i[ib] - gs_s[sb][r]) * acc[r] : 0.0f;
+        }
+        if (ib == sb) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sm.abt[ib][4 * g + r][c16] = a[r];
+        } else {
+          a_off[n - ib] = a;     // n - ib enumerates the off-diagonal tiles in order
+        }
+      }
+      a10 = s16_acc(a_off[0]);
+      a32 = s16_acc(a_off[5]);
+      a2lo = frag_acc(a_off[1], a_off[2]);
+      a3lo = frag_acc(a_off[3], a_off[4]);
+    }
+    // ---- T = (I + A)^{-1}: diagonal blocks by column elimination ----------
+    float t[16];
+    {
+      float col[16];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 v = ld4(&sm.abt[g][c16][4 * q4]);        // A[16g+i][16g+c16], all i
+        col[4 * q4] = v[0]; col[4 * q4 + 1] = v[1]; col[4 * q4 + 2] = v[2]; col[4 * q4 + 3] = v[3];
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) t[i] = (i == c16) ? 1.0f : 0.0f;
+      eliminate<0>(t, col);
+    }
+    // tb[c & 1] held T of chunk c - 2: wait until f1..f3 are done with it.
+    if (!wait_at_least(&sm.t_used[c & 1], 3 * (c / 2), &sm.abort_flag)) return false;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tb[(16 * g + i) * kP + 16 * g + c16] = bf(t[i]);
+    // ---- off-diagonal 16x16 blocks: T_hl = -T_hh A_hl T_ll for (1,0), (3,2)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int lo = 2 * p, hi = 2 * p + 1;
+      s16x4 tl;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tl[e] = static_cast<short>(tb[(16 * lo + 4 * g + e) * kP + 16 * lo + c16]);
+      const f32x4 y = mfma16(p == 0 ? a10 : a32, tl, zero4());
+      const s16x4 th = __builtin_bit_cast(
+          s16x4, *reinterpret_cast<const uint2*>(&tb[(16 * hi + c16) * kP + 16 * hi + 4 * g]));
+      const f32x4 z = mfma16(th, s16_acc(y), zero4());
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tb[(16 * hi + 4 * g + r) * kP + 16 * lo + c16] = bf(-z[r]);
+    }
+    // ---- lower-left 32x32 block: T_21 = -T_22 A_21 T_11 (2x2 block sense) --
+    {
+      bf16x8 tlo[2];
+#pragma unroll
+      for (int cj = 0; cj < 2; ++cj)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          tlo[cj][e] = __builtin_bit_cast(__bf16, tb[kperm(g, e) * kP + 16 * cj + c16]);
+      const bf16x8 th2 = frag_lds(&tb[(32 + c16) * kP], 32, g);
+      const bf16x8 th3 = frag_lds(&tb[(48 + c16) * kP], 32, g);
+#pragma unroll
+      for (int cj = 0; cj < 2; ++cj) {
+        const bf16x8 yb = frag_acc(mfma32(a2lo, tlo[cj], zero4()), mfma32(a3lo, tlo[cj], zero4()));
+        const f32x4 z2 = mfma32(th2, yb, zero4());
+        const f32x4 z3 = mfma32(th3, yb, zero4());
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          tb[(32 + 4 * g + r) * kP + 16 * cj + c16] = bf(-z2[r]);
+          tb[(48 + 4 * g + r) * kP + 16 * cj + c16] = bf(-z3[r]);
+        }
+      }
+    }
+    if (l == 0) __hip_atomic_store(&sm.t_ready[c & 1], c + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    // the chain reads the output scales from the slot
+    if (!wait_at_least(&sm.slot_free[c % kNS], 2 * (c / kNS), &sm.abort_flag)) return false;
+    S.gexp_t[c16 * 4 + g] = __expf(gi);
+    if (l == 0) S.glast[0] = __expf(glast);
+    signal_add(&sm.slot_full[c % kNS], l);
+    return true;
+  }
 
-  // ---- decayed Gram: A^T tile (sb, ib) = X_sb X_ib^T, scaled --------------
-  // lane holds A[16ib+c16][16sb+4g+r]; diagonal tiles go to LDS for the
-  // elimination, off-diagonal tiles stay in registers as MFMA operands.
-  s16x4 a10, a32;        // A blocks (1,0) and (3,2) as K=16 A fragments
-  bf16x8 a2lo, a3lo;     // A rows 32-47 / 48-63, columns 0-31, as K=32 A fragments
-  {
-    f32x4 a_off[6];
-#pragma unroll
-    for (int n = 0; n < 10; ++n) {
+  // ---- waves f1..f3 ---------------------------------------------------------
+  // Work split: f1: mask tiles with ib >= 2, key transposes fb 0..1, W fb 0..1;
+  // f2: mask tiles with ib < 2, key transposes fb 2, values cb 0..1, W fb 2;
+  // f3: key transposes fb 3, values cb 2..3, W fb 3.
+  const int fb0 = kRole == 1 ? 0 : fw;                          // first key block: 0, 2, 3
+  constexpr int nfb = kRole == 1 ? 2 : 1;
+  const int n0 = kRole == 1 ? 3 : 0, n1 = kRole == 1 ? 10 : fw == 2 ? 3 : 0;   // mask tiles [n0, n1)
+  if (!wait_at_least(&sm.slot_free[c % kNS], 2 * (c / kNS), &sm.abort_flag)) return false;
+
+  // ---- decayed read mask: M^T tile (sb, ib) = X_sb Q_ib^T -----------------
+  if (n1 > n0) {
+    const f32x4 gra_i = ld4(&G.graw_t[c16 * 4]);
+    for (int n = n0; n < n1; ++n) {
       int ib, sb;
       lower_tile(n, ib, sb);
-      f32x4 acc = mfma32(L.x[sb][0], L.x[ib][0], zero4());
-      acc = mfma32(L.x[sb][1], L.x[ib][1], acc);
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+        acc = mfma32(ring_frag_c(E.x, 16 * sb + c16, m, g), ring_frag_c(E.q, 16 * ib + c16, m, g), acc);
       const int i = 16 * ib + c16;
-      f32x4 a;
+      const f32x4 gs = ld4(&G.graw[16 * sb + 4 * g]);
+      const float gi_ib = ib == 0 ? gra_i[0] : ib == 1 ? gra_i[1] : ib == 2 ? gra_i[2] : gra_i[3];
+      f32x4 mv;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int s_ = 16 * sb + 4 * g + r;
-        a[r] = s_ < i ? eta_i[ib] * __expf(gpv_i[ib] - gs_s[sb][r]) * acc[r] : 0.0f;
+        mv[r] = s_ <= i ? __expf(gi_ib - gs[r]) * acc[r] : 0.0f;
       }
-      if (ib == sb) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) P.abt[ib][4 * g + r][c16] = a[r];
-      } else {
-        a_off[n - ib] = a;       // n - ib enumerates the off-diagonal tiles in order
-      }
-    }
-    a10 = s16_acc(a_off[0]);
-    a32 = s16_acc(a_off[5]);
-    a2lo = frag_acc(a_off[1], a_off[2]);
-    a3lo = frag_acc(a_off[3], a_off[4]);
-  }
-  // ---- T = (I + A)^{-1}: diagonal blocks by column elimination -----------
-  float t[16];
-  {
-    const int b = g, j = c16;
-    float col[16];
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const f32x4 v = ld4(&P.abt[b][j][4 * q4]);          // A[16b+i][16b+j], all i
-      col[4 * q4] = v[0]; col[4 * q4 + 1] = v[1]; col[4 * q4 + 2] = v[2]; col[4 * q4 + 3] = v[3];
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) t[i] = (i == j) ? 1.0f : 0.0f;
-    eliminate<0>(t, col);
-  }
-
-  // The slot may still be read by the chain for chunk c - kNS.
-  if (!wait_at_least(&sm.consumed[c % kNS], 4 * (c / kNS), &sm.abort_flag)) return;
-
-#pragma unroll
-  for (int i = 0; i < 16; ++i) S.tb[(16 * g + i) * kP + 16 * g + c16] = bf(t[i]);
-  S.eta[l] = eta;
-  S.gexp_t[c16 * 4 + g] = __expf(gi);
-  if (l == 0) S.glast[0] = __expf(glast);
-
-  // ---- off-diagonal 16x16 blocks: T_hl = -T_hh A_hl T_ll for (1,0), (3,2)
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int lo = 2 * p, hi = 2 * p + 1;
-    s16x4 tl;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) tl[e] = static_cast<short>(S.tb[(16 * lo + 4 * g + e) * kP + 16 * lo + c16]);
-    const f32x4 y = mfma16(p == 0 ? a10 : a32, tl, zero4());
-    const s16x4 th = __builtin_bit_cast(
-        s16x4, *reinterpret_cast<const uint2*>(&S.tb[(16 * hi + c16) * kP + 16 * hi + 4 * g]));
-    const f32x4 z = mfma16(th, s16_acc(y), zero4());
-#pragma unroll
-    for (int r = 0; r < 4; ++r) S.tb[(16 * hi + 4 * g + r) * kP + 16 * lo + c16] = bf(-z[r]);
-  }
-  // ---- lower-left 32x32 block: T_21 = -T_22 A_21 T_11 (2x2 block sense) --
-  {
-    bf16x8 tlo[2];
-#pragma unroll
-    for (int cj = 0; cj < 2; ++cj)
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        tlo[cj][e] = __builtin_bit_cast(__bf16, S.tb[kperm(g, e) * kP + 16 * cj + c16]);
-    const bf16x8 th2 = frag_lds(&S.tb[(32 + c16) * kP], 32, g);
-    const bf16x8 th3 = frag_lds(&S.tb[(48 + c16) * kP], 32, g);
-#pragma unroll
-    for (int cj = 0; cj < 2; ++cj) {
-      const f32x4 y2 = mfma32(a2lo, tlo[cj], zero4());     // rows 32-47
-      const f32x4 y3 = mfma32(a3lo, tlo[cj], zero4());     // rows 48-63
-      const bf16x8 yb = frag_acc(y2, y3);
-      const f32x4 z2 = mfma32(th2, yb, zero4());
-      const f32x4 z3 = mfma32(th3, yb, zero4());
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        S.tb[(32 + 4 * g + r) * kP + 16 * cj + c16] = bf(-z2[r]);
-        S.tb[(48 + 4 * g + r) * kP + 16 * cj + c16] = bf(-z3[r]);
-      }
+      store_half(&S.mf[((ib * 2 + (sb >> 1)) * 64 + l) * 8 + 4 * (sb & 1)], mv);
     }
   }
-  // ---- decayed read mask: M^T tile (sb, ib) = X_sb Q_ib^T ----------------
-#pragma unroll
-  for (int n = 0; n < 10; ++n) {
-    int ib, sb;
-    lower_tile(n, ib, sb);
-    f32x4 acc = mfma32(L.x[sb][0], L.q[ib][0], zero4());
-    acc = mfma32(L.x[sb][1], L.q[ib][1], acc);
-    const int i = 16 * ib + c16;
-    f32x4 mv;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int s_ = 16 * sb + 4 * g + r;
-      mv[r] = s_ <= i ? __expf(gra_i[ib] - gs_s[sb][r]) * acc[r] : 0.0f;
-    }
-    store_half(&S.mf[((ib * 2 + (sb >> 1)) * 64 + l) * 8 + 4 * (sb & 1)], mv);
-  }
-
-  // ---- decayed key transposes on the matrix cores ------------------------
+  // ---- decayed key transposes on the matrix cores --------------------------
   // D(sb, fb) = X_sb I_fb; lane holds X[16sb+4g+r][16fb+c16].
-  bf16x8 xg[4][2];                                         // (Diag(eta e^{g_{s-1}}) X)^T
+  bf16x8 xg[2][2];                                           // (Diag(eta e^{g_{s-1}}) X)^T
   {
     f32x4 sxg_s[4], sxh_s[4];
 #pragma unroll
     for (int sb = 0; sb < 4; ++sb) {
-      sxg_s[sb] = ld4(&P.sxg[16 * sb + 4 * g]);
-      sxh_s[sb] = ld4(&P.sxh[16 * sb + 4 * g]);
+      sxg_s[sb] = ld4(&G.sxg[16 * sb + 4 * g]);
+      sxh_s[sb] = ld4(&G.sxh[16 * sb + 4 * g]);
     }
-    const bf16x8 id0 = identity_frag(0, g, c16), id1 = identity_frag(1, g, c16);
 #pragma unroll
-    for (int fb = 0; fb < 4; ++fb) {
+    for (int k = 0; k < 2; ++k) {
+      if (k < nfb) {
+        const int fb = fb0 + k;
+        constexpr int mk = kRole == 1 ? 0 : 1;                // fb >> 1, known per role
+        const bf16x8 sel = select_frag(fb & 1, g, c16);
+        f32x4 d[4];
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb) d[sb] = mfma32(xf[sb][mk], sel, zero4());
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          xg[k][m] = frag_acc(d[2 * m] * sxg_s[2 * m], d[2 * m + 1] * sxg_s[2 * m + 1]);
+          store_frag(&S.xh[((fb * 2 + m) * 64 + l) * 8],
+                     frag_acc(d[2 * m] * sxh_s[2 * m], d[2 * m + 1] * sxh_s[2 * m + 1]));
+        }
+      }
+    }
+  }
+  // ---- value transposes (waves f2, f3): Diag(eta) V for two column blocks --
+  bf16x8 vt[2][2];                                           // [cb][m]
+  if constexpr (kRole == 2) {
+    f32x4 eta_s[4];
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) eta_s[sb] = ld4(&G.eta[16 * sb + 4 * g]);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const bf16x8 sel = select_frag(k, g, c16);
       f32x4 d[4];
 #pragma unroll
-      for (int sb = 0; sb < 4; ++sb)
-        d[sb] = mfma32(L.x[sb][fb >> 1], (fb & 1) ? id1 : id0, zero4());
+      for (int sb = 0; sb < 4; ++sb) d[sb] = mfma32(VF.v[sb], sel, zero4());
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        xg[fb][m] = frag_acc(d[2 * m] * sxg_s[2 * m], d[2 * m + 1] * sxg_s[2 * m + 1]);
-        store_frag(&S.xh[((fb * 2 + m) * 64 + l) * 8],
-                   frag_acc(d[2 * m] * sxh_s[2 * m], d[2 * m + 1] * sxh_s[2 * m + 1]));
-      }
+      for (int m = 0; m < 2; ++m) vt[k][m] = frag_acc(d[2 * m] * eta_s[2 * m], d[2 * m + 1] * eta_s[2 * m + 1]);
     }
+    // this wave's next chunk is c + 1
+    if (c + 1 < nchunks) load_values(VF, sq, c + 1, fw - 2, l);
   }
-  // The chunk's rows are no longer needed: prefetch this wave's next chunk.
-  if (c + kNF < nchunks) factor_load(L, sq, c + kNF, l);
-
-  // ---- W^T tiles (fb, ib) = (Diag(eta e^{g_{s-1}}) X)^T T^T; store -W ----
-  {
-    bf16x8 tf[4][2];
+  // ---- wait for T, then W^T tiles (fb, ib) = X~^T T^T and U = T V~ ---------
+  if (!wait_at_least(&sm.t_ready[c & 1], c + 1, &sm.abort_flag)) return false;
+  bf16x8 tf[4][2];
 #pragma unroll
-    for (int ib = 0; ib < 4; ++ib) {
-      tf[ib][0] = frag_lds(&S.tb[(16 * ib + c16) * kP], 0, g);
-      tf[ib][1] = frag_lds(&S.tb[(16 * ib + c16) * kP], 32, g);
-    }
+  for (int ib = 0; ib < 4; ++ib) {
+    tf[ib][0] = frag_lds(&tb[(16 * ib + c16) * kP], 0, g);
+    tf[ib][1] = frag_lds(&tb[(16 * ib + c16) * kP], 32, g);
+  }
+  signal_add(&sm.t_used[c & 1], l);
 #pragma unroll
-    for (int ib = 0; ib < 4; ++ib)
+  for (int k = 0; k < 2; ++k) {
+    if (k < nfb) {
+      const int fb = fb0 + k;
 #pragma unroll
-      for (int fb = 0; fb < 4; ++fb) {
-        f32x4 acc = mfma32(xg[fb][0], tf[ib][0], zero4());
-        if (ib >= 2) acc = mfma32(xg[fb][1], tf[ib][1], acc);  // T is lower triangular
+      for (int ib = 0; ib < 4; ++ib) {
+        f32x4 acc = mfma32(xg[k][0], tf[ib][0], zero4());
+        if (ib >= 2) acc = mfma32(xg[k][1], tf[ib][1], acc);   // T is lower triangular
         store_half(&S.wf[((ib * 2 + (fb >> 1)) * 64 + l) * 8 + 4 * (fb & 1)], -acc);
       }
+    }
   }
-  if (l == 0) __hip_atomic_store(&sm.full[c % kNS], c, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  if constexpr (kRole == 2) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int cb = 2 * (fw - 2) + k;
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib) {
+        f32x4 u = mfma32(tf[ib][0], vt[k][0], zero4());
+        if (ib >= 2) u = mfma32(tf[ib][1], vt[k][1], u);
+        store_half(&S.uf[((ib * 4 + cb) * 64 + l) * 4], u);
+      }
+    }
+  }
+  signal_add(&sm.slot_full[c % kNS], l);
+  return true;
 }
 
 // ---------------------------------------------------------------------------
-// Chain wave: consumes the slot of chunk c for value columns 16w..16w+15.
+// Chain wave w: consumes chunk c for value columns 32w..32w+31.
 // ---------------------------------------------------------------------------
-struct ChainLoads {
-  bf16x8 v[4];      // V rows of the four row blocks, k block covering columns 16w..
-  bf16x8 q[4][2];   // Q rows, fragments [row block][k step]
-};
-
-__device__ __forceinline__ void chain_load_v(ChainLoads& L, const Seq& sq, int c, int w, int l) {
-  const int g = l >> 4, c16 = l & 15;
-#pragma unroll
-  for (int sb = 0; sb < 4; ++sb) {
-    const int tok = c * kC + 16 * sb + c16;
-    L.v[sb] = frag_global(sq.V + int64_t(tok) * kD, 32 * (w >> 1), g, tok < sq.T);
-  }
-}
-__device__ __forceinline__ void chain_load_q(ChainLoads& L, const Seq& sq, int c, int l) {
-  const int g = l >> 4, c16 = l & 15;
-#pragma unroll
-  for (int ib = 0; ib < 4; ++ib) {
-    const int tok = c * kC + 16 * ib + c16;
-#pragma unroll
-    for (int m = 0; m < 2; ++m) L.q[ib][m] = frag_global(sq.Q + int64_t(tok) * kD, 32 * m, g, tok < sq.T);
-  }
-}
-
-__device__ bool chain_chunk(Smem& sm, ChainLoads& L, f32x4 (&Sst)[4], const Seq& sq, int c, int w,
-                            int l, bf16_t* o_bh, int nchunks) {
+__device__ bool chain_chunk(Smem& sm, f32x4 (&Sst)[4][2], const Seq& sq, int c, int w, int l,
+                            bf16_t* o_bh, int nchunks) {
   const int g = l >> 4, c16 = l & 15;
   const int t0 = c * kC;
-  if (!wait_at_least(&sm.full[c % kNS], c, &sm.abort_flag)) return false;
+  // ---- stream the entry of chunk c + 2 (it held chunk c - 1; both chain
+  // waves must be done with it)
+  if (c + 2 < nchunks) {
+    const int e = (c + 2) % kNI;
+    if (!wait_at_least(&sm.in_free[e], 2 * ((c + 2) / kNI), &sm.abort_flag)) return false;
+    ring_load(sm.in[e], sq, c + 2, w, l);
+  }
+  if (!wait_at_least(&sm.slot_full[c % kNS], kFactor * (c / kNS + 1), &sm.abort_flag)) return false;
   const Slot& S = sm.slot[c % kNS];
+  const InputEntry& E = sm.in[c % kNI];
 
-  // ---- wait done; first batch of slot reads: T rows, eta and -W fragments.
-  bf16x8 tf[4][2], wfr[4][2];
-  f32x4 eta_s[4];
+  // ---- slot reads: U tiles and -W fragments, then R = U - W S --------------
+  f32x4 R[4][2];
+  bf16x8 sb[2][2];                                           // S fragments [cb][m]
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    sb[k][0] = frag_acc(Sst[0][k], Sst[1][k]);
+    sb[k][1] = frag_acc(Sst[2][k], Sst[3][k]);
+  }
 #pragma unroll
   for (int ib = 0; ib < 4; ++ib) {
-    tf[ib][0] = frag_lds(&S.tb[(16 * ib + c16) * kP], 0, g);
-    if (ib >= 2) tf[ib][1] = frag_lds(&S.tb[(16 * ib + c16) * kP], 32, g);
+    const bf16x8 w0 = load_frag(&S.wf[((ib * 2 + 0) * 64 + l) * 8]);
+    const bf16x8 w1 = load_frag(&S.wf[((ib * 2 + 1) * 64 + l) * 8]);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      f32x4 u = load_half(&S.uf[((ib * 4 + 2 * w + k) * 64 + l) * 4]);
+      u = mfma32(w0, sb[k][0], u);
+      R[ib][k] = mfma32(w1, sb[k][1], u);
+    }
   }
-#pragma unroll
-  for (int sb = 0; sb < 4; ++sb) eta_s[sb] = ld4(&S.eta[16 * sb + 4 * g]);
-#pragma unroll
-  for (int ib = 0; ib < 4; ++ib)
-#pragma unroll
-    for (int m = 0; m < 2; ++m) wfr[ib][m] = load_frag(&S.wf[((ib * 2 + m) * 64 + l) * 8]);
-
-  // ---- U = T Diag(eta) V for columns 16w..: transpose the V tile on the matrix
-  // cores, scale rows by eta_s, then contract over tokens.
-  bf16x8 vt[2];
-  {
-    const bf16x8 id = identity_frag(w & 1, g, c16);
-    f32x4 d[4];
-#pragma unroll
-    for (int sb = 0; sb < 4; ++sb) d[sb] = mfma32(L.v[sb], id, zero4());
-#pragma unroll
-    for (int m = 0; m < 2; ++m) vt[m] = frag_acc(d[2 * m] * eta_s[2 * m], d[2 * m + 1] * eta_s[2 * m + 1]);
-  }
-  if (c + 1 < nchunks) chain_load_v(L, sq, c + 1, w, l);
-  // ---- R = U - W S (rows eta_i r_i of this column block)
-  const bf16x8 sb0 = frag_acc(Sst[0], Sst[1]);
-  const bf16x8 sb1 = frag_acc(Sst[2], Sst[3]);
-  f32x4 R[4];
-#pragma unroll
-  for (int ib = 0; ib < 4; ++ib) {
-    f32x4 u = mfma32(tf[ib][0], vt[0], zero4());
-    if (ib >= 2) u = mfma32(tf[ib][1], vt[1], u);
-    u = mfma32(wfr[ib][0], sb0, u);
-    R[ib] = mfma32(wfr[ib][1], sb1, u);
-  }
-  // ---- second batch: mask and decayed-key fragments, output and decay scales.
+  // ---- slot reads: mask and decayed-key fragments, output and decay scales --
   bf16x8 mfr[4][2], xhr[4][2];
 #pragma unroll
   for (int ib = 0; ib < 4; ++ib) {
@@ -550,34 +631,44 @@ __device__ bool chain_chunk(Smem& sm, ChainLoads& L, f32x4 (&Sst)[4], const Seq&
     for (int m = 0; m < 2; ++m) xhr[fb][m] = load_frag(&S.xh[((fb * 2 + m) * 64 + l) * 8]);
   const f32x4 gexp_i = ld4(&S.gexp_t[c16 * 4]);
   const float glast = S.glast[0];
-  // All slot data is in registers: hand the slot back to the factor waves.
-  if (l == 0) __hip_atomic_fetch_add(&sm.consumed[c % kNS], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  signal_add(&sm.slot_free[c % kNS], l);                     // slot contents are in registers
 
-  const bf16x8 rb0 = frag_acc(R[0], R[1]);
-  const bf16x8 rb1 = frag_acc(R[2], R[3]);
-  // ---- O^T tiles: e^{g_i} S^T Q^T + R^T M^T; lane holds o[t0+16ib+c16][16w+4g+r].
+  bf16x8 rb[2][2];                                           // R fragments [cb][m]
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    rb[k][0] = frag_acc(R[0][k], R[1][k]);
+    rb[k][1] = frag_acc(R[2][k], R[3][k]);
+  }
+  // ---- O^T tiles: e^{g_i} S^T Q^T + R^T M^T; lane holds o[t0+16ib+c16][32w+16k+4g+r]
 #pragma unroll
   for (int ib = 0; ib < 4; ++ib) {
-    f32x4 acc = mfma32(sb0, L.q[ib][0], zero4());
-    acc = mfma32(sb1, L.q[ib][1], acc);
-    acc = acc * gexp_i[ib];
-    acc = mfma32(rb0, mfr[ib][0], acc);
-    if (ib >= 2) acc = mfma32(rb1, mfr[ib][1], acc);
-    const int tok = t0 + 16 * ib + c16;
-    if (tok < sq.T) {
-      const uint32_t p0 = uint32_t(bf(acc[0])) | (uint32_t(bf(acc[1])) << 16);
-      const uint32_t p1 = uint32_t(bf(acc[2])) | (uint32_t(bf(acc[3])) << 16);
-      *reinterpret_cast<uint2*>(o_bh + int64_t(tok) * kD + 16 * w + 4 * g) = make_uint2(p0, p1);
+    const int i = 16 * ib + c16;
+    const bf16x8 q0 = ring_frag_p(E.q, i, 0, g), q1 = ring_frag_p(E.q, i, 1, g);
+    const int tok = t0 + i;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      f32x4 acc = mfma32(sb[k][0], q0, zero4());
+      acc = mfma32(sb[k][1], q1, acc);
+      acc = acc * gexp_i[ib];
+      acc = mfma32(rb[k][0], mfr[ib][0], acc);
+      if (ib >= 2) acc = mfma32(rb[k][1], mfr[ib][1], acc);
+      if (tok < sq.T) {
+        const uint32_t p0 = uint32_t(bf(acc[0])) | (uint32_t(bf(acc[1])) << 16);
+        const uint32_t p1 = uint32_t(bf(acc[2])) | (uint32_t(bf(acc[3])) << 16);
+        *reinterpret_cast<uint2*>(o_bh + int64_t(tok) * kD + 32 * w + 16 * k + 4 * g) = make_uint2(p0, p1);
+      }
     }
   }
-  if (c + 1 < nchunks) chain_load_q(L, sq, c + 1, l);
-  // ---- S <- e^{g_63} S + (Diag(e^{g_63-g}) X)^T R
+  signal_add(&sm.in_free[c % kNI], l);                       // done with the queries of chunk c
+  // ---- S <- e^{g_63} S + (Diag(e^{g_63-g}) X)^T R ---------------------------
 #pragma unroll
-  for (int fb = 0; fb < 4; ++fb) {
-    f32x4 acc = Sst[fb] * glast;
-    acc = mfma32(xhr[fb][0], rb0, acc);
-    Sst[fb] = mfma32(xhr[fb][1], rb1, acc);
-  }
+  for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      f32x4 acc = Sst[fb][k] * glast;
+      acc = mfma32(xhr[fb][0], rb[k][0], acc);
+      Sst[fb][k] = mfma32(xhr[fb][1], rb[k][1], acc);
+    }
   return true;
 }
 
@@ -605,45 +696,60 @@ falcon1_chunked_mfma_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __re
 
   // T's upper blocks and the structurally-zero halves of the mask fragments
   // are never written afterwards and stay zero.
-  for (int s = 0; s < kNS; ++s) {
-    for (int e = tid; e < kC * kP; e += kThreads) sm.slot[s].tb[e] = 0;
+  for (int e = tid; e < 2 * kC * kP; e += kThreads) sm.tb[e / (kC * kP)][e % (kC * kP)] = 0;
+  for (int s = 0; s < kNS; ++s)
     for (int e = tid; e < 4 * 2 * 64 * 8; e += kThreads) sm.slot[s].mf[e] = 0;
-  }
-  if (tid < kNS) {
-    sm.full[tid] = -1;
-    sm.consumed[tid] = 0;
-  }
+  if (tid < kNI) { sm.in_ready[tid] = 0; sm.in_free[tid] = 0; }
+  if (tid < kNS) { sm.slot_full[tid] = 0; sm.slot_free[tid] = 0; }
+  if (tid < 2) { sm.t_ready[tid] = 0; sm.t_used[tid] = 0; }
   if (tid == 0) sm.abort_flag = 0;
   __syncthreads();
 
-  if (wave < 4) {
+  if (wave < kChain) {
     const int w = wave;
-    f32x4 Sst[4];
+    // prologue: the first two ring entries
+    for (int c = 0; c < 2 && c < nchunks; ++c) ring_load(sm.in[c], sq, c, w, l);
+    __builtin_amdgcn_s_waitcnt(0);                          // this wave's loads have landed
+    for (int c = 0; c < 2 && c < nchunks; ++c) signal_add(&sm.in_ready[c], l);
+
+    f32x4 Sst[4][2];
 #pragma unroll
     for (int fb = 0; fb < 4; ++fb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        Sst[fb][r] = S0 ? S0[(bh * kD + 16 * fb + 4 * g + r) * kD + 16 * w + c16] : 0.0f;
-    ChainLoads L;
-    chain_load_v(L, sq, 0, w, l);
-    chain_load_q(L, sq, 0, l);
-    for (int c = 0; c < nchunks; ++c)
-      if (!chain_chunk(sm, L, Sst, sq, c, w, l, o + bh * T * kD, nchunks)) break;
+      for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          Sst[fb][k][r] = S0 ? S0[(bh * kD + 16 * fb + 4 * g + r) * kD + 32 * w + 16 * k + c16] : 0.0f;
+    for (int c = 0; c < nchunks; ++c) {
+      if (!chain_chunk(sm, Sst, sq, c, w, l, o + bh * T * kD, nchunks)) break;
+      if (c + 2 < nchunks) {
+        __builtin_amdgcn_s_waitcnt(0);                      // this wave's ring loads have landed
+        signal_add(&sm.in_ready[(c + 2) % kNI], l);
+      }
+    }
     if (S_T) {
 #pragma unroll
       for (int fb = 0; fb < 4; ++fb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          S_T[(bh * kD + 16 * fb + 4 * g + r) * kD + 16 * w + c16] = Sst[fb][r];
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            S_T[(bh * kD + 16 * fb + 4 * g + r) * kD + 32 * w + 16 * k + c16] = Sst[fb][k][r];
     }
   } else {
-    const int fw = wave - 4;
+    const int fw = wave - kChain;
     const bool fresh = (k_prev == nullptr);
-    FactorLoads L;
-    if (fw < nchunks) factor_load(L, sq, fw, l);
-    for (int c = fw; c < nchunks; c += kNF) {
-      factor_chunk(sm, L, sq, c, fw, l, eps, eps_gamma, fresh, nchunks);
-      if (__hip_atomic_load(&sm.abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) break;
+    ValueFrags VF;
+    if (fw == 0) {
+      for (int c = 0; c < nchunks; ++c)
+        if (!factor_chunk<0>(sm, VF, sq, c, fw, l, eps, eps_gamma, fresh, nchunks)) break;
+    } else if (fw == 1) {
+      for (int c = 0; c < nchunks; ++c)
+        if (!factor_chunk<1>(sm, VF, sq, c, fw, l, eps, eps_gamma, fresh, nchunks)) break;
+    } else {
+      load_values(VF, sq, 0, fw - 2, l);
+      for (int c = 0; c < nchunks; ++c)
+        if (!factor_chunk<2>(sm, VF, sq, c, fw, l, eps, eps_gamma, fresh, nchunks)) break;
     }
   }
 }
