@@ -55,9 +55,9 @@ namespace falcon {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kC = 64;            // chunk length
 constexpr int kD = 64;            // dk = dv
@@ -67,16 +67,31 @@ constexpr int kNS = 2;            // factor slots
 constexpr int kChain = 2;         // chain waves
 constexpr int kFactor = 4;        // factor waves
 constexpr int kThreads = 64 * (kChain + kFactor);
+constexpr int kSlotWriters = 3;    // factor waves f1..f3 fill a slot
 constexpr int kSpinLimit = 1 << 22;
 
-// Rows of one chunk as loaded from HBM: 64 rows of 128 bytes, the 16-byte
+// Gates of one chunk (a1), in the orders their readers want them.  "_t"
+// arrays hold row i = 16 ib + c16 at [c16 * 4 + ib], so that one 16-byte read
+// gives a lane the values of its column c16 in all four row blocks.
+struct ChunkGates {
+  float graw[kC];                 // g_s, token order
+  float sxg[kC];                  // eta_s e^{g_{s-1}}
+  float sxh[kC];                  // e^{g_63 - g_s}
+  float eta[kC];                  // eta_s
+  float eta_t[kC];                // eta_i
+  float gprev_t[kC];              // g_{i-1}
+  float graw_t[kC];               // g_i
+  float gexp_t[kC];               // e^{g_i}
+  float glast[4];                 // e^{g_63}
+};
+
+// One chunk of input as staged from HBM: 64 rows of 128 bytes, the 16-byte
 // segment q of row r stored at position q ^ ((r >> 1) & 7) (conflict-free
-// reads of 16 consecutive rows).
+// reads of 16 consecutive rows), and the chunk's gates.
 struct InputEntry {
   uint16_t x[kC * kD];            // keys phi(k_{t0+r-1})
   uint16_t q[kC * kD];            // queries phi(q_{t0+r})
-  float beta[kC];
-  float lam[kC];
+  ChunkGates gt;
 };
 
 // Factors of one chunk, as consumed by the chain waves.
@@ -85,30 +100,16 @@ struct Slot {
   uint16_t mf[4 * 2 * 64 * 8];    // M^T, B fragments [ib][m][lane][8]
   uint16_t xh[4 * 2 * 64 * 8];    // (Diag(e^{g_63-g}) X)^T, A fragments [fb][m][lane][8]
   uint16_t uf[4 * 4 * 64 * 4];    // U result tiles [ib][cb][lane][4], bf16
-  float gexp_t[kC];               // e^{g_i} at [c16 * 4 + ib] for i = 16 ib + c16
-  float glast[4];                 // e^{g_63}
-};
-
-// Gates of the chunk in the orders a factor wave reads them back.
-struct Gates {
-  float graw[kC];                 // g_s, token order
-  float sxg[kC];                  // eta_s e^{g_{s-1}}
-  float sxh[kC];                  // e^{g_63 - g_s}
-  float eta[kC];                  // eta_s, token order
-  float eta_t[kC];                // eta_i at [c16 * 4 + ib]
-  float gprev_t[kC];              // g_{i-1} at [c16 * 4 + ib]
-  float graw_t[kC];               // g_i at [c16 * 4 + ib]
 };
 
 struct Smem {
   InputEntry in[kNI];
   Slot slot[kNS];
   uint16_t tb[2][kC * kP];        // T = (I + A)^{-1}, row-major, by chunk parity
-  float abt[4][16][16];           // diagonal blocks of A: [b][s][i] = A[16b+i][16b+s]
-  Gates gates[kFactor];
-  int in_ready[kNI];              // +1 per chain wave when its half of an entry landed
+  float abt[4][16][16];           // diagonal blocks of -A: [b][s][i] = -A[16b+i][16b+s]
+  int in_ready[kNI];              // +1 when an entry's loads (issued by wave f1) have landed
   int in_free[kNI];               // +1 per chain wave when done with an entry
-  int slot_full[kNS];             // +1 per factor wave when its part is written
+  int slot_full[kNS];             // +1 per factor wave f1..f3 when its part is written
   int slot_free[kNS];             // +1 per chain wave when it has read a slot
   int t_ready[2];                 // chunk + 1 whose T is complete in tb[parity]
   int t_used[2];                  // +1 per factor wave 1..3 done reading tb[parity]
@@ -193,11 +194,6 @@ __device__ __forceinline__ bf16x8 select_frag(int h, int g, int c16) {
   return r;
 }
 
-// Lane n of each 16-lane row, broadcast to the row (DPP row_newbcast).
-template <int N>
-__device__ __forceinline__ float row_bcast(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + N, 0xf, 0xf, false));
-}
 // Value of lane l-n within the 16-lane row, 0 past the row start (DPP row_shr).
 template <int N>
 __device__ __forceinline__ float row_shr(float v) {
@@ -207,22 +203,64 @@ __device__ __forceinline__ float lane_value(float v, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }
 // Column elimination for a unit lower-triangular 16x16 block: lane j holds
-// column j of the strictly-lower part (col[i] = A[i][j]) and of the inverse
-// (t[i]); step S subtracts A[i][S] t[S] from every row i > S, with A[i][S]
-// broadcast from lane S.
-template <int S>
-__device__ __forceinline__ void eliminate(float (&t)[16], const float (&col)[16]) {
-  if constexpr (S < 15) {
-#pragma unroll
-    for (int i = S + 1; i < 16; ++i) t[i] = fmaf(-row_bcast<S>(col[i]), t[S], t[i]);
-    eliminate<S + 1>(t, col);
-  }
+// column j of the negated strictly-lower part (ncol[i] = -A[i][j]) and of
+// the inverse (t[i]).  Step S adds -A[i][S] t[S] to every row i > S, the
+// factor broadcast from lane S of the 16-lane row by the multiply-add's own
+// DPP source modifier (row_newbcast).  Each statement starts with two wait
+// states, which covers the DPP read-after-VALU-write hazard on its sources.
+#define FALCON_FMAC(D, A, S) "v_fmac_f32_dpp %" #D ", %" #A ", %" #S
+#define FALCON_BCAST(N) " row_newbcast:" #N " row_mask:0xf bank_mask:0xf\n\t"
+#define ELIM4(S, I)                                                                     \
+  asm volatile("s_nop 1\n\t" FALCON_FMAC(0, 4, 8) FALCON_BCAST(S) FALCON_FMAC(1, 5, 8)   \
+               FALCON_BCAST(S) FALCON_FMAC(2, 6, 8) FALCON_BCAST(S) FALCON_FMAC(3, 7, 8)   \
+               FALCON_BCAST(S)                                                          \
+               : "+v"(t[I]), "+v"(t[I + 1]), "+v"(t[I + 2]), "+v"(t[I + 3])              \
+               : "v"(ncol[I]), "v"(ncol[I + 1]), "v"(ncol[I + 2]), "v"(ncol[I + 3]), "v"(t[S]))
+#define ELIM3(S, I)                                                                     \
+  asm volatile("s_nop 1\n\t" FALCON_FMAC(0, 3, 6) FALCON_BCAST(S) FALCON_FMAC(1, 4, 6)   \
+               FALCON_BCAST(S) FALCON_FMAC(2, 5, 6) FALCON_BCAST(S)                      \
+               : "+v"(t[I]), "+v"(t[I + 1]), "+v"(t[I + 2])                              \
+               : "v"(ncol[I]), "v"(ncol[I + 1]), "v"(ncol[I + 2]), "v"(t[S]))
+#define ELIM2(S, I)                                                                     \
+  asm volatile("s_nop 1\n\t" FALCON_FMAC(0, 2, 4) FALCON_BCAST(S) FALCON_FMAC(1, 3, 4)   \
+               FALCON_BCAST(S)                                                          \
+               : "+v"(t[I]), "+v"(t[I + 1])                                             \
+               : "v"(ncol[I]), "v"(ncol[I + 1]), "v"(t[S]))
+#define ELIM1(S, I)                                                                     \
+  asm volatile("s_nop 1\n\t" FALCON_FMAC(0, 1, 2) FALCON_BCAST(S)                        \
+               : "+v"(t[I]) : "v"(ncol[I]), "v"(t[S]))
+
+__device__ __forceinline__ void eliminate16(float (&t)[16], const float (&ncol)[16]) {
+  ELIM4(0, 1); ELIM4(0, 5); ELIM4(0, 9); ELIM3(0, 13);
+  ELIM4(1, 2); ELIM4(1, 6); ELIM4(1, 10); ELIM2(1, 14);
+  ELIM4(2, 3); ELIM4(2, 7); ELIM4(2, 11); ELIM1(2, 15);
+  ELIM4(3, 4); ELIM4(3, 8); ELIM4(3, 12);
+  ELIM4(4, 5); ELIM4(4, 9); ELIM3(4, 13);
+  ELIM4(5, 6); ELIM4(5, 10); ELIM2(5, 14);
+  ELIM4(6, 7); ELIM4(6, 11); ELIM1(6, 15);
+  ELIM4(7, 8); ELIM4(7, 12);
+  ELIM4(8, 9); ELIM3(8, 13);
+  ELIM4(9, 10); ELIM2(9, 14);
+  ELIM4(10, 11); ELIM1(10, 15);
+  ELIM4(11, 12);
+  ELIM3(12, 13);
+  ELIM2(13, 14);
+  ELIM1(14, 15);
 }
+#undef ELIM4
+#undef ELIM3
+#undef ELIM2
+#undef ELIM1
+#undef FALCON_BCAST
+#undef FALCON_FMAC
 
 __device__ __forceinline__ bool wait_at_least(int* flag, int target, int* abort_flag) {
   for (int it = 0; it < kSpinLimit; ++it) {
-    const int v = __hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
-    if (__builtin_amdgcn_readfirstlane(v) >= target) return true;
+    const int v = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (__builtin_amdgcn_readfirstlane(v) >= target) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+      return true;
+    }
     if (__hip_atomic_load(abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) return false;
     __builtin_amdgcn_s_sleep(1);
   }
@@ -230,7 +268,8 @@ __device__ __forceinline__ bool wait_at_least(int* flag, int target, int* abort_
   return false;
 }
 __device__ __forceinline__ void signal_add(int* flag, int l) {
-  if (l == 0) __hip_atomic_fetch_add(flag, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  if (l == 0) __hip_atomic_fetch_add(flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 __device__ __forceinline__ bool aborted(int* abort_flag) {
   return __hip_atomic_load(abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0;
@@ -253,35 +292,115 @@ struct Seq {
 };
 
 // ---------------------------------------------------------------------------
-// Ring loads (chain waves): half h of the entry of chunk c.  h = 0 loads the
-// keys and the gates, h = 1 the queries.  Rows past the sequence are loaded
-// from a valid row (their step size is 0, so their finite values never
-// reach a result); so is the fresh-start key row -1 (eta_1 = 0).
+// Ring staging (wave f1): the keys, queries and gates of chunk c are fetched
+// into registers with fully coalesced 16-byte loads (one instruction covers
+// eight whole rows), and written to the swizzled ring entry later, once the
+// loads have had a chunk's worth of work to land.  Rows past the sequence are
+// fetched from a valid row (their step size is 0, so their finite values
+// never reach a result); so is the fresh-start key row -1 (eta_1 = 0).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void ring_load(InputEntry& E, const Seq& sq, int c, int h, int l) {
+struct RingRegs {
+  bf16x8 x[8];
+  bf16x8 q[8];
+  float beta, lam;
+};
+
+__device__ __forceinline__ void ring_fetch(RingRegs& R, const Seq& sq, int c, int l) {
   const int t0 = c * kC;
   const int T = sq.T;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int r = 8 * j + (l >> 3);
-    const int q = (l & 7) ^ ((r >> 1) & 7);          // logical segment stored at position l & 7
-    const bf16_t* src;
-    if (h == 0) {
-      const int kt = t0 + r - 1;
-      if (kt < 0) src = sq.k_prev ? sq.k_prev : sq.K;
-      else src = sq.K + int64_t(kt < T ? kt : T - 1) * kD;
-    } else {
-      const int tok = t0 + r;
-      src = sq.Q + int64_t(tok < T ? tok : T - 1) * kD;
+    const int kt = t0 + r - 1;
+    const bf16_t* xs = kt < 0 ? (sq.k_prev ? sq.k_prev : sq.K) : sq.K + int64_t(kt < T ? kt : T - 1) * kD;
+    const int tok = t0 + r < T ? t0 + r : T - 1;
+    R.x[j] = *reinterpret_cast<const bf16x8*>(xs + 8 * (l & 7));
+    R.q[j] = *reinterpret_cast<const bf16x8*>(sq.Q + int64_t(tok) * kD + 8 * (l & 7));
+  }
+  const int tok = t0 + l < T ? t0 + l : T - 1;
+  R.beta = sq.beta[tok];
+  R.lam = sq.lam[tok];
+}
+
+// Writes the staged rows of chunk c into entry E and derives the chunk's
+// gates (a1) from the staged registers: x_i = phi(k_{t0+i-1}), E_i = ||x_i||^2,
+// eta_i (Eq. 3.4, 0 at a fresh start and past the sequence), the clamped log
+// decay of Section 4.3 and its chunk-local inclusive prefix g_i (the
+// log-space renormalisation of Section 4.4 applied per chunk).
+__device__ __forceinline__ void ring_store(InputEntry& E, const RingRegs& R, const Seq& sq, int c, int l,
+                                           float eps, float eps_gamma, bool fresh) {
+  const int g = l >> 4, c16 = l & 15;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = 8 * j + (l >> 3);
+    const int off = r * kD + 8 * seg_pos(r, l & 7);
+    *reinterpret_cast<bf16x8*>(E.x + off) = R.x[j];
+    *reinterpret_cast<bf16x8*>(E.q + off) = R.q[j];
+  }
+  // energies: lane l holds 8 features of rows 8 j + (l >> 3); a transposing
+  // butterfly over the 8 lanes of a row leaves lane l with the energy of row
+  // 8 (l & 7) + (l >> 3), and one lane shuffle brings row l to lane l
+  float p[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float e = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const bf16x2 xv = {R.x[j][2 * k], R.x[j][2 * k + 1]};
+      e = __builtin_amdgcn_fdot2_f32_bf16(xv, xv, e, false);
     }
-    uint16_t* dst = (h == 0 ? E.x : E.q) + j * 512;  // 8 rows of 64 bf16
-    __builtin_amdgcn_global_load_lds(src + 8 * q, (lds_void*)(dst), 16, 0, 0);
+    p[j] = e;
   }
-  if (h == 0) {
-    const int tok = t0 + l < T ? t0 + l : T - 1;
-    __builtin_amdgcn_global_load_lds(sq.beta + tok, (lds_void*)(E.beta), 4, 0, 0);
-    __builtin_amdgcn_global_load_lds(sq.lam + tok, (lds_void*)(E.lam), 4, 0, 0);
+  float q4[4], q2[2];
+  {
+    const bool b = (l & 4) != 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) q4[k] = (b ? p[k + 4] : p[k]) + __shfl_xor(b ? p[k] : p[k + 4], 4);
   }
+  {
+    const bool b = (l & 2) != 0;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) q2[k] = (b ? q4[k + 2] : q4[k]) + __shfl_xor(b ? q4[k] : q4[k + 2], 2);
+  }
+  float energy;
+  {
+    const bool b = (l & 1) != 0;
+    energy = (b ? q2[1] : q2[0]) + __shfl_xor(b ? q2[0] : q2[1], 1);
+  }
+  energy = __shfl(energy, 8 * (l & 7) + (l >> 3));
+  const int tok = c * kC + l;                                // this lane's row is l
+  float eta = 0.f, lg = 0.f;
+  if (tok < sq.T) {
+    eta = nlms_eta(R.beta, energy, R.lam, eps, fresh && tok == 0);
+    lg = clamped_log_gamma(eta, R.lam, eps_gamma);
+  }
+  // inclusive prefix over the 64 rows: DPP shifts within 16-lane rows, then
+  // the row totals carried across rows
+  float gi = lg;
+  gi += row_shr<1>(gi);
+  gi += row_shr<2>(gi);
+  gi += row_shr<4>(gi);
+  gi += row_shr<8>(gi);
+  {
+    const float r0 = lane_value(gi, 15), r1 = lane_value(gi, 31), r2 = lane_value(gi, 47);
+    gi += (g >= 1 ? r0 : 0.0f) + (g >= 2 ? r1 : 0.0f) + (g >= 3 ? r2 : 0.0f);
+  }
+  float gprev = row_shr<1>(gi);
+  {
+    const float e15 = lane_value(gi, 15), e31 = lane_value(gi, 31), e47 = lane_value(gi, 47);
+    if (c16 == 0) gprev = g == 0 ? 0.0f : g == 1 ? e15 : g == 2 ? e31 : e47;
+  }
+  const float glast = lane_value(gi, 63);
+  ChunkGates& G = E.gt;
+  G.graw[l] = gi;
+  G.sxg[l] = eta * __expf(gprev);
+  G.sxh[l] = __expf(glast - gi);
+  G.eta[l] = eta;
+  G.eta_t[c16 * 4 + g] = eta;
+  G.gprev_t[c16 * 4 + g] = gprev;
+  G.graw_t[c16 * 4 + g] = gi;
+  G.gexp_t[c16 * 4 + g] = __expf(gi);
+  if (l == 0) G.glast[0] = __expf(glast);
 }
 
 // ---------------------------------------------------------------------------
@@ -310,64 +429,18 @@ __device__ bool factor_chunk(Smem& sm, ValueFrags& VF, const Seq& sq, int c, int
   const InputEntry& E = sm.in[c % kNI];
   Slot& S = sm.slot[c % kNS];
   uint16_t* tb = sm.tb[c & 1];
-  Gates& G = sm.gates[fw];
-  if (!wait_at_least(&sm.in_ready[c % kNI], 2 * (c / kNI + 1), &sm.abort_flag)) return false;
+  const ChunkGates& G = E.gt;
+  if (!wait_at_least(&sm.in_ready[c % kNI], c / kNI + 1, &sm.abort_flag)) return false;
 
-  // ---- a1: energies, step sizes, chunk-local log decays (every wave) -------
+  // key fragments: rows 16 ib + c16, k block m (contiguous order); wave f0
+  // needs both k blocks, f1 the first (key blocks 0-1), f2 and f3 the second
+  constexpr int m_lo = kRole == 2 ? 1 : 0;
+  constexpr int m_hi = kRole == 1 ? 1 : 2;
   bf16x8 xf[4][2];
 #pragma unroll
   for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
-    for (int m = 0; m < 2; ++m) xf[ib][m] = ring_frag_c(E.x, 16 * ib + c16, m, g);
-  float part[4];
-#pragma unroll
-  for (int ib = 0; ib < 4; ++ib) {
-    float e = 0.f;
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float xv = static_cast<float>(xf[ib][m][k]);
-        e = fmaf(xv, xv, e);
-      }
-    part[ib] = e;
-  }
-#pragma unroll
-  for (int ib = 0; ib < 4; ++ib) part[ib] += __shfl_xor(part[ib], 16);
-#pragma unroll
-  for (int ib = 0; ib < 4; ++ib) part[ib] += __shfl_xor(part[ib], 32);
-  const float energy = g == 0 ? part[0] : g == 1 ? part[1] : g == 2 ? part[2] : part[3];
-  const int tok = t0 + l;                                    // this lane's row is l
-  float eta = 0.f, lg = 0.f;
-  if (tok < sq.T) {
-    const float bt = E.beta[l], lt = E.lam[l];
-    eta = nlms_eta(bt, energy, lt, eps, fresh && tok == 0);
-    lg = clamped_log_gamma(eta, lt, eps_gamma);
-  }
-  // inclusive prefix over the 64 rows: DPP shifts within 16-lane rows, then
-  // the row totals carried across rows
-  float gi = lg;
-  gi += row_shr<1>(gi);
-  gi += row_shr<2>(gi);
-  gi += row_shr<4>(gi);
-  gi += row_shr<8>(gi);
-  {
-    const float r0 = lane_value(gi, 15), r1 = lane_value(gi, 31), r2 = lane_value(gi, 47);
-    gi += (g >= 1 ? r0 : 0.0f) + (g >= 2 ? r1 : 0.0f) + (g >= 3 ? r2 : 0.0f);
-  }
-  float gprev = row_shr<1>(gi);
-  {
-    const float e15 = lane_value(gi, 15), e31 = lane_value(gi, 31), e47 = lane_value(gi, 47);
-    if (c16 == 0) gprev = g == 0 ? 0.0f : g == 1 ? e15 : g == 2 ? e31 : e47;
-  }
-  const float glast = lane_value(gi, 63);
-  G.graw[l] = gi;
-  G.sxg[l] = eta * __expf(gprev);
-  G.sxh[l] = __expf(glast - gi);
-  G.eta[l] = eta;
-  G.eta_t[c16 * 4 + g] = eta;
-  G.gprev_t[c16 * 4 + g] = gprev;
-  G.graw_t[c16 * 4 + g] = gi;
+    for (int m = m_lo; m < m_hi; ++m) xf[ib][m] = ring_frag_c(E.x, 16 * ib + c16, m, g);
 
   if constexpr (kRole == 0) {
     // ---- decayed Gram: A^T tile (sb, ib) = X_sb X_ib^T, scaled ------------
@@ -395,7 +468,7 @@ __device__ bool factor_chunk(Smem& sm, ValueFrags& VF, const Seq& sq, int c, int
         }
         if (ib == sb) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) sm.abt[ib][4 * g + r][c16] = a[r];
+          for (int r = 0; r < 4; ++r) sm.abt[ib][4 * g + r][c16] = -a[r];
         } else {
           a_off[n - ib] = a;     // n - ib enumerates the off-diagonal tiles in order
         }
@@ -408,15 +481,15 @@ __device__ bool factor_chunk(Smem& sm, ValueFrags& VF, const Seq& sq, int c, int
     // ---- T = (I + A)^{-1}: diagonal blocks by column elimination ----------
     float t[16];
     {
-      float col[16];
+      float ncol[16];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 v = ld4(&sm.abt[g][c16][4 * q4]);        // A[16g+i][16g+c16], all i
-        col[4 * q4] = v[0]; col[4 * q4 + 1] = v[1]; col[4 * q4 + 2] = v[2]; col[4 * q4 + 3] = v[3];
+        const f32x4 v = ld4(&sm.abt[g][c16][4 * q4]);        // -A[16g+i][16g+c16], all i
+        ncol[4 * q4] = v[0]; ncol[4 * q4 + 1] = v[1]; ncol[4 * q4 + 2] = v[2]; ncol[4 * q4 + 3] = v[3];
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) t[i] = (i == c16) ? 1.0f : 0.0f;
-      eliminate<0>(t, col);
+      eliminate16(t, ncol);
     }
     // tb[c & 1] held T of chunk c - 2: wait until f1..f3 are done with it.
     if (!wait_at_least(&sm.t_used[c & 1], 3 * (c / 2), &sm.abort_flag)) return false;
@@ -458,46 +531,23 @@ __device__ bool factor_chunk(Smem& sm, ValueFrags& VF, const Seq& sq, int c, int
         }
       }
     }
-    if (l == 0) __hip_atomic_store(&sm.t_ready[c & 1], c + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-    // the chain reads the output scales from the slot
-    if (!wait_at_least(&sm.slot_free[c % kNS], 2 * (c / kNS), &sm.abort_flag)) return false;
-    S.gexp_t[c16 * 4 + g] = __expf(gi);
-    if (l == 0) S.glast[0] = __expf(glast);
-    signal_add(&sm.slot_full[c % kNS], l);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    if (l == 0) __hip_atomic_store(&sm.t_ready[c & 1], c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     return true;
   }
 
   // ---- waves f1..f3 ---------------------------------------------------------
-  // Work split: f1: mask tiles with ib >= 2, key transposes fb 0..1, W fb 0..1;
-  // f2: mask tiles with ib < 2, key transposes fb 2, values cb 0..1, W fb 2;
-  // f3: key transposes fb 3, values cb 2..3, W fb 3.
+  // Work split: f1: staging of chunk c + 1, key transposes fb 0..1, W fb 0..1;
+  // f2: key transposes fb 2, values cb 0..1, mask tiles 0..4, W fb 2;
+  // f3: key transposes fb 3, values cb 2..3, mask tiles 5..9, W fb 3.
   const int fb0 = kRole == 1 ? 0 : fw;                          // first key block: 0, 2, 3
   constexpr int nfb = kRole == 1 ? 2 : 1;
-  const int n0 = kRole == 1 ? 3 : 0, n1 = kRole == 1 ? 10 : fw == 2 ? 3 : 0;   // mask tiles [n0, n1)
   if (!wait_at_least(&sm.slot_free[c % kNS], 2 * (c / kNS), &sm.abort_flag)) return false;
+  // wave f1 streams the ring entry of chunk c + 1 (it held chunk c - 2)
+  const bool load_next = kRole == 1 && c + 1 < nchunks;
+  RingRegs rr;
+  if (load_next) ring_fetch(rr, sq, c + 1, l);
 
-  // ---- decayed read mask: M^T tile (sb, ib) = X_sb Q_ib^T -----------------
-  if (n1 > n0) {
-    const f32x4 gra_i = ld4(&G.graw_t[c16 * 4]);
-    for (int n = n0; n < n1; ++n) {
-      int ib, sb;
-      lower_tile(n, ib, sb);
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-        acc = mfma32(ring_frag_c(E.x, 16 * sb + c16, m, g), ring_frag_c(E.q, 16 * ib + c16, m, g), acc);
-      const int i = 16 * ib + c16;
-      const f32x4 gs = ld4(&G.graw[16 * sb + 4 * g]);
-      const float gi_ib = ib == 0 ? gra_i[0] : ib == 1 ? gra_i[1] : ib == 2 ? gra_i[2] : gra_i[3];
-      f32x4 mv;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int s_ = 16 * sb + 4 * g + r;
-        mv[r] = s_ <= i ? __expf(gi_ib - gs[r]) * acc[r] : 0.0f;
-      }
-      store_half(&S.mf[((ib * 2 + (sb >> 1)) * 64 + l) * 8 + 4 * (sb & 1)], mv);
-    }
-  }
   // ---- decayed key transposes on the matrix cores --------------------------
   // D(sb, fb) = X_sb I_fb; lane holds X[16sb+4g+r][16fb+c16].
   bf16x8 xg[2][2];                                           // (Diag(eta e^{g_{s-1}}) X)^T
@@ -543,6 +593,34 @@ __device__ bool factor_chunk(Smem& sm, ValueFrags& VF, const Seq& sq, int c, int
     }
     // this wave's next chunk is c + 1
     if (c + 1 < nchunks) load_values(VF, sq, c + 1, fw - 2, l);
+    // ---- decayed read mask: M^T tile (sb, ib) = X_sb Q_ib^T, s <= i -------
+    const f32x4 gra_i = ld4(&G.graw_t[c16 * 4]);
+    const int n0 = fw == 2 ? 0 : 5;
+#pragma unroll
+    for (int n5 = 0; n5 < 5; ++n5) {
+      int ib, sb;
+      lower_tile(n0 + n5, ib, sb);
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+        acc = mfma32(ring_frag_c(E.x, 16 * sb + c16, m, g), ring_frag_c(E.q, 16 * ib + c16, m, g), acc);
+      const int i = 16 * ib + c16;
+      const f32x4 gs = ld4(&G.graw[16 * sb + 4 * g]);
+      const float gi_ib = ib == 0 ? gra_i[0] : ib == 1 ? gra_i[1] : ib == 2 ? gra_i[2] : gra_i[3];
+      f32x4 mv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int s_ = 16 * sb + 4 * g + r;
+        mv[r] = s_ <= i ? __expf(gi_ib - gs[r]) * acc[r] : 0.0f;
+      }
+      store_half(&S.mf[((ib * 2 + (sb >> 1)) * 64 + l) * 8 + 4 * (sb & 1)], mv);
+    }
+  }
+  if (load_next) {
+    const int e = (c + 1) % kNI;
+    if (!wait_at_least(&sm.in_free[e], 2 * ((c + 1) / kNI), &sm.abort_flag)) return false;
+    ring_store(sm.in[e], rr, sq, c + 1, l, eps, eps_gamma, fresh);
+    signal_add(&sm.in_ready[e], l);
   }
   // ---- wait for T, then W^T tiles (fb, ib) = X~^T T^T and U = T V~ ---------
   if (!wait_at_least(&sm.t_ready[c & 1], c + 1, &sm.abort_flag)) return false;
@@ -588,14 +666,7 @@ __device__ bool chain_chunk(Smem& sm, f32x4 (&Sst)[4][2], const Seq& sq, int c, 
                             bf16_t* o_bh, int nchunks) {
   const int g = l >> 4, c16 = l & 15;
   const int t0 = c * kC;
-  // ---- stream the entry of chunk c + 2 (it held chunk c - 1; both chain
-  // waves must be done with it)
-  if (c + 2 < nchunks) {
-    const int e = (c + 2) % kNI;
-    if (!wait_at_least(&sm.in_free[e], 2 * ((c + 2) / kNI), &sm.abort_flag)) return false;
-    ring_load(sm.in[e], sq, c + 2, w, l);
-  }
-  if (!wait_at_least(&sm.slot_full[c % kNS], kFactor * (c / kNS + 1), &sm.abort_flag)) return false;
+  if (!wait_at_least(&sm.slot_full[c % kNS], kSlotWriters * (c / kNS + 1), &sm.abort_flag)) return false;
   const Slot& S = sm.slot[c % kNS];
   const InputEntry& E = sm.in[c % kNI];
 
@@ -629,9 +700,16 @@ __device__ bool chain_chunk(Smem& sm, f32x4 (&Sst)[4][2], const Seq& sq, int c, 
   for (int fb = 0; fb < 4; ++fb)
 #pragma unroll
     for (int m = 0; m < 2; ++m) xhr[fb][m] = load_frag(&S.xh[((fb * 2 + m) * 64 + l) * 8]);
-  const f32x4 gexp_i = ld4(&S.gexp_t[c16 * 4]);
-  const float glast = S.glast[0];
-  signal_add(&sm.slot_free[c % kNS], l);                     // slot contents are in registers
+  const f32x4 gexp_i = ld4(&E.gt.gexp_t[c16 * 4]);
+  const float glast = E.gt.glast[0];
+  bf16x8 qf[4][2];                                           // queries of row block ib
+#pragma unroll
+  for (int ib = 0; ib < 4; ++ib) {
+    qf[ib][0] = ring_frag_p(E.q, 16 * ib + c16, 0, g);
+    qf[ib][1] = ring_frag_p(E.q, 16 * ib + c16, 1, g);
+  }
+  signal_add(&sm.slot_free[c % kNS], l);                     // slot and entry contents are in registers
+  signal_add(&sm.in_free[c % kNI], l);
 
   bf16x8 rb[2][2];                                           // R fragments [cb][m]
 #pragma unroll
@@ -643,7 +721,7 @@ __device__ bool chain_chunk(Smem& sm, f32x4 (&Sst)[4][2], const Seq& sq, int c, 
 #pragma unroll
   for (int ib = 0; ib < 4; ++ib) {
     const int i = 16 * ib + c16;
-    const bf16x8 q0 = ring_frag_p(E.q, i, 0, g), q1 = ring_frag_p(E.q, i, 1, g);
+    const bf16x8 q0 = qf[ib][0], q1 = qf[ib][1];
     const int tok = t0 + i;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
@@ -659,7 +737,6 @@ __device__ bool chain_chunk(Smem& sm, f32x4 (&Sst)[4][2], const Seq& sq, int c, 
       }
     }
   }
-  signal_add(&sm.in_free[c % kNI], l);                       // done with the queries of chunk c
   // ---- S <- e^{g_63} S + (Diag(e^{g_63-g}) X)^T R ---------------------------
 #pragma unroll
   for (int fb = 0; fb < 4; ++fb)
@@ -707,11 +784,6 @@ falcon1_chunked_mfma_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __re
 
   if (wave < kChain) {
     const int w = wave;
-    // prologue: the first two ring entries
-    for (int c = 0; c < 2 && c < nchunks; ++c) ring_load(sm.in[c], sq, c, w, l);
-    __builtin_amdgcn_s_waitcnt(0);                          // this wave's loads have landed
-    for (int c = 0; c < 2 && c < nchunks; ++c) signal_add(&sm.in_ready[c], l);
-
     f32x4 Sst[4][2];
 #pragma unroll
     for (int fb = 0; fb < 4; ++fb)
@@ -722,10 +794,6 @@ falcon1_chunked_mfma_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __re
           Sst[fb][k][r] = S0 ? S0[(bh * kD + 16 * fb + 4 * g + r) * kD + 32 * w + 16 * k + c16] : 0.0f;
     for (int c = 0; c < nchunks; ++c) {
       if (!chain_chunk(sm, Sst, sq, c, w, l, o + bh * T * kD, nchunks)) break;
-      if (c + 2 < nchunks) {
-        __builtin_amdgcn_s_waitcnt(0);                      // this wave's ring loads have landed
-        signal_add(&sm.in_ready[(c + 2) % kNI], l);
-      }
     }
     if (S_T) {
 #pragma unroll
@@ -744,6 +812,13 @@ falcon1_chunked_mfma_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __re
       for (int c = 0; c < nchunks; ++c)
         if (!factor_chunk<0>(sm, VF, sq, c, fw, l, eps, eps_gamma, fresh, nchunks)) break;
     } else if (fw == 1) {
+      // prologue: the first ring entry
+      {
+        RingRegs rr;
+        ring_fetch(rr, sq, 0, l);
+        ring_store(sm.in[0], rr, sq, 0, l, eps, eps_gamma, fresh);
+        signal_add(&sm.in_ready[0], l);
+      }
       for (int c = 0; c < nchunks; ++c)
         if (!factor_chunk<1>(sm, VF, sq, c, fw, l, eps, eps_gamma, fresh, nchunks)) break;
     } else {
