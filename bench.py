@@ -114,6 +114,44 @@ def bench_decode(steps=50, warmup=5):
             "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
 
 
+def bench_chunked_workload(name, steps=20, warmup=3):
+    """Another chunked workload (inputs resident in HBM), timed with HIP events
+    on the launch stream; reported beside the headline line."""
+    import torch
+
+    from delta_rule_recurrence_amd import falcon as fb
+    from delta_rule_recurrence_amd import inputs as I
+
+    w = I.WORKLOADS[name]
+    d = {k: v.cuda() for k, v in I.workload_inputs(w).items()}
+    o = torch.empty((w.B, w.H, w.T, w.dv), dtype=torch.bfloat16, device="cuda")
+    S_T = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    p = fb.make_problem(w.B, w.H, w.T, w.dk, w.dv, variant=w.variant, io_dtype=torch.bfloat16,
+                        eps=w.eps, eps_gamma=w.eps_gamma)
+    ws = torch.empty(max(fb.falcon_workspace_bytes(p, w.C), 16), dtype=torch.uint8, device="cuda")
+
+    def step():
+        fb.falcon_fwd_chunked(d["phi_k"], d["phi_q"], d["v"], d["beta"], d["lam"], variant=w.variant,
+                              C=w.C, o=o, S_T=S_T, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = algorithmic_bytes(w.B, w.H, w.T, w.dk, w.dv)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": name, "variant": w.variant, "steps": steps, "us_per_step": ms * 1e3,
+            "tokens_per_s": w.B * w.T / (ms * 1e-3), "algorithmic_bytes": nbytes,
+            "workspace_bytes": int(ws.numel()), "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
+
+
 def calibrate_copy(nbytes=1 << 28, reps=5):
     """A plain device copy of known size, for scaling rocprofv3 FETCH_SIZE /
     WRITE_SIZE counters (each copy reads and writes nbytes once)."""
@@ -158,6 +196,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other chunked workloads (Falcon-1A 2x12x16384)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain copy of known size (for PMC counter scaling)")
     args = ap.parse_args()
@@ -232,6 +272,8 @@ def main():
     }
     if not args.no_decode:
         line["decode"] = bench_decode()
+    if not args.no_extra:
+        line["f1a_chunked"] = bench_chunked_workload("f1a_chunked_2x12x16384_d64")
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(d, w, o, S_T)
     print(json.dumps(line))

@@ -1,0 +1,194 @@
+// MFMA fragment helpers shared by the chunked kernels (gfx950, bf16 operands,
+// float32 accumulation, 64-wide wavefronts).
+//
+// v_mfma_f32_16x16x32_bf16 takes, in lane l, row (l & 15) of A and column
+// (l & 15) of B with eight k-values each; the result holds column (l & 15),
+// rows 4 (l >> 4) .. +3.  "Contiguous" fragments give lane group g = l >> 4
+// the k-values 8g..8g+7 of a 32-wide block (one 16-byte read of a row);
+// "result-compatible" fragments give it {4g..4g+3, 16+4g..16+4g+3}, so two
+// stacked result tiles are exactly the next operand fragment.  A and B
+// always use the same order, so every sum is unchanged.
+//
+// Staged rows: 64 rows of 64 bf16 (128 bytes), the 16-byte segment q of row r
+// stored at position q ^ ((r >> 1) & 7), which makes reads of 16 consecutive
+// rows at one segment conflict-free.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "falcon_device.h"
+
+namespace falcon {
+namespace frag {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kRowElems = 64;     // elements per staged row
+
+__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(s16x4 a, s16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ uint16_t bf(float f) { return f32_to_bf16(f); }
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// k offset (within a 32-wide block) of element e of lane group g in the
+// result-compatible order.
+__device__ __forceinline__ int kperm(int g, int e) { return e < 4 ? 4 * g + e : 12 + 4 * g + e; }
+
+__device__ __forceinline__ int seg_pos(int r, int q) { return q ^ ((r & 15) >> 1); }
+
+// Contiguous-order fragment: k = 32m + 8g .. +7 of row r of a ring matrix.
+__device__ __forceinline__ bf16x8 ring_frag_c(const uint16_t* mat, int r, int m, int g) {
+  const uint4 v = *reinterpret_cast<const uint4*>(mat + r * kRowElems + 8 * seg_pos(r, 4 * m + g));
+  return __builtin_bit_cast(bf16x8, v);
+}
+// Result-compatible fragment: k = 32m + kperm(g, 0..7) of row r of a ring matrix.
+__device__ __forceinline__ bf16x8 ring_frag_p(const uint16_t* mat, int r, int m, int g) {
+  const int off = 4 * (g & 1);
+  const uint2 a = *reinterpret_cast<const uint2*>(mat + r * kRowElems + 8 * seg_pos(r, 4 * m + (g >> 1)) + off);
+  const uint2 b = *reinterpret_cast<const uint2*>(mat + r * kRowElems + 8 * seg_pos(r, 4 * m + 2 + (g >> 1)) + off);
+  return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
+}
+// Result-compatible fragment of a bf16 row in a padded row-major array.
+__device__ __forceinline__ bf16x8 frag_lds(const uint16_t* row, int kbase, int g) {
+  const uint2 a = *reinterpret_cast<const uint2*>(row + kbase + 4 * g);
+  const uint2 b = *reinterpret_cast<const uint2*>(row + kbase + 16 + 4 * g);
+  return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
+}
+// Two stacked result tiles (k rows 0-15 and 16-31 of a block) as a fragment.
+__device__ __forceinline__ bf16x8 frag_acc(f32x4 lo, f32x4 hi) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r[e] = static_cast<__bf16>(lo[e]);
+    r[e + 4] = static_cast<__bf16>(hi[e]);
+  }
+  return r;
+}
+__device__ __forceinline__ bf16x8 load_frag(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+}
+__device__ __forceinline__ void store_frag(uint16_t* p, bf16x8 v) {
+  *reinterpret_cast<uint4*>(p) = __builtin_bit_cast(uint4, v);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2 h = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  return __builtin_bit_cast(uint32_t, h);
+}
+__device__ __forceinline__ void store_half(uint16_t* p, f32x4 v) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+}
+__device__ __forceinline__ f32x4 load_half(const uint16_t* p) {
+  const uint2 v = *reinterpret_cast<const uint2*>(p);
+  return f32x4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+               __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u)};
+}
+__device__ __forceinline__ s16x4 s16_acc(f32x4 v) {
+  s16x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = static_cast<short>(bf(v[e]));
+  return r;
+}
+__device__ __forceinline__ f32x4 ld4(const float* p) {
+  const float4 v = *reinterpret_cast<const float4*>(p);
+  return f32x4{v.x, v.y, v.z, v.w};
+}
+// Contiguous-order B fragment of the selection matrix picking columns
+// 16h..16h+15 of a 32-wide block (a product with it transposes a tile).
+__device__ __forceinline__ bf16x8 select_frag(int h, int g, int c16) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = static_cast<__bf16>(8 * g + e == 16 * h + c16 ? 1.0f : 0.0f);
+  return r;
+}
+
+// Value of lane l-n within the 16-lane row, 0 past the row start (DPP row_shr).
+template <int N>
+__device__ __forceinline__ float row_shr(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x110 + N, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float lane_value(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+// Lower 16x16 tiles (ib >= sb) of a 64x64 matrix, n = 0..9.
+__device__ __forceinline__ void lower_tile(int n, int& ib, int& sb) {
+  ib = n < 1 ? 0 : n < 3 ? 1 : n < 6 ? 2 : 3;
+  sb = n - (ib * (ib + 1)) / 2;
+}
+
+// Gates of one 64-token chunk (a1) from staged key rows: lane l holds the
+// eight features 8 (l & 7) .. +7 of rows 8 j + (l >> 3) in x[j], and the gates
+// beta, lam of token `tok` = chunk start + l.  Returns, for row l: eta_l
+// (Eq. 3.4; 0 at the fresh start and past the sequence), the chunk-local
+// inclusive prefix g_l of the clamped log decays (Section 4.3, "Decay
+// positivity"; Section 4.4 log-space renormalisation applied per chunk),
+// g_{l-1} (0 for l = 0) and g_63.
+__device__ __forceinline__ void chunk_gates(const bf16x8 (&x)[8], float beta, float lam, int tok, int T,
+                                            float eps, float eps_gamma, bool fresh, int l, float& eta,
+                                            float& gi, float& gprev, float& glast) {
+  const int g = l >> 4, c16 = l & 15;
+  // energies: a transposing butterfly over the 8 lanes of a row leaves lane
+  // l with the energy of row 8 (l & 7) + (l >> 3); one shuffle brings row l
+  // to lane l
+  float p[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float e = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const bf16x2 xv = {x[j][2 * k], x[j][2 * k + 1]};
+      e = __builtin_amdgcn_fdot2_f32_bf16(xv, xv, e, false);
+    }
+    p[j] = e;
+  }
+  float q4[4], q2[2];
+  {
+    const bool b = (l & 4) != 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) q4[k] = (b ? p[k + 4] : p[k]) + __shfl_xor(b ? p[k] : p[k + 4], 4);
+  }
+  {
+    const bool b = (l & 2) != 0;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) q2[k] = (b ? q4[k + 2] : q4[k]) + __shfl_xor(b ? q4[k] : q4[k + 2], 2);
+  }
+  float energy;
+  {
+    const bool b = (l & 1) != 0;
+    energy = (b ? q2[1] : q2[0]) + __shfl_xor(b ? q2[0] : q2[1], 1);
+  }
+  energy = __shfl(energy, 8 * (l & 7) + (l >> 3));
+  eta = 0.f;
+  float lg = 0.f;
+  if (tok < T) {
+    eta = nlms_eta(beta, energy, lam, eps, fresh && tok == 0);
+    lg = clamped_log_gamma(eta, lam, eps_gamma);
+  }
+  // inclusive prefix over the 64 rows: DPP shifts within 16-lane rows, then
+  // the row totals carried across rows
+  gi = lg;
+  gi += row_shr<1>(gi);
+  gi += row_shr<2>(gi);
+  gi += row_shr<4>(gi);
+  gi += row_shr<8>(gi);
+  {
+    const float r0 = lane_value(gi, 15), r1 = lane_value(gi, 31), r2 = lane_value(gi, 47);
+    gi += (g >= 1 ? r0 : 0.0f) + (g >= 2 ? r1 : 0.0f) + (g >= 3 ? r2 : 0.0f);
+  }
+  gprev = row_shr<1>(gi);
+  {
+    const float e15 = lane_value(gi, 15), e31 = lane_value(gi, 31), e47 = lane_value(gi, 47);
+    if (c16 == 0) gprev = g == 0 ? 0.0f : g == 1 ? e15 : g == 2 ? e31 : e47;
+  }
+  glast = lane_value(gi, 63);
+}
+
+}  // namespace frag
+}  // namespace falcon

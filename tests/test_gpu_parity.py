@@ -154,6 +154,50 @@ def test_nan_propagates_without_hang():
         assert torch.isfinite(o[0, 0, :20]).all()
 
 
+# ---- Falcon-1A chunk tiles (bf16, d = 64, C = 64): look-back across tiles ---
+
+@pytest.mark.parametrize("B,H,T", [(1, 1, 4096), (2, 3, 805), (3, 2, 1000), (1, 2, 256)])
+def test_falcon1a_tiles(B, H, T):
+    """Many tiles per sequence (a deep look-back chain), ragged tails and a
+    sequence that is exactly one tile."""
+    d = I.make_inputs(B, H, T, 64, 64, seed=300 + T, io_dtype="bf16")
+    O_ref, S_ref = oracle_forward("falcon1a", d)
+    o, S_T = _run("chunked", to_dev(d), "falcon1a")
+    torch.cuda.synchronize()
+    check(o, S_T, O_ref, S_ref, TOL["bf16"], f"falcon1a tiles {B}x{H}x{T}")
+
+
+def test_falcon1a_tiles_carried_state_and_continuation():
+    B, H, T, T1 = 2, 2, 1300, 517
+    d = I.make_inputs(B, H, T, 64, 64, seed=21, io_dtype="bf16")
+    S0 = I.random_state((B, H, 64, 64), seed=22)
+    O_ref, S_ref = oracle_forward("falcon1a", d, S0=S0)
+    dd = to_dev(d)
+    o, S_T = _run("chunked", dd, "falcon1a", S0=S0.cuda())
+    torch.cuda.synchronize()
+    check(o, S_T, O_ref, S_ref, TOL["bf16"], "falcon1a tiles carried S0")
+    first = {k: v[:, :, :T1].contiguous() for k, v in dd.items()}
+    second = {k: v[:, :, T1:].contiguous() for k, v in dd.items()}
+    o1, S1 = _run("chunked", first, "falcon1a", S0=S0.cuda())
+    kp = dd["phi_k"][:, :, T1 - 1].contiguous()
+    o2, S2 = _run("chunked", second, "falcon1a", S0=S1, k_prev=kp)
+    torch.cuda.synchronize()
+    check(torch.cat([o1, o2], dim=2), S2, O_ref, S_ref, TOL["bf16"], "falcon1a tiles split")
+
+
+def test_falcon1a_tiles_repeatable():
+    """Two calls on one workspace give the same bits: no state from the
+    previous call survives in the workspace, and the tile scan has a fixed
+    order."""
+    d = to_dev(I.make_inputs(2, 2, 900, 64, 64, seed=23, io_dtype="bf16"))
+    p = fb.make_problem(2, 2, 900, 64, 64, variant="falcon1a", io_dtype=torch.bfloat16)
+    ws = torch.full((fb.falcon_workspace_bytes(p, 64),), 0x7f, dtype=torch.uint8, device="cuda")
+    o1, s1 = _run("chunked", d, "falcon1a", workspace=ws)
+    o2, s2 = _run("chunked", d, "falcon1a", workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
 # ---- decode ------------------------------------------------------------------
 
 @pytest.mark.parametrize("variant", ["falcon1", "falcon1a", "falcon2", "falcon2a"])
