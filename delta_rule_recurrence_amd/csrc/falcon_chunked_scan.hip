@@ -131,6 +131,54 @@ __device__ __forceinline__ float stage_chunk(Stage& st, const Seq& sq, int c, in
   return glast;
 }
 
+// The rows of one chunk held in registers (coalesced loads: 8 whole rows per
+// instruction), so the next chunk's loads can be in flight while the current
+// one is computed.
+struct ChunkRegs {
+  bf16x8 x[8], q[8], v[8];
+  float beta, lam;
+};
+
+__device__ __forceinline__ void fetch_chunk(ChunkRegs& R, const Seq& sq, int c, int l) {
+  const int t0 = c * kC;
+  const int T = sq.T;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = 8 * j + (l >> 3);
+    const int kt = t0 + r - 1;
+    const bf16_t* xs = kt < 0 ? (sq.k_prev ? sq.k_prev : sq.K) : sq.K + int64_t(kt < T ? kt : T - 1) * kD;
+    const int tok = t0 + r < T ? t0 + r : T - 1;
+    R.x[j] = *reinterpret_cast<const bf16x8*>(xs + 8 * (l & 7));
+    R.q[j] = *reinterpret_cast<const bf16x8*>(sq.Q + int64_t(tok) * kD + 8 * (l & 7));
+    R.v[j] = *reinterpret_cast<const bf16x8*>(sq.V + int64_t(tok) * kD + 8 * (l & 7));
+  }
+  const int tok = t0 + l < T ? t0 + l : T - 1;
+  R.beta = sq.beta[tok];
+  R.lam = sq.lam[tok];
+}
+
+// Writes fetched rows into the stage and derives the chunk's gates; returns g_63.
+__device__ __forceinline__ float commit_chunk(Stage& st, const ChunkRegs& R, int c, int T, int l,
+                                              float eps, float eps_gamma, bool fresh) {
+  const int g = l >> 4, c16 = l & 15;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = 8 * j + (l >> 3);
+    const int off = r * kD + 8 * seg_pos(r, l & 7);
+    *reinterpret_cast<bf16x8*>(st.x + off) = R.x[j];
+    *reinterpret_cast<bf16x8*>(st.q + off) = R.q[j];
+    *reinterpret_cast<bf16x8*>(st.v + off) = R.v[j];
+  }
+  float eta, gi, gprev, glast;
+  chunk_gates(R.x, R.beta, R.lam, c * kC + l, T, eps, eps_gamma, fresh, l, eta, gi, gprev, glast);
+  st.graw[l] = gi;
+  st.sxh[l] = __expf(glast - gi);
+  st.eta[l] = eta;
+  st.graw_t[c16 * 4 + g] = gi;
+  st.gexp_t[c16 * 4 + g] = __expf(gi);
+  return glast;
+}
+
 // Diag(eta) V for value block cb, as fragments over tokens (k) with lane
 // column = value column 16 cb + c16: B operand of the state update, A
 // operand of the intra-chunk read.
@@ -321,9 +369,12 @@ falcon1a_tile_out_kernel(TileArgs a, ScanWorkspace ws) {
       for (int cb = 0; cb < 4; ++cb) S[fb][cb] = *reinterpret_cast<const f32x4*>(src + ((fb * 4 + cb) * 64 + l) * 4);
   }
   bf16_t* o_bh = a.o + bh * T * kD;
+  ChunkRegs R;
+  fetch_chunk(R, sq, c0, l);
   for (int c = c0; c < c1; ++c) {
     Stage& st = opaque(st_);
-    const float glast = stage_chunk(st, sq, c, l, true, a.eps, a.eps_gamma, fresh);
+    const float glast = commit_chunk(st, R, c, T, l, a.eps, a.eps_gamma, fresh);
+    if (c + 1 < c1) fetch_chunk(R, sq, c + 1, l);
     const float decay = __expf(glast);
     const int t0 = c * kC;
     // decayed read mask M^T tile (sb, ib) = X_sb Q_ib^T, s <= i, as B fragments
