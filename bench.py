@@ -31,11 +31,13 @@ KERNEL_SOURCES = ["delta_rule_recurrence_amd/csrc/falcon_chunked_mfma.hip",
                   "delta_rule_recurrence_amd/csrc/falcon_chunked.hip"]
 
 
-def algorithmic_bytes(B, H, T, dk, dv, io_bytes=2):
+def algorithmic_bytes(B, H, T, dk, dv, io_bytes=2, per_column_beta=False):
     """Compulsory HBM bytes of one forward: read phi(k), phi(q), v once, beta
-    and lam once, write o once and S_T once (S_0 = 0 is not read)."""
+    (one per token, or one per token and value column) and lam once, write o
+    once and S_T once (S_0 = 0 is not read)."""
     th = B * H * T
-    return th * (2 * dk + dv) * io_bytes + th * 2 * 4 + th * dv * io_bytes + B * H * dk * dv * 4
+    gates = th * ((dv if per_column_beta else 1) + 1) * 4
+    return th * (2 * dk + dv) * io_bytes + gates + th * dv * io_bytes + B * H * dk * dv * 4
 
 
 def algorithmic_flops(B, H, T, dk, dv, C):
@@ -145,7 +147,8 @@ def bench_chunked_workload(name, steps=20, warmup=3):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    nbytes = algorithmic_bytes(w.B, w.H, w.T, w.dk, w.dv)
+    nbytes = algorithmic_bytes(w.B, w.H, w.T, w.dk, w.dv,
+                               per_column_beta=w.variant in ("falcon2", "falcon2a"))
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"workload": name, "variant": w.variant, "steps": steps, "us_per_step": ms * 1e3,
             "tokens_per_s": w.B * w.T / (ms * 1e-3), "algorithmic_bytes": nbytes,
@@ -197,7 +200,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the other chunked workloads (Falcon-1A 2x12x16384)")
+                    help="skip the other chunked workloads (Falcon-1A 2x12x16384, Falcon-2 8x12x2048)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain copy of known size (for PMC counter scaling)")
     args = ap.parse_args()
@@ -274,6 +277,7 @@ def main():
         line["decode"] = bench_decode()
     if not args.no_extra:
         line["f1a_chunked"] = bench_chunked_workload("f1a_chunked_2x12x16384_d64")
+        line["f2_chunked"] = bench_chunked_workload("f2_chunked_8x12x2048_d64", steps=5, warmup=1)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(d, w, o, S_T)
     print(json.dumps(line))

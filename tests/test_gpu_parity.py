@@ -198,6 +198,41 @@ def test_falcon1a_tiles_repeatable():
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
 
 
+# ---- per-column rules (Falcon-2 / 2A, bf16, d = 64, C = 64) --------------------
+
+@pytest.mark.parametrize("variant", ["falcon2", "falcon2a"])
+def test_per_column_carried_state_and_continuation(variant):
+    B, H, T, T1 = 2, 2, 300, 130
+    d = I.make_inputs(B, H, T, 64, 64, seed=31, io_dtype="bf16", per_column_beta=True)
+    S0 = I.random_state((B, H, 64, 64), seed=32)
+    O_ref, S_ref = oracle_forward(variant, d, S0=S0)
+    dd = to_dev(d)
+    o, S_T = _run("chunked", dd, variant, S0=S0.cuda())
+    torch.cuda.synchronize()
+    check(o, S_T, O_ref, S_ref, TOL["bf16"], f"{variant} carried S0")
+    first = {k: v[:, :, :T1].contiguous() for k, v in dd.items()}
+    second = {k: v[:, :, T1:].contiguous() for k, v in dd.items()}
+    o1, S1 = _run("chunked", first, variant, S0=S0.cuda())
+    kp = dd["phi_k"][:, :, T1 - 1].contiguous()
+    o2, S2 = _run("chunked", second, variant, S0=S1, k_prev=kp)
+    torch.cuda.synchronize()
+    check(torch.cat([o1, o2], dim=2), S2, O_ref, S_ref, TOL["bf16"], f"{variant} split")
+
+
+def test_per_column_clamp_active():
+    """Large gains and ridge weights with small keys drive the per-column decay
+    onto its positive clamp."""
+    B, H, T = 1, 2, 200
+    d = I.make_inputs(B, H, T, 64, 64, seed=33, io_dtype="bf16", per_column_beta=True,
+                      feature_scale=0.05)
+    d["beta"] = 1.0 + 0.9 * torch.rand(d["beta"].shape, generator=torch.Generator().manual_seed(34))
+    d["lam"] = torch.full_like(d["lam"], 5.0)
+    O_ref, S_ref = oracle_forward("falcon2", d, eps_gamma=1e-3)
+    o, S_T = _run("chunked", to_dev(d), "falcon2", eps_gamma=1e-3)
+    torch.cuda.synchronize()
+    check(o, S_T, O_ref, S_ref, TOL["bf16"], "falcon2 clamp")
+
+
 # ---- decode ------------------------------------------------------------------
 
 @pytest.mark.parametrize("variant", ["falcon1", "falcon1a", "falcon2", "falcon2a"])
