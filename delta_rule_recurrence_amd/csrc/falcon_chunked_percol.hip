@@ -43,11 +43,9 @@ struct PcSmem {
   uint16_t q[kC * kD];            // queries, swizzled rows
   float kq[kC][4][16];            // x_i.x_s at [i][s % 4][s / 4] for s < i, else 0
   float pq[kC][4][16];            // q_i.x_s at [i][s % 4][s / 4] for s <= i, else 0
-  float xs[kC][kSlice];           // (X S)_{i,j}
-  float qs[kC][kSlice];           // (Q S)_{i,j}
-  float vv[kC][kSlice];           // v_{i,j}
-  float bb[kC][kSlice];           // beta_{i,j}
-  float os[kC][kSlice];           // o_{i,j} before the bf16 store
+  // per row i and column j: first {v, beta, (X S), (Q S)}, then, in place,
+  // {rhs a, eta, gamma, e^{g_i} (Q S)}, and after the rows o_{i,j} in .x
+  f32x4 rp[kC][kSlice];
   float en[kC];                   // ||x_i||^2
   float lm[kC];                   // lam_i
   uint16_t ut[kSlice][kC];        // e^{g_63-g_s} rho_s per column, bf16, [j][s]
@@ -60,48 +58,52 @@ __device__ __forceinline__ float quad_sum(float v) {
   return v;
 }
 
-struct RowCtx {
-  PcSmem& sm;
-  int t0, T, jc, qq;
-  bool fresh;
-  float eps, eps_gamma;
-};
-
 // Row I of one chunk for the lane's column (unrolled by recursion, so every
-// bound and register index is a compile-time constant).  u[k] holds
-// e^{g_{I-1}-g_s} rho_s for s = 4k + qq < I on entry and e^{g_I-g_s} rho_s for
-// s <= I on exit; eprev holds e^{g_{I-1}} on entry and e^{g_I} on exit.
+// bound and register index is a compile-time constant; the loop body reads
+// LDS only, so the compiler is free to fetch later rows early).  On entry
+// u[k] holds e^{g_{I-1}-g_s} rho_s for s = 4k + qq < I, on exit
+// e^{g_I-g_s} rho_s for s <= I.  Row I's output is kept by the lane that owns
+// s = I, in ov[I / 4].
 template <bool kReg, int I>
-__device__ __forceinline__ void solve_rows(RowCtx& cx, float (&u)[16], float& eprev) {
+__device__ __forceinline__ void solve_rows(const PcSmem& sm, int jc, int qq, float (&u)[16], float (&ov)[16]) {
   if constexpr (I < kC) {
-    PcSmem& sm = cx.sm;
-    const int t = cx.t0 + I;
-    const float en = sm.en[I], lmi = sm.lm[I];
-    const bool live = t < cx.T;
-    const float eta = live ? nlms_eta(sm.bb[I][cx.jc], en, lmi, cx.eps, cx.fresh && t == 0) : 0.0f;
-    const float gam = live ? clamped_gamma(eta, lmi, cx.eps_gamma) : 1.0f;
-    float rho;
+    const f32x4 p = sm.rp[I][jc];                  // a_I, eta_I, gamma_I, e^{g_I} (Q S)_I
+    float rho = p[0];
     if constexpr (kReg) {
       float dk = 0.f;
 #pragma unroll
-      for (int k = 0; 4 * k < I; ++k) dk = fmaf(sm.kq[I][cx.qq][k], u[k], dk);
-      dk = quad_sum(dk);
-      rho = eta * (sm.vv[I][cx.jc] - eprev * sm.xs[I][cx.jc] - dk);
-    } else {
-      rho = eta * sm.vv[I][cx.jc];
+      for (int k = 0; 4 * k < I; ++k) dk = fmaf(sm.kq[I][qq][k], u[k], dk);
+      rho = fmaf(-p[1], quad_sum(dk), rho);
     }
 #pragma unroll
-    for (int k = 0; 4 * k < I; ++k) u[k] *= gam;
-    if (cx.qq == (I & 3)) u[I >> 2] = rho;
-    const float ecur = eprev * gam;
+    for (int k = 0; 4 * k < I; ++k) u[k] *= p[2];
+    const bool own = qq == (I & 3);
+    if (own) u[I >> 2] = rho;
     float dp = 0.f;
 #pragma unroll
-    for (int k = 0; 4 * k <= I; ++k) dp = fmaf(sm.pq[I][cx.qq][k], u[k], dp);
+    for (int k = 0; 4 * k <= I; ++k) dp = fmaf(sm.pq[I][qq][k], u[k], dp);
     dp = quad_sum(dp);
-    if (cx.qq == 0) sm.os[I][cx.jc] = ecur * sm.qs[I][cx.jc] + dp;
-    eprev = ecur;
-    solve_rows<kReg, I + 1>(cx, u, eprev);
+    if (own) ov[I >> 2] = p[3] + dp;
+    solve_rows<kReg, I + 1>(sm, jc, qq, u, ov);
   }
+}
+
+// Inclusive product over the 64 lanes of a wave (DPP shifts within 16-lane
+// rows, then the row totals carried across rows).
+__device__ __forceinline__ float lane_prefix_product(float v, int g) {
+#pragma unroll
+  for (int sh = 1; sh < 16; sh <<= 1) {
+    float w;
+    switch (sh) {
+      case 1: w = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, 1.0f), __builtin_bit_cast(int, v), 0x111, 0xf, 0xf, false)); break;
+      case 2: w = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, 1.0f), __builtin_bit_cast(int, v), 0x112, 0xf, 0xf, false)); break;
+      case 4: w = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, 1.0f), __builtin_bit_cast(int, v), 0x114, 0xf, 0xf, false)); break;
+      default: w = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, 1.0f), __builtin_bit_cast(int, v), 0x118, 0xf, 0xf, false)); break;
+    }
+    v *= w;
+  }
+  const float r0 = lane_value(v, 15), r1 = lane_value(v, 31), r2 = lane_value(v, 47);
+  return v * (g >= 1 ? r0 : 1.0f) * (g >= 2 ? r1 : 1.0f) * (g >= 3 ? r2 : 1.0f);
 }
 
 template <bool kReg>
@@ -188,14 +190,15 @@ falcon2_chunked_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restric
       const bf16x8 va = *reinterpret_cast<const bf16x8*>(V + int64_t(tok) * kD + j0);
       const bf16x8 vb = *reinterpret_cast<const bf16x8*>(V + int64_t(tok) * kD + j0 + 8);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        sm.vv[l][e] = static_cast<float>(va[e]);
-        sm.vv[l][8 + e] = static_cast<float>(vb[e]);
-      }
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const f32x4 bt = *reinterpret_cast<const f32x4*>(Bt + int64_t(tok) * kD + j0 + 4 * e4);
 #pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4)
-        *reinterpret_cast<f32x4*>(&sm.bb[l][4 * e4]) =
-            *reinterpret_cast<const f32x4*>(Bt + int64_t(tok) * kD + j0 + 4 * e4);
+        for (int e = 0; e < 4; ++e) {
+          const int j = 4 * e4 + e;
+          sm.rp[l][j][0] = static_cast<float>(j < 8 ? va[j] : vb[j - 8]);
+          sm.rp[l][j][1] = bt[e];
+        }
+      }
     }
     // ---- shared products on the matrix cores -----------------------------
     // Gram and read tiles (ib, sb), sb <= ib: lane holds rows i = 16ib+4g+r,
@@ -236,25 +239,50 @@ falcon2_chunked_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restric
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          sm.qs[16 * ib + 4 * g + r][c16] = aq[r];
-          if (kReg) sm.xs[16 * ib + 4 * g + r][c16] = ax[r];
+          sm.rp[16 * ib + 4 * g + r][c16][3] = aq[r];
+          if (kReg) sm.rp[16 * ib + 4 * g + r][c16][2] = ax[r];
         }
       }
     }
+    // ---- per row and column: step sizes, decays, right-hand sides ---------
+    // lane l owns row i = l; e^{g_{i,j}} is the product of the row decays
+    {
+      const int t = t0 + l;
+      const bool live = t < T;
+      const float en = sm.en[l], lmi = sm.lm[l];
+      const float den = en + lmi + eps;
+      const float inv = (live && !(fresh && t == 0) && den != 0.0f) ? 1.0f / den : 0.0f;
+#pragma unroll 4
+      for (int j = 0; j < kSlice; ++j) {
+        const f32x4 in = sm.rp[l][j];                // v, beta, (X S), (Q S)
+        const float eta = in[1] * inv;
+        const float gam = live ? clamped_gamma(eta, lmi, eps_gamma) : 1.0f;
+        const float e_inc = lane_prefix_product(gam, g);
+        float e_exc = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+            __builtin_bit_cast(int, 1.0f), __builtin_bit_cast(int, e_inc), 0x111, 0xf, 0xf, false));
+        {
+          const float c15 = lane_value(e_inc, 15), c31 = lane_value(e_inc, 31), c47 = lane_value(e_inc, 47);
+          if (c16 == 0) e_exc = g == 0 ? 1.0f : g == 1 ? c15 : g == 2 ? c31 : c47;
+        }
+        const float a = kReg ? eta * (in[0] - e_exc * in[2]) : eta * in[0];
+        sm.rp[l][j] = f32x4{a, eta, gam, e_inc * in[3]};
+        if (l == 63) sm.e63[j] = e_inc;
+      }
+    }
     // ---- per-column rows: residual system, weights, outputs --------------
-    float u[16];
+    float u[16], ov[16];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) u[k] = 0.f;
-    float eprev = 1.f;                               // e^{g_{i-1,j}}
-    RowCtx ctx{sm, t0, T, jc, qq, fresh, eps, eps_gamma};
-    solve_rows<kReg, 0>(ctx, u, eprev);
+    for (int k = 0; k < 16; ++k) { u[k] = 0.f; ov[k] = 0.f; }
+    solve_rows<kReg, 0>(sm, jc, qq, u, ov);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) sm.rp[4 * k + qq][jc][0] = ov[k];
     // ---- outputs (row l of the slice) and the state update -----------------
     {
       const int tok = t0 + l;
       if (tok < T) {
         uint32_t w[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) w[e] = pack_bf16x2(sm.os[l][2 * e], sm.os[l][2 * e + 1]);
+        for (int e = 0; e < 8; ++e) w[e] = pack_bf16x2(sm.rp[l][2 * e][0], sm.rp[l][2 * e + 1][0]);
         uint4* dst = reinterpret_cast<uint4*>(o + (bh * T + tok) * kD + j0);
         dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
         dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
@@ -262,7 +290,6 @@ falcon2_chunked_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restric
     }
 #pragma unroll
     for (int k = 0; k < 16; ++k) sm.ut[jc][4 * k + qq] = bf(u[k]);
-    if (qq == 0) sm.e63[jc] = eprev;
     {
       const float dec = sm.e63[c16];
       const bf16x8 u0 = frag_lds(&sm.ut[c16][0], 0, g);
