@@ -1,15 +1,16 @@
-// Chunked-forward dispatch: the fused MFMA kernel where it applies (Falcon-1,
-// bf16 I/O, dk = dv = 64, C = 64), the chunk-tile look-back kernel for
-// Falcon-1A with the same shapes, the per-column kernel for Falcon-2 / 2A
-// with the same shapes, the general float32 kernel otherwise.
+// Chunked-forward dispatch for bf16 I/O with dk = dv = 64 and C = 64: the
+// two-launch WY + chain path for Falcon-1, the chunk-tile path for Falcon-1A,
+// the per-column path for Falcon-2 / 2A; the general float32 kernel for every
+// other case.
 #include "falcon_device.h"
 #include "falcon_launch.h"
 
 namespace falcon {
 
 hipError_t launch_chunked_generic(const ProblemArgs& a, hipStream_t st);
-bool chunked_mfma_applies(const ProblemArgs& a);
-hipError_t launch_chunked_mfma(const ProblemArgs& a, hipStream_t st);
+bool chunked_wy_applies(const ProblemArgs& a);
+size_t chunked_wy_workspace_bytes(const ProblemArgs& a);
+hipError_t launch_chunked_wy(const ProblemArgs& a, hipStream_t st);
 bool chunked_scan_applies(const ProblemArgs& a);
 size_t chunked_scan_workspace_bytes(const ProblemArgs& a);
 hipError_t launch_chunked_scan(const ProblemArgs& a, hipStream_t st);
@@ -17,11 +18,12 @@ bool chunked_percol_applies(const ProblemArgs& a);
 hipError_t launch_chunked_percol(const ProblemArgs& a, hipStream_t st);
 
 size_t chunked_workspace_bytes(const ProblemArgs& a) {
+  if (chunked_wy_applies(a)) return chunked_wy_workspace_bytes(a);
   return chunked_scan_applies(a) ? chunked_scan_workspace_bytes(a) : 0;
 }
 
 hipError_t launch_chunked(const ProblemArgs& a, hipStream_t st) {
-  if (chunked_mfma_applies(a)) return launch_chunked_mfma(a, st);
+  if (chunked_wy_applies(a)) return launch_chunked_wy(a, st);
   if (chunked_scan_applies(a)) return launch_chunked_scan(a, st);
   if (chunked_percol_applies(a)) return launch_chunked_percol(a, st);
   return launch_chunked_generic(a, st);

@@ -1,7 +1,7 @@
 // Chunk-parallel Falcon forward, general-shape float32 kernel (gfx950).
 //
-// Serves every (variant, dtype, dk, dv, C) combination; the bf16 Falcon-1
-// path with dk = dv = 64 has its own MFMA kernel (falcon_chunked_mfma.hip).
+// Serves every (variant, dtype, dk, dv, C) combination that has no MFMA path
+// (the bf16 cases with dk = dv = 64 and C = 64 have their own kernels).
 // All arithmetic is float32 on the vector ALUs; intermediates live in LDS.
 //
 // Chunk algebra (derived from the Section 4 summary rules with the chunk-

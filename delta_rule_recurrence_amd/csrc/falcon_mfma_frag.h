@@ -190,5 +190,57 @@ __device__ __forceinline__ void chunk_gates(const bf16x8 (&x)[8], float beta, fl
   glast = lane_value(gi, 63);
 }
 
+// Column elimination for a unit lower-triangular 16x16 block: lane j holds
+// column j of the negated strictly-lower part (ncol[i] = -A[i][j]) and of
+// the inverse (t[i]).  Step S adds -A[i][S] t[S] to every row i > S, the
+// factor broadcast from lane S of the 16-lane row by the multiply-add's own
+// DPP source modifier (row_newbcast).  Each statement starts with two wait
+// states, which covers the DPP read-after-VALU-write hazard on its sources.
+#define FALCON_FMAC(D, A, S) "v_fmac_f32_dpp %" #D ", %" #A ", %" #S
+#define FALCON_BCAST(N) " row_newbcast:" #N " row_mask:0xf bank_mask:0xf\n\t"
+#define ELIM4(S, I)                                                                     \
+  asm volatile("s_nop 1\n\t" FALCON_FMAC(0, 4, 8) FALCON_BCAST(S) FALCON_FMAC(1, 5, 8)   \
+               FALCON_BCAST(S) FALCON_FMAC(2, 6, 8) FALCON_BCAST(S) FALCON_FMAC(3, 7, 8)   \
+               FALCON_BCAST(S)                                                          \
+               : "+v"(t[I]), "+v"(t[I + 1]), "+v"(t[I + 2]), "+v"(t[I + 3])              \
+               : "v"(ncol[I]), "v"(ncol[I + 1]), "v"(ncol[I + 2]), "v"(ncol[I + 3]), "v"(t[S]))
+#define ELIM3(S, I)                                                                     \
+  asm volatile("s_nop 1\n\t" FALCON_FMAC(0, 3, 6) FALCON_BCAST(S) FALCON_FMAC(1, 4, 6)   \
+               FALCON_BCAST(S) FALCON_FMAC(2, 5, 6) FALCON_BCAST(S)                      \
+               : "+v"(t[I]), "+v"(t[I + 1]), "+v"(t[I + 2])                              \
+               : "v"(ncol[I]), "v"(ncol[I + 1]), "v"(ncol[I + 2]), "v"(t[S]))
+#define ELIM2(S, I)                                                                     \
+  asm volatile("s_nop 1\n\t" FALCON_FMAC(0, 2, 4) FALCON_BCAST(S) FALCON_FMAC(1, 3, 4)   \
+               FALCON_BCAST(S)                                                          \
+               : "+v"(t[I]), "+v"(t[I + 1])                                             \
+               : "v"(ncol[I]), "v"(ncol[I + 1]), "v"(t[S]))
+#define ELIM1(S, I)                                                                     \
+  asm volatile("s_nop 1\n\t" FALCON_FMAC(0, 1, 2) FALCON_BCAST(S)                        \
+               : "+v"(t[I]) : "v"(ncol[I]), "v"(t[S]))
+
+__device__ __forceinline__ void eliminate16(float (&t)[16], const float (&ncol)[16]) {
+  ELIM4(0, 1); ELIM4(0, 5); ELIM4(0, 9); ELIM3(0, 13);
+  ELIM4(1, 2); ELIM4(1, 6); ELIM4(1, 10); ELIM2(1, 14);
+  ELIM4(2, 3); ELIM4(2, 7); ELIM4(2, 11); ELIM1(2, 15);
+  ELIM4(3, 4); ELIM4(3, 8); ELIM4(3, 12);
+  ELIM4(4, 5); ELIM4(4, 9); ELIM3(4, 13);
+  ELIM4(5, 6); ELIM4(5, 10); ELIM2(5, 14);
+  ELIM4(6, 7); ELIM4(6, 11); ELIM1(6, 15);
+  ELIM4(7, 8); ELIM4(7, 12);
+  ELIM4(8, 9); ELIM3(8, 13);
+  ELIM4(9, 10); ELIM2(9, 14);
+  ELIM4(10, 11); ELIM1(10, 15);
+  ELIM4(11, 12);
+  ELIM3(12, 13);
+  ELIM2(13, 14);
+  ELIM1(14, 15);
+}
+#undef ELIM4
+#undef ELIM3
+#undef ELIM2
+#undef ELIM1
+#undef FALCON_BCAST
+#undef FALCON_FMAC
+
 }  // namespace frag
 }  // namespace falcon
