@@ -4,15 +4,20 @@
 // The chunk form (the log-space renormalisation of Section 4.4 with window 1,
 // applied per chunk; g_i the chunk-local prefix of log gamma):
 //   A_{i,s} = eta_i e^{g_{i-1}-g_s} (x_i . x_s) for s < i,   T = (I + A)^{-1}
-//   W = T Diag(eta e^{g_{s-1}}) X,   U = T Diag(eta) V
-//   R = U - W S,   S' = e^{g_63} S + (Diag(e^{g_63-g}) X)^T R
-//   O = Diag(e^g) Q S + (tril0(Q X^T) o [e^{g_i-g_s}]) R.
+//   W = T Diag(eta e^{g_{s-1}}) X,   U = T Diag(eta) V,   R = U - W S
+//   S' = e^{g_63} S + Xh^T R,   Xh = Diag(e^{g_63-g}) X
+//   O = Diag(e^g) Q S + M R,    M = tril0(Q X^T) o [e^{g_i-g_s}].
 // W and U depend only on the chunk's own keys, values and gates (the "WY"
-// factors of Section 4.2's chunk-parallel implementation).  They are built
-// for every chunk of every sequence at once (launch 1, one workgroup per
-// chunk, the whole chip busy) and written to the workspace in MFMA fragment
-// order; launch 2 then runs the short sequential part, the state passing and
-// the outputs, one workgroup per sequence, streaming the factors back.
+// factors of Section 4.2's chunk-parallel implementation), and so do the
+// products that carry S through the chunk.  Substituting R:
+//   S' = e^{g_63} S + K S + H,   K = -Xh^T W,   H = Xh^T U
+//   O  = Qt S + Ot,              Qt = Diag(e^g) Q - M W,   Ot = M U.
+// Launch 1 builds K, H, Qt and Ot for every chunk of every sequence at once
+// (one workgroup per chunk, the whole chip busy) and writes them to the
+// workspace in MFMA operand order.  Launch 2 runs the short sequential part:
+// per chunk, one 64x64x64 product for the state and one for the outputs,
+// streaming the chunk matrices back.  The state is rounded to bf16 only as
+// the operand of K S and Qt S; its decay term stays in float32.
 
 #include "falcon_device.h"
 #include "falcon_launch.h"
@@ -27,12 +32,13 @@ using namespace frag;
 constexpr int kC = 64;
 constexpr int kD = 64;
 constexpr int kP = 72;                  // bf16 row pitch of T in LDS
-// Per-chunk factor block in the workspace: -W fragments, U tiles and the
-// decayed keys (8 KiB each, bf16), then the chunk's gates (1 KiB, float).
-constexpr int kFactorBytes = 25600;
-constexpr int kFacU = 4096;             // bf16 element offsets of the parts
-constexpr int kFacXh = 8192;
-constexpr int kFacGates = 12288;        // float gates: g_s [64], g_i at [c16*4+ib] [64], e^{g_i} same order [64], e^{g_63}
+// Per-chunk block in the workspace (bf16 element offsets), 32 KiB:
+constexpr int kBlockElems = 16384;
+constexpr int kOutK = 0;                // K as A fragments [fb][m][lane][8]
+constexpr int kOutQt = 4096;            // Qt as B fragments [ib][m][lane][8]
+constexpr int kOutH = 8192;             // H as result tiles [cb][fb][lane][4]
+constexpr int kOutOt = 12288;           // Ot^T as result tiles [cb][ib][lane][4]
+// followed, after all blocks, by e^{g_63} of every chunk (float).
 constexpr int kSpinLimit = 1 << 22;
 
 struct Seq {
@@ -72,7 +78,12 @@ __device__ __forceinline__ const bf16_t* token_row(const bf16_t* base, const Seq
 }
 
 // ============================================================================
-// Launch 1: WY factors of one chunk per workgroup (four waves).
+// Launch 1: chunk matrices, one chunk per workgroup (four waves).
+//
+// "frag(Z)[b][m]" below is the operand fragment of row block b of a matrix Z
+// with k = 32 m + kperm: lane l holds Z[16 b + (l & 15)][32 m + kperm(l >> 4, e)].
+// A product of frag(P) and frag(Q) gives the tile P Q^T; two such tiles
+// stacked over consecutive row blocks of P are frag(Q P^T).
 // ============================================================================
 
 struct WyGates {
@@ -85,8 +96,11 @@ struct WyGates {
 };
 
 struct WySmem {
-  uint16_t x[kC * kD];            // keys, swizzled rows
-  uint16_t v[kC * kD];            // values, swizzled rows
+  uint16_t x[kC * kD];            // keys (swizzled rows); then frag(-W^T) [fb][m][lane][8]
+  uint16_t v[kC * kD];            // values (swizzled rows); then frag(U^T) [cb][m][lane][8]
+  uint16_t q[kC * kD];            // queries (swizzled rows)
+  uint16_t xh[kC * kD];           // frag(Xh^T) [fb][m][lane][8]
+  uint16_t mf[kC * kD];           // frag(M) [ib][m][lane][8]
   uint16_t tb[kC * kP];           // T, row-major
   float abt[4][16][16];           // diagonal blocks of -A: [b][s][i] = -A[16b+i][16b+s]
   WyGates G;
@@ -189,33 +203,32 @@ __device__ __forceinline__ void build_inverse(WySmem& sm, int l) {
   }
 }
 
-// Workspace block of one chunk: -W as A fragments [ib][m][lane][8] (lane row =
-// token 16 ib + c16, k = features 32 m + kperm), U as result tiles
-// [ib][cb][lane][4] (lane holds U[16ib+4g+r][16cb+c16]), the decayed keys
-// (Diag(e^{g_63-g}) X)^T as A fragments [fb][m][lane][8] (lane row = feature
-// 16 fb + c16, k = tokens 32 m + kperm), all bf16, then the gates in float.
+// Fragment slot [b][m] of a 64x64 fragment array.
+__device__ __forceinline__ int fslot(int b, int m, int l) { return ((b * 2 + m) * 64 + l) * 8; }
+
 __global__ void __launch_bounds__(256, 2)
-falcon1_wy_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restrict__ v,
-                  const float* __restrict__ beta, const float* __restrict__ lam,
-                  const bf16_t* __restrict__ k_prev, uint16_t* __restrict__ factors, int T, int nchunks,
-                  float eps, float eps_gamma) {
+falcon1_wy_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restrict__ phi_q,
+                  const bf16_t* __restrict__ v, const float* __restrict__ beta, const float* __restrict__ lam,
+                  const bf16_t* __restrict__ k_prev, uint16_t* __restrict__ blocks, float* __restrict__ decay63,
+                  int T, int nchunks, float eps, float eps_gamma) {
   __shared__ WySmem sm;
   const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;   // wave-uniform, so role branches are scalar
   const int g = l >> 4, c16 = l & 15;
   const int64_t bh = blockIdx.x / nchunks;
   const int c = blockIdx.x % nchunks;
-  const Seq sq = make_seq(phi_k, nullptr, v, beta, lam, k_prev, bh, T);
+  const Seq sq = make_seq(phi_k, phi_q, v, beta, lam, k_prev, bh, T);
   const bool fresh = (k_prev == nullptr);
-  uint16_t* out = factors + int64_t(blockIdx.x) * (kFactorBytes / 2);
+  uint16_t* out = blocks + int64_t(blockIdx.x) * kBlockElems;
 
-  // ---- stage keys and values: wave w rows 16w..16w+15, 8 lanes per row -----
+  // ---- stage keys, values and queries: wave w rows 16w..16w+15 -------------
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int r = 16 * w + 8 * j + (l >> 3);
     const int off = r * kD + 8 * seg_pos(r, l & 7);
     *reinterpret_cast<bf16x8*>(sm.x + off) = *reinterpret_cast<const bf16x8*>(key_row(sq, c, r) + 8 * (l & 7));
     *reinterpret_cast<bf16x8*>(sm.v + off) = *reinterpret_cast<const bf16x8*>(token_row(sq.V, sq, c, r) + 8 * (l & 7));
+    *reinterpret_cast<bf16x8*>(sm.q + off) = *reinterpret_cast<const bf16x8*>(token_row(sq.Q, sq, c, r) + 8 * (l & 7));
   }
   // T's upper blocks are never written
   for (int e = tid; e < kC * kP / 2; e += 256) reinterpret_cast<uint32_t*>(sm.tb)[e] = 0u;
@@ -237,21 +250,19 @@ falcon1_wy_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restrict__ v
     sm.G.eta[l] = eta;
     sm.G.eta_t[c16 * 4 + g] = eta;
     sm.G.gprev_t[c16 * 4 + g] = gprev;
-    float* gout = reinterpret_cast<float*>(out + kFacGates);
-    gout[l] = gi;
-    gout[64 + c16 * 4 + g] = gi;
-    gout[128 + c16 * 4 + g] = __expf(gi);
-    gout[192 + l] = __expf(glast);
+    if (l == 0) decay63[blockIdx.x] = __expf(glast);
   }
   __syncthreads();
-  bf16x8 xg[2][2];              // waves 1, 2: (Diag(eta e^{g_{s-1}}) X)^T for key blocks 2(w-1), 2(w-1)+1
-  bf16x8 vt[4][2];              // wave 3: Diag(eta) V for value blocks 0..3, as B fragments
+  // ---- T, scaled key transposes, value transposes, read mask ----------------
+  bf16x8 xg[2][2];              // waves 1, 2: frag((Diag(eta e^{g_{s-1}}) X)^T) for fb = 2(w-1) + h
+  bf16x8 vt[4][2];              // wave 3: frag((Diag(eta) V)^T) for all cb
   if (w == 0) {
     build_inverse(sm, l);
   } else if (w <= 2) {
     const int mk = w - 1;       // feature half
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+      // tile sb: lane holds X[16sb+4g+r][32mk+16h+c16]
       const bf16x8 sel = select_frag(h, g, c16);
       f32x4 d[4];
 #pragma unroll
@@ -259,8 +270,8 @@ falcon1_wy_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restrict__ v
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         xg[h][m] = frag_acc(d[2 * m] * ld4(&sm.G.sxg[32 * m + 4 * g]), d[2 * m + 1] * ld4(&sm.G.sxg[32 * m + 16 + 4 * g]));
-        *reinterpret_cast<bf16x8*>(out + kFacXh + (((2 * mk + h) * 2 + m) * 64 + l) * 8) =
-            frag_acc(d[2 * m] * ld4(&sm.G.sxh[32 * m + 4 * g]), d[2 * m + 1] * ld4(&sm.G.sxh[32 * m + 16 + 4 * g]));
+        store_frag(&sm.xh[fslot(2 * mk + h, m, l)],
+                   frag_acc(d[2 * m] * ld4(&sm.G.sxh[32 * m + 4 * g]), d[2 * m + 1] * ld4(&sm.G.sxh[32 * m + 16 + 4 * g])));
       }
     }
   } else {
@@ -274,84 +285,161 @@ falcon1_wy_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restrict__ v
       for (int m = 0; m < 2; ++m)
         vt[cb][m] = frag_acc(d[2 * m] * ld4(&sm.G.eta[32 * m + 4 * g]), d[2 * m + 1] * ld4(&sm.G.eta[32 * m + 16 + 4 * g]));
     }
-  }
-  __syncthreads();                                           // T complete
-  if (w == 0) return;
-  bf16x8 tf[4][2];
+    // M: tile (ib, sb) of X Q^T holds M[16ib+c16][16sb+4g+r] after the decay
+    // and the causal mask (s <= i); tiles sb = 2m, 2m+1 stack into frag(M)[ib][m]
 #pragma unroll
-  for (int ib = 0; ib < 4; ++ib) {
-    tf[ib][0] = frag_lds(&sm.tb[(16 * ib + c16) * kP], 0, g);
-    tf[ib][1] = frag_lds(&sm.tb[(16 * ib + c16) * kP], 32, g);
+    for (int n = 0; n < 10; ++n) {
+      int ib, sb;
+      lower_tile(n, ib, sb);
+      f32x4 acc = mfma32(ring_frag_c(sm.x, 16 * sb + c16, 0, g), ring_frag_c(sm.q, 16 * ib + c16, 0, g), zero4());
+      acc = mfma32(ring_frag_c(sm.x, 16 * sb + c16, 1, g), ring_frag_c(sm.q, 16 * ib + c16, 1, g), acc);
+      const f32x4 gs = ld4(&sm.G.graw[16 * sb + 4 * g]);
+      const float gi = sm.G.graw[16 * ib + c16];
+      const int i = 16 * ib + c16;
+      f32x4 mv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mv[r] = 16 * sb + 4 * g + r <= i ? __expf(gi - gs[r]) * acc[r] : 0.0f;
+      store_half(&sm.mf[fslot(ib, sb >> 1, l) + 4 * (sb & 1)], mv);
+    }
+    // the two half fragments above the diagonal that are read
+    store_half(&sm.mf[fslot(0, 0, l) + 4], zero4());
+    store_half(&sm.mf[fslot(2, 1, l) + 4], zero4());
   }
-  if (w <= 2) {
-    // -W^T tiles (fb, ib) for fb = 2m, 2m+1 stack into the A fragment (ib, m)
-    const int m = w - 1;
+  __syncthreads();                                           // T, Xh, M complete; x and v free
+  // ---- W and U as fragments over tokens --------------------------------------
+  if (w >= 1) {
+    bf16x8 tf[4][2];
 #pragma unroll
     for (int ib = 0; ib < 4; ++ib) {
-      f32x4 d0 = mfma32(xg[0][0], tf[ib][0], zero4());
-      f32x4 d1 = mfma32(xg[1][0], tf[ib][0], zero4());
-      if (ib >= 2) {                                          // T is lower triangular
-        d0 = mfma32(xg[0][1], tf[ib][1], d0);
-        d1 = mfma32(xg[1][1], tf[ib][1], d1);
-      }
-      *reinterpret_cast<bf16x8*>(out + ((ib * 2 + m) * 64 + l) * 8) = frag_acc(-d0, -d1);
+      tf[ib][0] = frag_lds(&sm.tb[(16 * ib + c16) * kP], 0, g);
+      tf[ib][1] = frag_lds(&sm.tb[(16 * ib + c16) * kP], 32, g);
     }
-  } else {
-    uint16_t* uo = out + kFacU;
+    if (w <= 2) {
+      // tile (ib, fb) = T (Diag(eta e^{g_{s-1}}) X): lane holds W[16ib+4g+r][16fb+c16];
+      // tiles ib = 2m, 2m+1 stack into frag(W^T)[fb][m] (stored negated)
 #pragma unroll
-    for (int ib = 0; ib < 4; ++ib)
+      for (int h = 0; h < 2; ++h) {
+        const int fb = 2 * (w - 1) + h;
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        f32x4 u = mfma32(tf[ib][0], vt[cb][0], zero4());
-        if (ib >= 2) u = mfma32(tf[ib][1], vt[cb][1], u);
-        store_half(uo + ((ib * 4 + cb) * 64 + l) * 4, u);
+        for (int m = 0; m < 2; ++m) {
+          f32x4 d0 = mfma32(tf[2 * m][0], xg[h][0], zero4());
+          f32x4 d1 = mfma32(tf[2 * m + 1][0], xg[h][0], zero4());
+          if (m == 1) {                                       // T is lower triangular
+            d0 = mfma32(tf[2 * m][1], xg[h][1], d0);
+            d1 = mfma32(tf[2 * m + 1][1], xg[h][1], d1);
+          }
+          store_frag(&sm.x[fslot(fb, m, l)], frag_acc(-d0, -d1));
+        }
       }
+    } else {
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          f32x4 d0 = mfma32(tf[2 * m][0], vt[cb][0], zero4());
+          f32x4 d1 = mfma32(tf[2 * m + 1][0], vt[cb][0], zero4());
+          if (m == 1) {
+            d0 = mfma32(tf[2 * m][1], vt[cb][1], d0);
+            d1 = mfma32(tf[2 * m + 1][1], vt[cb][1], d1);
+          }
+          store_frag(&sm.v[fslot(cb, m, l)], frag_acc(d0, d1));
+        }
+    }
+  }
+  __syncthreads();                                           // frag(-W^T), frag(U^T) complete
+  // ---- chunk matrices: wave w takes row block w of K, H^T-tiles fb = w, and
+  // token block ib = w of Qt and Ot --------------------------------------------
+  {
+    bf16x8 wt[4][2], ut[4][2];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        wt[b][m] = load_frag(&sm.x[fslot(b, m, l)]);
+        ut[b][m] = load_frag(&sm.v[fslot(b, m, l)]);
+      }
+    const bf16x8 xh0 = load_frag(&sm.xh[fslot(w, 0, l)]);
+    const bf16x8 xh1 = load_frag(&sm.xh[fslot(w, 1, l)]);
+    const bf16x8 mf0 = load_frag(&sm.mf[fslot(w, 0, l)]);
+    const bf16x8 mf1 = w >= 2 ? load_frag(&sm.mf[fslot(w, 1, l)]) : mf0;
+    // K: tile (fb', fb = w) of (-W^T) Xh = K^T; fb' = 2m, 2m+1 stack into frag(K)[w][m]
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      f32x4 t0 = mfma32(wt[2 * m][0], xh0, zero4());
+      t0 = mfma32(wt[2 * m][1], xh1, t0);
+      f32x4 t1 = mfma32(wt[2 * m + 1][0], xh0, zero4());
+      t1 = mfma32(wt[2 * m + 1][1], xh1, t1);
+      store_frag(out + kOutK + fslot(w, m, l), frag_acc(t0, t1));
+    }
+    // H: tile (fb = w, cb) of Xh^T U, lane holds H[16w+4g+r][16cb+c16]
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      f32x4 hacc = mfma32(xh0, ut[cb][0], zero4());
+      hacc = mfma32(xh1, ut[cb][1], hacc);
+      store_half(out + kOutH + ((cb * 4 + w) * 64 + l) * 4, hacc);
+    }
+    // Qt: tile (fb, ib = w) of e^{g_i} Q^T - W^T M^T = Qt^T; fb = 2m, 2m+1 stack into frag(Qt)[w][m]
+    {
+      const int i = 16 * w + c16;
+      const float egi = __expf(sm.G.graw[i]);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        f32x4 t[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int fb = 2 * m + h;
+          // e^{g_i} Q[i][16fb+4g .. +3]
+          const f32x4 qv = load_half(sm.q + i * kD + 8 * seg_pos(i, 2 * fb + (g >> 1)) + 4 * (g & 1));
+          f32x4 acc = qv * egi;
+          acc = mfma32(wt[fb][0], mf0, acc);
+          if (w >= 2) acc = mfma32(wt[fb][1], mf1, acc);
+          t[h] = acc;
+        }
+        store_frag(out + kOutQt + fslot(w, m, l), frag_acc(t[0], t[1]));
+      }
+    }
+    // Ot^T: tile (cb, ib = w) of U^T M^T, lane holds Ot[16w+c16][16cb+4g+r]
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      f32x4 oacc = mfma32(ut[cb][0], mf0, zero4());
+      if (w >= 2) oacc = mfma32(ut[cb][1], mf1, oacc);
+      store_half(out + kOutOt + ((cb * 4 + w) * 64 + l) * 4, oacc);
+    }
   }
 }
 
 // ============================================================================
-// Launch 2: state passing and outputs, one workgroup per sequence.
+// Launch 2: state passing and outputs.
 //
-// Seven waves: s0 stages the keys and queries of chunk c + 1 and s1 its factor
-// block into a 3-entry LDS ring; one mask wave builds the decayed read mask of
-// chunk c into one of two slots; chain waves c0..c3 (value columns
-// 16 w .. 16 w + 15, fp32 state in MFMA result registers) run R = U - W S, the
-// outputs and the state update.  Hand-over is through LDS counters with
-// bounded waits.
+// kSplit workgroups per sequence, each owning 64 / kSplit value columns (the
+// columns of S evolve independently).  kStagers staging waves each fetch every
+// kStagers-th chunk's K, Qt and this workgroup's columns of H and Ot into
+// registers, then into a kRing-entry LDS ring, so that several chunks are in
+// flight from memory at once; the chain waves (16 value columns each, fp32
+// state in MFMA result registers) run S' = e^{g_63} S + K S + H and
+// O = Qt S + Ot.  Hand-over is through LDS counters with bounded waits.
 // ============================================================================
 
-constexpr int kNI = 3;
-constexpr int kNS = 2;
-constexpr int kChainWaves = 4;
-constexpr int kStageWaves = 2;
-constexpr int kMaskWaves = 1;
-constexpr int kChainThreads = 64 * (kStageWaves + kMaskWaves + kChainWaves);
-
-struct ChainEntry {
-  uint16_t x[kC * kD];            // keys, swizzled rows
-  uint16_t q[kC * kD];            // queries, swizzled rows
-  uint16_t fac[kFactorBytes / 2]; // the chunk's factor block (with its gates)
-  __device__ const float* gates() const { return reinterpret_cast<const float*>(fac + kFacGates); }
-};
-
-struct ChainSlot {
-  uint16_t mf[4 * 2 * 64 * 8];    // M^T as B fragments [ib][m][lane][8]
-};
+constexpr int kSplit = 2;
+constexpr int kColWaves = 4 / kSplit;
+constexpr int kStagers = 4;
+constexpr int kRing = 4;
+constexpr int kChainThreads = 64 * (kColWaves + kStagers);
+constexpr int kEntryElems = 8192 + kColWaves * 2048;     // K, Qt, then per chain wave H and Ot
+constexpr int kEntryFrags = kEntryElems / 512;           // 16-byte fragments per lane
 
 struct ChainSmem {
-  ChainEntry in[kNI];
-  ChainSlot slot[kNS];
-  int in_ready[kNI];              // +1 per staging wave when its part of an entry is filled
-  int in_free[kNI];               // +1 per chain wave done with an entry
-  int slot_full[kNS];             // +1 per mask wave when its tiles of a slot are written
-  int slot_free[kNS];             // +1 per chain wave done with a slot
+  uint16_t d[kRing][kEntryElems];
+  float e63[kRing];
+  int in_ready[kRing];            // chunks stored into the entry so far
+  int in_free[kRing];             // +1 per chain wave done with an entry
   int abort_flag;
 };
 
 __device__ __forceinline__ bool wait_at_least(int* flag, int target, int* abort_flag) {
   for (int it = 0; it < kSpinLimit; ++it) {
-    const int v = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    if (__builtin_amdgcn_readfirstlane(v) >= target) {
+    const int val = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (__builtin_amdgcn_readfirstlane(val) >= target) {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
       return true;
     }
@@ -366,128 +454,57 @@ __device__ __forceinline__ void signal_add(int* flag, int l) {
   if (l == 0) __hip_atomic_fetch_add(flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-struct RowRegs {
-  bf16x8 x[8], q[8];
-};
-
-__device__ __forceinline__ void rows_fetch(RowRegs& R, const Seq& sq, int c, int l) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = 8 * j + (l >> 3);
-    R.x[j] = *reinterpret_cast<const bf16x8*>(key_row(sq, c, r) + 8 * (l & 7));
-    R.q[j] = *reinterpret_cast<const bf16x8*>(token_row(sq.Q, sq, c, r) + 8 * (l & 7));
-  }
-}
-
-__device__ __forceinline__ void rows_store(ChainEntry& E, const RowRegs& R, int l) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = 8 * j + (l >> 3);
-    const int off = r * kD + 8 * seg_pos(r, l & 7);
-    *reinterpret_cast<bf16x8*>(E.x + off) = R.x[j];
-    *reinterpret_cast<bf16x8*>(E.q + off) = R.q[j];
-  }
-}
-
-constexpr int kFacFrags = kFactorBytes / 16 / 64;   // 16-byte fragments per lane in a factor block
-
-struct FacRegs {
-  bf16x8 f[kFacFrags];
-};
-
-__device__ __forceinline__ void fac_fetch(FacRegs& R, const uint16_t* fac, int l) {
-#pragma unroll
-  for (int j = 0; j < kFacFrags; ++j) R.f[j] = *reinterpret_cast<const bf16x8*>(fac + (j * 64 + l) * 8);
-}
-__device__ __forceinline__ void fac_store(ChainEntry& E, const FacRegs& R, int l) {
-#pragma unroll
-  for (int j = 0; j < kFacFrags; ++j) *reinterpret_cast<bf16x8*>(E.fac + (j * 64 + l) * 8) = R.f[j];
+// Workspace element offset of ring-entry fragment j for column part `part`.
+__device__ __forceinline__ int entry_src(int j, int part) {
+  constexpr int kParts = 2 * kColWaves;                  // fragments of H (and of Ot) per part
+  if (j < 16) return j * 512;
+  if (j < 16 + kParts) return kOutH + part * kParts * 512 + (j - 16) * 512;
+  return kOutOt + part * kParts * 512 + (j - 16 - kParts) * 512;
 }
 
 __global__ void __launch_bounds__(kChainThreads)
-falcon1_chain_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restrict__ phi_q,
-                     const float* __restrict__ beta, const float* __restrict__ lam, const float* S0,
-                     const bf16_t* __restrict__ k_prev, const uint16_t* __restrict__ factors,
-                     bf16_t* __restrict__ o, float* S_T, int T, float eps, float eps_gamma) {
+falcon1_chain_kernel(const float* S0, const uint16_t* __restrict__ blocks, const float* __restrict__ decay63,
+                     bf16_t* __restrict__ o, float* S_T, int T, int nchunks, int64_t BH) {
   __shared__ ChainSmem sm;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, l = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
   const int g = l >> 4, c16 = l & 15;
-  const int64_t bh = blockIdx.x;
-  const int nchunks = (T + kC - 1) / kC;
-  const Seq sq = make_seq(phi_k, phi_q, nullptr, beta, lam, k_prev, bh, T);
-  const bool fresh = (k_prev == nullptr);
-  const uint16_t* fac_bh = factors + bh * nchunks * (kFactorBytes / 2);
+  // workgroups b and b + 8 (and so on) take the parts of one sequence, so they
+  // share an XCD and its L2
+  const int64_t bh = (int64_t(blockIdx.x) / (8 * kSplit)) * 8 + blockIdx.x % 8;
+  const int part = (blockIdx.x / 8) % kSplit;
+  if (bh >= BH) return;
+  const uint16_t* blk_bh = blocks + bh * nchunks * kBlockElems;
+  const float* e63_bh = decay63 + bh * nchunks;
 
-  // halves of the mask fragments above the diagonal are never written
-  for (int s = 0; s < kNS; ++s)
-    for (int e = tid; e < 4 * 2 * 64 * 8 / 2; e += kChainThreads) reinterpret_cast<uint32_t*>(sm.slot[s].mf)[e] = 0u;
-  if (tid < kNI) { sm.in_ready[tid] = 0; sm.in_free[tid] = 0; }
-  if (tid < kNS) { sm.slot_full[tid] = 0; sm.slot_free[tid] = 0; }
+  if (tid < kRing) { sm.in_ready[tid] = 0; sm.in_free[tid] = 0; }
   if (tid == 0) sm.abort_flag = 0;
   __syncthreads();
 
-  if (wave == 0) {
-    // ---- s0: keys and queries, one chunk ahead ------------------------------
-    RowRegs R;
-    if (nchunks > 0) rows_fetch(R, sq, 0, l);
-    for (int c = 0; c < nchunks; ++c) {
-      const int e = c % kNI;
-      if (!wait_at_least(&sm.in_free[e], kChainWaves * (c / kNI), &sm.abort_flag)) break;
-      rows_store(sm.in[e], R, l);
-      signal_add(&sm.in_ready[e], l);
-      if (c + 1 < nchunks) rows_fetch(R, sq, c + 1, l);
-    }
-    return;
-  }
-  if (wave == 1) {
-    // ---- s1: the chunk's factor block, one chunk ahead ---------------------
-    FacRegs R;
-    if (nchunks > 0) fac_fetch(R, fac_bh, l);
-    for (int c = 0; c < nchunks; ++c) {
-      const int e = c % kNI;
-      if (!wait_at_least(&sm.in_free[e], kChainWaves * (c / kNI), &sm.abort_flag)) break;
-      fac_store(sm.in[e], R, l);
-      signal_add(&sm.in_ready[e], l);
-      if (c + 1 < nchunks) fac_fetch(R, fac_bh + int64_t(c + 1) * (kFactorBytes / 2), l);
-    }
-    return;
-  }
-  if (wave < kStageWaves + kMaskWaves) {
-    // ---- mask waves: decayed read mask, tiles [n0, n0 + 10 / kMaskWaves) -----
-    constexpr int kTiles = 10 / kMaskWaves;
-    const int n0 = kTiles * (wave - kStageWaves);
-    for (int c = 0; c < nchunks; ++c) {
-      const ChainEntry& E = sm.in[c % kNI];
-      ChainSlot& Sl = sm.slot[c % kNS];
-      if (!wait_at_least(&sm.in_ready[c % kNI], kStageWaves * (c / kNI + 1), &sm.abort_flag)) break;
-      if (!wait_at_least(&sm.slot_free[c % kNS], kChainWaves * (c / kNS), &sm.abort_flag)) break;
-      const float* gts = E.gates();
-      const f32x4 gra_i = ld4(&gts[64 + c16 * 4]);
-      // M^T tile (sb, ib) = X_sb Q_ib^T scaled by e^{g_i-g_s}, s <= i
+  if (wave >= kColWaves) {
+    // ---- staging: chunks c = s, s + kStagers, ... -----------------------------
+    const int s = wave - kColWaves;
+    int src[kEntryFrags];
 #pragma unroll
-      for (int nt = 0; nt < kTiles; ++nt) {
-        int ib, sb;
-        lower_tile(n0 + nt, ib, sb);
-        f32x4 acc = mfma32(ring_frag_c(E.x, 16 * sb + c16, 0, g), ring_frag_c(E.q, 16 * ib + c16, 0, g), zero4());
-        acc = mfma32(ring_frag_c(E.x, 16 * sb + c16, 1, g), ring_frag_c(E.q, 16 * ib + c16, 1, g), acc);
-        const f32x4 gs = ld4(&gts[16 * sb + 4 * g]);
-        const float gi_ib = ib == 0 ? gra_i[0] : ib == 1 ? gra_i[1] : ib == 2 ? gra_i[2] : gra_i[3];
-        const int i = 16 * ib + c16;
-        f32x4 mv;
+    for (int j = 0; j < kEntryFrags; ++j) src[j] = entry_src(j, part) + l * 8;
+    for (int c = s; c < nchunks; c += kStagers) {
+      bf16x8 R[kEntryFrags];
+      const uint16_t* blk = blk_bh + int64_t(c) * kBlockElems;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int s_ = 16 * sb + 4 * g + r;
-          mv[r] = s_ <= i ? __expf(gi_ib - gs[r]) * acc[r] : 0.0f;
-        }
-        store_half(&Sl.mf[((ib * 2 + (sb >> 1)) * 64 + l) * 8 + 4 * (sb & 1)], mv);
-      }
-      signal_add(&sm.slot_full[c % kNS], l);
+      for (int j = 0; j < kEntryFrags; ++j) R[j] = load_frag(blk + src[j]);
+      const float e63 = e63_bh[c];
+      const int e = c % kRing;
+      if (!wait_at_least(&sm.in_free[e], kColWaves * (c / kRing), &sm.abort_flag)) break;
+#pragma unroll
+      for (int j = 0; j < kEntryFrags; ++j) store_frag(&sm.d[e][j * 512 + l * 8], R[j]);
+      if (l == 0) sm.e63[e] = e63;
+      signal_add(&sm.in_ready[e], l);
     }
     return;
   }
   // ---- chain waves ------------------------------------------------------------
-  const int cb = wave - kStageWaves - kMaskWaves;            // value columns 16 cb .. 16 cb + 15
+  const int cw = wave;
+  const int cb = part * kColWaves + cw;                      // value columns 16 cb .. 16 cb + 15
   f32x4 S[4];                                                // S[fb]: lane holds S[16fb+4g+r][16cb+c16]
 #pragma unroll
   for (int fb = 0; fb < 4; ++fb)
@@ -496,67 +513,52 @@ falcon1_chain_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restrict_
       S[fb][r] = S0 ? S0[(bh * kD + 16 * fb + 4 * g + r) * kD + 16 * cb + c16] : 0.0f;
   bf16_t* o_bh = o + bh * T * kD;
   for (int c = 0; c < nchunks; ++c) {
-    const ChainEntry& E = sm.in[c % kNI];
-    const ChainSlot& Sl = sm.slot[c % kNS];
-    if (!wait_at_least(&sm.slot_full[c % kNS], kMaskWaves * (c / kNS + 1), &sm.abort_flag)) break;
-    // everything this wave needs from the entry and the slot, into registers
-    bf16x8 wf[4][2], mfr[4][2], xhr[4][2], qf[4][2];
-    f32x4 uf[4];
+    const int e = c % kRing;
+    const uint16_t* D = sm.d[e];
+    if (!wait_at_least(&sm.in_ready[e], c / kRing + 1, &sm.abort_flag)) break;
+    bf16x8 kf[4][2], qf[4][2];
+    f32x4 hf[4], of[4];
 #pragma unroll
-    for (int ib = 0; ib < 4; ++ib) {
+    for (int b = 0; b < 4; ++b) {
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        wf[ib][m] = load_frag(&E.fac[((ib * 2 + m) * 64 + l) * 8]);
-        xhr[ib][m] = load_frag(&E.fac[kFacXh + ((ib * 2 + m) * 64 + l) * 8]);
-        qf[ib][m] = ring_frag_p(E.q, 16 * ib + c16, m, g);
+        kf[b][m] = load_frag(&D[kOutK + fslot(b, m, l)]);
+        qf[b][m] = load_frag(&D[kOutQt + fslot(b, m, l)]);
       }
-      mfr[ib][0] = load_frag(&Sl.mf[((ib * 2 + 0) * 64 + l) * 8]);
-      if (ib >= 2) mfr[ib][1] = load_frag(&Sl.mf[((ib * 2 + 1) * 64 + l) * 8]);
-      uf[ib] = load_half(&E.fac[kFacU + ((ib * 4 + cb) * 64 + l) * 4]);
+      hf[b] = load_half(&D[8192 + cw * 1024 + (b * 64 + l) * 4]);
+      of[b] = load_half(&D[8192 + kColWaves * 1024 + cw * 1024 + (b * 64 + l) * 4]);
     }
-    const f32x4 gexp_i = ld4(&E.gates()[128 + c16 * 4]);
-    const float glast = E.gates()[192];
-    signal_add(&sm.slot_free[c % kNS], l);
-    signal_add(&sm.in_free[c % kNI], l);
-    // R = U - W S (rows eta_i r_i); lane holds R[16ib+4g+r][16cb+c16]
+    const float e63 = sm.e63[e];
+    signal_add(&sm.in_free[e], l);
     const bf16x8 sb0 = frag_acc(S[0], S[1]);
     const bf16x8 sb1 = frag_acc(S[2], S[3]);
-    f32x4 R[4];
+    // S <- e^{g_63} S + K S + H
 #pragma unroll
-    for (int ib = 0; ib < 4; ++ib) {
-      f32x4 u = mfma32(wf[ib][0], sb0, uf[ib]);
-      R[ib] = mfma32(wf[ib][1], sb1, u);
+    for (int fb = 0; fb < 4; ++fb) {
+      f32x4 acc = S[fb] * e63 + hf[fb];
+      acc = mfma32(kf[fb][0], sb0, acc);
+      S[fb] = mfma32(kf[fb][1], sb1, acc);
     }
-    const bf16x8 rb0 = frag_acc(R[0], R[1]);
-    const bf16x8 rb1 = frag_acc(R[2], R[3]);
-    // O^T tiles: e^{g_i} S^T Q^T + R^T M^T; lane holds o[t0+16ib+c16][16cb+4g+r]
+    // O^T tiles: S^T Qt^T + Ot^T; lane holds o[t0+16ib+c16][16cb+4g+r]
     const int t0 = c * kC;
 #pragma unroll
     for (int ib = 0; ib < 4; ++ib) {
-      f32x4 acc = mfma32(sb0, qf[ib][0], zero4());
+      f32x4 acc = mfma32(sb0, qf[ib][0], of[ib]);
       acc = mfma32(sb1, qf[ib][1], acc);
-      acc = acc * gexp_i[ib];
-      acc = mfma32(rb0, mfr[ib][0], acc);
-      if (ib >= 2) acc = mfma32(rb1, mfr[ib][1], acc);
       const int tok = t0 + 16 * ib + c16;
       if (tok < T)
         *reinterpret_cast<uint2*>(o_bh + int64_t(tok) * kD + 16 * cb + 4 * g) =
             make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
     }
-    // S <- e^{g_63} S + (Diag(e^{g_63-g}) X)^T R
-#pragma unroll
-    for (int fb = 0; fb < 4; ++fb) {
-      f32x4 acc = S[fb] * glast;
-      acc = mfma32(xhr[fb][0], rb0, acc);
-      S[fb] = mfma32(xhr[fb][1], rb1, acc);
-    }
   }
+  // a wait that ran out (a hand-over that never came) leaves NaN in S_T
+  const bool aborted = __hip_atomic_load(&sm.abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0;
   if (S_T) {
 #pragma unroll
     for (int fb = 0; fb < 4; ++fb)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        S_T[(bh * kD + 16 * fb + 4 * g + r) * kD + 16 * cb + c16] = S[fb][r];
+        S_T[(bh * kD + 16 * fb + 4 * g + r) * kD + 16 * cb + c16] = aborted ? __builtin_nanf("") : S[fb][r];
   }
 }
 
@@ -567,22 +569,23 @@ bool chunked_wy_applies(const ProblemArgs& a) {
 }
 
 size_t chunked_wy_workspace_bytes(const ProblemArgs& a) {
-  const int64_t nchunks = (int64_t(a.T) + kC - 1) / kC;
-  return size_t(int64_t(a.B) * a.H * nchunks) * kFactorBytes;
+  const int64_t nblk = int64_t(a.B) * a.H * ((int64_t(a.T) + kC - 1) / kC);
+  return size_t(nblk) * (kBlockElems * 2 + 4);
 }
 
 hipError_t launch_chunked_wy(const ProblemArgs& a, hipStream_t st) {
   const int64_t BH = int64_t(a.B) * a.H;
   const int nchunks = (a.T + kC - 1) / kC;
   if (BH == 0 || nchunks == 0) return hipSuccess;
-  uint16_t* factors = static_cast<uint16_t*>(a.workspace);
+  uint16_t* blocks = static_cast<uint16_t*>(a.workspace);
+  float* decay63 = reinterpret_cast<float*>(blocks + BH * nchunks * kBlockElems);
   hipLaunchKernelGGL(falcon1_wy_kernel, dim3(unsigned(BH * nchunks)), dim3(256), 0, st,
-                     static_cast<const bf16_t*>(a.phi_k), static_cast<const bf16_t*>(a.v), a.beta, a.lam,
-                     static_cast<const bf16_t*>(a.k_prev), factors, a.T, nchunks, a.eps, a.eps_gamma);
-  hipLaunchKernelGGL(falcon1_chain_kernel, dim3(unsigned(BH)), dim3(kChainThreads), 0, st,
-                     static_cast<const bf16_t*>(a.phi_k), static_cast<const bf16_t*>(a.phi_q), a.beta, a.lam,
-                     a.S0, static_cast<const bf16_t*>(a.k_prev), factors, static_cast<bf16_t*>(a.o), a.S_T,
-                     a.T, a.eps, a.eps_gamma);
+                     static_cast<const bf16_t*>(a.phi_k), static_cast<const bf16_t*>(a.phi_q),
+                     static_cast<const bf16_t*>(a.v), a.beta, a.lam, static_cast<const bf16_t*>(a.k_prev),
+                     blocks, decay63, a.T, nchunks, a.eps, a.eps_gamma);
+  const int64_t groups = (BH + 7) / 8;
+  hipLaunchKernelGGL(falcon1_chain_kernel, dim3(unsigned(groups * 8 * kSplit)), dim3(kChainThreads), 0, st,
+                     a.S0, blocks, decay63, static_cast<bf16_t*>(a.o), a.S_T, a.T, nchunks, BH);
   return hipGetLastError();
 }
 

@@ -154,7 +154,7 @@ def test_nan_propagates_without_hang():
         assert torch.isfinite(o[0, 0, :20]).all()
 
 
-# ---- Falcon-1A chunk tiles (bf16, d = 64, C = 64): look-back across tiles ---
+# ---- Falcon-1A chunk tiles (bf16, d = 64, C = 64): tile aggregates, scan, sweep ---
 
 @pytest.mark.parametrize("B,H,T", [(1, 1, 4096), (2, 3, 805), (3, 2, 1000), (1, 2, 256)])
 def test_falcon1a_tiles(B, H, T):
@@ -194,6 +194,50 @@ def test_falcon1a_tiles_repeatable():
     ws = torch.full((fb.falcon_workspace_bytes(p, 64),), 0x7f, dtype=torch.uint8, device="cuda")
     o1, s1 = _run("chunked", d, "falcon1a", workspace=ws)
     o2, s2 = _run("chunked", d, "falcon1a", workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+# ---- Falcon-1 chunk matrices and chain (bf16, d = 64, C = 64) ------------------
+
+@pytest.mark.parametrize("B,H,T", [(1, 1, 64), (3, 5, 1000), (2, 7, 4100), (1, 9, 129)])
+def test_falcon1_chunk_maps(B, H, T):
+    """Falcon-1 bf16 d=64: chunk-parallel chunk matrices and the chain.
+    Covers a single chunk, ragged tails, many chunks per sequence, and
+    batch x head counts that leave part of the last group of eight
+    sequences empty."""
+    d = I.make_inputs(B, H, T, 64, 64, seed=400 + T, io_dtype="bf16")
+    O_ref, S_ref = oracle_forward("falcon1", d)
+    o, S_T = _run("chunked", to_dev(d), "falcon1")
+    torch.cuda.synchronize()
+    check(o, S_T, O_ref, S_ref, TOL["bf16"], f"falcon1 chunk maps {B}x{H}x{T}")
+
+
+def test_falcon1_chunk_maps_carried_state_and_continuation():
+    B, H, T, T1 = 2, 3, 1300, 517
+    d = I.make_inputs(B, H, T, 64, 64, seed=31, io_dtype="bf16")
+    S0 = I.random_state((B, H, 64, 64), seed=32)
+    O_ref, S_ref = oracle_forward("falcon1", d, S0=S0)
+    dd = to_dev(d)
+    o, S_T = _run("chunked", dd, "falcon1", S0=S0.cuda())
+    torch.cuda.synchronize()
+    check(o, S_T, O_ref, S_ref, TOL["bf16"], "falcon1 chunk maps carried S0")
+    first = {k: v[:, :, :T1].contiguous() for k, v in dd.items()}
+    second = {k: v[:, :, T1:].contiguous() for k, v in dd.items()}
+    o1, S1 = _run("chunked", first, "falcon1", S0=S0.cuda())
+    kp = dd["phi_k"][:, :, T1 - 1].contiguous()
+    o2, S2 = _run("chunked", second, "falcon1", S0=S1, k_prev=kp)
+    torch.cuda.synchronize()
+    check(torch.cat([o1, o2], dim=2), S2, O_ref, S_ref, TOL["bf16"], "falcon1 chunk maps split")
+
+
+def test_falcon1_chunk_maps_repeatable():
+    """Two calls on one workspace prefilled with garbage give the same bits."""
+    d = to_dev(I.make_inputs(3, 3, 700, 64, 64, seed=33, io_dtype="bf16"))
+    p = fb.make_problem(3, 3, 700, 64, 64, variant="falcon1", io_dtype=torch.bfloat16)
+    ws = torch.full((fb.falcon_workspace_bytes(p, 64),), 0x7f, dtype=torch.uint8, device="cuda")
+    o1, s1 = _run("chunked", d, "falcon1", workspace=ws)
+    o2, s2 = _run("chunked", d, "falcon1", workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
 

@@ -1,0 +1,55 @@
+"""Static checks of the gfx950 code the kernels compile to.
+
+Matrix (MFMA) instructions do not honour the EXEC mask: one issued inside
+a lane-masked region still writes its destination in every lane.  A branch
+on a value the compiler cannot prove wave-uniform around an MFMA is
+compiled to such a region (s_and_saveexec ... s_or_b64 exec) and, unless
+the region is skipped with s_cbranch_execz, silently changes the result.
+This test compiles every HIP source to assembly and fails on any MFMA in a
+masked region that is not skipped.
+"""
+
+import os
+import re
+import subprocess
+
+import pytest
+
+from delta_rule_recurrence_amd import build as B
+
+SOURCES = sorted(f for f in os.listdir(B.CSRC) if f.endswith(".hip"))
+
+
+def _masked_mfmas(asm: str):
+    bad, masked, skipped, fn = [], False, False, "?"
+    lines = asm.split("\n")
+    for i, line in enumerate(lines):
+        if re.match(r"^_Z\S+:", line):
+            fn = line.split(":")[0]
+        s = line.strip()
+        if re.match(r"s_(and|andn2|xor|or)_saveexec", s):
+            masked = True
+            skipped = i + 1 < len(lines) and lines[i + 1].strip().startswith("s_cbranch_execz")
+        elif s.startswith("s_or_b64 exec") or s.startswith("s_mov_b64 exec"):
+            masked = False
+        elif s.startswith("v_mfma") and masked and not skipped:
+            bad.append(f"{fn} line {i + 1}: {s}")
+    return bad
+
+
+def _hipcc():
+    try:
+        return B.hipcc()
+    except RuntimeError:
+        return None
+
+
+@pytest.mark.skipif(_hipcc() is None, reason="hipcc not available")
+@pytest.mark.parametrize("src", SOURCES)
+def test_no_mfma_under_exec_mask(src, tmp_path):
+    out = tmp_path / (src + ".s")
+    cmd = [B.hipcc(), *B.HIPCC_FLAGS, "--cuda-device-only", "-S", os.path.join(B.CSRC, src), "-o", str(out)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    bad = _masked_mfmas(out.read_text())
+    assert not bad, "MFMA inside an EXEC-masked region:\n" + "\n".join(bad[:10])
