@@ -97,10 +97,8 @@ struct WyGates {
 
 struct WySmem {
   uint16_t x[kC * kD];            // keys (swizzled rows); then frag(-W^T) [fb][m][lane][8]
-  uint16_t v[kC * kD];            // values (swizzled rows); then frag(U^T) [cb][m][lane][8]
-  uint16_t q[kC * kD];            // queries (swizzled rows)
   uint16_t xh[kC * kD];           // frag(Xh^T) [fb][m][lane][8]
-  uint16_t mf[kC * kD];           // frag(M) [ib][m][lane][8]
+  uint16_t ut[kC * kD];           // values (swizzled rows); then frag(U^T) [cb][m][lane][8]
   uint16_t tb[kC * kP];           // T, row-major
   float abt[4][16][16];           // diagonal blocks of -A: [b][s][i] = -A[16b+i][16b+s]
   WyGates G;
@@ -206,14 +204,29 @@ __device__ __forceinline__ void build_inverse(WySmem& sm, int l) {
 // Fragment slot [b][m] of a 64x64 fragment array.
 __device__ __forceinline__ int fslot(int b, int m, int l) { return ((b * 2 + m) * 64 + l) * 8; }
 
-__global__ void __launch_bounds__(256, 2)
+__device__ __forceinline__ bf16x8 ldg_frag(const bf16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+}
+__device__ __forceinline__ uint2 ldg_half(const bf16_t* p) { return *reinterpret_cast<const uint2*>(p); }
+__device__ __forceinline__ f32x4 unpack_half(uint2 v) {
+  return f32x4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+               __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u)};
+}
+
+// Every global load is issued at the start, so a workgroup waits for memory
+// once.  Keys and values are staged in LDS; each wave's queries and the gate
+// inputs go straight into registers.  Wave w owns token block ib = w of the
+// read mask M, Qt and Ot, and row block w of K and H.
+__global__ void __launch_bounds__(256, 4)
 falcon1_wy_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restrict__ phi_q,
                   const bf16_t* __restrict__ v, const float* __restrict__ beta, const float* __restrict__ lam,
                   const bf16_t* __restrict__ k_prev, uint16_t* __restrict__ blocks, float* __restrict__ decay63,
                   int T, int nchunks, float eps, float eps_gamma) {
   __shared__ WySmem sm;
   const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;   // wave-uniform, so role branches are scalar
+  // role index: wave-uniform (so role branches are scalar) and rotated by the
+  // workgroup, so the long inverse role is spread over the SIMDs
+  const int w = (__builtin_amdgcn_readfirstlane(tid >> 6) + int(blockIdx.x)) & 3, l = tid & 63;
   const int g = l >> 4, c16 = l & 15;
   const int64_t bh = blockIdx.x / nchunks;
   const int c = blockIdx.x % nchunks;
@@ -221,15 +234,24 @@ falcon1_wy_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restrict__ p
   const bool fresh = (k_prev == nullptr);
   uint16_t* out = blocks + int64_t(blockIdx.x) * kBlockElems;
 
-  // ---- stage keys, values and queries: wave w rows 16w..16w+15 -------------
+  // ---- stage keys and values (wave w rows 16w..16w+15); fetch this wave's
+  // queries and, for the gates, beta and lam of token c * 64 + l --------------
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int r = 16 * w + 8 * j + (l >> 3);
     const int off = r * kD + 8 * seg_pos(r, l & 7);
     *reinterpret_cast<bf16x8*>(sm.x + off) = *reinterpret_cast<const bf16x8*>(key_row(sq, c, r) + 8 * (l & 7));
-    *reinterpret_cast<bf16x8*>(sm.v + off) = *reinterpret_cast<const bf16x8*>(token_row(sq.V, sq, c, r) + 8 * (l & 7));
-    *reinterpret_cast<bf16x8*>(sm.q + off) = *reinterpret_cast<const bf16x8*>(token_row(sq.Q, sq, c, r) + 8 * (l & 7));
+    *reinterpret_cast<bf16x8*>(sm.ut + off) = *reinterpret_cast<const bf16x8*>(token_row(sq.V, sq, c, r) + 8 * (l & 7));
   }
+  const int gtok = c * kC + l < T ? c * kC + l : T - 1;
+  const float beta_l = sq.beta[gtok], lam_l = sq.lam[gtok];
+  // query row i = 16w + c16: contiguous fragments for Q X^T, and Q[i][16fb+4g..+3]
+  const bf16_t* qrow = token_row(sq.Q, sq, c, 16 * w + c16);
+  const bf16x8 qa0 = ldg_frag(qrow + 8 * g);
+  const bf16x8 qa1 = ldg_frag(qrow + 32 + 8 * g);
+  uint2 qi[4];
+#pragma unroll
+  for (int fb = 0; fb < 4; ++fb) qi[fb] = ldg_half(qrow + 16 * fb + 4 * g);
   // T's upper blocks are never written
   for (int e = tid; e < kC * kP / 2; e += 256) reinterpret_cast<uint32_t*>(sm.tb)[e] = 0u;
   __syncthreads();
@@ -241,9 +263,8 @@ falcon1_wy_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restrict__ p
       const int r = 8 * j + (l >> 3);
       x[j] = *reinterpret_cast<const bf16x8*>(sm.x + r * kD + 8 * seg_pos(r, l & 7));
     }
-    const int tok = c * kC + l < T ? c * kC + l : T - 1;
     float eta, gi, gprev, glast;
-    chunk_gates(x, sq.beta[tok], sq.lam[tok], c * kC + l, T, eps, eps_gamma, fresh, l, eta, gi, gprev, glast);
+    chunk_gates(x, beta_l, lam_l, c * kC + l, T, eps, eps_gamma, fresh, l, eta, gi, gprev, glast);
     sm.G.graw[l] = gi;
     sm.G.sxg[l] = eta * __expf(gprev);
     sm.G.sxh[l] = __expf(glast - gi);
@@ -253,7 +274,7 @@ falcon1_wy_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restrict__ p
     if (l == 0) decay63[blockIdx.x] = __expf(glast);
   }
   __syncthreads();
-  // ---- T, scaled key transposes, value transposes, read mask ----------------
+  // ---- T; scaled key and value transposes; this wave's rows of M -------------
   bf16x8 xg[2][2];              // waves 1, 2: frag((Diag(eta e^{g_{s-1}}) X)^T) for fb = 2(w-1) + h
   bf16x8 vt[4][2];              // wave 3: frag((Diag(eta) V)^T) for all cb
   if (w == 0) {
@@ -276,36 +297,42 @@ falcon1_wy_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restrict__ p
     }
   } else {
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      const bf16x8 sel = select_frag(cb & 1, g, c16);
-      f32x4 d[4];
+    for (int hv = 0; hv < 2; ++hv) {
 #pragma unroll
-      for (int sb = 0; sb < 4; ++sb) d[sb] = mfma32(ring_frag_c(sm.v, 16 * sb + c16, cb >> 1, g), sel, zero4());
+      for (int h = 0; h < 2; ++h) {
+        const int cb = 2 * hv + h;
+        const bf16x8 sel = select_frag(h, g, c16);
+        f32x4 d[4];
 #pragma unroll
-      for (int m = 0; m < 2; ++m)
-        vt[cb][m] = frag_acc(d[2 * m] * ld4(&sm.G.eta[32 * m + 4 * g]), d[2 * m + 1] * ld4(&sm.G.eta[32 * m + 16 + 4 * g]));
+        for (int sb = 0; sb < 4; ++sb) d[sb] = mfma32(ring_frag_c(sm.ut, 16 * sb + c16, hv, g), sel, zero4());
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+          vt[cb][m] = frag_acc(d[2 * m] * ld4(&sm.G.eta[32 * m + 4 * g]), d[2 * m + 1] * ld4(&sm.G.eta[32 * m + 16 + 4 * g]));
+      }
     }
-    // M: tile (ib, sb) of X Q^T holds M[16ib+c16][16sb+4g+r] after the decay
-    // and the causal mask (s <= i); tiles sb = 2m, 2m+1 stack into frag(M)[ib][m]
-#pragma unroll
-    for (int n = 0; n < 10; ++n) {
-      int ib, sb;
-      lower_tile(n, ib, sb);
-      f32x4 acc = mfma32(ring_frag_c(sm.x, 16 * sb + c16, 0, g), ring_frag_c(sm.q, 16 * ib + c16, 0, g), zero4());
-      acc = mfma32(ring_frag_c(sm.x, 16 * sb + c16, 1, g), ring_frag_c(sm.q, 16 * ib + c16, 1, g), acc);
-      const f32x4 gs = ld4(&sm.G.graw[16 * sb + 4 * g]);
-      const float gi = sm.G.graw[16 * ib + c16];
-      const int i = 16 * ib + c16;
-      f32x4 mv;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) mv[r] = 16 * sb + 4 * g + r <= i ? __expf(gi - gs[r]) * acc[r] : 0.0f;
-      store_half(&sm.mf[fslot(ib, sb >> 1, l) + 4 * (sb & 1)], mv);
-    }
-    // the two half fragments above the diagonal that are read
-    store_half(&sm.mf[fslot(0, 0, l) + 4], zero4());
-    store_half(&sm.mf[fslot(2, 1, l) + 4], zero4());
   }
-  __syncthreads();                                           // T, Xh, M complete; x and v free
+  // M rows of token block ib = w: tile sb of X Q^T holds M[16w+c16][16sb+4g+r]
+  // after the decay and the causal mask (s <= i); tiles 2m, 2m+1 stack into frag(M)[w][m]
+  bf16x8 mf[2];
+  {
+    const int i = 16 * w + c16;
+    const float gi = sm.G.graw[i];
+    f32x4 mt[4];
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+      mt[sb] = zero4();
+      if (sb <= w) {
+        f32x4 acc = mfma32(ring_frag_c(sm.x, 16 * sb + c16, 0, g), qa0, zero4());
+        acc = mfma32(ring_frag_c(sm.x, 16 * sb + c16, 1, g), qa1, acc);
+        const f32x4 gs = ld4(&sm.G.graw[16 * sb + 4 * g]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mt[sb][r] = 16 * sb + 4 * g + r <= i ? __expf(gi - gs[r]) * acc[r] : 0.0f;
+      }
+    }
+    mf[0] = frag_acc(mt[0], mt[1]);
+    mf[1] = frag_acc(mt[2], mt[3]);
+  }
+  __syncthreads();                                           // T, Xh complete; the key and value rows are free
   // ---- W and U as fragments over tokens --------------------------------------
   if (w >= 1) {
     bf16x8 tf[4][2];
@@ -342,13 +369,12 @@ falcon1_wy_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restrict__ p
             d0 = mfma32(tf[2 * m][1], vt[cb][1], d0);
             d1 = mfma32(tf[2 * m + 1][1], vt[cb][1], d1);
           }
-          store_frag(&sm.v[fslot(cb, m, l)], frag_acc(d0, d1));
+          store_frag(&sm.ut[fslot(cb, m, l)], frag_acc(d0, d1));
         }
     }
   }
   __syncthreads();                                           // frag(-W^T), frag(U^T) complete
-  // ---- chunk matrices: wave w takes row block w of K, H^T-tiles fb = w, and
-  // token block ib = w of Qt and Ot --------------------------------------------
+  // ---- chunk matrices ---------------------------------------------------------
   {
     bf16x8 wt[4][2], ut[4][2];
 #pragma unroll
@@ -356,12 +382,10 @@ falcon1_wy_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restrict__ p
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         wt[b][m] = load_frag(&sm.x[fslot(b, m, l)]);
-        ut[b][m] = load_frag(&sm.v[fslot(b, m, l)]);
+        ut[b][m] = load_frag(&sm.ut[fslot(b, m, l)]);
       }
     const bf16x8 xh0 = load_frag(&sm.xh[fslot(w, 0, l)]);
     const bf16x8 xh1 = load_frag(&sm.xh[fslot(w, 1, l)]);
-    const bf16x8 mf0 = load_frag(&sm.mf[fslot(w, 0, l)]);
-    const bf16x8 mf1 = w >= 2 ? load_frag(&sm.mf[fslot(w, 1, l)]) : mf0;
     // K: tile (fb', fb = w) of (-W^T) Xh = K^T; fb' = 2m, 2m+1 stack into frag(K)[w][m]
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
@@ -380,19 +404,16 @@ falcon1_wy_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restrict__ p
     }
     // Qt: tile (fb, ib = w) of e^{g_i} Q^T - W^T M^T = Qt^T; fb = 2m, 2m+1 stack into frag(Qt)[w][m]
     {
-      const int i = 16 * w + c16;
-      const float egi = __expf(sm.G.graw[i]);
+      const float egi = __expf(sm.G.graw[16 * w + c16]);
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         f32x4 t[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int fb = 2 * m + h;
-          // e^{g_i} Q[i][16fb+4g .. +3]
-          const f32x4 qv = load_half(sm.q + i * kD + 8 * seg_pos(i, 2 * fb + (g >> 1)) + 4 * (g & 1));
-          f32x4 acc = qv * egi;
-          acc = mfma32(wt[fb][0], mf0, acc);
-          if (w >= 2) acc = mfma32(wt[fb][1], mf1, acc);
+          f32x4 acc = unpack_half(qi[fb]) * egi;
+          acc = mfma32(wt[fb][0], mf[0], acc);
+          if (w >= 2) acc = mfma32(wt[fb][1], mf[1], acc);
           t[h] = acc;
         }
         store_frag(out + kOutQt + fslot(w, m, l), frag_acc(t[0], t[1]));
@@ -401,8 +422,8 @@ falcon1_wy_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restrict__ p
     // Ot^T: tile (cb, ib = w) of U^T M^T, lane holds Ot[16w+c16][16cb+4g+r]
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
-      f32x4 oacc = mfma32(ut[cb][0], mf0, zero4());
-      if (w >= 2) oacc = mfma32(ut[cb][1], mf1, oacc);
+      f32x4 oacc = mfma32(ut[cb][0], mf[0], zero4());
+      if (w >= 2) oacc = mfma32(ut[cb][1], mf[1], oacc);
       store_half(out + kOutOt + ((cb * 4 + w) * 64 + l) * 4, oacc);
     }
   }
@@ -503,8 +524,14 @@ falcon1_chain_kernel(const float* S0, const uint16_t* __restrict__ blocks, const
     return;
   }
   // ---- chain waves ------------------------------------------------------------
+  // Per chunk c: the reads of Qt and Ot are issued before the state update and
+  // the reads of chunk c + 1's K and H before the outputs, so LDS latency hides
+  // behind the matrix products.  A wait that runs out sets the abort flag; the
+  // loop still runs to its end (every later wait returns at once).
   const int cw = wave;
   const int cb = part * kColWaves + cw;                      // value columns 16 cb .. 16 cb + 15
+  const int hoff = 8192 + cw * 1024 + l * 4;                 // this wave's H tiles in an entry
+  const int ooff = 8192 + kColWaves * 1024 + cw * 1024 + l * 4;
   f32x4 S[4];                                                // S[fb]: lane holds S[16fb+4g+r][16cb+c16]
 #pragma unroll
   for (int fb = 0; fb < 4; ++fb)
@@ -512,44 +539,67 @@ falcon1_chain_kernel(const float* S0, const uint16_t* __restrict__ blocks, const
     for (int r = 0; r < 4; ++r)
       S[fb][r] = S0 ? S0[(bh * kD + 16 * fb + 4 * g + r) * kD + 16 * cb + c16] : 0.0f;
   bf16_t* o_bh = o + bh * T * kD;
+  bf16x8 kf[4][2];                                           // frag(K)[fb][m] of the current chunk
+  uint2 hf[4];                                               // its H tiles
+  float e63;
+  wait_at_least(&sm.in_ready[0], 1, &sm.abort_flag);
+#pragma unroll
+  for (int fb = 0; fb < 4; ++fb) {
+    kf[fb][0] = load_frag(&sm.d[0][kOutK + fslot(fb, 0, l)]);
+    kf[fb][1] = load_frag(&sm.d[0][kOutK + fslot(fb, 1, l)]);
+    hf[fb] = *reinterpret_cast<const uint2*>(&sm.d[0][hoff + fb * 256]);
+  }
+  e63 = sm.e63[0];
+  // the state as a bf16 operand, carried around the loop (forming it here also
+  // retires the S0 loads before the loop, so no wait in the loop covers the
+  // output stores)
+  bf16x8 sb0 = frag_acc(S[0], S[1]);
+  bf16x8 sb1 = frag_acc(S[2], S[3]);
   for (int c = 0; c < nchunks; ++c) {
-    const int e = c % kRing;
-    const uint16_t* D = sm.d[e];
-    if (!wait_at_least(&sm.in_ready[e], c / kRing + 1, &sm.abort_flag)) break;
-    bf16x8 kf[4][2], qf[4][2];
-    f32x4 hf[4], of[4];
+    const uint16_t* D = sm.d[c % kRing];
+    const int e1 = (c + 1) % kRing;
+    // chunk c + 1 must be in its entry before its reads below; after the last
+    // chunk those reads only see a stale entry and are not used
+    if (c + 1 < nchunks) wait_at_least(&sm.in_ready[e1], (c + 1) / kRing + 1, &sm.abort_flag);
+    bf16x8 qf[4][2];
+    uint2 of[4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        kf[b][m] = load_frag(&D[kOutK + fslot(b, m, l)]);
-        qf[b][m] = load_frag(&D[kOutQt + fslot(b, m, l)]);
-      }
-      hf[b] = load_half(&D[8192 + cw * 1024 + (b * 64 + l) * 4]);
-      of[b] = load_half(&D[8192 + kColWaves * 1024 + cw * 1024 + (b * 64 + l) * 4]);
+    for (int ib = 0; ib < 4; ++ib) {
+      qf[ib][0] = load_frag(&D[kOutQt + fslot(ib, 0, l)]);
+      qf[ib][1] = load_frag(&D[kOutQt + fslot(ib, 1, l)]);
+      of[ib] = *reinterpret_cast<const uint2*>(&D[ooff + ib * 256]);
     }
-    const float e63 = sm.e63[e];
-    signal_add(&sm.in_free[e], l);
-    const bf16x8 sb0 = frag_acc(S[0], S[1]);
-    const bf16x8 sb1 = frag_acc(S[2], S[3]);
     // S <- e^{g_63} S + K S + H
 #pragma unroll
     for (int fb = 0; fb < 4; ++fb) {
-      f32x4 acc = S[fb] * e63 + hf[fb];
+      f32x4 acc = S[fb] * e63 + unpack_half(hf[fb]);
       acc = mfma32(kf[fb][0], sb0, acc);
       S[fb] = mfma32(kf[fb][1], sb1, acc);
+    }
+    {
+      const uint16_t* D1 = sm.d[e1];
+#pragma unroll
+      for (int fb = 0; fb < 4; ++fb) {
+        kf[fb][0] = load_frag(&D1[kOutK + fslot(fb, 0, l)]);
+        kf[fb][1] = load_frag(&D1[kOutK + fslot(fb, 1, l)]);
+        hf[fb] = *reinterpret_cast<const uint2*>(&D1[hoff + fb * 256]);
+      }
+      e63 = sm.e63[e1];
     }
     // O^T tiles: S^T Qt^T + Ot^T; lane holds o[t0+16ib+c16][16cb+4g+r]
     const int t0 = c * kC;
 #pragma unroll
     for (int ib = 0; ib < 4; ++ib) {
-      f32x4 acc = mfma32(sb0, qf[ib][0], of[ib]);
+      f32x4 acc = mfma32(sb0, qf[ib][0], unpack_half(of[ib]));
       acc = mfma32(sb1, qf[ib][1], acc);
       const int tok = t0 + 16 * ib + c16;
       if (tok < T)
         *reinterpret_cast<uint2*>(o_bh + int64_t(tok) * kD + 16 * cb + 4 * g) =
             make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
     }
+    sb0 = frag_acc(S[0], S[1]);
+    sb1 = frag_acc(S[2], S[3]);
+    signal_add(&sm.in_free[c % kRing], l);
   }
   // a wait that ran out (a hand-over that never came) leaves NaN in S_T
   const bool aborted = __hip_atomic_load(&sm.abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0;
