@@ -14,15 +14,19 @@
 //   o_{i,j} = e^{g_{i,j}} (Q S)_{i,j} + sum_{s<=i} e^{g_{i,j}-g_{s,j}} (q_i.x_s) rho_{s,j}
 //   S'_{:,j} = e^{g_{63,j}} S_{:,j} + sum_s e^{g_{63,j}-g_{s,j}} x_s rho_{s,j}.
 // The decays differ per column, so the triangular system is solved per
-// column on the vector ALUs: with u_s = e^{g_{i-1}-g_s} rho_s carried from
-// row to row (u_s <- gamma_i u_s after row i), every coefficient is a plain
-// product and no exponential is evaluated; all factors are <= 1.  The
-// products that are shared by all columns (x_i.x_s, q_i.x_s, X S, Q S and the
-// state update) run on the matrix cores.
-//
-// One workgroup (one wave) per (batch, head, 16-column slice); four lanes per
-// column split every row's sums (s = 4k + lane % 4) and combine them with
-// DPP quad reductions.
+// column, in four 16-row blocks.  Lane layout in the solve: a 16-lane row of a
+// wave is one value column, lane li is row 16b + li of block b.
+//  * Earlier blocks enter through w_s = e^{g_{16b-1}-g_s} rho_s (kept per column
+//    in LDS, every factor <= 1): row i gets
+//    eta_i e^{g_{i-1}-g_{16b-1}} sum_{s<16b} (x_i.x_s) w_s, off the critical path.
+//  * Inside the block, forward substitution runs in registers: step s adds
+//    -c_{i,s} rho_s to every later row, rho_s broadcast from lane s by a DPP
+//    row broadcast (row_newbcast), 15 dependent steps per block.
+//  * The products shared by all columns (x_i.x_s, q_i.x_s, X S, Q S and the
+//    state update) run on the matrix cores.
+// One workgroup (four waves, four value columns each) per (batch, head,
+// 16-column slice); the next chunk's rows are fetched into registers while the
+// current one is solved.
 
 #include "falcon_device.h"
 #include "falcon_launch.h"
@@ -36,87 +40,201 @@ using namespace frag;
 
 constexpr int kC = 64;
 constexpr int kD = 64;
-constexpr int kSlice = 16;
+constexpr int kSlice = 16;                  // value columns per workgroup
+constexpr int kThreads = 256;
+constexpr int kGP = 68;                     // float row pitch of the Gram buffers (16-byte aligned, spreads banks)
 
 struct PcSmem {
-  uint16_t x[kC * kD];            // keys phi(k_{t0+r-1}), swizzled rows
-  uint16_t q[kC * kD];            // queries, swizzled rows
-  float kq[kC][4][16];            // x_i.x_s at [i][s % 4][s / 4] for s < i, else 0
-  float pq[kC][4][16];            // q_i.x_s at [i][s % 4][s / 4] for s <= i, else 0
-  // per row i and column j: first {v, beta, (X S), (Q S)}, then, in place,
-  // {rhs a, eta, gamma, e^{g_i} (Q S)}, and after the rows o_{i,j} in .x
-  f32x4 rp[kC][kSlice];
-  float en[kC];                   // ||x_i||^2
-  float lm[kC];                   // lam_i
-  uint16_t ut[kSlice][kC];        // e^{g_63-g_s} rho_s per column, bf16, [j][s]
-  float e63[kSlice];              // e^{g_63} per column
+  uint16_t x[kC * kD];                      // keys phi(k_{t0+r-1}), swizzled rows
+  uint16_t q[kC * kD];                      // queries, swizzled rows
+  float kq[kC][kGP];                        // [i][s] = x_i . x_s (s <= i written)
+  float pq[kC][kGP];                        // [i][s] = q_i . x_s (s <= i written)
+  float xs[kC][kSlice];                     // (X S)_{i,j}
+  float qs[kC][kSlice];                     // (Q S)_{i,j}
+  float vb[kC][kSlice];                     // v_{i,j}
+  float bt[kC][kSlice];                     // beta_{i,j}
+  float lm[kC];                             // lam_i
+  float en[kC];                             // ||x_i||^2
+  float w[kSlice][kC];                      // per column: e^{g_b-g_s} rho_s, b = end of the last solved block
+  float e63[kSlice];                        // e^{g_63} per column
+  uint16_t ob[kC][kSlice];                  // outputs of the chunk, bf16
 };
 
-__device__ __forceinline__ float quad_sum(float v) {
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xf, 0xf, true));  // [1,0,3,2]
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xf, 0xf, true));  // [2,3,0,1]
-  return v;
+// Lane N of the lane's 16-lane row (DPP row_newbcast; every lane has a
+// source, so no fill value is needed and the move can fuse into its user).
+template <int N>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + N, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+constexpr float kLog2e = 1.4426950408889634f;
+
+// The next chunk's inputs, fetched into registers during the current chunk.
+struct ChunkRegs {
+  bf16x8 x[2], q[2];                        // rows r = 32 j + (tid >> 3), segment tid & 7
+  bf16x8 v;                                 // tid < 128: row tid >> 1, columns j0 + 8 (tid & 1) ..
+  float4 bt;                                // row tid >> 2, columns j0 + 4 (tid & 3) ..
+  float lm;                                 // tid < 64: row tid
+};
+
+__device__ __forceinline__ void fetch_chunk(ChunkRegs& R, const bf16_t* K, const bf16_t* Q, const bf16_t* V,
+                                            const float* Bt, const float* Lm, const bf16_t* kp, int T, int t0,
+                                            int j0, int tid) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = 32 * j + (tid >> 3);
+    const int kt = t0 + r - 1;
+    const bf16_t* xsrc = kt < 0 ? (kp ? kp : K) : K + int64_t(kt < T ? kt : T - 1) * kD;
+    const int tok = t0 + r < T ? t0 + r : T - 1;
+    R.x[j] = *reinterpret_cast<const bf16x8*>(xsrc + 8 * (tid & 7));
+    R.q[j] = *reinterpret_cast<const bf16x8*>(Q + int64_t(tok) * kD + 8 * (tid & 7));
+  }
+  if (tid < 128) {
+    const int r = tid >> 1;
+    const int tok = t0 + r < T ? t0 + r : T - 1;
+    R.v = *reinterpret_cast<const bf16x8*>(V + int64_t(tok) * kD + j0 + 8 * (tid & 1));
+  }
+  {
+    const int r = tid >> 2;
+    const int tok = t0 + r < T ? t0 + r : T - 1;
+    R.bt = *reinterpret_cast<const float4*>(Bt + int64_t(tok) * kD + j0 + 4 * (tid & 3));
+  }
+  if (tid < 64) R.lm = Lm[t0 + tid < T ? t0 + tid : T - 1];
 }
 
-// Row I of one chunk for the lane's column (unrolled by recursion, so every
-// bound and register index is a compile-time constant; the loop body reads
-// LDS only, so the compiler is free to fetch later rows early).  On entry
-// u[k] holds e^{g_{I-1}-g_s} rho_s for s = 4k + qq < I, on exit
-// e^{g_I-g_s} rho_s for s <= I.  Row I's output is kept by the lane that owns
-// s = I, in ov[I / 4].
-template <bool kReg, int I>
-__device__ __forceinline__ void solve_rows(const PcSmem& sm, int jc, int qq, float (&u)[16], float (&ov)[16]) {
-  if constexpr (I < kC) {
-    const f32x4 p = sm.rp[I][jc];                  // a_I, eta_I, gamma_I, e^{g_I} (Q S)_I
-    float rho = p[0];
+__device__ __forceinline__ void stage_chunk(PcSmem& sm, const ChunkRegs& R, int tid) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = 32 * j + (tid >> 3);
+    const int off = r * kD + 8 * seg_pos(r, tid & 7);
+    *reinterpret_cast<bf16x8*>(sm.x + off) = R.x[j];
+    *reinterpret_cast<bf16x8*>(sm.q + off) = R.q[j];
+  }
+  if (tid < 128) {
+    const int r = tid >> 1;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sm.vb[r][8 * (tid & 1) + e] = static_cast<float>(R.v[e]);
+  }
+  *reinterpret_cast<float4*>(&sm.bt[tid >> 2][4 * (tid & 3)]) = R.bt;
+  if (tid < 64) sm.lm[tid] = R.lm;
+}
+
+// One 16-row block B of the per-column system and of the outputs, for the
+// lane's column jl and row i = 16 B + li.  g is kept in log2 units, so every
+// decay is one exp2.  gcarry holds g at the end of the previous block (0
+// before block 0) and is advanced to the end of this one.
+template <bool kReg, int B>
+__device__ __forceinline__ void solve_block(PcSmem& sm, int jl, int li, int t0, int T, bool fresh, float eps,
+                                            float eps_gamma, float& gcarry) {
+  const int i = 16 * B + li;
+  const int t = t0 + i;
+  const bool live = t < T;
+  // step size and decay of row i in column jl; g by a scan over the 16 rows
+  const float den = sm.en[i] + sm.lm[i] + eps;
+  const float eta = (live && !(fresh && t == 0) && den != 0.0f) ? sm.bt[i][jl] / den : 0.0f;
+  const float lg = live ? kLog2e * clamped_log_gamma(eta, sm.lm[i], eps_gamma) : 0.0f;
+  float gi = lg;
+  gi += row_shr<1>(gi);
+  gi += row_shr<2>(gi);
+  gi += row_shr<4>(gi);
+  gi += row_shr<8>(gi);
+  gi += gcarry;
+  const float gsh = row_shr<1>(gi);
+  const float gprev = li == 0 ? gcarry : gsh;
+  const float glast = row_bcast<15>(gi);
+  // earlier blocks, through w_s = e^{g_{16B-1}-g_s} rho_s
+  float a = kReg ? eta * (sm.vb[i][jl] - exp2_fast(gprev) * sm.xs[i][jl]) : eta * sm.vb[i][jl];
+  float o = exp2_fast(gi) * sm.qs[i][jl];
+  if constexpr (B > 0) {
+    float pk = 0.f, pp = 0.f;
+#pragma unroll
+    for (int s4 = 0; s4 < 4 * B; ++s4) {
+      const f32x4 w4 = ld4(&sm.w[jl][4 * s4]);
+      const f32x4 p4 = ld4(&sm.pq[i][4 * s4]);
+      pp += p4[0] * w4[0] + p4[1] * w4[1] + p4[2] * w4[2] + p4[3] * w4[3];
+      if constexpr (kReg) {
+        const f32x4 k4 = ld4(&sm.kq[i][4 * s4]);
+        pk += k4[0] * w4[0] + k4[1] * w4[1] + k4[2] * w4[2] + k4[3] * w4[3];
+      }
+    }
+    if constexpr (kReg) a -= eta * exp2_fast(gprev - gcarry) * pk;
+    o += exp2_fast(gi - gcarry) * pp;
+  }
+  // in-block decays e^{g_{i-1}-g_s} for s = 16B + sl < i
+  float ed[16];
+  ed[15] = 0.f;
+  // (the broadcast is taken in every lane; entries s >= i are selected away)
+#define FALCON_ED(SL) { const float gs = row_bcast<SL>(gi); const float e = exp2_fast(gprev - gs); ed[SL] = (SL) < li ? e : 0.0f; }
+  FALCON_ED(0) FALCON_ED(1) FALCON_ED(2) FALCON_ED(3) FALCON_ED(4) FALCON_ED(5) FALCON_ED(6) FALCON_ED(7)
+  FALCON_ED(8) FALCON_ED(9) FALCON_ED(10) FALCON_ED(11) FALCON_ED(12) FALCON_ED(13) FALCON_ED(14)
+#undef FALCON_ED
+  float kr[16], pr[16];
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) {
+    const f32x4 p4 = ld4(&sm.pq[i][16 * B + 4 * s4]);
+    pr[4 * s4] = p4[0]; pr[4 * s4 + 1] = p4[1]; pr[4 * s4 + 2] = p4[2]; pr[4 * s4 + 3] = p4[3];
     if constexpr (kReg) {
-      float dk = 0.f;
-#pragma unroll
-      for (int k = 0; 4 * k < I; ++k) dk = fmaf(sm.kq[I][qq][k], u[k], dk);
-      rho = fmaf(-p[1], quad_sum(dk), rho);
+      const f32x4 k4 = ld4(&sm.kq[i][16 * B + 4 * s4]);
+      kr[4 * s4] = k4[0]; kr[4 * s4 + 1] = k4[1]; kr[4 * s4 + 2] = k4[2]; kr[4 * s4 + 3] = k4[3];
     }
-#pragma unroll
-    for (int k = 0; 4 * k < I; ++k) u[k] *= p[2];
-    const bool own = qq == (I & 3);
-    if (own) u[I >> 2] = rho;
-    float dp = 0.f;
-#pragma unroll
-    for (int k = 0; 4 * k <= I; ++k) dp = fmaf(sm.pq[I][qq][k], u[k], dp);
-    dp = quad_sum(dp);
-    if (own) ov[I >> 2] = p[3] + dp;
-    solve_rows<kReg, I + 1>(sm, jc, qq, u, ov);
   }
-}
-
-// Inclusive product over the 64 lanes of a wave (DPP shifts within 16-lane
-// rows, then the row totals carried across rows).
-__device__ __forceinline__ float lane_prefix_product(float v, int g) {
+  if constexpr (kReg) {
+    // forward substitution: after step sl, lane sl holds rho_{16B+sl}
+    float nc[15];
 #pragma unroll
-  for (int sh = 1; sh < 16; sh <<= 1) {
-    float w;
-    switch (sh) {
-      case 1: w = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, 1.0f), __builtin_bit_cast(int, v), 0x111, 0xf, 0xf, false)); break;
-      case 2: w = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, 1.0f), __builtin_bit_cast(int, v), 0x112, 0xf, 0xf, false)); break;
-      case 4: w = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, 1.0f), __builtin_bit_cast(int, v), 0x114, 0xf, 0xf, false)); break;
-      default: w = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, 1.0f), __builtin_bit_cast(int, v), 0x118, 0xf, 0xf, false)); break;
-    }
-    v *= w;
+    for (int sl = 0; sl < 15; ++sl) nc[sl] = -eta * ed[sl] * kr[sl];
+    // a += a[lane SL] * nc[SL]: one multiply-add whose first source is read from
+    // lane SL of the 16-lane row; the leading s_nop covers the DPP
+    // read-after-write hazard on a
+#define FALCON_SUB(SL)                                                                                \
+  asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %0, %1 row_newbcast:" #SL " row_mask:0xf bank_mask:0xf" \
+               : "+v"(a) : "v"(nc[SL]));
+    FALCON_SUB(0) FALCON_SUB(1) FALCON_SUB(2) FALCON_SUB(3) FALCON_SUB(4) FALCON_SUB(5) FALCON_SUB(6)
+    FALCON_SUB(7) FALCON_SUB(8) FALCON_SUB(9) FALCON_SUB(10) FALCON_SUB(11) FALCON_SUB(12) FALCON_SUB(13)
+    FALCON_SUB(14)
+#undef FALCON_SUB
   }
-  const float r0 = lane_value(v, 15), r1 = lane_value(v, 31), r2 = lane_value(v, 47);
-  return v * (g >= 1 ? r0 : 1.0f) * (g >= 2 ? r1 : 1.0f) * (g >= 3 ? r2 : 1.0f);
+  const float rho = a;
+  // in-block part of the read: e^{g_i-g_s} = gamma_i e^{g_{i-1}-g_s} for s < i
+  // (ed is 0 for s >= i), and the diagonal term q_i.x_i rho_i
+  {
+    float o0 = 0.f, o1 = 0.f;
+#define FALCON_RD(SL, ACC)                                                                              \
+  {                                                                                                     \
+    const float cf = ed[SL] * pr[SL];                                                                   \
+    asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_newbcast:" #SL " row_mask:0xf bank_mask:0xf" \
+                 : "+v"(ACC) : "v"(rho), "v"(cf));                                                      \
+  }
+    FALCON_RD(0, o0) FALCON_RD(1, o1) FALCON_RD(2, o0) FALCON_RD(3, o1) FALCON_RD(4, o0) FALCON_RD(5, o1)
+    FALCON_RD(6, o0) FALCON_RD(7, o1) FALCON_RD(8, o0) FALCON_RD(9, o1) FALCON_RD(10, o0) FALCON_RD(11, o1)
+    FALCON_RD(12, o0) FALCON_RD(13, o1) FALCON_RD(14, o0)
+#undef FALCON_RD
+    o += exp2_fast(lg) * (o0 + o1) + sm.pq[i][i] * rho;
+  }
+  sm.ob[i][jl] = bf(o);
+  // w to the end of this block: earlier entries decay by e^{g_last-g_carry},
+  // this block's entries are e^{g_last-g_s} rho_s
+  {
+    const float blk = exp2_fast(glast - gcarry);
+#pragma unroll
+    for (int k = 0; k < B; ++k) sm.w[jl][16 * k + li] *= blk;
+    sm.w[jl][i] = exp2_fast(glast - gi) * rho;
+  }
+  gcarry = glast;
 }
 
 template <bool kReg>
-__global__ void __launch_bounds__(64)
+__global__ void __launch_bounds__(kThreads, 2)
 falcon2_chunked_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restrict__ phi_q,
                        const bf16_t* __restrict__ v, const float* __restrict__ beta,
                        const float* __restrict__ lam, const float* S0,
                        const bf16_t* __restrict__ k_prev, bf16_t* __restrict__ o, float* S_T, int T,
                        float eps, float eps_gamma) {
   __shared__ PcSmem sm;
-  const int l = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;   // wave-uniform
   const int g = l >> 4, c16 = l & 15;
-  const int jc = l >> 2, qq = l & 3;              // recurrence layout: column jc, sub-lane qq
+  const int jl = 4 * w + g, li = c16;                 // solve layout: column jl of the slice, block row li
   const int64_t bh = blockIdx.x >> 2;
   const int j0 = (blockIdx.x & 3) * kSlice;
   const bool fresh = (k_prev == nullptr);
@@ -127,104 +245,25 @@ falcon2_chunked_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restric
   const float* Lm = lam + bh * T;
   const bf16_t* kp = k_prev ? k_prev + bh * kD : nullptr;
 
-  // upper parts of the Gram buffers are never written and stay zero
-  for (int e = l; e < kC * 4 * 16; e += 64) {
-    (&sm.kq[0][0][0])[e] = 0.f;
-    (&sm.pq[0][0][0])[e] = 0.f;
-  }
-  // S[fb]: lane holds S[16fb+4g+r][j0+c16]
+  // wave 0 holds the state of the slice: S[fb], lane holds S[16fb+4g+r][j0+c16]
   f32x4 S[4];
 #pragma unroll
   for (int fb = 0; fb < 4; ++fb)
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      S[fb][r] = S0 ? S0[(bh * kD + 16 * fb + 4 * g + r) * kD + j0 + c16] : 0.0f;
+      S[fb][r] = (w == 0 && S0) ? S0[(bh * kD + 16 * fb + 4 * g + r) * kD + j0 + c16] : 0.0f;
 
   const int nchunks = (T + kC - 1) / kC;
+  ChunkRegs R;
+  fetch_chunk(R, K, Q, V, Bt, Lm, kp, T, 0, j0, tid);
   for (int c = 0; c < nchunks; ++c) {
     const int t0 = c * kC;
-    // ---- stage: rows of keys and queries, this slice's values and gains --
-    {
-      bf16x8 xr[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int r = 8 * j + (l >> 3);
-        const int kt = t0 + r - 1;
-        const bf16_t* xsrc = kt < 0 ? (kp ? kp : K) : K + int64_t(kt < T ? kt : T - 1) * kD;
-        const int tok = t0 + r < T ? t0 + r : T - 1;
-        xr[j] = *reinterpret_cast<const bf16x8*>(xsrc + 8 * (l & 7));
-        const bf16x8 qr = *reinterpret_cast<const bf16x8*>(Q + int64_t(tok) * kD + 8 * (l & 7));
-        const int off = r * kD + 8 * seg_pos(r, l & 7);
-        *reinterpret_cast<bf16x8*>(sm.x + off) = xr[j];
-        *reinterpret_cast<bf16x8*>(sm.q + off) = qr;
-      }
-      // energies of rows 8 (l & 7) + (l >> 3) by a butterfly over 8 lanes
-      float p[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float e = 0.f;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const bf16x2 xv = {xr[j][2 * k], xr[j][2 * k + 1]};
-          e = __builtin_amdgcn_fdot2_f32_bf16(xv, xv, e, false);
-        }
-        p[j] = e;
-      }
-      float q4[4], q2[2];
-      {
-        const bool b = (l & 4) != 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) q4[k] = (b ? p[k + 4] : p[k]) + __shfl_xor(b ? p[k] : p[k + 4], 4);
-      }
-      {
-        const bool b = (l & 2) != 0;
-#pragma unroll
-        for (int k = 0; k < 2; ++k) q2[k] = (b ? q4[k + 2] : q4[k]) + __shfl_xor(b ? q4[k] : q4[k + 2], 2);
-      }
-      {
-        const bool b = (l & 1) != 0;
-        sm.en[8 * (l & 7) + (l >> 3)] = (b ? q2[1] : q2[0]) + __shfl_xor(b ? q2[0] : q2[1], 1);
-      }
-      const int tok = t0 + l < T ? t0 + l : T - 1;
-      sm.lm[l] = Lm[tok];
-      const bf16x8 va = *reinterpret_cast<const bf16x8*>(V + int64_t(tok) * kD + j0);
-      const bf16x8 vb = *reinterpret_cast<const bf16x8*>(V + int64_t(tok) * kD + j0 + 8);
-#pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const f32x4 bt = *reinterpret_cast<const f32x4*>(Bt + int64_t(tok) * kD + j0 + 4 * e4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = 4 * e4 + e;
-          sm.rp[l][j][0] = static_cast<float>(j < 8 ? va[j] : vb[j - 8]);
-          sm.rp[l][j][1] = bt[e];
-        }
-      }
-    }
-    // ---- shared products on the matrix cores -----------------------------
-    // Gram and read tiles (ib, sb), sb <= ib: lane holds rows i = 16ib+4g+r,
-    // column s = 16sb+c16
-#pragma unroll
-    for (int n = 0; n < 10; ++n) {
-      int ib, sb;
-      lower_tile(n, ib, sb);
-      const bf16x8 xs0 = ring_frag_c(sm.x, 16 * sb + c16, 0, g), xs1 = ring_frag_c(sm.x, 16 * sb + c16, 1, g);
-      f32x4 dk = zero4(), dp = zero4();
-      if (kReg) {
-        dk = mfma32(ring_frag_c(sm.x, 16 * ib + c16, 0, g), xs0, dk);
-        dk = mfma32(ring_frag_c(sm.x, 16 * ib + c16, 1, g), xs1, dk);
-      }
-      dp = mfma32(ring_frag_c(sm.q, 16 * ib + c16, 0, g), xs0, dp);
-      dp = mfma32(ring_frag_c(sm.q, 16 * ib + c16, 1, g), xs1, dp);
-      const int s = 16 * sb + c16;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * ib + 4 * g + r;
-        if (kReg) sm.kq[i][s & 3][s >> 2] = s < i ? dk[r] : 0.0f;
-        sm.pq[i][s & 3][s >> 2] = s <= i ? dp[r] : 0.0f;
-      }
-    }
-    // X S and Q S for this slice: lane holds rows 16ib+4g+r, column j0+c16
-    {
+    stage_chunk(sm, R, tid);
+    __syncthreads();
+    if (c + 1 < nchunks) fetch_chunk(R, K, Q, V, Bt, Lm, kp, T, t0 + kC, j0, tid);
+    // ---- products shared by all columns, on the matrix cores ---------------
+    if (w == 0) {
+      // X S and Q S for the slice: lane holds rows 16ib+4g+r, column j0+c16
       const bf16x8 s0 = frag_acc(S[0], S[1]);
       const bf16x8 s1 = frag_acc(S[2], S[3]);
 #pragma unroll
@@ -239,61 +278,61 @@ falcon2_chunked_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restric
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          sm.rp[16 * ib + 4 * g + r][c16][3] = aq[r];
-          if (kReg) sm.rp[16 * ib + 4 * g + r][c16][2] = ax[r];
+          sm.qs[16 * ib + 4 * g + r][c16] = aq[r];
+          if (kReg) sm.xs[16 * ib + 4 * g + r][c16] = ax[r];
+        }
+      }
+    } else {
+      // Gram and read tiles (ib, sb), sb <= ib: lane holds rows i = 16ib+4g+r,
+      // column s = 16sb+c16; waves 1..3 take tiles [0,4), [4,7), [7,10)
+      const int n0 = w == 1 ? 0 : w == 2 ? 4 : 7;
+      const int n1 = w == 1 ? 4 : w == 2 ? 7 : 10;
+      for (int n = n0; n < n1; ++n) {
+        int ib, sb;
+        lower_tile(n, ib, sb);
+        const bf16x8 xs0 = ring_frag_c(sm.x, 16 * sb + c16, 0, g), xs1 = ring_frag_c(sm.x, 16 * sb + c16, 1, g);
+        f32x4 dk = mfma32(ring_frag_c(sm.x, 16 * ib + c16, 0, g), xs0, zero4());
+        dk = mfma32(ring_frag_c(sm.x, 16 * ib + c16, 1, g), xs1, dk);
+        f32x4 dp = mfma32(ring_frag_c(sm.q, 16 * ib + c16, 0, g), xs0, zero4());
+        dp = mfma32(ring_frag_c(sm.q, 16 * ib + c16, 1, g), xs1, dp);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * ib + 4 * g + r;
+          sm.kq[i][16 * sb + c16] = dk[r];
+          sm.pq[i][16 * sb + c16] = dp[r];
+          if (ib == sb && 4 * g + r == c16) sm.en[i] = dk[r];
         }
       }
     }
-    // ---- per row and column: step sizes, decays, right-hand sides ---------
-    // lane l owns row i = l; e^{g_{i,j}} is the product of the row decays
+    __syncthreads();
+    // ---- per-column rows, block by block ------------------------------------
     {
-      const int t = t0 + l;
-      const bool live = t < T;
-      const float en = sm.en[l], lmi = sm.lm[l];
-      const float den = en + lmi + eps;
-      const float inv = (live && !(fresh && t == 0) && den != 0.0f) ? 1.0f / den : 0.0f;
-#pragma unroll 4
-      for (int j = 0; j < kSlice; ++j) {
-        const f32x4 in = sm.rp[l][j];                // v, beta, (X S), (Q S)
-        const float eta = in[1] * inv;
-        const float gam = live ? clamped_gamma(eta, lmi, eps_gamma) : 1.0f;
-        const float e_inc = lane_prefix_product(gam, g);
-        float e_exc = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-            __builtin_bit_cast(int, 1.0f), __builtin_bit_cast(int, e_inc), 0x111, 0xf, 0xf, false));
-        {
-          const float c15 = lane_value(e_inc, 15), c31 = lane_value(e_inc, 31), c47 = lane_value(e_inc, 47);
-          if (c16 == 0) e_exc = g == 0 ? 1.0f : g == 1 ? c15 : g == 2 ? c31 : c47;
-        }
-        const float a = kReg ? eta * (in[0] - e_exc * in[2]) : eta * in[0];
-        sm.rp[l][j] = f32x4{a, eta, gam, e_inc * in[3]};
-        if (l == 63) sm.e63[j] = e_inc;
-      }
+      float gcarry = 0.f;
+      solve_block<kReg, 0>(sm, jl, li, t0, T, fresh, eps, eps_gamma, gcarry);
+      solve_block<kReg, 1>(sm, jl, li, t0, T, fresh, eps, eps_gamma, gcarry);
+      solve_block<kReg, 2>(sm, jl, li, t0, T, fresh, eps, eps_gamma, gcarry);
+      solve_block<kReg, 3>(sm, jl, li, t0, T, fresh, eps, eps_gamma, gcarry);
+      if (li == 0) sm.e63[jl] = exp2_fast(gcarry);
     }
-    // ---- per-column rows: residual system, weights, outputs --------------
-    float u[16], ov[16];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) { u[k] = 0.f; ov[k] = 0.f; }
-    solve_rows<kReg, 0>(sm, jc, qq, u, ov);
-#pragma unroll
-    for (int k = 0; k < 16; ++k) sm.rp[4 * k + qq][jc][0] = ov[k];
-    // ---- outputs (row l of the slice) and the state update -----------------
-    {
-      const int tok = t0 + l;
-      if (tok < T) {
-        uint32_t w[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) w[e] = pack_bf16x2(sm.rp[l][2 * e][0], sm.rp[l][2 * e + 1][0]);
-        uint4* dst = reinterpret_cast<uint4*>(o + (bh * T + tok) * kD + j0);
-        dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-        dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
-      }
+    __syncthreads();
+    // ---- outputs of the chunk (rows of the slice) -----------------------------
+    if (tid < 2 * kC) {
+      const int r = tid >> 1;
+      if (t0 + r < T)
+        *reinterpret_cast<uint4*>(o + (bh * T + t0 + r) * kD + j0 + 8 * (tid & 1)) =
+            *reinterpret_cast<const uint4*>(&sm.ob[r][8 * (tid & 1)]);
     }
-#pragma unroll
-    for (int k = 0; k < 16; ++k) sm.ut[jc][4 * k + qq] = bf(u[k]);
-    {
+    // ---- state update (wave 0): S <- e^{g_63} S + X^T W ------------------------
+    if (w == 0) {
       const float dec = sm.e63[c16];
-      const bf16x8 u0 = frag_lds(&sm.ut[c16][0], 0, g);
-      const bf16x8 u1 = frag_lds(&sm.ut[c16][0], 32, g);
+      // frag(W^T): lane holds w_{c16, 32m + kperm(g, e)}
+      bf16x8 u[2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const f32x4 lo = ld4(&sm.w[c16][32 * m + 4 * g]);
+        const f32x4 hi = ld4(&sm.w[c16][32 * m + 16 + 4 * g]);
+        u[m] = frag_acc(lo, hi);
+      }
 #pragma unroll
       for (int fb = 0; fb < 4; ++fb) {
         const bf16x8 sel = select_frag(fb & 1, g, c16);
@@ -301,12 +340,13 @@ falcon2_chunked_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restric
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb) d[sb] = mfma32(ring_frag_c(sm.x, 16 * sb + c16, fb >> 1, g), sel, zero4());
         f32x4 acc = S[fb] * dec;
-        acc = mfma32(frag_acc(d[0], d[1]), u0, acc);
-        S[fb] = mfma32(frag_acc(d[2], d[3]), u1, acc);
+        acc = mfma32(frag_acc(d[0], d[1]), u[0], acc);
+        S[fb] = mfma32(frag_acc(d[2], d[3]), u[1], acc);
       }
     }
+    __syncthreads();
   }
-  if (S_T) {
+  if (w == 0 && S_T) {
 #pragma unroll
     for (int fb = 0; fb < 4; ++fb)
 #pragma unroll
@@ -323,13 +363,13 @@ bool chunked_percol_applies(const ProblemArgs& a) {
 hipError_t launch_chunked_percol(const ProblemArgs& a, hipStream_t st) {
   const dim3 grid(unsigned(int64_t(a.B) * a.H * (kD / kSlice)));
   if (a.variant == kF2)
-    hipLaunchKernelGGL(falcon2_chunked_kernel<true>, grid, dim3(64), 0, st,
+    hipLaunchKernelGGL(falcon2_chunked_kernel<true>, grid, dim3(kThreads), 0, st,
                        static_cast<const bf16_t*>(a.phi_k), static_cast<const bf16_t*>(a.phi_q),
                        static_cast<const bf16_t*>(a.v), a.beta, a.lam, a.S0,
                        static_cast<const bf16_t*>(a.k_prev), static_cast<bf16_t*>(a.o), a.S_T, a.T, a.eps,
                        a.eps_gamma);
   else
-    hipLaunchKernelGGL(falcon2_chunked_kernel<false>, grid, dim3(64), 0, st,
+    hipLaunchKernelGGL(falcon2_chunked_kernel<false>, grid, dim3(kThreads), 0, st,
                        static_cast<const bf16_t*>(a.phi_k), static_cast<const bf16_t*>(a.phi_q),
                        static_cast<const bf16_t*>(a.v), a.beta, a.lam, a.S0,
                        static_cast<const bf16_t*>(a.k_prev), static_cast<bf16_t*>(a.o), a.S_T, a.T, a.eps,
