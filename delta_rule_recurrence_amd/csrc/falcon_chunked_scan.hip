@@ -9,14 +9,18 @@
 // (the log-space renormalisation of Section 4.4 with window 1, applied per
 // chunk).  A sequence is cut into tiles of kTileChunks chunks and the forward
 // runs as three launches, none of which waits on another workgroup:
-//   1. every tile (one wave each) sweeps its chunks from S = 0 and stores its
-//      local state change ("aggregate") and its total log decay;
+//   1. every tile sweeps its chunks from S = 0 and stores its local state
+//      change ("aggregate") and its total log decay;
 //   2. per sequence, an element-parallel scan over the tiles forms the state
 //      at each tile's start, S_{t+1} = e^{L_t} S_t + aggregate_t, streaming
 //      the aggregates (this is the only sequential step, and it is a
 //      per-element multiply-add);
 //   3. every tile sweeps its chunks again from its true start state, writing
 //      the outputs.
+// A tile is one workgroup of four waves; wave w owns value block w (16
+// columns) of the state and of the outputs.  Per chunk, wave 0 derives the
+// gates while every wave forms its share of the raw transposes and of the read
+// mask; the scaled key fragments and mask rows are exchanged through LDS.
 // Aggregates and start states live in the workspace in "register order":
 // entry ((fb * 4 + cb) * 64 + lane) * 4 + r holds S[16 fb + 4 g + r][16 cb + c16]
 // with g = lane >> 4, c16 = lane & 15, so each wave moves them with 16-byte
@@ -39,16 +43,23 @@ constexpr int kScanThreads = 256;   // a scan block covers 1024 state elements, 
 constexpr int kScanDepth = 8;       // tiles of aggregates in flight per scan thread
 constexpr int kStateFloats = kD * kD;
 
-// One staged chunk: key, query and value rows (swizzled) and its gates.
-struct Stage {
-  uint16_t x[kC * kD];            // keys phi(k_{t0+r-1})
-  uint16_t q[kC * kD];            // queries phi(q_{t0+r})
-  uint16_t v[kC * kD];            // values v_{t0+r}
+constexpr int kTileThreads = 256;   // four waves per tile
+
+// One staged chunk, the chunk's gates, and the fragments the waves exchange.
+// The aggregate pass needs no queries and no read mask.
+template <bool kOut>
+struct TileSmem {
+  uint16_t x[kC * kD];            // keys phi(k_{t0+r-1}), swizzled rows
+  uint16_t q[kOut ? kC * kD : 8]; // queries phi(q_{t0+r}), swizzled rows
+  uint16_t v[kC * kD];            // values v_{t0+r}, swizzled rows
+  uint16_t xh[4 * 2 * 64 * 8];    // frag((Diag(e^{g_63-g}) X)^T)[fb][m]
+  uint16_t mf[kOut ? 4 * 2 * 64 * 8 : 8];   // frag(M)[ib][m], M = tril0(Q X^T) o [e^{g_i-g_s}]
   float graw[kC];                 // g_s, token order
   float sxh[kC];                  // e^{g_63 - g_s}
   float eta[kC];                  // eta_s
   float graw_t[kC];               // g_i at [c16 * 4 + ib] for i = 16 ib + c16
   float gexp_t[kC];               // e^{g_i}, same order
+  float glast;                    // g_63
 };
 
 // Workspace: per tile its aggregate, its start state (both register order,
@@ -78,152 +89,47 @@ struct Seq {
   int T;
 };
 
-// Rows t0 .. t0+63 of a [T, 64] matrix (clamped to T - 1) into a swizzled
-// stage buffer.
-__device__ __forceinline__ void stage_rows(uint16_t* dst, const bf16_t* src, int t0, int T, int l) {
-  bf16x8 v[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = 8 * j + (l >> 3);
-    const int tok = t0 + r < T ? t0 + r : T - 1;
-    v[j] = *reinterpret_cast<const bf16x8*>(src + int64_t(tok) * kD + 8 * (l & 7));
-  }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = 8 * j + (l >> 3);
-    *reinterpret_cast<bf16x8*>(dst + r * kD + 8 * seg_pos(r, l & 7)) = v[j];
-  }
-}
-
-// Stages chunk c (all of it, or keys and values only) and its gates.  One
-// wave: every LDS access is in program order, so no barrier is needed.
-__device__ __forceinline__ float stage_chunk(Stage& st, const Seq& sq, int c, int l, bool with_q,
-                                             float eps, float eps_gamma, bool fresh) {
-  const int t0 = c * kC;
-  const int T = sq.T;
-  const int g = l >> 4, c16 = l & 15;
-  // one matrix at a time: 8 coalesced 16-byte loads (8 whole rows each), then
-  // their swizzled LDS writes; the key registers stay live for the gates
-  bf16x8 x[8];
-  const int tok = t0 + l < T ? t0 + l : T - 1;
-  const float beta = sq.beta[tok], lam = sq.lam[tok];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = 8 * j + (l >> 3);
-    const int kt = t0 + r - 1;
-    const bf16_t* xs = kt < 0 ? (sq.k_prev ? sq.k_prev : sq.K) : sq.K + int64_t(kt < T ? kt : T - 1) * kD;
-    x[j] = *reinterpret_cast<const bf16x8*>(xs + 8 * (l & 7));
-  }
-  stage_rows(st.v, sq.V, t0, T, l);
-  if (with_q) stage_rows(st.q, sq.Q, t0, T, l);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = 8 * j + (l >> 3);
-    *reinterpret_cast<bf16x8*>(st.x + r * kD + 8 * seg_pos(r, l & 7)) = x[j];
-  }
-  float eta, gi, gprev, glast;
-  chunk_gates(x, beta, lam, t0 + l, T, eps, eps_gamma, fresh, l, eta, gi, gprev, glast);
-  st.graw[l] = gi;
-  st.sxh[l] = __expf(glast - gi);
-  st.eta[l] = eta;
-  st.graw_t[c16 * 4 + g] = gi;
-  st.gexp_t[c16 * 4 + g] = __expf(gi);
-  return glast;
-}
-
-// The rows of one chunk held in registers (coalesced loads: 8 whole rows per
-// instruction), so the next chunk's loads can be in flight while the current
-// one is computed.
-struct ChunkRegs {
-  bf16x8 x[8], q[8], v[8];
-  float beta, lam;
+// This wave's rows (16 w .. 16 w + 15) of the next chunk, held in registers
+// so their loads are in flight while the current chunk is computed.
+struct WaveRows {
+  bf16x8 x[2], q[2], v[2];
+  float beta, lam;                // wave 0: gates of token c * 64 + lane
 };
 
-__device__ __forceinline__ void fetch_chunk(ChunkRegs& R, const Seq& sq, int c, int l) {
+__device__ __forceinline__ void fetch_rows(WaveRows& R, const Seq& sq, int c, int w, int l, bool with_q) {
   const int t0 = c * kC;
   const int T = sq.T;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = 8 * j + (l >> 3);
+  for (int j = 0; j < 2; ++j) {
+    const int r = 16 * w + 8 * j + (l >> 3);
     const int kt = t0 + r - 1;
     const bf16_t* xs = kt < 0 ? (sq.k_prev ? sq.k_prev : sq.K) : sq.K + int64_t(kt < T ? kt : T - 1) * kD;
     const int tok = t0 + r < T ? t0 + r : T - 1;
     R.x[j] = *reinterpret_cast<const bf16x8*>(xs + 8 * (l & 7));
-    R.q[j] = *reinterpret_cast<const bf16x8*>(sq.Q + int64_t(tok) * kD + 8 * (l & 7));
     R.v[j] = *reinterpret_cast<const bf16x8*>(sq.V + int64_t(tok) * kD + 8 * (l & 7));
+    if (with_q) R.q[j] = *reinterpret_cast<const bf16x8*>(sq.Q + int64_t(tok) * kD + 8 * (l & 7));
   }
-  const int tok = t0 + l < T ? t0 + l : T - 1;
-  R.beta = sq.beta[tok];
-  R.lam = sq.lam[tok];
+  if (w == 0) {
+    const int tok = t0 + l < T ? t0 + l : T - 1;
+    R.beta = sq.beta[tok];
+    R.lam = sq.lam[tok];
+  }
 }
 
-// Writes fetched rows into the stage and derives the chunk's gates; returns g_63.
-__device__ __forceinline__ float commit_chunk(Stage& st, const ChunkRegs& R, int c, int T, int l,
-                                              float eps, float eps_gamma, bool fresh) {
-  const int g = l >> 4, c16 = l & 15;
+template <bool kOut>
+__device__ __forceinline__ void commit_rows(TileSmem<kOut>& sm, const WaveRows& R, int w, int l) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = 8 * j + (l >> 3);
+  for (int j = 0; j < 2; ++j) {
+    const int r = 16 * w + 8 * j + (l >> 3);
     const int off = r * kD + 8 * seg_pos(r, l & 7);
-    *reinterpret_cast<bf16x8*>(st.x + off) = R.x[j];
-    *reinterpret_cast<bf16x8*>(st.q + off) = R.q[j];
-    *reinterpret_cast<bf16x8*>(st.v + off) = R.v[j];
-  }
-  float eta, gi, gprev, glast;
-  chunk_gates(R.x, R.beta, R.lam, c * kC + l, T, eps, eps_gamma, fresh, l, eta, gi, gprev, glast);
-  st.graw[l] = gi;
-  st.sxh[l] = __expf(glast - gi);
-  st.eta[l] = eta;
-  st.graw_t[c16 * 4 + g] = gi;
-  st.gexp_t[c16 * 4 + g] = __expf(gi);
-  return glast;
-}
-
-// Diag(eta) V for value block cb, as fragments over tokens (k) with lane
-// column = value column 16 cb + c16: B operand of the state update, A
-// operand of the intra-chunk read.
-__device__ __forceinline__ void value_frags(const Stage& st, int cb, int g, int c16, bf16x8 (&vt)[2]) {
-  const bf16x8 sel = select_frag(cb & 1, g, c16);
-  f32x4 d[4];
-#pragma unroll
-  for (int sb = 0; sb < 4; ++sb)
-    d[sb] = mfma32(ring_frag_c(st.v, 16 * sb + c16, cb >> 1, g), sel, zero4());   // V[16sb+4g+r][16cb+c16]
-#pragma unroll
-  for (int m = 0; m < 2; ++m)
-    vt[m] = frag_acc(d[2 * m] * ld4(&st.eta[32 * m + 4 * g]), d[2 * m + 1] * ld4(&st.eta[32 * m + 16 + 4 * g]));
-}
-
-// (Diag(e^{g_63-g}) X)^T for key block fb: A operand, lane row = feature.
-__device__ __forceinline__ void key_frags(const Stage& st, int fb, int g, int c16, bf16x8 (&xh)[2]) {
-  const bf16x8 sel = select_frag(fb & 1, g, c16);
-  f32x4 d[4];
-#pragma unroll
-  for (int sb = 0; sb < 4; ++sb)
-    d[sb] = mfma32(ring_frag_c(st.x, 16 * sb + c16, fb >> 1, g), sel, zero4());   // X[16sb+4g+r][16fb+c16]
-#pragma unroll
-  for (int m = 0; m < 2; ++m)
-    xh[m] = frag_acc(d[2 * m] * ld4(&st.sxh[32 * m + 4 * g]), d[2 * m + 1] * ld4(&st.sxh[32 * m + 16 + 4 * g]));
-}
-
-// Value block cb of S <- e^{g_63} S + (Diag(e^{g_63-g}) X)^T Diag(eta) V;
-// S[fb][cb] holds S[16fb+4g+r][16cb+c16].
-__device__ __forceinline__ void state_update_cb(f32x4 (&S)[4][4], int cb, const bf16x8 (&xh)[4][2],
-                                                const bf16x8 (&vt)[2], float decay) {
-#pragma unroll
-  for (int fb = 0; fb < 4; ++fb) {
-    f32x4 acc = S[fb][cb] * decay;
-    acc = mfma32(xh[fb][0], vt[0], acc);
-    S[fb][cb] = mfma32(xh[fb][1], vt[1], acc);
+    *reinterpret_cast<bf16x8*>(sm.x + off) = R.x[j];
+    *reinterpret_cast<bf16x8*>(sm.v + off) = R.v[j];
+    if constexpr (kOut) *reinterpret_cast<bf16x8*>(sm.q + off) = R.q[j];
   }
 }
 
-__device__ __forceinline__ void store_state(float* dst, const f32x4 (&S)[4][4], int l) {
-#pragma unroll
-  for (int fb = 0; fb < 4; ++fb)
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-      *reinterpret_cast<f32x4*>(dst + ((fb * 4 + cb) * 64 + l) * 4) = S[fb][cb];
-}
+// Fragment slot [b][m] of a 64x64 fragment array.
+__device__ __forceinline__ int fslot(int b, int m, int l) { return ((b * 2 + m) * 64 + l) * 8; }
 
 struct TileArgs {
   const bf16_t* phi_k;
@@ -249,20 +155,124 @@ __device__ __forceinline__ Seq seq_of(const TileArgs& a, int64_t bh) {
   return sq;
 }
 
-// Stage reached through an opaque offset, so that LDS addresses are rebuilt
-// every chunk instead of being hoisted (and spilled) across the chunk loop.
-__device__ __forceinline__ Stage& opaque(Stage& st) {
-  int zero = 0;
-  asm volatile("" : "+v"(zero));
-  return *reinterpret_cast<Stage*>(reinterpret_cast<char*>(&st) + zero);
+// One chunk of a tile for wave w (value block w).  R holds the chunk's rows on
+// entry; after they are in LDS, chunk c_next (if < c_end) is fetched into R.
+template <bool kOut>
+__device__ __forceinline__ void tile_chunk(TileSmem<kOut>& sm, WaveRows& R, const Seq& sq, const TileArgs& a,
+                                           int c, int c_next, int c_end, int w, int l, bool fresh, f32x4 (&S)[4],
+                                           float& logd, bf16_t* o_bh) {
+  const int g = l >> 4, c16 = l & 15;
+  const int cb = w;
+  const int T = a.T;
+  commit_rows<kOut>(sm, R, w, l);
+  const float beta = R.beta, lam = R.lam;
+  __syncthreads();
+  if (c_next < c_end) fetch_rows(R, sq, c_next, w, l, kOut);
+  // ---- gates (wave 0); raw key block fb = w, value block cb = w, mask rows ib = w
+  if (w == 0) {
+    bf16x8 x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = 8 * j + (l >> 3);
+      x[j] = *reinterpret_cast<const bf16x8*>(sm.x + r * kD + 8 * seg_pos(r, l & 7));
+    }
+    float eta, gi, gprev, glast;
+    chunk_gates(x, beta, lam, c * kC + l, T, a.eps, a.eps_gamma, fresh, l, eta, gi, gprev, glast);
+    sm.graw[l] = gi;
+    sm.sxh[l] = __expf(glast - gi);
+    sm.eta[l] = eta;
+    sm.graw_t[c16 * 4 + g] = gi;
+    sm.gexp_t[c16 * 4 + g] = __expf(gi);
+    if (l == 0) sm.glast = glast;
+  }
+  f32x4 dx[4], dv[4];                             // X[16sb+4g+r][16w+c16], V[16sb+4g+r][16w+c16]
+  {
+    const bf16x8 sel = select_frag(w & 1, g, c16);
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+      dx[sb] = mfma32(ring_frag_c(sm.x, 16 * sb + c16, w >> 1, g), sel, zero4());
+      dv[sb] = mfma32(ring_frag_c(sm.v, 16 * sb + c16, w >> 1, g), sel, zero4());
+    }
+  }
+  f32x4 mt[4];                                    // (Q X^T)[16w+c16][16sb+4g+r] for sb <= w
+#pragma unroll
+  for (int sb = 0; sb < 4; ++sb) {
+    mt[sb] = zero4();
+    if constexpr (kOut) {
+      if (sb <= w) {
+        f32x4 acc = mfma32(ring_frag_c(sm.x, 16 * sb + c16, 0, g), ring_frag_c(sm.q, 16 * w + c16, 0, g), zero4());
+        mt[sb] = mfma32(ring_frag_c(sm.x, 16 * sb + c16, 1, g), ring_frag_c(sm.q, 16 * w + c16, 1, g), acc);
+      }
+    }
+  }
+  __syncthreads();                                // gates ready
+  // ---- scale: Xh^T block w and mask rows w to LDS, Diag(eta) V^T block w kept
+  bf16x8 vt[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    vt[m] = frag_acc(dv[2 * m] * ld4(&sm.eta[32 * m + 4 * g]), dv[2 * m + 1] * ld4(&sm.eta[32 * m + 16 + 4 * g]));
+    store_frag(&sm.xh[fslot(w, m, l)],
+               frag_acc(dx[2 * m] * ld4(&sm.sxh[32 * m + 4 * g]), dx[2 * m + 1] * ld4(&sm.sxh[32 * m + 16 + 4 * g])));
+  }
+  if constexpr (kOut) {
+    const int i = 16 * w + c16;
+    const float gi = sm.graw[i];
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+      const f32x4 gs = ld4(&sm.graw[16 * sb + 4 * g]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mt[sb][r] = 16 * sb + 4 * g + r <= i ? __expf(gi - gs[r]) * mt[sb][r] : 0.0f;
+    }
+    store_frag(&sm.mf[fslot(w, 0, l)], frag_acc(mt[0], mt[1]));
+    store_frag(&sm.mf[fslot(w, 1, l)], frag_acc(mt[2], mt[3]));
+  }
+  const float e63 = __expf(sm.glast);
+  if (w == 0) logd += sm.glast;
+  __syncthreads();                                // key fragments and mask complete
+  if constexpr (kOut) {
+    // O^T tiles of value block cb: e^{g_i} S^T Q^T + (Diag(eta) V)^T M^T;
+    // lane holds o[t0+16ib+c16][16cb+4g+r]
+    const f32x4 gexp_i = ld4(&sm.gexp_t[c16 * 4]);
+    const bf16x8 s0 = frag_acc(S[0], S[1]);
+    const bf16x8 s1 = frag_acc(S[2], S[3]);
+    const int t0 = c * kC;
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib) {
+      const int i = 16 * ib + c16;
+      f32x4 acc = mfma32(s0, ring_frag_p(sm.q, i, 0, g), zero4());
+      acc = mfma32(s1, ring_frag_p(sm.q, i, 1, g), acc);
+      acc = acc * gexp_i[ib];
+      acc = mfma32(vt[0], load_frag(&sm.mf[fslot(ib, 0, l)]), acc);
+      if (ib >= 2) acc = mfma32(vt[1], load_frag(&sm.mf[fslot(ib, 1, l)]), acc);
+      const int tok = t0 + i;
+      if (tok < T)
+        *reinterpret_cast<uint2*>(o_bh + int64_t(tok) * kD + 16 * cb + 4 * g) =
+            make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+    }
+  }
+  // S <- e^{g_63} S + (Diag(e^{g_63-g}) X)^T Diag(eta) V for value block cb
+  // (the key fragments are read after the outputs, so fewer registers are live)
+#pragma unroll
+  for (int fb = 0; fb < 4; ++fb) {
+    f32x4 acc = S[fb] * e63;
+    acc = mfma32(load_frag(&sm.xh[fslot(fb, 0, l)]), vt[0], acc);
+    S[fb] = mfma32(load_frag(&sm.xh[fslot(fb, 1, l)]), vt[1], acc);
+  }
+  __syncthreads();                                // the stage is free for the next chunk
 }
 
-// ---- launch 1: tile aggregates ------------------------------------------------
-__global__ void __launch_bounds__(64, 2)
-falcon1a_tile_agg_kernel(TileArgs a, ScanWorkspace ws) {
-  __shared__ Stage st_;
-  const int l = threadIdx.x;
-  const int g = l >> 4, c16 = l & 15;
+// ---- launches 1 and 3: a tile's chunks, four waves --------------------------
+// kOut = false: sweep from S = 0 and store the tile's aggregate and log decay.
+// kOut = true: sweep from the tile's start state and write the outputs.
+// Each wave fetches its rows of the next chunk while the current one is
+// computed.
+template <bool kOut>
+__global__ void __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(kOut ? 3 : 4)))
+falcon1a_tile_kernel(TileArgs a, ScanWorkspace ws) {
+  __shared__ TileSmem<kOut> sm;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;   // wave-uniform
+  const int cb = w;                               // value block of this wave
   const int t = blockIdx.x;                       // tile t of sequence t / ntiles_seq
   const int64_t bh = t / a.ntiles_seq;
   const int tile = t % a.ntiles_seq;
@@ -271,29 +281,23 @@ falcon1a_tile_agg_kernel(TileArgs a, ScanWorkspace ws) {
   const int c1 = c0 + kTileChunks < nchunks ? c0 + kTileChunks : nchunks;
   const Seq sq = seq_of(a, bh);
   const bool fresh = (a.k_prev == nullptr);
-  f32x4 S[4][4];
+  // S[fb]: lane holds S[16fb+4g+r][16cb+c16]
+  f32x4 S[4];
 #pragma unroll
   for (int fb = 0; fb < 4; ++fb)
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) S[fb][cb] = zero4();
+    S[fb] = kOut ? *reinterpret_cast<const f32x4*>(ws.start + int64_t(t) * kStateFloats + ((fb * 4 + cb) * 64 + l) * 4)
+                 : zero4();
+  bf16_t* o_bh = a.o + bh * a.T * kD;
   float logd = 0.f;
-  for (int c = c0; c < c1; ++c) {
-    Stage& st = opaque(st_);
-    const float glast = stage_chunk(st, sq, c, l, false, a.eps, a.eps_gamma, fresh);
-    const float decay = __expf(glast);
-    bf16x8 xh[4][2];
+  WaveRows R;
+  fetch_rows(R, sq, c0, w, l, kOut);
+  for (int c = c0; c < c1; ++c) tile_chunk<kOut>(sm, R, sq, a, c, c + 1, c1, w, l, fresh, S, logd, o_bh);
+  if (!kOut) {
 #pragma unroll
-    for (int fb = 0; fb < 4; ++fb) key_frags(st, fb, g, c16, xh[fb]);
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      bf16x8 vt[2];
-      value_frags(st, cb, g, c16, vt);
-      state_update_cb(S, cb, xh, vt, decay);
-    }
-    logd += glast;
+    for (int fb = 0; fb < 4; ++fb)
+      *reinterpret_cast<f32x4*>(ws.agg + int64_t(t) * kStateFloats + ((fb * 4 + cb) * 64 + l) * 4) = S[fb];
+    if (w == 0 && l == 0) ws.logdecay[t] = logd;
   }
-  store_state(ws.agg + int64_t(t) * kStateFloats, S, l);
-  if (l == 0) ws.logdecay[t] = logd;
 }
 
 // ---- launch 2: start state of every tile -------------------------------------
@@ -345,93 +349,6 @@ falcon1a_tile_scan_kernel(const float* S0, float* S_T, int ntiles_seq, ScanWorks
   }
 }
 
-// ---- launch 3: outputs from each tile's start state --------------------------
-__global__ void __launch_bounds__(64)
-falcon1a_tile_out_kernel(TileArgs a, ScanWorkspace ws) {
-  __shared__ Stage st_;
-  const int l = threadIdx.x;
-  const int g = l >> 4, c16 = l & 15;
-  const int t = blockIdx.x;
-  const int64_t bh = t / a.ntiles_seq;
-  const int tile = t % a.ntiles_seq;
-  const int nchunks = (a.T + kC - 1) / kC;
-  const int c0 = tile * kTileChunks;
-  const int c1 = c0 + kTileChunks < nchunks ? c0 + kTileChunks : nchunks;
-  const Seq sq = seq_of(a, bh);
-  const bool fresh = (a.k_prev == nullptr);
-  const int T = a.T;
-  f32x4 S[4][4];
-  {
-    const float* src = ws.start + int64_t(t) * kStateFloats;
-#pragma unroll
-    for (int fb = 0; fb < 4; ++fb)
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) S[fb][cb] = *reinterpret_cast<const f32x4*>(src + ((fb * 4 + cb) * 64 + l) * 4);
-  }
-  bf16_t* o_bh = a.o + bh * T * kD;
-  ChunkRegs R;
-  fetch_chunk(R, sq, c0, l);
-  for (int c = c0; c < c1; ++c) {
-    Stage& st = opaque(st_);
-    const float glast = commit_chunk(st, R, c, T, l, a.eps, a.eps_gamma, fresh);
-    if (c + 1 < c1) fetch_chunk(R, sq, c + 1, l);
-    const float decay = __expf(glast);
-    const int t0 = c * kC;
-    // decayed read mask M^T tile (sb, ib) = X_sb Q_ib^T, s <= i, as B fragments
-    bf16x8 mfr[4][2];
-    {
-      const f32x4 gra_i = ld4(&st.graw_t[c16 * 4]);
-#pragma unroll
-      for (int ib = 0; ib < 4; ++ib) {
-        f32x4 mt[4];
-#pragma unroll
-        for (int sb = 0; sb < 4; ++sb) {
-          mt[sb] = zero4();
-          if (sb > ib) continue;
-          f32x4 acc = mfma32(ring_frag_c(st.x, 16 * sb + c16, 0, g), ring_frag_c(st.q, 16 * ib + c16, 0, g), zero4());
-          acc = mfma32(ring_frag_c(st.x, 16 * sb + c16, 1, g), ring_frag_c(st.q, 16 * ib + c16, 1, g), acc);
-          const f32x4 gs = ld4(&st.graw[16 * sb + 4 * g]);
-          const int i = 16 * ib + c16;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int s_ = 16 * sb + 4 * g + r;
-            mt[sb][r] = s_ <= i ? __expf(gra_i[ib] - gs[r]) * acc[r] : 0.0f;
-          }
-        }
-        mfr[ib][0] = frag_acc(mt[0], mt[1]);
-        mfr[ib][1] = frag_acc(mt[2], mt[3]);
-      }
-    }
-    bf16x8 xh[4][2];
-#pragma unroll
-    for (int fb = 0; fb < 4; ++fb) key_frags(st, fb, g, c16, xh[fb]);
-    const f32x4 gexp_i = ld4(&st.gexp_t[c16 * 4]);
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      bf16x8 vt[2];
-      value_frags(st, cb, g, c16, vt);
-      // O^T tiles of value block cb: e^{g_i} S^T Q^T + (Diag(eta) V)^T M^T;
-      // lane holds o[t0+16ib+c16][16cb+4g+r]
-      const bf16x8 s0 = frag_acc(S[0][cb], S[1][cb]);
-      const bf16x8 s1 = frag_acc(S[2][cb], S[3][cb]);
-#pragma unroll
-      for (int ib = 0; ib < 4; ++ib) {
-        const int i = 16 * ib + c16;
-        f32x4 acc = mfma32(s0, ring_frag_p(st.q, i, 0, g), zero4());
-        acc = mfma32(s1, ring_frag_p(st.q, i, 1, g), acc);
-        acc = acc * gexp_i[ib];
-        acc = mfma32(vt[0], mfr[ib][0], acc);
-        if (ib >= 2) acc = mfma32(vt[1], mfr[ib][1], acc);
-        const int tok = t0 + i;
-        if (tok < T)
-          *reinterpret_cast<uint2*>(o_bh + int64_t(tok) * kD + 16 * cb + 4 * g) =
-              make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
-      }
-      state_update_cb(S, cb, xh, vt, decay);
-    }
-  }
-}
-
 int64_t scan_tiles_per_seq(const ProblemArgs& a) {
   const int64_t nchunks = (int64_t(a.T) + kC - 1) / kC;
   return (nchunks + kTileChunks - 1) / kTileChunks;
@@ -470,10 +387,10 @@ hipError_t launch_chunked_scan(const ProblemArgs& a, hipStream_t st) {
   ta.ntiles_seq = int(nts);
   ta.eps = a.eps;
   ta.eps_gamma = a.eps_gamma;
-  hipLaunchKernelGGL(falcon1a_tile_agg_kernel, dim3(unsigned(ntiles)), dim3(64), 0, st, ta, ws);
+  hipLaunchKernelGGL(falcon1a_tile_kernel<false>, dim3(unsigned(ntiles)), dim3(kTileThreads), 0, st, ta, ws);
   hipLaunchKernelGGL(falcon1a_tile_scan_kernel, dim3(unsigned(BH * 4)), dim3(kScanThreads), 0, st, a.S0,
                      a.S_T, int(nts), ws);
-  hipLaunchKernelGGL(falcon1a_tile_out_kernel, dim3(unsigned(ntiles)), dim3(64), 0, st, ta, ws);
+  hipLaunchKernelGGL(falcon1a_tile_kernel<true>, dim3(unsigned(ntiles)), dim3(kTileThreads), 0, st, ta, ws);
   return hipGetLastError();
 }
 
