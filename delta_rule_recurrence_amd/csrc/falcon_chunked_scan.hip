@@ -170,14 +170,8 @@ __device__ __forceinline__ void tile_chunk(TileSmem<kOut>& sm, WaveRows& R, cons
   if (c_next < c_end) fetch_rows(R, sq, c_next, w, l, kOut);
   // ---- gates (wave 0); raw key block fb = w, value block cb = w, mask rows ib = w
   if (w == 0) {
-    bf16x8 x[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int r = 8 * j + (l >> 3);
-      x[j] = *reinterpret_cast<const bf16x8*>(sm.x + r * kD + 8 * seg_pos(r, l & 7));
-    }
     float eta, gi, gprev, glast;
-    chunk_gates(x, beta, lam, c * kC + l, T, a.eps, a.eps_gamma, fresh, l, eta, gi, gprev, glast);
+    chunk_gates(sm.x, beta, lam, c * kC + l, T, a.eps, a.eps_gamma, fresh, l, eta, gi, gprev, glast);
     sm.graw[l] = gi;
     sm.sxh[l] = __expf(glast - gi);
     sm.eta[l] = eta;

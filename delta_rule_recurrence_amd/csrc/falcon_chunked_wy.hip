@@ -257,14 +257,8 @@ falcon1_wy_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restrict__ p
   __syncthreads();
   // ---- a1: gates (wave 0) ----------------------------------------------------
   if (w == 0) {
-    bf16x8 x[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int r = 8 * j + (l >> 3);
-      x[j] = *reinterpret_cast<const bf16x8*>(sm.x + r * kD + 8 * seg_pos(r, l & 7));
-    }
     float eta, gi, gprev, glast;
-    chunk_gates(x, beta_l, lam_l, c * kC + l, T, eps, eps_gamma, fresh, l, eta, gi, gprev, glast);
+    chunk_gates(sm.x, beta_l, lam_l, c * kC + l, T, eps, eps_gamma, fresh, l, eta, gi, gprev, glast);
     sm.G.graw[l] = gi;
     sm.G.sxg[l] = eta * __expf(gprev);
     sm.G.sxh[l] = __expf(glast - gi);

@@ -123,48 +123,27 @@ __device__ __forceinline__ void lower_tile(int n, int& ib, int& sb) {
   sb = n - (ib * (ib + 1)) / 2;
 }
 
-// Gates of one 64-token chunk (a1) from staged key rows: lane l holds the
-// eight features 8 (l & 7) .. +7 of rows 8 j + (l >> 3) in x[j], and the gates
-// beta, lam of token `tok` = chunk start + l.  Returns, for row l: eta_l
-// (Eq. 3.4; 0 at the fresh start and past the sequence), the chunk-local
-// inclusive prefix g_l of the clamped log decays (Section 4.3, "Decay
-// positivity"; Section 4.4 log-space renormalisation applied per chunk),
-// g_{l-1} (0 for l = 0) and g_63.
-__device__ __forceinline__ void chunk_gates(const bf16x8 (&x)[8], float beta, float lam, int tok, int T,
+// Gates of one 64-token chunk (a1) from the staged key rows xs (64 swizzled
+// rows in LDS) and the gates beta, lam of token `tok` = chunk start + l.
+// Returns, for row l: eta_l (Eq. 3.4; 0 at the fresh start and past the
+// sequence), the chunk-local inclusive prefix g_l of the clamped log decays
+// (Section 4.3, "Decay positivity"; Section 4.4 log-space renormalisation
+// applied per chunk), g_{l-1} (0 for l = 0) and g_63.
+__device__ __forceinline__ void chunk_gates(const uint16_t* xs, float beta, float lam, int tok, int T,
                                             float eps, float eps_gamma, bool fresh, int l, float& eta,
                                             float& gi, float& gprev, float& glast) {
   const int g = l >> 4, c16 = l & 15;
-  // energies: a transposing butterfly over the 8 lanes of a row leaves lane
-  // l with the energy of row 8 (l & 7) + (l >> 3); one shuffle brings row l
-  // to lane l
-  float p[8];
+  // energy of row l: lane l reads its own row (eight 16-byte segments)
+  float energy = 0.f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    float e = 0.f;
+  for (int q = 0; q < 8; ++q) {
+    const bf16x8 v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(xs + l * kRowElems + 8 * seg_pos(l, q)));
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const bf16x2 xv = {x[j][2 * k], x[j][2 * k + 1]};
-      e = __builtin_amdgcn_fdot2_f32_bf16(xv, xv, e, false);
+      const bf16x2 xv = {v[2 * k], v[2 * k + 1]};
+      energy = __builtin_amdgcn_fdot2_f32_bf16(xv, xv, energy, false);
     }
-    p[j] = e;
   }
-  float q4[4], q2[2];
-  {
-    const bool b = (l & 4) != 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) q4[k] = (b ? p[k + 4] : p[k]) + __shfl_xor(b ? p[k] : p[k + 4], 4);
-  }
-  {
-    const bool b = (l & 2) != 0;
-#pragma unroll
-    for (int k = 0; k < 2; ++k) q2[k] = (b ? q4[k + 2] : q4[k]) + __shfl_xor(b ? q4[k] : q4[k + 2], 2);
-  }
-  float energy;
-  {
-    const bool b = (l & 1) != 0;
-    energy = (b ? q2[1] : q2[0]) + __shfl_xor(b ? q2[0] : q2[1], 1);
-  }
-  energy = __shfl(energy, 8 * (l & 7) + (l >> 3));
   eta = 0.f;
   float lg = 0.f;
   if (tok < T) {
