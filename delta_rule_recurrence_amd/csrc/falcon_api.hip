@@ -95,6 +95,50 @@ falcon_status empty_forward(const ProblemArgs& a, hipStream_t st) {
   return finish(falcon::launch_state_copy(a.S0, a.S_T, n, st));
 }
 
+// Validates the backward's arguments and fills the launch arguments.
+falcon_status check_backward(const falcon_problem* p, const void* phi_k, const void* phi_q,
+                             const void* v, const float* beta, const float* lam, const float* S0,
+                             const void* k_prev, const void* dO, const float* dS_T, float* dphi_k,
+                             float* dphi_q, float* dv, float* dbeta, float* dlam, float* dS0,
+                             float* dk_prev, ProblemArgs* out, falcon::BwdBuffers* buf) {
+  falcon_status s = check_problem(p);
+  if (s != FALCON_OK) return s;
+  if (p->variant != FALCON_1) return FALCON_ERR_VARIANT;
+  if (p->dk != 64 || p->dv != 64) return FALCON_ERR_SHAPE;
+  const int64_t bh = int64_t(p->B) * p->H;
+  const int64_t es = p->io_dtype == FALCON_BF16 ? 2 : 4;
+  const bool work = bh > 0 && p->T > 0;
+  if (work && (!phi_k || !phi_q || !v || !beta || !lam || !dO || !dphi_k || !dphi_q || !dv ||
+               !dbeta || !dlam))
+    return FALCON_ERR_NULL;
+  const void* ptrs[] = {phi_k, phi_q, v, beta, lam, S0, k_prev, dO, dS_T,
+                        dphi_k, dphi_q, dv, dbeta, dlam, dS0, dk_prev};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return FALCON_ERR_ALIGN;
+  const int64_t nt = bh * p->T * 64, ns = bh * 64 * 64;
+  const Range inputs[] = {{phi_k, nt * es}, {phi_q, nt * es}, {v, nt * es},
+                          {beta, bh * p->T * 4}, {lam, bh * p->T * 4}, {S0, ns * 4},
+                          {k_prev, bh * 64 * es}, {dO, nt * es}, {dS_T, ns * 4}};
+  const Range outputs[] = {{dphi_k, nt * 4}, {dphi_q, nt * 4}, {dv, nt * 4},
+                           {dbeta, bh * p->T * 4}, {dlam, bh * p->T * 4}, {dS0, ns * 4},
+                           {k_prev ? dk_prev : nullptr, bh * 64 * 4}};
+  for (int i = 0; i < 7; ++i) {
+    for (const Range& r : inputs)
+      if (overlap(outputs[i], r)) return FALCON_ERR_ALIAS;
+    for (int j = i + 1; j < 7; ++j)
+      if (overlap(outputs[i], outputs[j])) return FALCON_ERR_ALIAS;
+  }
+  *out = ProblemArgs{};
+  out->B = p->B; out->H = p->H; out->T = p->T; out->dk = p->dk; out->dv = p->dv;
+  out->variant = p->variant;
+  out->bf16 = p->io_dtype == FALCON_BF16;
+  out->eps = p->eps; out->eps_gamma = p->eps_gamma;
+  out->phi_k = phi_k; out->phi_q = phi_q; out->v = v; out->beta = beta; out->lam = lam;
+  out->S0 = S0; out->k_prev = k_prev;
+  *buf = falcon::BwdBuffers{dO, dS_T, dphi_k, dphi_q, dv, dbeta, dlam, dS0, k_prev ? dk_prev : nullptr};
+  return FALCON_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -157,6 +201,43 @@ falcon_status falcon_fwd_chunked(const falcon_problem* p, const void* phi_k, con
   if (int64_t(a.B) * a.H == 0 || a.T == 0) return empty_forward(a, stream);
   (void)hipGetLastError();
   return finish(falcon::launch_chunked(a, stream));
+}
+
+size_t falcon_bwd_workspace_bytes(const falcon_problem* p) {
+  if (check_problem(p) != FALCON_OK) return static_cast<size_t>(-1);
+  if (p->variant != FALCON_1 || p->dk != 64 || p->dv != 64) return static_cast<size_t>(-1);
+  ProblemArgs a{};
+  a.B = p->B; a.H = p->H; a.T = p->T; a.dk = p->dk; a.dv = p->dv; a.variant = p->variant;
+  return falcon::bwd_workspace_bytes(a);
+}
+
+falcon_status falcon_bwd_chunked(const falcon_problem* p, const void* phi_k, const void* phi_q,
+                                 const void* v, const float* beta, const float* lam,
+                                 const float* S0, const void* k_prev, const void* dO,
+                                 const float* dS_T, float* dphi_k, float* dphi_q, float* dv,
+                                 float* dbeta, float* dlam, float* dS0, float* dk_prev,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  ProblemArgs a;
+  falcon::BwdBuffers b;
+  falcon_status s = check_backward(p, phi_k, phi_q, v, beta, lam, S0, k_prev, dO, dS_T, dphi_k,
+                                   dphi_q, dv, dbeta, dlam, dS0, dk_prev, &a, &b);
+  if (s != FALCON_OK) return s;
+  const size_t need = falcon::bwd_workspace_bytes(a);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return FALCON_ERR_WORKSPACE;
+  if (workspace && !aligned16(workspace)) return FALCON_ERR_ALIGN;
+  a.workspace = workspace;
+  a.workspace_bytes = workspace_bytes;
+  const int64_t bh = int64_t(a.B) * a.H;
+  if (bh == 0) return FALCON_OK;
+  (void)hipGetLastError();
+  if (a.T == 0) {
+    // no token: dS0 = dS_T and the previous key reaches nothing
+    hipError_t e = hipSuccess;
+    if (b.dS0) e = falcon::launch_state_copy(b.dS_T, b.dS0, bh * 64 * 64, stream);
+    if (e == hipSuccess && b.dk_prev) e = falcon::launch_state_copy(nullptr, b.dk_prev, bh * 64, stream);
+    return finish(e);
+  }
+  return finish(falcon::launch_bwd(a, b, stream));
 }
 
 falcon_status falcon_decode_step(const falcon_problem* p, const void* phi_k_prev,

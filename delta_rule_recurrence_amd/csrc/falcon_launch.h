@@ -42,10 +42,27 @@ struct DecodeArgs {
   void* o;
 };
 
+// Gradient buffers of the Falcon-1 backward (all float32 except dO, which has
+// the io dtype).
+struct BwdBuffers {
+  const void* dO;
+  const float* dS_T;     // may be null (no loss on the final state)
+  float* dphi_k;
+  float* dphi_q;
+  float* dv;
+  float* dbeta;
+  float* dlam;
+  float* dS0;            // may be null
+  float* dk_prev;        // may be null; written only when k_prev is given
+};
+
 hipError_t launch_recurrent(const ProblemArgs& a, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_chunked(const ProblemArgs& a, hipStream_t st);
 size_t chunked_workspace_bytes(const ProblemArgs& a);
+// Falcon-1 backward (dk = dv = 64): workspace size and launch.
+size_t bwd_workspace_bytes(const ProblemArgs& a);
+hipError_t launch_bwd(const ProblemArgs& a, const BwdBuffers& b, hipStream_t st);
 // Copy S0 (or zeros when S0 is null) to S_T; used when there is no token.
 hipError_t launch_state_copy(const float* S0, float* S_T, int64_t n, hipStream_t st);
 

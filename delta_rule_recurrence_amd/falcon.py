@@ -41,6 +41,9 @@ _SIGNATURES = {
                                             _P, _P, _P, ctypes.c_int32, _P, ctypes.c_size_t, _P]),
     "falcon_decode_step": (ctypes.c_int32, [ctypes.POINTER(FalconProblem), _P, _P, _P, _P, _P,
                                             _P, _P, _P, _P]),
+    "falcon_bwd_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(FalconProblem)]),
+    "falcon_bwd_chunked": (ctypes.c_int32, [ctypes.POINTER(FalconProblem)] + [_P] * 17
+                           + [ctypes.c_size_t, _P]),
 }
 
 _lib = None
@@ -157,3 +160,43 @@ def falcon_decode_step(phi_k_prev, phi_q, v, beta, lam, S, *, variant="falcon1",
         ctypes.byref(p), _ptr(phi_k_prev), _ptr(phi_q), _ptr(v), _ptr(beta), _ptr(lam), _ptr(S),
         _ptr(is_first), _ptr(o), _stream(stream)))
     return o
+
+
+def falcon_bwd_workspace_bytes(problem: FalconProblem) -> int:
+    return int(load_library().falcon_bwd_workspace_bytes(ctypes.byref(problem)))
+
+
+def falcon_bwd_chunked(phi_k, phi_q, v, beta, lam, dO, *, S0=None, k_prev=None, dS_T=None,
+                       eps=1e-6, eps_gamma=1e-6, grads=None, workspace=None, stream=None):
+    """Gradients of ``<dO, o> + <dS_T, S_T>`` for the Falcon-1 forward.
+
+    Returns a dict with float32 tensors dphi_k, dphi_q, dv, dbeta, dlam, dS0
+    and dk_prev (None when ``k_prev`` is None).  ``grads`` may hold
+    preallocated outputs under the same names.
+    """
+    B, H, T, dk = phi_k.shape
+    dv_ = v.shape[-1]
+    dev = v.device
+    f32 = torch.float32
+    shapes = {"dphi_k": (B, H, T, dk), "dphi_q": (B, H, T, dk), "dv": (B, H, T, dv_),
+              "dbeta": (B, H, T), "dlam": (B, H, T), "dS0": (B, H, dk, dv_), "dk_prev": (B, H, dk)}
+    g = dict(grads or {})
+    for name, shape in shapes.items():
+        if g.get(name) is None and (name != "dk_prev" or k_prev is not None):
+            g[name] = torch.empty(shape, dtype=f32, device=dev)
+    if k_prev is None:
+        g["dk_prev"] = None
+    p = make_problem(B, H, T, dk, dv_, variant="falcon1", io_dtype=v.dtype, eps=eps,
+                     eps_gamma=eps_gamma)
+    need = falcon_bwd_workspace_bytes(p)
+    if need == ctypes.c_size_t(-1).value:
+        raise FalconError(-2)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().falcon_bwd_chunked(
+        ctypes.byref(p), _ptr(phi_k), _ptr(phi_q), _ptr(v), _ptr(beta), _ptr(lam), _ptr(S0),
+        _ptr(k_prev), _ptr(dO), _ptr(dS_T), _ptr(g["dphi_k"]), _ptr(g["dphi_q"]), _ptr(g["dv"]),
+        _ptr(g["dbeta"]), _ptr(g["dlam"]), _ptr(g["dS0"]), _ptr(g["dk_prev"]), _ptr(workspace),
+        wbytes, _stream(stream)))
+    return g

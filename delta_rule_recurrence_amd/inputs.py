@@ -49,6 +49,8 @@ WORKLOADS = {
     "f1_chunked_8x12x2048_d64": Workload("f1_chunked_8x12x2048_d64", "falcon1", 8, 12, 2048, 64, 64, 64, "bf16", 1),
     "f1a_chunked_2x12x16384_d64": Workload("f1a_chunked_2x12x16384_d64", "falcon1a", 2, 12, 16384, 64, 64, 64, "bf16", 2),
     "f2_chunked_8x12x2048_d64": Workload("f2_chunked_8x12x2048_d64", "falcon2", 8, 12, 2048, 64, 64, 64, "bf16", 3),
+    # the backward of the Falcon-1 training shape (C names the forward's chunk)
+    "f1_backward_8x12x2048_d64": Workload("f1_backward_8x12x2048_d64", "falcon1", 8, 12, 2048, 64, 64, 64, "bf16", 5),
 }
 
 # Decode workload: batch 512, 12 heads, d = 128, 1000 steps after a prefix.
@@ -99,6 +101,19 @@ def make_inputs(B, H, T, dk, dv, *, seed, io_dtype="bf16", per_column_beta=False
 def workload_inputs(w: Workload):
     return make_inputs(w.B, w.H, w.T, w.dk, w.dv, seed=w.seed, io_dtype=w.io_dtype,
                        per_column_beta=w.variant in ("falcon2", "falcon2a"))
+
+
+def make_cotangents(B, H, T, dv, *, seed, io_dtype="bf16", dk=None, with_state=False):
+    """Seeded upstream gradients for the backward: ``dO`` ``[B,H,T,dv]`` in
+    the I/O dtype (N(0,1) scaled by 1/sqrt(dv), rounded once) and, when
+    ``with_state``, ``dS_T`` ``[B,H,dk,dv]`` float32 (N(0,1) * 0.1), drawn in
+    that order from ``default_rng([seed, 1])``."""
+    rng = np.random.default_rng([seed, 1])
+    out = {"dO": _round(rng.standard_normal((B, H, T, dv)) / np.sqrt(dv), io_dtype), "dS_T": None}
+    if with_state:
+        dk = dv if dk is None else dk
+        out["dS_T"] = torch.from_numpy((rng.standard_normal((B, H, dk, dv)) * 0.1).astype(np.float32))
+    return out
 
 
 def random_state(shape, *, seed, scale=0.1):

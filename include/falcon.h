@@ -165,6 +165,53 @@ falcon_status falcon_decode_step(const falcon_problem* p,
                                  float* S, const uint8_t* is_first,
                                  void* o, hipStream_t stream);
 
+/*
+ * falcon_bwd_chunked -- gradients of the FALCON_1 forward.  Training
+ * differentiates through the update itself (paper, Section 3); this entry
+ * point returns, for the scalar loss
+ *
+ *     L = <dO, o> + <dS_T, S_T>     (o, S_T the result of falcon_fwd_*),
+ *
+ * the derivatives of L with respect to every input.  It recomputes the
+ * forward in 32-token chunks (Section 4.2's chunk-parallel form), runs the
+ * state chain forward and the adjoint chain backward, and then the chunk-local
+ * reverse mode in parallel over chunks.  All arithmetic is float32.
+ *
+ * Supported: variant FALCON_1, dk = dv = 64, io dtype float32 or bfloat16,
+ * any T >= 0.  Other variants return FALCON_ERR_VARIANT, other widths
+ * FALCON_ERR_SHAPE.  The clamp of Section 4.3 is part of the forward: where it
+ * binds (eta lam > 1 - eps_gamma) gamma is constant and passes no gradient.
+ *
+ *  phi_k .. k_prev : the forward's inputs, as in falcon_fwd_chunked.
+ *  dO      : [B, H, T, dv] io dtype, dL/do.
+ *  dS_T    : [B, H, dk, dv] float32, dL/dS_T, or NULL for zero.
+ *  dphi_k, dphi_q : [B, H, T, dk] float32.  dphi_k[..., T-1, :] is 0 (the
+ *            last key is read by no token of this call).
+ *  dv      : [B, H, T, dv] float32.
+ *  dbeta, dlam : [B, H, T] float32.
+ *  dS0     : [B, H, dk, dv] float32, dL/dS_0, or NULL to skip.
+ *  dk_prev : [B, H, dk] float32, dL/dk_prev, or NULL to skip; ignored (not
+ *            written) when k_prev is NULL.
+ *  Every output must not overlap any input or another output
+ *  (FALCON_ERR_ALIAS).
+ *  workspace : device scratch of at least falcon_bwd_workspace_bytes(p)
+ *              bytes, 16-byte aligned (the per-chunk maps, the state
+ *              entering each chunk and the adjoint leaving it; 80 KiB per
+ *              32-token chunk per (b, h)).
+ */
+falcon_status falcon_bwd_chunked(const falcon_problem* p,
+                                 const void* phi_k, const void* phi_q, const void* v,
+                                 const float* beta, const float* lam,
+                                 const float* S0, const void* k_prev,
+                                 const void* dO, const float* dS_T,
+                                 float* dphi_k, float* dphi_q, float* dv,
+                                 float* dbeta, float* dlam, float* dS0, float* dk_prev,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Device scratch needed by falcon_bwd_chunked; (size_t)-1 for an invalid or
+ * unsupported problem. */
+size_t falcon_bwd_workspace_bytes(const falcon_problem* p);
+
 #ifdef __cplusplus
 }
 #endif

@@ -157,3 +157,46 @@ def test_decode_validation(lib):
         assert dec(**{name: fake(9, misalign=4)}) == ALIGN, name
     assert dec(o=fake(5)) == ALIAS
     assert dec(S=fake(1)) == ALIAS
+
+
+def call_bwd(lib, p, ws=None, wsb=0, **over):
+    a = dict(k=fake(0), q=fake(1), v=fake(2), beta=fake(3), lam=fake(4), S0=None, kp=None,
+             dO=fake(5), dST=None, dk=fake(6), dq=fake(7), dv=fake(8), dbeta=fake(9),
+             dlam=fake(10), dS0=fake(11), dkp=None)
+    a.update(over)
+    return lib.falcon_bwd_chunked(ctypes.byref(p) if p is not None else None, a["k"], a["q"],
+                                  a["v"], a["beta"], a["lam"], a["S0"], a["kp"], a["dO"], a["dST"],
+                                  a["dk"], a["dq"], a["dv"], a["dbeta"], a["dlam"], a["dS0"],
+                                  a["dkp"], ws, wsb, None)
+
+
+def test_backward_validation(lib):
+    need = fb.falcon_bwd_workspace_bytes(prob())
+    # 80 KiB per 32-token chunk per (b, h): T = 40 -> 2 chunks, B*H = 6
+    assert need == 6 * 2 * 80 * 1024
+    ws = fake(20)
+    assert call_bwd(lib, None) == NULL
+    assert call_bwd(lib, prob(variant="falcon1a"), ws, need) == VARIANT
+    assert call_bwd(lib, prob(variant="falcon2"), ws, need) == VARIANT
+    assert call_bwd(lib, prob(dk=32, dv=32), ws, need) == SHAPE
+    assert call_bwd(lib, prob(dv=128), ws, need) == SHAPE
+    assert fb.falcon_bwd_workspace_bytes(prob(dk=32)) == ctypes.c_size_t(-1).value
+    assert fb.falcon_bwd_workspace_bytes(prob(variant="falcon2")) == ctypes.c_size_t(-1).value
+    assert call_bwd(lib, prob(eps_gamma=2.0), ws, need) == VALUE
+    for name in ("k", "q", "v", "beta", "lam", "dO", "dk", "dq", "dv", "dbeta", "dlam"):
+        assert call_bwd(lib, prob(), ws, need, **{name: None}) == NULL, name
+    for i, name in enumerate(("k", "q", "v", "dO", "dk", "dq", "dS0")):
+        assert call_bwd(lib, prob(), ws, need, **{name: fake(30 + i, misalign=4)}) == ALIGN, name
+    assert call_bwd(lib, prob(), None, 0) == WORKSPACE
+    assert call_bwd(lib, prob(), ws, need - 1) == WORKSPACE
+    assert call_bwd(lib, prob(), fake(20, misalign=8), need) == ALIGN
+    # outputs may overlap neither an input nor one another
+    assert call_bwd(lib, prob(), ws, need, dq=fake(1)) == ALIAS
+    assert call_bwd(lib, prob(), ws, need, dv=fake(6)) == ALIAS
+    assert call_bwd(lib, prob(), ws, need, dS0=fake(40), dST=fake(40)) == ALIAS
+    assert call_bwd(lib, prob(), ws, need, dkp=fake(6), kp=fake(41)) == ALIAS
+    # dk_prev is ignored on a fresh start, so it cannot alias then
+    assert call_bwd(lib, prob(B=0), dkp=fake(6)) == OK
+    # nothing to do
+    assert call_bwd(lib, prob(B=0)) == OK
+    assert call_bwd(lib, prob(H=0), k=None, dk=None) == OK
