@@ -159,6 +159,58 @@ def bench_chunked_workload(name, steps=20, warmup=3):
             "workspace_bytes": int(ws.numel()), "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
 
 
+def backward_bytes(B, H, T, dk, dv, io_bytes=2):
+    """Compulsory HBM bytes of one Falcon-1 backward: read phi(k), phi(q), v and
+    dO once (io dtype), beta and lam once, dS_T once; write the float32
+    gradients dphi_k, dphi_q, dv, dbeta, dlam once and dS0 once."""
+    th = B * H * T
+    state = B * H * dk * dv * 4
+    return th * ((2 * dk + 2 * dv) * io_bytes + 8) + th * ((2 * dk + dv) * 4 + 8) + 2 * state
+
+
+def bench_backward(name="f1_backward_8x12x2048_d64", steps=10, warmup=2):
+    """The Falcon-1 backward (falcon_bwd_chunked) at the training shape, with a
+    loss on both the outputs and the final state; inputs, cotangents, gradient
+    buffers and workspace resident in HBM, timed with HIP events on the
+    launch stream."""
+    import torch
+
+    from delta_rule_recurrence_amd import falcon as fb
+    from delta_rule_recurrence_amd import inputs as I
+
+    w = I.WORKLOADS[name]
+    d = {k: v.cuda() for k, v in I.workload_inputs(w).items()}
+    cot = I.make_cotangents(w.B, w.H, w.T, w.dv, seed=w.seed, io_dtype=w.io_dtype, with_state=True)
+    cot = {k: v.cuda() for k, v in cot.items()}
+    p = fb.make_problem(w.B, w.H, w.T, w.dk, w.dv, variant="falcon1", io_dtype=torch.bfloat16,
+                        eps=w.eps, eps_gamma=w.eps_gamma)
+    ws = torch.empty(fb.falcon_bwd_workspace_bytes(p), dtype=torch.uint8, device="cuda")
+    grads = fb.falcon_bwd_chunked(d["phi_k"], d["phi_q"], d["v"], d["beta"], d["lam"], cot["dO"],
+                                  dS_T=cot["dS_T"], eps=w.eps, eps_gamma=w.eps_gamma, workspace=ws)
+
+    def step():
+        fb.falcon_bwd_chunked(d["phi_k"], d["phi_q"], d["v"], d["beta"], d["lam"], cot["dO"],
+                              dS_T=cot["dS_T"], eps=w.eps, eps_gamma=w.eps_gamma, grads=grads,
+                              workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = backward_bytes(w.B, w.H, w.T, w.dk, w.dv)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": name, "steps": steps, "us_per_step": ms * 1e3,
+            "tokens_per_s": w.B * w.T / (ms * 1e-3), "algorithmic_bytes": nbytes,
+            "workspace_bytes": int(ws.numel()), "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
+
+
 def calibrate_copy(nbytes=1 << 28, reps=5):
     """A plain device copy of known size, for scaling rocprofv3 FETCH_SIZE /
     WRITE_SIZE counters (each copy reads and writes nbytes once)."""
@@ -204,7 +256,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the other chunked workloads (Falcon-1A 2x12x16384, Falcon-2 8x12x2048)")
+                    help="skip the other workloads (Falcon-1A 2x12x16384, Falcon-2 8x12x2048, "
+                         "the Falcon-1 backward 8x12x2048)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain copy of known size (for PMC counter scaling)")
     args = ap.parse_args()
@@ -283,6 +336,7 @@ def main():
     if not args.no_extra:
         line["f1a_chunked"] = bench_chunked_workload("f1a_chunked_2x12x16384_d64")
         line["f2_chunked"] = bench_chunked_workload("f2_chunked_8x12x2048_d64", steps=5, warmup=1)
+        line["f1_backward"] = bench_backward()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(d, w, o, S_T)
     print(json.dumps(line))

@@ -3,27 +3,34 @@
 // Forward, per 32-token chunk with incoming state S (g_i the chunk-local
 // prefix of log gamma, gp_i = g_{i-1}, G = g_31; x_i, q_i, v_i the chunk's
 // shifted keys, queries and values):
-//   A_{is} = eta_i e^{gp_i-g_s} (x_i.x_s) (s < i),  W = (I + A)^{-1} Diag(eta e^{gp}) X,
-//   U = (I + A)^{-1} Diag(eta) V,  Xh = Diag(e^{G-g}) X,  M_{is} = (q_i.x_s) e^{g_i-g_s} (s <= i),
+//   A_{is} = eta_i e^{gp_i-g_s} (x_i.x_s) (s < i),  T = (I + A)^{-1},
+//   W = T Diag(eta e^{gp}) X,  U = T Diag(eta) V,  Xh = Diag(e^{G-g}) X,
+//   M_{is} = (q_i.x_s) e^{g_i-g_s} (s <= i),
 //   S' = P S + H,  O = Qt S + Ot   with
 //   P = e^G I - Xh^T W,  H = Xh^T U,  Qt = Diag(e^g) Q - M W,  Ot = M U
 // (the chunk-parallel form of Section 4.2 with the log-space renormalisation
 // of Section 4.4 applied per chunk; exact up to rounding).  Training
 // differentiates through the update (Section 3), so for L = <dO, O> +
 // <dS_T, S_T> the backward is:
-//   1. chunk maps P, H, Qt, Ot for every chunk (chunk-parallel);
-//   2. forward state chain, saving the state S_c entering each chunk;
-//   3. reverse adjoint chain: with Lam_c = dL/dS at the end of chunk c,
-//      Lam_{c-1} = P_c^T Lam_c + Qt_c^T dO_c, and dS0 = the last Lam;
-//   4. per chunk (chunk-parallel), reverse mode through the chunk maps from
-//      dP = Lam S_c^T, dH = Lam, dQt = dO S_c^T, dOt = dO:
-//        dW = -Xh dP - M^T dQt,  dU = Xh Lam + M^T dO,  dXh = -W dP^T + U Lam^T,
+//   1. chunk maps P, H, Qt for every chunk (chunk-parallel);
+//   2. in one launch, the forward state chain, saving the state S_c entering
+//      each chunk, and the reverse adjoint chain: with Lam_c = dL/dS at the
+//      end of chunk c, Lam_{c-1} = P_c^T Lam_c + Qt_c^T dO_c, and dS0 = the
+//      last Lam (the two chains need only the maps);
+//   3. per chunk (chunk-parallel), reverse mode through the chunk maps from
+//      dP = Lam S_c^T, dH = Lam, dQt = dO S_c^T, dOt = dO (dP is never formed:
+//      Xh dP = (Xh Lam) S_c^T and W dP^T = (W S_c) Lam^T):
+//        dW = -(Xh Lam) S_c^T - M^T dQt,  dU = Xh Lam + M^T dO,  dXh = (U - W S_c) Lam^T,
 //        dM = -dQt W^T + dO U^T,  dQ = Diag(e^g) dQt + (dM o D) X,
-//        dY = (I + A)^{-T} dW,  dZ = (I + A)^{-T} dU,  dA = -dY W^T - dZ U^T,
+//        dY = T^T dW,  dZ = T^T dU,  dA = -dY W^T - dZ U^T,
 //      then the Gram, the decays and the gates (eta, the clamped log decay,
 //      the prefix sums) by the chain rule, and the key shift x_t = phi(k_{t-1}).
 // Every product runs on the matrix cores in float32 (v_mfma_f32_16x16x4f32)
-// with operands in LDS; the triangular solves run one column per thread.
+// with operands in LDS.  T comes from a blocked inverse: the two 16 x 16
+// diagonal blocks by substitution (a column per lane), the off-diagonal
+// block as -T22 A21 T11.
+
+#include <stddef.h>
 
 #include "falcon_device.h"
 #include "falcon_launch.h"
@@ -37,19 +44,30 @@ constexpr int kD = 64;         // dk = dv
 constexpr int kPW = 68;        // float pitch of 64-wide LDS matrices
 constexpr int kPN = 36;        // float pitch of 32-wide LDS matrices
 constexpr int kThreads = 256;  // four waves
-constexpr int kMapFloats = kD * kD * 2 + kBC * kD * 2;   // P, H, Qt, Ot
+// Per-chunk maps, stored in the operand order of the chain kernel's MFMAs
+// (a 16x16 tile per wave and column group, four floats per lane):
+//   PA  P as the A operand of P S:      ((w*4 + j)*64 + l)*4 + e <-> P[16w + (l&15)][4(4j+e) + (l>>4)]
+//   PB  P as the B operand of Lam^T P:  ((w*4 + j)*64 + l)*4 + e <-> P[4(4j+e) + (l>>4)][16w + (l&15)]
+//   HD  H in accumulator order:         ((w*4 + cg)*64 + l)*4 + r <-> H[16w + 4(l>>4) + r][16cg + (l&15)]
+//   QB  Qt as the B operand of dO^T Qt: ((w*2 + j)*64 + l)*4 + e <-> Qt[4(4j+e) + (l>>4)][16w + (l&15)]
+constexpr int kOffPA = 0, kOffPB = 4096, kOffHD = 8192, kOffQB = 12288;
+constexpr int kMapFloats = 14336;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // D (M x N) = op(A) op(B) on the matrix cores in float32; A is M x K (stored
 // K x M when TA), B is K x N (stored N x K when TB), both in LDS with float
-// pitches pa, pb.  The 16x16 output tiles go round-robin to the four waves
-// (the same lane always gets the same output element for a given M, N), and
-// epi(row, col, value) receives each result.
+// pitches pa, pb (multiples of 4, 16-byte aligned rows).  The 16x16 output
+// tiles go round-robin to the four waves (the same lane always gets the same
+// output element for a given M, N), and epi(row, col, value) receives each
+// result.  Within each 16-wide slice of K, lane group g supplies k = 16m + 4g
+// + e at step e, so an operand stored with K contiguous is read 16 bytes at a
+// time.
 template <int M, int N, int K, bool TA, bool TB, typename Epi>
 __device__ __forceinline__ void mm(const float* A, int pa, const float* B, int pb, int w, int l, Epi epi) {
   const int g = l >> 4, c16 = l & 15;
   constexpr int TN = N / 16;
+  static_assert(K % 16 == 0, "K must be a multiple of 16");
   static_assert((M / 16) * TN % 4 == 0, "tiles must split evenly over the four waves");
 #pragma unroll
   for (int it = 0; it < (M / 16) * TN / 4; ++it) {
@@ -57,38 +75,37 @@ __device__ __forceinline__ void mm(const float* A, int pa, const float* B, int p
     const int tm = tile / TN, tn = tile % TN;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < K / 4; ++kb) {
-      const int k = 4 * kb + g;
-      const float a = TA ? A[k * pa + 16 * tm + c16] : A[(16 * tm + c16) * pa + k];
-      const float b = TB ? B[(16 * tn + c16) * pb + k] : B[k * pb + 16 * tn + c16];
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+    for (int m = 0; m < K / 16; ++m) {
+      const int k0 = 16 * m + 4 * g;
+      float av[4], bv[4];
+      if (TA) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) av[e] = A[(k0 + e) * pa + 16 * tm + c16];
+      } else {
+        const float4 v = *reinterpret_cast<const float4*>(A + (16 * tm + c16) * pa + k0);
+        av[0] = v.x; av[1] = v.y; av[2] = v.z; av[3] = v.w;
+      }
+      if (TB) {
+        const float4 v = *reinterpret_cast<const float4*>(B + (16 * tn + c16) * pb + k0);
+        bv[0] = v.x; bv[1] = v.y; bv[2] = v.z; bv[3] = v.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bv[e] = B[(k0 + e) * pb + 16 * tn + c16];
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], bv[e], acc, 0, 0, 0);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) epi(16 * tm + 4 * g + r, 16 * tn + c16, acc[r]);
   }
 }
 
-// out = (I + A)^{-1} r and out = (I + A)^{-T} r for A strictly lower (32 x 32
-// in LDS); r(i) gives row i of the right-hand side's column.
-template <typename R>
-__device__ __forceinline__ void solve_lower(const float (*AA)[kPN], R r, float (&out)[kBC]) {
-#pragma unroll
-  for (int i = 0; i < kBC; ++i) {
-    float acc = r(i);
-#pragma unroll
-    for (int s = 0; s < i; ++s) acc = fmaf(-AA[i][s], out[s], acc);
-    out[i] = acc;
-  }
-}
-template <typename R>
-__device__ __forceinline__ void solve_lower_t(const float (*AA)[kPN], R r, float (&out)[kBC]) {
-#pragma unroll
-  for (int i = kBC - 1; i >= 0; --i) {
-    float acc = r(i);
-#pragma unroll
-    for (int s = i + 1; s < kBC; ++s) acc = fmaf(-AA[s][i], out[s], acc);
-    out[i] = acc;
-  }
+// Sum over the eight consecutive lanes that share a row.
+__device__ __forceinline__ float sum8(float v) {
+  v += __shfl_xor(v, 1);
+  v += __shfl_xor(v, 2);
+  v += __shfl_xor(v, 4);
+  return v;
 }
 
 struct BwdArgs {
@@ -108,25 +125,67 @@ struct BwdArgs {
   float* dlam;
   float* dS0;
   float* dk_prev;
-  float* maps;     // per chunk: P [64][64], H [64][64], Qt [32][64], Ot [32][64]
-  float* ckpt;     // per chunk: S entering the chunk [64][64]
-  float* adj;      // per chunk: dL/dS at the end of the chunk [64][64]
+  float* maps;     // per chunk: PA, PB, HD, QB (above)
+  float* ckpt;     // per chunk: S entering the chunk, ((cg*4 + w)*64 + l)*4 + r <-> S[16w + 4(l>>4) + r][16cg + (l&15)]
+  float* adj;      // per chunk: dL/dS at its end, ((cg*4 + w)*64 + l)*4 + r <-> Lam[16w + (l&15)][16cg + 4(l>>4) + r]
   int T, nchunks;
   float eps, eps_gamma;
 };
 
 // The forward quantities of one chunk, in LDS.
-struct ChunkCore {
+struct __align__(16) ChunkCore {
   float X[kBC][kPW];     // x_i = phi(k_{t0+i-1}); 0 at a fresh start and past T
   float Q[kBC][kPW];     // q_i; 0 past T
-  float KX[kBC][kPN];    // x_i . x_s
-  float AA[kBC][kPN];    // A, strictly lower
-  float MM[kBC][kPN];    // M, lower with the diagonal
+  float V[kBC][kPW];     // v_i; 0 past T
   float W[kBC][kPW];
   float U[kBC][kPW];
-  float eta[kBC], g[kBC], gp[kBC], lg[kBC], lamv[kBC], betav[kBC], den[kBC];
+  float KX[kBC][kPN];    // x_i . x_s
+  float AA[kBC][kPN];    // A, strictly lower; then T Diag(eta e^{gp})
+  float TT[kBC][kPN];    // T = (I + A)^{-1}
+  float MM[kBC][kPN];    // M, lower with the diagonal
+  float ZZ[16][20];      // A21 T11
+  float en[kBC], eta[kBC], g[kBC], gp[kBC], lamv[kBC], den[kBC];
   int flags[kBC];        // 1: eta from the formula, 2: the clamp binds, 4: live row
   float G;
+};
+
+// Eight consecutive elements of a row (16-byte aligned), held as loaded and
+// widened to float only when used, so that every load of a phase can be
+// issued before the first wait.
+template <typename IO> struct Raw8;
+template <> struct Raw8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = reinterpret_cast<const float4*>(p)[0];
+    b = reinterpret_cast<const float4*>(p)[1];
+  }
+  __device__ __forceinline__ void get(float (&o)[8]) const {
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+  }
+};
+template <> struct Raw8<bf16_t> {
+  uint4 r;
+  __device__ __forceinline__ void load(const bf16_t* p) { r = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void get(float (&o)[8]) const {
+    const uint32_t u[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      o[2 * k] = __uint_as_float(u[k] << 16);
+      o[2 * k + 1] = __uint_as_float(u[k] & 0xffff0000u);
+    }
+  }
+};
+// One element held as loaded (the bf16 bit pattern, or the float).
+template <typename IO> struct Raw1;
+template <> struct Raw1<float> {
+  float x;
+  __device__ __forceinline__ void load(const float* p) { x = *p; }
+  __device__ __forceinline__ float get() const { return x; }
+};
+template <> struct Raw1<bf16_t> {
+  uint32_t x;
+  __device__ __forceinline__ void load(const bf16_t* p) { x = p->bits; }
+  __device__ __forceinline__ float get() const { return __uint_as_float(x << 16); }
 };
 
 template <typename IO>
@@ -134,66 +193,104 @@ __device__ __forceinline__ float ld_row(const IO* base, int64_t row, int col) {
   return io<IO>::load(base, row * kD + col);
 }
 
-// Loads the chunk's keys, queries and gate inputs; derives the gates; forms
-// the Gram, A, M and (by two triangular solves) W and U.
+// This thread's share of a chunk's inputs: row tid >> 3, columns 8 (tid & 7) + 0..7.
 template <typename IO>
-__device__ void chunk_forward(ChunkCore& cc, const BwdArgs& a, int64_t bh, int c, int tid, int w, int l) {
+struct ChunkRegs {
+  Raw8<IO> x, q, v;
+  float beta, lam;
+  bool live, xlive, glive;
+};
+
+template <typename IO>
+__device__ __forceinline__ void chunk_load(ChunkRegs<IO>& r, const BwdArgs& a, int64_t bh, int c, int tid) {
+  // Loads are unconditional (rows past T and a missing previous key read a
+  // valid row) and masked when stored, so no branch separates them.
   const int T = a.T;
-  const int t0 = c * kBC;
-  const bool fresh = (a.k_prev == nullptr);
+  const int i = tid >> 3, f0 = (tid & 7) * 8;
+  const int t = c * kBC + i;
+  r.live = t < T;
+  const int tc = r.live ? t : T - 1;
   const IO* K = static_cast<const IO*>(a.phi_k) + bh * T * kD;
   const IO* Qp = static_cast<const IO*>(a.phi_q) + bh * T * kD;
   const IO* V = static_cast<const IO*>(a.v) + bh * T * kD;
-  const IO* kp = a.k_prev ? static_cast<const IO*>(a.k_prev) + bh * kD : nullptr;
-  for (int e = tid; e < kBC * kD; e += kThreads) {
-    const int i = e >> 6, f = e & 63;
-    const int t = t0 + i;
-    float xv = 0.f, qv = 0.f;
-    if (t < T) {
-      if (t >= 1) xv = ld_row(K, t - 1, f);
-      else if (kp) xv = io<IO>::load(kp, f);
-      qv = ld_row(Qp, t, f);
+  const IO* kp = a.k_prev ? static_cast<const IO*>(a.k_prev) + bh * kD : K;
+  r.xlive = r.live && (t >= 1 || a.k_prev != nullptr);
+  // key row t - 1 for a live row t >= 1; any other row reads row 0 (T >= 1)
+  r.x.load((t == 0 ? kp : K + int64_t(r.live ? t - 1 : 0) * kD) + f0);
+  r.q.load(Qp + int64_t(tc) * kD + f0);
+  r.v.load(V + int64_t(tc) * kD + f0);
+  const int tg = c * kBC + (tid & 31);
+  r.glive = tid < kBC && tg < T;
+  const int tgc = tg < T ? tg : T - 1;
+  r.beta = a.beta[bh * T + tgc];
+  r.lam = a.lam[bh * T + tgc];
+}
+
+template <typename IO>
+__device__ __forceinline__ void chunk_store(ChunkCore& cc, const ChunkRegs<IO>& r, int tid) {
+  const int i = tid >> 3, f0 = (tid & 7) * 8;
+  float x[8], q[8], v[8];
+  r.x.get(x);
+  r.q.get(q);
+  r.v.get(v);
+  float e = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    x[k] = r.xlive ? x[k] : 0.f;
+    q[k] = r.live ? q[k] : 0.f;
+    v[k] = r.live ? v[k] : 0.f;
+    e = fmaf(x[k], x[k], e);
+  }
+#pragma unroll
+  for (int k = 0; k < 8; k += 4) {
+    *reinterpret_cast<float4*>(&cc.X[i][f0 + k]) = make_float4(x[k], x[k + 1], x[k + 2], x[k + 3]);
+    *reinterpret_cast<float4*>(&cc.Q[i][f0 + k]) = make_float4(q[k], q[k + 1], q[k + 2], q[k + 3]);
+    *reinterpret_cast<float4*>(&cc.V[i][f0 + k]) = make_float4(v[k], v[k + 1], v[k + 2], v[k + 3]);
+  }
+  e = sum8(e);
+  if ((tid & 7) == 0) cc.en[i] = e;
+  if (tid < kBC) {
+    cc.lamv[tid] = r.glive ? r.lam : 0.f;
+    cc.den[tid] = r.glive ? r.beta : 0.f;   // beta until the gates replace it by the denominator
+  }
+}
+
+// Gates, the Gram, A, M, the inverse T and the factors W, U of one chunk whose
+// inputs are in LDS (after a barrier).  Ends with a barrier.
+__device__ void chunk_forward(ChunkCore& cc, const BwdArgs& a, int c, int tid, int w, int l) {
+  const int T = a.T;
+  const int t0 = c * kBC;
+  const bool fresh = (a.k_prev == nullptr);
+  if (w == 0) {
+    // gates of row i (Eq. 3.4; Section 4.3 clamp; Section 3 fresh-start
+    // sentinel), then the chunk-local prefix sums of the log decays
+    const int i = l, t = t0 + i;
+    float lg = 0.f;
+    if (i < kBC) {
+      const bool live = t < T;
+      const float lamv = cc.lamv[i];
+      const float den = cc.en[i] + lamv + a.eps;
+      const bool on = live && !(fresh && t == 0) && den != 0.0f;
+      const float eta = on ? cc.den[i] / den : 0.0f;
+      const float alpha = eta * lamv;
+      const bool clamped = alpha > 1.0f - a.eps_gamma;
+      lg = live ? log1pf(-fminf(alpha, 1.0f - a.eps_gamma)) : 0.0f;
+      cc.eta[i] = eta;
+      cc.den[i] = den;
+      cc.flags[i] = (on ? 1 : 0) | (clamped ? 2 : 0) | (live ? 4 : 0);
     }
-    cc.X[i][f] = xv;
-    cc.Q[i][f] = qv;
-  }
-  if (tid < kBC) {
-    const int t = t0 + tid;
-    cc.betav[tid] = t < T ? a.beta[bh * T + t] : 0.f;
-    cc.lamv[tid] = t < T ? a.lam[bh * T + t] : 0.f;
-  }
-  __syncthreads();
-  if (tid < kBC) {
-    // gates of row i (Eq. 3.4; Section 4.3 clamp; Section 3 fresh-start sentinel)
-    const int i = tid, t = t0 + i;
-    float en = 0.f;
-#pragma unroll 16
-    for (int f = 0; f < kD; ++f) en = fmaf(cc.X[i][f], cc.X[i][f], en);
-    const bool live = t < T;
-    const float lamv = cc.lamv[i];
-    const float den = en + lamv + a.eps;
-    const bool on = live && !(fresh && t == 0) && den != 0.0f;
-    const float eta = on ? cc.betav[i] / den : 0.0f;
-    const float alpha = eta * lamv;
-    const bool clamped = alpha > 1.0f - a.eps_gamma;
-    const float lg = live ? log1pf(-fminf(alpha, 1.0f - a.eps_gamma)) : 0.0f;
-    cc.eta[i] = eta;
-    cc.den[i] = den;
-    cc.lg[i] = lg;
-    cc.flags[i] = (on ? 1 : 0) | (clamped ? 2 : 0) | (live ? 4 : 0);
-  }
-  __syncthreads();
-  if (tid < kBC) {
-    // chunk-local prefix sums of the log decays
-    const int i = tid;
-    float gi = 0.f, gpv = 0.f;
-    for (int r = 0; r <= i; ++r) {
-      gpv = gi;
-      gi += cc.lg[r];
+    float gi = lg;
+#pragma unroll
+    for (int d = 1; d < kBC; d <<= 1) {
+      const float n = __shfl_up(gi, d);
+      if (i >= d) gi += n;
     }
-    cc.g[i] = gi;
-    cc.gp[i] = gpv;
-    if (i == kBC - 1) cc.G = gi;
+    const float gpv = __shfl_up(gi, 1);
+    if (i < kBC) {
+      cc.g[i] = gi;
+      cc.gp[i] = i == 0 ? 0.f : gpv;
+      if (i == kBC - 1) cc.G = gi;
+    }
   }
   __syncthreads();
   // Gram, A and M
@@ -205,144 +302,312 @@ __device__ void chunk_forward(ChunkCore& cc, const BwdArgs& a, int64_t bh, int c
     cc.MM[r][s] = s <= r ? __expf(cc.g[r] - cc.g[s]) * v : 0.f;
   });
   __syncthreads();
-  // W = (I + A)^{-1} Diag(eta e^{gp}) X and U = (I + A)^{-1} Diag(eta) V, a column per thread
-  if (tid < 2 * kD) {
-    const int j = tid & 63;
-    float col[kBC];
-    if (tid < kD) {
-      solve_lower(cc.AA, [&](int i) { return cc.eta[i] * __expf(cc.gp[i]) * cc.X[i][j]; }, col);
+  // T11, T22 by substitution: lane j solves (I + A_bb) t = e_jj, b = j / 16
+  if (tid < kBC) {
+    const int b = tid >> 4, jj = tid & 15, o = 16 * b;
+    float col[16];
 #pragma unroll
-      for (int i = 0; i < kBC; ++i) cc.W[i][j] = col[i];
-    } else {
-      solve_lower(cc.AA, [&](int i) { return t0 + i < T ? cc.eta[i] * ld_row(V, t0 + i, j) : 0.f; }, col);
+    for (int i = 0; i < 16; ++i) {
+      float acc = i == jj ? 1.f : 0.f;
 #pragma unroll
-      for (int i = 0; i < kBC; ++i) cc.U[i][j] = col[i];
+      for (int s = 0; s < i; ++s) acc = fmaf(-cc.AA[o + i][o + s], col[s], acc);
+      col[i] = acc;
     }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) cc.TT[o + i][o + jj] = col[i];
+  } else if (tid >= 64 && tid < 64 + 256 / 2) {
+    // upper-right block of T is zero
+    const int e = tid - 64;
+    cc.TT[e >> 3][16 + 2 * (e & 7)] = 0.f;
+    cc.TT[e >> 3][17 + 2 * (e & 7)] = 0.f;
   }
+  __syncthreads();
+  {
+    // Z = A21 T11
+    const int i = tid >> 4, j = tid & 15;
+    float z = 0.f;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) z = fmaf(cc.AA[16 + i][s], cc.TT[s][j], z);
+    cc.ZZ[i][j] = z;
+  }
+  __syncthreads();
+  {
+    // T21 = -T22 Z
+    const int i = tid >> 4, j = tid & 15;
+    float z = 0.f;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) z = fmaf(cc.TT[16 + i][16 + s], cc.ZZ[s][j], z);
+    cc.TT[16 + i][j] = -z;
+  }
+  __syncthreads();
+}
+
+// W = T Diag(eta e^{gp}) X and U = T Diag(eta) V, with TZ = T Diag(eta) in
+// the caller's 32 x 36 scratch; AA becomes T Diag(eta e^{gp}).  Ends with a barrier.
+__device__ void chunk_factors(ChunkCore& cc, float (*TZ)[kPN], int tid, int w, int l) {
+  for (int e = tid; e < kBC * kBC; e += kThreads) {
+    const int i = e >> 5, s = e & 31;
+    const float t = cc.TT[i][s];
+    cc.AA[i][s] = t * cc.eta[s] * __expf(cc.gp[s]);
+    TZ[i][s] = t * cc.eta[s];
+  }
+  __syncthreads();
+  mm<kBC, kD, kBC, false, false>(&cc.AA[0][0], kPN, &cc.X[0][0], kPW, w, l,
+                                 [&](int r, int s, float v) { cc.W[r][s] = v; });
+  mm<kBC, kD, kBC, false, false>(&TZ[0][0], kPN, &cc.V[0][0], kPW, w, l,
+                                 [&](int r, int s, float v) { cc.U[r][s] = v; });
   __syncthreads();
 }
 
 // ---- launch 1: chunk maps --------------------------------------------------------
-struct MapSmem {
-  ChunkCore cc;
-  float XH[kBC][kPW];    // Diag(e^{G-g}) X
-};
-
 template <typename IO>
 __global__ void __launch_bounds__(kThreads) falcon1_bwd_maps_kernel(BwdArgs a) {
-  __shared__ MapSmem sm;
+  __shared__ ChunkCore cc;
+  __shared__ float TZ[kBC][kPN];
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;   // wave-uniform
   const int64_t bh = blockIdx.x / a.nchunks;
   const int c = blockIdx.x % a.nchunks;
-  ChunkCore& cc = sm.cc;
-  chunk_forward<IO>(cc, a, bh, c, tid, w, l);
+  {
+    ChunkRegs<IO> r;
+    chunk_load<IO>(r, a, bh, c, tid);
+    chunk_store<IO>(cc, r, tid);
+  }
+  __syncthreads();
+  chunk_forward(cc, a, c, tid, w, l);
+  chunk_factors(cc, TZ, tid, w, l);
+  // V is dead: it holds Xh = Diag(e^{G-g}) X.  KX and AA (adjacent, dead)
+  // hold Qt; X and Q (adjacent) hold P, then H, once Qt is formed.
+  float (*XH)[kPW] = cc.V;
+  float (*QT)[kPW] = reinterpret_cast<float (*)[kPW]>(&cc.KX[0][0]);
+  float (*PS)[kPW] = reinterpret_cast<float (*)[kPW]>(&cc.X[0][0]);
+  static_assert(sizeof(cc.KX) + sizeof(cc.AA) >= sizeof(float) * kBC * kPW, "Qt does not fit");
+  static_assert(offsetof(ChunkCore, AA) == offsetof(ChunkCore, KX) + sizeof(cc.KX), "KX, AA not adjacent");
+  static_assert(sizeof(cc.X) + sizeof(cc.Q) >= sizeof(float) * kD * kPW, "P does not fit");
+  static_assert(offsetof(ChunkCore, Q) == offsetof(ChunkCore, X) + sizeof(cc.X), "X, Q not adjacent");
   for (int e = tid; e < kBC * kD; e += kThreads) {
     const int i = e >> 6, f = e & 63;
-    sm.XH[i][f] = __expf(cc.G - cc.g[i]) * cc.X[i][f];
+    XH[i][f] = __expf(cc.G - cc.g[i]) * cc.X[i][f];
   }
+  __syncthreads();
+  // Qt = Diag(e^g) Q - M W
+  mm<kBC, kD, kBC, false, false>(&cc.MM[0][0], kPN, &cc.W[0][0], kPW, w, l, [&](int r, int s, float v) {
+    QT[r][s] = __expf(cc.g[r]) * cc.Q[r][s] - v;
+  });
   __syncthreads();
   float* out = a.maps + int64_t(blockIdx.x) * kMapFloats;
   const float eG = __expf(cc.G);
-  // P = e^G I - Xh^T W, H = Xh^T U
-  mm<kD, kD, kBC, true, false>(&sm.XH[0][0], kPW, &cc.W[0][0], kPW, w, l,
-                               [&](int r, int s, float v) { out[r * kD + s] = (r == s ? eG : 0.f) - v; });
-  mm<kD, kD, kBC, true, false>(&sm.XH[0][0], kPW, &cc.U[0][0], kPW, w, l,
-                               [&](int r, int s, float v) { out[kD * kD + r * kD + s] = v; });
-  // Qt = Diag(e^g) Q - M W, Ot = M U
-  mm<kBC, kD, kBC, false, false>(&cc.MM[0][0], kPN, &cc.W[0][0], kPW, w, l, [&](int r, int s, float v) {
-    out[2 * kD * kD + r * kD + s] = __expf(cc.g[r]) * cc.Q[r][s] - v;
-  });
-  mm<kBC, kD, kBC, false, false>(&cc.MM[0][0], kPN, &cc.U[0][0], kPW, w, l,
-                                 [&](int r, int s, float v) { out[2 * kD * kD + kBC * kD + r * kD + s] = v; });
+  // P = e^G I - Xh^T W
+  mm<kD, kD, kBC, true, false>(&XH[0][0], kPW, &cc.W[0][0], kPW, w, l,
+                               [&](int r, int s, float v) { PS[r][s] = (r == s ? eG : 0.f) - v; });
+  __syncthreads();
+  for (int q = tid; q < 1024; q += kThreads) {
+    const int ww = q >> 8, j = (q >> 6) & 3, ll = q & 63, lo = ll & 15, hi = ll >> 4;
+    float4 pa, pb;
+    pa.x = PS[16 * ww + lo][4 * (4 * j + 0) + hi];
+    pa.y = PS[16 * ww + lo][4 * (4 * j + 1) + hi];
+    pa.z = PS[16 * ww + lo][4 * (4 * j + 2) + hi];
+    pa.w = PS[16 * ww + lo][4 * (4 * j + 3) + hi];
+    pb.x = PS[4 * (4 * j + 0) + hi][16 * ww + lo];
+    pb.y = PS[4 * (4 * j + 1) + hi][16 * ww + lo];
+    pb.z = PS[4 * (4 * j + 2) + hi][16 * ww + lo];
+    pb.w = PS[4 * (4 * j + 3) + hi][16 * ww + lo];
+    reinterpret_cast<float4*>(out + kOffPA)[q] = pa;
+    reinterpret_cast<float4*>(out + kOffPB)[q] = pb;
+  }
+  for (int q = tid; q < 512; q += kThreads) {
+    const int ww = q >> 7, j = (q >> 6) & 1, ll = q & 63, lo = ll & 15, hi = ll >> 4;
+    float4 qb;
+    qb.x = QT[4 * (4 * j + 0) + hi][16 * ww + lo];
+    qb.y = QT[4 * (4 * j + 1) + hi][16 * ww + lo];
+    qb.z = QT[4 * (4 * j + 2) + hi][16 * ww + lo];
+    qb.w = QT[4 * (4 * j + 3) + hi][16 * ww + lo];
+    reinterpret_cast<float4*>(out + kOffQB)[q] = qb;
+  }
+  __syncthreads();
+  // H = Xh^T U
+  mm<kD, kD, kBC, true, false>(&XH[0][0], kPW, &cc.U[0][0], kPW, w, l,
+                               [&](int r, int s, float v) { PS[r][s] = v; });
+  __syncthreads();
+  for (int q = tid; q < 1024; q += kThreads) {
+    const int ww = q >> 8, cg = (q >> 6) & 3, ll = q & 63, lo = ll & 15, hi = ll >> 4;
+    float4 hd;
+    hd.x = PS[16 * ww + 4 * hi + 0][16 * cg + lo];
+    hd.y = PS[16 * ww + 4 * hi + 1][16 * cg + lo];
+    hd.z = PS[16 * ww + 4 * hi + 2][16 * cg + lo];
+    hd.w = PS[16 * ww + 4 * hi + 3][16 * cg + lo];
+    reinterpret_cast<float4*>(out + kOffHD)[q] = hd;
+  }
 }
 
-// ---- launches 2 and 3: the state chain and the adjoint chain -------------------
+// ---- launch 2: the state chain and the adjoint chain ---------------------------
+// Columns of S evolve independently under S' = P S + H, and so do the rows of
+// Lam^T under Lam^T' = Lam^T P + dO^T Qt, so each sequence's chains split
+// into four 16-column groups.  One workgroup runs one (chain, sequence,
+// group); its four waves own the 16-row blocks of the 64 x 16 block, held in
+// MFMA accumulators, and share the block through LDS.  Each chunk's operands
+// are loaded kRing chunks ahead of their use.  The four groups
+// of a (chain, sequence) are placed on one XCD (workgroups go round-robin over
+// the eight XCDs), so P is fetched from HBM once per XCD L2.
 struct ChainSmem {
-  float S[2][kD][kPW];   // state (or adjoint), double-buffered
-  float P[kD][kPW];      // this chunk's P
-  float B[kD][kPW];      // this chunk's H (state chain) or Qt in rows 0..31 (adjoint chain)
-  float O[kBC][kPW];     // this chunk's dO (adjoint chain)
+  float B[kD][16];       // state chain: S[:, 16cg .. 16cg+15] (k rows)
+  float L[16][kPW];      // adjoint chain: Lam^T[16cg .. 16cg+15][:]
 };
 
-// State chain: S_c into ckpt[c], then S <- P_c S + H_c.
-__global__ void __launch_bounds__(kThreads) falcon1_bwd_state_kernel(BwdArgs a) {
-  __shared__ ChainSmem sm;
-  const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
-  const int64_t bh = blockIdx.x;
-  for (int e = tid; e < kD * kD; e += kThreads)
-    sm.S[0][e >> 6][e & 63] = a.S0 ? a.S0[bh * kD * kD + e] : 0.f;
-  int cur = 0;
-  for (int c = 0; c < a.nchunks; ++c) {
-    const float* mp = a.maps + (bh * a.nchunks + c) * kMapFloats;
-    float* ck = a.ckpt + (bh * a.nchunks + c) * kD * kD;
-    for (int e = tid; e < kD * kD; e += kThreads) {
-      sm.P[e >> 6][e & 63] = mp[e];
-      sm.B[e >> 6][e & 63] = mp[kD * kD + e];
-    }
-    __syncthreads();
-    float (*S)[kPW] = sm.S[cur];
-    float (*Sn)[kPW] = sm.S[cur ^ 1];
-    for (int e = tid; e < kD * kD; e += kThreads) ck[e] = S[e >> 6][e & 63];
-    mm<kD, kD, kD, false, false>(&sm.P[0][0], kPW, &S[0][0], kPW, w, l,
-                                 [&](int r, int s, float v) { Sn[r][s] = v + sm.B[r][s]; });
-    __syncthreads();
-    cur ^= 1;
-  }
-}
+constexpr int kRing = 4;   // chunks of operands in flight per chain
 
-// Adjoint chain: adj[c] = Lam at the end of chunk c, then
-// Lam <- P_c^T Lam + Qt_c^T dO_c; finally dS0 = Lam.
 template <typename IO>
-__global__ void __launch_bounds__(kThreads) falcon1_bwd_adjoint_kernel(BwdArgs a) {
+__device__ __forceinline__ void chain_state(const BwdArgs& a, ChainSmem& sm, int64_t bh, int cg, int w, int l) {
+  const int g = l >> 4, c16 = l & 15;
+  const int n = a.nchunks;
+  // S0 block in accumulator order: lane holds S[16w + 4g + r][16cg + c16]
+  f32x4 S;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) S[r] = a.S0 ? a.S0[bh * kD * kD + (16 * w + 4 * g + r) * kD + 16 * cg + c16] : 0.f;
+  const float* mp = a.maps + bh * n * kMapFloats;
+  float4 pa[kRing][4], hd[kRing];
+  auto load = [&](int c, float4 (&p4)[4], float4& h) {
+    const float* cp = mp + c * kMapFloats;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) p4[j] = reinterpret_cast<const float4*>(cp + kOffPA)[(w * 4 + j) * 64 + l];
+    h = reinterpret_cast<const float4*>(cp + kOffHD)[(w * 4 + cg) * 64 + l];
+  };
+#pragma unroll
+  for (int d = 0; d < kRing; ++d)
+    if (d < n) load(d, pa[d], hd[d]);
+  for (int c0 = 0; c0 < n; c0 += kRing) {
+#pragma unroll
+    for (int d = 0; d < kRing; ++d) {
+      const int c = c0 + d;
+      if (c < n) {
+        // S (entering chunk c) to LDS and to the checkpoint
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sm.B[16 * w + 4 * g + r][c16] = S[r];
+        float* ck = a.ckpt + (bh * n + c) * kD * kD;
+        reinterpret_cast<float4*>(ck)[(cg * 4 + w) * 64 + l] = make_float4(S[0], S[1], S[2], S[3]);
+        __syncthreads();
+        f32x4 acc = {hd[d].x, hd[d].y, hd[d].z, hd[d].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float pe[4] = {pa[d][j].x, pa[d][j].y, pa[d][j].z, pa[d][j].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int kb = 4 * j + e;
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pe[e], sm.B[4 * kb + g][c16], acc, 0, 0, 0);
+          }
+        }
+        S = acc;
+        __syncthreads();
+        if (c + kRing < n) load(c + kRing, pa[d], hd[d]);
+      }
+    }
+  }
+}
+
+template <typename IO>
+__device__ __forceinline__ void chain_adjoint(const BwdArgs& a, ChainSmem& sm, int64_t bh, int cg, int w, int l) {
+  const int g = l >> 4, c16 = l & 15;
+  const int T = a.T, n = a.nchunks;
+  const IO* dO = static_cast<const IO*>(a.dO) + bh * T * kD;
+  // Lam^T block in accumulator order: lane holds Lam^T[16cg + 4g + r][16w + c16] = Lam[16w + c16][16cg + 4g + r]
+  f32x4 Lt;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    Lt[r] = a.dS_T ? a.dS_T[bh * kD * kD + (16 * w + c16) * kD + 16 * cg + 4 * g + r] : 0.f;
+  const float* mp = a.maps + bh * n * kMapFloats;
+  float4 pb[kRing][4], qb[kRing][2];
+  Raw1<IO> od[kRing][8];
+  auto load = [&](int c, float4 (&p4)[4], float4 (&q4)[2], Raw1<IO> (&o8)[8]) {
+    const float* cp = mp + c * kMapFloats;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) p4[j] = reinterpret_cast<const float4*>(cp + kOffPB)[(w * 4 + j) * 64 + l];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) q4[j] = reinterpret_cast<const float4*>(cp + kOffQB)[(w * 2 + j) * 64 + l];
+    // dO^T[16cg + c16][4kb + g] = dO[t0 + 4kb + g][16cg + c16]; rows past T
+    // read row T - 1 and are replaced by 0 where used
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+      const int t = c * kBC + 4 * kb + g;
+      o8[kb].load(dO + int64_t(t < T ? t : T - 1) * kD + 16 * cg + c16);
+    }
+  };
+#pragma unroll
+  for (int d = 0; d < kRing; ++d)
+    if (d < n) load(n - 1 - d, pb[d], qb[d], od[d]);
+  for (int c0 = 0; c0 < n; c0 += kRing) {
+#pragma unroll
+    for (int d = 0; d < kRing; ++d) {
+      const int step = c0 + d, c = n - 1 - step;
+      if (step < n) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sm.L[4 * g + r][16 * w + c16] = Lt[r];
+        float* ad = a.adj + (bh * n + c) * kD * kD;
+        reinterpret_cast<float4*>(ad)[(cg * 4 + w) * 64 + l] = make_float4(Lt[0], Lt[1], Lt[2], Lt[3]);
+        __syncthreads();
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float pe[4] = {pb[d][j].x, pb[d][j].y, pb[d][j].z, pb[d][j].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int kb = 4 * j + e;
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.L[c16][4 * kb + g], pe[e], acc, 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const float qe[4] = {qb[d][j].x, qb[d][j].y, qb[d][j].z, qb[d][j].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int t = c * kBC + 4 * (4 * j + e) + g;
+            const float ov = t < T ? od[d][4 * j + e].get() : 0.f;
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ov, qe[e], acc, 0, 0, 0);
+          }
+        }
+        Lt = acc;
+        __syncthreads();
+        if (step + kRing < n) load(c - kRing, pb[d], qb[d], od[d]);
+      }
+    }
+  }
+  if (a.dS0) {
+    float* d = a.dS0 + bh * kD * kD + (16 * w + c16) * kD + 16 * cg + 4 * g;
+    *reinterpret_cast<float4*>(d) = make_float4(Lt[0], Lt[1], Lt[2], Lt[3]);
+  }
+}
+
+template <typename IO>
+__global__ void __launch_bounds__(kThreads) falcon1_bwd_chain_kernel(BwdArgs a, int nunits) {
   __shared__ ChainSmem sm;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
-  const int64_t bh = blockIdx.x;
-  const int T = a.T;
-  const IO* dO = static_cast<const IO*>(a.dO) + bh * T * kD;
-  for (int e = tid; e < kD * kD; e += kThreads)
-    sm.S[0][e >> 6][e & 63] = a.dS_T ? a.dS_T[bh * kD * kD + e] : 0.f;
-  int cur = 0;
-  for (int c = a.nchunks - 1; c >= 0; --c) {
-    const float* mp = a.maps + (bh * a.nchunks + c) * kMapFloats;
-    float* ad = a.adj + (bh * a.nchunks + c) * kD * kD;
-    for (int e = tid; e < kD * kD; e += kThreads) sm.P[e >> 6][e & 63] = mp[e];
-    for (int e = tid; e < kBC * kD; e += kThreads) {
-      const int i = e >> 6, f = e & 63, t = c * kBC + i;
-      sm.B[i][f] = mp[2 * kD * kD + e];
-      sm.O[i][f] = t < T ? ld_row(dO, t, f) : 0.f;
-    }
-    __syncthreads();
-    float (*S)[kPW] = sm.S[cur];
-    float (*Sn)[kPW] = sm.S[cur ^ 1];
-    for (int e = tid; e < kD * kD; e += kThreads) ad[e] = S[e >> 6][e & 63];
-    mm<kD, kD, kD, true, false>(&sm.P[0][0], kPW, &S[0][0], kPW, w, l,
-                                [&](int r, int s, float v) { Sn[r][s] = v; });
-    mm<kD, kD, kBC, true, false>(&sm.B[0][0], kPW, &sm.O[0][0], kPW, w, l,
-                                 [&](int r, int s, float v) { Sn[r][s] += v; });
-    __syncthreads();
-    cur ^= 1;
-  }
-  if (a.dS0)
-    for (int e = tid; e < kD * kD; e += kThreads) a.dS0[bh * kD * kD + e] = sm.S[cur][e >> 6][e & 63];
+  // unit u = (sequence, chain); its four column groups share one XCD
+  const int b = blockIdx.x;
+  const int slot = b >> 3;
+  const int cg = slot & 3;
+  const int u = (slot >> 2) * 8 + (b & 7);
+  if (u >= nunits) return;   // whole workgroup
+  const int64_t bh = u >> 1;
+  if (u & 1)
+    chain_adjoint<IO>(a, sm, bh, cg, w, l);
+  else
+    chain_state<IO>(a, sm, bh, cg, w, l);
 }
 
-// ---- launch 4: reverse mode through one chunk ----------------------------------
-struct GradSmem {
+// ---- launch 3: reverse mode through one chunk ----------------------------------
+struct __align__(16) GradSmem {
   ChunkCore cc;
-  float SC[kD][kPW];     // S entering the chunk; later dXh in rows 0..31
+  float SC[kD][kPW];     // S entering the chunk
   float LL[kD][kPW];     // dL/dS at the end of the chunk
-  float DP[kD][kPW];     // dP
-  float DO[kBC][kPW];    // dO
-  float DQT[kBC][kPW];   // dQt
-  float DW[kBC][kPW];    // dW, then dY
-  float DU[kBC][kPW];    // dU, then dZ
-  float DM[kBC][kPN];    // dM, then dM o D, then dA, then its decayed, eta-scaled form
-  float DX[kBC][kPW];    // dX accumulator
+  float DO[kBC][kPW];    // dO, then dZ
+  float DQT[kBC][kPW];   // dQt, then dY
+  float DW[kBC][kPW];    // dW
+  float DU[kBC][kPW];    // Xh Lam, then dU
+  float RR[kBC][kPW];    // U - W S, then the dX accumulator
+  float DXH[kBC][kPW];   // dXh
+  float DM[kBC][kPN];    // T Diag(eta); then dM, dM o D, dA, its decayed form, eta-scaled
   float dg[kBC], dgp[kBC], deta[kBC], dgt[kBC];
-  float dG;
+  float trp[4];
 };
 
 template <typename IO>
@@ -355,75 +620,109 @@ __global__ void __launch_bounds__(kThreads) falcon1_bwd_chunk_kernel(BwdArgs a) 
   const int T = a.T;
   const int t0 = c * kBC;
   ChunkCore& cc = sm.cc;
-  const IO* dO = static_cast<const IO*>(a.dO) + bh * T * kD;
-  const IO* V = static_cast<const IO*>(a.v) + bh * T * kD;
   {
-    const float* ck = a.ckpt + (bh * a.nchunks + c) * kD * kD;
-    const float* ad = a.adj + (bh * a.nchunks + c) * kD * kD;
-    for (int e = tid; e < kD * kD; e += kThreads) {
-      sm.SC[e >> 6][e & 63] = ck[e];
-      sm.LL[e >> 6][e & 63] = ad[e];
+    // every load of the chunk is issued before the first LDS store
+    ChunkRegs<IO> r;
+    chunk_load<IO>(r, a, bh, c, tid);
+    Raw8<IO> odr;
+    const int orow = t0 + (tid >> 3);
+    odr.load(static_cast<const IO*>(a.dO) + (bh * T + (orow < T ? orow : T - 1)) * kD + (tid & 7) * 8);
+    const float4* ck = reinterpret_cast<const float4*>(a.ckpt + (bh * a.nchunks + c) * kD * kD);
+    const float4* ad = reinterpret_cast<const float4*>(a.adj + (bh * a.nchunks + c) * kD * kD);
+    float4 s4[4], l4[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      s4[k] = ck[tid + k * kThreads];
+      l4[k] = ad[tid + k * kThreads];
     }
-    for (int e = tid; e < kBC * kD; e += kThreads) {
-      const int i = e >> 6, f = e & 63, t = t0 + i;
-      sm.DO[i][f] = t < T ? ld_row(dO, t, f) : 0.f;
+    chunk_store<IO>(cc, r, tid);
+    {
+      const int i = tid >> 3, f0 = (tid & 7) * 8;
+      float od[8];
+      odr.get(od);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) od[k] = orow < T ? od[k] : 0.f;
+      *reinterpret_cast<float4*>(&sm.DO[i][f0]) = make_float4(od[0], od[1], od[2], od[3]);
+      *reinterpret_cast<float4*>(&sm.DO[i][f0 + 4]) = make_float4(od[4], od[5], od[6], od[7]);
     }
+    float trace = 0.f;   // this thread's part of tr(Lam S_c^T)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int q = tid + k * kThreads;
+      const int cg = q >> 8, ww = (q >> 6) & 3, lo = q & 15, hi = (q >> 4) & 3;
+      sm.SC[16 * ww + 4 * hi + 0][16 * cg + lo] = s4[k].x;
+      sm.SC[16 * ww + 4 * hi + 1][16 * cg + lo] = s4[k].y;
+      sm.SC[16 * ww + 4 * hi + 2][16 * cg + lo] = s4[k].z;
+      sm.SC[16 * ww + 4 * hi + 3][16 * cg + lo] = s4[k].w;
+      sm.LL[16 * ww + lo][16 * cg + 4 * hi + 0] = l4[k].x;
+      sm.LL[16 * ww + lo][16 * cg + 4 * hi + 1] = l4[k].y;
+      sm.LL[16 * ww + lo][16 * cg + 4 * hi + 2] = l4[k].z;
+      sm.LL[16 * ww + lo][16 * cg + 4 * hi + 3] = l4[k].w;
+    }
+    __syncthreads();
+    // tr(Lam S^T) = sum of Lam o S, a 16-float slice per thread
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = tid * 16 + 4 * k, rr = e >> 6, cl = e & 63;
+      const float4 x = *reinterpret_cast<const float4*>(&sm.LL[rr][cl]);
+      const float4 y = *reinterpret_cast<const float4*>(&sm.SC[rr][cl]);
+      trace = fmaf(x.x, y.x, fmaf(x.y, y.y, fmaf(x.z, y.z, fmaf(x.w, y.w, trace))));
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) trace += __shfl_xor(trace, off);
+    if (l == 0) sm.trp[w] = trace;
   }
-  chunk_forward<IO>(cc, a, bh, c, tid, w, l);
+  chunk_forward(cc, a, c, tid, w, l);
+  chunk_factors(cc, sm.DM, tid, w, l);
   const float eG = __expf(cc.G);
   auto xs = [&](int i) { return __expf(cc.G - cc.g[i]); };
-  // dP = Lam S_c^T, dQt = dO S_c^T
-  mm<kD, kD, kD, false, true>(&sm.LL[0][0], kPW, &sm.SC[0][0], kPW, w, l,
-                              [&](int r, int s, float v) { sm.DP[r][s] = v; });
+  // Xh Lam (into DU), R = U - W S_c, dQt = dO S_c^T
+  mm<kBC, kD, kD, false, false>(&cc.X[0][0], kPW, &sm.LL[0][0], kPW, w, l,
+                                [&](int r, int s, float v) { sm.DU[r][s] = xs(r) * v; });
+  mm<kBC, kD, kD, false, false>(&cc.W[0][0], kPW, &sm.SC[0][0], kPW, w, l,
+                                [&](int r, int s, float v) { sm.RR[r][s] = cc.U[r][s] - v; });
   mm<kBC, kD, kD, false, true>(&sm.DO[0][0], kPW, &sm.SC[0][0], kPW, w, l,
                                [&](int r, int s, float v) { sm.DQT[r][s] = v; });
   __syncthreads();
-  float (*DXH)[kPW] = sm.SC;   // S_c is no longer needed
-  // dW = -Xh dP - M^T dQt, dU = Xh Lam + M^T dO
-  mm<kBC, kD, kD, false, false>(&cc.X[0][0], kPW, &sm.DP[0][0], kPW, w, l,
-                                [&](int r, int s, float v) { sm.DW[r][s] = -xs(r) * v; });
-  mm<kBC, kD, kBC, true, false>(&cc.MM[0][0], kPN, &sm.DQT[0][0], kPW, w, l,
-                                [&](int r, int s, float v) { sm.DW[r][s] -= v; });
-  mm<kBC, kD, kD, false, false>(&cc.X[0][0], kPW, &sm.LL[0][0], kPW, w, l,
-                                [&](int r, int s, float v) { sm.DU[r][s] = xs(r) * v; });
-  mm<kBC, kD, kBC, true, false>(&cc.MM[0][0], kPN, &sm.DO[0][0], kPW, w, l,
-                                [&](int r, int s, float v) { sm.DU[r][s] += v; });
-  // dXh = -W dP^T + U Lam^T, dM = -dQt W^T + dO U^T
-  mm<kBC, kD, kD, false, true>(&cc.W[0][0], kPW, &sm.DP[0][0], kPW, w, l,
-                               [&](int r, int s, float v) { DXH[r][s] = -v; });
-  mm<kBC, kD, kD, false, true>(&cc.U[0][0], kPW, &sm.LL[0][0], kPW, w, l,
-                               [&](int r, int s, float v) { DXH[r][s] += v; });
+  // dW = -(Xh Lam) S_c^T, dXh = R Lam^T, dM = -dQt W^T + dO U^T
+  mm<kBC, kD, kD, false, true>(&sm.DU[0][0], kPW, &sm.SC[0][0], kPW, w, l,
+                               [&](int r, int s, float v) { sm.DW[r][s] = -v; });
+  mm<kBC, kD, kD, false, true>(&sm.RR[0][0], kPW, &sm.LL[0][0], kPW, w, l,
+                               [&](int r, int s, float v) { sm.DXH[r][s] = v; });
   mm<kBC, kBC, kD, false, true>(&sm.DQT[0][0], kPW, &cc.W[0][0], kPW, w, l,
                                 [&](int r, int s, float v) { sm.DM[r][s] = -v; });
   mm<kBC, kBC, kD, false, true>(&sm.DO[0][0], kPW, &cc.U[0][0], kPW, w, l,
                                 [&](int r, int s, float v) { sm.DM[r][s] += v; });
   __syncthreads();
-  // decay terms of M, Qt and Xh; dG from P = e^G I + ...
-  if (tid < kBC) {
-    const int i = tid;
-    float qd = 0.f, xd = 0.f;
-#pragma unroll 16
-    for (int f = 0; f < kD; ++f) {
+  // dW -= M^T dQt, dU = Xh Lam + M^T dO
+  mm<kBC, kD, kBC, true, false>(&cc.MM[0][0], kPN, &sm.DQT[0][0], kPW, w, l,
+                                [&](int r, int s, float v) { sm.DW[r][s] -= v; });
+  mm<kBC, kD, kBC, true, false>(&cc.MM[0][0], kPN, &sm.DO[0][0], kPW, w, l,
+                                [&](int r, int s, float v) { sm.DU[r][s] += v; });
+  {
+    // decay terms of M, Qt and Xh (eight lanes per row)
+    const int i = tid >> 3, p = tid & 7;
+    float qd = 0.f, xd = 0.f, rowm = 0.f, colm = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int f = 8 * p + k;
       qd = fmaf(cc.Q[i][f], sm.DQT[i][f], qd);
-      xd = fmaf(cc.X[i][f], DXH[i][f], xd);
+      xd = fmaf(cc.X[i][f], sm.DXH[i][f], xd);
     }
-    float rowm = 0.f, colm = 0.f;
-#pragma unroll 8
-    for (int s = 0; s < kBC; ++s) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int s = 4 * p + k;
       rowm = fmaf(sm.DM[i][s], cc.MM[i][s], rowm);
       colm = fmaf(sm.DM[s][i], cc.MM[s][i], colm);
     }
-    const float z = xs(i) * xd;
-    sm.dg[i] = __expf(cc.g[i]) * qd + rowm - colm - z;
-    sm.dgt[i] = z;
+    qd = sum8(qd); xd = sum8(xd); rowm = sum8(rowm); colm = sum8(colm);
+    if (p == 0) {
+      const float z = xs(i) * xd;
+      sm.dg[i] = __expf(cc.g[i]) * qd + rowm - colm - z;
+      sm.dgt[i] = z;
+    }
   }
   __syncthreads();
-  if (tid == 0) {
-    float tr = 0.f, zs = 0.f;
-    for (int f = 0; f < kD; ++f) tr += sm.DP[f][f];
-    for (int i = 0; i < kBC; ++i) zs += sm.dgt[i];
-    sm.dG = eG * tr + zs;
-  }
   // dM o D, D_{is} = e^{g_i-g_s} for s <= i
   for (int e = tid; e < kBC * kBC; e += kThreads) {
     const int i = e >> 5, s = e & 31;
@@ -436,40 +735,50 @@ __global__ void __launch_bounds__(kThreads) falcon1_bwd_chunk_kernel(BwdArgs a) 
     if (t0 + r < T) dq_out[int64_t(t0 + r) * kD + s] = __expf(cc.g[r]) * sm.DQT[r][s] + v;
   });
   mm<kBC, kD, kBC, true, false>(&sm.DM[0][0], kPN, &cc.Q[0][0], kPW, w, l,
-                                [&](int r, int s, float v) { sm.DX[r][s] = xs(r) * DXH[r][s] + v; });
+                                [&](int r, int s, float v) { sm.RR[r][s] = xs(r) * sm.DXH[r][s] + v; });
   __syncthreads();
-  // dY = (I + A)^{-T} dW, dZ = (I + A)^{-T} dU (in place), a column per thread
-  if (tid < 2 * kD) {
-    const int j = tid & 63;
-    float (*D)[kPW] = tid < kD ? sm.DW : sm.DU;
-    float col[kBC];
-    solve_lower_t(cc.AA, [&](int i) { return D[i][j]; }, col);
-#pragma unroll
-    for (int i = 0; i < kBC; ++i) D[i][j] = col[i];
-  }
+  // dY = T^T dW (into DQT), dZ = T^T dU (into DO)
+  float (*DY)[kPW] = sm.DQT;
+  float (*DZ)[kPW] = sm.DO;
+  mm<kBC, kD, kBC, true, false>(&cc.TT[0][0], kPN, &sm.DW[0][0], kPW, w, l,
+                                [&](int r, int s, float v) { DY[r][s] = v; });
+  mm<kBC, kD, kBC, true, false>(&cc.TT[0][0], kPN, &sm.DU[0][0], kPW, w, l,
+                                [&](int r, int s, float v) { DZ[r][s] = v; });
   __syncthreads();
   // dA = -dY W^T - dZ U^T (strictly lower part used)
-  mm<kBC, kBC, kD, false, true>(&sm.DW[0][0], kPW, &cc.W[0][0], kPW, w, l,
+  mm<kBC, kBC, kD, false, true>(&DY[0][0], kPW, &cc.W[0][0], kPW, w, l,
                                 [&](int r, int s, float v) { sm.DM[r][s] = -v; });
-  mm<kBC, kBC, kD, false, true>(&sm.DU[0][0], kPW, &cc.U[0][0], kPW, w, l,
+  mm<kBC, kBC, kD, false, true>(&DZ[0][0], kPW, &cc.U[0][0], kPW, w, l,
                                 [&](int r, int s, float v) { sm.DM[r][s] -= v; });
   // Y = Diag(eta e^{gp}) X, Z = Diag(eta) V
   float* dv_out = a.dv + bh * T * kD;
-  for (int e = tid; e < kBC * kD; e += kThreads) {
-    const int i = e >> 6, f = e & 63;
-    sm.DX[i][f] = fmaf(cc.eta[i] * __expf(cc.gp[i]), sm.DW[i][f], sm.DX[i][f]);
-    if (t0 + i < T) dv_out[int64_t(t0 + i) * kD + f] = cc.eta[i] * sm.DU[i][f];
-  }
-  if (tid < kBC) {
-    const int i = tid;
+  {
+    const int i = tid >> 3, p = tid & 7;
+    const float egp = __expf(cc.gp[i]), eta = cc.eta[i];
     float xy = 0.f, vz = 0.f;
-    for (int f = 0; f < kD; ++f) {
-      xy = fmaf(cc.X[i][f], sm.DW[i][f], xy);
-      if (t0 + i < T) vz = fmaf(ld_row(V, t0 + i, f), sm.DU[i][f], vz);
+#pragma unroll
+    for (int k = 0; k < 8; k += 4) {
+      const int f = 8 * p + k;
+      const float4 dy = *reinterpret_cast<const float4*>(&DY[i][f]);
+      const float4 dz = *reinterpret_cast<const float4*>(&DZ[i][f]);
+      const float4 x = *reinterpret_cast<const float4*>(&cc.X[i][f]);
+      const float4 v = *reinterpret_cast<const float4*>(&cc.V[i][f]);
+      float4 dx = *reinterpret_cast<const float4*>(&sm.RR[i][f]);
+      xy = fmaf(x.x, dy.x, fmaf(x.y, dy.y, fmaf(x.z, dy.z, fmaf(x.w, dy.w, xy))));
+      vz = fmaf(v.x, dz.x, fmaf(v.y, dz.y, fmaf(v.z, dz.z, fmaf(v.w, dz.w, vz))));
+      const float sy = eta * egp;
+      dx.x = fmaf(sy, dy.x, dx.x); dx.y = fmaf(sy, dy.y, dx.y);
+      dx.z = fmaf(sy, dy.z, dx.z); dx.w = fmaf(sy, dy.w, dx.w);
+      *reinterpret_cast<float4*>(&sm.RR[i][f]) = dx;
+      if (t0 + i < T)
+        *reinterpret_cast<float4*>(dv_out + int64_t(t0 + i) * kD + f) =
+            make_float4(eta * dz.x, eta * dz.y, eta * dz.z, eta * dz.w);
     }
-    const float egp = __expf(cc.gp[i]);
-    sm.deta[i] = egp * xy + vz;
-    sm.dgp[i] = cc.eta[i] * egp * xy;
+    xy = sum8(xy); vz = sum8(vz);
+    if (p == 0) {
+      sm.deta[i] = egp * xy + vz;
+      sm.dgp[i] = eta * egp * xy;
+    }
   }
   __syncthreads();
   // A_{is} = eta_i e^{gp_i-g_s} k_{is}: D2 = dA o e^{gp_i-g_s} (s < i)
@@ -478,16 +787,21 @@ __global__ void __launch_bounds__(kThreads) falcon1_bwd_chunk_kernel(BwdArgs a) 
     sm.DM[i][s] = s < i ? sm.DM[i][s] * __expf(cc.gp[i] - cc.g[s]) : 0.f;
   }
   __syncthreads();
-  if (tid < kBC) {
-    const int i = tid;
+  {
+    const int i = tid >> 3, p = tid & 7;
     float row = 0.f, col = 0.f;
-    for (int s = 0; s < kBC; ++s) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int s = 4 * p + k;
       row = fmaf(sm.DM[i][s], cc.KX[i][s], row);
       col = fmaf(cc.eta[s] * sm.DM[s][i], cc.KX[s][i], col);
     }
-    sm.deta[i] += row;
-    sm.dgp[i] += cc.eta[i] * row;
-    sm.dg[i] -= col;
+    row = sum8(row); col = sum8(col);
+    if (p == 0) {
+      sm.deta[i] += row;
+      sm.dgp[i] += cc.eta[i] * row;
+      sm.dg[i] -= col;
+    }
   }
   __syncthreads();
   // dK = Diag(eta) D2 (strictly lower), dX += (dK + dK^T) X
@@ -497,52 +811,71 @@ __global__ void __launch_bounds__(kThreads) falcon1_bwd_chunk_kernel(BwdArgs a) 
   }
   __syncthreads();
   mm<kBC, kD, kBC, false, false>(&sm.DM[0][0], kPN, &cc.X[0][0], kPW, w, l,
-                                 [&](int r, int s, float v) { sm.DX[r][s] += v; });
+                                 [&](int r, int s, float v) { sm.RR[r][s] += v; });
   mm<kBC, kD, kBC, true, false>(&sm.DM[0][0], kPN, &cc.X[0][0], kPW, w, l,
-                                [&](int r, int s, float v) { sm.DX[r][s] += v; });
-  __syncthreads();
+                                [&](int r, int s, float v) { sm.RR[r][s] += v; });
   // gates: g -> log decay -> (eta, lam); eta -> (beta, lam, ||x||^2)
-  if (tid < kBC) {
-    const int i = tid;
-    sm.dgt[i] = sm.dg[i] + (i + 1 < kBC ? sm.dgp[i + 1] : 0.f) + (i == kBC - 1 ? sm.dG : 0.f);
-  }
-  __syncthreads();
-  if (tid < kBC) {
-    const int i = tid;
-    float dlg = 0.f;
-    for (int r = i; r < kBC; ++r) dlg += sm.dgt[r];
-    const int fl = cc.flags[i];
-    const float eta = cc.eta[i], lamv = cc.lamv[i];
-    float deta = sm.deta[i], dlam = 0.f;
-    if ((fl & 4) && !(fl & 2)) {
-      const float dalpha = -dlg / (1.0f - eta * lamv);
-      deta += dalpha * lamv;
-      dlam += dalpha * eta;
+  if (w == 0) {
+    const int i = l;
+    float dgt = 0.f;
+    if (i < kBC) {
+      float dG = 0.f;
+      if (i == kBC - 1) {
+        float zs = 0.f;
+        for (int r = 0; r < kBC; ++r) zs += sm.dgt[r];
+        dG = eG * (sm.trp[0] + sm.trp[1] + sm.trp[2] + sm.trp[3]) + zs;
+      }
+      dgt = sm.dg[i] + (i + 1 < kBC ? sm.dgp[i + 1] : 0.f) + dG;
     }
-    float dbeta = 0.f, dE = 0.f;
-    if (fl & 1) {
-      const float den = cc.den[i];
-      dbeta = deta / den;
-      const float dden = -deta * eta / den;
-      dlam += dden;
-      dE = dden;
+    // suffix sums over the chunk: dlg_i = sum_{r >= i} dgt_r
+    float dlg = dgt;
+#pragma unroll
+    for (int d = 1; d < kBC; d <<= 1) {
+      const float n = __shfl_down(dlg, d);
+      if (i + d < kBC) dlg += n;
     }
-    const int t = t0 + i;
-    if (t < T) {
-      a.dbeta[bh * T + t] = dbeta;
-      a.dlam[bh * T + t] = dlam;
+    if (i < kBC) {
+      const int fl = cc.flags[i];
+      const float eta = cc.eta[i], lamv = cc.lamv[i];
+      float deta = sm.deta[i], dlam = 0.f;
+      if ((fl & 4) && !(fl & 2)) {
+        const float dalpha = -dlg / (1.0f - eta * lamv);
+        deta += dalpha * lamv;
+        dlam += dalpha * eta;
+      }
+      float dbeta = 0.f, dE = 0.f;
+      if (fl & 1) {
+        const float den = cc.den[i];
+        dbeta = deta / den;
+        const float dden = -deta * eta / den;
+        dlam += dden;
+        dE = dden;
+      }
+      const int t = t0 + i;
+      if (t < T) {
+        a.dbeta[bh * T + t] = dbeta;
+        a.dlam[bh * T + t] = dlam;
+      }
+      sm.dgp[i] = dE;     // reused: d||x_i||^2
     }
-    sm.deta[i] = dE;     // reused: d||x_i||^2
   }
   __syncthreads();
   // x_t = phi(k_{t-1}): row i of dX is the gradient of key t0 + i - 1
   float* dk_out = a.dphi_k + bh * T * kD;
   const bool fresh = (a.k_prev == nullptr);
-  for (int e = tid; e < kBC * kD; e += kThreads) {
-    const int i = e >> 6, f = e & 63, t = t0 + i;
-    const float dx = fmaf(2.0f * sm.deta[i], cc.X[i][f], sm.DX[i][f]);
-    if (t >= 1 && t < T) dk_out[int64_t(t - 1) * kD + f] = dx;
-    if (t == 0 && !fresh && a.dk_prev) a.dk_prev[bh * kD + f] = dx;
+  {
+    const int i = tid >> 3, f0 = (tid & 7) * 8, t = t0 + i;
+    const float dE2 = 2.0f * sm.dgp[i];
+    float o[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o[k] = fmaf(dE2, cc.X[i][f0 + k], sm.RR[i][f0 + k]);
+    float* dst = nullptr;
+    if (t >= 1 && t < T) dst = dk_out + int64_t(t - 1) * kD + f0;
+    else if (t == 0 && !fresh && a.dk_prev) dst = a.dk_prev + bh * kD + f0;
+    if (dst) {
+      reinterpret_cast<float4*>(dst)[0] = make_float4(o[0], o[1], o[2], o[3]);
+      reinterpret_cast<float4*>(dst)[1] = make_float4(o[4], o[5], o[6], o[7]);
+    }
   }
   // the last key feeds no token of this call
   if (c == a.nchunks - 1)
@@ -571,15 +904,15 @@ hipError_t launch_bwd(const ProblemArgs& p, const BwdBuffers& b, hipStream_t st)
   a.ckpt = ws + n * kMapFloats;
   a.adj = a.ckpt + n * kD * kD;
   a.T = p.T; a.nchunks = nchunks; a.eps = p.eps; a.eps_gamma = p.eps_gamma;
+  const int nunits = int(2 * BH);
+  const unsigned chain_blocks = unsigned((nunits + 7) / 8) * 32u;
   if (p.bf16) {
     hipLaunchKernelGGL(falcon1_bwd_maps_kernel<bf16_t>, dim3(unsigned(n)), dim3(kThreads), 0, st, a);
-    hipLaunchKernelGGL(falcon1_bwd_state_kernel, dim3(unsigned(BH)), dim3(kThreads), 0, st, a);
-    hipLaunchKernelGGL(falcon1_bwd_adjoint_kernel<bf16_t>, dim3(unsigned(BH)), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(falcon1_bwd_chain_kernel<bf16_t>, dim3(chain_blocks), dim3(kThreads), 0, st, a, nunits);
     hipLaunchKernelGGL(falcon1_bwd_chunk_kernel<bf16_t>, dim3(unsigned(n)), dim3(kThreads), 0, st, a);
   } else {
     hipLaunchKernelGGL(falcon1_bwd_maps_kernel<float>, dim3(unsigned(n)), dim3(kThreads), 0, st, a);
-    hipLaunchKernelGGL(falcon1_bwd_state_kernel, dim3(unsigned(BH)), dim3(kThreads), 0, st, a);
-    hipLaunchKernelGGL(falcon1_bwd_adjoint_kernel<float>, dim3(unsigned(BH)), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(falcon1_bwd_chain_kernel<float>, dim3(chain_blocks), dim3(kThreads), 0, st, a, nunits);
     hipLaunchKernelGGL(falcon1_bwd_chunk_kernel<float>, dim3(unsigned(n)), dim3(kThreads), 0, st, a);
   }
   return hipGetLastError();
