@@ -12,11 +12,11 @@
 // of Section 4.4 applied per chunk; exact up to rounding).  Training
 // differentiates through the update (Section 3), so for L = <dO, O> +
 // <dS_T, S_T> the backward is:
-//   1. chunk maps P, H, Qt for every chunk (chunk-parallel);
+//   1. chunk maps P, H and G = Qt^T dO for every chunk (chunk-parallel);
 //   2. in one launch, the forward state chain, saving the state S_c entering
 //      each chunk, and the reverse adjoint chain: with Lam_c = dL/dS at the
-//      end of chunk c, Lam_{c-1} = P_c^T Lam_c + Qt_c^T dO_c, and dS0 = the
-//      last Lam (the two chains need only the maps);
+//      end of chunk c, Lam_{c-1} = P_c^T Lam_c + G_c, and dS0 = the last Lam
+//      (the two chains need only the maps);
 //   3. per chunk (chunk-parallel), reverse mode through the chunk maps from
 //      dP = Lam S_c^T, dH = Lam, dQt = dO S_c^T, dOt = dO (dP is never formed:
 //      Xh dP = (Xh Lam) S_c^T and W dP^T = (W S_c) Lam^T):
@@ -49,9 +49,9 @@ constexpr int kThreads = 256;  // four waves
 //   PA  P as the A operand of P S:      ((w*4 + j)*64 + l)*4 + e <-> P[16w + (l&15)][4(4j+e) + (l>>4)]
 //   PB  P as the B operand of Lam^T P:  ((w*4 + j)*64 + l)*4 + e <-> P[4(4j+e) + (l>>4)][16w + (l&15)]
 //   HD  H in accumulator order:         ((w*4 + cg)*64 + l)*4 + r <-> H[16w + 4(l>>4) + r][16cg + (l&15)]
-//   QB  Qt as the B operand of dO^T Qt: ((w*2 + j)*64 + l)*4 + e <-> Qt[4(4j+e) + (l>>4)][16w + (l&15)]
-constexpr int kOffPA = 0, kOffPB = 4096, kOffHD = 8192, kOffQB = 12288;
-constexpr int kMapFloats = 14336;
+//   GD  G^T in accumulator order:       ((w*4 + cg)*64 + l)*4 + r <-> G[16w + (l&15)][16cg + 4(l>>4) + r]
+constexpr int kOffPA = 0, kOffPB = 4096, kOffHD = 8192, kOffGD = 12288;
+constexpr int kMapFloats = 16384;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -125,7 +125,7 @@ struct BwdArgs {
   float* dlam;
   float* dS0;
   float* dk_prev;
-  float* maps;     // per chunk: PA, PB, HD, QB (above)
+  float* maps;     // per chunk: PA, PB, HD, GD (above)
   float* ckpt;     // per chunk: S entering the chunk, ((cg*4 + w)*64 + l)*4 + r <-> S[16w + 4(l>>4) + r][16cg + (l&15)]
   float* adj;      // per chunk: dL/dS at its end, ((cg*4 + w)*64 + l)*4 + r <-> Lam[16w + (l&15)][16cg + 4(l>>4) + r]
   int T, nchunks;
@@ -364,14 +364,26 @@ template <typename IO>
 __global__ void __launch_bounds__(kThreads) falcon1_bwd_maps_kernel(BwdArgs a) {
   __shared__ ChunkCore cc;
   __shared__ float TZ[kBC][kPN];
+  __shared__ __align__(16) float DO[kBC][kPW];
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;   // wave-uniform
   const int64_t bh = blockIdx.x / a.nchunks;
   const int c = blockIdx.x % a.nchunks;
+  const int T = a.T;
   {
     ChunkRegs<IO> r;
     chunk_load<IO>(r, a, bh, c, tid);
+    Raw8<IO> odr;
+    const int orow = c * kBC + (tid >> 3);
+    odr.load(static_cast<const IO*>(a.dO) + (bh * T + (orow < T ? orow : T - 1)) * kD + (tid & 7) * 8);
     chunk_store<IO>(cc, r, tid);
+    float od[8];
+    odr.get(od);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) od[k] = orow < T ? od[k] : 0.f;
+    const int i = tid >> 3, f0 = (tid & 7) * 8;
+    *reinterpret_cast<float4*>(&DO[i][f0]) = make_float4(od[0], od[1], od[2], od[3]);
+    *reinterpret_cast<float4*>(&DO[i][f0 + 4]) = make_float4(od[4], od[5], od[6], od[7]);
   }
   __syncthreads();
   chunk_forward(cc, a, c, tid, w, l);
@@ -415,15 +427,6 @@ __global__ void __launch_bounds__(kThreads) falcon1_bwd_maps_kernel(BwdArgs a) {
     reinterpret_cast<float4*>(out + kOffPA)[q] = pa;
     reinterpret_cast<float4*>(out + kOffPB)[q] = pb;
   }
-  for (int q = tid; q < 512; q += kThreads) {
-    const int ww = q >> 7, j = (q >> 6) & 1, ll = q & 63, lo = ll & 15, hi = ll >> 4;
-    float4 qb;
-    qb.x = QT[4 * (4 * j + 0) + hi][16 * ww + lo];
-    qb.y = QT[4 * (4 * j + 1) + hi][16 * ww + lo];
-    qb.z = QT[4 * (4 * j + 2) + hi][16 * ww + lo];
-    qb.w = QT[4 * (4 * j + 3) + hi][16 * ww + lo];
-    reinterpret_cast<float4*>(out + kOffQB)[q] = qb;
-  }
   __syncthreads();
   // H = Xh^T U
   mm<kD, kD, kBC, true, false>(&XH[0][0], kPW, &cc.U[0][0], kPW, w, l,
@@ -438,11 +441,25 @@ __global__ void __launch_bounds__(kThreads) falcon1_bwd_maps_kernel(BwdArgs a) {
     hd.w = PS[16 * ww + 4 * hi + 3][16 * cg + lo];
     reinterpret_cast<float4*>(out + kOffHD)[q] = hd;
   }
+  __syncthreads();
+  // G = Qt^T dO
+  mm<kD, kD, kBC, true, false>(&QT[0][0], kPW, &DO[0][0], kPW, w, l,
+                               [&](int r, int s, float v) { PS[r][s] = v; });
+  __syncthreads();
+  for (int q = tid; q < 1024; q += kThreads) {
+    const int ww = q >> 8, cg = (q >> 6) & 3, ll = q & 63, lo = ll & 15, hi = ll >> 4;
+    float4 gd;
+    gd.x = PS[16 * ww + lo][16 * cg + 4 * hi + 0];
+    gd.y = PS[16 * ww + lo][16 * cg + 4 * hi + 1];
+    gd.z = PS[16 * ww + lo][16 * cg + 4 * hi + 2];
+    gd.w = PS[16 * ww + lo][16 * cg + 4 * hi + 3];
+    reinterpret_cast<float4*>(out + kOffGD)[q] = gd;
+  }
 }
 
 // ---- launch 2: the state chain and the adjoint chain ---------------------------
 // Columns of S evolve independently under S' = P S + H, and so do the rows of
-// Lam^T under Lam^T' = Lam^T P + dO^T Qt, so each sequence's chains split
+// Lam^T under Lam^T' = Lam^T P + G^T, so each sequence's chains split
 // into four 16-column groups.  One workgroup runs one (chain, sequence,
 // group); its four waves own the 16-row blocks of the 64 x 16 block, held in
 // MFMA accumulators, and share the block through LDS.  Each chunk's operands
@@ -454,8 +471,12 @@ struct ChainSmem {
   float L[16][kPW];      // adjoint chain: Lam^T[16cg .. 16cg+15][:]
 };
 
-constexpr int kRing = 4;   // chunks of operands in flight per chain
+constexpr int kRing = 3;   // chunks of operands in flight per chain
 
+// The chain loops run full groups of kRing steps whose prefetches are
+// unconditional (a prefetch past the last chunk re-reads the last chunk), so
+// the compiler knows how many loads follow each one and waits only for the
+// oldest; the last n % kRing steps run without prefetches.
 template <typename IO>
 __device__ __forceinline__ void chain_state(const BwdArgs& a, ChainSmem& sm, int64_t bh, int cg, int w, int l) {
   const int g = l >> 4, c16 = l & 15;
@@ -467,117 +488,111 @@ __device__ __forceinline__ void chain_state(const BwdArgs& a, ChainSmem& sm, int
   const float* mp = a.maps + bh * n * kMapFloats;
   float4 pa[kRing][4], hd[kRing];
   auto load = [&](int c, float4 (&p4)[4], float4& h) {
-    const float* cp = mp + c * kMapFloats;
+    const float* cp = mp + (c < n ? c : n - 1) * kMapFloats;
 #pragma unroll
     for (int j = 0; j < 4; ++j) p4[j] = reinterpret_cast<const float4*>(cp + kOffPA)[(w * 4 + j) * 64 + l];
     h = reinterpret_cast<const float4*>(cp + kOffHD)[(w * 4 + cg) * 64 + l];
   };
+  auto step = [&](int c, const float4 (&p4)[4], const float4& h) {
+    // S (entering chunk c) to LDS and to the checkpoint, then S <- P S + H
 #pragma unroll
-  for (int d = 0; d < kRing; ++d)
-    if (d < n) load(d, pa[d], hd[d]);
-  for (int c0 = 0; c0 < n; c0 += kRing) {
+    for (int r = 0; r < 4; ++r) sm.B[16 * w + 4 * g + r][c16] = S[r];
+    float* ck = a.ckpt + (bh * n + c) * kD * kD;
+    reinterpret_cast<float4*>(ck)[(cg * 4 + w) * 64 + l] = make_float4(S[0], S[1], S[2], S[3]);
+    __syncthreads();
+    f32x4 acc = {h.x, h.y, h.z, h.w};
 #pragma unroll
-    for (int d = 0; d < kRing; ++d) {
-      const int c = c0 + d;
-      if (c < n) {
-        // S (entering chunk c) to LDS and to the checkpoint
+    for (int j = 0; j < 4; ++j) {
+      const float pe[4] = {p4[j].x, p4[j].y, p4[j].z, p4[j].w};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sm.B[16 * w + 4 * g + r][c16] = S[r];
-        float* ck = a.ckpt + (bh * n + c) * kD * kD;
-        reinterpret_cast<float4*>(ck)[(cg * 4 + w) * 64 + l] = make_float4(S[0], S[1], S[2], S[3]);
-        __syncthreads();
-        f32x4 acc = {hd[d].x, hd[d].y, hd[d].z, hd[d].w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float pe[4] = {pa[d][j].x, pa[d][j].y, pa[d][j].z, pa[d][j].w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int kb = 4 * j + e;
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pe[e], sm.B[4 * kb + g][c16], acc, 0, 0, 0);
-          }
-        }
-        S = acc;
-        __syncthreads();
-        if (c + kRing < n) load(c + kRing, pa[d], hd[d]);
+      for (int e = 0; e < 4; ++e) {
+        const int kb = 4 * j + e;
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pe[e], sm.B[4 * kb + g][c16], acc, 0, 0, 0);
       }
     }
+    S = acc;
+    __syncthreads();
+  };
+#pragma unroll
+  for (int d = 0; d < kRing; ++d) load(d, pa[d], hd[d]);
+  int c0 = 0;
+  for (; c0 + kRing <= n; c0 += kRing) {
+#pragma unroll
+    for (int d = 0; d < kRing; ++d) {
+      step(c0 + d, pa[d], hd[d]);
+      load(c0 + d + kRing, pa[d], hd[d]);
+    }
   }
+#pragma unroll
+  for (int d = 0; d < kRing - 1; ++d)
+    if (c0 + d < n) step(c0 + d, pa[d], hd[d]);
 }
 
 template <typename IO>
 __device__ __forceinline__ void chain_adjoint(const BwdArgs& a, ChainSmem& sm, int64_t bh, int cg, int w, int l) {
   const int g = l >> 4, c16 = l & 15;
-  const int T = a.T, n = a.nchunks;
-  const IO* dO = static_cast<const IO*>(a.dO) + bh * T * kD;
+  const int n = a.nchunks;
   // Lam^T block in accumulator order: lane holds Lam^T[16cg + 4g + r][16w + c16] = Lam[16w + c16][16cg + 4g + r]
   f32x4 Lt;
 #pragma unroll
   for (int r = 0; r < 4; ++r)
     Lt[r] = a.dS_T ? a.dS_T[bh * kD * kD + (16 * w + c16) * kD + 16 * cg + 4 * g + r] : 0.f;
   const float* mp = a.maps + bh * n * kMapFloats;
-  float4 pb[kRing][4], qb[kRing][2];
-  Raw1<IO> od[kRing][8];
-  auto load = [&](int c, float4 (&p4)[4], float4 (&q4)[2], Raw1<IO> (&o8)[8]) {
-    const float* cp = mp + c * kMapFloats;
+  float4 pb[kRing][4], gd[kRing];
+  // operands of step s, which processes chunk n - 1 - s
+  auto load = [&](int s, float4 (&p4)[4], float4& g4) {
+    const float* cp = mp + (s < n ? n - 1 - s : 0) * kMapFloats;
 #pragma unroll
     for (int j = 0; j < 4; ++j) p4[j] = reinterpret_cast<const float4*>(cp + kOffPB)[(w * 4 + j) * 64 + l];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) q4[j] = reinterpret_cast<const float4*>(cp + kOffQB)[(w * 2 + j) * 64 + l];
-    // dO^T[16cg + c16][4kb + g] = dO[t0 + 4kb + g][16cg + c16]; rows past T
-    // read row T - 1 and are replaced by 0 where used
-#pragma unroll
-    for (int kb = 0; kb < 8; ++kb) {
-      const int t = c * kBC + 4 * kb + g;
-      o8[kb].load(dO + int64_t(t < T ? t : T - 1) * kD + 16 * cg + c16);
-    }
+    g4 = reinterpret_cast<const float4*>(cp + kOffGD)[(w * 4 + cg) * 64 + l];
   };
+  auto step = [&](int s, const float4 (&p4)[4], const float4& g4) {
+    // Lam^T (at the end of chunk c) to LDS and to the adjoint store, then
+    // Lam^T <- Lam^T P + G^T
+    const int c = n - 1 - s;
 #pragma unroll
-  for (int d = 0; d < kRing; ++d)
-    if (d < n) load(n - 1 - d, pb[d], qb[d], od[d]);
-  for (int c0 = 0; c0 < n; c0 += kRing) {
+    for (int r = 0; r < 4; ++r) sm.L[4 * g + r][16 * w + c16] = Lt[r];
+    float* ad = a.adj + (bh * n + c) * kD * kD;
+    reinterpret_cast<float4*>(ad)[(cg * 4 + w) * 64 + l] = make_float4(Lt[0], Lt[1], Lt[2], Lt[3]);
+    __syncthreads();
+    f32x4 acc = {g4.x, g4.y, g4.z, g4.w};
 #pragma unroll
-    for (int d = 0; d < kRing; ++d) {
-      const int step = c0 + d, c = n - 1 - step;
-      if (step < n) {
+    for (int j = 0; j < 4; ++j) {
+      const float pe[4] = {p4[j].x, p4[j].y, p4[j].z, p4[j].w};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sm.L[4 * g + r][16 * w + c16] = Lt[r];
-        float* ad = a.adj + (bh * n + c) * kD * kD;
-        reinterpret_cast<float4*>(ad)[(cg * 4 + w) * 64 + l] = make_float4(Lt[0], Lt[1], Lt[2], Lt[3]);
-        __syncthreads();
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float pe[4] = {pb[d][j].x, pb[d][j].y, pb[d][j].z, pb[d][j].w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int kb = 4 * j + e;
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.L[c16][4 * kb + g], pe[e], acc, 0, 0, 0);
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const float qe[4] = {qb[d][j].x, qb[d][j].y, qb[d][j].z, qb[d][j].w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int t = c * kBC + 4 * (4 * j + e) + g;
-            const float ov = t < T ? od[d][4 * j + e].get() : 0.f;
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ov, qe[e], acc, 0, 0, 0);
-          }
-        }
-        Lt = acc;
-        __syncthreads();
-        if (step + kRing < n) load(c - kRing, pb[d], qb[d], od[d]);
+      for (int e = 0; e < 4; ++e) {
+        const int kb = 4 * j + e;
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.L[c16][4 * kb + g], pe[e], acc, 0, 0, 0);
       }
     }
+    Lt = acc;
+    __syncthreads();
+  };
+#pragma unroll
+  for (int d = 0; d < kRing; ++d) load(d, pb[d], gd[d]);
+  int s0 = 0;
+  for (; s0 + kRing <= n; s0 += kRing) {
+#pragma unroll
+    for (int d = 0; d < kRing; ++d) {
+      step(s0 + d, pb[d], gd[d]);
+      load(s0 + d + kRing, pb[d], gd[d]);
+    }
   }
+#pragma unroll
+  for (int d = 0; d < kRing - 1; ++d)
+    if (s0 + d < n) step(s0 + d, pb[d], gd[d]);
   if (a.dS0) {
     float* d = a.dS0 + bh * kD * kD + (16 * w + c16) * kD + 16 * cg + 4 * g;
     *reinterpret_cast<float4*>(d) = make_float4(Lt[0], Lt[1], Lt[2], Lt[3]);
   }
 }
 
+// At most 168 registers: three waves per SIMD keep all 2 x 4 x B x H
+// workgroups of the 8 x 12 training shape resident at once (three per CU),
+// so no chain waits for a free CU.
 template <typename IO>
-__global__ void __launch_bounds__(kThreads) falcon1_bwd_chain_kernel(BwdArgs a, int nunits) {
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
+falcon1_bwd_chain_kernel(BwdArgs a, int nunits) {
   __shared__ ChainSmem sm;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;

@@ -196,7 +196,7 @@ falcon_status falcon_decode_step(const falcon_problem* p,
  *  (FALCON_ERR_ALIAS).
  *  workspace : device scratch of at least falcon_bwd_workspace_bytes(p)
  *              bytes, 16-byte aligned (the per-chunk maps, the state
- *              entering each chunk and the adjoint leaving it; 88 KiB per
+ *              entering each chunk and the adjoint leaving it; 96 KiB per
  *              32-token chunk per (b, h)).
  */
 falcon_status falcon_bwd_chunked(const falcon_problem* p,
