@@ -58,45 +58,55 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // D (M x N) = op(A) op(B) on the matrix cores in float32; A is M x K (stored
 // K x M when TA), B is K x N (stored N x K when TB), both in LDS with float
 // pitches pa, pb (multiples of 4, 16-byte aligned rows).  The 16x16 output
-// tiles go round-robin to the four waves (the same lane always gets the same
-// output element for a given M, N), and epi(row, col, value) receives each
-// result.  Within each 16-wide slice of K, lane group g supplies k = 16m + 4g
-// + e at step e, so an operand stored with K contiguous is read 16 bytes at a
-// time.
+// tiles go round-robin to the four waves (tile w + 4 it; the same lane always
+// gets the same output element for a given M, N), and epi(row, col, value)
+// receives each result.  With N / 16 dividing 4, all of a wave's tiles share
+// one column block, so the wave reads its B fragments once; the operands are
+// read up front and the tiles' accumulation chains interleave.  Within each
+// 16-wide slice of K, lane group g supplies k = 16m + 4g + e at step e, so
+// an operand stored with K contiguous is read 16 bytes at a time.
 template <int M, int N, int K, bool TA, bool TB, typename Epi>
 __device__ __forceinline__ void mm(const float* A, int pa, const float* B, int pb, int w, int l, Epi epi) {
   const int g = l >> 4, c16 = l & 15;
-  constexpr int TN = N / 16;
+  constexpr int TN = N / 16, TM = M / 16, IT = TM * TN / 4, KS = K / 4;
   static_assert(K % 16 == 0, "K must be a multiple of 16");
-  static_assert((M / 16) * TN % 4 == 0, "tiles must split evenly over the four waves");
+  static_assert(TM * TN % 4 == 0 && 4 % TN == 0, "tiles must split evenly over the four waves");
+  const int tn = w % TN;
+  float bv[KS], av[IT][KS];
 #pragma unroll
-  for (int it = 0; it < (M / 16) * TN / 4; ++it) {
-    const int tile = w + 4 * it;
-    const int tm = tile / TN, tn = tile % TN;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int m = 0; m < K / 16; ++m) {
+    const int k0 = 16 * m + 4 * g;
+    if (TB) {
+      const float4 v = *reinterpret_cast<const float4*>(B + (16 * tn + c16) * pb + k0);
+      bv[4 * m] = v.x; bv[4 * m + 1] = v.y; bv[4 * m + 2] = v.z; bv[4 * m + 3] = v.w;
+    } else {
 #pragma unroll
-    for (int m = 0; m < K / 16; ++m) {
-      const int k0 = 16 * m + 4 * g;
-      float av[4], bv[4];
-      if (TA) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) av[e] = A[(k0 + e) * pa + 16 * tm + c16];
-      } else {
-        const float4 v = *reinterpret_cast<const float4*>(A + (16 * tm + c16) * pa + k0);
-        av[0] = v.x; av[1] = v.y; av[2] = v.z; av[3] = v.w;
-      }
-      if (TB) {
-        const float4 v = *reinterpret_cast<const float4*>(B + (16 * tn + c16) * pb + k0);
-        bv[0] = v.x; bv[1] = v.y; bv[2] = v.z; bv[3] = v.w;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) bv[e] = B[(k0 + e) * pb + 16 * tn + c16];
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], bv[e], acc, 0, 0, 0);
+      for (int e = 0; e < 4; ++e) bv[4 * m + e] = B[(k0 + e) * pb + 16 * tn + c16];
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) epi(16 * tm + 4 * g + r, 16 * tn + c16, acc[r]);
+    for (int it = 0; it < IT; ++it) {
+      const int tm = (w + 4 * it) / TN;
+      if (TA) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) av[it][4 * m + e] = A[(k0 + e) * pa + 16 * tm + c16];
+      } else {
+        const float4 v = *reinterpret_cast<const float4*>(A + (16 * tm + c16) * pa + k0);
+        av[it][4 * m] = v.x; av[it][4 * m + 1] = v.y; av[it][4 * m + 2] = v.z; av[it][4 * m + 3] = v.w;
+      }
+    }
+  }
+  f32x4 acc[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) acc[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < KS; ++k)
+#pragma unroll
+    for (int it = 0; it < IT; ++it) acc[it] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[it][k], bv[k], acc[it], 0, 0, 0);
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int tm = (w + 4 * it) / TN;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) epi(16 * tm + 4 * g + r, 16 * tn + c16, acc[it][r]);
   }
 }
 
