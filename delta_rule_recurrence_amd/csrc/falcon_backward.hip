@@ -59,55 +59,123 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // K x M when TA), B is K x N (stored N x K when TB), both in LDS with float
 // pitches pa, pb (multiples of 4, 16-byte aligned rows).  The 16x16 output
 // tiles go round-robin to the four waves (tile w + 4 it; the same lane always
-// gets the same output element for a given M, N), and epi(row, col, value)
-// receives each result.  With N / 16 dividing 4, all of a wave's tiles share
-// one column block, so the wave reads its B fragments once; the operands are
-// read up front and the tiles' accumulation chains interleave.  Within each
-// 16-wide slice of K, lane group g supplies k = 16m + 4g + e at step e, so
-// an operand stored with K contiguous is read 16 bytes at a time.
-template <int M, int N, int K, bool TA, bool TB, typename Epi>
-__device__ __forceinline__ void mm(const float* A, int pa, const float* B, int pb, int w, int l, Epi epi) {
-  const int g = l >> 4, c16 = l & 15;
-  constexpr int TN = N / 16, TM = M / 16, IT = TM * TN / 4, KS = K / 4;
+// holds the same output element for a given M, N, so products of equal M, N
+// can be summed in registers).  With N / 16 dividing 4, all of a wave's tiles
+// share one column block, so the wave reads its B fragments once.  Within
+// each 16-wide slice of K, lane group g supplies k = 16m + 4g + e at step e,
+// so an operand stored with K contiguous is read 16 bytes at a time.
+//
+// load() reads the operands into registers, run() issues the MFMAs, store()
+// hands each result to epi(row, col, value).  Several products of a phase
+// load first, run next and store last, so that their LDS reads overlap and
+// no product waits behind another's stores.
+template <int M, int N, int K, bool TA, bool TB>
+struct Mm {
+  static constexpr int TN = N / 16, TM = M / 16, IT = TM * TN / 4, KS = K / 4;
   static_assert(K % 16 == 0, "K must be a multiple of 16");
   static_assert(TM * TN % 4 == 0 && 4 % TN == 0, "tiles must split evenly over the four waves");
-  const int tn = w % TN;
-  float bv[KS], av[IT][KS];
+  float bv[KS];
+  float av[IT][KS];
+  f32x4 acc[IT];
+
+  // rs(row) scales row `row` of A (rows of op(A)).
+  template <typename RowScale>
+  __device__ __forceinline__ void load(const float* A, int pa, const float* B, int pb, int w, int l, RowScale rs) {
+    const int g = l >> 4, c16 = l & 15;
+    const int tn = w % TN;
 #pragma unroll
-  for (int m = 0; m < K / 16; ++m) {
-    const int k0 = 16 * m + 4 * g;
-    if (TB) {
-      const float4 v = *reinterpret_cast<const float4*>(B + (16 * tn + c16) * pb + k0);
-      bv[4 * m] = v.x; bv[4 * m + 1] = v.y; bv[4 * m + 2] = v.z; bv[4 * m + 3] = v.w;
-    } else {
+    for (int m = 0; m < K / 16; ++m) {
+      const int k0 = 16 * m + 4 * g;
+      if (TB) {
+        const float4 v = *reinterpret_cast<const float4*>(B + (16 * tn + c16) * pb + k0);
+        bv[4 * m] = v.x; bv[4 * m + 1] = v.y; bv[4 * m + 2] = v.z; bv[4 * m + 3] = v.w;
+      } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) bv[4 * m + e] = B[(k0 + e) * pb + 16 * tn + c16];
+        for (int e = 0; e < 4; ++e) bv[4 * m + e] = B[(k0 + e) * pb + 16 * tn + c16];
+      }
+#pragma unroll
+      for (int it = 0; it < IT; ++it) {
+        const int tm = (w + 4 * it) / TN;
+        if (TA) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) av[it][4 * m + e] = A[(k0 + e) * pa + 16 * tm + c16];
+        } else {
+          const float4 v = *reinterpret_cast<const float4*>(A + (16 * tm + c16) * pa + k0);
+          av[it][4 * m] = v.x; av[it][4 * m + 1] = v.y; av[it][4 * m + 2] = v.z; av[it][4 * m + 3] = v.w;
+        }
+      }
     }
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-      const int tm = (w + 4 * it) / TN;
-      if (TA) {
+      const float sc = rs(16 * ((w + 4 * it) / TN) + c16);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) av[it][4 * m + e] = A[(k0 + e) * pa + 16 * tm + c16];
+      for (int k = 0; k < KS; ++k) av[it][k] *= sc;
+    }
+  }
+  __device__ __forceinline__ void load(const float* A, int pa, const float* B, int pb, int w, int l) {
+    const int g = l >> 4, c16 = l & 15;
+    const int tn = w % TN;
+#pragma unroll
+    for (int m = 0; m < K / 16; ++m) {
+      const int k0 = 16 * m + 4 * g;
+      if (TB) {
+        const float4 v = *reinterpret_cast<const float4*>(B + (16 * tn + c16) * pb + k0);
+        bv[4 * m] = v.x; bv[4 * m + 1] = v.y; bv[4 * m + 2] = v.z; bv[4 * m + 3] = v.w;
       } else {
-        const float4 v = *reinterpret_cast<const float4*>(A + (16 * tm + c16) * pa + k0);
-        av[it][4 * m] = v.x; av[it][4 * m + 1] = v.y; av[it][4 * m + 2] = v.z; av[it][4 * m + 3] = v.w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bv[4 * m + e] = B[(k0 + e) * pb + 16 * tn + c16];
+      }
+#pragma unroll
+      for (int it = 0; it < IT; ++it) {
+        const int tm = (w + 4 * it) / TN;
+        if (TA) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) av[it][4 * m + e] = A[(k0 + e) * pa + 16 * tm + c16];
+        } else {
+          const float4 v = *reinterpret_cast<const float4*>(A + (16 * tm + c16) * pa + k0);
+          av[it][4 * m] = v.x; av[it][4 * m + 1] = v.y; av[it][4 * m + 2] = v.z; av[it][4 * m + 3] = v.w;
+        }
       }
     }
   }
-  f32x4 acc[IT];
+  // acc = op(A) op(B), or init + op(A) op(B)
+  __device__ __forceinline__ void run() {
 #pragma unroll
-  for (int it = 0; it < IT; ++it) acc[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int k = 0; k < KS; ++k)
-#pragma unroll
-    for (int it = 0; it < IT; ++it) acc[it] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[it][k], bv[k], acc[it], 0, 0, 0);
-#pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int tm = (w + 4 * it) / TN;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) epi(16 * tm + 4 * g + r, 16 * tn + c16, acc[it][r]);
+    for (int it = 0; it < IT; ++it) acc[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+    mac();
   }
+  template <int K2, bool TA2, bool TB2>
+  __device__ __forceinline__ void run(const Mm<M, N, K2, TA2, TB2>& init) {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) acc[it] = init.acc[it];
+    mac();
+  }
+  __device__ __forceinline__ void mac() {
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
+#pragma unroll
+      for (int it = 0; it < IT; ++it) acc[it] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[it][k], bv[k], acc[it], 0, 0, 0);
+  }
+  template <typename Epi>
+  __device__ __forceinline__ void store(int w, int l, Epi epi) const {
+    const int g = l >> 4, c16 = l & 15;
+    const int tn = w % TN;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int tm = (w + 4 * it) / TN;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) epi(16 * tm + 4 * g + r, 16 * tn + c16, acc[it][r]);
+    }
+  }
+};
+
+// One product: load, run, store.
+template <int M, int N, int K, bool TA, bool TB, typename Epi>
+__device__ __forceinline__ void mm(const float* A, int pa, const float* B, int pb, int w, int l, Epi epi) {
+  Mm<M, N, K, TA, TB> f;
+  f.load(A, pa, B, pb, w, l);
+  f.run();
+  f.store(w, l, epi);
 }
 
 // Sum over the eight consecutive lanes that share a row.
@@ -303,14 +371,19 @@ __device__ void chunk_forward(ChunkCore& cc, const BwdArgs& a, int c, int tid, i
     }
   }
   __syncthreads();
-  // Gram, A and M
-  mm<kBC, kBC, kD, false, true>(&cc.X[0][0], kPW, &cc.X[0][0], kPW, w, l, [&](int r, int s, float v) {
-    cc.KX[r][s] = v;
-    cc.AA[r][s] = s < r ? cc.eta[r] * __expf(cc.gp[r] - cc.g[s]) * v : 0.f;
-  });
-  mm<kBC, kBC, kD, false, true>(&cc.Q[0][0], kPW, &cc.X[0][0], kPW, w, l, [&](int r, int s, float v) {
-    cc.MM[r][s] = s <= r ? __expf(cc.g[r] - cc.g[s]) * v : 0.f;
-  });
+  {
+    // Gram, A and M
+    Mm<kBC, kBC, kD, false, true> fk, fm;
+    fk.load(&cc.X[0][0], kPW, &cc.X[0][0], kPW, w, l);
+    fm.load(&cc.Q[0][0], kPW, &cc.X[0][0], kPW, w, l);
+    fk.run();
+    fm.run();
+    fk.store(w, l, [&](int r, int s, float v) {
+      cc.KX[r][s] = v;
+      cc.AA[r][s] = s < r ? cc.eta[r] * __expf(cc.gp[r] - cc.g[s]) * v : 0.f;
+    });
+    fm.store(w, l, [&](int r, int s, float v) { cc.MM[r][s] = s <= r ? __expf(cc.g[r] - cc.g[s]) * v : 0.f; });
+  }
   __syncthreads();
   // T11, T22 by substitution: lane j solves (I + A_bb) t = e_jj, b = j / 16
   if (tid < kBC) {
@@ -362,10 +435,13 @@ __device__ void chunk_factors(ChunkCore& cc, float (*TZ)[kPN], int tid, int w, i
     TZ[i][s] = t * cc.eta[s];
   }
   __syncthreads();
-  mm<kBC, kD, kBC, false, false>(&cc.AA[0][0], kPN, &cc.X[0][0], kPW, w, l,
-                                 [&](int r, int s, float v) { cc.W[r][s] = v; });
-  mm<kBC, kD, kBC, false, false>(&TZ[0][0], kPN, &cc.V[0][0], kPW, w, l,
-                                 [&](int r, int s, float v) { cc.U[r][s] = v; });
+  Mm<kBC, kD, kBC, false, false> fw, fu;
+  fw.load(&cc.AA[0][0], kPN, &cc.X[0][0], kPW, w, l);
+  fu.load(&TZ[0][0], kPN, &cc.V[0][0], kPW, w, l);
+  fw.run();
+  fu.run();
+  fw.store(w, l, [&](int r, int s, float v) { cc.W[r][s] = v; });
+  fu.store(w, l, [&](int r, int s, float v) { cc.U[r][s] = v; });
   __syncthreads();
 }
 
@@ -701,29 +777,49 @@ __global__ void __launch_bounds__(kThreads) falcon1_bwd_chunk_kernel(BwdArgs a) 
   chunk_factors(cc, sm.DM, tid, w, l);
   const float eG = __expf(cc.G);
   auto xs = [&](int i) { return __expf(cc.G - cc.g[i]); };
-  // Xh Lam (into DU), R = U - W S_c, dQt = dO S_c^T
-  mm<kBC, kD, kD, false, false>(&cc.X[0][0], kPW, &sm.LL[0][0], kPW, w, l,
-                                [&](int r, int s, float v) { sm.DU[r][s] = xs(r) * v; });
-  mm<kBC, kD, kD, false, false>(&cc.W[0][0], kPW, &sm.SC[0][0], kPW, w, l,
-                                [&](int r, int s, float v) { sm.RR[r][s] = cc.U[r][s] - v; });
-  mm<kBC, kD, kD, false, true>(&sm.DO[0][0], kPW, &sm.SC[0][0], kPW, w, l,
-                               [&](int r, int s, float v) { sm.DQT[r][s] = v; });
+  {
+    // Xh Lam (into DW), dU = Xh Lam + M^T dO, R = U - W S_c, dQt = dO S_c^T
+    Mm<kBC, kD, kD, false, false> fxl, fws;
+    Mm<kBC, kD, kD, false, true> fdq;
+    Mm<kBC, kD, kBC, true, false> fmo;
+    fxl.load(&cc.X[0][0], kPW, &sm.LL[0][0], kPW, w, l, xs);
+    fws.load(&cc.W[0][0], kPW, &sm.SC[0][0], kPW, w, l);
+    fdq.load(&sm.DO[0][0], kPW, &sm.SC[0][0], kPW, w, l);
+    fmo.load(&cc.MM[0][0], kPN, &sm.DO[0][0], kPW, w, l);
+    fxl.run();
+    fws.run();
+    fdq.run();
+    fmo.run(fxl);
+    fxl.store(w, l, [&](int r, int s, float v) { sm.DW[r][s] = v; });
+    fmo.store(w, l, [&](int r, int s, float v) { sm.DU[r][s] = v; });
+    fws.store(w, l, [&](int r, int s, float v) { sm.RR[r][s] = cc.U[r][s] - v; });
+    fdq.store(w, l, [&](int r, int s, float v) { sm.DQT[r][s] = v; });
+  }
   __syncthreads();
-  // dW = -(Xh Lam) S_c^T, dXh = R Lam^T, dM = -dQt W^T + dO U^T
-  mm<kBC, kD, kD, false, true>(&sm.DU[0][0], kPW, &sm.SC[0][0], kPW, w, l,
-                               [&](int r, int s, float v) { sm.DW[r][s] = -v; });
-  mm<kBC, kD, kD, false, true>(&sm.RR[0][0], kPW, &sm.LL[0][0], kPW, w, l,
-                               [&](int r, int s, float v) { sm.DXH[r][s] = v; });
-  mm<kBC, kBC, kD, false, true>(&sm.DQT[0][0], kPW, &cc.W[0][0], kPW, w, l,
-                                [&](int r, int s, float v) { sm.DM[r][s] = -v; });
-  mm<kBC, kBC, kD, false, true>(&sm.DO[0][0], kPW, &cc.U[0][0], kPW, w, l,
-                                [&](int r, int s, float v) { sm.DM[r][s] += v; });
+  {
+    // dW = -(Xh Lam) S_c^T - M^T dQt, dXh = R Lam^T, dM = -dQt W^T + dO U^T
+    Mm<kBC, kD, kD, false, true> fxs, fxh;
+    Mm<kBC, kD, kBC, true, false> fmq;
+    Mm<kBC, kBC, kD, false, true> fm1, fm2;
+    fxs.load(&sm.DW[0][0], kPW, &sm.SC[0][0], kPW, w, l);
+    fmq.load(&cc.MM[0][0], kPN, &sm.DQT[0][0], kPW, w, l);
+    fxh.load(&sm.RR[0][0], kPW, &sm.LL[0][0], kPW, w, l);
+    fm1.load(&sm.DQT[0][0], kPW, &cc.W[0][0], kPW, w, l);
+    fm2.load(&sm.DO[0][0], kPW, &cc.U[0][0], kPW, w, l);
+    __syncthreads();   // every wave has read Xh Lam from DW
+    fxs.run();
+    fmq.run(fxs);
+    fxh.run();
+    fm1.run();
+    fm2.run();
+#pragma unroll
+    for (int it = 0; it < fm2.IT; ++it) fm2.acc[it] -= fm1.acc[it];
+    fmq.store(w, l, [&](int r, int s, float v) { sm.DW[r][s] = -v; });
+    fxh.store(w, l, [&](int r, int s, float v) { sm.DXH[r][s] = v; });
+    fm2.store(w, l, [&](int r, int s, float v) { sm.DM[r][s] = v; });
+  }
   __syncthreads();
-  // dW -= M^T dQt, dU = Xh Lam + M^T dO
-  mm<kBC, kD, kBC, true, false>(&cc.MM[0][0], kPN, &sm.DQT[0][0], kPW, w, l,
-                                [&](int r, int s, float v) { sm.DW[r][s] -= v; });
-  mm<kBC, kD, kBC, true, false>(&cc.MM[0][0], kPN, &sm.DO[0][0], kPW, w, l,
-                                [&](int r, int s, float v) { sm.DU[r][s] += v; });
+  float (*DXH)[kPW] = sm.DXH;
   {
     // decay terms of M, Qt and Xh (eight lanes per row)
     const int i = tid >> 3, p = tid & 7;
@@ -756,25 +852,41 @@ __global__ void __launch_bounds__(kThreads) falcon1_bwd_chunk_kernel(BwdArgs a) 
   __syncthreads();
   // dQ = Diag(e^g) dQt + (dM o D) X;  dX = Diag(e^{G-g}) dXh + (dM o D)^T Q
   float* dq_out = a.dphi_q + bh * T * kD;
-  mm<kBC, kD, kBC, false, false>(&sm.DM[0][0], kPN, &cc.X[0][0], kPW, w, l, [&](int r, int s, float v) {
-    if (t0 + r < T) dq_out[int64_t(t0 + r) * kD + s] = __expf(cc.g[r]) * sm.DQT[r][s] + v;
-  });
-  mm<kBC, kD, kBC, true, false>(&sm.DM[0][0], kPN, &cc.Q[0][0], kPW, w, l,
-                                [&](int r, int s, float v) { sm.RR[r][s] = xs(r) * sm.DXH[r][s] + v; });
+  {
+    Mm<kBC, kD, kBC, false, false> fq;
+    Mm<kBC, kD, kBC, true, false> fx;
+    fq.load(&sm.DM[0][0], kPN, &cc.X[0][0], kPW, w, l);
+    fx.load(&sm.DM[0][0], kPN, &cc.Q[0][0], kPW, w, l);
+    fq.run();
+    fx.run();
+    fq.store(w, l, [&](int r, int s, float v) {
+      if (t0 + r < T) dq_out[int64_t(t0 + r) * kD + s] = __expf(cc.g[r]) * sm.DQT[r][s] + v;
+    });
+    fx.store(w, l, [&](int r, int s, float v) { sm.RR[r][s] = xs(r) * sm.DXH[r][s] + v; });
+  }
   __syncthreads();
   // dY = T^T dW (into DQT), dZ = T^T dU (into DO)
   float (*DY)[kPW] = sm.DQT;
   float (*DZ)[kPW] = sm.DO;
-  mm<kBC, kD, kBC, true, false>(&cc.TT[0][0], kPN, &sm.DW[0][0], kPW, w, l,
-                                [&](int r, int s, float v) { DY[r][s] = v; });
-  mm<kBC, kD, kBC, true, false>(&cc.TT[0][0], kPN, &sm.DU[0][0], kPW, w, l,
-                                [&](int r, int s, float v) { DZ[r][s] = v; });
+  {
+    Mm<kBC, kD, kBC, true, false> fy, fz;
+    fy.load(&cc.TT[0][0], kPN, &sm.DW[0][0], kPW, w, l);
+    fz.load(&cc.TT[0][0], kPN, &sm.DU[0][0], kPW, w, l);
+    fy.run();
+    fz.run();
+    fy.store(w, l, [&](int r, int s, float v) { DY[r][s] = v; });
+    fz.store(w, l, [&](int r, int s, float v) { DZ[r][s] = v; });
+  }
   __syncthreads();
   // dA = -dY W^T - dZ U^T (strictly lower part used)
-  mm<kBC, kBC, kD, false, true>(&DY[0][0], kPW, &cc.W[0][0], kPW, w, l,
-                                [&](int r, int s, float v) { sm.DM[r][s] = -v; });
-  mm<kBC, kBC, kD, false, true>(&DZ[0][0], kPW, &cc.U[0][0], kPW, w, l,
-                                [&](int r, int s, float v) { sm.DM[r][s] -= v; });
+  {
+    Mm<kBC, kBC, kD, false, true> fa, fb;
+    fa.load(&DY[0][0], kPW, &cc.W[0][0], kPW, w, l);
+    fb.load(&DZ[0][0], kPW, &cc.U[0][0], kPW, w, l);
+    fa.run();
+    fb.run(fa);
+    fb.store(w, l, [&](int r, int s, float v) { sm.DM[r][s] = -v; });
+  }
   // Y = Diag(eta e^{gp}) X, Z = Diag(eta) V
   float* dv_out = a.dv + bh * T * kD;
   {
@@ -835,10 +947,15 @@ __global__ void __launch_bounds__(kThreads) falcon1_bwd_chunk_kernel(BwdArgs a) 
     sm.DM[i][s] *= cc.eta[i];
   }
   __syncthreads();
-  mm<kBC, kD, kBC, false, false>(&sm.DM[0][0], kPN, &cc.X[0][0], kPW, w, l,
-                                 [&](int r, int s, float v) { sm.RR[r][s] += v; });
-  mm<kBC, kD, kBC, true, false>(&sm.DM[0][0], kPN, &cc.X[0][0], kPW, w, l,
-                                [&](int r, int s, float v) { sm.RR[r][s] += v; });
+  {
+    Mm<kBC, kD, kBC, false, false> f1;
+    Mm<kBC, kD, kBC, true, false> f2;
+    f1.load(&sm.DM[0][0], kPN, &cc.X[0][0], kPW, w, l);
+    f2.load(&sm.DM[0][0], kPN, &cc.X[0][0], kPW, w, l);
+    f1.run();
+    f2.run(f1);
+    f2.store(w, l, [&](int r, int s, float v) { sm.RR[r][s] += v; });
+  }
   // gates: g -> log decay -> (eta, lam); eta -> (beta, lam, ||x||^2)
   if (w == 0) {
     const int i = l;
