@@ -168,6 +168,27 @@ def backward_bytes(B, H, T, dk, dv, io_bytes=2):
     return th * ((2 * dk + 2 * dv) * io_bytes + 8) + th * ((2 * dk + dv) * 4 + 8) + 2 * state
 
 
+FP32_MFMA_PEAK_TFLOPS = 157.3   # MI355X dense fp32 MFMA, published
+
+
+def backward_flops(B, H, T, dk=64, dv=64, C=32):
+    """Matrix-core flops of the Falcon-1 backward as designed (32-token
+    chunks, every product in fp32 MFMA), per chunk:
+      maps:  Gram and M (2 C^2 d), W and U (C^2 (dk + dv)), P, H and G
+             (3 C dk dv, dk^2 C for P), Q~ (C^2 dk)
+      chains: P S and Lam^T P (2 dk^2 dv)
+      chunk: the recomputed Gram, M, W, U; X^ Lam, W S, dO S^T, (X^ Lam) S^T,
+             R Lam^T (5 C dk dv); M^T dO, M^T dQ~, dM (2), (dM o D) X and
+             (dM o D)^T Q, T^T dW, T^T dU, dA (2), dK X, dK^T X (12 C^2 d).
+    Multiply-adds count two flops; VALU work is not counted."""
+    nchunks = -(-T // C)
+    d = dk
+    maps = 2 * C * C * d + C * C * (dk + dv) + dk * dk * C + 2 * C * dk * dv + C * C * dk
+    chains = 2 * dk * dk * dv
+    chunk = 2 * C * C * d + C * C * (dk + dv) + 5 * C * dk * dv + 12 * C * C * d
+    return 2.0 * B * H * nchunks * (maps + chains + chunk)
+
+
 def bench_backward(name="f1_backward_8x12x2048_d64", steps=10, warmup=2):
     """The Falcon-1 backward (falcon_bwd_chunked) at the training shape, with a
     loss on both the outputs and the final state; inputs, cotangents, gradient
@@ -206,9 +227,16 @@ def bench_backward(name="f1_backward_8x12x2048_d64", steps=10, warmup=2):
     ms = e0.elapsed_time(e1) / steps
     nbytes = backward_bytes(w.B, w.H, w.T, w.dk, w.dv)
     gbs = nbytes / (ms * 1e-3) / 1e9
+    flops = backward_flops(w.B, w.H, w.T, w.dk, w.dv)
+    tflops = flops / (ms * 1e-3) / 1e12
     return {"workload": name, "steps": steps, "us_per_step": ms * 1e3,
             "tokens_per_s": w.B * w.T / (ms * 1e-3), "algorithmic_bytes": nbytes,
-            "workspace_bytes": int(ws.numel()), "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
+            "workspace_bytes": int(ws.numel()), "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+            "roofline": {"bound": "mfma", "achieved": tflops, "peak": FP32_MFMA_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": tflops / FP32_MFMA_PEAK_TFLOPS,
+                         "traffic": None, "algorithmic_flops": flops, "dtype": "f32",
+                         "kernels": ["falcon1_bwd_maps_kernel", "falcon1_bwd_chain_kernel",
+                                     "falcon1_bwd_chunk_kernel"]}}
 
 
 def calibrate_copy(nbytes=1 << 28, reps=5):
