@@ -58,10 +58,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // D (M x N) = op(A) op(B) on the matrix cores in float32; A is M x K (stored
 // K x M when TA), B is K x N (stored N x K when TB), both in LDS with float
 // pitches pa, pb (multiples of 4, 16-byte aligned rows).  The 16x16 output
-// tiles go round-robin to the four waves (tile w + 4 it; the same lane always
-// holds the same output element for a given M, N, so products of equal M, N
-// can be summed in registers).  With N / 16 dividing 4, all of a wave's tiles
-// share one column block, so the wave reads its B fragments once.  Within
+// tiles go round-robin to NW waves (tile w + NW it for wave w < NW; the same
+// lane always holds the same output element for given M, N, NW, so such
+// products can be summed in registers).  With N / 16 dividing NW, all of a
+// wave's tiles share one column block, so the wave reads its B fragments once.  Within
 // each 16-wide slice of K, lane group g supplies k = 16m + 4g + e at step e,
 // so an operand stored with K contiguous is read 16 bytes at a time.
 //
@@ -69,11 +69,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // hands each result to epi(row, col, value).  Several products of a phase
 // load first, run next and store last, so that their LDS reads overlap and
 // no product waits behind another's stores.
-template <int M, int N, int K, bool TA, bool TB>
+template <int M, int N, int K, bool TA, bool TB, int NW = 4>
 struct Mm {
-  static constexpr int TN = N / 16, TM = M / 16, IT = TM * TN / 4, KS = K / 4;
+  static constexpr int TN = N / 16, TM = M / 16, IT = TM * TN / NW, KS = K / 4;
   static_assert(K % 16 == 0, "K must be a multiple of 16");
-  static_assert(TM * TN % 4 == 0 && 4 % TN == 0, "tiles must split evenly over the four waves");
+  static_assert(TM * TN % NW == 0 && NW % TN == 0, "tiles must split evenly over the waves");
   float bv[KS];
   float av[IT][KS];
   f32x4 acc[IT];
@@ -95,7 +95,7 @@ struct Mm {
       }
 #pragma unroll
       for (int it = 0; it < IT; ++it) {
-        const int tm = (w + 4 * it) / TN;
+        const int tm = (w + NW * it) / TN;
         if (TA) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) av[it][4 * m + e] = A[(k0 + e) * pa + 16 * tm + c16];
@@ -107,7 +107,7 @@ struct Mm {
     }
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-      const float sc = rs(16 * ((w + 4 * it) / TN) + c16);
+      const float sc = rs(16 * ((w + NW * it) / TN) + c16);
 #pragma unroll
       for (int k = 0; k < KS; ++k) av[it][k] *= sc;
     }
@@ -127,7 +127,7 @@ struct Mm {
       }
 #pragma unroll
       for (int it = 0; it < IT; ++it) {
-        const int tm = (w + 4 * it) / TN;
+        const int tm = (w + NW * it) / TN;
         if (TA) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) av[it][4 * m + e] = A[(k0 + e) * pa + 16 * tm + c16];
@@ -145,7 +145,7 @@ struct Mm {
     mac();
   }
   template <int K2, bool TA2, bool TB2>
-  __device__ __forceinline__ void run(const Mm<M, N, K2, TA2, TB2>& init) {
+  __device__ __forceinline__ void run(const Mm<M, N, K2, TA2, TB2, NW>& init) {
 #pragma unroll
     for (int it = 0; it < IT; ++it) acc[it] = init.acc[it];
     mac();
@@ -162,7 +162,7 @@ struct Mm {
     const int tn = w % TN;
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-      const int tm = (w + 4 * it) / TN;
+      const int tm = (w + NW * it) / TN;
 #pragma unroll
       for (int r = 0; r < 4; ++r) epi(16 * tm + 4 * g + r, 16 * tn + c16, acc[it][r]);
     }
@@ -335,7 +335,9 @@ __device__ __forceinline__ void chunk_store(ChunkCore& cc, const ChunkRegs<IO>& 
 
 // Gates, the Gram, A, M, the inverse T and the factors W, U of one chunk whose
 // inputs are in LDS (after a barrier).  Ends with a barrier.
+template <int NT>
 __device__ void chunk_forward(ChunkCore& cc, const BwdArgs& a, int c, int tid, int w, int l) {
+  static_assert(NT == 256 || NT == 512, "four or eight waves");
   const int T = a.T;
   const int t0 = c * kBC;
   const bool fresh = (a.k_prev == nullptr);
@@ -372,17 +374,27 @@ __device__ void chunk_forward(ChunkCore& cc, const BwdArgs& a, int c, int tid, i
   }
   __syncthreads();
   {
-    // Gram, A and M
-    Mm<kBC, kBC, kD, false, true> fk, fm;
-    fk.load(&cc.X[0][0], kPW, &cc.X[0][0], kPW, w, l);
-    fm.load(&cc.Q[0][0], kPW, &cc.X[0][0], kPW, w, l);
-    fk.run();
-    fm.run();
-    fk.store(w, l, [&](int r, int s, float v) {
+    // Gram, A and M (with eight waves, the Gram on waves 0-3 and M on 4-7)
+    auto store_k = [&](int r, int s, float v) {
       cc.KX[r][s] = v;
       cc.AA[r][s] = s < r ? cc.eta[r] * __expf(cc.gp[r] - cc.g[s]) * v : 0.f;
-    });
-    fm.store(w, l, [&](int r, int s, float v) { cc.MM[r][s] = s <= r ? __expf(cc.g[r] - cc.g[s]) * v : 0.f; });
+    };
+    auto store_m = [&](int r, int s, float v) { cc.MM[r][s] = s <= r ? __expf(cc.g[r] - cc.g[s]) * v : 0.f; };
+    if (NT == 512) {
+      Mm<kBC, kBC, kD, false, true> f;
+      f.load(w < 4 ? &cc.X[0][0] : &cc.Q[0][0], kPW, &cc.X[0][0], kPW, w & 3, l);
+      f.run();
+      if (w < 4) f.store(w & 3, l, store_k);
+      else f.store(w & 3, l, store_m);
+    } else {
+      Mm<kBC, kBC, kD, false, true> fk, fm;
+      fk.load(&cc.X[0][0], kPW, &cc.X[0][0], kPW, w, l);
+      fm.load(&cc.Q[0][0], kPW, &cc.X[0][0], kPW, w, l);
+      fk.run();
+      fm.run();
+      fk.store(w, l, store_k);
+      fm.store(w, l, store_m);
+    }
   }
   __syncthreads();
   // T11, T22 by substitution: lane j solves (I + A_bb) t = e_jj, b = j / 16
@@ -405,7 +417,7 @@ __device__ void chunk_forward(ChunkCore& cc, const BwdArgs& a, int c, int tid, i
     cc.TT[e >> 3][17 + 2 * (e & 7)] = 0.f;
   }
   __syncthreads();
-  {
+  if (tid < 256) {
     // Z = A21 T11
     const int i = tid >> 4, j = tid & 15;
     float z = 0.f;
@@ -414,7 +426,7 @@ __device__ void chunk_forward(ChunkCore& cc, const BwdArgs& a, int c, int tid, i
     cc.ZZ[i][j] = z;
   }
   __syncthreads();
-  {
+  if (tid < 256) {
     // T21 = -T22 Z
     const int i = tid >> 4, j = tid & 15;
     float z = 0.f;
@@ -427,15 +439,16 @@ __device__ void chunk_forward(ChunkCore& cc, const BwdArgs& a, int c, int tid, i
 
 // W = T Diag(eta e^{gp}) X and U = T Diag(eta) V, with TZ = T Diag(eta) in
 // the caller's 32 x 36 scratch; AA becomes T Diag(eta e^{gp}).  Ends with a barrier.
+template <int NT>
 __device__ void chunk_factors(ChunkCore& cc, float (*TZ)[kPN], int tid, int w, int l) {
-  for (int e = tid; e < kBC * kBC; e += kThreads) {
+  for (int e = tid; e < kBC * kBC; e += NT) {
     const int i = e >> 5, s = e & 31;
     const float t = cc.TT[i][s];
     cc.AA[i][s] = t * cc.eta[s] * __expf(cc.gp[s]);
     TZ[i][s] = t * cc.eta[s];
   }
   __syncthreads();
-  Mm<kBC, kD, kBC, false, false> fw, fu;
+  Mm<kBC, kD, kBC, false, false, NT / 64> fw, fu;
   fw.load(&cc.AA[0][0], kPN, &cc.X[0][0], kPW, w, l);
   fu.load(&TZ[0][0], kPN, &cc.V[0][0], kPW, w, l);
   fw.run();
@@ -472,8 +485,8 @@ __global__ void __launch_bounds__(kThreads) falcon1_bwd_maps_kernel(BwdArgs a) {
     *reinterpret_cast<float4*>(&DO[i][f0 + 4]) = make_float4(od[4], od[5], od[6], od[7]);
   }
   __syncthreads();
-  chunk_forward(cc, a, c, tid, w, l);
-  chunk_factors(cc, TZ, tid, w, l);
+  chunk_forward<kThreads>(cc, a, c, tid, w, l);
+  chunk_factors<kThreads>(cc, TZ, tid, w, l);
   // V is dead: it holds Xh = Diag(e^{G-g}) X.  KX and AA (adjacent, dead)
   // hold Qt; X and Q (adjacent) hold P, then H, once Qt is formed.
   float (*XH)[kPW] = cc.V;
@@ -696,23 +709,38 @@ falcon1_bwd_chain_kernel(BwdArgs a, int nunits) {
 }
 
 // ---- launch 3: reverse mode through one chunk ----------------------------------
+// Eight waves: the chunk's LDS (156 KB) allows one workgroup per CU, and a
+// single wave per SIMD issues fp32 MFMAs at two thirds of the rate two waves
+// reach, so two waves share each SIMD.
+constexpr int kThreads3 = 512;
+constexpr int kWaves3 = kThreads3 / 64;
+
 struct __align__(16) GradSmem {
   ChunkCore cc;
   float SC[kD][kPW];     // S entering the chunk
   float LL[kD][kPW];     // dL/dS at the end of the chunk
   float DO[kBC][kPW];    // dO, then dZ
   float DQT[kBC][kPW];   // dQt, then dY
-  float DW[kBC][kPW];    // dW
-  float DU[kBC][kPW];    // Xh Lam, then dU
+  float DW[kBC][kPW];    // Xh Lam, then dW
+  float DU[kBC][kPW];    // dU
   float RR[kBC][kPW];    // U - W S, then the dX accumulator
   float DXH[kBC][kPW];   // dXh
   float DM[kBC][kPN];    // T Diag(eta); then dM, dM o D, dA, its decayed form, eta-scaled
   float dg[kBC], dgp[kBC], deta[kBC], dgt[kBC];
-  float trp[4];
+  float trp[kWaves3];
 };
 
+// Sum over the sixteen consecutive lanes that share a row.
+__device__ __forceinline__ float sum16(float v) {
+  v += __shfl_xor(v, 1);
+  v += __shfl_xor(v, 2);
+  v += __shfl_xor(v, 4);
+  v += __shfl_xor(v, 8);
+  return v;
+}
+
 template <typename IO>
-__global__ void __launch_bounds__(kThreads) falcon1_bwd_chunk_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(kThreads3) falcon1_bwd_chunk_kernel(BwdArgs a) {
   __shared__ GradSmem sm;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
@@ -721,24 +749,30 @@ __global__ void __launch_bounds__(kThreads) falcon1_bwd_chunk_kernel(BwdArgs a) 
   const int T = a.T;
   const int t0 = c * kBC;
   ChunkCore& cc = sm.cc;
+  // rows of 64 shared by 16 lanes: row ri, columns 4 rp + 0..3
+  const int ri = tid >> 4, rp = tid & 15;
   {
-    // every load of the chunk is issued before the first LDS store
+    // every load of the chunk is issued before the first LDS store: waves
+    // 0-3 take the chunk's keys, queries, values and gates, waves 4-7 dO,
+    // and all eight the state and the adjoint
     ChunkRegs<IO> r;
-    chunk_load<IO>(r, a, bh, c, tid);
     Raw8<IO> odr;
-    const int orow = t0 + (tid >> 3);
-    odr.load(static_cast<const IO*>(a.dO) + (bh * T + (orow < T ? orow : T - 1)) * kD + (tid & 7) * 8);
+    const int u = tid & 255;
+    const int orow = t0 + (u >> 3);
+    if (w < 4) chunk_load<IO>(r, a, bh, c, u);
+    else odr.load(static_cast<const IO*>(a.dO) + (bh * T + (orow < T ? orow : T - 1)) * kD + (u & 7) * 8);
     const float4* ck = reinterpret_cast<const float4*>(a.ckpt + (bh * a.nchunks + c) * kD * kD);
     const float4* ad = reinterpret_cast<const float4*>(a.adj + (bh * a.nchunks + c) * kD * kD);
-    float4 s4[4], l4[4];
+    float4 s4[2], l4[2];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      s4[k] = ck[tid + k * kThreads];
-      l4[k] = ad[tid + k * kThreads];
+    for (int k = 0; k < 2; ++k) {
+      s4[k] = ck[tid + k * kThreads3];
+      l4[k] = ad[tid + k * kThreads3];
     }
-    chunk_store<IO>(cc, r, tid);
-    {
-      const int i = tid >> 3, f0 = (tid & 7) * 8;
+    if (w < 4) {
+      chunk_store<IO>(cc, r, u);
+    } else {
+      const int i = u >> 3, f0 = (u & 7) * 8;
       float od[8];
       odr.get(od);
 #pragma unroll
@@ -746,10 +780,9 @@ __global__ void __launch_bounds__(kThreads) falcon1_bwd_chunk_kernel(BwdArgs a) 
       *reinterpret_cast<float4*>(&sm.DO[i][f0]) = make_float4(od[0], od[1], od[2], od[3]);
       *reinterpret_cast<float4*>(&sm.DO[i][f0 + 4]) = make_float4(od[4], od[5], od[6], od[7]);
     }
-    float trace = 0.f;   // this thread's part of tr(Lam S_c^T)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int q = tid + k * kThreads;
+    for (int k = 0; k < 2; ++k) {
+      const int q = tid + k * kThreads3;
       const int cg = q >> 8, ww = (q >> 6) & 3, lo = q & 15, hi = (q >> 4) & 3;
       sm.SC[16 * ww + 4 * hi + 0][16 * cg + lo] = s4[k].x;
       sm.SC[16 * ww + 4 * hi + 1][16 * cg + lo] = s4[k].y;
@@ -761,10 +794,11 @@ __global__ void __launch_bounds__(kThreads) falcon1_bwd_chunk_kernel(BwdArgs a) 
       sm.LL[16 * ww + lo][16 * cg + 4 * hi + 3] = l4[k].w;
     }
     __syncthreads();
-    // tr(Lam S^T) = sum of Lam o S, a 16-float slice per thread
+    // tr(Lam S^T) = sum of Lam o S, an 8-float slice per thread
+    float trace = 0.f;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int e = tid * 16 + 4 * k, rr = e >> 6, cl = e & 63;
+    for (int k = 0; k < 2; ++k) {
+      const int e = tid * 8 + 4 * k, rr = e >> 6, cl = e & 63;
       const float4 x = *reinterpret_cast<const float4*>(&sm.LL[rr][cl]);
       const float4 y = *reinterpret_cast<const float4*>(&sm.SC[rr][cl]);
       trace = fmaf(x.x, y.x, fmaf(x.y, y.y, fmaf(x.z, y.z, fmaf(x.w, y.w, trace))));
@@ -773,15 +807,15 @@ __global__ void __launch_bounds__(kThreads) falcon1_bwd_chunk_kernel(BwdArgs a) 
     for (int off = 32; off >= 1; off >>= 1) trace += __shfl_xor(trace, off);
     if (l == 0) sm.trp[w] = trace;
   }
-  chunk_forward(cc, a, c, tid, w, l);
-  chunk_factors(cc, sm.DM, tid, w, l);
+  chunk_forward<kThreads3>(cc, a, c, tid, w, l);
+  chunk_factors<kThreads3>(cc, sm.DM, tid, w, l);
   const float eG = __expf(cc.G);
   auto xs = [&](int i) { return __expf(cc.G - cc.g[i]); };
   {
     // Xh Lam (into DW), dU = Xh Lam + M^T dO, R = U - W S_c, dQt = dO S_c^T
-    Mm<kBC, kD, kD, false, false> fxl, fws;
-    Mm<kBC, kD, kD, false, true> fdq;
-    Mm<kBC, kD, kBC, true, false> fmo;
+    Mm<kBC, kD, kD, false, false, kWaves3> fxl, fws;
+    Mm<kBC, kD, kD, false, true, kWaves3> fdq;
+    Mm<kBC, kD, kBC, true, false, kWaves3> fmo;
     fxl.load(&cc.X[0][0], kPW, &sm.LL[0][0], kPW, w, l, xs);
     fws.load(&cc.W[0][0], kPW, &sm.SC[0][0], kPW, w, l);
     fdq.load(&sm.DO[0][0], kPW, &sm.SC[0][0], kPW, w, l);
@@ -797,47 +831,47 @@ __global__ void __launch_bounds__(kThreads) falcon1_bwd_chunk_kernel(BwdArgs a) 
   }
   __syncthreads();
   {
-    // dW = -(Xh Lam) S_c^T - M^T dQt, dXh = R Lam^T, dM = -dQt W^T + dO U^T
-    Mm<kBC, kD, kD, false, true> fxs, fxh;
-    Mm<kBC, kD, kBC, true, false> fmq;
-    Mm<kBC, kBC, kD, false, true> fm1, fm2;
+    // dW = -(Xh Lam) S_c^T - M^T dQt, dXh = R Lam^T, dM = dO U^T - dQt W^T
+    // (-dQt W^T on waves 0-3, dO U^T on waves 4-7)
+    Mm<kBC, kD, kD, false, true, kWaves3> fxs, fxh;
+    Mm<kBC, kD, kBC, true, false, kWaves3> fmq;
+    Mm<kBC, kBC, kD, false, true> fmx;
     fxs.load(&sm.DW[0][0], kPW, &sm.SC[0][0], kPW, w, l);
     fmq.load(&cc.MM[0][0], kPN, &sm.DQT[0][0], kPW, w, l);
     fxh.load(&sm.RR[0][0], kPW, &sm.LL[0][0], kPW, w, l);
-    fm1.load(&sm.DQT[0][0], kPW, &cc.W[0][0], kPW, w, l);
-    fm2.load(&sm.DO[0][0], kPW, &cc.U[0][0], kPW, w, l);
+    fmx.load(w < 4 ? &sm.DQT[0][0] : &sm.DO[0][0], kPW, w < 4 ? &cc.W[0][0] : &cc.U[0][0], kPW, w & 3, l);
     __syncthreads();   // every wave has read Xh Lam from DW
     fxs.run();
     fmq.run(fxs);
     fxh.run();
-    fm1.run();
-    fm2.run();
-#pragma unroll
-    for (int it = 0; it < fm2.IT; ++it) fm2.acc[it] -= fm1.acc[it];
+    fmx.run();
     fmq.store(w, l, [&](int r, int s, float v) { sm.DW[r][s] = -v; });
     fxh.store(w, l, [&](int r, int s, float v) { sm.DXH[r][s] = v; });
-    fm2.store(w, l, [&](int r, int s, float v) { sm.DM[r][s] = v; });
+    if (w < 4) fmx.store(w & 3, l, [&](int r, int s, float v) { sm.DM[r][s] = -v; });
+    __syncthreads();
+    if (w >= 4) fmx.store(w & 3, l, [&](int r, int s, float v) { sm.DM[r][s] += v; });
   }
   __syncthreads();
-  float (*DXH)[kPW] = sm.DXH;
   {
-    // decay terms of M, Qt and Xh (eight lanes per row)
-    const int i = tid >> 3, p = tid & 7;
+    // decay terms of M, Qt and Xh (sixteen lanes per row)
+    const int i = ri;
     float qd = 0.f, xd = 0.f, rowm = 0.f, colm = 0.f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int f = 8 * p + k;
-      qd = fmaf(cc.Q[i][f], sm.DQT[i][f], qd);
-      xd = fmaf(cc.X[i][f], sm.DXH[i][f], xd);
+    {
+      const float4 q4 = *reinterpret_cast<const float4*>(&cc.Q[i][4 * rp]);
+      const float4 t4 = *reinterpret_cast<const float4*>(&sm.DQT[i][4 * rp]);
+      const float4 x4 = *reinterpret_cast<const float4*>(&cc.X[i][4 * rp]);
+      const float4 h4 = *reinterpret_cast<const float4*>(&sm.DXH[i][4 * rp]);
+      qd = q4.x * t4.x + q4.y * t4.y + q4.z * t4.z + q4.w * t4.w;
+      xd = x4.x * h4.x + x4.y * h4.y + x4.z * h4.z + x4.w * h4.w;
     }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int s = 4 * p + k;
-      rowm = fmaf(sm.DM[i][s], cc.MM[i][s], rowm);
-      colm = fmaf(sm.DM[s][i], cc.MM[s][i], colm);
+    for (int k = 0; k < 2; ++k) {
+      const int s2 = 2 * rp + k;
+      rowm = fmaf(sm.DM[i][s2], cc.MM[i][s2], rowm);
+      colm = fmaf(sm.DM[s2][i], cc.MM[s2][i], colm);
     }
-    qd = sum8(qd); xd = sum8(xd); rowm = sum8(rowm); colm = sum8(colm);
-    if (p == 0) {
+    qd = sum16(qd); xd = sum16(xd); rowm = sum16(rowm); colm = sum16(colm);
+    if (rp == 0) {
       const float z = xs(i) * xd;
       sm.dg[i] = __expf(cc.g[i]) * qd + rowm - colm - z;
       sm.dgt[i] = z;
@@ -845,64 +879,58 @@ __global__ void __launch_bounds__(kThreads) falcon1_bwd_chunk_kernel(BwdArgs a) 
   }
   __syncthreads();
   // dM o D, D_{is} = e^{g_i-g_s} for s <= i
-  for (int e = tid; e < kBC * kBC; e += kThreads) {
-    const int i = e >> 5, s = e & 31;
-    sm.DM[i][s] = s <= i ? sm.DM[i][s] * __expf(cc.g[i] - cc.g[s]) : 0.f;
+  for (int e = tid; e < kBC * kBC; e += kThreads3) {
+    const int i = e >> 5, s2 = e & 31;
+    sm.DM[i][s2] = s2 <= i ? sm.DM[i][s2] * __expf(cc.g[i] - cc.g[s2]) : 0.f;
   }
   __syncthreads();
   // dQ = Diag(e^g) dQt + (dM o D) X;  dX = Diag(e^{G-g}) dXh + (dM o D)^T Q
   float* dq_out = a.dphi_q + bh * T * kD;
   {
-    Mm<kBC, kD, kBC, false, false> fq;
-    Mm<kBC, kD, kBC, true, false> fx;
+    Mm<kBC, kD, kBC, false, false, kWaves3> fq;
+    Mm<kBC, kD, kBC, true, false, kWaves3> fx;
     fq.load(&sm.DM[0][0], kPN, &cc.X[0][0], kPW, w, l);
     fx.load(&sm.DM[0][0], kPN, &cc.Q[0][0], kPW, w, l);
     fq.run();
     fx.run();
-    fq.store(w, l, [&](int r, int s, float v) {
-      if (t0 + r < T) dq_out[int64_t(t0 + r) * kD + s] = __expf(cc.g[r]) * sm.DQT[r][s] + v;
+    fq.store(w, l, [&](int r, int s2, float v) {
+      if (t0 + r < T) dq_out[int64_t(t0 + r) * kD + s2] = __expf(cc.g[r]) * sm.DQT[r][s2] + v;
     });
-    fx.store(w, l, [&](int r, int s, float v) { sm.RR[r][s] = xs(r) * sm.DXH[r][s] + v; });
+    fx.store(w, l, [&](int r, int s2, float v) { sm.RR[r][s2] = xs(r) * sm.DXH[r][s2] + v; });
   }
   __syncthreads();
   // dY = T^T dW (into DQT), dZ = T^T dU (into DO)
   float (*DY)[kPW] = sm.DQT;
   float (*DZ)[kPW] = sm.DO;
   {
-    Mm<kBC, kD, kBC, true, false> fy, fz;
+    Mm<kBC, kD, kBC, true, false, kWaves3> fy, fz;
     fy.load(&cc.TT[0][0], kPN, &sm.DW[0][0], kPW, w, l);
     fz.load(&cc.TT[0][0], kPN, &sm.DU[0][0], kPW, w, l);
     fy.run();
     fz.run();
-    fy.store(w, l, [&](int r, int s, float v) { DY[r][s] = v; });
-    fz.store(w, l, [&](int r, int s, float v) { DZ[r][s] = v; });
+    fy.store(w, l, [&](int r, int s2, float v) { DY[r][s2] = v; });
+    fz.store(w, l, [&](int r, int s2, float v) { DZ[r][s2] = v; });
   }
   __syncthreads();
-  // dA = -dY W^T - dZ U^T (strictly lower part used)
-  {
-    Mm<kBC, kBC, kD, false, true> fa, fb;
-    fa.load(&DY[0][0], kPW, &cc.W[0][0], kPW, w, l);
-    fb.load(&DZ[0][0], kPW, &cc.U[0][0], kPW, w, l);
-    fa.run();
-    fb.run(fa);
-    fb.store(w, l, [&](int r, int s, float v) { sm.DM[r][s] = -v; });
-  }
-  // Y = Diag(eta e^{gp}) X, Z = Diag(eta) V
   float* dv_out = a.dv + bh * T * kD;
   {
-    const int i = tid >> 3, p = tid & 7;
-    const float egp = __expf(cc.gp[i]), eta = cc.eta[i];
-    float xy = 0.f, vz = 0.f;
-#pragma unroll
-    for (int k = 0; k < 8; k += 4) {
-      const int f = 8 * p + k;
+    // dA = -dY W^T - dZ U^T (strictly lower part used; dY W^T on waves 0-3,
+    // dZ U^T on waves 4-7)
+    Mm<kBC, kBC, kD, false, true> fa;
+    fa.load(w < 4 ? &DY[0][0] : &DZ[0][0], kPW, w < 4 ? &cc.W[0][0] : &cc.U[0][0], kPW, w & 3, l);
+    fa.run();
+    // Y = Diag(eta e^{gp}) X, Z = Diag(eta) V: dX += Diag(eta e^{gp}) dY,
+    // dV = Diag(eta) dZ, and the eta / gp terms
+    {
+      const int i = ri, f = 4 * rp;
+      const float egp = __expf(cc.gp[i]), eta = cc.eta[i];
       const float4 dy = *reinterpret_cast<const float4*>(&DY[i][f]);
       const float4 dz = *reinterpret_cast<const float4*>(&DZ[i][f]);
       const float4 x = *reinterpret_cast<const float4*>(&cc.X[i][f]);
       const float4 v = *reinterpret_cast<const float4*>(&cc.V[i][f]);
       float4 dx = *reinterpret_cast<const float4*>(&sm.RR[i][f]);
-      xy = fmaf(x.x, dy.x, fmaf(x.y, dy.y, fmaf(x.z, dy.z, fmaf(x.w, dy.w, xy))));
-      vz = fmaf(v.x, dz.x, fmaf(v.y, dz.y, fmaf(v.z, dz.z, fmaf(v.w, dz.w, vz))));
+      float xy = x.x * dy.x + x.y * dy.y + x.z * dy.z + x.w * dy.w;
+      float vz = v.x * dz.x + v.y * dz.y + v.z * dz.z + v.w * dz.w;
       const float sy = eta * egp;
       dx.x = fmaf(sy, dy.x, dx.x); dx.y = fmaf(sy, dy.y, dx.y);
       dx.z = fmaf(sy, dy.z, dx.z); dx.w = fmaf(sy, dy.w, dx.w);
@@ -910,31 +938,34 @@ __global__ void __launch_bounds__(kThreads) falcon1_bwd_chunk_kernel(BwdArgs a) 
       if (t0 + i < T)
         *reinterpret_cast<float4*>(dv_out + int64_t(t0 + i) * kD + f) =
             make_float4(eta * dz.x, eta * dz.y, eta * dz.z, eta * dz.w);
+      xy = sum16(xy); vz = sum16(vz);
+      if (rp == 0) {
+        sm.deta[i] = egp * xy + vz;
+        sm.dgp[i] = eta * egp * xy;
+      }
     }
-    xy = sum8(xy); vz = sum8(vz);
-    if (p == 0) {
-      sm.deta[i] = egp * xy + vz;
-      sm.dgp[i] = eta * egp * xy;
-    }
+    if (w < 4) fa.store(w & 3, l, [&](int r, int s2, float v) { sm.DM[r][s2] = -v; });
+    __syncthreads();
+    if (w >= 4) fa.store(w & 3, l, [&](int r, int s2, float v) { sm.DM[r][s2] -= v; });
   }
   __syncthreads();
   // A_{is} = eta_i e^{gp_i-g_s} k_{is}: D2 = dA o e^{gp_i-g_s} (s < i)
-  for (int e = tid; e < kBC * kBC; e += kThreads) {
-    const int i = e >> 5, s = e & 31;
-    sm.DM[i][s] = s < i ? sm.DM[i][s] * __expf(cc.gp[i] - cc.g[s]) : 0.f;
+  for (int e = tid; e < kBC * kBC; e += kThreads3) {
+    const int i = e >> 5, s2 = e & 31;
+    sm.DM[i][s2] = s2 < i ? sm.DM[i][s2] * __expf(cc.gp[i] - cc.g[s2]) : 0.f;
   }
   __syncthreads();
   {
-    const int i = tid >> 3, p = tid & 7;
+    const int i = ri;
     float row = 0.f, col = 0.f;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int s = 4 * p + k;
-      row = fmaf(sm.DM[i][s], cc.KX[i][s], row);
-      col = fmaf(cc.eta[s] * sm.DM[s][i], cc.KX[s][i], col);
+    for (int k = 0; k < 2; ++k) {
+      const int s2 = 2 * rp + k;
+      row = fmaf(sm.DM[i][s2], cc.KX[i][s2], row);
+      col = fmaf(cc.eta[s2] * sm.DM[s2][i], cc.KX[s2][i], col);
     }
-    row = sum8(row); col = sum8(col);
-    if (p == 0) {
+    row = sum16(row); col = sum16(col);
+    if (rp == 0) {
       sm.deta[i] += row;
       sm.dgp[i] += cc.eta[i] * row;
       sm.dg[i] -= col;
@@ -942,19 +973,19 @@ __global__ void __launch_bounds__(kThreads) falcon1_bwd_chunk_kernel(BwdArgs a) 
   }
   __syncthreads();
   // dK = Diag(eta) D2 (strictly lower), dX += (dK + dK^T) X
-  for (int e = tid; e < kBC * kBC; e += kThreads) {
-    const int i = e >> 5, s = e & 31;
-    sm.DM[i][s] *= cc.eta[i];
+  for (int e = tid; e < kBC * kBC; e += kThreads3) {
+    const int i = e >> 5, s2 = e & 31;
+    sm.DM[i][s2] *= cc.eta[i];
   }
   __syncthreads();
   {
-    Mm<kBC, kD, kBC, false, false> f1;
-    Mm<kBC, kD, kBC, true, false> f2;
+    Mm<kBC, kD, kBC, false, false, kWaves3> f1;
+    Mm<kBC, kD, kBC, true, false, kWaves3> f2;
     f1.load(&sm.DM[0][0], kPN, &cc.X[0][0], kPW, w, l);
     f2.load(&sm.DM[0][0], kPN, &cc.X[0][0], kPW, w, l);
     f1.run();
     f2.run(f1);
-    f2.store(w, l, [&](int r, int s, float v) { sm.RR[r][s] += v; });
+    f2.store(w, l, [&](int r, int s2, float v) { sm.RR[r][s2] += v; });
   }
   // gates: g -> log decay -> (eta, lam); eta -> (beta, lam, ||x||^2)
   if (w == 0) {
@@ -963,9 +994,10 @@ __global__ void __launch_bounds__(kThreads) falcon1_bwd_chunk_kernel(BwdArgs a) 
     if (i < kBC) {
       float dG = 0.f;
       if (i == kBC - 1) {
-        float zs = 0.f;
+        float zs = 0.f, tr = 0.f;
         for (int r = 0; r < kBC; ++r) zs += sm.dgt[r];
-        dG = eG * (sm.trp[0] + sm.trp[1] + sm.trp[2] + sm.trp[3]) + zs;
+        for (int r = 0; r < kWaves3; ++r) tr += sm.trp[r];
+        dG = eG * tr + zs;
       }
       dgt = sm.dg[i] + (i + 1 < kBC ? sm.dgp[i + 1] : 0.f) + dG;
     }
@@ -1006,22 +1038,19 @@ __global__ void __launch_bounds__(kThreads) falcon1_bwd_chunk_kernel(BwdArgs a) 
   float* dk_out = a.dphi_k + bh * T * kD;
   const bool fresh = (a.k_prev == nullptr);
   {
-    const int i = tid >> 3, f0 = (tid & 7) * 8, t = t0 + i;
+    const int i = ri, f0 = 4 * rp, t = t0 + i;
     const float dE2 = 2.0f * sm.dgp[i];
-    float o[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) o[k] = fmaf(dE2, cc.X[i][f0 + k], sm.RR[i][f0 + k]);
+    const float4 x = *reinterpret_cast<const float4*>(&cc.X[i][f0]);
+    const float4 d = *reinterpret_cast<const float4*>(&sm.RR[i][f0]);
+    const float4 o = make_float4(fmaf(dE2, x.x, d.x), fmaf(dE2, x.y, d.y), fmaf(dE2, x.z, d.z), fmaf(dE2, x.w, d.w));
     float* dst = nullptr;
     if (t >= 1 && t < T) dst = dk_out + int64_t(t - 1) * kD + f0;
     else if (t == 0 && !fresh && a.dk_prev) dst = a.dk_prev + bh * kD + f0;
-    if (dst) {
-      reinterpret_cast<float4*>(dst)[0] = make_float4(o[0], o[1], o[2], o[3]);
-      reinterpret_cast<float4*>(dst)[1] = make_float4(o[4], o[5], o[6], o[7]);
-    }
+    if (dst) *reinterpret_cast<float4*>(dst) = o;
   }
   // the last key feeds no token of this call
   if (c == a.nchunks - 1)
-    for (int f = tid; f < kD; f += kThreads) dk_out[int64_t(T - 1) * kD + f] = 0.f;
+    for (int f = tid; f < kD; f += kThreads3) dk_out[int64_t(T - 1) * kD + f] = 0.f;
 }
 
 }  // namespace
@@ -1051,11 +1080,11 @@ hipError_t launch_bwd(const ProblemArgs& p, const BwdBuffers& b, hipStream_t st)
   if (p.bf16) {
     hipLaunchKernelGGL(falcon1_bwd_maps_kernel<bf16_t>, dim3(unsigned(n)), dim3(kThreads), 0, st, a);
     hipLaunchKernelGGL(falcon1_bwd_chain_kernel<bf16_t>, dim3(chain_blocks), dim3(kThreads), 0, st, a, nunits);
-    hipLaunchKernelGGL(falcon1_bwd_chunk_kernel<bf16_t>, dim3(unsigned(n)), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(falcon1_bwd_chunk_kernel<bf16_t>, dim3(unsigned(n)), dim3(kThreads3), 0, st, a);
   } else {
     hipLaunchKernelGGL(falcon1_bwd_maps_kernel<float>, dim3(unsigned(n)), dim3(kThreads), 0, st, a);
     hipLaunchKernelGGL(falcon1_bwd_chain_kernel<float>, dim3(chain_blocks), dim3(kThreads), 0, st, a, nunits);
-    hipLaunchKernelGGL(falcon1_bwd_chunk_kernel<float>, dim3(unsigned(n)), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(falcon1_bwd_chunk_kernel<float>, dim3(unsigned(n)), dim3(kThreads3), 0, st, a);
   }
   return hipGetLastError();
 }
