@@ -106,6 +106,7 @@ falcon_status check_backward(const falcon_problem* p, const void* phi_k, const v
   if (p->variant != FALCON_1) return FALCON_ERR_VARIANT;
   if (p->dk != 64 || p->dv != 64) return FALCON_ERR_SHAPE;
   const int64_t bh = int64_t(p->B) * p->H;
+  if (bh * ((int64_t(p->T) + 31) / 32) > (int64_t(1) << 30)) return FALCON_ERR_SHAPE;   // chunk count
   const int64_t es = p->io_dtype == FALCON_BF16 ? 2 : 4;
   const bool work = bh > 0 && p->T > 0;
   if (work && (!phi_k || !phi_q || !v || !beta || !lam || !dO || !dphi_k || !dphi_q || !dv ||

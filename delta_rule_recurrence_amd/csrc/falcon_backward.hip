@@ -78,9 +78,10 @@ struct Mm {
   float av[IT][KS];
   f32x4 acc[IT];
 
-  // rs(row) scales row `row` of A (rows of op(A)).
-  template <typename RowScale>
-  __device__ __forceinline__ void load(const float* A, int pa, const float* B, int pb, int w, int l, RowScale rs) {
+  // ra(row) scales row `row` of op(A); kb(k) scales row k of op(B).
+  template <typename RowScale, typename KScale>
+  __device__ __forceinline__ void load(const float* A, int pa, const float* B, int pb, int w, int l, RowScale ra,
+                                       KScale kb) {
     const int g = l >> 4, c16 = l & 15;
     const int tn = w % TN;
 #pragma unroll
@@ -93,6 +94,8 @@ struct Mm {
 #pragma unroll
         for (int e = 0; e < 4; ++e) bv[4 * m + e] = B[(k0 + e) * pb + 16 * tn + c16];
       }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bv[4 * m + e] *= kb(k0 + e);
 #pragma unroll
       for (int it = 0; it < IT; ++it) {
         const int tm = (w + NW * it) / TN;
@@ -107,36 +110,17 @@ struct Mm {
     }
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-      const float sc = rs(16 * ((w + NW * it) / TN) + c16);
+      const float sc = ra(16 * ((w + NW * it) / TN) + c16);
 #pragma unroll
       for (int k = 0; k < KS; ++k) av[it][k] *= sc;
     }
   }
+  template <typename RowScale>
+  __device__ __forceinline__ void load(const float* A, int pa, const float* B, int pb, int w, int l, RowScale ra) {
+    load(A, pa, B, pb, w, l, ra, [](int) { return 1.f; });
+  }
   __device__ __forceinline__ void load(const float* A, int pa, const float* B, int pb, int w, int l) {
-    const int g = l >> 4, c16 = l & 15;
-    const int tn = w % TN;
-#pragma unroll
-    for (int m = 0; m < K / 16; ++m) {
-      const int k0 = 16 * m + 4 * g;
-      if (TB) {
-        const float4 v = *reinterpret_cast<const float4*>(B + (16 * tn + c16) * pb + k0);
-        bv[4 * m] = v.x; bv[4 * m + 1] = v.y; bv[4 * m + 2] = v.z; bv[4 * m + 3] = v.w;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) bv[4 * m + e] = B[(k0 + e) * pb + 16 * tn + c16];
-      }
-#pragma unroll
-      for (int it = 0; it < IT; ++it) {
-        const int tm = (w + NW * it) / TN;
-        if (TA) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) av[it][4 * m + e] = A[(k0 + e) * pa + 16 * tm + c16];
-        } else {
-          const float4 v = *reinterpret_cast<const float4*>(A + (16 * tm + c16) * pa + k0);
-          av[it][4 * m] = v.x; av[it][4 * m + 1] = v.y; av[it][4 * m + 2] = v.z; av[it][4 * m + 3] = v.w;
-        }
-      }
-    }
+    load(A, pa, B, pb, w, l, [](int) { return 1.f; }, [](int) { return 1.f; });
   }
   // acc = op(A) op(B), or init + op(A) op(B)
   __device__ __forceinline__ void run() {
@@ -336,7 +320,8 @@ __device__ __forceinline__ void chunk_store(ChunkCore& cc, const ChunkRegs<IO>& 
 // Gates, the Gram, A, M, the inverse T and the factors W, U of one chunk whose
 // inputs are in LDS (after a barrier).  Ends with a barrier.
 template <int NT>
-__device__ void chunk_forward(ChunkCore& cc, const BwdArgs& a, int c, int tid, int w, int l) {
+__device__ void chunk_forward(ChunkCore& cc, const BwdArgs& a, int c, int tid, int w, int l,
+                              float (*qx)[kPN] = nullptr) {
   static_assert(NT == 256 || NT == 512, "four or eight waves");
   const int T = a.T;
   const int t0 = c * kBC;
@@ -379,7 +364,10 @@ __device__ void chunk_forward(ChunkCore& cc, const BwdArgs& a, int c, int tid, i
       cc.KX[r][s] = v;
       cc.AA[r][s] = s < r ? cc.eta[r] * __expf(cc.gp[r] - cc.g[s]) * v : 0.f;
     };
-    auto store_m = [&](int r, int s, float v) { cc.MM[r][s] = s <= r ? __expf(cc.g[r] - cc.g[s]) * v : 0.f; };
+    auto store_m = [&](int r, int s, float v) {
+      cc.MM[r][s] = s <= r ? __expf(cc.g[r] - cc.g[s]) * v : 0.f;
+      if (qx) qx[r][s] = v;
+    };
     if (NT == 512) {
       Mm<kBC, kBC, kD, false, true> f;
       f.load(w < 4 ? &cc.X[0][0] : &cc.Q[0][0], kPW, &cc.X[0][0], kPW, w & 3, l);
@@ -725,7 +713,8 @@ struct __align__(16) GradSmem {
   float DU[kBC][kPW];    // dU
   float RR[kBC][kPW];    // U - W S, then the dX accumulator
   float DXH[kBC][kPW];   // dXh
-  float DM[kBC][kPN];    // T Diag(eta); then dM, dM o D, dA, its decayed form, eta-scaled
+  float DM[kBC][kPN];    // T Diag(eta); then dM o D; then D2 = dA o e^{gp_i - g_s}
+  float QX[kBC][kPN];    // q_i . x_s
   float dg[kBC], dgp[kBC], deta[kBC], dgt[kBC];
   float trp[kWaves3];
 };
@@ -739,61 +728,91 @@ __device__ __forceinline__ float sum16(float v) {
   return v;
 }
 
+// This thread's share of one chunk's inputs, held as loaded.  Waves 0-3 take
+// the keys, queries, values and gates, waves 4-7 dO, all eight the state and
+// the adjoint.
 template <typename IO>
-__global__ void __launch_bounds__(kThreads3) falcon1_bwd_chunk_kernel(BwdArgs a) {
+struct GradRegs {
+  ChunkRegs<IO> r;
+  Raw8<IO> odr;
+  float4 s4[2], l4[2];
+  bool olive;
+};
+
+template <typename IO>
+__device__ __forceinline__ void grad_load(GradRegs<IO>& g, const BwdArgs& a, int64_t bh, int c, int tid, int w) {
+  const int T = a.T;
+  const int u = tid & 255;
+  const int orow = c * kBC + (u >> 3);
+  g.olive = orow < T;
+  if (w < 4) chunk_load<IO>(g.r, a, bh, c, u);
+  else g.odr.load(static_cast<const IO*>(a.dO) + (bh * T + (orow < T ? orow : T - 1)) * kD + (u & 7) * 8);
+  const float4* ck = reinterpret_cast<const float4*>(a.ckpt + (bh * a.nchunks + c) * kD * kD);
+  const float4* ad = reinterpret_cast<const float4*>(a.adj + (bh * a.nchunks + c) * kD * kD);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    g.s4[k] = ck[tid + k * kThreads3];
+    g.l4[k] = ad[tid + k * kThreads3];
+  }
+}
+
+template <typename IO>
+__device__ __forceinline__ void grad_store(GradSmem& sm, const GradRegs<IO>& g, int tid, int w) {
+  const int u = tid & 255;
+  if (w < 4) {
+    chunk_store<IO>(sm.cc, g.r, u);
+  } else {
+    const int i = u >> 3, f0 = (u & 7) * 8;
+    float od[8];
+    g.odr.get(od);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) od[k] = g.olive ? od[k] : 0.f;
+    *reinterpret_cast<float4*>(&sm.DO[i][f0]) = make_float4(od[0], od[1], od[2], od[3]);
+    *reinterpret_cast<float4*>(&sm.DO[i][f0 + 4]) = make_float4(od[4], od[5], od[6], od[7]);
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int q = tid + k * kThreads3;
+    const int cg = q >> 8, ww = (q >> 6) & 3, lo = q & 15, hi = (q >> 4) & 3;
+    sm.SC[16 * ww + 4 * hi + 0][16 * cg + lo] = g.s4[k].x;
+    sm.SC[16 * ww + 4 * hi + 1][16 * cg + lo] = g.s4[k].y;
+    sm.SC[16 * ww + 4 * hi + 2][16 * cg + lo] = g.s4[k].z;
+    sm.SC[16 * ww + 4 * hi + 3][16 * cg + lo] = g.s4[k].w;
+    sm.LL[16 * ww + lo][16 * cg + 4 * hi + 0] = g.l4[k].x;
+    sm.LL[16 * ww + lo][16 * cg + 4 * hi + 1] = g.l4[k].y;
+    sm.LL[16 * ww + lo][16 * cg + 4 * hi + 2] = g.l4[k].z;
+    sm.LL[16 * ww + lo][16 * cg + 4 * hi + 3] = g.l4[k].w;
+  }
+}
+
+// Persistent: workgroup b handles chunks b, b + gridDim.x, ... (sequence-
+// major order) and loads the next chunk's inputs while it works on the
+// current one, so the loads' latency is hidden behind a whole chunk.
+template <typename IO>
+__global__ void __launch_bounds__(kThreads3) falcon1_bwd_chunk_kernel(BwdArgs a, int total) {
   __shared__ GradSmem sm;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
-  const int64_t bh = blockIdx.x / a.nchunks;
-  const int c = blockIdx.x % a.nchunks;
   const int T = a.T;
-  const int t0 = c * kBC;
   ChunkCore& cc = sm.cc;
   // rows of 64 shared by 16 lanes: row ri, columns 4 rp + 0..3
   const int ri = tid >> 4, rp = tid & 15;
+  const int first = blockIdx.x;
+  if (first >= total) return;   // whole workgroup
+  GradRegs<IO> in;
+  grad_load<IO>(in, a, first / a.nchunks, first % a.nchunks, tid, w);
+  for (int job = first; job < total; job += gridDim.x) {
+  const int64_t bh = job / a.nchunks;
+  const int c = job % a.nchunks;
+  const int t0 = c * kBC;
+  grad_store<IO>(sm, in, tid, w);
+  __syncthreads();
   {
-    // every load of the chunk is issued before the first LDS store: waves
-    // 0-3 take the chunk's keys, queries, values and gates, waves 4-7 dO,
-    // and all eight the state and the adjoint
-    ChunkRegs<IO> r;
-    Raw8<IO> odr;
-    const int u = tid & 255;
-    const int orow = t0 + (u >> 3);
-    if (w < 4) chunk_load<IO>(r, a, bh, c, u);
-    else odr.load(static_cast<const IO*>(a.dO) + (bh * T + (orow < T ? orow : T - 1)) * kD + (u & 7) * 8);
-    const float4* ck = reinterpret_cast<const float4*>(a.ckpt + (bh * a.nchunks + c) * kD * kD);
-    const float4* ad = reinterpret_cast<const float4*>(a.adj + (bh * a.nchunks + c) * kD * kD);
-    float4 s4[2], l4[2];
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      s4[k] = ck[tid + k * kThreads3];
-      l4[k] = ad[tid + k * kThreads3];
-    }
-    if (w < 4) {
-      chunk_store<IO>(cc, r, u);
-    } else {
-      const int i = u >> 3, f0 = (u & 7) * 8;
-      float od[8];
-      odr.get(od);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) od[k] = orow < T ? od[k] : 0.f;
-      *reinterpret_cast<float4*>(&sm.DO[i][f0]) = make_float4(od[0], od[1], od[2], od[3]);
-      *reinterpret_cast<float4*>(&sm.DO[i][f0 + 4]) = make_float4(od[4], od[5], od[6], od[7]);
-    }
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int q = tid + k * kThreads3;
-      const int cg = q >> 8, ww = (q >> 6) & 3, lo = q & 15, hi = (q >> 4) & 3;
-      sm.SC[16 * ww + 4 * hi + 0][16 * cg + lo] = s4[k].x;
-      sm.SC[16 * ww + 4 * hi + 1][16 * cg + lo] = s4[k].y;
-      sm.SC[16 * ww + 4 * hi + 2][16 * cg + lo] = s4[k].z;
-      sm.SC[16 * ww + 4 * hi + 3][16 * cg + lo] = s4[k].w;
-      sm.LL[16 * ww + lo][16 * cg + 4 * hi + 0] = l4[k].x;
-      sm.LL[16 * ww + lo][16 * cg + 4 * hi + 1] = l4[k].y;
-      sm.LL[16 * ww + lo][16 * cg + 4 * hi + 2] = l4[k].z;
-      sm.LL[16 * ww + lo][16 * cg + 4 * hi + 3] = l4[k].w;
-    }
-    __syncthreads();
+    // the next chunk's inputs (this chunk's again after the last one)
+    const int next = job + gridDim.x < total ? job + int(gridDim.x) : job;
+    grad_load<IO>(in, a, next / a.nchunks, next % a.nchunks, tid, w);
+  }
+  {
     // tr(Lam S^T) = sum of Lam o S, an 8-float slice per thread
     float trace = 0.f;
 #pragma unroll
@@ -807,7 +826,7 @@ __global__ void __launch_bounds__(kThreads3) falcon1_bwd_chunk_kernel(BwdArgs a)
     for (int off = 32; off >= 1; off >>= 1) trace += __shfl_xor(trace, off);
     if (l == 0) sm.trp[w] = trace;
   }
-  chunk_forward<kThreads3>(cc, a, c, tid, w, l);
+  chunk_forward<kThreads3>(cc, a, c, tid, w, l, sm.QX);
   chunk_factors<kThreads3>(cc, sm.DM, tid, w, l);
   const float eG = __expf(cc.G);
   auto xs = [&](int i) { return __expf(cc.G - cc.g[i]); };
@@ -849,11 +868,16 @@ __global__ void __launch_bounds__(kThreads3) falcon1_bwd_chunk_kernel(BwdArgs a)
     fxh.store(w, l, [&](int r, int s, float v) { sm.DXH[r][s] = v; });
     if (w < 4) fmx.store(w & 3, l, [&](int r, int s, float v) { sm.DM[r][s] = -v; });
     __syncthreads();
-    if (w >= 4) fmx.store(w & 3, l, [&](int r, int s, float v) { sm.DM[r][s] += v; });
+    // dM o D, D_{is} = e^{g_i-g_s} for s <= i
+    if (w >= 4)
+      fmx.store(w & 3, l, [&](int r, int s, float v) {
+        sm.DM[r][s] = s <= r ? (sm.DM[r][s] + v) * __expf(cc.g[r] - cc.g[s]) : 0.f;
+      });
   }
   __syncthreads();
   {
-    // decay terms of M, Qt and Xh (sixteen lanes per row)
+    // decay terms of M, Qt and Xh (sixteen lanes per row); with M = (Q X^T) o D,
+    // dM o M summed over a row or a column is (dM o D) o (Q X^T)
     const int i = ri;
     float qd = 0.f, xd = 0.f, rowm = 0.f, colm = 0.f;
     {
@@ -867,8 +891,8 @@ __global__ void __launch_bounds__(kThreads3) falcon1_bwd_chunk_kernel(BwdArgs a)
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int s2 = 2 * rp + k;
-      rowm = fmaf(sm.DM[i][s2], cc.MM[i][s2], rowm);
-      colm = fmaf(sm.DM[s2][i], cc.MM[s2][i], colm);
+      rowm = fmaf(sm.DM[i][s2], sm.QX[i][s2], rowm);
+      colm = fmaf(sm.DM[s2][i], sm.QX[s2][i], colm);
     }
     qd = sum16(qd); xd = sum16(xd); rowm = sum16(rowm); colm = sum16(colm);
     if (rp == 0) {
@@ -877,13 +901,6 @@ __global__ void __launch_bounds__(kThreads3) falcon1_bwd_chunk_kernel(BwdArgs a)
       sm.dgt[i] = z;
     }
   }
-  __syncthreads();
-  // dM o D, D_{is} = e^{g_i-g_s} for s <= i
-  for (int e = tid; e < kBC * kBC; e += kThreads3) {
-    const int i = e >> 5, s2 = e & 31;
-    sm.DM[i][s2] = s2 <= i ? sm.DM[i][s2] * __expf(cc.g[i] - cc.g[s2]) : 0.f;
-  }
-  __syncthreads();
   // dQ = Diag(e^g) dQt + (dM o D) X;  dX = Diag(e^{G-g}) dXh + (dM o D)^T Q
   float* dq_out = a.dphi_q + bh * T * kD;
   {
@@ -946,13 +963,11 @@ __global__ void __launch_bounds__(kThreads3) falcon1_bwd_chunk_kernel(BwdArgs a)
     }
     if (w < 4) fa.store(w & 3, l, [&](int r, int s2, float v) { sm.DM[r][s2] = -v; });
     __syncthreads();
-    if (w >= 4) fa.store(w & 3, l, [&](int r, int s2, float v) { sm.DM[r][s2] -= v; });
-  }
-  __syncthreads();
-  // A_{is} = eta_i e^{gp_i-g_s} k_{is}: D2 = dA o e^{gp_i-g_s} (s < i)
-  for (int e = tid; e < kBC * kBC; e += kThreads3) {
-    const int i = e >> 5, s2 = e & 31;
-    sm.DM[i][s2] = s2 < i ? sm.DM[i][s2] * __expf(cc.gp[i] - cc.g[s2]) : 0.f;
+    // A_{is} = eta_i e^{gp_i-g_s} k_{is}: D2 = dA o e^{gp_i-g_s} (s < i)
+    if (w >= 4)
+      fa.store(w & 3, l, [&](int r, int s2, float v) {
+        sm.DM[r][s2] = s2 < r ? (sm.DM[r][s2] - v) * __expf(cc.gp[r] - cc.g[s2]) : 0.f;
+      });
   }
   __syncthreads();
   {
@@ -971,22 +986,18 @@ __global__ void __launch_bounds__(kThreads3) falcon1_bwd_chunk_kernel(BwdArgs a)
       sm.dg[i] -= col;
     }
   }
-  __syncthreads();
-  // dK = Diag(eta) D2 (strictly lower), dX += (dK + dK^T) X
-  for (int e = tid; e < kBC * kBC; e += kThreads3) {
-    const int i = e >> 5, s2 = e & 31;
-    sm.DM[i][s2] *= cc.eta[i];
-  }
-  __syncthreads();
   {
+    // dK = Diag(eta) D2 (strictly lower): dX += dK X + dK^T X = Diag(eta) D2 X + D2^T Diag(eta) X
+    auto eta_of = [&](int i) { return cc.eta[i]; };
     Mm<kBC, kD, kBC, false, false, kWaves3> f1;
     Mm<kBC, kD, kBC, true, false, kWaves3> f2;
-    f1.load(&sm.DM[0][0], kPN, &cc.X[0][0], kPW, w, l);
-    f2.load(&sm.DM[0][0], kPN, &cc.X[0][0], kPW, w, l);
+    f1.load(&sm.DM[0][0], kPN, &cc.X[0][0], kPW, w, l, eta_of);
+    f2.load(&sm.DM[0][0], kPN, &cc.X[0][0], kPW, w, l, [](int) { return 1.f; }, eta_of);
     f1.run();
     f2.run(f1);
     f2.store(w, l, [&](int r, int s2, float v) { sm.RR[r][s2] += v; });
   }
+  __syncthreads();
   // gates: g -> log decay -> (eta, lam); eta -> (beta, lam, ||x||^2)
   if (w == 0) {
     const int i = l;
@@ -1051,6 +1062,8 @@ __global__ void __launch_bounds__(kThreads3) falcon1_bwd_chunk_kernel(BwdArgs a)
   // the last key feeds no token of this call
   if (c == a.nchunks - 1)
     for (int f = tid; f < kD; f += kThreads3) dk_out[int64_t(T - 1) * kD + f] = 0.f;
+  __syncthreads();   // LDS is refilled for the next chunk
+  }
 }
 
 }  // namespace
@@ -1077,14 +1090,21 @@ hipError_t launch_bwd(const ProblemArgs& p, const BwdBuffers& b, hipStream_t st)
   a.T = p.T; a.nchunks = nchunks; a.eps = p.eps; a.eps_gamma = p.eps_gamma;
   const int nunits = int(2 * BH);
   const unsigned chain_blocks = unsigned((nunits + 7) / 8) * 32u;
+  // one chunk-kernel workgroup per CU (its LDS allows no more)
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
+    ncu = 256;
+  const int jobs = int(n);
+  const unsigned chunk_blocks = unsigned(jobs < ncu ? jobs : ncu);
   if (p.bf16) {
     hipLaunchKernelGGL(falcon1_bwd_maps_kernel<bf16_t>, dim3(unsigned(n)), dim3(kThreads), 0, st, a);
     hipLaunchKernelGGL(falcon1_bwd_chain_kernel<bf16_t>, dim3(chain_blocks), dim3(kThreads), 0, st, a, nunits);
-    hipLaunchKernelGGL(falcon1_bwd_chunk_kernel<bf16_t>, dim3(unsigned(n)), dim3(kThreads3), 0, st, a);
+    hipLaunchKernelGGL(falcon1_bwd_chunk_kernel<bf16_t>, dim3(chunk_blocks), dim3(kThreads3), 0, st, a, jobs);
   } else {
     hipLaunchKernelGGL(falcon1_bwd_maps_kernel<float>, dim3(unsigned(n)), dim3(kThreads), 0, st, a);
     hipLaunchKernelGGL(falcon1_bwd_chain_kernel<float>, dim3(chain_blocks), dim3(kThreads), 0, st, a, nunits);
-    hipLaunchKernelGGL(falcon1_bwd_chunk_kernel<float>, dim3(unsigned(n)), dim3(kThreads3), 0, st, a);
+    hipLaunchKernelGGL(falcon1_bwd_chunk_kernel<float>, dim3(chunk_blocks), dim3(kThreads3), 0, st, a, jobs);
   }
   return hipGetLastError();
 }
