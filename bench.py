@@ -177,15 +177,16 @@ def backward_flops(B, H, T, dk=64, dv=64, C=32):
       maps:  Gram and M (2 C^2 d), W and U (C^2 (dk + dv)), P, H and G
              (3 C dk dv, dk^2 C for P), Q~ (C^2 dk)
       chains: P S and Lam^T P (2 dk^2 dv)
-      chunk: the recomputed Gram, M, W, U; X^ Lam, W S, dO S^T, (X^ Lam) S^T,
-             R Lam^T (5 C dk dv); M^T dO, M^T dQ~, dM (2), (dM o D) X and
-             (dM o D)^T Q, T^T dW, T^T dU, dA (2), dK X, dK^T X (12 C^2 d).
+      chunk: the recomputed Gram and M (W, U and T come from the maps);
+             X^ Lam, W S, dO S^T, (X^ Lam) S^T, R Lam^T (5 C dk dv); M^T dO,
+             M^T dQ~, dM (2), (dM o D) X and (dM o D)^T Q, T^T dW, T^T dU,
+             dA (2), dK X, dK^T X (12 C^2 d).
     Multiply-adds count two flops; VALU work is not counted."""
     nchunks = -(-T // C)
     d = dk
     maps = 2 * C * C * d + C * C * (dk + dv) + dk * dk * C + 2 * C * dk * dv + C * C * dk
     chains = 2 * dk * dk * dv
-    chunk = 2 * C * C * d + C * C * (dk + dv) + 5 * C * dk * dv + 12 * C * C * d
+    chunk = 2 * C * C * d + 5 * C * dk * dv + 12 * C * C * d
     return 2.0 * B * H * nchunks * (maps + chains + chunk)
 
 

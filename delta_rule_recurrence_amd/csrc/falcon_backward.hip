@@ -52,6 +52,11 @@ constexpr int kThreads = 256;  // four waves
 //   GD  G^T in accumulator order:       ((w*4 + cg)*64 + l)*4 + r <-> G[16w + (l&15)][16cg + 4(l>>4) + r]
 constexpr int kOffPA = 0, kOffPB = 4096, kOffHD = 8192, kOffGD = 12288;
 constexpr int kMapFloats = 16384;
+// Per-chunk forward factors the maps kernel hands to the chunk kernel, row-major:
+// W [32][64], U [32][64], T [32][32], then the gates eta, g, gp, den, lam,
+// flags (int bits) [32] each and G.
+constexpr int kFacW = 0, kFacU = 2048, kFacT = 4096, kFacGates = 5120;
+constexpr int kFacFloats = 5376;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -190,6 +195,7 @@ struct BwdArgs {
   float* maps;     // per chunk: PA, PB, HD, GD (above)
   float* ckpt;     // per chunk: S entering the chunk, ((cg*4 + w)*64 + l)*4 + r <-> S[16w + 4(l>>4) + r][16cg + (l&15)]
   float* adj;      // per chunk: dL/dS at its end, ((cg*4 + w)*64 + l)*4 + r <-> Lam[16w + (l&15)][16cg + 4(l>>4) + r]
+  float* fac;      // per chunk: the forward factors (above)
   int T, nchunks;
   float eps, eps_gamma;
 };
@@ -289,7 +295,7 @@ __device__ __forceinline__ void chunk_load(ChunkRegs<IO>& r, const BwdArgs& a, i
 }
 
 template <typename IO>
-__device__ __forceinline__ void chunk_store(ChunkCore& cc, const ChunkRegs<IO>& r, int tid) {
+__device__ __forceinline__ void chunk_store(ChunkCore& cc, const ChunkRegs<IO>& r, int tid, bool gate_inputs = true) {
   const int i = tid >> 3, f0 = (tid & 7) * 8;
   float x[8], q[8], v[8];
   r.x.get(x);
@@ -311,7 +317,7 @@ __device__ __forceinline__ void chunk_store(ChunkCore& cc, const ChunkRegs<IO>& 
   }
   e = sum8(e);
   if ((tid & 7) == 0) cc.en[i] = e;
-  if (tid < kBC) {
+  if (gate_inputs && tid < kBC) {
     cc.lamv[tid] = r.glive ? r.lam : 0.f;
     cc.den[tid] = r.glive ? r.beta : 0.f;   // beta until the gates replace it by the denominator
   }
@@ -475,6 +481,33 @@ __global__ void __launch_bounds__(kThreads) falcon1_bwd_maps_kernel(BwdArgs a) {
   __syncthreads();
   chunk_forward<kThreads>(cc, a, c, tid, w, l);
   chunk_factors<kThreads>(cc, TZ, tid, w, l);
+  {
+    // W, U, T and the gates for the chunk kernel
+    float* fo = a.fac + int64_t(blockIdx.x) * kFacFloats;
+    for (int q = tid; q < 512; q += kThreads) {
+      const int i = q >> 4, f = 4 * (q & 15);
+      reinterpret_cast<float4*>(fo + kFacW)[q] = *reinterpret_cast<const float4*>(&cc.W[i][f]);
+      reinterpret_cast<float4*>(fo + kFacU)[q] = *reinterpret_cast<const float4*>(&cc.U[i][f]);
+    }
+    {
+      const int i = tid >> 3, f = 4 * (tid & 7);
+      reinterpret_cast<float4*>(fo + kFacT)[tid] = *reinterpret_cast<const float4*>(&cc.TT[i][f]);
+    }
+    if (tid < 193) {
+      const int k = tid >> 5, i = tid & 31;
+      float v;
+      switch (k) {
+        case 0: v = cc.eta[i]; break;
+        case 1: v = cc.g[i]; break;
+        case 2: v = cc.gp[i]; break;
+        case 3: v = cc.den[i]; break;
+        case 4: v = cc.lamv[i]; break;
+        case 5: v = __int_as_float(cc.flags[i]); break;
+        default: v = cc.G; break;
+      }
+      fo[kFacGates + tid] = v;
+    }
+  }
   // V is dead: it holds Xh = Diag(e^{G-g}) X.  KX and AA (adjacent, dead)
   // hold Qt; X and Q (adjacent) hold P, then H, once Qt is formed.
   float (*XH)[kPW] = cc.V;
@@ -736,6 +769,8 @@ struct GradRegs {
   ChunkRegs<IO> r;
   Raw8<IO> odr;
   float4 s4[2], l4[2];
+  float4 wf, uf, tf;   // W, U (all threads), T (threads < 256)
+  float gf;            // gates (threads < 256)
   bool olive;
 };
 
@@ -754,13 +789,18 @@ __device__ __forceinline__ void grad_load(GradRegs<IO>& g, const BwdArgs& a, int
     g.s4[k] = ck[tid + k * kThreads3];
     g.l4[k] = ad[tid + k * kThreads3];
   }
+  const float* fo = a.fac + (bh * a.nchunks + c) * kFacFloats;
+  g.wf = reinterpret_cast<const float4*>(fo + kFacW)[tid];
+  g.uf = reinterpret_cast<const float4*>(fo + kFacU)[tid];
+  g.tf = reinterpret_cast<const float4*>(fo + kFacT)[u];
+  g.gf = fo[kFacGates + u];
 }
 
 template <typename IO>
 __device__ __forceinline__ void grad_store(GradSmem& sm, const GradRegs<IO>& g, int tid, int w) {
   const int u = tid & 255;
   if (w < 4) {
-    chunk_store<IO>(sm.cc, g.r, u);
+    chunk_store<IO>(sm.cc, g.r, u, false);   // the gates come with the factors
   } else {
     const int i = u >> 3, f0 = (u & 7) * 8;
     float od[8];
@@ -769,6 +809,27 @@ __device__ __forceinline__ void grad_store(GradSmem& sm, const GradRegs<IO>& g, 
     for (int k = 0; k < 8; ++k) od[k] = g.olive ? od[k] : 0.f;
     *reinterpret_cast<float4*>(&sm.DO[i][f0]) = make_float4(od[0], od[1], od[2], od[3]);
     *reinterpret_cast<float4*>(&sm.DO[i][f0 + 4]) = make_float4(od[4], od[5], od[6], od[7]);
+  }
+  {
+    ChunkCore& cc = sm.cc;
+    const int i = tid >> 4, f = 4 * (tid & 15);
+    *reinterpret_cast<float4*>(&cc.W[i][f]) = g.wf;
+    *reinterpret_cast<float4*>(&cc.U[i][f]) = g.uf;
+    if (w < 4) {
+      *reinterpret_cast<float4*>(&cc.TT[u >> 3][4 * (u & 7)]) = g.tf;
+      if (u < 193) {
+        const int k = u >> 5, r = u & 31;
+        switch (k) {
+          case 0: cc.eta[r] = g.gf; break;
+          case 1: cc.g[r] = g.gf; break;
+          case 2: cc.gp[r] = g.gf; break;
+          case 3: cc.den[r] = g.gf; break;
+          case 4: cc.lamv[r] = g.gf; break;
+          case 5: cc.flags[r] = __float_as_int(g.gf); break;
+          default: cc.G = g.gf; break;
+        }
+      }
+    }
   }
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
@@ -826,8 +887,22 @@ __global__ void __launch_bounds__(kThreads3) falcon1_bwd_chunk_kernel(BwdArgs a,
     for (int off = 32; off >= 1; off >>= 1) trace += __shfl_xor(trace, off);
     if (l == 0) sm.trp[w] = trace;
   }
-  chunk_forward<kThreads3>(cc, a, c, tid, w, l, sm.QX);
-  chunk_factors<kThreads3>(cc, sm.DM, tid, w, l);
+  {
+    // Gram (waves 0-3) and Q X^T (waves 4-7); M = tril(Q X^T) o D.  The gates,
+    // T, W and U come from the maps kernel.
+    Mm<kBC, kBC, kD, false, true> f;
+    f.load(w < 4 ? &cc.X[0][0] : &cc.Q[0][0], kPW, &cc.X[0][0], kPW, w & 3, l);
+    f.run();
+    if (w < 4) {
+      f.store(w & 3, l, [&](int r, int s2, float v) { cc.KX[r][s2] = v; });
+    } else {
+      f.store(w & 3, l, [&](int r, int s2, float v) {
+        sm.QX[r][s2] = v;
+        cc.MM[r][s2] = s2 <= r ? __expf(cc.g[r] - cc.g[s2]) * v : 0.f;
+      });
+    }
+  }
+  __syncthreads();
   const float eG = __expf(cc.G);
   auto xs = [&](int i) { return __expf(cc.G - cc.g[i]); };
   {
@@ -1071,7 +1146,7 @@ __global__ void __launch_bounds__(kThreads3) falcon1_bwd_chunk_kernel(BwdArgs a,
 size_t bwd_workspace_bytes(const ProblemArgs& p) {
   const int64_t nchunks = (int64_t(p.T) + kBC - 1) / kBC;
   const int64_t n = int64_t(p.B) * p.H * nchunks;
-  return size_t(n) * (kMapFloats + 2 * kD * kD) * sizeof(float);
+  return size_t(n) * (kMapFloats + 2 * kD * kD + kFacFloats) * sizeof(float);
 }
 
 hipError_t launch_bwd(const ProblemArgs& p, const BwdBuffers& b, hipStream_t st) {
@@ -1087,6 +1162,7 @@ hipError_t launch_bwd(const ProblemArgs& p, const BwdBuffers& b, hipStream_t st)
   a.maps = ws;
   a.ckpt = ws + n * kMapFloats;
   a.adj = a.ckpt + n * kD * kD;
+  a.fac = a.adj + n * kD * kD;
   a.T = p.T; a.nchunks = nchunks; a.eps = p.eps; a.eps_gamma = p.eps_gamma;
   const int nunits = int(2 * BH);
   const unsigned chain_blocks = unsigned((nunits + 7) / 8) * 32u;

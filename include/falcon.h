@@ -195,9 +195,10 @@ falcon_status falcon_decode_step(const falcon_problem* p,
  *  Every output must not overlap any input or another output
  *  (FALCON_ERR_ALIAS).
  *  workspace : device scratch of at least falcon_bwd_workspace_bytes(p)
- *              bytes, 16-byte aligned (the per-chunk maps, the state
- *              entering each chunk and the adjoint leaving it; 96 KiB per
- *              32-token chunk per (b, h)).
+ *              bytes, 16-byte aligned (per 32-token chunk per (b, h): the
+ *              chunk maps, the state entering the chunk, the adjoint
+ *              leaving it and the forward factors W, U, T and the gates;
+ *              117 KiB).
  */
 falcon_status falcon_bwd_chunked(const falcon_problem* p,
                                  const void* phi_k, const void* phi_q, const void* v,
