@@ -45,9 +45,12 @@ constexpr int kPW = 68;        // float pitch of 64-wide LDS matrices
 constexpr int kPN = 36;        // float pitch of 32-wide LDS matrices
 constexpr int kThreads = 256;  // four waves
 // Per-chunk maps, stored in the operand order of the chain kernel's MFMAs
-// (a 16x16 tile per wave and column group, four floats per lane):
-//   PA  P as the A operand of P S:      ((w*4 + j)*64 + l)*4 + e <-> P[16w + (l&15)][4(4j+e) + (l>>4)]
-//   PB  P as the B operand of Lam^T P:  ((w*4 + j)*64 + l)*4 + e <-> P[4(4j+e) + (l>>4)][16w + (l&15)]
+// (a 16x16 tile per wave and column group, four floats per lane; the chain's
+// contraction index k runs over 16m + 4(l>>4) + e at step e of block m, so
+// every map is exactly a 16x16 accumulator tile of a product the maps
+// kernel forms, stored as it sits in the lanes):
+//   PA  P as the A operand of P S:      ((w*4 + m)*64 + l)*4 + e <-> P[16w + (l&15)][16m + 4(l>>4) + e]
+//   PB  P as the B operand of Lam^T P:  ((w*4 + m)*64 + l)*4 + e <-> P[16m + 4(l>>4) + e][16w + (l&15)]
 //   HD  H in accumulator order:         ((w*4 + cg)*64 + l)*4 + r <-> H[16w + 4(l>>4) + r][16cg + (l&15)]
 //   GD  G^T in accumulator order:       ((w*4 + cg)*64 + l)*4 + r <-> G[16w + (l&15)][16cg + 4(l>>4) + r]
 constexpr int kOffPA = 0, kOffPB = 4096, kOffHD = 8192, kOffGD = 12288;
@@ -508,72 +511,59 @@ __global__ void __launch_bounds__(kThreads) falcon1_bwd_maps_kernel(BwdArgs a) {
       fo[kFacGates + tid] = v;
     }
   }
-  // V is dead: it holds Xh = Diag(e^{G-g}) X.  KX and AA (adjacent, dead)
-  // hold Qt; X and Q (adjacent) hold P, then H, once Qt is formed.
-  float (*XH)[kPW] = cc.V;
+  // KX and AA (two adjacent 32 x 36 arrays, dead after the factors) hold Qt.
   float (*QT)[kPW] = reinterpret_cast<float (*)[kPW]>(&cc.KX[0][0]);
-  float (*PS)[kPW] = reinterpret_cast<float (*)[kPW]>(&cc.X[0][0]);
   static_assert(sizeof(cc.KX) + sizeof(cc.AA) >= sizeof(float) * kBC * kPW, "Qt does not fit");
   static_assert(offsetof(ChunkCore, AA) == offsetof(ChunkCore, KX) + sizeof(cc.KX), "KX, AA not adjacent");
-  static_assert(sizeof(cc.X) + sizeof(cc.Q) >= sizeof(float) * kD * kPW, "P does not fit");
-  static_assert(offsetof(ChunkCore, Q) == offsetof(ChunkCore, X) + sizeof(cc.X), "X, Q not adjacent");
-  for (int e = tid; e < kBC * kD; e += kThreads) {
-    const int i = e >> 6, f = e & 63;
-    XH[i][f] = __expf(cc.G - cc.g[i]) * cc.X[i][f];
-  }
-  __syncthreads();
   // Qt = Diag(e^g) Q - M W
   mm<kBC, kD, kBC, false, false>(&cc.MM[0][0], kPN, &cc.W[0][0], kPW, w, l, [&](int r, int s, float v) {
     QT[r][s] = __expf(cc.g[r]) * cc.Q[r][s] - v;
   });
   __syncthreads();
+  // P = e^G I - X^T Diag(e^{G-g}) W and its transpose, H = X^T Diag(e^{G-g}) U
+  // and G^T = dO^T Qt, each written straight from the accumulators: the tile
+  // (tm, tn) of a wave is one 1 KiB run of its map.
   float* out = a.maps + int64_t(blockIdx.x) * kMapFloats;
   const float eG = __expf(cc.G);
-  // P = e^G I - Xh^T W
-  mm<kD, kD, kBC, true, false>(&XH[0][0], kPW, &cc.W[0][0], kPW, w, l,
-                               [&](int r, int s, float v) { PS[r][s] = (r == s ? eG : 0.f) - v; });
-  __syncthreads();
-  for (int q = tid; q < 1024; q += kThreads) {
-    const int ww = q >> 8, j = (q >> 6) & 3, ll = q & 63, lo = ll & 15, hi = ll >> 4;
-    float4 pa, pb;
-    pa.x = PS[16 * ww + lo][4 * (4 * j + 0) + hi];
-    pa.y = PS[16 * ww + lo][4 * (4 * j + 1) + hi];
-    pa.z = PS[16 * ww + lo][4 * (4 * j + 2) + hi];
-    pa.w = PS[16 * ww + lo][4 * (4 * j + 3) + hi];
-    pb.x = PS[4 * (4 * j + 0) + hi][16 * ww + lo];
-    pb.y = PS[4 * (4 * j + 1) + hi][16 * ww + lo];
-    pb.z = PS[4 * (4 * j + 2) + hi][16 * ww + lo];
-    pb.w = PS[4 * (4 * j + 3) + hi][16 * ww + lo];
-    reinterpret_cast<float4*>(out + kOffPA)[q] = pa;
-    reinterpret_cast<float4*>(out + kOffPB)[q] = pb;
+  auto xs = [&](int t) { return __expf(cc.G - cc.g[t]); };
+  auto one = [](int) { return 1.f; };
+  auto put = [&](float* base, int idx, const f32x4& v) {
+    reinterpret_cast<float4*>(base)[idx] = make_float4(v[0], v[1], v[2], v[3]);
+  };
+  const int g4 = 4 * (l >> 4), c16 = l & 15;
+  {
+    Mm<kD, kD, kBC, true, false> fp, fpt;
+    fp.load(&cc.X[0][0], kPW, &cc.W[0][0], kPW, w, l, one, xs);
+    fpt.load(&cc.W[0][0], kPW, &cc.X[0][0], kPW, w, l, one, xs);
+    fp.run();
+    fpt.run();
+#pragma unroll
+    for (int it = 0; it < fp.IT; ++it) {
+      const int tm = it, tn = w;   // N = 64 over four waves: column block w, row block it
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float d = (16 * tm + g4 + r == 16 * tn + c16) ? eG : 0.f;
+        fp.acc[it][r] = d - fp.acc[it][r];
+        fpt.acc[it][r] = d - fpt.acc[it][r];
+      }
+      // P tile (tm, tn) is PB block (w = tn, m = tm); P^T tile (tm, tn) is PA block (w = tn, m = tm)
+      put(out + kOffPB, (tn * 4 + tm) * 64 + l, fp.acc[it]);
+      put(out + kOffPA, (tn * 4 + tm) * 64 + l, fpt.acc[it]);
+    }
   }
-  __syncthreads();
-  // H = Xh^T U
-  mm<kD, kD, kBC, true, false>(&XH[0][0], kPW, &cc.U[0][0], kPW, w, l,
-                               [&](int r, int s, float v) { PS[r][s] = v; });
-  __syncthreads();
-  for (int q = tid; q < 1024; q += kThreads) {
-    const int ww = q >> 8, cg = (q >> 6) & 3, ll = q & 63, lo = ll & 15, hi = ll >> 4;
-    float4 hd;
-    hd.x = PS[16 * ww + 4 * hi + 0][16 * cg + lo];
-    hd.y = PS[16 * ww + 4 * hi + 1][16 * cg + lo];
-    hd.z = PS[16 * ww + 4 * hi + 2][16 * cg + lo];
-    hd.w = PS[16 * ww + 4 * hi + 3][16 * cg + lo];
-    reinterpret_cast<float4*>(out + kOffHD)[q] = hd;
-  }
-  __syncthreads();
-  // G = Qt^T dO
-  mm<kD, kD, kBC, true, false>(&QT[0][0], kPW, &DO[0][0], kPW, w, l,
-                               [&](int r, int s, float v) { PS[r][s] = v; });
-  __syncthreads();
-  for (int q = tid; q < 1024; q += kThreads) {
-    const int ww = q >> 8, cg = (q >> 6) & 3, ll = q & 63, lo = ll & 15, hi = ll >> 4;
-    float4 gd;
-    gd.x = PS[16 * ww + lo][16 * cg + 4 * hi + 0];
-    gd.y = PS[16 * ww + lo][16 * cg + 4 * hi + 1];
-    gd.z = PS[16 * ww + lo][16 * cg + 4 * hi + 2];
-    gd.w = PS[16 * ww + lo][16 * cg + 4 * hi + 3];
-    reinterpret_cast<float4*>(out + kOffGD)[q] = gd;
+  {
+    Mm<kD, kD, kBC, true, false> fh, fg;
+    fh.load(&cc.X[0][0], kPW, &cc.U[0][0], kPW, w, l, one, xs);
+    fg.load(&DO[0][0], kPW, &QT[0][0], kPW, w, l);
+    fh.run();
+    fg.run();
+#pragma unroll
+    for (int it = 0; it < fh.IT; ++it) {
+      const int tm = it, tn = w;
+      // H tile (tm, tn) is HD block (w = tm, cg = tn); G^T tile (tm, tn) is GD block (w = tn, cg = tm)
+      put(out + kOffHD, (tm * 4 + tn) * 64 + l, fh.acc[it]);
+      put(out + kOffGD, (tn * 4 + tm) * 64 + l, fg.acc[it]);
+    }
   }
 }
 
@@ -587,7 +577,7 @@ __global__ void __launch_bounds__(kThreads) falcon1_bwd_maps_kernel(BwdArgs a) {
 // of a (chain, sequence) are placed on one XCD (workgroups go round-robin over
 // the eight XCDs), so P is fetched from HBM once per XCD L2.
 struct ChainSmem {
-  float B[kD][16];       // state chain: S[:, 16cg .. 16cg+15] (k rows)
+  float Bt[16][kPW];     // state chain: S[:, 16cg .. 16cg+15] transposed (Bt[c][k] = S[k][16cg + c])
   float L[16][kPW];      // adjoint chain: Lam^T[16cg .. 16cg+15][:]
 };
 
@@ -610,25 +600,24 @@ __device__ __forceinline__ void chain_state(const BwdArgs& a, ChainSmem& sm, int
   auto load = [&](int c, float4 (&p4)[4], float4& h) {
     const float* cp = mp + (c < n ? c : n - 1) * kMapFloats;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) p4[j] = reinterpret_cast<const float4*>(cp + kOffPA)[(w * 4 + j) * 64 + l];
+    for (int m = 0; m < 4; ++m) p4[m] = reinterpret_cast<const float4*>(cp + kOffPA)[(w * 4 + m) * 64 + l];
     h = reinterpret_cast<const float4*>(cp + kOffHD)[(w * 4 + cg) * 64 + l];
   };
   auto step = [&](int c, const float4 (&p4)[4], const float4& h) {
     // S (entering chunk c) to LDS and to the checkpoint, then S <- P S + H
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sm.B[16 * w + 4 * g + r][c16] = S[r];
+    *reinterpret_cast<float4*>(&sm.Bt[c16][16 * w + 4 * g]) = make_float4(S[0], S[1], S[2], S[3]);
     float* ck = a.ckpt + (bh * n + c) * kD * kD;
     reinterpret_cast<float4*>(ck)[(cg * 4 + w) * 64 + l] = make_float4(S[0], S[1], S[2], S[3]);
     __syncthreads();
     f32x4 acc = {h.x, h.y, h.z, h.w};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float pe[4] = {p4[j].x, p4[j].y, p4[j].z, p4[j].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int kb = 4 * j + e;
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pe[e], sm.B[4 * kb + g][c16], acc, 0, 0, 0);
-      }
+    for (int m = 0; m < 4; ++m) {
+      // k = 16m + 4g + e
+      const float4 b4 = *reinterpret_cast<const float4*>(&sm.Bt[c16][16 * m + 4 * g]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(p4[m].x, b4.x, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(p4[m].y, b4.y, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(p4[m].z, b4.z, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(p4[m].w, b4.w, acc, 0, 0, 0);
     }
     S = acc;
     __syncthreads();
@@ -663,7 +652,7 @@ __device__ __forceinline__ void chain_adjoint(const BwdArgs& a, ChainSmem& sm, i
   auto load = [&](int s, float4 (&p4)[4], float4& g4) {
     const float* cp = mp + (s < n ? n - 1 - s : 0) * kMapFloats;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) p4[j] = reinterpret_cast<const float4*>(cp + kOffPB)[(w * 4 + j) * 64 + l];
+    for (int m = 0; m < 4; ++m) p4[m] = reinterpret_cast<const float4*>(cp + kOffPB)[(w * 4 + m) * 64 + l];
     g4 = reinterpret_cast<const float4*>(cp + kOffGD)[(w * 4 + cg) * 64 + l];
   };
   auto step = [&](int s, const float4 (&p4)[4], const float4& g4) {
@@ -677,13 +666,13 @@ __device__ __forceinline__ void chain_adjoint(const BwdArgs& a, ChainSmem& sm, i
     __syncthreads();
     f32x4 acc = {g4.x, g4.y, g4.z, g4.w};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float pe[4] = {p4[j].x, p4[j].y, p4[j].z, p4[j].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int kb = 4 * j + e;
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.L[c16][4 * kb + g], pe[e], acc, 0, 0, 0);
-      }
+    for (int m = 0; m < 4; ++m) {
+      // k = 16m + 4g + e
+      const float4 a4 = *reinterpret_cast<const float4*>(&sm.L[c16][16 * m + 4 * g]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.x, p4[m].x, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.y, p4[m].y, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.z, p4[m].z, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.w, p4[m].w, acc, 0, 0, 0);
     }
     Lt = acc;
     __syncthreads();
