@@ -240,6 +240,64 @@ def bench_backward(name="f1_backward_8x12x2048_d64", steps=10, warmup=2):
                                      "falcon1_bwd_chunk_kernel"]}}
 
 
+def oracle_sample(kind, budget_s=3.0):
+    """The oracle as it stands, timed on one host core over a bounded sample of
+    another workload (a few seconds each), scaled to that workload's unit.
+    Returns the bench-line object."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from delta_rule_recurrence_amd import inputs as I
+    from oracle import falcon_backward as ob
+    from oracle import falcon_oracle as orc
+
+    f = I.as_f64
+    with threadpool_limits(limits=1):
+        if kind in ("f1a", "f2"):
+            name = "f1a_chunked_2x12x16384_d64" if kind == "f1a" else "f2_chunked_8x12x2048_d64"
+            w = I.WORKLOADS[name]
+            Ts = 2048 if kind == "f1a" else w.T
+            d = I.workload_inputs(w)
+            t0 = time.perf_counter()
+            orc.falcon_forward(w.variant, f(d["phi_k"][:, :, :Ts]), f(d["phi_q"][:, :, :Ts]),
+                               f(d["v"][:, :, :Ts]), f(d["beta"][:, :, :Ts]), f(d["lam"][:, :, :Ts]),
+                               eps=w.eps, eps_gamma=w.eps_gamma)
+            dt = time.perf_counter() - t0
+            return {"value": w.B * Ts / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                    "sample": f"all {w.B}x{w.H} sequences, first {Ts} of {w.T} tokens (fp64 numpy)",
+                    "seconds": round(dt, 3)}
+        if kind == "decode":
+            D = I.DECODE
+            rows = 64
+            S = f(I.random_state((D["B"], D["H"], D["dk"], D["dv"]), seed=D["seed"], scale=0.05)[:rows])
+            st = {k: f(v[:rows]) for k, v in I.decode_step_inputs(1, D["B"], D["H"], D["dk"], D["dv"],
+                                                                   seed=D["seed"]).items()}
+            t0 = time.perf_counter()
+            orc.falcon_decode_step("falcon1", S, st["phi_k"], st["phi_q"], st["v"], st["beta"], st["lam"],
+                                   eps=D["eps"], eps_gamma=D["eps_gamma"])
+            dt = time.perf_counter() - t0
+            return {"value": rows / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                    "sample": f"one decode step for {rows} of {D['B']} batch rows x {D['H']} heads (fp64 numpy)",
+                    "seconds": round(dt, 4)}
+        if kind == "backward":
+            w = I.WORKLOADS["f1_backward_8x12x2048_d64"]
+            d = I.workload_inputs(w)
+            cot = I.make_cotangents(w.B, w.H, w.T, w.dv, seed=w.seed, io_dtype=w.io_dtype, with_state=True)
+            hs = 4   # sequences (b = 0, h = 0..3): the oracle keeps every state of the sweep
+            sl = (slice(0, 1), slice(0, hs))
+            t0 = time.perf_counter()
+            ob.falcon1_backward(f(d["phi_k"][sl]), f(d["phi_q"][sl]), f(d["v"][sl]), f(d["beta"][sl]),
+                                f(d["lam"][sl]), f(cot["dO"][sl]), eps=w.eps, eps_gamma=w.eps_gamma,
+                                dS_T=f(cot["dS_T"][sl]))
+            dt = time.perf_counter() - t0
+            # tokens/s of the whole batch at this per-sequence rate
+            return {"value": hs * w.T / dt / w.H, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                    "sample": f"{hs} of {w.B}x{w.H} sequences x {w.T} tokens (fp64 numpy); value = "
+                              f"B*T tokens/s at that per-sequence rate",
+                    "seconds": round(dt, 3)}
+    raise ValueError(kind)
+
+
 def calibrate_copy(nbytes=1 << 28, reps=5):
     """A plain device copy of known size, for scaling rocprofv3 FETCH_SIZE /
     WRITE_SIZE counters (each copy reads and writes nbytes once)."""
@@ -368,6 +426,13 @@ def main():
         line["f1_backward"] = bench_backward()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(d, w, o, S_T)
+        # the oracle beside every other workload, on a bounded sample each
+        if not args.no_decode:
+            line["decode"]["cpu_oracle"] = oracle_sample("decode")
+        if not args.no_extra:
+            line["f1a_chunked"]["cpu_oracle"] = oracle_sample("f1a")
+            line["f2_chunked"]["cpu_oracle"] = oracle_sample("f2")
+            line["f1_backward"]["cpu_oracle"] = oracle_sample("backward")
     print(json.dumps(line))
 
 
