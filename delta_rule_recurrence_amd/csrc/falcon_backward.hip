@@ -50,11 +50,12 @@ constexpr int kThreads = 256;  // four waves
 // every map is exactly a 16x16 accumulator tile of a product the maps
 // kernel forms, stored as it sits in the lanes):
 //   PA  P as the A operand of P S:      ((w*4 + m)*64 + l)*4 + e <-> P[16w + (l&15)][16m + 4(l>>4) + e]
-//   PB  P as the B operand of Lam^T P:  ((w*4 + m)*64 + l)*4 + e <-> P[16m + 4(l>>4) + e][16w + (l&15)]
 //   HD  H in accumulator order:         ((w*4 + cg)*64 + l)*4 + r <-> H[16w + 4(l>>4) + r][16cg + (l&15)]
 //   GD  G^T in accumulator order:       ((w*4 + cg)*64 + l)*4 + r <-> G[16w + (l&15)][16cg + 4(l>>4) + r]
-constexpr int kOffPA = 0, kOffPB = 4096, kOffHD = 8192, kOffGD = 12288;
-constexpr int kMapFloats = 16384;
+// The adjoint chain needs P's column blocks; it reads PA too and regroups it
+// through LDS, so P is stored once.
+constexpr int kOffPA = 0, kOffHD = 4096, kOffGD = 8192;
+constexpr int kMapFloats = 12288;
 // Per-chunk forward factors the maps kernel hands to the chunk kernel, row-major:
 // W [32][64], U [32][64], T [32][32], then the gates eta, g, gp, den, lam,
 // flags (int bits) [32] each and G.
@@ -195,7 +196,7 @@ struct BwdArgs {
   float* dlam;
   float* dS0;
   float* dk_prev;
-  float* maps;     // per chunk: PA, PB, HD, GD (above)
+  float* maps;     // per chunk: PA, HD, GD (above)
   float* ckpt;     // per chunk: S entering the chunk, ((cg*4 + w)*64 + l)*4 + r <-> S[16w + 4(l>>4) + r][16cg + (l&15)]
   float* adj;      // per chunk: dL/dS at its end, ((cg*4 + w)*64 + l)*4 + r <-> Lam[16w + (l&15)][16cg + 4(l>>4) + r]
   float* fac;      // per chunk: the forward factors (above)
@@ -520,8 +521,8 @@ __global__ void __launch_bounds__(kThreads) falcon1_bwd_maps_kernel(BwdArgs a) {
     QT[r][s] = __expf(cc.g[r]) * cc.Q[r][s] - v;
   });
   __syncthreads();
-  // P = e^G I - X^T Diag(e^{G-g}) W and its transpose, H = X^T Diag(e^{G-g}) U
-  // and G^T = dO^T Qt, each written straight from the accumulators: the tile
+  // P^T = e^G I - W^T Diag(e^{G-g}) X, H = X^T Diag(e^{G-g}) U and
+  // G^T = dO^T Qt, each written straight from the accumulators: the tile
   // (tm, tn) of a wave is one 1 KiB run of its map.
   float* out = a.maps + int64_t(blockIdx.x) * kMapFloats;
   const float eG = __expf(cc.G);
@@ -532,22 +533,18 @@ __global__ void __launch_bounds__(kThreads) falcon1_bwd_maps_kernel(BwdArgs a) {
   };
   const int g4 = 4 * (l >> 4), c16 = l & 15;
   {
-    Mm<kD, kD, kBC, true, false> fp, fpt;
-    fp.load(&cc.X[0][0], kPW, &cc.W[0][0], kPW, w, l, one, xs);
+    Mm<kD, kD, kBC, true, false> fpt;
     fpt.load(&cc.W[0][0], kPW, &cc.X[0][0], kPW, w, l, one, xs);
-    fp.run();
     fpt.run();
 #pragma unroll
-    for (int it = 0; it < fp.IT; ++it) {
+    for (int it = 0; it < fpt.IT; ++it) {
       const int tm = it, tn = w;   // N = 64 over four waves: column block w, row block it
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float d = (16 * tm + g4 + r == 16 * tn + c16) ? eG : 0.f;
-        fp.acc[it][r] = d - fp.acc[it][r];
         fpt.acc[it][r] = d - fpt.acc[it][r];
       }
-      // P tile (tm, tn) is PB block (w = tn, m = tm); P^T tile (tm, tn) is PA block (w = tn, m = tm)
-      put(out + kOffPB, (tn * 4 + tm) * 64 + l, fp.acc[it]);
+      // P^T tile (tm, tn) is PA block (w = tn, m = tm)
       put(out + kOffPA, (tn * 4 + tm) * 64 + l, fpt.acc[it]);
     }
   }
@@ -579,6 +576,7 @@ __global__ void __launch_bounds__(kThreads) falcon1_bwd_maps_kernel(BwdArgs a) {
 struct ChainSmem {
   float Bt[16][kPW];     // state chain: S[:, 16cg .. 16cg+15] transposed (Bt[c][k] = S[k][16cg + c])
   float L[16][kPW];      // adjoint chain: Lam^T[16cg .. 16cg+15][:]
+  float P[kD][kPW];      // adjoint chain: this chunk's P
 };
 
 constexpr int kRing = 3;   // chunks of operands in flight per chain
@@ -597,44 +595,52 @@ __device__ __forceinline__ void chain_state(const BwdArgs& a, ChainSmem& sm, int
   for (int r = 0; r < 4; ++r) S[r] = a.S0 ? a.S0[bh * kD * kD + (16 * w + 4 * g + r) * kD + 16 * cg + c16] : 0.f;
   const float* mp = a.maps + bh * n * kMapFloats;
   float4 pa[kRing][4], hd[kRing];
-  auto load = [&](int c, float4 (&p4)[4], float4& h) {
+  auto load = [&](int c, float4 (&p4)[4], float4& h) __attribute__((always_inline)) {
     const float* cp = mp + (c < n ? c : n - 1) * kMapFloats;
 #pragma unroll
     for (int m = 0; m < 4; ++m) p4[m] = reinterpret_cast<const float4*>(cp + kOffPA)[(w * 4 + m) * 64 + l];
     h = reinterpret_cast<const float4*>(cp + kOffHD)[(w * 4 + cg) * 64 + l];
   };
-  auto step = [&](int c, const float4 (&p4)[4], const float4& h) {
+  auto step = [&](int c, const float4 (&p4)[4], const float4& h) __attribute__((always_inline)) {
     // S (entering chunk c) to LDS and to the checkpoint, then S <- P S + H
     *reinterpret_cast<float4*>(&sm.Bt[c16][16 * w + 4 * g]) = make_float4(S[0], S[1], S[2], S[3]);
     float* ck = a.ckpt + (bh * n + c) * kD * kD;
     reinterpret_cast<float4*>(ck)[(cg * 4 + w) * 64 + l] = make_float4(S[0], S[1], S[2], S[3]);
     __syncthreads();
-    f32x4 acc = {h.x, h.y, h.z, h.w};
+    // k = 16m + 4g + e; one accumulator per k block m, so the four dependent
+    // MFMA chains interleave
+    float4 b4[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      // k = 16m + 4g + e
-      const float4 b4 = *reinterpret_cast<const float4*>(&sm.Bt[c16][16 * m + 4 * g]);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(p4[m].x, b4.x, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(p4[m].y, b4.y, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(p4[m].z, b4.z, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(p4[m].w, b4.w, acc, 0, 0, 0);
-    }
-    S = acc;
+    for (int m = 0; m < 4; ++m) b4[m] = *reinterpret_cast<const float4*>(&sm.Bt[c16][16 * m + 4 * g]);
+    f32x4 acc[4] = {{h.x, h.y, h.z, h.w}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(p4[m].x, b4[m].x, acc[m], 0, 0, 0);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(p4[m].y, b4[m].y, acc[m], 0, 0, 0);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(p4[m].z, b4[m].z, acc[m], 0, 0, 0);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(p4[m].w, b4[m].w, acc[m], 0, 0, 0);
+    S = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     __syncthreads();
   };
-#pragma unroll
-  for (int d = 0; d < kRing; ++d) load(d, pa[d], hd[d]);
+  // the ring slots are named explicitly (slot d holds chunk c0 + d), so they
+  // stay in registers
+  static_assert(kRing == 3, "the ring is unrolled by hand");
+  load(0, pa[0], hd[0]);
+  load(1, pa[1], hd[1]);
+  load(2, pa[2], hd[2]);
   int c0 = 0;
   for (; c0 + kRing <= n; c0 += kRing) {
-#pragma unroll
-    for (int d = 0; d < kRing; ++d) {
-      step(c0 + d, pa[d], hd[d]);
-      load(c0 + d + kRing, pa[d], hd[d]);
-    }
+    step(c0 + 0, pa[0], hd[0]);
+    load(c0 + 0 + kRing, pa[0], hd[0]);
+    step(c0 + 1, pa[1], hd[1]);
+    load(c0 + 1 + kRing, pa[1], hd[1]);
+    step(c0 + 2, pa[2], hd[2]);
+    load(c0 + 2 + kRing, pa[2], hd[2]);
   }
-#pragma unroll
-  for (int d = 0; d < kRing - 1; ++d)
-    if (c0 + d < n) step(c0 + d, pa[d], hd[d]);
+  if (c0 + 0 < n) step(c0 + 0, pa[0], hd[0]);
+  if (c0 + 1 < n) step(c0 + 1, pa[1], hd[1]);
 }
 
 template <typename IO>
@@ -649,47 +655,65 @@ __device__ __forceinline__ void chain_adjoint(const BwdArgs& a, ChainSmem& sm, i
   const float* mp = a.maps + bh * n * kMapFloats;
   float4 pb[kRing][4], gd[kRing];
   // operands of step s, which processes chunk n - 1 - s
-  auto load = [&](int s, float4 (&p4)[4], float4& g4) {
+  auto load = [&](int s, float4 (&p4)[4], float4& g4) __attribute__((always_inline)) {
     const float* cp = mp + (s < n ? n - 1 - s : 0) * kMapFloats;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) p4[m] = reinterpret_cast<const float4*>(cp + kOffPB)[(w * 4 + m) * 64 + l];
+    for (int m = 0; m < 4; ++m) p4[m] = reinterpret_cast<const float4*>(cp + kOffPA)[(w * 4 + m) * 64 + l];
     g4 = reinterpret_cast<const float4*>(cp + kOffGD)[(w * 4 + cg) * 64 + l];
   };
-  auto step = [&](int s, const float4 (&p4)[4], const float4& g4) {
+  auto step = [&](int s, const float4 (&p4)[4], const float4& g4) __attribute__((always_inline)) {
     // Lam^T (at the end of chunk c) to LDS and to the adjoint store, then
     // Lam^T <- Lam^T P + G^T
     const int c = n - 1 - s;
 #pragma unroll
     for (int r = 0; r < 4; ++r) sm.L[4 * g + r][16 * w + c16] = Lt[r];
+    // this wave's rows 16w..16w+15 of P (PA order) into LDS; the product below
+    // reads P's column block w
+    // (stored component-wise: a 16-byte store of the slot itself makes the
+    // compiler keep the whole ring in scratch memory)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const float4 q = p4[m];
+      float* dst = &sm.P[16 * w + c16][16 * m + 4 * g];
+      dst[0] = q.x; dst[1] = q.y; dst[2] = q.z; dst[3] = q.w;
+    }
     float* ad = a.adj + (bh * n + c) * kD * kD;
     reinterpret_cast<float4*>(ad)[(cg * 4 + w) * 64 + l] = make_float4(Lt[0], Lt[1], Lt[2], Lt[3]);
     __syncthreads();
-    f32x4 acc = {g4.x, g4.y, g4.z, g4.w};
+    // k = 16m + 4g + e; one accumulator per k block m (interleaved chains)
+    float4 a4[4], b4[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      // k = 16m + 4g + e
-      const float4 a4 = *reinterpret_cast<const float4*>(&sm.L[c16][16 * m + 4 * g]);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.x, p4[m].x, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.y, p4[m].y, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.z, p4[m].z, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.w, p4[m].w, acc, 0, 0, 0);
+      a4[m] = *reinterpret_cast<const float4*>(&sm.L[c16][16 * m + 4 * g]);
+      b4[m] = make_float4(sm.P[16 * m + 4 * g + 0][16 * w + c16], sm.P[16 * m + 4 * g + 1][16 * w + c16],
+                          sm.P[16 * m + 4 * g + 2][16 * w + c16], sm.P[16 * m + 4 * g + 3][16 * w + c16]);
     }
-    Lt = acc;
+    f32x4 acc[4] = {{g4.x, g4.y, g4.z, g4.w}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[m].x, b4[m].x, acc[m], 0, 0, 0);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[m].y, b4[m].y, acc[m], 0, 0, 0);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[m].z, b4[m].z, acc[m], 0, 0, 0);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[m].w, b4[m].w, acc[m], 0, 0, 0);
+    Lt = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     __syncthreads();
   };
-#pragma unroll
-  for (int d = 0; d < kRing; ++d) load(d, pb[d], gd[d]);
+  load(0, pb[0], gd[0]);
+  load(1, pb[1], gd[1]);
+  load(2, pb[2], gd[2]);
   int s0 = 0;
   for (; s0 + kRing <= n; s0 += kRing) {
-#pragma unroll
-    for (int d = 0; d < kRing; ++d) {
-      step(s0 + d, pb[d], gd[d]);
-      load(s0 + d + kRing, pb[d], gd[d]);
-    }
+    step(s0 + 0, pb[0], gd[0]);
+    load(s0 + 0 + kRing, pb[0], gd[0]);
+    step(s0 + 1, pb[1], gd[1]);
+    load(s0 + 1 + kRing, pb[1], gd[1]);
+    step(s0 + 2, pb[2], gd[2]);
+    load(s0 + 2 + kRing, pb[2], gd[2]);
   }
-#pragma unroll
-  for (int d = 0; d < kRing - 1; ++d)
-    if (s0 + d < n) step(s0 + d, pb[d], gd[d]);
+  if (s0 + 0 < n) step(s0 + 0, pb[0], gd[0]);
+  if (s0 + 1 < n) step(s0 + 1, pb[1], gd[1]);
   if (a.dS0) {
     float* d = a.dS0 + bh * kD * kD + (16 * w + c16) * kD + 16 * cg + 4 * g;
     *reinterpret_cast<float4*>(d) = make_float4(Lt[0], Lt[1], Lt[2], Lt[3]);
@@ -700,7 +724,7 @@ __device__ __forceinline__ void chain_adjoint(const BwdArgs& a, ChainSmem& sm, i
 // workgroups of the 8 x 12 training shape resident at once (three per CU),
 // so no chain waits for a free CU.
 template <typename IO>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
 falcon1_bwd_chain_kernel(BwdArgs a, int nunits) {
   __shared__ ChainSmem sm;
   const int tid = threadIdx.x;

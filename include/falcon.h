@@ -198,7 +198,7 @@ falcon_status falcon_decode_step(const falcon_problem* p,
  *              bytes, 16-byte aligned (per 32-token chunk per (b, h): the
  *              chunk maps, the state entering the chunk, the adjoint
  *              leaving it and the forward factors W, U, T and the gates;
- *              117 KiB).
+ *              101 KiB).
  */
 falcon_status falcon_bwd_chunked(const falcon_problem* p,
                                  const void* phi_k, const void* phi_q, const void* v,

@@ -172,8 +172,8 @@ def call_bwd(lib, p, ws=None, wsb=0, **over):
 
 def test_backward_validation(lib):
     need = fb.falcon_bwd_workspace_bytes(prob())
-    # 117 KiB per 32-token chunk per (b, h): T = 40 -> 2 chunks, B*H = 6
-    assert need == 6 * 2 * 117 * 1024
+    # 101 KiB per 32-token chunk per (b, h): T = 40 -> 2 chunks, B*H = 6
+    assert need == 6 * 2 * 101 * 1024
     ws = fake(20)
     assert call_bwd(lib, None) == NULL
     assert call_bwd(lib, prob(variant="falcon1a"), ws, need) == VARIANT
