@@ -159,6 +159,43 @@ def bench_chunked_workload(name, steps=20, warmup=3):
             "workspace_bytes": int(ws.numel()), "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
 
 
+def bench_recurrent(name="f1_chunked_8x12x2048_d64", steps=5, warmup=1):
+    """The recurrent entry point (falcon_fwd_recurrent: one pass over T per
+    sequence with the state on chip) on the headline workload, timed like the
+    chunked legs."""
+    import torch
+
+    from delta_rule_recurrence_amd import falcon as fb
+    from delta_rule_recurrence_amd import inputs as I
+
+    w = I.WORKLOADS[name]
+    d = {k: v.cuda() for k, v in I.workload_inputs(w).items()}
+    o = torch.empty((w.B, w.H, w.T, w.dv), dtype=torch.bfloat16, device="cuda")
+    S_T = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+
+    def step():
+        fb.falcon_fwd_recurrent(d["phi_k"], d["phi_q"], d["v"], d["beta"], d["lam"], variant=w.variant,
+                                o=o, S_T=S_T, eps=w.eps, eps_gamma=w.eps_gamma)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = algorithmic_bytes(w.B, w.H, w.T, w.dk, w.dv)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": name, "entry": "falcon_fwd_recurrent", "steps": steps, "us_per_step": ms * 1e3,
+            "tokens_per_s": w.B * w.T / (ms * 1e-3), "algorithmic_bytes": nbytes, "hbm_gbs": gbs,
+            "hbm_frac": gbs / HBM_PEAK_GBS,
+            "bound": "latency (T dependent steps per sequence)"}
+
+
 def backward_bytes(B, H, T, dk, dv, io_bytes=2):
     """Compulsory HBM bytes of one Falcon-1 backward: read phi(k), phi(q), v and
     dO once (io dtype), beta and lam once, dS_T once; write the float32
@@ -344,9 +381,11 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the other workloads (Falcon-1A 2x12x16384, Falcon-2 8x12x2048, "
-                         "the Falcon-1 backward 8x12x2048)")
+                         "the Falcon-1 backward 8x12x2048, the recurrent entry point)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain copy of known size (for PMC counter scaling)")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="only time the Falcon-1 backward leg (--steps calls), for profiling")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the Falcon forward "
@@ -361,6 +400,9 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.backward_only:
+        print(json.dumps({"f1_backward": bench_backward(steps=args.steps, warmup=1)}))
         return
     w = I.WORKLOADS[WORKLOAD]
     d = I.workload_inputs(w)
@@ -424,6 +466,7 @@ def main():
         line["f1a_chunked"] = bench_chunked_workload("f1a_chunked_2x12x16384_d64")
         line["f2_chunked"] = bench_chunked_workload("f2_chunked_8x12x2048_d64", steps=5, warmup=1)
         line["f1_backward"] = bench_backward()
+        line["f1_recurrent"] = bench_recurrent()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(d, w, o, S_T)
         # the oracle beside every other workload, on a bounded sample each
@@ -433,6 +476,8 @@ def main():
             line["f1a_chunked"]["cpu_oracle"] = oracle_sample("f1a")
             line["f2_chunked"]["cpu_oracle"] = oracle_sample("f2")
             line["f1_backward"]["cpu_oracle"] = oracle_sample("backward")
+            # the recurrent entry point computes the headline workload: same oracle figure
+            line["f1_recurrent"]["cpu_oracle"] = dict(line["cpu_baseline"])
     print(json.dumps(line))
 
 
