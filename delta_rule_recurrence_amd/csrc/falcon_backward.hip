@@ -328,14 +328,19 @@ __device__ __forceinline__ void chunk_store(ChunkCore& cc, const ChunkRegs<IO>& 
 }
 
 // Gates, the Gram, A, M, the inverse T and the factors W, U of one chunk whose
-// inputs are in LDS (after a barrier).  Ends with a barrier.
-template <int NT>
-__device__ void chunk_forward(ChunkCore& cc, const BwdArgs& a, int c, int tid, int w, int l,
-                              float (*qx)[kPN] = nullptr) {
-  static_assert(NT == 256 || NT == 512, "four or eight waves");
+// inputs are in LDS (after a barrier), on four waves.  The Gram and Q X^T are
+// issued first; wave 0 forms the gates while its products run, and the
+// decays are applied from the registers after the barrier.  Ends with a
+// barrier.
+__device__ void chunk_forward(ChunkCore& cc, const BwdArgs& a, int c, int tid, int w, int l) {
   const int T = a.T;
   const int t0 = c * kBC;
   const bool fresh = (a.k_prev == nullptr);
+  Mm<kBC, kBC, kD, false, true> fk, fm;
+  fk.load(&cc.X[0][0], kPW, &cc.X[0][0], kPW, w, l);
+  fm.load(&cc.Q[0][0], kPW, &cc.X[0][0], kPW, w, l);
+  fk.run();
+  fm.run();
   if (w == 0) {
     // gates of row i (Eq. 3.4; Section 4.3 clamp; Section 3 fresh-start
     // sentinel), then the chunk-local prefix sums of the log decays
@@ -368,32 +373,12 @@ __device__ void chunk_forward(ChunkCore& cc, const BwdArgs& a, int c, int tid, i
     }
   }
   __syncthreads();
-  {
-    // Gram, A and M (with eight waves, the Gram on waves 0-3 and M on 4-7)
-    auto store_k = [&](int r, int s, float v) {
-      cc.KX[r][s] = v;
-      cc.AA[r][s] = s < r ? cc.eta[r] * __expf(cc.gp[r] - cc.g[s]) * v : 0.f;
-    };
-    auto store_m = [&](int r, int s, float v) {
-      cc.MM[r][s] = s <= r ? __expf(cc.g[r] - cc.g[s]) * v : 0.f;
-      if (qx) qx[r][s] = v;
-    };
-    if (NT == 512) {
-      Mm<kBC, kBC, kD, false, true> f;
-      f.load(w < 4 ? &cc.X[0][0] : &cc.Q[0][0], kPW, &cc.X[0][0], kPW, w & 3, l);
-      f.run();
-      if (w < 4) f.store(w & 3, l, store_k);
-      else f.store(w & 3, l, store_m);
-    } else {
-      Mm<kBC, kBC, kD, false, true> fk, fm;
-      fk.load(&cc.X[0][0], kPW, &cc.X[0][0], kPW, w, l);
-      fm.load(&cc.Q[0][0], kPW, &cc.X[0][0], kPW, w, l);
-      fk.run();
-      fm.run();
-      fk.store(w, l, store_k);
-      fm.store(w, l, store_m);
-    }
-  }
+  // A = tril(Diag(eta) K o e^{gp_i - g_s}, -1), M = tril(Q X^T o e^{g_i - g_s})
+  fk.store(w, l, [&](int r, int s, float v) {
+    cc.KX[r][s] = v;
+    cc.AA[r][s] = s < r ? cc.eta[r] * __expf(cc.gp[r] - cc.g[s]) * v : 0.f;
+  });
+  fm.store(w, l, [&](int r, int s, float v) { cc.MM[r][s] = s <= r ? __expf(cc.g[r] - cc.g[s]) * v : 0.f; });
   __syncthreads();
   // T11, T22 by substitution: lane j solves (I + A_bb) t = e_jj, b = j / 16
   if (tid < kBC) {
@@ -437,16 +422,15 @@ __device__ void chunk_forward(ChunkCore& cc, const BwdArgs& a, int c, int tid, i
 
 // W = T Diag(eta e^{gp}) X and U = T Diag(eta) V, with TZ = T Diag(eta) in
 // the caller's 32 x 36 scratch; AA becomes T Diag(eta e^{gp}).  Ends with a barrier.
-template <int NT>
 __device__ void chunk_factors(ChunkCore& cc, float (*TZ)[kPN], int tid, int w, int l) {
-  for (int e = tid; e < kBC * kBC; e += NT) {
+  for (int e = tid; e < kBC * kBC; e += kThreads) {
     const int i = e >> 5, s = e & 31;
     const float t = cc.TT[i][s];
     cc.AA[i][s] = t * cc.eta[s] * __expf(cc.gp[s]);
     TZ[i][s] = t * cc.eta[s];
   }
   __syncthreads();
-  Mm<kBC, kD, kBC, false, false, NT / 64> fw, fu;
+  Mm<kBC, kD, kBC, false, false> fw, fu;
   fw.load(&cc.AA[0][0], kPN, &cc.X[0][0], kPW, w, l);
   fu.load(&TZ[0][0], kPN, &cc.V[0][0], kPW, w, l);
   fw.run();
@@ -457,37 +441,59 @@ __device__ void chunk_factors(ChunkCore& cc, float (*TZ)[kPN], int tid, int w, i
 }
 
 // ---- launch 1: chunk maps --------------------------------------------------------
+// Persistent like the chunk kernel: workgroup b handles chunks b, b +
+// gridDim.x, ... and loads the next chunk's inputs while it works on the
+// current one.
 template <typename IO>
-__global__ void __launch_bounds__(kThreads) falcon1_bwd_maps_kernel(BwdArgs a) {
+struct MapRegs {
+  ChunkRegs<IO> r;
+  Raw8<IO> odr;
+  bool olive;
+};
+
+template <typename IO>
+__device__ __forceinline__ void map_load(MapRegs<IO>& m, const BwdArgs& a, int job, int tid) {
+  const int64_t bh = job / a.nchunks;
+  const int c = job % a.nchunks;
+  const int T = a.T;
+  chunk_load<IO>(m.r, a, bh, c, tid);
+  const int orow = c * kBC + (tid >> 3);
+  m.olive = orow < T;
+  m.odr.load(static_cast<const IO*>(a.dO) + (bh * T + (orow < T ? orow : T - 1)) * kD + (tid & 7) * 8);
+}
+
+template <typename IO>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+falcon1_bwd_maps_kernel(BwdArgs a, int total) {
   __shared__ ChunkCore cc;
   __shared__ float TZ[kBC][kPN];
   __shared__ __align__(16) float DO[kBC][kPW];
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;   // wave-uniform
-  const int64_t bh = blockIdx.x / a.nchunks;
-  const int c = blockIdx.x % a.nchunks;
-  const int T = a.T;
+  const int first = blockIdx.x;
+  if (first >= total) return;   // whole workgroup
+  MapRegs<IO> in;
+  map_load<IO>(in, a, first, tid);
+  for (int job = first; job < total; job += gridDim.x) {
+  const int c = job % a.nchunks;
   {
-    ChunkRegs<IO> r;
-    chunk_load<IO>(r, a, bh, c, tid);
-    Raw8<IO> odr;
-    const int orow = c * kBC + (tid >> 3);
-    odr.load(static_cast<const IO*>(a.dO) + (bh * T + (orow < T ? orow : T - 1)) * kD + (tid & 7) * 8);
-    chunk_store<IO>(cc, r, tid);
+    chunk_store<IO>(cc, in.r, tid);
     float od[8];
-    odr.get(od);
+    in.odr.get(od);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) od[k] = orow < T ? od[k] : 0.f;
+    for (int k = 0; k < 8; ++k) od[k] = in.olive ? od[k] : 0.f;
     const int i = tid >> 3, f0 = (tid & 7) * 8;
     *reinterpret_cast<float4*>(&DO[i][f0]) = make_float4(od[0], od[1], od[2], od[3]);
     *reinterpret_cast<float4*>(&DO[i][f0 + 4]) = make_float4(od[4], od[5], od[6], od[7]);
   }
   __syncthreads();
-  chunk_forward<kThreads>(cc, a, c, tid, w, l);
-  chunk_factors<kThreads>(cc, TZ, tid, w, l);
+  // the next chunk's inputs (this chunk's again after the last one)
+  map_load<IO>(in, a, job + int(gridDim.x) < total ? job + int(gridDim.x) : job, tid);
+  chunk_forward(cc, a, c, tid, w, l);
+  chunk_factors(cc, TZ, tid, w, l);
   {
     // W, U, T and the gates for the chunk kernel
-    float* fo = a.fac + int64_t(blockIdx.x) * kFacFloats;
+    float* fo = a.fac + int64_t(job) * kFacFloats;
     for (int q = tid; q < 512; q += kThreads) {
       const int i = q >> 4, f = 4 * (q & 15);
       reinterpret_cast<float4*>(fo + kFacW)[q] = *reinterpret_cast<const float4*>(&cc.W[i][f]);
@@ -524,7 +530,7 @@ __global__ void __launch_bounds__(kThreads) falcon1_bwd_maps_kernel(BwdArgs a) {
   // P^T = e^G I - W^T Diag(e^{G-g}) X, H = X^T Diag(e^{G-g}) U and
   // G^T = dO^T Qt, each written straight from the accumulators: the tile
   // (tm, tn) of a wave is one 1 KiB run of its map.
-  float* out = a.maps + int64_t(blockIdx.x) * kMapFloats;
+  float* out = a.maps + int64_t(job) * kMapFloats;
   const float eG = __expf(cc.G);
   auto xs = [&](int t) { return __expf(cc.G - cc.g[t]); };
   auto one = [](int) { return 1.f; };
@@ -561,6 +567,8 @@ __global__ void __launch_bounds__(kThreads) falcon1_bwd_maps_kernel(BwdArgs a) {
       put(out + kOffHD, (tm * 4 + tn) * 64 + l, fh.acc[it]);
       put(out + kOffGD, (tn * 4 + tm) * 64 + l, fg.acc[it]);
     }
+  }
+  __syncthreads();   // LDS is refilled for the next chunk
   }
 }
 
@@ -1186,12 +1194,14 @@ hipError_t launch_bwd(const ProblemArgs& p, const BwdBuffers& b, hipStream_t st)
     ncu = 256;
   const int jobs = int(n);
   const unsigned chunk_blocks = unsigned(jobs < ncu ? jobs : ncu);
+  // two maps workgroups per CU (LDS)
+  const unsigned map_blocks = unsigned(jobs < 2 * ncu ? jobs : 2 * ncu);
   if (p.bf16) {
-    hipLaunchKernelGGL(falcon1_bwd_maps_kernel<bf16_t>, dim3(unsigned(n)), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(falcon1_bwd_maps_kernel<bf16_t>, dim3(map_blocks), dim3(kThreads), 0, st, a, jobs);
     hipLaunchKernelGGL(falcon1_bwd_chain_kernel<bf16_t>, dim3(chain_blocks), dim3(kThreads), 0, st, a, nunits);
     hipLaunchKernelGGL(falcon1_bwd_chunk_kernel<bf16_t>, dim3(chunk_blocks), dim3(kThreads3), 0, st, a, jobs);
   } else {
-    hipLaunchKernelGGL(falcon1_bwd_maps_kernel<float>, dim3(unsigned(n)), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(falcon1_bwd_maps_kernel<float>, dim3(map_blocks), dim3(kThreads), 0, st, a, jobs);
     hipLaunchKernelGGL(falcon1_bwd_chain_kernel<float>, dim3(chain_blocks), dim3(kThreads), 0, st, a, nunits);
     hipLaunchKernelGGL(falcon1_bwd_chunk_kernel<float>, dim3(chunk_blocks), dim3(kThreads3), 0, st, a, jobs);
   }

@@ -25,7 +25,9 @@ def _masked_mfmas(asm: str):
     lines = asm.split("\n")
     for i, line in enumerate(lines):
         if re.match(r"^_Z\S+:", line):
+            # a new function starts unmasked
             fn = line.split(":")[0]
+            masked, skipped = False, False
         s = line.strip()
         if re.match(r"s_(and|andn2|xor|or)_saveexec", s):
             masked = True
