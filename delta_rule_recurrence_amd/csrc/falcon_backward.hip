@@ -751,7 +751,7 @@ falcon1_bwd_chain_kernel(BwdArgs a, int nunits) {
 }
 
 // ---- launch 3: reverse mode through one chunk ----------------------------------
-// Eight waves: the chunk's LDS (156 KB) allows one workgroup per CU, and a
+// Eight waves: the chunk's LDS (161 KB) allows one workgroup per CU, and a
 // single wave per SIMD issues fp32 MFMAs at two thirds of the rate two waves
 // reach, so two waves share each SIMD.
 constexpr int kThreads3 = 512;
@@ -783,8 +783,8 @@ __device__ __forceinline__ float sum16(float v) {
 }
 
 // This thread's share of one chunk's inputs, held as loaded.  Waves 0-3 take
-// the keys, queries, values and gates, waves 4-7 dO, all eight the state and
-// the adjoint.
+// the keys, queries and values, waves 4-7 dO, all eight the state, the
+// adjoint and W, U; the first 256 threads T and the gates.
 template <typename IO>
 struct GradRegs {
   ChunkRegs<IO> r;
