@@ -335,6 +335,40 @@ def oracle_sample(kind, budget_s=3.0):
     raise ValueError(kind)
 
 
+def measured_peaks():
+    """Achievable figures on this machine, next to the published peaks: a plain
+    2 GiB device-to-device copy (reads and writes each byte once) and square
+    GEMMs through torch (hipBLASLt) in bf16 and fp32."""
+    import torch
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+
+    nbytes = 1 << 31
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    t_copy = timed(lambda: b.copy_(a), 10)
+    del a, b
+    out = {"copy_gbs": 2 * nbytes / t_copy / 1e9}
+    for name, dt, n in (("bf16_gemm_tflops", torch.bfloat16, 8192), ("fp32_gemm_tflops", torch.float32, 4096)):
+        x = torch.randn(n, n, device="cuda", dtype=dt)
+        y = torch.randn(n, n, device="cuda", dtype=dt)
+        t = timed(lambda: torch.mm(x, y), 10)
+        out[name] = 2 * n ** 3 / t / 1e12
+        del x, y
+    out["note"] = ("copy = 2 x bytes / time; GEMMs through torch.mm (hipBLASLt), "
+                   "bf16 8192^3 and fp32 4096^3")
+    return out
+
+
 def calibrate_copy(nbytes=1 << 28, reps=5):
     """A plain device copy of known size, for scaling rocprofv3 FETCH_SIZE /
     WRITE_SIZE counters (each copy reads and writes nbytes once)."""
@@ -460,12 +494,16 @@ def main():
                      "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes": bytes_alg, "kernel_ms": ev_ms, "kernels": STEP_KERNELS},
     }
+    line["measured_peaks"] = measured_peaks()
+    line["roofline"]["frac_of_measured_copy"] = achieved_gbs / line["measured_peaks"]["copy_gbs"]
     if not args.no_decode:
         line["decode"] = bench_decode()
     if not args.no_extra:
         line["f1a_chunked"] = bench_chunked_workload("f1a_chunked_2x12x16384_d64")
         line["f2_chunked"] = bench_chunked_workload("f2_chunked_8x12x2048_d64", steps=5, warmup=1)
         line["f1_backward"] = bench_backward()
+        rb = line["f1_backward"]["roofline"]
+        rb["frac_of_measured_fp32_gemm"] = rb["achieved"] / line["measured_peaks"]["fp32_gemm_tflops"]
         line["f1_recurrent"] = bench_recurrent()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(d, w, o, S_T)
