@@ -154,3 +154,17 @@ def test_backward_full_workload_sampled():
         gsub = {k: (None if v is None else v[b:b + 1, h:h + 1]) for k, v in got.items()}
         errs = compare(gsub, ref, f"full workload (b={b}, h={h})")
         print((b, h), {k: f"{v:.2e}" for k, v in errs.items()})
+
+
+def test_backward_long_single_sequence():
+    """One sequence of 4130 tokens: 130 chunks (the chain ring's last group is
+    partial), a single workgroup per chain, the persistent kernels' grids
+    larger than the work."""
+    B, H, T = 1, 1, 4130
+    d = I.make_inputs(B, H, T, 64, 64, seed=81, io_dtype="bf16")
+    cot = I.make_cotangents(B, H, T, 64, seed=81, io_dtype="bf16", with_state=True)
+    S0 = I.random_state((B, H, 64, 64), seed=82)
+    ref = oracle_grads(d, cot, S0=S0)
+    got = gpu_grads(d, cot, S0=S0)
+    errs = compare(got, ref, "long single sequence")
+    print({k: f"{v:.2e}" for k, v in errs.items()})
