@@ -47,14 +47,15 @@ constexpr int kGP = 68;                     // float row pitch of the Gram buffe
 struct PcSmem {
   uint16_t x[kC * kD];                      // keys phi(k_{t0+r-1}), swizzled rows
   uint16_t q[kC * kD];                      // queries, swizzled rows
-  float kq[kC][kGP];                        // [i][s] = x_i . x_s (s <= i written)
-  float pq[kC][kGP];                        // [i][s] = q_i . x_s (s <= i written)
+  float kq[kC][kGP];                        // [i][s] = x_i . x_s for s < i, 0 for i <= s < 16(i/16 + 1)
+  float pq[kC][kGP];                        // [i][s] = q_i . x_s for s < i, 0 for i <= s < 16(i/16 + 1)
   float xs[kC][kSlice];                     // (X S)_{i,j}
   float qs[kC][kSlice];                     // (Q S)_{i,j}
   float vb[kC][kSlice];                     // v_{i,j}
   float bt[kC][kSlice];                     // beta_{i,j}
   float lm[kC];                             // lam_i
   float en[kC];                             // ||x_i||^2
+  float pd[kC];                             // q_i . x_i
   float w[kSlice][kC];                      // per column: e^{g_b-g_s} rho_s, b = end of the last solved block
   float e63[kSlice];                        // e^{g_63} per column
   uint16_t ob[kC][kSlice];                  // outputs of the chunk, bf16
@@ -68,6 +69,19 @@ __device__ __forceinline__ float row_bcast(float v) {
 }
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 constexpr float kLog2e = 1.4426950408889634f;
+
+// log2 of the clamped decay 1 - min(eta lam, 1 - eps_gamma) (Section 4.3) in
+// float32, as log2(u) (1 - gamma) / (1 - u) with u = 1 - alpha rounded: the
+// ratio cancels the rounding of u (Kahan's compensated log1p), so small alpha
+// keeps its relative accuracy; log2 and the reciprocal are the hardware's.
+// Also returns gamma itself (u).
+__device__ __forceinline__ float log2_gamma(float eta, float lam, float eps_gamma, float& gamma) {
+  const float alpha = fminf(eta * lam, 1.0f - eps_gamma);
+  const float u = 1.0f - alpha;
+  const float d = u - 1.0f;
+  gamma = u;
+  return d == 0.0f ? -kLog2e * alpha : __builtin_amdgcn_logf(u) * (-alpha * __builtin_amdgcn_rcpf(d));
+}
 
 // The next chunk's inputs, fetched into registers during the current chunk.
 struct ChunkRegs {
@@ -131,8 +145,12 @@ __device__ __forceinline__ void solve_block(PcSmem& sm, int jl, int li, int t0, 
   const bool live = t < T;
   // step size and decay of row i in column jl; g by a scan over the 16 rows
   const float den = sm.en[i] + sm.lm[i] + eps;
-  const float eta = (live && !(fresh && t == 0) && den != 0.0f) ? sm.bt[i][jl] / den : 0.0f;
-  const float lg = live ? kLog2e * clamped_log_gamma(eta, sm.lm[i], eps_gamma) : 0.0f;
+  const float eta =
+      (live && !(fresh && t == 0) && den != 0.0f) ? sm.bt[i][jl] * __builtin_amdgcn_rcpf(den) : 0.0f;
+  float gam;
+  const float lg0 = log2_gamma(eta, sm.lm[i], eps_gamma, gam);
+  const float lg = live ? lg0 : 0.0f;
+  gam = live ? gam : 1.0f;
   float gi = lg;
   gi += row_shr<1>(gi);
   gi += row_shr<2>(gi);
@@ -146,27 +164,44 @@ __device__ __forceinline__ void solve_block(PcSmem& sm, int jl, int li, int t0, 
   float a = kReg ? eta * (sm.vb[i][jl] - exp2_fast(gprev) * sm.xs[i][jl]) : eta * sm.vb[i][jl];
   float o = exp2_fast(gi) * sm.qs[i][jl];
   if constexpr (B > 0) {
-    float pk = 0.f, pp = 0.f;
+    float pk0 = 0.f, pk1 = 0.f, pp0 = 0.f, pp1 = 0.f;
 #pragma unroll
     for (int s4 = 0; s4 < 4 * B; ++s4) {
       const f32x4 w4 = ld4(&sm.w[jl][4 * s4]);
       const f32x4 p4 = ld4(&sm.pq[i][4 * s4]);
-      pp += p4[0] * w4[0] + p4[1] * w4[1] + p4[2] * w4[2] + p4[3] * w4[3];
+      pp0 = fmaf(p4[0], w4[0], pp0);
+      pp1 = fmaf(p4[1], w4[1], pp1);
+      pp0 = fmaf(p4[2], w4[2], pp0);
+      pp1 = fmaf(p4[3], w4[3], pp1);
       if constexpr (kReg) {
         const f32x4 k4 = ld4(&sm.kq[i][4 * s4]);
-        pk += k4[0] * w4[0] + k4[1] * w4[1] + k4[2] * w4[2] + k4[3] * w4[3];
+        pk0 = fmaf(k4[0], w4[0], pk0);
+        pk1 = fmaf(k4[1], w4[1], pk1);
+        pk0 = fmaf(k4[2], w4[2], pk0);
+        pk1 = fmaf(k4[3], w4[3], pk1);
       }
     }
-    if constexpr (kReg) a -= eta * exp2_fast(gprev - gcarry) * pk;
-    o += exp2_fast(gi - gcarry) * pp;
+    if constexpr (kReg) a -= eta * exp2_fast(gprev - gcarry) * (pk0 + pk1);
+    o += exp2_fast(gi - gcarry) * (pp0 + pp1);
   }
-  // in-block decays e^{g_{i-1}-g_s} for s = 16B + sl < i
-  float ed[16];
-  ed[15] = 0.f;
-  // (the broadcast is taken in every lane; entries s >= i are selected away)
-#define FALCON_ED(SL) { const float gs = row_bcast<SL>(gi); const float e = exp2_fast(gprev - gs); ed[SL] = (SL) < li ? e : 0.0f; }
-  FALCON_ED(0) FALCON_ED(1) FALCON_ED(2) FALCON_ED(3) FALCON_ED(4) FALCON_ED(5) FALCON_ED(6) FALCON_ED(7)
-  FALCON_ED(8) FALCON_ED(9) FALCON_ED(10) FALCON_ED(11) FALCON_ED(12) FALCON_ED(13) FALCON_ED(14)
+  // in-block decays e^{g_{i-1}-g_s} = gamma_{s+1} ... gamma_{i-1} for
+  // s = 16B + sl < i, as a suffix product over sl with gamma_{sl+1} taken from
+  // lane sl + 1 by the DPP operand of the multiply; for s >= i - 1 the product
+  // restarts at 1 (the Gram entries are 0 for s >= i, and every factor stays
+  // in [0, 1]).  The leading s_nop covers the DPP read-after-write hazard on
+  // gam.
+  float ed[15];
+  ed[14] = 1.0f;
+#define FALCON_ED(SL, NOP)                                                                       \
+  {                                                                                              \
+    float p;                                                                                     \
+    asm volatile(NOP "v_mul_f32_dpp %0, %1, %2 row_newbcast:" #SL " row_mask:0xf bank_mask:0xf" \
+                 : "=v"(p) : "v"(gam), "v"(ed[SL]));                                             \
+    ed[SL - 1] = (SL) < li ? p : 1.0f;                                                           \
+  }
+  FALCON_ED(14, "s_nop 1\n\t") FALCON_ED(13, "") FALCON_ED(12, "") FALCON_ED(11, "") FALCON_ED(10, "")
+  FALCON_ED(9, "") FALCON_ED(8, "") FALCON_ED(7, "") FALCON_ED(6, "") FALCON_ED(5, "") FALCON_ED(4, "")
+  FALCON_ED(3, "") FALCON_ED(2, "") FALCON_ED(1, "")
 #undef FALCON_ED
   float kr[16], pr[16];
 #pragma unroll
@@ -196,7 +231,7 @@ __device__ __forceinline__ void solve_block(PcSmem& sm, int jl, int li, int t0, 
   }
   const float rho = a;
   // in-block part of the read: e^{g_i-g_s} = gamma_i e^{g_{i-1}-g_s} for s < i
-  // (ed is 0 for s >= i), and the diagonal term q_i.x_i rho_i
+  // (the Gram entries are 0 for s >= i), and the diagonal term q_i.x_i rho_i
   {
     float o0 = 0.f, o1 = 0.f;
 #define FALCON_RD(SL, ACC)                                                                              \
@@ -209,7 +244,7 @@ __device__ __forceinline__ void solve_block(PcSmem& sm, int jl, int li, int t0, 
     FALCON_RD(6, o0) FALCON_RD(7, o1) FALCON_RD(8, o0) FALCON_RD(9, o1) FALCON_RD(10, o0) FALCON_RD(11, o1)
     FALCON_RD(12, o0) FALCON_RD(13, o1) FALCON_RD(14, o0)
 #undef FALCON_RD
-    o += exp2_fast(lg) * (o0 + o1) + sm.pq[i][i] * rho;
+    o += exp2_fast(lg) * (o0 + o1) + sm.pd[i] * rho;
   }
   sm.ob[i][jl] = bf(o);
   // w to the end of this block: earlier entries decay by e^{g_last-g_carry},
@@ -295,12 +330,18 @@ falcon2_chunked_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restric
         dk = mfma32(ring_frag_c(sm.x, 16 * ib + c16, 1, g), xs1, dk);
         f32x4 dp = mfma32(ring_frag_c(sm.q, 16 * ib + c16, 0, g), xs0, zero4());
         dp = mfma32(ring_frag_c(sm.q, 16 * ib + c16, 1, g), xs1, dp);
+        // a diagonal tile keeps its strict lower triangle only (the solve
+        // reads it without a mask); its diagonal goes to en and pd
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = 16 * ib + 4 * g + r;
-          sm.kq[i][16 * sb + c16] = dk[r];
-          sm.pq[i][16 * sb + c16] = dp[r];
-          if (ib == sb && 4 * g + r == c16) sm.en[i] = dk[r];
+          const bool upper = ib == sb && c16 >= 4 * g + r;
+          sm.kq[i][16 * sb + c16] = upper ? 0.0f : dk[r];
+          sm.pq[i][16 * sb + c16] = upper ? 0.0f : dp[r];
+          if (ib == sb && 4 * g + r == c16) {
+            sm.en[i] = dk[r];
+            sm.pd[i] = dp[r];
+          }
         }
       }
     }
