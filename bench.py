@@ -52,6 +52,17 @@ def algorithmic_flops(B, H, T, dk, dv, C):
     return B * H * T * per
 
 
+FP32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector, published (packed fp32 issue)
+
+
+def recurrence_flops(B, H, T, dk, dv):
+    """Arithmetic the per-column rules (Falcon-2 / 2A) cannot avoid, per
+    token-head: the residual read S^T x (2 dk dv), the decayed rank-1 write
+    gamma_j S + x (eta_j r_j) (3 dk dv: a multiply and a multiply-add per
+    element) and the output read S^T q (2 dk dv)."""
+    return 7.0 * B * H * T * dk * dv
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
@@ -154,9 +165,22 @@ def bench_chunked_workload(name, steps=20, warmup=3):
     nbytes = algorithmic_bytes(w.B, w.H, w.T, w.dk, w.dv,
                                per_column_beta=w.variant in ("falcon2", "falcon2a"))
     gbs = nbytes / (ms * 1e-3) / 1e9
-    return {"workload": name, "variant": w.variant, "steps": steps, "us_per_step": ms * 1e3,
-            "tokens_per_s": w.B * w.T / (ms * 1e-3), "algorithmic_bytes": nbytes,
-            "workspace_bytes": int(ws.numel()), "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
+    out = {"workload": name, "variant": w.variant, "steps": steps, "us_per_step": ms * 1e3,
+           "tokens_per_s": w.B * w.T / (ms * 1e-3), "algorithmic_bytes": nbytes,
+           "workspace_bytes": int(ws.numel()), "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
+    if w.variant in ("falcon2", "falcon2a"):
+        # per-column systems: bound by vector-ALU issue, not by bytes
+        flops = recurrence_flops(w.B, w.H, w.T, w.dk, w.dv)
+        tf = flops / (ms * 1e-3) / 1e12
+        out["roofline"] = {"bound": "alu", "achieved": tf, "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": tf / FP32_VALU_PEAK_TFLOPS, "traffic": None, "algorithmic_flops": flops,
+                           "kernels": ["falcon2_chunked_kernel"]}
+    elif w.variant == "falcon1a":
+        out["roofline"] = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": gbs / HBM_PEAK_GBS, "traffic": None, "algorithmic_bytes": nbytes,
+                           "kernels": ["falcon1a_tile_kernel<false>", "falcon1a_tile_scan_kernel",
+                                       "falcon1a_tile_kernel<true>"]}
+    return out
 
 
 def bench_recurrent(name="f1_chunked_8x12x2048_d64", steps=5, warmup=1):

@@ -264,14 +264,19 @@ falcon2_chunked_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restric
                        const bf16_t* __restrict__ v, const float* __restrict__ beta,
                        const float* __restrict__ lam, const float* S0,
                        const bf16_t* __restrict__ k_prev, bf16_t* __restrict__ o, float* S_T, int T,
-                       float eps, float eps_gamma) {
+                       int64_t BH, float eps, float eps_gamma) {
   __shared__ PcSmem sm;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;   // wave-uniform
   const int g = l >> 4, c16 = l & 15;
   const int jl = 4 * w + g, li = c16;                 // solve layout: column jl of the slice, block row li
-  const int64_t bh = blockIdx.x >> 2;
-  const int j0 = (blockIdx.x & 3) * kSlice;
+  // the four slices of a sequence are workgroups b, b + 8, b + 16, b + 24:
+  // consecutive workgroups go to different XCDs, so these share one XCD and
+  // its L2, and the keys and queries that every slice reads come from HBM once
+  const int b = blockIdx.x;
+  const int64_t bh = int64_t(b / 32) * 8 + b % 8;
+  const int j0 = ((b / 8) & 3) * kSlice;
+  if (bh >= BH) return;
   const bool fresh = (k_prev == nullptr);
   const bf16_t* K = phi_k + bh * T * kD;
   const bf16_t* Q = phi_q + bh * T * kD;
@@ -402,18 +407,19 @@ bool chunked_percol_applies(const ProblemArgs& a) {
 }
 
 hipError_t launch_chunked_percol(const ProblemArgs& a, hipStream_t st) {
-  const dim3 grid(unsigned(int64_t(a.B) * a.H * (kD / kSlice)));
+  const int64_t BH = int64_t(a.B) * a.H;
+  const dim3 grid(unsigned((BH + 7) / 8 * 8 * (kD / kSlice)));
   if (a.variant == kF2)
     hipLaunchKernelGGL(falcon2_chunked_kernel<true>, grid, dim3(kThreads), 0, st,
                        static_cast<const bf16_t*>(a.phi_k), static_cast<const bf16_t*>(a.phi_q),
                        static_cast<const bf16_t*>(a.v), a.beta, a.lam, a.S0,
-                       static_cast<const bf16_t*>(a.k_prev), static_cast<bf16_t*>(a.o), a.S_T, a.T, a.eps,
+                       static_cast<const bf16_t*>(a.k_prev), static_cast<bf16_t*>(a.o), a.S_T, a.T, BH, a.eps,
                        a.eps_gamma);
   else
     hipLaunchKernelGGL(falcon2_chunked_kernel<false>, grid, dim3(kThreads), 0, st,
                        static_cast<const bf16_t*>(a.phi_k), static_cast<const bf16_t*>(a.phi_q),
                        static_cast<const bf16_t*>(a.v), a.beta, a.lam, a.S0,
-                       static_cast<const bf16_t*>(a.k_prev), static_cast<bf16_t*>(a.o), a.S_T, a.T, a.eps,
+                       static_cast<const bf16_t*>(a.k_prev), static_cast<bf16_t*>(a.o), a.S_T, a.T, BH, a.eps,
                        a.eps_gamma);
   return hipGetLastError();
 }
