@@ -4,7 +4,7 @@
 // one pass over their inputs.  Thread layout: a thread owns 16 consecutive
 // state rows of one value column (recurrent) or of four value columns
 // (decode); the dk/16 threads that share a column reduce their partial dot
-// products with cross-lane shuffles (recurrent) or through LDS (decode).
+// products with DPP lane moves (recurrent) or through LDS (decode).
 //
 // Paper: "Fast Weight Attention for Continual Learning", Section 4 naming and
 // formula summary (the rules), Eq. (3.4) (step size), Section 4.3 "Decay
@@ -20,116 +20,221 @@ namespace {
 
 constexpr int kRows = 16;  // state rows held by one thread
 
-template <typename IO>
-__device__ __forceinline__ void load16(const IO* p, float out[kRows]) {
-#pragma unroll
-  for (int i = 0; i < kRows; ++i) out[i] = io<IO>::load(p, i);
-}
-template <>
-__device__ __forceinline__ void load16<bf16_t>(const bf16_t* p, float out[kRows]) {
-  const uint4* q = reinterpret_cast<const uint4*>(p);
-  const uint4 a = q[0], b = q[1];
-  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    out[2 * i] = __uint_as_float(w[i] << 16);
-    out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-  }
-}
-template <>
-__device__ __forceinline__ void load16<float>(const float* p, float out[kRows]) {
-  const float4* q = reinterpret_cast<const float4*>(p);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float4 a = q[i];
-    out[4 * i] = a.x; out[4 * i + 1] = a.y; out[4 * i + 2] = a.z; out[4 * i + 3] = a.w;
-  }
-}
-
-__device__ __forceinline__ float group_sum(float v, int rs) {
-  for (int m = 1; m < rs; m <<= 1) v += __shfl_xor(v, m);
+// Sum over the RS consecutive lanes that share a value column.
+template <int RS>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (RS >= 2)    // lanes l ^ 1: quad_perm [1, 0, 3, 2]
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xb1, 0xf, 0xf, false));
+  if constexpr (RS >= 4)    // lanes l ^ 2: quad_perm [2, 3, 0, 1]
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4e, 0xf, 0xf, false));
+  if constexpr (RS >= 8) v += __shfl_xor(v, 4);
   return v;
 }
 
-// One workgroup per (b*h, value-column tile).  blockDim.x = ncols * rs with
-// rs = dk / 16; thread tid = col * rs + r owns rows [16 r, 16 r + 16) of
-// column col of the tile.
-template <typename IO, int VARIANT>
+// ---- recurrent form ----------------------------------------------------------
+// One workgroup per (b*h, value-column tile) with NCOLS * RS threads, RS =
+// dk / 16: thread tid = col * RS + r owns rows [16 r, 16 r + 16) of column col
+// of the tile.  The inputs come through LDS in blocks of 32 (or 16) tokens:
+// while a block is swept, the next one is loaded straight from global memory
+// into the other LDS buffer (direct-to-LDS loads, 16 bytes per lane), so no step waits
+// for global memory; after a block lands, one pass computes the energies
+// ||x_t||^2 of its tokens.  The per-step work is then the state's dot
+// products and update, with the cross-lane sums in DPP.
+
+// Tokens per staged block: 32, or 16 for rows of 256 bytes and more, so the
+// two buffers stay within 64 KB of LDS.
+__host__ __device__ constexpr int block_tokens(int dk, int io_bytes) { return dk * io_bytes >= 256 ? 16 : 32; }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Byte layout of one LDS buffer of tc tokens (every part a multiple of 16 bytes).
+struct RecLayout {
+  int x, q, v, b, l, e, bytes;
+  __host__ __device__ RecLayout(int tc, int dk, int ncols, int io_bytes, bool per_col) {
+    x = 0;
+    q = x + tc * dk * io_bytes;
+    v = q + tc * dk * io_bytes;
+    b = v + tc * ncols * io_bytes;
+    l = b + tc * (per_col ? ncols : 1) * 4;
+    e = l + tc * 4;
+    bytes = e + tc * 4;
+  }
+};
+
+// Direct-to-LDS staging: lane l of an instruction writes bytes
+// [16 l, 16 l + 16) (or [4 l, 4 l + 4)) after the wave-uniform LDS address.
+// `wl` lanes per wave (the whole block when it is smaller than a wave) and
+// `nw` waves cover the units in turn.
+//
+// Rows [0, tc) of a slab whose row t starts at base + row_of(t) * stride,
+// row_bytes each (a multiple of 16), into dense LDS rows at dst.  Rows past
+// the sequence read a valid row (row_of clamps); their values are never used.
+template <typename RowOf>
+__device__ __forceinline__ void stage_rows(char* dst, const char* base, int64_t stride_bytes, int row_bytes,
+                                           int tc, RowOf row_of, int wave, int nw, int wl, int lane) {
+  const int per_row = row_bytes / 16;
+  const int units = tc * per_row;
+  for (int u0 = wl * wave; u0 < units; u0 += wl * nw) {
+    const int u = u0 + lane;
+    const int t = u / per_row, piece = u - t * per_row;
+    const char* src = base + row_of(t) * stride_bytes + piece * 16;
+    if (u < units) __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + 16 * u0), 16, 0, 0);
+  }
+}
+// One 4-byte value per row (the per-token gates).
+template <typename RowOf>
+__device__ __forceinline__ void stage_words(char* dst, const char* base, int64_t stride_bytes, int tc,
+                                            RowOf row_of, int wave, int nw, int wl, int lane) {
+  for (int u0 = wl * wave; u0 < tc; u0 += wl * nw) {
+    const int u = u0 + lane;
+    if (u < tc) __builtin_amdgcn_global_load_lds(base + row_of(u) * stride_bytes, (lds_void*)(dst + 4 * u0), 4, 0, 0);
+  }
+}
+
+template <typename IO>
+__device__ __forceinline__ void lds16(const char* p, float out[kRows]) {
+  if constexpr (sizeof(IO) == 2) {
+    const uint4 a = *reinterpret_cast<const uint4*>(p), b = *reinterpret_cast<const uint4*>(p + 16);
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      out[2 * i] = __uint_as_float(w[i] << 16);
+      out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 a = reinterpret_cast<const float4*>(p)[i];
+      out[4 * i] = a.x; out[4 * i + 1] = a.y; out[4 * i + 2] = a.z; out[4 * i + 3] = a.w;
+    }
+  }
+}
+template <typename IO>
+__device__ __forceinline__ float lds1(const char* p, int i) {
+  if constexpr (sizeof(IO) == 2) return __uint_as_float(uint32_t(reinterpret_cast<const uint16_t*>(p)[i]) << 16);
+  else return reinterpret_cast<const float*>(p)[i];
+}
+
+template <typename IO, int VARIANT, int RS>
 __global__ void __launch_bounds__(512)
 recurrent_kernel(const IO* __restrict__ phi_k, const IO* __restrict__ phi_q,
                  const IO* __restrict__ v, const float* __restrict__ beta,
                  const float* __restrict__ lam, const float* S0, const IO* __restrict__ k_prev,
-                 IO* __restrict__ o, float* S_T, int T, int dk, int dv, float eps,
-                 float eps_gamma) {
-  const int rs = dk / kRows;
-  const int ncols = blockDim.x / rs;
-  const int r = threadIdx.x % rs;
-  const int col = blockIdx.y * ncols + threadIdx.x / rs;
+                 IO* __restrict__ o, float* S_T, int T, int dv, float eps, float eps_gamma) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int dk = RS * kRows;
+  constexpr int io_bytes = sizeof(IO);
+  constexpr bool per_col = is_per_column(VARIANT);
+  constexpr int tc = block_tokens(dk, io_bytes);
+  const int ncols = blockDim.x / RS;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int nw = (blockDim.x + 63) >> 6;
+  const int wl = blockDim.x < 64 ? blockDim.x : 64;
+  const int r = tid % RS;
+  const int cl = tid / RS;                          // column within the tile
+  const int col0 = blockIdx.y * ncols;
+  const int col = col0 + cl;
   const int64_t bh = blockIdx.x;
-  const IO* K = phi_k + bh * T * dk + r * kRows;
-  const IO* Q = phi_q + bh * T * dk + r * kRows;
-  const IO* V = v + bh * T * dv + col;
-  const float* Lm = lam + bh * T;
-  const float* Bt = beta + (is_per_column(VARIANT) ? bh * T * dv + col : bh * T);
-  const int bstride = is_per_column(VARIANT) ? dv : 1;
+  const RecLayout L(tc, dk, ncols, io_bytes, per_col);
+  const bool fresh = (k_prev == nullptr);
 
   float S[kRows];
 #pragma unroll
   for (int i = 0; i < kRows; ++i)
     S[i] = S0 ? S0[(bh * dk + r * kRows + i) * dv + col] : 0.0f;
 
-  const bool fresh = (k_prev == nullptr);
-  float x[kRows], q[kRows];
-  if (fresh) {
-#pragma unroll
-    for (int i = 0; i < kRows; ++i) x[i] = 0.0f;
-  } else {
-    load16<IO>(k_prev + bh * dk + r * kRows, x);
-  }
-  load16<IO>(Q, q);
-  float vt = io<IO>::load(V, 0), bt = Bt[0], lt = Lm[0];
+  const char* Kb = reinterpret_cast<const char*>(phi_k + bh * int64_t(T) * dk);
+  const char* Qb = reinterpret_cast<const char*>(phi_q + bh * int64_t(T) * dk);
+  const char* Vb = reinterpret_cast<const char*>(v + bh * int64_t(T) * dv + col0);
+  const char* Bb = reinterpret_cast<const char*>(beta + (per_col ? bh * int64_t(T) * dv + col0 : bh * int64_t(T)));
+  const char* Lb = reinterpret_cast<const char*>(lam + bh * int64_t(T));
+  const char* KP = k_prev ? reinterpret_cast<const char*>(k_prev + bh * dk) : nullptr;
 
-  for (int t = 0; t < T; ++t) {
-    // Prefetch step t+1 (its key is this step's k_t).
-    float xn[kRows], qn[kRows];
-    float vn = 0.f, bn = 0.f, ln = 0.f;
-    const bool more = (t + 1 < T);
-    if (more) {
-      load16<IO>(K + int64_t(t) * dk, xn);
-      load16<IO>(Q + int64_t(t + 1) * dk, qn);
-      vn = io<IO>::load(V, int64_t(t + 1) * dv);
-      bn = Bt[int64_t(t + 1) * bstride];
-      ln = Lm[t + 1];
+  // block j's inputs into buffer j & 1
+  auto stage = [&](int j) {
+    char* buf = smem + (j & 1) * L.bytes;
+    const int t0 = j * tc;
+    auto tok = [&](int t) { const int g = t0 + t; return int64_t(g < T ? g : T - 1); };
+    // x_t = phi(k_{t-1}); x_0 is the previous key, or (fresh start, step size
+    // 0) any valid row
+    {
+      const int per_row = dk * io_bytes / 16;
+      const int units = tc * per_row;
+      for (int u0 = wl * wave; u0 < units; u0 += wl * nw) {
+        const int u = u0 + lane;
+        const int t = u / per_row, piece = u - t * per_row;
+        const int g = t0 + t - 1;
+        const char* src = (g < 0 && KP) ? KP + piece * 16
+                                        : Kb + int64_t(g < 0 ? 0 : (g < T ? g : T - 1)) * dk * io_bytes + piece * 16;
+        if (u < units) __builtin_amdgcn_global_load_lds(src, (lds_void*)(buf + L.x + 16 * u0), 16, 0, 0);
+      }
     }
+    stage_rows(buf + L.q, Qb, int64_t(dk) * io_bytes, dk * io_bytes, tc, tok, wave, nw, wl, lane);
+    stage_rows(buf + L.v, Vb, int64_t(dv) * io_bytes, ncols * io_bytes, tc, tok, wave, nw, wl, lane);
+    if constexpr (per_col) stage_rows(buf + L.b, Bb, int64_t(dv) * 4, ncols * 4, tc, tok, wave, nw, wl, lane);
+    else stage_words(buf + L.b, Bb, 4, tc, tok, wave, nw, wl, lane);
+    stage_words(buf + L.l, Lb, 4, tc, tok, wave, nw, wl, lane);
+  };
 
-    float e = 0.f;
+  const int nblocks = (T + tc - 1) / tc;
+  if (nblocks > 0) stage(0);
+  for (int j = 0; j < nblocks; ++j) {
+    char* buf = smem + (j & 1) * L.bytes;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's loads of block j have landed
+    __syncthreads();                                   // all of block j landed; block j - 1 is done
+    if (j + 1 < nblocks) stage(j + 1);
+    // energies ||x_t||^2 of the block's tokens
+    for (int t = tid; t < tc; t += blockDim.x) {
+      float e = 0.f;
+      const char* xr = buf + L.x + t * dk * io_bytes;
 #pragma unroll
-    for (int i = 0; i < kRows; ++i) e = fmaf(x[i], x[i], e);
-    e = group_sum(e, rs);
-    const float eta = nlms_eta(bt, e, lt, eps, fresh && t == 0);
-    const float gamma = clamped_gamma(eta, lt, eps_gamma);
-
-    float target = vt;
-    if constexpr (is_regression(VARIANT)) {
-      float p = 0.f;
-#pragma unroll
-      for (int i = 0; i < kRows; ++i) p = fmaf(S[i], x[i], p);
-      target = vt - group_sum(p, rs);             // r_t = v_t - S_{t-1}^T x_t
+      for (int i = 0; i < dk; ++i) {
+        const float xv = lds1<IO>(xr, i);
+        e = fmaf(xv, xv, e);
+      }
+      reinterpret_cast<float*>(buf + L.e)[t] = e;
     }
-    const float w = eta * target;
-    float po = 0.f;
+    __syncthreads();
+    const int t0 = j * tc;
+    const int nt = T - t0 < tc ? T - t0 : tc;
+    for (int t = 0; t < nt; ++t) {
+      float x[kRows], q[kRows];
+      lds16<IO>(buf + L.x + (t * dk + r * kRows) * io_bytes, x);
+      lds16<IO>(buf + L.q + (t * dk + r * kRows) * io_bytes, q);
+      const float vt = lds1<IO>(buf + L.v, t * ncols + cl);
+      const float bt = reinterpret_cast<const float*>(buf + L.b)[per_col ? t * ncols + cl : t];
+      const float lt = reinterpret_cast<const float*>(buf + L.l)[t];
+      const float e = reinterpret_cast<const float*>(buf + L.e)[t];
+      const float eta = nlms_eta(bt, e, lt, eps, fresh && t0 + t == 0);
+      const float gamma = clamped_gamma(eta, lt, eps_gamma);
+      float target = vt;
+      if constexpr (is_regression(VARIANT)) {
+        float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
 #pragma unroll
-    for (int i = 0; i < kRows; ++i) {
-      S[i] = fmaf(gamma, S[i], w * x[i]);         // S_t = gamma S + eta x r^T
-      po = fmaf(S[i], q[i], po);
-    }
-    po = group_sum(po, rs);                       // o_t = S_t^T q_t
-    if (r == 0) io<IO>::store(o, (bh * T + t) * dv + col, po);
-
-    if (more) {
+        for (int i = 0; i < kRows; i += 4) {
+          p0 = fmaf(S[i], x[i], p0);
+          p1 = fmaf(S[i + 1], x[i + 1], p1);
+          p2 = fmaf(S[i + 2], x[i + 2], p2);
+          p3 = fmaf(S[i + 3], x[i + 3], p3);
+        }
+        target = vt - group_sum<RS>((p0 + p1) + (p2 + p3));   // r_t = v_t - S_{t-1}^T x_t
+      }
+      const float w = eta * target;
+      float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
 #pragma unroll
-      for (int i = 0; i < kRows; ++i) { x[i] = xn[i]; q[i] = qn[i]; }
-      vt = vn; bt = bn; lt = ln;
+      for (int i = 0; i < kRows; i += 4) {
+        S[i] = fmaf(gamma, S[i], w * x[i]);                 // S_t = gamma S + eta x r^T
+        S[i + 1] = fmaf(gamma, S[i + 1], w * x[i + 1]);
+        S[i + 2] = fmaf(gamma, S[i + 2], w * x[i + 2]);
+        S[i + 3] = fmaf(gamma, S[i + 3], w * x[i + 3]);
+        o0 = fmaf(S[i], q[i], o0);
+        o1 = fmaf(S[i + 1], q[i + 1], o1);
+        o2 = fmaf(S[i + 2], q[i + 2], o2);
+        o3 = fmaf(S[i + 3], q[i + 3], o3);
+      }
+      const float po = group_sum<RS>((o0 + o1) + (o2 + o3));  // o_t = S_t^T q_t
+      if (r == 0) io<IO>::store(o, (bh * T + t0 + t) * dv + col, po);
     }
   }
   if (S_T) {
@@ -229,17 +334,28 @@ decode_kernel(const IO* __restrict__ x_in, const IO* __restrict__ q_in,
   }
 }
 
-template <typename IO, int VARIANT>
-hipError_t launch_recurrent_t(const ProblemArgs& a, hipStream_t st) {
-  const int rs = a.dk / kRows;
+template <typename IO, int VARIANT, int RS>
+hipError_t launch_recurrent_rs(const ProblemArgs& a, hipStream_t st) {
   const int ncols = a.dv < 64 ? a.dv : 64;
-  dim3 grid(a.B * a.H, a.dv / ncols), block(ncols * rs);
-  hipLaunchKernelGGL((recurrent_kernel<IO, VARIANT>), grid, block, 0, st,
+  const RecLayout L(block_tokens(RS * kRows, int(sizeof(IO))), RS * kRows, ncols, int(sizeof(IO)),
+                    is_per_column(VARIANT));
+  dim3 grid(a.B * a.H, a.dv / ncols), block(ncols * RS);
+  hipLaunchKernelGGL((recurrent_kernel<IO, VARIANT, RS>), grid, block, size_t(2 * L.bytes), st,
                      static_cast<const IO*>(a.phi_k), static_cast<const IO*>(a.phi_q),
                      static_cast<const IO*>(a.v), a.beta, a.lam, a.S0,
-                     static_cast<const IO*>(a.k_prev), static_cast<IO*>(a.o), a.S_T, a.T,
-                     a.dk, a.dv, a.eps, a.eps_gamma);
+                     static_cast<const IO*>(a.k_prev), static_cast<IO*>(a.o), a.S_T, a.T, a.dv,
+                     a.eps, a.eps_gamma);
   return hipGetLastError();
+}
+
+template <typename IO, int VARIANT>
+hipError_t launch_recurrent_t(const ProblemArgs& a, hipStream_t st) {
+  switch (a.dk) {
+    case 16: return launch_recurrent_rs<IO, VARIANT, 1>(a, st);
+    case 32: return launch_recurrent_rs<IO, VARIANT, 2>(a, st);
+    case 64: return launch_recurrent_rs<IO, VARIANT, 4>(a, st);
+    default: return launch_recurrent_rs<IO, VARIANT, 8>(a, st);
+  }
 }
 
 template <typename IO, int VARIANT>
