@@ -18,28 +18,36 @@ namespace falcon {
 
 namespace {
 
-constexpr int kRows = 16;  // state rows held by one thread
+constexpr int kRows = 16;  // state rows held by one decode thread
 
-// Sum over the RS consecutive lanes that share a value column.
+// Sum over the RS consecutive lanes (RS <= 16, aligned) that share a value
+// column: lanes l ^ 1 and l ^ 2 by quad permutes; then, with every quad
+// holding its sum, the mirror inside 8 lanes pairs each quad with the other
+// one, and the mirror inside 16 lanes pairs the two halves.
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
 template <int RS>
 __device__ __forceinline__ float group_sum(float v) {
-  if constexpr (RS >= 2)    // lanes l ^ 1: quad_perm [1, 0, 3, 2]
-    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xb1, 0xf, 0xf, false));
-  if constexpr (RS >= 4)    // lanes l ^ 2: quad_perm [2, 3, 0, 1]
-    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4e, 0xf, 0xf, false));
-  if constexpr (RS >= 8) v += __shfl_xor(v, 4);
+  if constexpr (RS >= 2) v = dpp_add<0xb1>(v);    // quad_perm [1, 0, 3, 2]
+  if constexpr (RS >= 4) v = dpp_add<0x4e>(v);    // quad_perm [2, 3, 0, 1]
+  if constexpr (RS >= 8) v = dpp_add<0x141>(v);   // row_half_mirror
+  if constexpr (RS >= 16) v = dpp_add<0x140>(v);  // row_mirror
   return v;
 }
 
 // ---- recurrent form ----------------------------------------------------------
 // One workgroup per (b*h, value-column tile) with NCOLS * RS threads, RS =
-// dk / 16: thread tid = col * RS + r owns rows [16 r, 16 r + 16) of column col
-// of the tile.  The inputs come through LDS in blocks of 32 (or 16) tokens:
+// dk / 8: thread tid = col * RS + r owns rows [8 r, 8 r + 8) of column col of
+// the tile (two waves per SIMD at d = 64, so one hides the other's latency).  The inputs come through LDS in blocks of 32 (or 16) tokens:
 // while a block is swept, the next one is loaded straight from global memory
 // into the other LDS buffer (direct-to-LDS loads, 16 bytes per lane), so no step waits
-// for global memory; after a block lands, one pass computes the energies
-// ||x_t||^2 of its tokens.  The per-step work is then the state's dot
-// products and update, with the cross-lane sums in DPP.
+// for global memory.  After a block lands, one pass widens bf16 keys and
+// queries to float32 (one LDS region, read by the steps) and forms each
+// token's gates: eta_t and gamma_t, or for per-column gains 1 / (||x_t||^2 +
+// lam_t + eps) (0 where the step size is 0).  The per-step work is then the
+// state's dot products and update, with the cross-lane sums in DPP.
 
 // Tokens per staged block: 32, or 16 for rows of 256 bytes and more, so the
 // two buffers stay within 64 KB of LDS.
@@ -47,17 +55,23 @@ __host__ __device__ constexpr int block_tokens(int dk, int io_bytes) { return dk
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Byte layout of one LDS buffer of tc tokens (every part a multiple of 16 bytes).
+// Byte layout of one LDS buffer of tc tokens (every part a multiple of 16
+// bytes), and of the float32 keys and queries of the block being swept
+// (bf16 inputs only), which follow the two buffers.
 struct RecLayout {
-  int x, q, v, b, l, e, bytes;
+  int x, q, v, b, l, g, bytes;           // g: per token (eta, gamma), or (1 / (||x||^2 + lam + eps), -)
+  int xf, qf, total;
   __host__ __device__ RecLayout(int tc, int dk, int ncols, int io_bytes, bool per_col) {
     x = 0;
     q = x + tc * dk * io_bytes;
     v = q + tc * dk * io_bytes;
     b = v + tc * ncols * io_bytes;
     l = b + tc * (per_col ? ncols : 1) * 4;
-    e = l + tc * 4;
-    bytes = e + tc * 4;
+    g = l + tc * 4;
+    bytes = g + tc * 8;
+    xf = 2 * bytes;
+    qf = xf + (io_bytes == 2 ? tc * dk * 4 : 0);
+    total = qf + (io_bytes == 2 ? tc * dk * 4 : 0);
   }
 };
 
@@ -91,19 +105,21 @@ __device__ __forceinline__ void stage_words(char* dst, const char* base, int64_t
   }
 }
 
+constexpr int kRowsR = 8;  // state rows per thread in the recurrent form
+
 template <typename IO>
-__device__ __forceinline__ void lds16(const char* p, float out[kRows]) {
+__device__ __forceinline__ void lds8(const char* p, float out[kRowsR]) {
   if constexpr (sizeof(IO) == 2) {
-    const uint4 a = *reinterpret_cast<const uint4*>(p), b = *reinterpret_cast<const uint4*>(p + 16);
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    const uint4 a = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
       out[2 * i] = __uint_as_float(w[i] << 16);
       out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {
       const float4 a = reinterpret_cast<const float4*>(p)[i];
       out[4 * i] = a.x; out[4 * i + 1] = a.y; out[4 * i + 2] = a.z; out[4 * i + 3] = a.w;
     }
@@ -116,13 +132,13 @@ __device__ __forceinline__ float lds1(const char* p, int i) {
 }
 
 template <typename IO, int VARIANT, int RS>
-__global__ void __launch_bounds__(512)
+__global__ void __launch_bounds__(1024)
 recurrent_kernel(const IO* __restrict__ phi_k, const IO* __restrict__ phi_q,
                  const IO* __restrict__ v, const float* __restrict__ beta,
                  const float* __restrict__ lam, const float* S0, const IO* __restrict__ k_prev,
                  IO* __restrict__ o, float* S_T, int T, int dv, float eps, float eps_gamma) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  constexpr int dk = RS * kRows;
+  constexpr int dk = RS * kRowsR;
   constexpr int io_bytes = sizeof(IO);
   constexpr bool per_col = is_per_column(VARIANT);
   constexpr int tc = block_tokens(dk, io_bytes);
@@ -139,10 +155,10 @@ recurrent_kernel(const IO* __restrict__ phi_k, const IO* __restrict__ phi_q,
   const RecLayout L(tc, dk, ncols, io_bytes, per_col);
   const bool fresh = (k_prev == nullptr);
 
-  float S[kRows];
+  float S[kRowsR];
 #pragma unroll
-  for (int i = 0; i < kRows; ++i)
-    S[i] = S0 ? S0[(bh * dk + r * kRows + i) * dv + col] : 0.0f;
+  for (int i = 0; i < kRowsR; ++i)
+    S[i] = S0 ? S0[(bh * dk + r * kRowsR + i) * dv + col] : 0.0f;
 
   const char* Kb = reinterpret_cast<const char*>(phi_k + bh * int64_t(T) * dk);
   const char* Qb = reinterpret_cast<const char*>(phi_q + bh * int64_t(T) * dk);
@@ -184,7 +200,26 @@ recurrent_kernel(const IO* __restrict__ phi_k, const IO* __restrict__ phi_q,
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's loads of block j have landed
     __syncthreads();                                   // all of block j landed; block j - 1 is done
     if (j + 1 < nblocks) stage(j + 1);
-    // energies ||x_t||^2 of the block's tokens
+    // bf16 keys and queries widened once, 8 per thread and pass
+    if constexpr (io_bytes == 2) {
+      for (int u = tid; u < tc * dk / 8; u += blockDim.x) {
+        const uint4 kx = reinterpret_cast<const uint4*>(buf + L.x)[u];
+        const uint4 kq = reinterpret_cast<const uint4*>(buf + L.q)[u];
+        const uint32_t wx[4] = {kx.x, kx.y, kx.z, kx.w}, wq[4] = {kq.x, kq.y, kq.z, kq.w};
+        float4* fx = reinterpret_cast<float4*>(smem + L.xf) + 2 * u;
+        float4* fq = reinterpret_cast<float4*>(smem + L.qf) + 2 * u;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          fx[h] = make_float4(__uint_as_float(wx[2 * h] << 16), __uint_as_float(wx[2 * h] & 0xffff0000u),
+                              __uint_as_float(wx[2 * h + 1] << 16), __uint_as_float(wx[2 * h + 1] & 0xffff0000u));
+          fq[h] = make_float4(__uint_as_float(wq[2 * h] << 16), __uint_as_float(wq[2 * h] & 0xffff0000u),
+                              __uint_as_float(wq[2 * h + 1] << 16), __uint_as_float(wq[2 * h + 1] & 0xffff0000u));
+        }
+      }
+    }
+    // gates per token: rd = 1 / (||x_t||^2 + lam_t + eps), 0 where the step
+    // size is 0 (a zero denominator, or the first step of a fresh start); with
+    // one gain per token also eta_t = beta_t rd (Eq. 3.4) and gamma_t
     for (int t = tid; t < tc; t += blockDim.x) {
       float e = 0.f;
       const char* xr = buf + L.x + t * dk * io_bytes;
@@ -193,26 +228,44 @@ recurrent_kernel(const IO* __restrict__ phi_k, const IO* __restrict__ phi_q,
         const float xv = lds1<IO>(xr, i);
         e = fmaf(xv, xv, e);
       }
-      reinterpret_cast<float*>(buf + L.e)[t] = e;
+      const float lt = reinterpret_cast<const float*>(buf + L.l)[t];
+      const float den = e + lt + eps;
+      const bool off = den == 0.0f || (fresh && j * tc + t == 0);
+      const float rd = off ? 0.0f : 1.0f / den;
+      float2 gt = make_float2(rd, 0.0f);
+      if constexpr (!per_col) {
+        const float eta = reinterpret_cast<const float*>(buf + L.b)[t] * rd;
+        gt = make_float2(eta, clamped_gamma(eta, lt, eps_gamma));
+      }
+      reinterpret_cast<float2*>(buf + L.g)[t] = gt;
     }
     __syncthreads();
     const int t0 = j * tc;
     const int nt = T - t0 < tc ? T - t0 : tc;
     for (int t = 0; t < nt; ++t) {
-      float x[kRows], q[kRows];
-      lds16<IO>(buf + L.x + (t * dk + r * kRows) * io_bytes, x);
-      lds16<IO>(buf + L.q + (t * dk + r * kRows) * io_bytes, q);
+      float x[kRowsR], q[kRowsR];
+      if constexpr (io_bytes == 2) {
+        lds8<float>(smem + L.xf + (t * dk + r * kRowsR) * 4, x);
+        lds8<float>(smem + L.qf + (t * dk + r * kRowsR) * 4, q);
+      } else {
+        lds8<IO>(buf + L.x + (t * dk + r * kRowsR) * io_bytes, x);
+        lds8<IO>(buf + L.q + (t * dk + r * kRowsR) * io_bytes, q);
+      }
       const float vt = lds1<IO>(buf + L.v, t * ncols + cl);
-      const float bt = reinterpret_cast<const float*>(buf + L.b)[per_col ? t * ncols + cl : t];
-      const float lt = reinterpret_cast<const float*>(buf + L.l)[t];
-      const float e = reinterpret_cast<const float*>(buf + L.e)[t];
-      const float eta = nlms_eta(bt, e, lt, eps, fresh && t0 + t == 0);
-      const float gamma = clamped_gamma(eta, lt, eps_gamma);
+      const float2 gt = reinterpret_cast<const float2*>(buf + L.g)[t];
+      float eta, gamma;
+      if constexpr (per_col) {
+        eta = reinterpret_cast<const float*>(buf + L.b)[t * ncols + cl] * gt.x;   // Eq. 3.4
+        gamma = clamped_gamma(eta, reinterpret_cast<const float*>(buf + L.l)[t], eps_gamma);
+      } else {
+        eta = gt.x;
+        gamma = gt.y;
+      }
       float target = vt;
       if constexpr (is_regression(VARIANT)) {
         float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
 #pragma unroll
-        for (int i = 0; i < kRows; i += 4) {
+        for (int i = 0; i < kRowsR; i += 4) {
           p0 = fmaf(S[i], x[i], p0);
           p1 = fmaf(S[i + 1], x[i + 1], p1);
           p2 = fmaf(S[i + 2], x[i + 2], p2);
@@ -223,7 +276,7 @@ recurrent_kernel(const IO* __restrict__ phi_k, const IO* __restrict__ phi_q,
       const float w = eta * target;
       float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
 #pragma unroll
-      for (int i = 0; i < kRows; i += 4) {
+      for (int i = 0; i < kRowsR; i += 4) {
         S[i] = fmaf(gamma, S[i], w * x[i]);                 // S_t = gamma S + eta x r^T
         S[i + 1] = fmaf(gamma, S[i + 1], w * x[i + 1]);
         S[i + 2] = fmaf(gamma, S[i + 2], w * x[i + 2]);
@@ -239,7 +292,7 @@ recurrent_kernel(const IO* __restrict__ phi_k, const IO* __restrict__ phi_q,
   }
   if (S_T) {
 #pragma unroll
-    for (int i = 0; i < kRows; ++i) S_T[(bh * dk + r * kRows + i) * dv + col] = S[i];
+    for (int i = 0; i < kRowsR; ++i) S_T[(bh * dk + r * kRowsR + i) * dv + col] = S[i];
   }
 }
 
@@ -336,11 +389,12 @@ decode_kernel(const IO* __restrict__ x_in, const IO* __restrict__ q_in,
 
 template <typename IO, int VARIANT, int RS>
 hipError_t launch_recurrent_rs(const ProblemArgs& a, hipStream_t st) {
-  const int ncols = a.dv < 64 ? a.dv : 64;
-  const RecLayout L(block_tokens(RS * kRows, int(sizeof(IO))), RS * kRows, ncols, int(sizeof(IO)),
+  // 32-column tiles: twice the workgroups of 64-column ones, one wave per SIMD
+  const int ncols = a.dv < 32 ? a.dv : 32;
+  const RecLayout L(block_tokens(RS * kRowsR, int(sizeof(IO))), RS * kRowsR, ncols, int(sizeof(IO)),
                     is_per_column(VARIANT));
   dim3 grid(a.B * a.H, a.dv / ncols), block(ncols * RS);
-  hipLaunchKernelGGL((recurrent_kernel<IO, VARIANT, RS>), grid, block, size_t(2 * L.bytes), st,
+  hipLaunchKernelGGL((recurrent_kernel<IO, VARIANT, RS>), grid, block, size_t(L.total), st,
                      static_cast<const IO*>(a.phi_k), static_cast<const IO*>(a.phi_q),
                      static_cast<const IO*>(a.v), a.beta, a.lam, a.S0,
                      static_cast<const IO*>(a.k_prev), static_cast<IO*>(a.o), a.S_T, a.T, a.dv,
@@ -351,10 +405,10 @@ hipError_t launch_recurrent_rs(const ProblemArgs& a, hipStream_t st) {
 template <typename IO, int VARIANT>
 hipError_t launch_recurrent_t(const ProblemArgs& a, hipStream_t st) {
   switch (a.dk) {
-    case 16: return launch_recurrent_rs<IO, VARIANT, 1>(a, st);
-    case 32: return launch_recurrent_rs<IO, VARIANT, 2>(a, st);
-    case 64: return launch_recurrent_rs<IO, VARIANT, 4>(a, st);
-    default: return launch_recurrent_rs<IO, VARIANT, 8>(a, st);
+    case 16: return launch_recurrent_rs<IO, VARIANT, 2>(a, st);
+    case 32: return launch_recurrent_rs<IO, VARIANT, 4>(a, st);
+    case 64: return launch_recurrent_rs<IO, VARIANT, 8>(a, st);
+    default: return launch_recurrent_rs<IO, VARIANT, 16>(a, st);
   }
 }
 
