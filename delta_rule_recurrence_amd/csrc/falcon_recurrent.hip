@@ -38,16 +38,16 @@ __device__ __forceinline__ float group_sum(float v) {
 }
 
 // ---- recurrent form ----------------------------------------------------------
-// One workgroup per (b*h, value-column tile) with NCOLS * RS threads, RS =
-// dk / 8: thread tid = col * RS + r owns rows [8 r, 8 r + 8) of column col of
-// the tile (two waves per SIMD at d = 64, so one hides the other's latency).  The inputs come through LDS in blocks of 32 (or 16) tokens:
-// while a block is swept, the next one is loaded straight from global memory
-// into the other LDS buffer (direct-to-LDS loads, 16 bytes per lane), so no step waits
-// for global memory.  After a block lands, one pass widens bf16 keys and
-// queries to float32 (one LDS region, read by the steps) and forms each
-// token's gates: eta_t and gamma_t, or for per-column gains 1 / (||x_t||^2 +
-// lam_t + eps) (0 where the step size is 0).  The per-step work is then the
-// state's dot products and update, with the cross-lane sums in DPP.
+// One workgroup per (b*h, 32-column tile) with NCOLS * RS threads, RS = dk / 8:
+// thread tid = col * RS + r owns rows [8 r, 8 r + 8) of column col of the tile.
+// The inputs come through LDS in blocks of 32 (or 16) tokens: while a block is
+// swept, the next one is loaded straight from global memory into the other
+// LDS buffer (direct-to-LDS loads, 16 bytes per lane), so no step waits for
+// global memory.  After a block lands, one pass widens bf16 keys and queries
+// to float32 (one LDS region, read by the steps) and forms each token's gates:
+// eta_t and gamma_t, or for per-column gains 1 / (||x_t||^2 + lam_t + eps)
+// (0 where the step size is 0).  The per-step work is then the state's dot
+// products and update, with the cross-lane sums in DPP.
 
 // Tokens per staged block: 32, or 16 for rows of 256 bytes and more, so the
 // two buffers stay within 64 KB of LDS.
