@@ -123,6 +123,19 @@ __device__ __forceinline__ void lower_tile(int n, int& ib, int& sb) {
   sb = n - (ib * (ib + 1)) / 2;
 }
 
+// log gamma = log1p(-alpha), alpha = min(eta lam, 1 - eps_gamma) (Section
+// 4.3), in float32 as ln(u) (-alpha) / (u - 1) with u = 1 - alpha rounded: the
+// ratio cancels the rounding of u (Kahan's compensated log1p), so small alpha
+// keeps its relative accuracy; ln is the hardware log2 times ln 2, and the
+// division a hardware reciprocal (a few ulp in all).
+__device__ __forceinline__ float fast_log_gamma(float eta, float lam, float eps_gamma) {
+  const float alpha = fminf(eta * lam, 1.0f - eps_gamma);
+  const float u = 1.0f - alpha;
+  const float d = u - 1.0f;
+  return d == 0.0f ? -alpha
+                   : __builtin_amdgcn_logf(u) * 0.6931471805599453f * (-alpha * __builtin_amdgcn_rcpf(d));
+}
+
 // Gates of one 64-token chunk (a1) from the staged key rows xs (64 swizzled
 // rows in LDS) and the gates beta, lam of token `tok` = chunk start + l.
 // Returns, for row l: eta_l (Eq. 3.4; 0 at the fresh start and past the
@@ -144,12 +157,12 @@ __device__ __forceinline__ void chunk_gates(const uint16_t* xs, float beta, floa
       energy = __builtin_amdgcn_fdot2_f32_bf16(xv, xv, energy, false);
     }
   }
-  eta = 0.f;
-  float lg = 0.f;
-  if (tok < T) {
-    eta = nlms_eta(beta, energy, lam, eps, fresh && tok == 0);
-    lg = clamped_log_gamma(eta, lam, eps_gamma);
-  }
+  // Eq. 3.4 with the hardware reciprocal; 0 at the fresh start, for a zero
+  // denominator and past the sequence
+  const float den = energy + lam + eps;
+  const bool on = tok < T && !(fresh && tok == 0) && den != 0.0f;
+  eta = on ? beta * __builtin_amdgcn_rcpf(den) : 0.0f;
+  const float lg = tok < T ? fast_log_gamma(eta, lam, eps_gamma) : 0.0f;
   // inclusive prefix over the 64 rows: DPP shifts within 16-lane rows, then
   // the row totals carried across rows
   gi = lg;
