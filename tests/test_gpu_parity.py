@@ -300,3 +300,27 @@ def test_decode_steps_match_forward(variant, io, dk, dv):
                                           is_first=first if t == 0 else None))
     torch.cuda.synchronize()
     check(torch.stack(outs, dim=2), S, O_ref, S_ref, TOL[io], f"decode {variant}")
+
+
+# ---- sequences shorter than a staged block or a chunk -------------------------
+
+@pytest.mark.parametrize("entry", ["recurrent", "chunked"])
+@pytest.mark.parametrize("case", [("falcon1", "bf16", 1, 64, 64), ("falcon1", "f32", 5, 16, 16),
+                                  ("falcon1a", "bf16", 17, 64, 64), ("falcon2", "f32", 33, 32, 64),
+                                  ("falcon2a", "bf16", 5, 128, 32), ("falcon1", "bf16", 17, 128, 128)],
+                         ids=lambda c: "-".join(map(str, c)))
+def test_short_sequences(entry, case):
+    """T below the recurrent form's 16/32-token staging block and the 64-token
+    chunk (the first block is also the ragged last one), with a carried state
+    and a previous key."""
+    variant, io, T, dk, dv = case
+    B, H = 2, 3
+    per_col = variant in ("falcon2", "falcon2a")
+    d = I.make_inputs(B, H, T, dk, dv, seed=200 + T, io_dtype=io, per_column_beta=per_col)
+    S0 = I.random_state((B, H, dk, dv), seed=201)
+    kp = I.make_inputs(B, H, 1, dk, dv, seed=202, io_dtype=io)["phi_k"][:, :, 0].contiguous()
+    O_ref, S_ref = oracle_forward(variant, d, S0=S0, k_prev=kp)
+    o, S_T = _run(entry, to_dev(d), variant, C=64 if dk == 64 and dv == 64 else 16, S0=S0.cuda(),
+                  k_prev=kp.cuda())
+    torch.cuda.synchronize()
+    check(o, S_T, O_ref, S_ref, TOL[io], f"{entry} short {case}")
