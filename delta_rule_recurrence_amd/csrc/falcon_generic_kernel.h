@@ -1,0 +1,578 @@
+// Chunk-parallel Falcon forward, general-shape float32 kernel (gfx950).
+//
+// Serves every (variant, dtype, dk, dv, C) combination that has no MFMA path
+// (the bf16 cases with dk = dv = 64 and C = 64 have their own kernels).
+// All arithmetic is float32 on the vector ALUs; intermediates live in LDS.
+// The kernel template is instantiated once per chunk size, each in a source
+// file of its own (falcon_chunked_generic_c16/c32/c64.hip) so the three
+// compile in parallel; falcon_chunked_generic.hip picks the value tile and
+// dispatches.
+//
+// Chunk algebra (derived from the Section 4 summary rules with the chunk-
+// local log-space renormalisation of Section 4.4, "Algorithm 3 realizes
+// Eq. (4.16) chunk-locally via log-prefix decays", taken with window B = 1).
+// For a chunk with local rows i = 0..C-1, incoming state S and per value
+// column j (scalar rules use one gate column for all j):
+//   g_i      = sum_{r<=i} log gamma_r             (float32, all exponents <= 0;
+//              held in base-2 units, so each decay is one exp2)
+//   rho_i    = eta_i r_i  (scaled residual, regression rules) solves the
+//              merged residual system
+//              rho_i + sum_{s<i} eta_i e^{g_{i-1}-g_s} (x_i.x_s) rho_s
+//                    = eta_i (v_i - e^{g_{i-1}} (X S)_i)
+//              ("injected-value and projected-history paths share this
+//              triangular factor ... one merged residual system", §4.2);
+//   rho_i    = eta_i v_i                            (inner-product rules)
+//   o_i      = e^{g_i} (Q S)_i + sum_{s<=i} e^{g_i-g_s} (q_i.x_s) rho_s
+//   S_next   = e^{g_{C-1}} S + sum_s e^{g_{C-1}-g_s} x_s rho_s^T
+// Rows past the end of the sequence get eta = 0 and log gamma = 0, so a
+// ragged last chunk needs no special case.
+//
+// Mapping.  One workgroup of 256 threads owns one sequence and one tile of
+// nv = 16 NB value columns and walks its chunks in order.  The threads form a
+// 16 x 16 grid (ty, tx); every contraction gives a thread the rows ty + 16 a
+// and the columns tx + 16 b of its output, so a wave reads four operand rows
+// that sit in distinct LDS banks (row pitches are a multiple of 4 words plus
+// 4) and sixteen consecutive words of the other operand.  Operands that run
+// along the contraction index are read as float4.  Per-thread tiles have
+// compile-time shapes (C / 16 chunk rows, NB value columns; key rows in
+// groups of four), so no multiply-add sits behind a run-time guard.  Each
+// chunk's inputs are loaded into registers in one batch at the top of the
+// chunk and staged into LDS.  The substitution runs one thread per value
+// column in 16-row blocks, the block's unknowns in registers.  Sums stop at
+// the diagonal (s <= i), never multiplying a masked zero by a later row's
+// value, so a non-finite input reaches no earlier output.
+#pragma once
+
+#include "falcon_device.h"
+#include "falcon_generic.h"
+
+namespace falcon {
+
+namespace generic_detail {
+
+// Four consecutive I/O elements, loaded raw and widened when staged into LDS.
+template <typename T> struct quad;
+template <> struct quad<float> {
+  using raw = float4;
+  __device__ __forceinline__ static raw load(const float* p, int i) {
+    return *reinterpret_cast<const float4*>(p + i);
+  }
+  __device__ __forceinline__ static raw zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+  __device__ __forceinline__ static float4 widen(raw r) { return r; }
+};
+template <> struct quad<bf16_t> {
+  using raw = uint2;
+  __device__ __forceinline__ static raw load(const bf16_t* p, int i) {
+    return *reinterpret_cast<const uint2*>(p + i);
+  }
+  __device__ __forceinline__ static raw zero() { return make_uint2(0u, 0u); }
+  __device__ __forceinline__ static float4 widen(raw r) {
+    return make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
+                       __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u));
+  }
+};
+
+__device__ __forceinline__ float4 ld4(const float* p) {
+  return *reinterpret_cast<const float4*>(p);
+}
+__device__ __forceinline__ void st4(float* p, float4 x) { *reinterpret_cast<float4*>(p) = x; }
+__device__ __forceinline__ float dot4(float4 a, float4 b, float acc) {
+  return fmaf(a.w, b.w, fmaf(a.z, b.z, fmaf(a.y, b.y, fmaf(a.x, b.x, acc))));
+}
+__device__ __forceinline__ float comp(float4 a, int k) {
+  return k == 0 ? a.x : k == 1 ? a.y : k == 2 ? a.z : a.w;
+}
+
+// LDS-only workgroup barrier: orders the workgroup's LDS traffic without
+// waiting for its outstanding global stores.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <typename IO, int VARIANT, int C, int NB>
+__global__ void __launch_bounds__(kGenericThreads)
+chunked_generic_kernel(const IO* __restrict__ phi_k, const IO* __restrict__ phi_q,
+                       const IO* __restrict__ v, const float* __restrict__ beta,
+                       const float* __restrict__ lam, const float* S0,
+                       const IO* __restrict__ k_prev, IO* __restrict__ o, float* S_T, int T,
+                       int dk, int dv, int64_t BH, float eps, float eps_gamma) {
+  constexpr int kThreads = kGenericThreads;
+  constexpr bool kPerCol = is_per_column(VARIANT);
+  constexpr bool kReg = is_regression(VARIANT);
+  constexpr int MC = C / 16;                      // chunk rows (and columns) per thread
+  constexpr int nv = 16 * NB;                     // value columns of the tile
+  constexpr int ng = kPerCol ? nv : 1;            // gate columns
+  constexpr int kXQ = C * 128 / (4 * kThreads);   // float4 groups of X (and of Q) per thread, dk <= 128
+  constexpr int kV = (C * nv / 4 + kThreads - 1) / kThreads;   // float4 groups of v per thread
+  constexpr int nvq = C * nv / 4;
+  constexpr int lv = NB == 1 ? 2 : NB == 2 ? 3 : 4;            // log2(nv / 4)
+  using Q4 = quad<IO>;
+  extern __shared__ float4 lds4[];
+  float* lds = reinterpret_cast<float*>(lds4);
+  const GenericLayout L(C, dk, nv, ng, kReg);
+  float* Xs = lds + L.off_x;      // [C][xp]  shifted keys x_i
+  float* Qs = lds + L.off_q;      // [C][xp]  queries
+  float* Ps = lds + L.off_p;      // [C][pp]  q_i.x_s for s <= i (decayed for scalar gates)
+  float* Gs = lds + L.off_g;      // [C][pp]  x_i.x_s for s < i (the coupling for scalar gates)
+  float* Rs = lds + L.off_r;      // [C][nv]  v, then the right-hand side, then rho
+  float* Ss = lds + L.off_s;      // [dk][nv] state tile
+  float* Eta = lds + L.off_eta;   // [C][ng]  beta, then eta
+  float* Lg = lds + L.off_lg;     // [C][ng]  inclusive prefix g of log2 gamma
+  float* En = lds + L.off_en;     // [C]      energies x_i.x_i, then 2^{g_{C-1}-g_s}
+  float* Lm = lds + L.off_lm;     // [C]      lam
+
+  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  // The value tiles of one sequence are workgroups 8k + x for one x: consecutive
+  // workgroups go to different XCDs, so the tiles share an XCD and its L2, and
+  // the keys and queries every tile reads come from HBM once.
+  const int ntile = dv / nv;
+  const int kk8 = blockIdx.x >> 3;
+  const int64_t bh = int64_t(kk8 / ntile) * 8 + (blockIdx.x & 7);
+  const int j0 = (kk8 % ntile) * nv;
+  if (bh >= BH) return;
+  const bool fresh = (k_prev == nullptr);
+  const int mk = dk >> 4;
+  const int lq = __builtin_ctz(dk >> 2);
+  const int nxq = (C * dk) >> 2;
+
+  for (int e = tid; e < dk * nv; e += kThreads) {
+    const int f = e / nv, j = e % nv;
+    Ss[e] = S0 ? S0[(bh * dk + f) * dv + j0 + j] : 0.0f;
+  }
+
+  typename Q4::raw xr[kXQ], qr[kXQ], vr[kV];
+  float4 br[kPerCol ? kV : 1];
+  float bs = 0.f, ls = 0.f;
+  // Loads of one chunk: row t0 + i of the sequence, offsets within the chunk
+  // (at most C * 128 elements) from a base pointer that is uniform.
+  auto fetch = [&](int t0) {
+    const int rows = min(C, T - t0);
+    const int64_t row0 = bh * T + t0;
+    const IO* Kc = phi_k + row0 * dk;   // x_i = phi_k row t0 + i - 1: offset off - dk
+    const IO* Qc = phi_q + row0 * dk;
+#pragma unroll
+    for (int u = 0; u < kXQ; ++u) {
+      const int e = tid + u * kThreads;
+      const int i = e >> lq, off = e << 2;     // i * dk + f
+      xr[u] = Q4::zero();
+      qr[u] = Q4::zero();
+      if (e < nxq && i < rows) {
+        qr[u] = Q4::load(Qc, off);
+        if (t0 + i >= 1) xr[u] = Q4::load(Kc, off - dk);
+        else if (!fresh) xr[u] = Q4::load(k_prev + bh * dk, off);
+      }
+    }
+    const IO* Vc = v + row0 * dv + j0;
+    const float* Bc = beta + row0 * dv + j0;
+#pragma unroll
+    for (int u = 0; u < kV; ++u) {
+      const int e = tid + u * kThreads;
+      const int i = e >> lv, j = (e & (nv / 4 - 1)) << 2;
+      vr[u] = Q4::zero();
+      if constexpr (kPerCol) br[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (e < nvq && i < rows) {
+        vr[u] = Q4::load(Vc, i * dv + j);
+        if constexpr (kPerCol) br[u] = *reinterpret_cast<const float4*>(Bc + i * dv + j);
+      }
+    }
+    bs = 0.f;
+    ls = 0.f;
+    if (tid < rows) {
+      if constexpr (!kPerCol) bs = beta[row0 + tid];
+      ls = lam[row0 + tid];
+    }
+  };
+
+  const int nchunks = (T + C - 1) / C;
+  for (int c = 0; c < nchunks; ++c) {
+    const int t0 = c * C;
+    fetch(t0);
+    lds_barrier();  // the previous chunk is done with every buffer
+    // ---- stage this chunk --------------------------------------------------
+#pragma unroll
+    for (int u = 0; u < kXQ; ++u) {
+      const int e = tid + u * kThreads;
+      if (e < nxq) {
+        const int i = e >> lq, f = (e & ((dk >> 2) - 1)) << 2;
+        st4(Xs + i * L.xp + f, Q4::widen(xr[u]));
+        st4(Qs + i * L.xp + f, Q4::widen(qr[u]));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kV; ++u) {
+      const int e = tid + u * kThreads;
+      if (e < nvq) {
+        const int i = e >> lv, j = (e & (nv / 4 - 1)) << 2;
+        st4(Rs + i * nv + j, Q4::widen(vr[u]));
+        if constexpr (kPerCol) st4(Eta + i * nv + j, br[u]);
+      }
+    }
+    if (tid < C) {
+      if constexpr (!kPerCol) Eta[tid] = bs;
+      Lm[tid] = ls;
+    }
+    lds_barrier();
+
+    // ---- products that need no gate: Q X^T, X X^T, Q S, X S; energies ------
+    float pa[MC][MC], ga[MC][MC], qs[MC][NB], xs[MC][NB];
+#pragma unroll
+    for (int a = 0; a < MC; ++a) {
+#pragma unroll
+      for (int b = 0; b < MC; ++b) pa[a][b] = ga[a][b] = 0.f;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) qs[a][b] = xs[a][b] = 0.f;
+    }
+    for (int f = 0; f < dk; f += 4) {
+      float4 qi[MC], xi[MC], xc[MC];
+#pragma unroll
+      for (int a = 0; a < MC; ++a) {
+        qi[a] = ld4(Qs + (ty + 16 * a) * L.xp + f);
+        if (kReg) xi[a] = ld4(Xs + (ty + 16 * a) * L.xp + f);
+        xc[a] = ld4(Xs + (tx + 16 * a) * L.xp + f);
+      }
+      float sv[4][NB];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) sv[k][b] = Ss[(f + k) * nv + tx + 16 * b];
+#pragma unroll
+      for (int a = 0; a < MC; ++a) {
+#pragma unroll
+        for (int b = 0; b <= a; ++b) {   // tiles with b > a lie above the diagonal
+          pa[a][b] = dot4(qi[a], xc[b], pa[a][b]);
+          if (kReg) ga[a][b] = dot4(xi[a], xc[b], ga[a][b]);
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            qs[a][b] = fmaf(comp(qi[a], k), sv[k][b], qs[a][b]);
+            if (kReg) xs[a][b] = fmaf(comp(xi[a], k), sv[k][b], xs[a][b]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int a = 0; a < MC; ++a) {
+      const int i = ty + 16 * a;
+#pragma unroll
+      for (int b = 0; b < MC; ++b) {
+        const int s = tx + 16 * b;
+        Ps[i * L.pp + s] = s <= i ? pa[a][b] : 0.f;
+        if (kReg) Gs[i * L.pp + s] = s < i ? ga[a][b] : 0.f;
+      }
+    }
+    if (tid < C) {
+      float en = 0.f;
+      for (int f = 0; f < dk; f += 4) {
+        const float4 x = ld4(Xs + tid * L.xp + f);
+        en = dot4(x, x, en);
+      }
+      En[tid] = en;
+    }
+    lds_barrier();
+
+    // ---- a1: step sizes and log decays, then the prefix g ------------------
+    constexpr float kLog2e = 1.44269504088896341f;
+    if constexpr (!kPerCol) {
+      if (tid < 64) {   // wave 0: one row per lane, scan across the wave
+        float eta = 0.f, lg = 0.f;
+        const int t = t0 + tid;
+        if (tid < C && t < T) {
+          eta = nlms_eta(Eta[tid], En[tid], Lm[tid], eps, fresh && t == 0);
+          lg = clamped_log_gamma(eta, Lm[tid], eps_gamma) * kLog2e;
+        }
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const float y = __shfl_up(lg, d, 64);
+          if (tid >= d) lg += y;
+        }
+        if (tid < C) {
+          Eta[tid] = eta;
+          Lg[tid] = lg;
+        }
+      }
+    } else {
+      for (int e = tid; e < C * ng; e += kThreads) {
+        const int i = e >> (lv + 2);
+        const int t = t0 + i;
+        float eta = 0.f, lg = 0.f;
+        if (t < T) {
+          eta = nlms_eta(Eta[e], En[i], Lm[i], eps, fresh && t == 0);
+          lg = clamped_log_gamma(eta, Lm[i], eps_gamma) * kLog2e;
+        }
+        Eta[e] = eta;
+        Lg[e] = lg;
+      }
+      lds_barrier();
+      if (tid < ng) {
+        float acc = 0.f;
+        for (int i = 0; i < C; ++i) {
+          acc += Lg[i * ng + tid];
+          Lg[i * ng + tid] = acc;
+        }
+      }
+    }
+    lds_barrier();
+
+    // ---- right-hand side; masked (and, for scalar gates, decayed) P and G --
+#pragma unroll
+    for (int a = 0; a < MC; ++a) {
+      const int i = ty + 16 * a;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int j = tx + 16 * b;
+        const int cc = kPerCol ? j : 0;
+        const float eta = Eta[i * ng + cc];
+        float& r = Rs[i * nv + j];
+        if (kReg) {
+          const float gprev = i > 0 ? Lg[(i - 1) * ng + cc] : 0.0f;
+          r = eta * fmaf(exp2f(gprev), -xs[a][b], r);   // eta (v - 2^{g_{i-1}} X S)
+        } else {
+          r = eta * r;
+        }
+      }
+      if constexpr (!kPerCol) {
+#pragma unroll
+        for (int b = 0; b < MC; ++b) {
+          const int s = tx + 16 * b;
+          if (s <= i) Ps[i * L.pp + s] *= exp2f(Lg[i] - Lg[s]);
+          if (kReg && s < i) Gs[i * L.pp + s] *= Eta[i] * exp2f(Lg[i - 1] - Lg[s]);
+        }
+      }
+    }
+    if (!kPerCol && tid < C) En[tid] = exp2f(Lg[C - 1] - Lg[tid]);
+    lds_barrier();
+
+    // ---- a2/a3: forward substitution of the merged residual system --------
+    // 16-row blocks.  Before block B0 is solved, all threads subtract the
+    // contributions of the solved rows s < B0 from its right-hand sides (row
+    // B0 + ty, columns tx + 16 b); then one thread per value column solves the
+    // block's 16 x 16 lower triangle in registers.
+    if constexpr (kReg) {
+      for (int B0 = 0; B0 < C; B0 += 16) {
+        if (B0 > 0) {
+          const int i = B0 + ty;
+          float acc[NB], gref[NB];
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            acc[b] = 0.f;
+            // per-column gates: 2^{g_{i-1}-g_s} = 2^{g_{i-1}-g_ref} 2^{g_ref-g_s} with
+            // g_ref = g_{B0-1}; both factors are <= 1 since g never increases
+            gref[b] = kPerCol ? Lg[(B0 - 1) * ng + tx + 16 * b] : 0.f;
+          }
+          for (int s0 = 0; s0 < B0; s0 += 4) {
+            const float4 g = ld4(Gs + i * L.pp + s0);
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+#pragma unroll
+              for (int b = 0; b < NB; ++b) {
+                const int j = tx + 16 * b;
+                float rv = Rs[(s0 + k) * nv + j];
+                if (kPerCol) rv *= exp2f(gref[b] - Lg[(s0 + k) * ng + j]);
+                acc[b] = fmaf(comp(g, k), rv, acc[b]);
+              }
+          }
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            const int j = tx + 16 * b;
+            if (kPerCol) acc[b] *= Eta[i * ng + j] * exp2f(Lg[(i - 1) * ng + j] - gref[b]);
+            Rs[i * nv + j] -= acc[b];
+          }
+          lds_barrier();
+        }
+        if (tid < nv) {
+          const int j = tid;
+          float r[16], eB[16], gB[16];
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) {
+            const int i = B0 + rr;
+            r[rr] = Rs[i * nv + j];
+            if (kPerCol) {
+              eB[rr] = Eta[i * ng + j];
+              gB[rr] = i > 0 ? Lg[(i - 1) * ng + j] : 0.f;
+            }
+          }
+#pragma unroll
+          for (int rr = 1; rr < 16; ++rr) {
+            const float* gi = Gs + (B0 + rr) * L.pp + B0;
+            float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+            for (int s4 = 0; s4 < rr; s4 += 4) {
+              const float4 g = ld4(gi + s4);
+#pragma unroll
+              for (int k = 0; k < 4; ++k) {
+                if (s4 + k < rr) {
+                  float cf = comp(g, k);
+                  if (kPerCol) cf *= eB[rr] * exp2f(gB[rr] - Lg[(B0 + s4 + k) * ng + j]);
+                  if (k & 1) a1 = fmaf(cf, r[s4 + k], a1);
+                  else a0 = fmaf(cf, r[s4 + k], a0);
+                }
+              }
+            }
+            r[rr] -= a0 + a1;
+          }
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) Rs[(B0 + rr) * nv + j] = r[rr];
+        }
+        lds_barrier();
+      }
+    }
+
+    // ---- a4: outputs ---------------------------------------------------------
+    {
+      float acc[MC][NB], gi[MC][NB];
+#pragma unroll
+      for (int a = 0; a < MC; ++a)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const int i = ty + 16 * a, j = tx + 16 * b;
+          gi[a][b] = Lg[i * ng + (kPerCol ? j : 0)];
+          acc[a][b] = exp2f(gi[a][b]) * qs[a][b];
+        }
+      constexpr int kStepUnroll = kPerCol ? 1 : 4;   // one exp per term keeps per-column code small
+#pragma unroll 1
+      for (int sb = 0; sb < MC; ++sb) {
+#pragma unroll kStepUnroll
+        for (int s4 = 0; s4 < 16; s4 += 4) {
+          const int s = 16 * sb + s4;
+          float rv[4][NB], gs[4][NB];
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+              rv[k][b] = Rs[(s + k) * nv + tx + 16 * b];
+              if (kPerCol) gs[k][b] = Lg[(s + k) * ng + tx + 16 * b];
+            }
+#pragma unroll
+          for (int a = 0; a < MC; ++a) {
+            if (a < sb) continue;   // static index, uniform skip
+            const float4 p = ld4(Ps + (ty + 16 * a) * L.pp + s);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              // in the diagonal block only the columns s <= i take part
+              const bool on = a > sb || s4 + k <= ty;
+#pragma unroll
+              for (int b = 0; b < NB; ++b) {
+                float cf = comp(p, k);
+                if (kPerCol) cf *= exp2f(gi[a][b] - gs[k][b]);
+                const float nx = fmaf(cf, rv[k][b], acc[a][b]);
+                acc[a][b] = on ? nx : acc[a][b];
+              }
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int a = 0; a < MC; ++a) {
+        const int t = t0 + ty + 16 * a;
+        if (t < T) {
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+            io<IO>::store(o, (bh * T + t) * dv + j0 + tx + 16 * b, acc[a][b]);
+        }
+      }
+    }
+
+    // ---- a3: state update S = 2^{g_{C-1}} S + sum_s 2^{g_{C-1}-g_s} x_s rho_s^T
+    // (reads X, rho and the weights, all final; each thread owns its S entries:
+    // key rows ty + 16 a in groups of four, rows past dk wrap onto valid ones
+    // and are not stored)
+    {
+      float glast[NB], dlast[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        glast[b] = Lg[(C - 1) * ng + (kPerCol ? tx + 16 * b : 0)];
+        dlast[b] = exp2f(glast[b]);
+      }
+      for (int a0 = 0; a0 < mk; a0 += 4) {
+        int fr[4];
+        float sacc[4][NB];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          fr[a] = (ty + 16 * (a0 + a)) & (dk - 1);
+#pragma unroll
+          for (int b = 0; b < NB; ++b) sacc[a][b] = dlast[b] * Ss[fr[a] * nv + tx + 16 * b];
+        }
+#pragma unroll 4
+        for (int s = 0; s < C; ++s) {
+          float rw[NB], xv[4];
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            const int j = tx + 16 * b;
+            const float w = kPerCol ? exp2f(glast[b] - Lg[s * ng + j]) : En[s];
+            rw[b] = Rs[s * nv + j] * w;
+          }
+#pragma unroll
+          for (int a = 0; a < 4; ++a) xv[a] = Xs[s * L.xp + fr[a]];
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) sacc[a][b] = fmaf(xv[a], rw[b], sacc[a][b]);
+        }
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+          if (a0 + a < mk) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) Ss[fr[a] * nv + tx + 16 * b] = sacc[a][b];
+          }
+      }
+    }
+  }
+  __syncthreads();
+  if (S_T) {
+    for (int e = tid; e < dk * nv; e += kThreads) {
+      const int f = e / nv, j = e % nv;
+      S_T[(bh * dk + f) * dv + j0 + j] = Ss[e];
+    }
+  }
+}
+
+template <typename IO, int VARIANT, int C, int NB>
+hipError_t launch_one(const ProblemArgs& a, size_t lds, hipStream_t st) {
+  auto kern = chunked_generic_kernel<IO, VARIANT, C, NB>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     static_cast<int>(lds));
+  if (e != hipSuccess) return e;
+  const int64_t BH = int64_t(a.B) * a.H;
+  const int64_t blocks = (BH + 7) / 8 * 8 * (a.dv / (16 * NB));
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kGenericThreads), lds, st,
+                     static_cast<const IO*>(a.phi_k), static_cast<const IO*>(a.phi_q),
+                     static_cast<const IO*>(a.v), a.beta, a.lam, a.S0,
+                     static_cast<const IO*>(a.k_prev), static_cast<IO*>(a.o), a.S_T, a.T, a.dk,
+                     a.dv, BH, a.eps, a.eps_gamma);
+  return hipGetLastError();
+}
+
+template <typename IO, int VARIANT, int C>
+hipError_t launch_tile(const ProblemArgs& a, int nv, size_t lds, hipStream_t st) {
+  switch (nv) {
+    case 16: return launch_one<IO, VARIANT, C, 1>(a, lds, st);
+    case 32: return launch_one<IO, VARIANT, C, 2>(a, lds, st);
+    default: return launch_one<IO, VARIANT, C, 4>(a, lds, st);
+  }
+}
+
+template <typename IO, int C>
+hipError_t launch_variant(const ProblemArgs& a, int nv, size_t lds, hipStream_t st) {
+  switch (a.variant) {
+    case kF1: return launch_tile<IO, kF1, C>(a, nv, lds, st);
+    case kF1A: return launch_tile<IO, kF1A, C>(a, nv, lds, st);
+    case kF2: return launch_tile<IO, kF2, C>(a, nv, lds, st);
+    default: return launch_tile<IO, kF2A, C>(a, nv, lds, st);
+  }
+}
+
+}  // namespace generic_detail
+
+template <int C>
+hipError_t launch_generic_c(const ProblemArgs& a, int nv, size_t lds, hipStream_t st) {
+  return a.bf16 ? generic_detail::launch_variant<bf16_t, C>(a, nv, lds, st)
+                : generic_detail::launch_variant<float, C>(a, nv, lds, st);
+}
+
+}  // namespace falcon
