@@ -448,7 +448,7 @@ chunked_generic_kernel(const IO* __restrict__ phi_k, const IO* __restrict__ phi_
             }
 #pragma unroll
           for (int a = 0; a < MC; ++a) {
-            if (a < sb) continue;   // static index, uniform skip
+            if (a < sb) continue;   // above the diagonal (static index, uniform skip)
             const float4 p = ld4(Ps + (ty + 16 * a) * L.pp + s);
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
@@ -478,8 +478,8 @@ chunked_generic_kernel(const IO* __restrict__ phi_k, const IO* __restrict__ phi_
 
     // ---- a3: state update S = 2^{g_{C-1}} S + sum_s 2^{g_{C-1}-g_s} x_s rho_s^T
     // (reads X, rho and the weights, all final; each thread owns its S entries:
-    // key rows ty + 16 a in groups of four, rows past dk wrap onto valid ones
-    // and are not stored)
+    // key rows f0 + 4 ty + a, a < 4, for f0 = 0, 64; rows past dk wrap onto
+    // valid ones and are not stored)
     {
       float glast[NB], dlast[NB];
 #pragma unroll
@@ -487,37 +487,35 @@ chunked_generic_kernel(const IO* __restrict__ phi_k, const IO* __restrict__ phi_
         glast[b] = Lg[(C - 1) * ng + (kPerCol ? tx + 16 * b : 0)];
         dlast[b] = exp2f(glast[b]);
       }
-      for (int a0 = 0; a0 < mk; a0 += 4) {
-        int fr[4];
+      for (int f0 = 0; f0 < dk; f0 += 64) {
+        const bool own = f0 + 4 * ty < dk;
+        const int fb = (f0 + 4 * ty) & (dk - 1);
         float sacc[4][NB];
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          fr[a] = (ty + 16 * (a0 + a)) & (dk - 1);
+        for (int a = 0; a < 4; ++a)
 #pragma unroll
-          for (int b = 0; b < NB; ++b) sacc[a][b] = dlast[b] * Ss[fr[a] * nv + tx + 16 * b];
-        }
+          for (int b = 0; b < NB; ++b) sacc[a][b] = dlast[b] * Ss[(fb + a) * nv + tx + 16 * b];
 #pragma unroll 4
         for (int s = 0; s < C; ++s) {
-          float rw[NB], xv[4];
+          float rw[NB];
 #pragma unroll
           for (int b = 0; b < NB; ++b) {
             const int j = tx + 16 * b;
             const float w = kPerCol ? exp2f(glast[b] - Lg[s * ng + j]) : En[s];
             rw[b] = Rs[s * nv + j] * w;
           }
-#pragma unroll
-          for (int a = 0; a < 4; ++a) xv[a] = Xs[s * L.xp + fr[a]];
+          const float4 xv = ld4(Xs + s * L.xp + fb);
 #pragma unroll
           for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int b = 0; b < NB; ++b) sacc[a][b] = fmaf(xv[a], rw[b], sacc[a][b]);
+            for (int b = 0; b < NB; ++b) sacc[a][b] = fmaf(comp(xv, a), rw[b], sacc[a][b]);
         }
+        if (own) {
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
-          if (a0 + a < mk) {
+          for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int b = 0; b < NB; ++b) Ss[fr[a] * nv + tx + 16 * b] = sacc[a][b];
-          }
+            for (int b = 0; b < NB; ++b) Ss[(fb + a) * nv + tx + 16 * b] = sacc[a][b];
+        }
       }
     }
   }
