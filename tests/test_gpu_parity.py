@@ -324,3 +324,33 @@ def test_short_sequences(entry, case):
                   k_prev=kp.cuda())
     torch.cuda.synchronize()
     check(o, S_T, O_ref, S_ref, TOL[io], f"{entry} short {case}")
+
+
+# ---- general chunked kernel: every value-tile width ---------------------------
+
+# The general kernel narrows its value tile (64 -> 32 -> 16 columns) while the
+# narrower tiles still give no more workgroups than the 256 CUs, so small
+# batches run 16-column tiles; these batches keep 32- and 64-column tiles
+# (and the LDS-driven 32-column tile of a per-column rule at dk = dv = 128).
+GENERAL_TILES = [
+    # (variant, io, B, H, T, dk, dv, C)                    value tile
+    ("falcon1", "f32", 8, 12, 130, 64, 64, 64),            # 32: B*H = 96
+    ("falcon2", "f32", 8, 12, 100, 64, 64, 32),            # 32
+    ("falcon1a", "bf16", 16, 16, 70, 64, 64, 32),          # 64: B*H = 256
+    ("falcon2a", "f32", 16, 16, 50, 32, 64, 16),           # 64, dk = 32
+    ("falcon1", "bf16", 4, 40, 90, 128, 64, 32),           # 64, dk = 128 (two key-row groups)
+    ("falcon2", "bf16", 2, 64, 40, 128, 128, 64),          # 32 (LDS), two tiles per sequence
+]
+
+
+@pytest.mark.parametrize("case", GENERAL_TILES, ids=lambda c: "-".join(map(str, c)))
+def test_general_kernel_value_tiles(case):
+    variant, io, B, H, T, dk, dv, C = case
+    per_col = variant in ("falcon2", "falcon2a")
+    d = I.make_inputs(B, H, T, dk, dv, seed=300 + T, io_dtype=io, per_column_beta=per_col)
+    S0 = I.random_state((B, H, dk, dv), seed=301)
+    kp = I.make_inputs(B, H, 1, dk, dv, seed=302, io_dtype=io)["phi_k"][:, :, 0].contiguous()
+    O_ref, S_ref = oracle_forward(variant, d, S0=S0, k_prev=kp)
+    o, S_T = _run("chunked", to_dev(d), variant, C=C, S0=S0.cuda(), k_prev=kp.cuda())
+    torch.cuda.synchronize()
+    check(o, S_T, O_ref, S_ref, TOL[io], f"general tiles {case}")
