@@ -215,7 +215,38 @@ chunked_generic_kernel(const IO* __restrict__ phi_k, const IO* __restrict__ phi_
     }
     lds_barrier();
 
-    // ---- products that need no gate: Q X^T, X X^T, Q S, X S; energies ------
+    constexpr float kLog2e = 1.44269504088896341f;
+    // ---- a1, scalar gates: wave 0 forms the energies, step sizes and the
+    // prefix g (one row per lane, scan across the wave) before its share of
+    // the products, so the decays fold into P and G as they are stored
+    if constexpr (!kPerCol) {
+      if (tid < 64) {
+        float eta = 0.f, lg = 0.f;
+        const int t = t0 + tid;
+        if (tid < C && t < T) {
+          float en = 0.f;
+          for (int f = 0; f < dk; f += 4) {
+            const float4 x = ld4(Xs + tid * L.xp + f);
+            en = dot4(x, x, en);
+          }
+          eta = nlms_eta(Eta[tid], en, Lm[tid], eps, fresh && t == 0);
+          lg = clamped_log_gamma(eta, Lm[tid], eps_gamma) * kLog2e;
+        }
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const float y = __shfl_up(lg, d, 64);
+          if (tid >= d) lg += y;
+        }
+        const float glast = __shfl(lg, C - 1, 64);
+        if (tid < C) {
+          Eta[tid] = eta;
+          Lg[tid] = lg;
+          En[tid] = exp2f(glast - lg);   // state-update weight 2^{g_{C-1}-g_s}
+        }
+      }
+    }
+
+    // ---- products: Q X^T, X X^T, Q S, X S ----------------------------------
     float pa[MC][MC], ga[MC][MC], qs[MC][NB], xs[MC][NB];
 #pragma unroll
     for (int a = 0; a < MC; ++a) {
@@ -254,47 +285,28 @@ chunked_generic_kernel(const IO* __restrict__ phi_k, const IO* __restrict__ phi_
         }
       }
     }
-#pragma unroll
-    for (int a = 0; a < MC; ++a) {
-      const int i = ty + 16 * a;
-#pragma unroll
-      for (int b = 0; b < MC; ++b) {
-        const int s = tx + 16 * b;
-        Ps[i * L.pp + s] = s <= i ? pa[a][b] : 0.f;
-        if (kReg) Gs[i * L.pp + s] = s < i ? ga[a][b] : 0.f;
-      }
-    }
-    if (tid < C) {
-      float en = 0.f;
-      for (int f = 0; f < dk; f += 4) {
-        const float4 x = ld4(Xs + tid * L.xp + f);
-        en = dot4(x, x, en);
-      }
-      En[tid] = en;
-    }
-    lds_barrier();
 
-    // ---- a1: step sizes and log decays, then the prefix g ------------------
-    constexpr float kLog2e = 1.44269504088896341f;
-    if constexpr (!kPerCol) {
-      if (tid < 64) {   // wave 0: one row per lane, scan across the wave
-        float eta = 0.f, lg = 0.f;
-        const int t = t0 + tid;
-        if (tid < C && t < T) {
-          eta = nlms_eta(Eta[tid], En[tid], Lm[tid], eps, fresh && t == 0);
-          lg = clamped_log_gamma(eta, Lm[tid], eps_gamma) * kLog2e;
-        }
+    if constexpr (kPerCol) {
+      // ---- per-column gates follow the products ------------------------------
 #pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-          const float y = __shfl_up(lg, d, 64);
-          if (tid >= d) lg += y;
-        }
-        if (tid < C) {
-          Eta[tid] = eta;
-          Lg[tid] = lg;
+      for (int a = 0; a < MC; ++a) {
+        const int i = ty + 16 * a;
+#pragma unroll
+        for (int b = 0; b < MC; ++b) {
+          const int s = tx + 16 * b;
+          Ps[i * L.pp + s] = s <= i ? pa[a][b] : 0.f;
+          if (kReg) Gs[i * L.pp + s] = s < i ? ga[a][b] : 0.f;
         }
       }
-    } else {
+      if (tid < C) {
+        float en = 0.f;
+        for (int f = 0; f < dk; f += 4) {
+          const float4 x = ld4(Xs + tid * L.xp + f);
+          en = dot4(x, x, en);
+        }
+        En[tid] = en;
+      }
+      lds_barrier();
       for (int e = tid; e < C * ng; e += kThreads) {
         const int i = e >> (lv + 2);
         const int t = t0 + i;
@@ -315,7 +327,7 @@ chunked_generic_kernel(const IO* __restrict__ phi_k, const IO* __restrict__ phi_
         }
       }
     }
-    lds_barrier();
+    lds_barrier();   // gates and prefix visible
 
     // ---- right-hand side; masked (and, for scalar gates, decayed) P and G --
 #pragma unroll
@@ -335,15 +347,16 @@ chunked_generic_kernel(const IO* __restrict__ phi_k, const IO* __restrict__ phi_
         }
       }
       if constexpr (!kPerCol) {
+        const float gi = Lg[i], gi1 = i > 0 ? Lg[i - 1] : 0.f, ei = Eta[i];
 #pragma unroll
         for (int b = 0; b < MC; ++b) {
           const int s = tx + 16 * b;
-          if (s <= i) Ps[i * L.pp + s] *= exp2f(Lg[i] - Lg[s]);
-          if (kReg && s < i) Gs[i * L.pp + s] *= Eta[i] * exp2f(Lg[i - 1] - Lg[s]);
+          const float gs = Lg[s];
+          Ps[i * L.pp + s] = (b <= a && s <= i) ? pa[a][b] * exp2f(gi - gs) : 0.f;
+          if (kReg) Gs[i * L.pp + s] = (b <= a && s < i) ? ga[a][b] * ei * exp2f(gi1 - gs) : 0.f;
         }
       }
     }
-    if (!kPerCol && tid < C) En[tid] = exp2f(Lg[C - 1] - Lg[tid]);
     lds_barrier();
 
     // ---- a2/a3: forward substitution of the merged residual system --------
