@@ -408,24 +408,49 @@ chunked_generic_kernel(const IO* __restrict__ phi_k, const IO* __restrict__ phi_
               gB[rr] = i > 0 ? Lg[(i - 1) * ng + j] : 0.f;
             }
           }
+          if constexpr (kPerCol) {
+            // per-column gates: the decay 2^{g_{i-1}-g_s} between two rows of
+            // the block is the product of the gammas of rows s+1..i-1; each row
+            // walks its terms from s = i-1 down, extending the product, so the
+            // decays never wait on the unknowns.  gm[m] = gamma of row B0 + m.
+            float gm[16];
 #pragma unroll
-          for (int rr = 1; rr < 16; ++rr) {
-            const float* gi = Gs + (B0 + rr) * L.pp + B0;
-            float a0 = 0.f, a1 = 0.f;
+            for (int m = 1; m < 15; ++m) gm[m] = exp2f(gB[m + 1] - gB[m]);
 #pragma unroll
-            for (int s4 = 0; s4 < rr; s4 += 4) {
-              const float4 g = ld4(gi + s4);
+            for (int rr = 1; rr < 16; ++rr) {
+              const float* gi = Gs + (B0 + rr) * L.pp + B0;
+              float4 gv[4];
 #pragma unroll
-              for (int k = 0; k < 4; ++k) {
-                if (s4 + k < rr) {
-                  float cf = comp(g, k);
-                  if (kPerCol) cf *= eB[rr] * exp2f(gB[rr] - Lg[(B0 + s4 + k) * ng + j]);
-                  if (k & 1) a1 = fmaf(cf, r[s4 + k], a1);
-                  else a0 = fmaf(cf, r[s4 + k], a0);
+              for (int q = 0; q < 4; ++q)
+                if (4 * q < rr) gv[q] = ld4(gi + 4 * q);
+              float d = eB[rr], a0 = 0.f, a1 = 0.f;
+#pragma unroll
+              for (int ss = rr - 1; ss >= 0; --ss) {
+                const float cf = comp(gv[ss >> 2], ss & 3) * d;
+                if (ss & 1) a1 = fmaf(cf, r[ss], a1);
+                else a0 = fmaf(cf, r[ss], a0);
+                if (ss > 0) d *= gm[ss];
+              }
+              r[rr] -= a0 + a1;
+            }
+          } else {
+#pragma unroll
+            for (int rr = 1; rr < 16; ++rr) {
+              const float* gi = Gs + (B0 + rr) * L.pp + B0;
+              float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+              for (int s4 = 0; s4 < rr; s4 += 4) {
+                const float4 g = ld4(gi + s4);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                  if (s4 + k < rr) {
+                    if (k & 1) a1 = fmaf(comp(g, k), r[s4 + k], a1);
+                    else a0 = fmaf(comp(g, k), r[s4 + k], a0);
+                  }
                 }
               }
+              r[rr] -= a0 + a1;
             }
-            r[rr] -= a0 + a1;
           }
 #pragma unroll
           for (int rr = 0; rr < 16; ++rr) Rs[(B0 + rr) * nv + j] = r[rr];
