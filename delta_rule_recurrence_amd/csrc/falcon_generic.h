@@ -13,7 +13,7 @@ constexpr int kGenericThreads = 256;
 struct GenericLayout {
   int C, dk, nv, ng;   // chunk, key width, value tile, gate columns (1 or nv)
   int xp, pp;          // row pitches of X, Q (dk + 4) and of P, G (C + 4)
-  int off_x, off_q, off_p, off_g, off_r, off_s, off_eta, off_lg, off_en, off_lm, total;
+  int off_x, off_q, off_p, off_g, off_r, off_s, off_eta, off_lg, off_en, off_lm, off_y, total;
   __host__ __device__ GenericLayout(int C_, int dk_, int nv_, int ng_, bool reg)
       : C(C_), dk(dk_), nv(nv_), ng(ng_), xp(dk_ + 4), pp(C_ + 4) {
     off_x = 0;
@@ -26,7 +26,8 @@ struct GenericLayout {
     off_lg = off_eta + C * ng;
     off_en = off_lg + C * ng;
     off_lm = off_en + C;
-    total = off_lm + C;
+    off_y = off_lm + C;
+    total = off_y + (ng > 1 ? C * nv : 0);   // per-column rules: decay-scaled rho
   }
 };
 

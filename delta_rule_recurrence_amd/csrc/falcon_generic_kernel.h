@@ -38,9 +38,11 @@
 // groups of four), so no multiply-add sits behind a run-time guard.  Each
 // chunk's inputs are loaded into registers in one batch at the top of the
 // chunk and staged into LDS.  The substitution runs one thread per value
-// column in 16-row blocks, the block's unknowns in registers.  Sums stop at
-// the diagonal (s <= i), never multiplying a masked zero by a later row's
-// value, so a non-finite input reaches no earlier output.
+// column in 16-row blocks, the block's unknowns in registers; per-column
+// rules also keep the solved unknowns scaled by the decay to their block's
+// last row, so sums over a whole earlier block take one exp2 per column.
+// Sums stop at the diagonal (s <= i), never multiplying a masked zero by a
+// later row's value, so a non-finite input reaches no earlier output.
 #pragma once
 
 #include "falcon_device.h"
@@ -122,6 +124,10 @@ chunked_generic_kernel(const IO* __restrict__ phi_k, const IO* __restrict__ phi_
   float* Lg = lds + L.off_lg;     // [C][ng]  inclusive prefix g of log2 gamma
   float* En = lds + L.off_en;     // [C]      energies x_i.x_i, then 2^{g_{C-1}-g_s}
   float* Lm = lds + L.off_lm;     // [C]      lam
+  // [C][nv], per-column rules: Y_s = rho_s 2^{g_{P0+15}-g_s} for s in the
+  // 16-row block starting at P0 (every factor <= 1), so a sum over a whole
+  // earlier block needs one exp2 per column instead of one per term
+  float* Ys = lds + L.off_y;
 
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
   // The value tiles of one sequence are workgroups 8k + x for one x: consecutive
@@ -344,6 +350,7 @@ chunked_generic_kernel(const IO* __restrict__ phi_k, const IO* __restrict__ phi_
           r = eta * fmaf(exp2f(gprev), -xs[a][b], r);   // eta (v - 2^{g_{i-1}} X S)
         } else {
           r = eta * r;
+          if (kPerCol) Ys[i * nv + j] = r * exp2f(Lg[(16 * a + 15) * ng + j] - Lg[i * ng + j]);
         }
       }
       if constexpr (!kPerCol) {
@@ -376,17 +383,23 @@ chunked_generic_kernel(const IO* __restrict__ phi_k, const IO* __restrict__ phi_
             // g_ref = g_{B0-1}; both factors are <= 1 since g never increases
             gref[b] = kPerCol ? Lg[(B0 - 1) * ng + tx + 16 * b] : 0.f;
           }
-          for (int s0 = 0; s0 < B0; s0 += 4) {
-            const float4 g = ld4(Gs + i * L.pp + s0);
+          for (int P0 = 0; P0 < B0; P0 += 16) {
+            float sc[NB];   // per-column gates: 2^{g_ref-g_{P0+15}} <= 1 rescales Y
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
+            for (int b = 0; b < NB; ++b)
+              sc[b] = kPerCol ? exp2f(gref[b] - Lg[(P0 + 15) * ng + tx + 16 * b]) : 1.f;
 #pragma unroll
-              for (int b = 0; b < NB; ++b) {
-                const int j = tx + 16 * b;
-                float rv = Rs[(s0 + k) * nv + j];
-                if (kPerCol) rv *= exp2f(gref[b] - Lg[(s0 + k) * ng + j]);
-                acc[b] = fmaf(comp(g, k), rv, acc[b]);
-              }
+            for (int s0 = P0; s0 < P0 + 16; s0 += 4) {
+              const float4 g = ld4(Gs + i * L.pp + s0);
+#pragma unroll
+              for (int k = 0; k < 4; ++k)
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                  const int j = tx + 16 * b;
+                  const float rv = kPerCol ? Ys[(s0 + k) * nv + j] * sc[b] : Rs[(s0 + k) * nv + j];
+                  acc[b] = fmaf(comp(g, k), rv, acc[b]);
+                }
+            }
           }
 #pragma unroll
           for (int b = 0; b < NB; ++b) {
@@ -416,6 +429,7 @@ chunked_generic_kernel(const IO* __restrict__ phi_k, const IO* __restrict__ phi_
             float gm[16];
 #pragma unroll
             for (int m = 1; m < 15; ++m) gm[m] = exp2f(gB[m + 1] - gB[m]);
+            gm[0] = 1.f;
 #pragma unroll
             for (int rr = 1; rr < 16; ++rr) {
               const float* gi = Gs + (B0 + rr) * L.pp + B0;
@@ -432,6 +446,15 @@ chunked_generic_kernel(const IO* __restrict__ phi_k, const IO* __restrict__ phi_
                 if (ss > 0) d *= gm[ss];
               }
               r[rr] -= a0 + a1;
+            }
+            // decay-scaled copy: Y_{B0+ss} = r_ss prod_{m=ss+1..15} gamma_{B0+m}
+            gm[15] = exp2f(Lg[(B0 + 15) * ng + j] - gB[15]);
+            float fsc = 1.f;
+            Ys[(B0 + 15) * nv + j] = r[15];
+#pragma unroll
+            for (int ss = 14; ss >= 0; --ss) {
+              fsc *= gm[ss + 1];
+              Ys[(B0 + ss) * nv + j] = r[ss] * fsc;
             }
           } else {
 #pragma unroll
@@ -470,37 +493,91 @@ chunked_generic_kernel(const IO* __restrict__ phi_k, const IO* __restrict__ phi_
           gi[a][b] = Lg[i * ng + (kPerCol ? j : 0)];
           acc[a][b] = exp2f(gi[a][b]) * qs[a][b];
         }
-      constexpr int kStepUnroll = kPerCol ? 1 : 4;   // one exp per term keeps per-column code small
+      if constexpr (!kPerCol) {
+        // P carries the decays: plain sums, the select only in the diagonal block
 #pragma unroll 1
-      for (int sb = 0; sb < MC; ++sb) {
-#pragma unroll kStepUnroll
-        for (int s4 = 0; s4 < 16; s4 += 4) {
-          const int s = 16 * sb + s4;
-          float rv[4][NB], gs[4][NB];
+        for (int sb = 0; sb < MC; ++sb) {
+#pragma unroll 4
+          for (int s4 = 0; s4 < 16; s4 += 4) {
+            const int s = 16 * sb + s4;
+            float rv[4][NB];
 #pragma unroll
-          for (int k = 0; k < 4; ++k)
+            for (int k = 0; k < 4; ++k)
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-              rv[k][b] = Rs[(s + k) * nv + tx + 16 * b];
-              if (kPerCol) gs[k][b] = Lg[(s + k) * ng + tx + 16 * b];
-            }
+              for (int b = 0; b < NB; ++b) rv[k][b] = Rs[(s + k) * nv + tx + 16 * b];
 #pragma unroll
-          for (int a = 0; a < MC; ++a) {
-            if (a < sb) continue;   // above the diagonal (static index, uniform skip)
-            const float4 p = ld4(Ps + (ty + 16 * a) * L.pp + s);
+            for (int a = 0; a < MC; ++a) {
+              if (a < sb) continue;   // above the diagonal (static index, uniform skip)
+              const float4 p = ld4(Ps + (ty + 16 * a) * L.pp + s);
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              // in the diagonal block only the columns s <= i take part
-              const bool on = a > sb || s4 + k <= ty;
+              for (int k = 0; k < 4; ++k) {
+                // in the diagonal block only the columns s <= i take part
+                const bool on = a > sb || s4 + k <= ty;
 #pragma unroll
-              for (int b = 0; b < NB; ++b) {
-                float cf = comp(p, k);
-                if (kPerCol) cf *= exp2f(gi[a][b] - gs[k][b]);
-                const float nx = fmaf(cf, rv[k][b], acc[a][b]);
-                acc[a][b] = on ? nx : acc[a][b];
+                for (int b = 0; b < NB; ++b) {
+                  const float nx = fmaf(comp(p, k), rv[k][b], acc[a][b]);
+                  acc[a][b] = on ? nx : acc[a][b];
+                }
               }
             }
           }
+        }
+      } else {
+        // per-column gates: an earlier block sb contributes
+        // 2^{g_i - g_end} sum_s P_is Y_s (g_end = g_{16 sb + 15}, one exp2 per
+        // block and column); the diagonal block takes one exp2 per term
+#pragma unroll 1
+        for (int sb = 0; sb < MC; ++sb) {
+          float gend[NB], part[MC][NB];
+#pragma unroll
+          for (int b = 0; b < NB; ++b) gend[b] = Lg[(16 * sb + 15) * ng + tx + 16 * b];
+#pragma unroll
+          for (int a = 0; a < MC; ++a)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) part[a][b] = 0.f;
+#pragma unroll 1
+          for (int s4 = 0; s4 < 16; s4 += 4) {
+            const int s = 16 * sb + s4;
+            float yv[4][NB], rv[4][NB], gs[4][NB];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+#pragma unroll
+              for (int b = 0; b < NB; ++b) {
+                const int j = tx + 16 * b;
+                yv[k][b] = Ys[(s + k) * nv + j];
+                rv[k][b] = Rs[(s + k) * nv + j];
+                gs[k][b] = Lg[(s + k) * ng + j];
+              }
+#pragma unroll
+            for (int a = 0; a < MC; ++a) {
+              if (a < sb) continue;   // above the diagonal (static index, uniform skip)
+              const float4 p = ld4(Ps + (ty + 16 * a) * L.pp + s);
+              if (a > sb) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+#pragma unroll
+                  for (int b = 0; b < NB; ++b) part[a][b] = fmaf(comp(p, k), yv[k][b], part[a][b]);
+              } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                  const bool on = s4 + k <= ty;   // columns s <= i only
+#pragma unroll
+                  for (int b = 0; b < NB; ++b) {
+                    const float cf = comp(p, k) * exp2f(gi[a][b] - gs[k][b]);
+                    const float nx = fmaf(cf, rv[k][b], acc[a][b]);
+                    acc[a][b] = on ? nx : acc[a][b];
+                  }
+                }
+              }
+            }
+          }
+#pragma unroll
+          for (int a = 0; a < MC; ++a)
+            if (a > sb) {
+#pragma unroll
+              for (int b = 0; b < NB; ++b)
+                acc[a][b] = fmaf(exp2f(gi[a][b] - gend[b]), part[a][b], acc[a][b]);
+            }
         }
       }
 #pragma unroll
@@ -533,20 +610,25 @@ chunked_generic_kernel(const IO* __restrict__ phi_k, const IO* __restrict__ phi_
         for (int a = 0; a < 4; ++a)
 #pragma unroll
           for (int b = 0; b < NB; ++b) sacc[a][b] = dlast[b] * Ss[(fb + a) * nv + tx + 16 * b];
+        for (int P0 = 0; P0 < C; P0 += 16) {
+          float sc[NB];   // per-column gates: 2^{g_{C-1}-g_{P0+15}} <= 1 rescales Y
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+            sc[b] = kPerCol ? exp2f(glast[b] - Lg[(P0 + 15) * ng + tx + 16 * b]) : 1.f;
 #pragma unroll 4
-        for (int s = 0; s < C; ++s) {
-          float rw[NB];
+          for (int s = P0; s < P0 + 16; ++s) {
+            float rw[NB];
 #pragma unroll
-          for (int b = 0; b < NB; ++b) {
-            const int j = tx + 16 * b;
-            const float w = kPerCol ? exp2f(glast[b] - Lg[s * ng + j]) : En[s];
-            rw[b] = Rs[s * nv + j] * w;
+            for (int b = 0; b < NB; ++b) {
+              const int j = tx + 16 * b;
+              rw[b] = kPerCol ? Ys[s * nv + j] * sc[b] : Rs[s * nv + j] * En[s];
+            }
+            const float4 xv = ld4(Xs + s * L.xp + fb);
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+              for (int b = 0; b < NB; ++b) sacc[a][b] = fmaf(comp(xv, a), rw[b], sacc[a][b]);
           }
-          const float4 xv = ld4(Xs + s * L.xp + fb);
-#pragma unroll
-          for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int b = 0; b < NB; ++b) sacc[a][b] = fmaf(comp(xv, a), rw[b], sacc[a][b]);
         }
         if (own) {
 #pragma unroll
