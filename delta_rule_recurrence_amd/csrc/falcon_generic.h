@@ -12,17 +12,17 @@ constexpr int kGenericThreads = 256;
 
 struct GenericLayout {
   int C, dk, nv, ng;   // chunk, key width, value tile, gate columns (1 or nv)
-  int xp, pp;          // row pitches of X, Q (dk + 4) and of P, G (C + 4)
+  int xp, pp, sp;      // row pitches of X, Q (dk + 4), of P, G (C + 4) and of S^T (dk + 4)
   int off_x, off_q, off_p, off_g, off_r, off_s, off_eta, off_lg, off_en, off_lm, off_y, total;
   __host__ __device__ GenericLayout(int C_, int dk_, int nv_, int ng_, bool reg)
-      : C(C_), dk(dk_), nv(nv_), ng(ng_), xp(dk_ + 4), pp(C_ + 4) {
+      : C(C_), dk(dk_), nv(nv_), ng(ng_), xp(dk_ + 4), pp(C_ + 4), sp(dk_ + 4) {
     off_x = 0;
     off_q = off_x + C * xp;
-    off_p = off_q + C * xp;
+    off_p = off_q + C * (xp > nv ? xp : nv);   // Q, then Q S
     off_g = off_p + C * pp;
     off_r = off_g + (reg ? C * pp : 0);
     off_s = off_r + C * nv;
-    off_eta = off_s + dk * nv;
+    off_eta = off_s + nv * sp;
     off_lg = off_eta + C * ng;
     off_en = off_lg + C * ng;
     off_lm = off_en + C;

@@ -45,6 +45,8 @@
 // later row's value, so a non-finite input reaches no earlier output.
 #pragma once
 
+#include <type_traits>
+
 #include "falcon_device.h"
 #include "falcon_generic.h"
 
@@ -85,6 +87,35 @@ __device__ __forceinline__ float comp(float4 a, int k) {
   return k == 0 ? a.x : k == 1 ? a.y : k == 2 ? a.z : a.w;
 }
 
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+// Product tiles of one chunk, in order: P (MC (MC + 1) / 2 tiles on and below
+// the diagonal, row-major), G (same, regression rules only), Q S (MC x NB),
+// X S (regression rules only).  Tile t (wave-uniform) -> kind, row tile ta,
+// column tile tb.
+enum TileKind : int { kTileP = 0, kTileG = 1, kTileQS = 2, kTileXS = 3 };
+template <int MC, int NB, bool kReg>
+__device__ __forceinline__ void decode_tile(int t, int& kind, int& ta, int& tb) {
+  constexpr int nPt = MC * (MC + 1) / 2, nSt = MC * NB;
+  int u = t;
+  if (u < nPt) {
+    kind = kTileP;
+  } else if (kReg && u < 2 * nPt) {
+    kind = kTileG;
+    u -= nPt;
+  } else {
+    u -= kReg ? 2 * nPt : nPt;
+    kind = u < nSt ? kTileQS : kTileXS;
+    if (u >= nSt) u -= nSt;
+    ta = u / NB;
+    tb = u % NB;
+    return;
+  }
+  ta = 0;
+  while ((ta + 1) * (ta + 2) / 2 <= u) ++ta;
+  tb = u - ta * (ta + 1) / 2;
+}
+
 // LDS-only workgroup barrier: orders the workgroup's LDS traffic without
 // waiting for its outstanding global stores.
 __device__ __forceinline__ void lds_barrier() {
@@ -115,11 +146,11 @@ chunked_generic_kernel(const IO* __restrict__ phi_k, const IO* __restrict__ phi_
   float* lds = reinterpret_cast<float*>(lds4);
   const GenericLayout L(C, dk, nv, ng, kReg);
   float* Xs = lds + L.off_x;      // [C][xp]  shifted keys x_i
-  float* Qs = lds + L.off_q;      // [C][xp]  queries
+  float* Qs = lds + L.off_q;      // [C][xp]  queries; after the products Q S as [C][nv]
   float* Ps = lds + L.off_p;      // [C][pp]  q_i.x_s for s <= i (decayed for scalar gates)
   float* Gs = lds + L.off_g;      // [C][pp]  x_i.x_s for s < i (the coupling for scalar gates)
   float* Rs = lds + L.off_r;      // [C][nv]  v, then the right-hand side, then rho
-  float* Ss = lds + L.off_s;      // [dk][nv] state tile
+  float* St = lds + L.off_s;      // [nv][sp] state tile, transposed (S^T)
   float* Eta = lds + L.off_eta;   // [C][ng]  beta, then eta
   float* Lg = lds + L.off_lg;     // [C][ng]  inclusive prefix g of log2 gamma
   float* En = lds + L.off_en;     // [C]      energies x_i.x_i, then 2^{g_{C-1}-g_s}
@@ -145,7 +176,7 @@ chunked_generic_kernel(const IO* __restrict__ phi_k, const IO* __restrict__ phi_
 
   for (int e = tid; e < dk * nv; e += kThreads) {
     const int f = e / nv, j = e % nv;
-    Ss[e] = S0 ? S0[(bh * dk + f) * dv + j0 + j] : 0.0f;
+    St[j * L.sp + f] = S0 ? S0[(bh * dk + f) * dv + j0 + j] : 0.0f;
   }
 
   typename Q4::raw xr[kXQ], qr[kXQ], vr[kV];
@@ -252,41 +283,86 @@ chunked_generic_kernel(const IO* __restrict__ phi_k, const IO* __restrict__ phi_
       }
     }
 
-    // ---- products: Q X^T, X X^T, Q S, X S ----------------------------------
-    float pa[MC][MC], ga[MC][MC], qs[MC][NB], xs[MC][NB];
+    // ---- products on the matrix cores: P = Q X^T and G = X X^T (16 x 16
+    // tiles on and below the diagonal), Q S and X S; tiles dealt round-robin
+    // to the waves.  Each lane reads four consecutive k of its A row and of its
+    // B column, so four MFMAs cover 16 k (A and B share that k permutation, so
+    // every dot product is unchanged).
+    // 64-column tiles (NB = 4) keep the products on the vector ALUs: with 13
+    // MFMA tiles per wave their register needs slowed the later phases more
+    // than the matrix cores saved here.
+    constexpr bool kMfma = NB <= 2;
+    constexpr int nPt = MC * (MC + 1) / 2;             // tiles of P (and of G)
+    constexpr int nSt = MC * NB;                       // tiles of Q S (and of X S)
+    constexpr int nTiles = (nPt + nSt) * (kReg ? 2 : 1);
+    constexpr int kPerWave = (nTiles + 3) / 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), ln = tid & 63;
+    const int lr = ln & 15, lk = 4 * (ln >> 4);
+    f32x4v tacc[kMfma ? kPerWave : 1];
 #pragma unroll
-    for (int a = 0; a < MC; ++a) {
+    for (int q = 0; q < (kMfma ? kPerWave : 1); ++q) tacc[q] = f32x4v{0.f, 0.f, 0.f, 0.f};
+    // one code path per wave, so that each unrolled tile number is a constant
+    // and the tile's kind and place fold at compile time
+    auto products = [&](auto wave) {
+      constexpr int W = decltype(wave)::value;
 #pragma unroll
-      for (int b = 0; b < MC; ++b) pa[a][b] = ga[a][b] = 0.f;
-#pragma unroll
-      for (int b = 0; b < NB; ++b) qs[a][b] = xs[a][b] = 0.f;
-    }
-    for (int f = 0; f < dk; f += 4) {
-      float4 qi[MC], xi[MC], xc[MC];
-#pragma unroll
-      for (int a = 0; a < MC; ++a) {
-        qi[a] = ld4(Qs + (ty + 16 * a) * L.xp + f);
-        if (kReg) xi[a] = ld4(Xs + (ty + 16 * a) * L.xp + f);
-        xc[a] = ld4(Xs + (tx + 16 * a) * L.xp + f);
+      for (int q = 0; q < kPerWave; ++q) {
+        const int t = W + 4 * q;
+        if (t < nTiles) {
+          int kind, ta, tb;
+          decode_tile<MC, NB, kReg>(t, kind, ta, tb);
+          const float* Ap = (kind == kTileP || kind == kTileQS ? Qs : Xs) + (16 * ta + lr) * L.xp + lk;
+          const float* Bp = kind <= kTileG ? Xs + (16 * tb + lr) * L.xp + lk
+                                           : St + (16 * tb + lr) * L.sp + lk;
+#pragma unroll 2
+          for (int f = 0; f < dk; f += 16) {
+            const float4 av = ld4(Ap + f), bv = ld4(Bp + f);
+            tacc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, bv.x, tacc[q], 0, 0, 0);
+            tacc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.y, bv.y, tacc[q], 0, 0, 0);
+            tacc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, bv.z, tacc[q], 0, 0, 0);
+            tacc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.w, bv.w, tacc[q], 0, 0, 0);
+          }
+        }
       }
-      float sv[4][NB];
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-#pragma unroll
-        for (int b = 0; b < NB; ++b) sv[k][b] = Ss[(f + k) * nv + tx + 16 * b];
+    };
+    // register tiles (vector ALUs): rows ty + 16 a, columns tx + 16 b
+    float pa[MC][MC], ga[MC][MC], qs[MC][NB], xs[MC][NB];
+    if constexpr (kMfma) {
+      switch (w) {
+        case 0: products(std::integral_constant<int, 0>{}); break;
+        case 1: products(std::integral_constant<int, 1>{}); break;
+        case 2: products(std::integral_constant<int, 2>{}); break;
+        default: products(std::integral_constant<int, 3>{}); break;
+      }
+    } else {
 #pragma unroll
       for (int a = 0; a < MC; ++a) {
 #pragma unroll
-        for (int b = 0; b <= a; ++b) {   // tiles with b > a lie above the diagonal
-          pa[a][b] = dot4(qi[a], xc[b], pa[a][b]);
-          if (kReg) ga[a][b] = dot4(xi[a], xc[b], ga[a][b]);
+        for (int b = 0; b < MC; ++b) pa[a][b] = ga[a][b] = 0.f;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) qs[a][b] = xs[a][b] = 0.f;
+      }
+      for (int f = 0; f < dk; f += 4) {
+        float4 qi[MC], xi[MC], xc[MC], sv[NB];
+#pragma unroll
+        for (int a = 0; a < MC; ++a) {
+          qi[a] = ld4(Qs + (ty + 16 * a) * L.xp + f);
+          if (kReg) xi[a] = ld4(Xs + (ty + 16 * a) * L.xp + f);
+          xc[a] = ld4(Xs + (tx + 16 * a) * L.xp + f);
         }
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
+        for (int b = 0; b < NB; ++b) sv[b] = ld4(St + (tx + 16 * b) * L.sp + f);
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            qs[a][b] = fmaf(comp(qi[a], k), sv[k][b], qs[a][b]);
-            if (kReg) xs[a][b] = fmaf(comp(xi[a], k), sv[k][b], xs[a][b]);
+        for (int a = 0; a < MC; ++a) {
+#pragma unroll
+          for (int b = 0; b <= a; ++b) {   // tiles with b > a lie above the diagonal
+            pa[a][b] = dot4(qi[a], xc[b], pa[a][b]);
+            if (kReg) ga[a][b] = dot4(xi[a], xc[b], ga[a][b]);
+          }
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            qs[a][b] = dot4(qi[a], sv[b], qs[a][b]);
+            if (kReg) xs[a][b] = dot4(xi[a], sv[b], xs[a][b]);
           }
         }
       }
@@ -294,16 +370,6 @@ chunked_generic_kernel(const IO* __restrict__ phi_k, const IO* __restrict__ phi_
 
     if constexpr (kPerCol) {
       // ---- per-column gates follow the products ------------------------------
-#pragma unroll
-      for (int a = 0; a < MC; ++a) {
-        const int i = ty + 16 * a;
-#pragma unroll
-        for (int b = 0; b < MC; ++b) {
-          const int s = tx + 16 * b;
-          Ps[i * L.pp + s] = s <= i ? pa[a][b] : 0.f;
-          if (kReg) Gs[i * L.pp + s] = s < i ? ga[a][b] : 0.f;
-        }
-      }
       if (tid < C) {
         float en = 0.f;
         for (int f = 0; f < dk; f += 4) {
@@ -335,32 +401,89 @@ chunked_generic_kernel(const IO* __restrict__ phi_k, const IO* __restrict__ phi_
     }
     lds_barrier();   // gates and prefix visible
 
-    // ---- right-hand side; masked (and, for scalar gates, decayed) P and G --
+    // ---- tiles to LDS: P and G masked (and, for scalar gates, decayed), Q S;
+    // X S becomes the right-hand side eta (v - 2^{g_{i-1}} X S) in place
+    // (tile element r of a lane: row 16 ta + lk + r, column 16 tb + lr)
+    auto store_tiles = [&](auto wave) {
+      constexpr int W = decltype(wave)::value;
 #pragma unroll
-    for (int a = 0; a < MC; ++a) {
-      const int i = ty + 16 * a;
+      for (int q = 0; q < kPerWave; ++q) {
+        const int t = W + 4 * q;
+        if (t < nTiles) {
+          int kind, ta, tb;
+          decode_tile<MC, NB, kReg>(t, kind, ta, tb);
+          const int col = 16 * tb + lr;
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const int j = tx + 16 * b;
-        const int cc = kPerCol ? j : 0;
-        const float eta = Eta[i * ng + cc];
-        float& r = Rs[i * nv + j];
-        if (kReg) {
-          const float gprev = i > 0 ? Lg[(i - 1) * ng + cc] : 0.0f;
-          r = eta * fmaf(exp2f(gprev), -xs[a][b], r);   // eta (v - 2^{g_{i-1}} X S)
-        } else {
-          r = eta * r;
-          if (kPerCol) Ys[i * nv + j] = r * exp2f(Lg[(16 * a + 15) * ng + j] - Lg[i * ng + j]);
+          for (int r = 0; r < 4; ++r) {
+            const int i = 16 * ta + lk + r;
+            const float v = tacc[q][r];
+            if (kind == kTileP) {
+              float p = 0.f;
+              if (col <= i) p = kPerCol ? v : v * exp2f(Lg[i] - Lg[col]);
+              Ps[i * L.pp + col] = p;
+            } else if (kind == kTileG) {
+              float g = 0.f;
+              if (col < i) g = kPerCol ? v : v * Eta[i] * exp2f(Lg[max(i - 1, 0)] - Lg[col]);
+              Gs[i * L.pp + col] = g;
+            } else if (kind == kTileQS) {
+              Qs[i * nv + col] = v;
+            } else {
+              const int cc = kPerCol ? col : 0;
+              const float gprev = i > 0 ? Lg[(i - 1) * ng + cc] : 0.0f;
+              float& rr = Rs[i * nv + col];
+              rr = Eta[i * ng + cc] * fmaf(exp2f(gprev), -v, rr);
+            }
+          }
         }
       }
-      if constexpr (!kPerCol) {
-        const float gi = Lg[i], gi1 = i > 0 ? Lg[i - 1] : 0.f, ei = Eta[i];
+    };
+    if constexpr (kMfma) {
+      switch (w) {
+        case 0: store_tiles(std::integral_constant<int, 0>{}); break;
+        case 1: store_tiles(std::integral_constant<int, 1>{}); break;
+        case 2: store_tiles(std::integral_constant<int, 2>{}); break;
+        default: store_tiles(std::integral_constant<int, 3>{}); break;
+      }
+    } else {
+#pragma unroll
+      for (int a = 0; a < MC; ++a) {
+        const int i = ty + 16 * a;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const int j = tx + 16 * b;
+          Qs[i * nv + j] = qs[a][b];
+          if (kReg) {
+            const int cc = kPerCol ? j : 0;
+            const float gprev = i > 0 ? Lg[(i - 1) * ng + cc] : 0.0f;
+            float& r = Rs[i * nv + j];
+            r = Eta[i * ng + cc] * fmaf(exp2f(gprev), -xs[a][b], r);
+          }
+        }
+        const float gi = kPerCol ? 0.f : Lg[i * ng];
+        const float gi1 = kPerCol ? 0.f : Lg[max(i - 1, 0) * ng];
+        const float ei = kPerCol ? 0.f : Eta[i * ng];
 #pragma unroll
         for (int b = 0; b < MC; ++b) {
-          const int s = tx + 16 * b;
-          const float gs = Lg[s];
-          Ps[i * L.pp + s] = (b <= a && s <= i) ? pa[a][b] * exp2f(gi - gs) : 0.f;
-          if (kReg) Gs[i * L.pp + s] = (b <= a && s < i) ? ga[a][b] * ei * exp2f(gi1 - gs) : 0.f;
+          const int s2 = tx + 16 * b;
+          float p = 0.f, g = 0.f;
+          if (b <= a && s2 <= i) p = kPerCol ? pa[a][b] : pa[a][b] * exp2f(gi - Lg[s2 * ng]);
+          if (kReg && b <= a && s2 < i) g = kPerCol ? ga[a][b] : ga[a][b] * ei * exp2f(gi1 - Lg[s2 * ng]);
+          Ps[i * L.pp + s2] = p;
+          if (kReg) Gs[i * L.pp + s2] = g;
+        }
+      }
+    }
+    if constexpr (!kReg) {
+#pragma unroll
+      for (int a = 0; a < MC; ++a) {
+        const int i = ty + 16 * a;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const int j = tx + 16 * b;
+          const int cc = kPerCol ? j : 0;
+          float& r = Rs[i * nv + j];
+          r = Eta[i * ng + cc] * r;   // rho = eta v
+          if (kPerCol) Ys[i * nv + j] = r * exp2f(Lg[(16 * a + 15) * ng + j] - Lg[i * ng + j]);
         }
       }
     }
@@ -491,7 +614,7 @@ chunked_generic_kernel(const IO* __restrict__ phi_k, const IO* __restrict__ phi_
         for (int b = 0; b < NB; ++b) {
           const int i = ty + 16 * a, j = tx + 16 * b;
           gi[a][b] = Lg[i * ng + (kPerCol ? j : 0)];
-          acc[a][b] = exp2f(gi[a][b]) * qs[a][b];
+          acc[a][b] = exp2f(gi[a][b]) * Qs[i * nv + j];   // Q S
         }
       if constexpr (!kPerCol) {
         // P carries the decays: plain sums, the select only in the diagonal block
@@ -607,9 +730,11 @@ chunked_generic_kernel(const IO* __restrict__ phi_k, const IO* __restrict__ phi_
         const int fb = (f0 + 4 * ty) & (dk - 1);
         float sacc[4][NB];
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+        for (int b = 0; b < NB; ++b) {
+          const float4 s4v = ld4(St + (tx + 16 * b) * L.sp + fb);
 #pragma unroll
-          for (int b = 0; b < NB; ++b) sacc[a][b] = dlast[b] * Ss[(fb + a) * nv + tx + 16 * b];
+          for (int a = 0; a < 4; ++a) sacc[a][b] = dlast[b] * comp(s4v, a);
+        }
         for (int P0 = 0; P0 < C; P0 += 16) {
           float sc[NB];   // per-column gates: 2^{g_{C-1}-g_{P0+15}} <= 1 rescales Y
 #pragma unroll
@@ -632,9 +757,9 @@ chunked_generic_kernel(const IO* __restrict__ phi_k, const IO* __restrict__ phi_
         }
         if (own) {
 #pragma unroll
-          for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int b = 0; b < NB; ++b) Ss[(fb + a) * nv + tx + 16 * b] = sacc[a][b];
+          for (int b = 0; b < NB; ++b)
+            st4(St + (tx + 16 * b) * L.sp + fb,
+                make_float4(sacc[0][b], sacc[1][b], sacc[2][b], sacc[3][b]));
         }
       }
     }
@@ -643,7 +768,7 @@ chunked_generic_kernel(const IO* __restrict__ phi_k, const IO* __restrict__ phi_
   if (S_T) {
     for (int e = tid; e < dk * nv; e += kThreads) {
       const int f = e / nv, j = e % nv;
-      S_T[(bh * dk + f) * dv + j0 + j] = Ss[e];
+      S_T[(bh * dk + f) * dv + j0 + j] = St[j * L.sp + f];
     }
   }
 }

@@ -21,8 +21,18 @@ SOURCES = sorted(f for f in os.listdir(B.CSRC) if f.endswith(".hip"))
 
 
 def _masked_mfmas(asm: str):
+    """Linear scan: a saveexec opens a masked region (skipped on an empty mask
+    when s_cbranch_execz follows), a restoring s_or_b64 / s_mov_b64 of exec
+    closes it.  A saveexec followed by s_cbranch_execnz and an unconditional
+    s_branch is a region the block layout placed at the branch target (a
+    rotated loop): the text after it is reached only through labels, so it
+    leaves the scan's state unchanged."""
     bad, masked, skipped, fn = [], False, False, "?"
     lines = asm.split("\n")
+
+    def nxt(i, k):
+        return lines[i + k].strip() if i + k < len(lines) else ""
+
     for i, line in enumerate(lines):
         if re.match(r"^_Z\S+:", line):
             # a new function starts unmasked
@@ -30,8 +40,10 @@ def _masked_mfmas(asm: str):
             masked, skipped = False, False
         s = line.strip()
         if re.match(r"s_(and|andn2|xor|or)_saveexec", s):
+            if nxt(i, 1).startswith("s_cbranch_execnz") and nxt(i, 2).startswith("s_branch"):
+                continue
             masked = True
-            skipped = i + 1 < len(lines) and lines[i + 1].strip().startswith("s_cbranch_execz")
+            skipped = nxt(i, 1).startswith("s_cbranch_execz")
         elif s.startswith("s_or_b64 exec") or s.startswith("s_mov_b64 exec"):
             masked = False
         elif s.startswith("v_mfma") and masked and not skipped:
