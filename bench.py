@@ -141,9 +141,10 @@ def bench_chunked_workload(name, steps=20, warmup=3):
 
     w = I.WORKLOADS[name]
     d = {k: v.cuda() for k, v in I.workload_inputs(w).items()}
-    o = torch.empty((w.B, w.H, w.T, w.dv), dtype=torch.bfloat16, device="cuda")
+    io = I.TORCH_DTYPE[w.io_dtype]
+    o = torch.empty((w.B, w.H, w.T, w.dv), dtype=io, device="cuda")
     S_T = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
-    p = fb.make_problem(w.B, w.H, w.T, w.dk, w.dv, variant=w.variant, io_dtype=torch.bfloat16,
+    p = fb.make_problem(w.B, w.H, w.T, w.dk, w.dv, variant=w.variant, io_dtype=io,
                         eps=w.eps, eps_gamma=w.eps_gamma)
     ws = torch.empty(max(fb.falcon_workspace_bytes(p, w.C), 16), dtype=torch.uint8, device="cuda")
 
@@ -162,10 +163,10 @@ def bench_chunked_workload(name, steps=20, warmup=3):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    nbytes = algorithmic_bytes(w.B, w.H, w.T, w.dk, w.dv,
+    nbytes = algorithmic_bytes(w.B, w.H, w.T, w.dk, w.dv, io_bytes=4 if w.io_dtype == "f32" else 2,
                                per_column_beta=w.variant in ("falcon2", "falcon2a"))
     gbs = nbytes / (ms * 1e-3) / 1e9
-    out = {"workload": name, "variant": w.variant, "steps": steps, "us_per_step": ms * 1e3,
+    out = {"workload": name, "variant": w.variant, "io": w.io_dtype, "steps": steps, "us_per_step": ms * 1e3,
            "tokens_per_s": w.B * w.T / (ms * 1e-3), "algorithmic_bytes": nbytes,
            "workspace_bytes": int(ws.numel()), "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
     if w.variant in ("falcon2", "falcon2a"):
@@ -175,6 +176,11 @@ def bench_chunked_workload(name, steps=20, warmup=3):
         out["roofline"] = {"bound": "alu", "achieved": tf, "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                            "frac": tf / FP32_VALU_PEAK_TFLOPS, "traffic": None, "algorithmic_flops": flops,
                            "kernels": ["falcon2_chunked_kernel"]}
+    elif w.io_dtype == "f32":
+        # the general chunked kernel: chunks of a sequence are dependent and one
+        # workgroup fills a CU's LDS
+        out["bound"] = "latency (dependent chunks per sequence, one wave per SIMD)"
+        out["kernels"] = ["chunked_generic_kernel"]
     elif w.variant == "falcon1a":
         out["roofline"] = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": gbs / HBM_PEAK_GBS, "traffic": None, "algorithmic_bytes": nbytes,
@@ -532,6 +538,7 @@ def main():
         rb = line["f1_backward"]["roofline"]
         rb["frac_of_measured_fp32_gemm"] = rb["achieved"] / line["measured_peaks"]["fp32_gemm_tflops"]
         line["f1_recurrent"] = bench_recurrent()
+        line["f1_chunked_f32"] = bench_chunked_workload("f1_chunked_f32_8x12x2048_d64", steps=5, warmup=1)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(d, w, o, S_T)
         # the oracle beside every other workload, on a bounded sample each
@@ -543,6 +550,8 @@ def main():
             line["f1_backward"]["cpu_oracle"] = oracle_sample("backward")
             # the recurrent entry point computes the headline workload: same oracle figure
             line["f1_recurrent"]["cpu_oracle"] = dict(line["cpu_baseline"])
+            # the same recurrence in float32 I/O (the oracle computes in fp64 either way)
+            line["f1_chunked_f32"]["cpu_oracle"] = dict(line["cpu_baseline"])
     print(json.dumps(line))
 
 

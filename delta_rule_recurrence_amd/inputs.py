@@ -43,7 +43,7 @@ class Workload:
     eps_gamma: float = 1e-6
 
 
-# The five workloads the build is measured and checked on.
+# The workloads the build is measured and checked on.
 WORKLOADS = {
     "f1_recurrent_tiny": Workload("f1_recurrent_tiny", "falcon1", 1, 1, 64, 16, 16, 16, "f32", 0),
     "f1_chunked_8x12x2048_d64": Workload("f1_chunked_8x12x2048_d64", "falcon1", 8, 12, 2048, 64, 64, 64, "bf16", 1),
@@ -51,6 +51,8 @@ WORKLOADS = {
     "f2_chunked_8x12x2048_d64": Workload("f2_chunked_8x12x2048_d64", "falcon2", 8, 12, 2048, 64, 64, 64, "bf16", 3),
     # the backward of the Falcon-1 training shape (C names the forward's chunk)
     "f1_backward_8x12x2048_d64": Workload("f1_backward_8x12x2048_d64", "falcon1", 8, 12, 2048, 64, 64, 64, "bf16", 5),
+    # the training shape with float32 I/O: served by the general chunked kernel
+    "f1_chunked_f32_8x12x2048_d64": Workload("f1_chunked_f32_8x12x2048_d64", "falcon1", 8, 12, 2048, 64, 64, 64, "f32", 6),
 }
 
 # Decode workload: batch 512, 12 heads, d = 128, 1000 steps after a prefix.

@@ -15,7 +15,7 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("name", ["f1_chunked_8x12x2048_d64", "f1a_chunked_2x12x16384_d64",
-                                  "f2_chunked_8x12x2048_d64"])
+                                  "f2_chunked_8x12x2048_d64", "f1_chunked_f32_8x12x2048_d64"])
 def test_full_workload(name):
     w = I.WORKLOADS[name]
     d = I.workload_inputs(w)
