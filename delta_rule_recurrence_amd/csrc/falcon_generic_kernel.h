@@ -1,8 +1,10 @@
 // Chunk-parallel Falcon forward, general-shape float32 kernel (gfx950).
 //
-// Serves every (variant, dtype, dk, dv, C) combination that has no MFMA path
-// (the bf16 cases with dk = dv = 64 and C = 64 have their own kernels).
-// All arithmetic is float32 on the vector ALUs; intermediates live in LDS.
+// Serves every (variant, dtype, dk, dv, C) combination that has no dedicated
+// kernel (the bf16 cases with dk = dv = 64 and C = 64 have their own).  All
+// arithmetic is float32: the chunk's four contractions on the fp32 matrix
+// cores (16- and 32-column value tiles) or on the vector ALUs (64-column
+// tiles), everything else on the vector ALUs; intermediates live in LDS.
 // The kernel template is instantiated once per chunk size, each in a source
 // file of its own (falcon_chunked_generic_c16/c32/c64.hip) so the three
 // compile in parallel; falcon_chunked_generic.hip picks the value tile and
@@ -28,12 +30,14 @@
 // ragged last chunk needs no special case.
 //
 // Mapping.  One workgroup of 256 threads owns one sequence and one tile of
-// nv = 16 NB value columns and walks its chunks in order.  The threads form a
-// 16 x 16 grid (ty, tx); every contraction gives a thread the rows ty + 16 a
-// and the columns tx + 16 b of its output, so a wave reads four operand rows
-// that sit in distinct LDS banks (row pitches are a multiple of 4 words plus
-// 4) and sixteen consecutive words of the other operand.  Operands that run
-// along the contraction index are read as float4.  Per-thread tiles have
+// nv = 16 NB value columns and walks its chunks in order.  On the matrix
+// cores the chunk's products are 16 x 16 tiles dealt round-robin to the four
+// waves.  Elsewhere the threads form a 16 x 16 grid (ty, tx); a contraction
+// gives a thread the rows ty + 16 a and the columns tx + 16 b of its output,
+// so a wave reads four operand rows that sit in distinct LDS banks (row
+// pitches are a multiple of 4 words plus 4) and sixteen consecutive words of
+// the other operand.  Operands that run along the contraction index are read
+// as float4.  Per-thread tiles have
 // compile-time shapes (C / 16 chunk rows, NB value columns; key rows in
 // groups of four), so no multiply-add sits behind a run-time guard.  Each
 // chunk's inputs are loaded into registers in one batch at the top of the
