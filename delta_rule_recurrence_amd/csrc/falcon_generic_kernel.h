@@ -662,7 +662,7 @@ chunked_generic_kernel(const IO* __restrict__ phi_k, const IO* __restrict__ phi_
           for (int a = 0; a < MC; ++a)
 #pragma unroll
             for (int b = 0; b < NB; ++b) part[a][b] = 0.f;
-#pragma unroll 1
+#pragma unroll 2
           for (int s4 = 0; s4 < 16; s4 += 4) {
             const int s = 16 * sb + s4;
             float yv[4][NB], rv[4][NB], gs[4][NB];
