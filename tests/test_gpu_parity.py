@@ -340,6 +340,7 @@ GENERAL_TILES = [
     ("falcon2a", "f32", 16, 16, 50, 32, 64, 16),           # 64, dk = 32
     ("falcon1", "bf16", 4, 40, 90, 128, 64, 32),           # 64, dk = 128 (two key-row groups)
     ("falcon2", "bf16", 2, 64, 40, 128, 128, 64),          # 32 (LDS), two tiles per sequence
+    ("falcon1", "f32", 4, 40, 70, 128, 64, 64),            # 64: the largest LDS footprint (150 KB)
 ]
 
 
