@@ -609,7 +609,22 @@ chunked_generic_kernel(const IO* __restrict__ phi_k, const IO* __restrict__ phi_
       }
     }
 
-    // ---- a4: outputs ---------------------------------------------------------
+    // ---- a4: outputs, and for scalar gates the state update of key rows
+    // 4 ty + a (a < 4) in the same walk over the rows of rho (16- and 32-column
+    // tiles; with 64 columns the extra registers cost more than the shared
+    // loads save) ---------------------------------------------------------------
+    constexpr bool kFuse = !kPerCol && NB <= 2;
+    const int fb0 = (4 * ty) & (dk - 1);
+    float sacc0[4][NB];
+    if constexpr (kFuse) {
+      const float dl = exp2f(Lg[C - 1]);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const float4 s4v = ld4(St + (tx + 16 * b) * L.sp + fb0);
+#pragma unroll
+        for (int a = 0; a < 4; ++a) sacc0[a][b] = dl * comp(s4v, a);
+      }
+    }
     {
       float acc[MC][NB], gi[MC][NB];
 #pragma unroll
@@ -646,6 +661,17 @@ chunked_generic_kernel(const IO* __restrict__ phi_k, const IO* __restrict__ phi_
                   acc[a][b] = on ? nx : acc[a][b];
                 }
               }
+            }
+            // state rows 4 ty + a: S += 2^{g_{C-1}-g_s} x_s rho_s^T for these four s
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const float4 xv = ld4(Xs + (s + k) * L.xp + fb0);
+              const float w = En[s + k];
+#pragma unroll
+              for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+                  sacc0[a][b] = fmaf(comp(xv, a) * w, rv[k][b], sacc0[a][b]);
             }
           }
         }
@@ -729,7 +755,15 @@ chunked_generic_kernel(const IO* __restrict__ phi_k, const IO* __restrict__ phi_
         glast[b] = Lg[(C - 1) * ng + (kPerCol ? tx + 16 * b : 0)];
         dlast[b] = exp2f(glast[b]);
       }
-      for (int f0 = 0; f0 < dk; f0 += 64) {
+      if constexpr (kFuse) {
+        if (4 * ty < dk) {
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+            st4(St + (tx + 16 * b) * L.sp + fb0,
+                make_float4(sacc0[0][b], sacc0[1][b], sacc0[2][b], sacc0[3][b]));
+        }
+      }
+      for (int f0 = kFuse ? 64 : 0; f0 < dk; f0 += 64) {
         const bool own = f0 + 4 * ty < dk;
         const int fb = (f0 + 4 * ty) & (dk - 1);
         float sacc[4][NB];
