@@ -3,10 +3,15 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "falcon.h"
 #include "falcon_launch.h"
 
 namespace {
+
+// Polls a bounded wait makes before giving up (falcon_set_wait_limit).
+std::atomic<int32_t> g_wait_limit{falcon::kDefaultSpinLimit};
 
 using falcon::DecodeArgs;
 using falcon::ProblemArgs;
@@ -42,9 +47,12 @@ bool per_column(int variant) { return variant == FALCON_2 || variant == FALCON_2
 
 // Validates the arguments shared by the two forward entry points and fills
 // the launch arguments.
+// `ws` is the part of a workspace the call will use (none for the recurrent
+// form); it may overlap no input and no output.
 falcon_status check_forward(const falcon_problem* p, const void* phi_k, const void* phi_q,
                             const void* v, const float* beta, const float* lam, const float* S0,
-                            const void* k_prev, void* o, float* S_T, ProblemArgs* out) {
+                            const void* k_prev, void* o, float* S_T, ProblemArgs* out,
+                            Range ws = Range{nullptr, 0}) {
   falcon_status s = check_problem(p);
   if (s != FALCON_OK) return s;
   const int64_t bh = int64_t(p->B) * p->H;
@@ -73,6 +81,9 @@ falcon_status check_forward(const falcon_problem* p, const void* phi_k, const vo
   for (int i = 0; i < 5; ++i)
     if (overlap(rs, inputs[i])) return FALCON_ERR_ALIAS;
   if (overlap(rs, inputs[6])) return FALCON_ERR_ALIAS;
+  if (overlap(ws, ro) || overlap(ws, Range{S0, rs.bytes})) return FALCON_ERR_ALIAS;
+  for (const Range& r : inputs)
+    if (overlap(ws, r)) return FALCON_ERR_ALIAS;
 
   *out = ProblemArgs{};
   out->B = p->B; out->H = p->H; out->T = p->T; out->dk = p->dk; out->dv = p->dv;
@@ -81,6 +92,7 @@ falcon_status check_forward(const falcon_problem* p, const void* phi_k, const vo
   out->eps = p->eps; out->eps_gamma = p->eps_gamma;
   out->phi_k = phi_k; out->phi_q = phi_q; out->v = v; out->beta = beta; out->lam = lam;
   out->S0 = S0; out->k_prev = k_prev; out->o = o; out->S_T = S_T;
+  out->spin_limit = g_wait_limit.load(std::memory_order_relaxed);
   return FALCON_OK;
 }
 
@@ -140,11 +152,32 @@ falcon_status check_backward(const falcon_problem* p, const void* phi_k, const v
   return FALCON_OK;
 }
 
+// True when the backward's workspace range overlaps any input or output.
+bool bwd_workspace_overlaps(const ProblemArgs& a, const falcon::BwdBuffers& b, Range ws) {
+  const int64_t bh = int64_t(a.B) * a.H;
+  const int64_t es = a.bf16 ? 2 : 4;
+  const int64_t nt = bh * a.T * 64, ns = bh * 64 * 64;
+  const Range all[] = {{a.phi_k, nt * es}, {a.phi_q, nt * es}, {a.v, nt * es},
+                       {a.beta, bh * a.T * 4}, {a.lam, bh * a.T * 4}, {a.S0, ns * 4},
+                       {a.k_prev, bh * 64 * es}, {b.dO, nt * es}, {b.dS_T, ns * 4},
+                       {b.dphi_k, nt * 4}, {b.dphi_q, nt * 4}, {b.dv, nt * 4},
+                       {b.dbeta, bh * a.T * 4}, {b.dlam, bh * a.T * 4}, {b.dS0, ns * 4},
+                       {b.dk_prev, bh * 64 * 4}};
+  for (const Range& r : all)
+    if (overlap(ws, r)) return true;
+  return false;
+}
+
 }  // namespace
 
 extern "C" {
 
 int32_t falcon_abi_version(void) { return FALCON_ABI_VERSION; }
+
+int32_t falcon_set_wait_limit(int32_t polls) {
+  if (polls < 0) return -1;
+  return g_wait_limit.exchange(polls, std::memory_order_relaxed);
+}
 
 const char* falcon_status_string(int32_t s) {
   switch (s) {
@@ -158,7 +191,7 @@ const char* falcon_status_string(int32_t s) {
     case FALCON_ERR_VARIANT: return "FALCON_ERR_VARIANT: unknown variant";
     case FALCON_ERR_HIP: return "FALCON_ERR_HIP: the HIP runtime reported a launch error";
     case FALCON_ERR_VALUE: return "FALCON_ERR_VALUE: eps must be finite and >= 0, eps_gamma in (0,1)";
-    case FALCON_ERR_ALIAS: return "FALCON_ERR_ALIAS: an output overlaps an input";
+    case FALCON_ERR_ALIAS: return "FALCON_ERR_ALIAS: an output or the workspace overlaps another argument";
     default: return "unknown falcon_status";
   }
 }
@@ -197,6 +230,12 @@ falcon_status falcon_fwd_chunked(const falcon_problem* p, const void* phi_k, con
   const size_t need = falcon::chunked_workspace_bytes(a);
   if (need > 0 && (!workspace || workspace_bytes < need)) return FALCON_ERR_WORKSPACE;
   if (workspace && !aligned16(workspace)) return FALCON_ERR_ALIGN;
+  if (need > 0) {
+    s = check_forward(p, phi_k, phi_q, v, beta, lam, S0, k_prev, o, S_T, &a,
+                      Range{workspace, static_cast<int64_t>(need)});
+    if (s != FALCON_OK) return s;
+    a.C = C;
+  }
   a.workspace = workspace;
   a.workspace_bytes = workspace_bytes;
   if (int64_t(a.B) * a.H == 0 || a.T == 0) return empty_forward(a, stream);
@@ -226,6 +265,8 @@ falcon_status falcon_bwd_chunked(const falcon_problem* p, const void* phi_k, con
   const size_t need = falcon::bwd_workspace_bytes(a);
   if (need > 0 && (!workspace || workspace_bytes < need)) return FALCON_ERR_WORKSPACE;
   if (workspace && !aligned16(workspace)) return FALCON_ERR_ALIGN;
+  if (need > 0 && bwd_workspace_overlaps(a, b, Range{workspace, static_cast<int64_t>(need)}))
+    return FALCON_ERR_ALIAS;
   a.workspace = workspace;
   a.workspace_bytes = workspace_bytes;
   const int64_t bh = int64_t(a.B) * a.H;

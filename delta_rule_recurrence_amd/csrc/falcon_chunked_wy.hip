@@ -39,7 +39,6 @@ constexpr int kOutQt = 4096;            // Qt as B fragments [ib][m][lane][8]
 constexpr int kOutH = 8192;             // H as result tiles [cb][fb][lane][4]
 constexpr int kOutOt = 12288;           // Ot^T as result tiles [cb][ib][lane][4]
 // followed, after all blocks, by e^{g_63} of every chunk (float).
-constexpr int kSpinLimit = 1 << 22;
 
 struct Seq {
   const bf16_t* K;
@@ -451,8 +450,11 @@ struct ChainSmem {
   int abort_flag;
 };
 
-__device__ __forceinline__ bool wait_at_least(int* flag, int target, int* abort_flag) {
-  for (int it = 0; it < kSpinLimit; ++it) {
+// Polls `flag` until it reaches `target`, at most `limit` times.  A wait
+// that runs out sets the workgroup's abort flag and returns false; once the
+// flag is set every later wait returns false at once.
+__device__ __forceinline__ bool wait_at_least(int* flag, int target, int* abort_flag, int limit) {
+  for (int it = 0; it < limit; ++it) {
     const int val = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     if (__builtin_amdgcn_readfirstlane(val) >= target) {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
@@ -477,52 +479,18 @@ __device__ __forceinline__ int entry_src(int j, int part) {
   return kOutOt + part * kParts * 512 + (j - 16 - kParts) * 512;
 }
 
-__global__ void __launch_bounds__(kChainThreads)
-falcon1_chain_kernel(const float* S0, const uint16_t* __restrict__ blocks, const float* __restrict__ decay63,
-                     bf16_t* __restrict__ o, float* S_T, int T, int nchunks, int64_t BH) {
-  __shared__ ChainSmem sm;
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
-  const int g = l >> 4, c16 = l & 15;
-  // workgroups b and b + 8 (and so on) take the parts of one sequence, so they
-  // share an XCD and its L2
-  const int64_t bh = (int64_t(blockIdx.x) / (8 * kSplit)) * 8 + blockIdx.x % 8;
-  const int part = (blockIdx.x / 8) % kSplit;
-  if (bh >= BH) return;
-  const uint16_t* blk_bh = blocks + bh * nchunks * kBlockElems;
-  const float* e63_bh = decay63 + bh * nchunks;
-
-  if (tid < kRing) { sm.in_ready[tid] = 0; sm.in_free[tid] = 0; }
-  if (tid == 0) sm.abort_flag = 0;
-  __syncthreads();
-
-  if (wave >= kColWaves) {
-    // ---- staging: chunks c = s, s + kStagers, ... -----------------------------
-    const int s = wave - kColWaves;
-    int src[kEntryFrags];
-#pragma unroll
-    for (int j = 0; j < kEntryFrags; ++j) src[j] = entry_src(j, part) + l * 8;
-    for (int c = s; c < nchunks; c += kStagers) {
-      bf16x8 R[kEntryFrags];
-      const uint16_t* blk = blk_bh + int64_t(c) * kBlockElems;
-#pragma unroll
-      for (int j = 0; j < kEntryFrags; ++j) R[j] = load_frag(blk + src[j]);
-      const float e63 = e63_bh[c];
-      const int e = c % kRing;
-      if (!wait_at_least(&sm.in_free[e], kColWaves * (c / kRing), &sm.abort_flag)) break;
-#pragma unroll
-      for (int j = 0; j < kEntryFrags; ++j) store_frag(&sm.d[e][j * 512 + l * 8], R[j]);
-      if (l == 0) sm.e63[e] = e63;
-      signal_add(&sm.in_ready[e], l);
-    }
-    return;
-  }
+// The two chain waves of a workgroup: the state of value columns
+// 16 cb .. 16 cb + 15 in MFMA result registers, one step per chunk.
+__device__ __forceinline__ void chain_waves(ChainSmem& sm, const float* S0, bf16_t* __restrict__ o, float* S_T,
+                                            int64_t bh, int part, int wave, int l, int T, int nchunks,
+                                            int spin_limit) {
   // ---- chain waves ------------------------------------------------------------
   // Per chunk c: the reads of Qt and Ot are issued before the state update and
   // the reads of chunk c + 1's K and H before the outputs, so LDS latency hides
   // behind the matrix products.  A wait that runs out sets the abort flag; the
   // loop still runs to its end (every later wait returns at once).
   const int cw = wave;
+  const int g = l >> 4, c16 = l & 15;
   const int cb = part * kColWaves + cw;                      // value columns 16 cb .. 16 cb + 15
   const int hoff = 8192 + cw * 1024 + l * 4;                 // this wave's H tiles in an entry
   const int ooff = 8192 + kColWaves * 1024 + cw * 1024 + l * 4;
@@ -536,7 +504,7 @@ falcon1_chain_kernel(const float* S0, const uint16_t* __restrict__ blocks, const
   bf16x8 kf[4][2];                                           // frag(K)[fb][m] of the current chunk
   uint2 hf[4];                                               // its H tiles
   float e63;
-  wait_at_least(&sm.in_ready[0], 1, &sm.abort_flag);
+  wait_at_least(&sm.in_ready[0], 1, &sm.abort_flag, spin_limit);
 #pragma unroll
   for (int fb = 0; fb < 4; ++fb) {
     kf[fb][0] = load_frag(&sm.d[0][kOutK + fslot(fb, 0, l)]);
@@ -554,7 +522,7 @@ falcon1_chain_kernel(const float* S0, const uint16_t* __restrict__ blocks, const
     const int e1 = (c + 1) % kRing;
     // chunk c + 1 must be in its entry before its reads below; after the last
     // chunk those reads only see a stale entry and are not used
-    if (c + 1 < nchunks) wait_at_least(&sm.in_ready[e1], (c + 1) / kRing + 1, &sm.abort_flag);
+    if (c + 1 < nchunks) wait_at_least(&sm.in_ready[e1], (c + 1) / kRing + 1, &sm.abort_flag, spin_limit);
     bf16x8 qf[4][2];
     uint2 of[4];
 #pragma unroll
@@ -595,14 +563,78 @@ falcon1_chain_kernel(const float* S0, const uint16_t* __restrict__ blocks, const
     sb1 = frag_acc(S[2], S[3]);
     signal_add(&sm.in_free[c % kRing], l);
   }
-  // a wait that ran out (a hand-over that never came) leaves NaN in S_T
-  const bool aborted = __hip_atomic_load(&sm.abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0;
+  // the final state (overwritten with NaN after the loop if any wait ran out)
   if (S_T) {
 #pragma unroll
     for (int fb = 0; fb < 4; ++fb)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        S_T[(bh * kD + 16 * fb + 4 * g + r) * kD + 16 * cb + c16] = aborted ? __builtin_nanf("") : S[fb][r];
+        S_T[(bh * kD + 16 * fb + 4 * g + r) * kD + 16 * cb + c16] = S[fb][r];
+  }
+}
+
+__global__ void __launch_bounds__(kChainThreads)
+falcon1_chain_kernel(const float* S0, const uint16_t* __restrict__ blocks, const float* __restrict__ decay63,
+                     bf16_t* __restrict__ o, float* S_T, int T, int nchunks, int64_t BH, int spin_limit) {
+  __shared__ ChainSmem sm;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
+  const int g = l >> 4, c16 = l & 15;
+  // workgroups b and b + 8 (and so on) take the parts of one sequence, so they
+  // share an XCD and its L2
+  const int64_t bh = (int64_t(blockIdx.x) / (8 * kSplit)) * 8 + blockIdx.x % 8;
+  const int part = (blockIdx.x / 8) % kSplit;
+  if (bh >= BH) return;
+  const uint16_t* blk_bh = blocks + bh * nchunks * kBlockElems;
+  const float* e63_bh = decay63 + bh * nchunks;
+
+  if (tid < kRing) { sm.in_ready[tid] = 0; sm.in_free[tid] = 0; }
+  if (tid == 0) sm.abort_flag = 0;
+  __syncthreads();
+
+  if (wave >= kColWaves) {
+    // ---- staging: chunks c = s, s + kStagers, ... -----------------------------
+    const int s = wave - kColWaves;
+    int src[kEntryFrags];
+#pragma unroll
+    for (int j = 0; j < kEntryFrags; ++j) src[j] = entry_src(j, part) + l * 8;
+    for (int c = s; c < nchunks; c += kStagers) {
+      bf16x8 R[kEntryFrags];
+      const uint16_t* blk = blk_bh + int64_t(c) * kBlockElems;
+#pragma unroll
+      for (int j = 0; j < kEntryFrags; ++j) R[j] = load_frag(blk + src[j]);
+      const float e63 = e63_bh[c];
+      const int e = c % kRing;
+      if (!wait_at_least(&sm.in_free[e], kColWaves * (c / kRing), &sm.abort_flag, spin_limit)) break;
+#pragma unroll
+      for (int j = 0; j < kEntryFrags; ++j) store_frag(&sm.d[e][j * 512 + l * 8], R[j]);
+      if (l == 0) sm.e63[e] = e63;
+      signal_add(&sm.in_ready[e], l);
+    }
+  } else {
+    chain_waves(sm, S0, o, S_T, bh, part, wave, l, T, nchunks, spin_limit);
+  }
+  // Every wave gets here.  A wait that ran out anywhere in the workgroup (a
+  // hand-over that never came) poisons this part of the sequence: its outputs
+  // and its final state become NaN, so an abort can never pass for a result.
+  __syncthreads();
+  if (wave < kColWaves &&
+      __hip_atomic_load(&sm.abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0) {
+    const int cb = part * kColWaves + wave;
+    const uint16_t nan_bits = 0x7fc0;
+    const uint32_t nan2 = uint32_t(nan_bits) | (uint32_t(nan_bits) << 16);
+    bf16_t* o_bh = o + bh * T * kD;
+    // the wave's own columns, after its own stores to them (program order)
+    for (int tok = l >> 1; tok < T; tok += 32)
+      *reinterpret_cast<uint4*>(o_bh + int64_t(tok) * kD + 16 * cb + 8 * (l & 1)) = make_uint4(nan2, nan2, nan2, nan2);
+    if (S_T) {
+      const int g = l >> 4, c16 = l & 15;
+#pragma unroll
+      for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          S_T[(bh * kD + 16 * fb + 4 * g + r) * kD + 16 * cb + c16] = __builtin_nanf("");
+    }
   }
 }
 
@@ -629,7 +661,7 @@ hipError_t launch_chunked_wy(const ProblemArgs& a, hipStream_t st) {
                      blocks, decay63, a.T, nchunks, a.eps, a.eps_gamma);
   const int64_t groups = (BH + 7) / 8;
   hipLaunchKernelGGL(falcon1_chain_kernel, dim3(unsigned(groups * 8 * kSplit)), dim3(kChainThreads), 0, st,
-                     a.S0, blocks, decay63, static_cast<bf16_t*>(a.o), a.S_T, a.T, nchunks, BH);
+                     a.S0, blocks, decay63, static_cast<bf16_t*>(a.o), a.S_T, a.T, nchunks, BH, a.spin_limit);
   return hipGetLastError();
 }
 

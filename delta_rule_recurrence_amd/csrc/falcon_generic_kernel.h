@@ -10,9 +10,9 @@
 // compile in parallel; falcon_chunked_generic.hip picks the value tile and
 // dispatches.
 //
-// Chunk algebra (derived from the Section 4 summary rules with the chunk-
-// local log-space renormalisation of Section 4.4, "Algorithm 3 realizes
-// Eq. (4.16) chunk-locally via log-prefix decays", taken with window B = 1).
+// Chunk algebra (derived from the Section 4 summary rules with the log-space
+// renormalisation of Section 4.4, Eq. (4.16), applied per chunk with decays
+// taken from chunk-local log prefixes, at window B = 1).
 // For a chunk with local rows i = 0..C-1, incoming state S and per value
 // column j (scalar rules use one gate column for all j):
 //   g_i      = sum_{r<=i} log gamma_r             (float32, all exponents <= 0;
@@ -21,8 +21,9 @@
 //              merged residual system
 //              rho_i + sum_{s<i} eta_i e^{g_{i-1}-g_s} (x_i.x_s) rho_s
 //                    = eta_i (v_i - e^{g_{i-1}} (X S)_i)
-//              ("injected-value and projected-history paths share this
-//              triangular factor ... one merged residual system", §4.2);
+//              (Section 4.2: the new values and the carried state's
+//              prediction enter through the same unit-lower triangular
+//              operator, so one solve per chunk covers both);
 //   rho_i    = eta_i v_i                            (inner-product rules)
 //   o_i      = e^{g_i} (Q S)_i + sum_{s<=i} e^{g_i-g_s} (q_i.x_s) rho_s
 //   S_next   = e^{g_{C-1}} S + sum_s e^{g_{C-1}-g_s} x_s rho_s^T

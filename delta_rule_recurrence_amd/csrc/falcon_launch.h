@@ -25,7 +25,12 @@ struct ProblemArgs {
   int C;                 // chunk size (chunked path only)
   void* workspace;
   size_t workspace_bytes;
+  int spin_limit;        // polls before a bounded wait between waves gives up
 };
+
+// Default number of polls of a bounded wait (each poll sleeps ~64 cycles):
+// about 0.1-0.2 s, far beyond any legitimate hand-over.
+constexpr int kDefaultSpinLimit = 1 << 22;
 
 struct DecodeArgs {
   int B, H, dk, dv;

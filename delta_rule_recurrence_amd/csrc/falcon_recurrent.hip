@@ -7,9 +7,9 @@
 // products with DPP lane moves (recurrent) or through LDS (decode).
 //
 // Paper: "Fast Weight Attention for Continual Learning", Section 4 naming and
-// formula summary (the rules), Eq. (3.4) (step size), Section 4.3 "Decay
-// positivity" (clamp); the per-token order follows the Falcon-1 step listing
-// of the rcap.io post (residual from the pre-update state, read after write).
+// formula summary (the rules: the residual is taken against the state before
+// the write, Eq. 3.3, and the read comes after the write), Eq. (3.4) (step
+// size), Section 4.3 "Decay positivity" (clamp).
 
 #include "falcon_device.h"
 #include "falcon_launch.h"

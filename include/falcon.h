@@ -33,8 +33,9 @@
  *  - Calls are asynchronous and stream-ordered on `stream` (a hipStream_t;
  *    NULL means the legacy default stream).  The library never synchronises
  *    the device, allocates no device memory in these entry points, and keeps
- *    no global mutable state, so concurrent calls on different streams are
- *    safe as long as their output buffers do not overlap.
+ *    no global mutable state besides the wait limit of falcon_set_wait_limit,
+ *    so concurrent calls on different streams are safe as long as their
+ *    output buffers and workspaces do not overlap.
  *  - Every argument is validated before anything is launched; on error the
  *    call returns a negative falcon_status and touches no memory.
  *  - Launch failures reported by the HIP runtime return FALCON_ERR_HIP.
@@ -72,7 +73,8 @@ typedef enum {
   FALCON_ERR_VARIANT = -7,   /* variant not a falcon_variant                  */
   FALCON_ERR_HIP = -8,       /* the HIP runtime reported an error at launch  */
   FALCON_ERR_VALUE = -9,     /* eps < 0 / not finite, eps_gamma not in (0,1) */
-  FALCON_ERR_ALIAS = -10     /* o overlaps an input                           */
+  FALCON_ERR_ALIAS = -10     /* an output or the workspace overlaps another
+                                argument                                     */
 } falcon_status;
 
 typedef enum {
@@ -106,6 +108,19 @@ int32_t falcon_abi_version(void);
 const char* falcon_status_string(int32_t status);
 
 /*
+ * falcon_set_wait_limit -- the one process-wide setting of the library.  Some
+ * kernels hand data between waves or workgroups through flags in memory;
+ * every such wait is bounded and gives up after `polls` polls (default
+ * 4194304, about 0.1-0.2 s).  A call in which a wait gave up does not hang:
+ * it finishes and reports the failure in its results, every output element
+ * and every final-state element of the affected sequences being NaN.
+ * Meant for tests of that path and for debugging; calls made while it
+ * changes read either value.  polls = 0 makes every such wait give up at
+ * once.  Returns the previous limit, or -1 (nothing changed) for polls < 0.
+ */
+int32_t falcon_set_wait_limit(int32_t polls);
+
+/*
  * falcon_fwd_recurrent -- the recurrent form (paper, Section 4.6 and the
  * complexity table of the juhoplayground post: O(N) sequential scan, O(1)
  * state).  One pass over T per (b, h) with the state held on-chip.
@@ -132,7 +147,8 @@ falcon_status falcon_fwd_recurrent(const falcon_problem* p,
  *
  *  C         : chunk length, 16, 32 or 64.
  *  workspace : device scratch of at least falcon_workspace_bytes(p, C)
- *              bytes (may be NULL when that is 0).
+ *              bytes (may be NULL when that is 0); the bytes the call uses
+ *              may overlap no input and no output (FALCON_ERR_ALIAS).
  */
 falcon_status falcon_fwd_chunked(const falcon_problem* p,
                                  const void* phi_k, const void* phi_q, const void* v,
@@ -148,7 +164,14 @@ size_t falcon_workspace_bytes(const falcon_problem* p, int32_t C);
 
 /*
  * falcon_decode_step -- one read-after-write token for every (b, h) from a
- * carried state (the recurrent form at inference).  p->T is ignored.
+ * carried state: the rule of the paper's Section 4 naming summary (Falcon-1:
+ * residual against the state before the write, Eq. 3.3; step size Eq. 3.4;
+ * decay clamp of Section 4.3) applied to a single token, which is the
+ * recurrent form run at inference with O(1) state per head (complexity table
+ * of the juhoplayground post).  The read o = S_t^T phi(q_t) comes after the
+ * write.  p->T is ignored.  Validation, status codes and stream semantics are
+ * those of the forward entry points; S is both read and written, so it may
+ * overlap no other argument.
  *
  *  phi_k_prev : [B, H, dk] io dtype, the PREVIOUS token's key feature x_t.
  *  phi_q, v   : [B, H, dk] / [B, H, dv] io dtype, this token's query, value.

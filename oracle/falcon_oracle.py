@@ -9,9 +9,8 @@ What it computes is the sequential recurrence exactly as the paper states it,
 one token at a time, in float64, vectorised only over the independent
 (batch, head) axes.  Citations refer to *Fast Weight Attention for Continual
 Learning* (arXiv 2608.27763) as rendered on the hyper.ai page (English body):
-section / equation numbers are the paper's.  "[rcap]" is the rcap.io post on
-the same paper (its Falcon-1 step listing), "[juho]" the juhoplayground
-post (its complexity table and Falcon-3A mask), "[rainbus]" the
+section / equation numbers are the paper's.  "[juho]" is the juhoplayground
+post on the same paper (its complexity table), "[rainbus]" the
 paper.rainbus.top review.
 
 Readings taken where the pages leave a step open (each also listed in the
@@ -91,8 +90,8 @@ def falcon_forward(variant, phi_k, phi_q, v, beta, lam, *, eps, eps_gamma=1e-6,
       Falcon-2  (§4 summary; §4.2):     S = S Diag(gamma) + x (eta ⊙ r)^T
       Falcon-2A (§4 summary; Eq. 4.7):   S = S Diag(gamma) + x (eta ⊙ v_t)^T
       o_t = S_t^T phi(q_t)                (read after write, §4 summary)
-    This is also the Falcon-1 step of [rcap]'s listing, with the paper's t = 1
-    sentinel added (the listing has no special case for t = 1).
+    The residual r uses the state before the write (Eq. 3.3), and the first
+    step follows the t = 1 sentinel of §3.
 
     Returns ``(O, S_T)`` (and the list of states S_1..S_T when
     ``return_states``), all float64.

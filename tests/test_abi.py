@@ -200,3 +200,122 @@ def test_backward_validation(lib):
     # nothing to do
     assert call_bwd(lib, prob(B=0)) == OK
     assert call_bwd(lib, prob(H=0), k=None, dk=None) == OK
+
+
+def test_workspace_overlap_is_rejected(lib):
+    p = prob(T=200)
+    need = fb.falcon_workspace_bytes(p, 64)
+    assert need > 0
+    # the workspace may overlap no input and no output
+    for name, i in (("k", 0), ("v", 2), ("beta", 3), ("o", 5), ("ST", 6)):
+        assert call_chunked(lib, p, ws=fake(i), wsb=need) == ALIAS, name
+    assert call_chunked(lib, p, ws=fake(20), wsb=need, S0=ctypes.c_void_p(BASE + 20 * STRIDE + 4096)) == ALIAS
+    # backward: the workspace against an output
+    bneed = fb.falcon_bwd_workspace_bytes(prob())
+    assert call_bwd(lib, prob(), fake(6), bneed) == ALIAS
+    assert call_bwd(lib, prob(), fake(2), bneed) == ALIAS
+
+
+# ---- the Python binding checks shapes, dtypes and devices before any pointer
+# crosses the C ABI (CPU tensors: the checks run before the device check) ----
+
+def _fwd_tensors(B=2, H=3, T=40, dk=64, dv=64, io=None, per_col=False):
+    import torch
+    io = torch.bfloat16 if io is None else io
+    return dict(phi_k=torch.zeros(B, H, T, dk, dtype=io), phi_q=torch.zeros(B, H, T, dk, dtype=io),
+                v=torch.zeros(B, H, T, dv, dtype=io),
+                beta=torch.zeros((B, H, T, dv) if per_col else (B, H, T)),
+                lam=torch.zeros(B, H, T))
+
+
+@pytest.mark.parametrize("fn", ["chunked", "recurrent"])
+def test_binding_rejects_mismatched_forward_arguments(fn):
+    import torch
+    call = fb.falcon_fwd_chunked if fn == "chunked" else fb.falcon_fwd_recurrent
+
+    def run(variant="falcon1", **over):
+        d = _fwd_tensors(per_col=variant in ("falcon2", "falcon2a"))
+        extra = {k: over.pop(k) for k in list(over) if k in ("S0", "k_prev", "o", "S_T", "workspace")}
+        d.update(over)
+        if fn == "recurrent":
+            extra.pop("workspace", None)
+        return call(d["phi_k"], d["phi_q"], d["v"], d["beta"], d["lam"], variant=variant, **extra)
+
+    bad = [
+        (dict(phi_q=torch.zeros(2, 3, 41, 64, dtype=torch.bfloat16)), "phi_q"),
+        (dict(phi_q=torch.zeros(2, 3, 40, 64)), "phi_q"),                 # f32 query, bf16 values
+        (dict(v=torch.zeros(2, 3, 40, 64, dtype=torch.float16)), "io dtype"),
+        (dict(beta=torch.zeros(2, 3, 40, dtype=torch.float64)), "beta"),
+        (dict(lam=torch.zeros(2, 3)), "lam"),
+        (dict(S0=torch.zeros(2, 3, 64, 64, dtype=torch.bfloat16)), "S0"),
+        (dict(S0=torch.zeros(2, 3, 64, 32)), "S0"),
+        (dict(k_prev=torch.zeros(2, 3, 64)), "k_prev"),
+        (dict(o=torch.zeros(2, 3, 39, 64, dtype=torch.bfloat16)), "^o:"),
+        (dict(S_T=torch.zeros(2, 3, 64, 64, dtype=torch.float64)), "S_T"),
+        (dict(phi_k=torch.zeros(2, 3, 40)), "phi_k"),
+    ]
+    for over, what in bad:
+        with pytest.raises(ValueError, match=what):
+            run(**over)
+    # a Falcon-2 call needs per-column gains
+    with pytest.raises(ValueError, match="beta"):
+        d = _fwd_tensors()
+        call(d["phi_k"], d["phi_q"], d["v"], d["beta"], d["lam"], variant="falcon2")
+    with pytest.raises(ValueError, match="variant"):
+        run(variant="falcon3")
+    if fn == "chunked":
+        with pytest.raises(ValueError, match="workspace"):
+            run(workspace=torch.zeros(16, dtype=torch.uint8))
+    # well-formed CPU tensors get as far as the device check
+    with pytest.raises(ValueError, match="device"):
+        run()
+
+
+def test_binding_rejects_mismatched_decode_and_backward_arguments():
+    import torch
+    B, H, dk, dv = 2, 3, 64, 64
+    bf = torch.bfloat16
+    x, q, v = torch.zeros(B, H, dk, dtype=bf), torch.zeros(B, H, dk, dtype=bf), torch.zeros(B, H, dv, dtype=bf)
+    beta, lam, S = torch.zeros(B, H), torch.zeros(B, H), torch.zeros(B, H, dk, dv)
+    with pytest.raises(ValueError, match="lam"):
+        fb.falcon_decode_step(x, q, v, beta, torch.zeros(B, H, 1), S)
+    with pytest.raises(ValueError, match="beta"):
+        fb.falcon_decode_step(x, q, v, beta, lam, S, variant="falcon2")
+    with pytest.raises(ValueError, match="^S:"):
+        fb.falcon_decode_step(x, q, v, beta, lam, torch.zeros(B, H, dk, dv, dtype=bf))
+    with pytest.raises(ValueError, match="is_first"):
+        fb.falcon_decode_step(x, q, v, beta, lam, S, is_first=torch.zeros(B, dtype=torch.int32))
+    with pytest.raises(ValueError, match="^o:"):
+        fb.falcon_decode_step(x, q, v, beta, lam, S, o=torch.zeros(B, H, dv))
+    with pytest.raises(ValueError, match="device"):
+        fb.falcon_decode_step(x, q, v, beta, lam, S)
+    d = _fwd_tensors()
+    dO = torch.zeros(2, 3, 40, 64, dtype=bf)
+    with pytest.raises(ValueError, match="dO"):
+        fb.falcon_bwd_chunked(d["phi_k"], d["phi_q"], d["v"], d["beta"], d["lam"], dO.float())
+    with pytest.raises(ValueError, match="dS_T"):
+        fb.falcon_bwd_chunked(d["phi_k"], d["phi_q"], d["v"], d["beta"], d["lam"], dO,
+                              dS_T=torch.zeros(2, 3, 64))
+    with pytest.raises(ValueError, match="dbeta"):
+        fb.falcon_bwd_chunked(d["phi_k"], d["phi_q"], d["v"], d["beta"], d["lam"], dO,
+                              grads={"dbeta": torch.zeros(2, 3, 41)})
+    with pytest.raises(ValueError, match="unknown"):
+        fb.falcon_bwd_chunked(d["phi_k"], d["phi_q"], d["v"], d["beta"], d["lam"], dO,
+                              grads={"dx": torch.zeros(1)})
+    with pytest.raises(ValueError, match="workspace"):
+        fb.falcon_bwd_chunked(d["phi_k"], d["phi_q"], d["v"], d["beta"], d["lam"], dO,
+                              workspace=torch.zeros(8, dtype=torch.uint8))
+
+
+def test_wait_limit_setting(lib):
+    prev = fb.falcon_set_wait_limit(1000)
+    try:
+        assert prev == 1 << 22
+        assert fb.falcon_set_wait_limit(0) == 1000
+        assert lib.falcon_set_wait_limit(-5) == -1          # rejected, unchanged
+        assert fb.falcon_set_wait_limit(7) == 0
+        with pytest.raises(ValueError):
+            fb.falcon_set_wait_limit(-1)
+    finally:
+        fb.falcon_set_wait_limit(prev)
+    assert fb.falcon_set_wait_limit(prev) == prev
