@@ -3,7 +3,10 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include <atomic>
+#include <mutex>
 
 #include "falcon.h"
 #include "falcon_launch.h"
@@ -44,6 +47,7 @@ falcon_status check_problem(const falcon_problem* p) {
 }
 
 bool per_column(int variant) { return variant == FALCON_2 || variant == FALCON_2A; }
+bool is_per_column_variant(int variant) { return per_column(variant); }
 
 // Validates the arguments shared by the two forward entry points and fills
 // the launch arguments.
@@ -168,6 +172,54 @@ bool bwd_workspace_overlaps(const ProblemArgs& a, const falcon::BwdBuffers& b, R
   return false;
 }
 
+// ---- scratch of the allocation-free chunked entry point ---------------------
+// One static device array per GPU the library runs on, held until the process
+// ends.  In host code `scratch` only names the symbol; its device address is
+// looked up once per device (hipGetSymbolAddress, with that device current)
+// and only that address is ever handed to a kernel.
+__device__ __align__(256) unsigned char scratch[FALCON_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch, or nullptr on failure.
+void* scratch_for_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+// The forward's arguments restricted to sequences [s0, s0 + n) (sequences are
+// the contiguous (b, h) slabs of every tensor), as a problem with B = 1, H = n.
+ProblemArgs sequence_slice(const ProblemArgs& a, int64_t s0, int n) {
+  ProblemArgs r = a;
+  const int64_t es = a.bf16 ? 2 : 4;
+  const int64_t tk = int64_t(a.T) * a.dk, tv = int64_t(a.T) * a.dv, st = int64_t(a.dk) * a.dv;
+  const int64_t bstride = is_per_column_variant(a.variant) ? tv : a.T;
+  auto off = [&](const void* p, int64_t elems, int64_t bytes) -> const void* {
+    return p ? static_cast<const char*>(p) + s0 * elems * bytes : nullptr;
+  };
+  r.B = 1;
+  r.H = n;
+  r.phi_k = off(a.phi_k, tk, es);
+  r.phi_q = off(a.phi_q, tk, es);
+  r.v = off(a.v, tv, es);
+  r.beta = static_cast<const float*>(off(a.beta, bstride, 4));
+  r.lam = static_cast<const float*>(off(a.lam, a.T, 4));
+  r.S0 = static_cast<const float*>(off(a.S0, st, 4));
+  r.k_prev = off(a.k_prev, a.dk, es);
+  r.o = const_cast<void*>(off(a.o, tv, es));
+  r.S_T = static_cast<float*>(const_cast<void*>(off(a.S_T, st, 4)));
+  return r;
+}
+
 }  // namespace
 
 extern "C" {
@@ -192,6 +244,8 @@ const char* falcon_status_string(int32_t s) {
     case FALCON_ERR_HIP: return "FALCON_ERR_HIP: the HIP runtime reported a launch error";
     case FALCON_ERR_VALUE: return "FALCON_ERR_VALUE: eps must be finite and >= 0, eps_gamma in (0,1)";
     case FALCON_ERR_ALIAS: return "FALCON_ERR_ALIAS: an output or the workspace overlaps another argument";
+    case FALCON_ERR_SCRATCH:
+      return "FALCON_ERR_SCRATCH: one sequence needs more scratch than the allocation-free entry point holds";
     default: return "unknown falcon_status";
   }
 }
@@ -241,6 +295,46 @@ falcon_status falcon_fwd_chunked(const falcon_problem* p, const void* phi_k, con
   if (int64_t(a.B) * a.H == 0 || a.T == 0) return empty_forward(a, stream);
   (void)hipGetLastError();
   return finish(falcon::launch_chunked(a, stream));
+}
+
+falcon_status falcon_fwd_chunked_noalloc(const falcon_problem* p, const void* phi_k,
+                                         const void* phi_q, const void* v, const float* beta,
+                                         const float* lam, const float* S0, const void* k_prev,
+                                         void* o, float* S_T, int32_t C, hipStream_t stream) {
+  ProblemArgs a;
+  falcon_status s = check_forward(p, phi_k, phi_q, v, beta, lam, S0, k_prev, o, S_T, &a);
+  if (s != FALCON_OK) return s;
+  if (C != 16 && C != 32 && C != 64) return FALCON_ERR_CHUNK;
+  a.C = C;
+  const int64_t BH = int64_t(a.B) * a.H;
+  if (BH == 0 || a.T == 0) return empty_forward(a, stream);
+  // sequences per launch group: as many as the scratch holds
+  ProblemArgs one = sequence_slice(a, 0, 1);
+  const size_t per_seq = falcon::chunked_workspace_bytes(one);
+  int64_t group = BH;
+  if (per_seq > 0) {
+    if (per_seq > size_t(FALCON_NOALLOC_SCRATCH_BYTES)) return FALCON_ERR_SCRATCH;
+    group = std::min<int64_t>(BH, int64_t(FALCON_NOALLOC_SCRATCH_BYTES / per_seq));
+    while (group > 1 &&
+           falcon::chunked_workspace_bytes(sequence_slice(a, 0, int(group))) > size_t(FALCON_NOALLOC_SCRATCH_BYTES))
+      --group;
+  }
+  void* ptr = nullptr;
+  if (per_seq > 0) {
+    ptr = scratch_for_current_device();
+    if (!ptr) return FALCON_ERR_HIP;
+  }
+  (void)hipGetLastError();
+  // Groups run one after another on the stream, so each reuses the scratch
+  // only after the previous group's kernels have finished with it.
+  for (int64_t s0 = 0; s0 < BH; s0 += group) {
+    ProblemArgs g = sequence_slice(a, s0, int(std::min<int64_t>(group, BH - s0)));
+    g.workspace = ptr;
+    g.workspace_bytes = per_seq > 0 ? size_t(FALCON_NOALLOC_SCRATCH_BYTES) : 0;
+    const hipError_t e = falcon::launch_chunked(g, stream);
+    if (e != hipSuccess) return FALCON_ERR_HIP;
+  }
+  return FALCON_OK;
 }
 
 size_t falcon_bwd_workspace_bytes(const falcon_problem* p) {

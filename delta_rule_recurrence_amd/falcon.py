@@ -40,6 +40,8 @@ _SIGNATURES = {
                                               _P, _P, _P, _P, _P]),
     "falcon_fwd_chunked": (ctypes.c_int32, [ctypes.POINTER(FalconProblem), _P, _P, _P, _P, _P, _P,
                                             _P, _P, _P, ctypes.c_int32, _P, ctypes.c_size_t, _P]),
+    "falcon_fwd_chunked_noalloc": (ctypes.c_int32, [ctypes.POINTER(FalconProblem), _P, _P, _P, _P, _P,
+                                                    _P, _P, _P, _P, ctypes.c_int32, _P]),
     "falcon_decode_step": (ctypes.c_int32, [ctypes.POINTER(FalconProblem), _P, _P, _P, _P, _P,
                                             _P, _P, _P, _P]),
     "falcon_bwd_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(FalconProblem)]),
@@ -219,6 +221,22 @@ def falcon_fwd_chunked(phi_k, phi_q, v, beta, lam, *, variant="falcon1", C=64, S
     _check(load_library().falcon_fwd_chunked(
         ctypes.byref(p), _ptr(phi_k), _ptr(phi_q), _ptr(v), _ptr(beta), _ptr(lam), _ptr(S0),
         _ptr(k_prev), _ptr(o), _ptr(S_T), int(C), _ptr(workspace), wbytes, _stream(stream)))
+    return o, S_T
+
+
+def falcon_fwd_chunked_noalloc(phi_k, phi_q, v, beta, lam, o, *, variant="falcon1", C=64, S0=None,
+                               k_prev=None, eps=1e-6, eps_gamma=1e-6, S_T=None, stream=None):
+    """Chunk-parallel form without any allocation: the caller passes ``o``
+    (and ``S_T``, or None to skip the final state); scratch comes from the
+    library's static device buffer.  Returns ``(o, S_T)``."""
+    if o is None:
+        raise ValueError("o is required: this entry point allocates nothing")
+    B, H, T, dk, dv, o, S_T = _forward_setup(phi_k, phi_q, v, beta, lam, variant, S0, k_prev, o,
+                                             S_T, False)
+    p = make_problem(B, H, T, dk, dv, variant=variant, io_dtype=v.dtype, eps=eps, eps_gamma=eps_gamma)
+    _check(load_library().falcon_fwd_chunked_noalloc(
+        ctypes.byref(p), _ptr(phi_k), _ptr(phi_q), _ptr(v), _ptr(beta), _ptr(lam), _ptr(S0),
+        _ptr(k_prev), _ptr(o), _ptr(S_T), int(C), _stream(stream)))
     return o, S_T
 
 

@@ -73,8 +73,10 @@ typedef enum {
   FALCON_ERR_VARIANT = -7,   /* variant not a falcon_variant                  */
   FALCON_ERR_HIP = -8,       /* the HIP runtime reported an error at launch  */
   FALCON_ERR_VALUE = -9,     /* eps < 0 / not finite, eps_gamma not in (0,1) */
-  FALCON_ERR_ALIAS = -10     /* an output or the workspace overlaps another
+  FALCON_ERR_ALIAS = -10,    /* an output or the workspace overlaps another
                                 argument                                     */
+  FALCON_ERR_SCRATCH = -11   /* falcon_fwd_chunked_noalloc: one sequence needs
+                                more than FALCON_NOALLOC_SCRATCH_BYTES        */
 } falcon_status;
 
 typedef enum {
@@ -161,6 +163,35 @@ falcon_status falcon_fwd_chunked(const falcon_problem* p,
 /* Device scratch needed by falcon_fwd_chunked for this problem and C;
  * returns (size_t)-1 for an invalid problem. */
 size_t falcon_workspace_bytes(const falcon_problem* p, int32_t C);
+
+/* Size of the static device buffer behind falcon_fwd_chunked_noalloc. */
+#define FALCON_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * falcon_fwd_chunked_noalloc -- falcon_fwd_chunked for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments and results as
+ * falcon_fwd_chunked, without the workspace: the kernels that need scratch
+ * use a static device buffer of FALCON_NOALLOC_SCRATCH_BYTES (64 MiB) that the
+ * library holds on every GPU it runs on until the process ends.  When the
+ * problem needs more scratch than that, the sequences are processed in
+ * groups that fit, one group after another on `stream`; a problem in which a
+ * single sequence needs more returns FALCON_ERR_SCRATCH (for Falcon-1 with
+ * bf16 I/O, dk = dv = 64 and C = 64 that is T > 131008 tokens).  The call
+ * allocates nothing.
+ *
+ * The buffer of a GPU is shared by every call on that GPU and keeps the last
+ * call's contents; no part of it needs to start at zero.  Calls that overlap
+ * in time on one GPU (different streams or threads without ordering) race on
+ * it and must not be made.  `stream` must belong to the current device, whose
+ * buffer is used.  The first call on a device looks the buffer up (the HIP
+ * runtime's symbol lookup, no allocation); FALCON_ERR_HIP if that fails.
+ */
+falcon_status falcon_fwd_chunked_noalloc(const falcon_problem* p,
+                                         const void* phi_k, const void* phi_q, const void* v,
+                                         const float* beta, const float* lam,
+                                         const float* S0, const void* k_prev,
+                                         void* o, float* S_T, int32_t C, hipStream_t stream);
 
 /*
  * falcon_decode_step -- one read-after-write token for every (b, h) from a

@@ -319,3 +319,20 @@ def test_wait_limit_setting(lib):
     finally:
         fb.falcon_set_wait_limit(prev)
     assert fb.falcon_set_wait_limit(prev) == prev
+
+
+def test_noalloc_validation(lib):
+    def call(p, C=64, **over):
+        a = fwd_args(**over)
+        return lib.falcon_fwd_chunked_noalloc(ctypes.byref(p) if p is not None else None, a["k"], a["q"],
+                                              a["v"], a["beta"], a["lam"], a["S0"], a["kp"], a["o"],
+                                              a["ST"], C, None)
+    assert call(None) == NULL
+    assert call(prob(dk=48)) == SHAPE
+    assert call(prob(), C=8) == CHUNK
+    assert call(prob(), o=fake(2)) == ALIAS
+    assert call(prob(), k=None) == NULL
+    # one Falcon-1 sequence of 2048 chunks needs more than the 64 MiB static buffer
+    assert call(prob(B=1, H=1, T=2048 * 64)) == -11
+    assert "scratch" in fb.falcon_status_string(-11)
+    assert call(prob(T=0), ST=None) == OK                   # nothing to do, nothing launched
