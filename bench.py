@@ -524,6 +524,17 @@ def cpu_baseline(d, w, o_gpu, S_gpu, pool=None, nproc=1):
             "seconds": round(wall, 3), "os_cpu_count": os.cpu_count(), "single_core": one}
 
 
+# Other workloads that --leg runs alone (for profiling): name -> fn(steps, warmup)
+LEGS = {
+    "decode": lambda steps, warmup: bench_decode(warmup=warmup),
+    "f1a": lambda steps, warmup: bench_chunked_workload("f1a_chunked_2x12x16384_d64", steps, warmup),
+    "f2": lambda steps, warmup: bench_chunked_workload("f2_chunked_8x12x2048_d64", steps, warmup),
+    "f32": lambda steps, warmup: bench_chunked_workload("f1_chunked_f32_8x12x2048_d64", steps, warmup),
+    "recurrent": lambda steps, warmup: bench_recurrent(steps=steps, warmup=warmup),
+    "backward": lambda steps, warmup: bench_backward(steps=steps, warmup=warmup),
+}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -538,6 +549,10 @@ def main():
                     help="only run a plain copy of known size (for PMC counter scaling)")
     ap.add_argument("--backward-only", action="store_true",
                     help="only time the Falcon-1 backward leg (--steps calls), for profiling")
+    ap.add_argument("--leg", choices=sorted(LEGS),
+                    help="only time this other workload (--steps calls after --warmup), for profiling")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the copy and GEMM reference rates (for profiling the headline step)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the Falcon forward "
@@ -561,6 +576,9 @@ def main():
     if args.backward_only:
         print(json.dumps({"f1_backward": bench_backward(steps=args.steps, warmup=1)}))
         return
+    if args.leg:
+        print(json.dumps({args.leg: LEGS[args.leg](args.steps, args.warmup)}))
+        return
     w = I.WORKLOADS[WORKLOAD]
     d = I.workload_inputs(w)
     dev = {k: v.cuda() for k, v in d.items()}
@@ -577,7 +595,7 @@ def main():
 
     # the copy and GEMM reference rates are measured first: about a second of
     # GPU work, after which the clocks have ramped up for the timed steps
-    peaks = measured_peaks()
+    peaks = None if args.no_peaks else measured_peaks()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -621,8 +639,9 @@ def main():
                      "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes": bytes_alg, "kernel_ms": ev_ms, "kernels": STEP_KERNELS},
     }
-    line["measured_peaks"] = peaks
-    line["roofline"]["frac_of_measured_copy"] = achieved_gbs / line["measured_peaks"]["copy_gbs"]
+    if peaks:
+        line["measured_peaks"] = peaks
+        line["roofline"]["frac_of_measured_copy"] = achieved_gbs / peaks["copy_gbs"]
     if not args.no_decode:
         line["decode"] = bench_decode()
     if not args.no_extra:
@@ -630,7 +649,8 @@ def main():
         line["f2_chunked"] = bench_chunked_workload("f2_chunked_8x12x2048_d64", steps=5, warmup=1)
         line["f1_backward"] = bench_backward()
         rb = line["f1_backward"]["roofline"]
-        rb["frac_of_measured_fp32_gemm"] = rb["achieved"] / line["measured_peaks"]["fp32_gemm_tflops"]
+        if peaks:
+            rb["frac_of_measured_fp32_gemm"] = rb["achieved"] / peaks["fp32_gemm_tflops"]
         line["f1_recurrent"] = bench_recurrent()
         line["f1_chunked_f32"] = bench_chunked_workload("f1_chunked_f32_8x12x2048_d64", steps=5, warmup=1)
     if not args.no_cpu_baseline:
