@@ -25,13 +25,23 @@ METRIC = "tokens/sec + % MFMA peak, Falcon-1 chunked fwd B=8 H=12 T=2048 d=64 bf
 WORKLOAD = "f1_chunked_8x12x2048_d64"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "falcon1_chunked_wy_8x12x2048_d64_pmc.md")
-# The headline step runs two launches: the chunk-parallel WY factors and the
-# per-sequence chain (state passing and outputs).
+FP32_MFMA_PEAK_TFLOPS = 157.3   # MI355X dense fp32 MFMA, published
+# The headline step runs two launches: the chunk-parallel chunk matrices and
+# the per-sequence chain (state passing and outputs).
 STEP_KERNELS = ["falcon1_wy_kernel", "falcon1_chain_kernel"]
-KERNEL_SOURCES = ["delta_rule_recurrence_amd/csrc/falcon_chunked_wy.hip",
-                  "delta_rule_recurrence_amd/csrc/falcon_mfma_frag.h",
-                  "delta_rule_recurrence_amd/csrc/falcon_chunked.hip"]
+# rocprofv3 counter summaries under profiles/ (<name>_counters.md), each valid
+# while the sources of its kernels hash to the value recorded in it.
+_CSRC = "delta_rule_recurrence_amd/csrc/"
+PROFILE_SOURCES = {
+    "falcon1_chunked_8x12x2048_d64": [_CSRC + "falcon_chunked_wy.hip", _CSRC + "falcon_mfma_frag.h",
+                                      _CSRC + "falcon_chunked.hip"],
+    "falcon1a_chunked_2x12x16384_d64": [_CSRC + "falcon_chunked_scan.hip", _CSRC + "falcon_mfma_frag.h"],
+    "falcon2_chunked_8x12x2048_d64": [_CSRC + "falcon_chunked_percol.hip", _CSRC + "falcon_mfma_frag.h"],
+    "falcon1_decode_512x12_d128": [_CSRC + "falcon_recurrent.hip"],
+    "falcon1_recurrent_8x12x2048_d64": [_CSRC + "falcon_recurrent.hip"],
+    "falcon1_chunked_f32_8x12x2048_d64": [_CSRC + "falcon_generic_kernel.h", _CSRC + "falcon_chunked_generic.hip",
+                                          _CSRC + "falcon_chunked_generic_c64.hip"],
+}
 
 
 def algorithmic_bytes(B, H, T, dk, dv, io_bytes=2, per_column_beta=False):
@@ -66,27 +76,56 @@ def recurrence_flops(B, H, T, dk, dv):
     return 7.0 * B * H * T * dk * dv
 
 
-def kernel_source_hash():
+def kernel_source_hash(name):
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in PROFILE_SOURCES[name]:
         p = os.path.join(ROOT, rel)
         if os.path.exists(p):
             h.update(open(p, "rb").read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per step (both launches) from the committed rocprofv3 PMC
-    summary, or None when the kernel sources changed after the counters were
+def profile_counters(name):
+    """Per-call totals from the committed rocprofv3 summary
+    profiles/<name>_counters.md (HBM traffic from FETCH_SIZE / WRITE_SIZE
+    scaled by a plain copy, MFMA flops from SQ_INSTS_VALU_MFMA_MOPS_*, kernel
+    time), or None when the kernel sources changed after the counters were
     taken."""
-    if not os.path.exists(PMC_SUMMARY):
+    path = os.path.join(ROOT, "profiles", f"{name}_counters.md")
+    if not os.path.exists(path):
         return None
-    text = open(PMC_SUMMARY).read()
-    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
-    m_bytes = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not (m_hash and m_bytes) or m_hash.group(1) != kernel_source_hash():
+    m = re.search(r"^pmc_json:\s*(\{.*\})\s*$", open(path).read(), flags=re.M)
+    if not m:
         return None
-    return float(m_bytes.group(1))
+    d = json.loads(m.group(1))
+    if d.get("kernel_source_sha256_16") != kernel_source_hash(name):
+        return None
+    return d
+
+
+def counter_fields(name, ms):
+    """Roofline `traffic` and the counter-derived MFMA share of peak for a leg
+    whose call takes `ms` milliseconds (None where no valid summary exists)."""
+    c = profile_counters(name)
+    if c is None:
+        return None, None
+    t = ms * 1e-3
+    mfma = {"bf16_pct_of_peak": 100.0 * c["mfma_bf16_flops"] / t / (BF16_MFMA_PEAK_TFLOPS * 1e12),
+            "f32_pct_of_peak": 100.0 * c["mfma_f32_flops"] / t / (FP32_MFMA_PEAK_TFLOPS * 1e12),
+            "bf16_flops_per_call": c["mfma_bf16_flops"], "f32_flops_per_call": c["mfma_f32_flops"],
+            "source": f"profiles/{name}_counters.md (SQ_INSTS_VALU_MFMA_MOPS_* x 512)"}
+    return c["traffic_bytes"], mfma
+
+
+def attach_counters(out, profile, ms):
+    """Fill a leg's roofline `traffic` and its counter-derived MFMA share from
+    the committed summary of its kernels (left null when none is valid)."""
+    traffic, mfma = counter_fields(profile, ms)
+    if "roofline" in out:
+        out["roofline"]["traffic"] = traffic
+    out["mfma_counters"] = mfma
+    out["counters_profile"] = f"profiles/{profile}_counters.md"
+    return out
 
 
 def decode_bytes(B, H, dk, dv, io_bytes=2):
@@ -145,12 +184,13 @@ def bench_decode(warmup=5):
     ms = e0.elapsed_time(e1) / steps
     nbytes = decode_bytes(B, H, dk, dv)
     gbs = nbytes / (ms * 1e-3) / 1e9
-    return {"workload": D["name"], "steps": steps, "state": "from a 128-token prefix (chunked, f32 I/O)",
-            "us_per_step": ms * 1e3, "tokens_per_s": B / (ms * 1e-3), "algorithmic_bytes": nbytes,
-            "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
-            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "traffic": None, "algorithmic_bytes": nbytes,
-                         "kernels": ["decode_kernel"]}}
+    out = {"workload": D["name"], "steps": steps, "state": "from a 128-token prefix (chunked, f32 I/O)",
+           "us_per_step": ms * 1e3, "tokens_per_s": B / (ms * 1e-3), "algorithmic_bytes": nbytes,
+           "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+           "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": gbs / HBM_PEAK_GBS, "traffic": None, "algorithmic_bytes": nbytes,
+                        "kernels": ["decode_kernel"]}}
+    return attach_counters(out, "falcon1_decode_512x12_d128", ms)
 
 
 def bench_chunked_workload(name, steps=20, warmup=3):
@@ -208,14 +248,19 @@ def bench_chunked_workload(name, steps=20, warmup=3):
     elif w.io_dtype == "f32":
         # the general chunked kernel: chunks of a sequence are dependent and one
         # workgroup fills a CU's LDS
-        out["bound"] = "latency (dependent chunks per sequence, one wave per SIMD)"
-        out["kernels"] = ["chunked_generic_kernel"]
+        out["roofline"] = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": gbs / HBM_PEAK_GBS, "traffic": None, "algorithmic_bytes": nbytes,
+                           "kernels": ["chunked_generic_kernel"]}
+        out["limited_by"] = "latency (dependent chunks per sequence, one wave per SIMD)"
     elif w.variant == "falcon1a":
         out["roofline"] = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": gbs / HBM_PEAK_GBS, "traffic": None, "algorithmic_bytes": nbytes,
                            "kernels": ["falcon1a_tile_kernel<false>", "falcon1a_tile_scan_kernel",
                                        "falcon1a_tile_kernel<true>"]}
-    return out
+    profile = {"f1a_chunked_2x12x16384_d64": "falcon1a_chunked_2x12x16384_d64",
+               "f2_chunked_8x12x2048_d64": "falcon2_chunked_8x12x2048_d64",
+               "f1_chunked_f32_8x12x2048_d64": "falcon1_chunked_f32_8x12x2048_d64"}.get(name)
+    return attach_counters(out, profile, ms) if profile else out
 
 
 def bench_recurrent(name="f1_chunked_8x12x2048_d64", steps=5, warmup=1):
@@ -249,10 +294,14 @@ def bench_recurrent(name="f1_chunked_8x12x2048_d64", steps=5, warmup=1):
     ms = e0.elapsed_time(e1) / steps
     nbytes = algorithmic_bytes(w.B, w.H, w.T, w.dk, w.dv)
     gbs = nbytes / (ms * 1e-3) / 1e9
-    return {"workload": name, "entry": "falcon_fwd_recurrent", "steps": steps, "us_per_step": ms * 1e3,
-            "tokens_per_s": w.B * w.T / (ms * 1e-3), "algorithmic_bytes": nbytes, "hbm_gbs": gbs,
-            "hbm_frac": gbs / HBM_PEAK_GBS,
-            "bound": "latency (T dependent steps per sequence)"}
+    out = {"workload": name, "entry": "falcon_fwd_recurrent", "steps": steps, "us_per_step": ms * 1e3,
+           "tokens_per_s": w.B * w.T / (ms * 1e-3), "algorithmic_bytes": nbytes, "hbm_gbs": gbs,
+           "hbm_frac": gbs / HBM_PEAK_GBS,
+           "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": gbs / HBM_PEAK_GBS, "traffic": None, "algorithmic_bytes": nbytes,
+                        "kernels": ["recurrent_kernel"]},
+           "limited_by": "latency (T dependent steps per sequence)"}
+    return attach_counters(out, "falcon1_recurrent_8x12x2048_d64", ms)
 
 
 def backward_bytes(B, H, T, dk, dv, io_bytes=2):
@@ -264,7 +313,6 @@ def backward_bytes(B, H, T, dk, dv, io_bytes=2):
     return th * ((2 * dk + 2 * dv) * io_bytes + 8) + th * ((2 * dk + dv) * 4 + 8) + 2 * state
 
 
-FP32_MFMA_PEAK_TFLOPS = 157.3   # MI355X dense fp32 MFMA, published
 
 
 def backward_flops(B, H, T, dk=64, dv=64, C=32):
@@ -617,7 +665,7 @@ def main():
     # The step is the two launches back to back on one stream; the event time
     # brackets both, and the roofline is taken over the whole step.
     achieved_gbs = bytes_alg / (ev_ms * 1e-3) / 1e9
-    traffic = measured_traffic()
+    traffic, mfma_counters = counter_fields("falcon1_chunked_8x12x2048_d64", ev_ms)
     line = {
         "metric": METRIC,
         "value": tokens / (ms_per_step * 1e-3),
@@ -635,6 +683,10 @@ def main():
                    "dk": w.dk, "dv": w.dv, "C": w.C, "io": "bf16", "state": "f32"},
         # algorithmic flops of the chunk form (not a counter) over the step time
         "mfma_pct_of_peak_algorithmic": 100.0 * flops_alg / (ev_ms * 1e-3) / (BF16_MFMA_PEAK_TFLOPS * 1e12),
+        # flops the matrix cores executed (rocprofv3 SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512, committed
+        # summary) over the step time
+        "mfma_pct_of_peak_counters": None if mfma_counters is None else mfma_counters["bf16_pct_of_peak"],
+        "mfma_counters": mfma_counters,
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes": bytes_alg, "kernel_ms": ev_ms, "kernels": STEP_KERNELS},
