@@ -19,6 +19,8 @@
 // streaming the chunk matrices back.  The state is rounded to bf16 only as
 // the operand of K S and Qt S; its decay term stays in float32.
 
+#include <stdlib.h>
+
 #include "falcon_device.h"
 #include "falcon_launch.h"
 #include "falcon_mfma_frag.h"
@@ -92,6 +94,7 @@ struct WyGates {
   float eta[kC];                  // eta_s
   float eta_t[kC];                // eta_i at [c16 * 4 + ib] for i = 16 ib + c16
   float gprev_t[kC];              // g_{i-1}, same order
+  float e63;                      // e^{g_63}
 };
 
 struct WySmem {
@@ -101,6 +104,7 @@ struct WySmem {
   uint16_t tb[kC * kP];           // T, row-major
   float abt[4][16][16];           // diagonal blocks of -A: [b][s][i] = -A[16b+i][16b+s]
   WyGates G;
+  int go;                         // the output policy's verdict, shared by the waves
 };
 
 // T = (I + A)^{-1} into sm.tb (wave 0): the decayed Gram on MFMA, the four
@@ -212,26 +216,32 @@ __device__ __forceinline__ f32x4 unpack_half(uint2 v) {
                __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u)};
 }
 
+// The chunk matrices of chunk c of sequence bh, computed by one workgroup of
+// four waves and handed to `out`: out.prefetch() is called at the start,
+// out.acquire() by every wave before the first store (it returns the same
+// verdict in every wave; false: store nothing); each wave then stores its
+// row block of K and H to out.block() (element offsets Out::kK, Out::kH), the
+// wave holding the gates stores e^{g_63} to out.decay(), and every wave hands
+// its token block of Qt (fragments) and of Ot^T (bf16 tiles) to out.finish().
+//
 // Every global load is issued at the start, so a workgroup waits for memory
 // once.  Keys and values are staged in LDS; each wave's queries and the gate
 // inputs go straight into registers.  Wave w owns token block ib = w of the
 // read mask M, Qt and Ot, and row block w of K and H.
-__global__ void __launch_bounds__(256, 4)
-falcon1_wy_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restrict__ phi_q,
-                  const bf16_t* __restrict__ v, const float* __restrict__ beta, const float* __restrict__ lam,
-                  const bf16_t* __restrict__ k_prev, uint16_t* __restrict__ blocks, float* __restrict__ decay63,
-                  int T, int nchunks, float eps, float eps_gamma) {
-  __shared__ WySmem sm;
+template <class Out>
+__device__ __forceinline__ void wy_chunk(WySmem& sm, const bf16_t* __restrict__ phi_k,
+                                         const bf16_t* __restrict__ phi_q, const bf16_t* __restrict__ v,
+                                         const float* __restrict__ beta, const float* __restrict__ lam,
+                                         const bf16_t* __restrict__ k_prev, int64_t bh, int c, int T,
+                                         float eps, float eps_gamma, Out& out) {
   const int tid = threadIdx.x;
   // role index: wave-uniform (so role branches are scalar) and rotated by the
   // workgroup, so the long inverse role is spread over the SIMDs
   const int w = (__builtin_amdgcn_readfirstlane(tid >> 6) + int(blockIdx.x)) & 3, l = tid & 63;
   const int g = l >> 4, c16 = l & 15;
-  const int64_t bh = blockIdx.x / nchunks;
-  const int c = blockIdx.x % nchunks;
   const Seq sq = make_seq(phi_k, phi_q, v, beta, lam, k_prev, bh, T);
   const bool fresh = (k_prev == nullptr);
-  uint16_t* out = blocks + int64_t(blockIdx.x) * kBlockElems;
+  out.prefetch(w);
 
   // ---- stage keys and values (wave w rows 16w..16w+15); fetch this wave's
   // queries and, for the gates, beta and lam of token c * 64 + l --------------
@@ -264,7 +274,7 @@ falcon1_wy_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restrict__ p
     sm.G.eta[l] = eta;
     sm.G.eta_t[c16 * 4 + g] = eta;
     sm.G.gprev_t[c16 * 4 + g] = gprev;
-    if (l == 0) decay63[blockIdx.x] = __expf(glast);
+    if (l == 0) sm.G.e63 = __expf(glast);
   }
   __syncthreads();
   // ---- T; scaled key and value transposes; this wave's rows of M -------------
@@ -368,6 +378,9 @@ falcon1_wy_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restrict__ p
   }
   __syncthreads();                                           // frag(-W^T), frag(U^T) complete
   // ---- chunk matrices ---------------------------------------------------------
+  if (!out.acquire(sm, w, l)) return;
+  uint16_t* dst = out.block();
+  if (w == 0 && l == 0) *out.decay() = sm.G.e63;
   {
     bf16x8 wt[4][2], ut[4][2];
 #pragma unroll
@@ -386,16 +399,17 @@ falcon1_wy_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restrict__ p
       t0 = mfma32(wt[2 * m][1], xh1, t0);
       f32x4 t1 = mfma32(wt[2 * m + 1][0], xh0, zero4());
       t1 = mfma32(wt[2 * m + 1][1], xh1, t1);
-      store_frag(out + kOutK + fslot(w, m, l), frag_acc(t0, t1));
+      store_frag(dst + Out::kK + fslot(w, m, l), frag_acc(t0, t1));
     }
     // H: tile (fb = w, cb) of Xh^T U, lane holds H[16w+4g+r][16cb+c16]
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
       f32x4 hacc = mfma32(xh0, ut[cb][0], zero4());
       hacc = mfma32(xh1, ut[cb][1], hacc);
-      store_half(out + kOutH + ((cb * 4 + w) * 64 + l) * 4, hacc);
+      store_half(dst + Out::kH + ((cb * 4 + w) * 64 + l) * 4, hacc);
     }
     // Qt: tile (fb, ib = w) of e^{g_i} Q^T - W^T M^T = Qt^T; fb = 2m, 2m+1 stack into frag(Qt)[w][m]
+    bf16x8 qt[2];
     {
       const float egi = __expf(sm.G.graw[16 * w + c16]);
 #pragma unroll
@@ -409,17 +423,48 @@ falcon1_wy_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restrict__ p
           if (w >= 2) acc = mfma32(wt[fb][1], mf[1], acc);
           t[h] = acc;
         }
-        store_frag(out + kOutQt + fslot(w, m, l), frag_acc(t[0], t[1]));
+        qt[m] = frag_acc(t[0], t[1]);
       }
     }
-    // Ot^T: tile (cb, ib = w) of U^T M^T, lane holds Ot[16w+c16][16cb+4g+r]
+    // Ot^T: tile (cb, ib = w) of U^T M^T, lane holds Ot[16w+c16][16cb+4g+r] (bf16)
+    uint2 ot[4];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
       f32x4 oacc = mfma32(ut[cb][0], mf[0], zero4());
       if (w >= 2) oacc = mfma32(ut[cb][1], mf[1], oacc);
-      store_half(out + kOutOt + ((cb * 4 + w) * 64 + l) * 4, oacc);
+      ot[cb] = make_uint2(pack_bf16x2(oacc[0], oacc[1]), pack_bf16x2(oacc[2], oacc[3]));
     }
+    out.finish(sm, w, l, qt, ot);
   }
+}
+
+// Output policy of the two-launch form: every chunk has its own block of the
+// workspace holding K, Qt, H and Ot; nothing to wait for or announce.
+struct BlockOut {
+  static constexpr int kK = kOutK, kH = kOutH;
+  uint16_t* blk;
+  float* e63;
+  __device__ void prefetch(int) {}
+  __device__ bool acquire(WySmem&, int, int) { return true; }
+  __device__ uint16_t* block() { return blk; }
+  __device__ float* decay() { return e63; }
+  __device__ void finish(WySmem&, int w, int l, const bf16x8 (&qt)[2], const uint2 (&ot)[4]) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) store_frag(blk + kOutQt + fslot(w, m, l), qt[m]);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) *reinterpret_cast<uint2*>(blk + kOutOt + ((cb * 4 + w) * 64 + l) * 4) = ot[cb];
+  }
+};
+
+__global__ void __launch_bounds__(256, 4)
+falcon1_wy_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restrict__ phi_q,
+                  const bf16_t* __restrict__ v, const float* __restrict__ beta, const float* __restrict__ lam,
+                  const bf16_t* __restrict__ k_prev, uint16_t* __restrict__ blocks, float* __restrict__ decay63,
+                  int T, int nchunks, float eps, float eps_gamma) {
+  __shared__ WySmem sm;
+  BlockOut out{blocks + int64_t(blockIdx.x) * kBlockElems, decay63 + blockIdx.x};
+  wy_chunk(sm, phi_k, phi_q, v, beta, lam, k_prev, blockIdx.x / nchunks, blockIdx.x % nchunks, T, eps, eps_gamma,
+           out);
 }
 
 // ============================================================================
@@ -638,30 +683,418 @@ falcon1_chain_kernel(const float* S0, const uint16_t* __restrict__ blocks, const
   }
 }
 
+// ============================================================================
+// One launch: chunk workgroups and per-sequence chains side by side.
+//
+// Chunk workgroups build and store the chunk matrices exactly as in the
+// two-launch form and announce each block with a flag; the chain of a
+// sequence starts on a chunk as soon as it is announced, so the sequential
+// part overlaps the chunk-parallel part and reads the blocks from L2 rather
+// than HBM.
+//
+// Placement: workgroup b runs on XCD b mod 8 (workgroups are dealt to the
+// XCDs in turn).  The chain of sequence s runs in workgroups s and BHpad + s
+// (value-column halves) and chunk c of s in workgroup BHpad (c + 2) + s, so
+// all of a sequence's work sits on XCD s mod 8 and shares its L2.  Chains come
+// first in the grid, so they are resident before any chunk workgroup is
+// dispatched, and chunk workgroups never wait, so every wait of a chain ends.
+// The waits are nevertheless bounded: a wait that gives up poisons the
+// sequence's outputs and final state with NaN.
+//
+// Hand-over without device-wide fences: a chunk workgroup's stores reach the
+// L2 of its XCD before it announces them (s_waitcnt vmcnt(0) in every wave,
+// then a barrier, then the flag store); the chain, on the same XCD, reads the
+// flag with a device-scope load and only then the block, from that L2.  No
+// block address is read before its announcement or twice by one CU in a
+// launch, and the vector L1 starts every launch empty, so no L1 line is ever
+// stale; the decays, several to a line, are read with device-scope loads.
+// Flags carry the writer's XCD, and a chain that sees another XCD gives up
+// (NaN) rather than read an incoherent L2.
+// ============================================================================
+
+constexpr int kTagMask = 0xffffff;
+
+struct FusedArgs {
+  const bf16_t* phi_k;
+  const bf16_t* phi_q;
+  const bf16_t* v;
+  const float* beta;
+  const float* lam;
+  const bf16_t* k_prev;
+  const float* S0;
+  bf16_t* o;
+  float* S_T;
+  uint16_t* blocks;                    // [BH][nchunks][kBlockElems]
+  float* decay63;                      // [BH][nchunks]
+  int* flags;                          // [BHpad][nflag], zero at launch
+  int T, nchunks, nflag, BH, BHpad, spin_limit;
+  float eps, eps_gamma;
+};
+
+__device__ __forceinline__ int xcc_id() {
+  return __builtin_amdgcn_s_getreg((3 << 11) | 20) & 15;      // HW_REG_XCC_ID, bits 3:0
+}
+__device__ __forceinline__ int load_flag(const int* f) {
+  return __builtin_amdgcn_readfirstlane(__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+// 1: the flag announces chunk c from this XCD; 0: not yet; -1: from another XCD
+__device__ __forceinline__ int tag_state(int v, int c, int xcc) {
+  if ((v & kTagMask) != ((c + 1) & kTagMask)) return 0;
+  return (v >> 24) == xcc ? 1 : -1;
+}
+
+// Output policy of a chunk workgroup of the one-launch form: the block of the
+// two-launch form, then its announcement.
+struct FlagOut {
+  static constexpr int kK = kOutK, kH = kOutH;
+  uint16_t* blk;
+  float* e63;
+  int* ready;                          // this chunk's flag
+  int tag;                             // (XCD << 24) | (c + 1)
+  __device__ void prefetch(int) {}
+  __device__ bool acquire(WySmem&, int, int) { return true; }
+  __device__ uint16_t* block() { return blk; }
+  __device__ float* decay() { return e63; }
+  __device__ void finish(WySmem&, int w, int l, const bf16x8 (&qt)[2], const uint2 (&ot)[4]) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) store_frag(blk + kOutQt + fslot(w, m, l), qt[m]);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) *reinterpret_cast<uint2*>(blk + kOutOt + ((cb * 4 + w) * 64 + l) * 4) = ot[cb];
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");       // this wave's stores are in L2
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_store(ready, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+};
+
+// Chain workgroup of one value-column half of a sequence: waves 0 and 1 hold
+// the state of value columns 16 cb .. 16 cb + 15 (cb = 2 part + wave) and
+// fetch their own H and Ot tiles; waves 2 and 3 stage K and Qt, which both
+// chain waves need, into a double-buffered LDS entry (16 KiB each).
+struct ChainSmemKQ {
+  uint16_t kq[2][8192];
+  int ready[2];                        // chunks stored into entry j so far
+  int freed[2];                        // +1 per chain wave done reading entry j
+  int seen[2];                         // chunks of entry j seen announced so far
+  int abort_flag;
+};
+
+union FusedSmem {
+  WySmem p;
+  ChainSmemKQ c;
+};
+
+// Waits until chunk c is announced by a chunk workgroup on this XCD; `seen`
+// is its flag as read earlier (0 if never), so that a chunk announced in time
+// costs no wait.  A wait that gives up (any wait, with a limit of 0), or a
+// writer on another XCD, sets the workgroup's abort flag.
+__device__ __forceinline__ void wait_chunk(const int* flag, int c, int xcc, int limit, int seen, int* abort_flag) {
+  if (__hip_atomic_load(abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) return;
+  int v = __builtin_amdgcn_readfirstlane(seen);
+  for (int it = 0; limit > 0; ++it) {
+    const int st = tag_state(v, c, xcc);
+    if (st == 1) return;
+    if (st < 0 || it >= limit) break;
+    if (it > 0) __builtin_amdgcn_s_sleep(1);
+    v = load_flag(flag);
+  }
+  __hip_atomic_store(abort_flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// K and Qt of a chunk: 16 fragments of 1 KiB, a lane's 16 bytes of each.
+struct KQShare {
+  bf16x8 f[16];
+};
+
+// Staging wave j: chunks j, j + 2, ... into entry j, each read into
+// registers as soon as the previous one is stored.  A chunk is read only
+// after its announcement: an early read would leave stale lines in this CU's
+// L1 for the real read to hit.  The stagers alone poll the flags and pass on
+// what they see through `seen`, so the chain waves wait on LDS only.
+__device__ __forceinline__ void kq_stager(ChainSmemKQ& sm, const FusedArgs& a, int s, int j, int l, int xcc) {
+  const int n = a.nchunks;
+  const int* fl = a.flags + int64_t(s) * a.nflag;
+  const uint16_t* blocks = a.blocks + int64_t(s) * n * kBlockElems + l * 8;
+  int ahead = j < n ? __hip_atomic_load(&fl[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+  for (int c = j, k = 0; c < n; c += 2, ++k) {
+    wait_chunk(&fl[c], c, xcc, a.spin_limit, ahead, &sm.abort_flag);
+    signal_add(&sm.seen[j], l);                            // the chain waves may now read its tiles
+    KQShare r;
+    const uint16_t* blk = blocks + int64_t(c) * kBlockElems;
+#pragma unroll
+    for (int f = 0; f < 16; ++f) r.f[f] = load_frag(blk + f * 512);
+    if (c + 2 < n) ahead = __hip_atomic_load(&fl[c + 2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // entry j is free once both chain waves have read its previous chunk
+    wait_at_least(&sm.freed[j], 2 * k, &sm.abort_flag, a.spin_limit);
+#pragma unroll
+    for (int f = 0; f < 16; ++f) store_frag(&sm.kq[j][f * 512 + l * 8], r.f[f]);
+    signal_add(&sm.ready[j], l);
+  }
+}
+
+// This wave's H and Ot tiles of a chunk and its decay.
+struct TileShare {
+  uint2 h0, h1, h2, h3, o0, o1, o2, o3;
+  float e63;
+};
+__device__ __forceinline__ TileShare load_tiles(const uint16_t* blk, const float* e63, int cb, int l) {
+  TileShare r;
+  const uint2* h = reinterpret_cast<const uint2*>(blk + kOutH + (cb * 4 * 64 + l) * 4);
+  const uint2* o = reinterpret_cast<const uint2*>(blk + kOutOt + (cb * 4 * 64 + l) * 4);
+  r.h0 = h[0];
+  r.h1 = h[64];
+  r.h2 = h[128];
+  r.h3 = h[192];
+  r.o0 = o[0];
+  r.o1 = o[64];
+  r.o2 = o[128];
+  r.o3 = o[192];
+  r.e63 = __hip_atomic_load(e63, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return r;
+}
+
+// What a chain wave carries from chunk to chunk.
+struct ChainCtx {
+  const uint16_t* blocks;              // the sequence's blocks
+  const float* e63;                    // the sequence's decays
+  bf16_t* o;                           // the sequence's outputs
+  int cb, l;
+};
+
+// One chunk of a chain wave: S <- e^{g_63} S + K S + H and O = Qt S + Ot, with
+// the operand roundings of the two-launch chain.  `cur` holds this chunk's H
+// and Ot tiles; the next chunk's are read into `nxt` once it is announced, so
+// their latency hides behind this chunk's work.  Every chunk but the last
+// (kLast) issues the same loads and stores on every path, and the caller
+// alternates two tile sets rather than copying one into the other: the
+// compiler then waits for exactly the loads a step uses, never for the
+// previous chunk's output stores.
+template <bool kLast>
+__device__ __forceinline__ void chain_step(ChainSmemKQ& sm, const FusedArgs& a, ChainCtx& x, int c,
+                                           const TileShare& cur, TileShare& nxt, f32x4 (&S)[4], bf16x8& sb0,
+                                           bf16x8& sb1) {
+  const int l = x.l;
+  if constexpr (!kLast) {
+    wait_at_least(&sm.seen[(c + 1) & 1], ((c + 1) >> 1) + 1, &sm.abort_flag, a.spin_limit);
+    nxt = load_tiles(x.blocks + int64_t(c + 1) * kBlockElems, x.e63 + c + 1, x.cb, l);
+  }
+  const int j = c & 1;
+  wait_at_least(&sm.ready[j], (c >> 1) + 1, &sm.abort_flag, a.spin_limit);
+  const uint16_t* D = sm.kq[j];
+  // O^T tiles from the state at the chunk's start: S^T Qt^T + Ot^T; lane
+  // holds o[c*64+16ib+c16][16cb+4g+r]
+  const int g = l >> 4, c16 = l & 15;
+  const uint2 oc[4] = {cur.o0, cur.o1, cur.o2, cur.o3};
+#pragma unroll
+  for (int ib = 0; ib < 4; ++ib) {
+    const bf16x8 q0 = load_frag(&D[kOutQt + fslot(ib, 0, l)]);
+    const bf16x8 q1 = load_frag(&D[kOutQt + fslot(ib, 1, l)]);
+    f32x4 acc = mfma32(sb0, q0, unpack_half(oc[ib]));
+    acc = mfma32(sb1, q1, acc);
+    const int tok = c * kC + 16 * ib + c16;
+    if (!kLast || tok < a.T)
+      *reinterpret_cast<uint2*>(x.o + int64_t(tok) * kD + 16 * x.cb + 4 * g) =
+          make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+  }
+  // S <- e^{g_63} S + K S + H
+  const float ec = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(cur.e63)));
+  const uint2 hc[4] = {cur.h0, cur.h1, cur.h2, cur.h3};
+#pragma unroll
+  for (int fb = 0; fb < 4; ++fb) {
+    const bf16x8 k0 = load_frag(&D[kOutK + fslot(fb, 0, l)]);
+    const bf16x8 k1 = load_frag(&D[kOutK + fslot(fb, 1, l)]);
+    f32x4 acc = S[fb] * ec + unpack_half(hc[fb]);
+    acc = mfma32(k0, sb0, acc);
+    S[fb] = mfma32(k1, sb1, acc);
+  }
+  signal_add(&sm.freed[j], l);                             // (its fence waits for the reads above)
+  sb0 = frag_acc(S[0], S[1]);
+  sb1 = frag_acc(S[2], S[3]);
+}
+
+// Chain wave cw: the state of value columns 16 cb .. 16 cb + 15 in MFMA result
+// registers.  Its H and Ot tiles come straight from L2, K and Qt from the
+// staged LDS entry.  The first chunk is peeled off the loop so that the loop
+// is entered with the loads and stores in flight that its back edge has.
+__device__ __forceinline__ void kq_chain(ChainSmemKQ& sm, const FusedArgs& a, int s, int part, int cw, int l) {
+  const int g = l >> 4, c16 = l & 15;
+  const int n = a.nchunks;
+  ChainCtx x;
+  x.blocks = a.blocks + int64_t(s) * n * kBlockElems;
+  x.e63 = a.decay63 + int64_t(s) * n;
+  x.o = a.o + int64_t(s) * a.T * kD;
+  x.cb = part * 2 + cw;
+  x.l = l;
+  f32x4 S[4];                                              // S[fb]: lane holds S[16fb+4g+r][16cb+c16]
+  const float* S0 = a.S0 ? a.S0 + int64_t(s) * kD * kD + 16 * x.cb + c16 : nullptr;
+#pragma unroll
+  for (int fb = 0; fb < 4; ++fb) {
+    S[fb] = zero4();
+    if (S0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S[fb][r] = S0[(16 * fb + 4 * g + r) * kD];
+    }
+  }
+  bf16x8 sb0 = frag_acc(S[0], S[1]);
+  bf16x8 sb1 = frag_acc(S[2], S[3]);
+  wait_at_least(&sm.seen[0], 1, &sm.abort_flag, a.spin_limit);
+  TileShare ta = load_tiles(x.blocks, x.e63, x.cb, l);
+  TileShare tb{};
+  if (n == 1) {
+    chain_step<true>(sm, a, x, 0, ta, tb, S, sb0, sb1);
+  } else {
+    chain_step<false>(sm, a, x, 0, ta, tb, S, sb0, sb1);
+    int c = 1;
+    for (; c + 2 < n; c += 2) {
+      chain_step<false>(sm, a, x, c, tb, ta, S, sb0, sb1);
+      chain_step<false>(sm, a, x, c + 1, ta, tb, S, sb0, sb1);
+    }
+    if (c + 1 < n) {
+      chain_step<false>(sm, a, x, c, tb, ta, S, sb0, sb1);
+      chain_step<true>(sm, a, x, c + 1, ta, tb, S, sb0, sb1);
+    } else {
+      chain_step<true>(sm, a, x, c, tb, ta, S, sb0, sb1);
+    }
+  }
+  if (a.S_T) {
+#pragma unroll
+    for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        a.S_T[(int64_t(s) * kD + 16 * fb + 4 * g + r) * kD + 16 * x.cb + c16] = S[fb][r];
+  }
+}
+
+__device__ __forceinline__ void chain_workgroup(ChainSmemKQ& sm, const FusedArgs& a, int s, int part) {
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
+  if (tid < 2) {
+    sm.ready[tid] = 0;
+    sm.freed[tid] = 0;
+    sm.seen[tid] = 0;
+  }
+  if (tid == 0) sm.abort_flag = 0;
+  __syncthreads();
+  const int xcc = xcc_id();
+  if (wave >= 2) kq_stager(sm, a, s, wave - 2, l, xcc);
+  else kq_chain(sm, a, s, part, wave, l);
+  // Every wave gets here.  A wait that gave up anywhere in the workgroup
+  // poisons this half of the sequence: its outputs and final state are NaN.
+  __syncthreads();
+  if (wave < 2 && __hip_atomic_load(&sm.abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0) {
+    const int cb = part * 2 + wave;
+    const uint16_t nan_bits = 0x7fc0;
+    const uint32_t nan2 = uint32_t(nan_bits) | (uint32_t(nan_bits) << 16);
+    bf16_t* o_s = a.o + int64_t(s) * a.T * kD;
+    for (int tok = l >> 1; tok < a.T; tok += 32)
+      *reinterpret_cast<uint4*>(o_s + int64_t(tok) * kD + 16 * cb + 8 * (l & 1)) = make_uint4(nan2, nan2, nan2, nan2);
+    if (a.S_T) {
+      const int g = l >> 4, c16 = l & 15;
+#pragma unroll
+      for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          a.S_T[(int64_t(s) * kD + 16 * fb + 4 * g + r) * kD + 16 * cb + c16] = __builtin_nanf("");
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256, 4) falcon1_fused_kernel(FusedArgs a) {
+  __shared__ FusedSmem sm;
+  const int b = blockIdx.x;
+  if (b < 2 * a.BHpad) {
+    const int s = b % a.BHpad, part = b / a.BHpad;
+    if (s < a.BH) chain_workgroup(sm.c, a, s, part);
+    return;
+  }
+  const int j = b - 2 * a.BHpad;
+  const int s = j % a.BHpad, c = j / a.BHpad;
+  if (s >= a.BH) return;
+  const int64_t q = int64_t(s) * a.nchunks + c;
+  FlagOut out{a.blocks + q * kBlockElems, a.decay63 + q, a.flags + int64_t(s) * a.nflag + c,
+              (xcc_id() << 24) | ((c + 1) & kTagMask)};
+  wy_chunk(sm.p, a.phi_k, a.phi_q, a.v, a.beta, a.lam, a.k_prev, s, c, a.T, a.eps, a.eps_gamma, out);
+}
+
+__global__ void zero_ints_kernel(int* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+bool use_two_launch_form() {
+  static const bool v = [] {
+    const char* e = getenv("FALCON_F1_TWO_LAUNCH");
+    return e && e[0] == '1';
+  }();
+  return v;
+}
+
 }  // namespace
 
 bool chunked_wy_applies(const ProblemArgs& a) {
   return a.bf16 && a.variant == kF1 && a.dk == kD && a.dv == kD && a.C == kC && a.T > 0;
 }
 
+// Workspace: a 32 KiB block of chunk matrices per chunk, then the decays
+// e^{g_63}; the one-launch form adds a line of flags per sequence in front.
+struct WyLayout {
+  int64_t BHpad, nflag, flags_bytes, e63_bytes, blocks_bytes, total;
+  WyLayout(int64_t BH, int64_t nchunks) {
+    BHpad = (BH + 7) / 8 * 8;
+    nflag = (nchunks + 63) / 64 * 64;
+    flags_bytes = BHpad * nflag * 4;
+    e63_bytes = (BH * nchunks * 4 + 255) / 256 * 256;
+    blocks_bytes = BH * nchunks * int64_t(kBlockElems) * 2;
+    total = flags_bytes + e63_bytes + blocks_bytes;
+  }
+};
+
 size_t chunked_wy_workspace_bytes(const ProblemArgs& a) {
-  const int64_t nblk = int64_t(a.B) * a.H * ((int64_t(a.T) + kC - 1) / kC);
-  return size_t(nblk) * (kBlockElems * 2 + 4);
+  return size_t(WyLayout(int64_t(a.B) * a.H, (int64_t(a.T) + kC - 1) / kC).total);
 }
 
 hipError_t launch_chunked_wy(const ProblemArgs& a, hipStream_t st) {
   const int64_t BH = int64_t(a.B) * a.H;
   const int nchunks = (a.T + kC - 1) / kC;
   if (BH == 0 || nchunks == 0) return hipSuccess;
-  uint16_t* blocks = static_cast<uint16_t*>(a.workspace);
-  float* decay63 = reinterpret_cast<float*>(blocks + BH * nchunks * kBlockElems);
-  hipLaunchKernelGGL(falcon1_wy_kernel, dim3(unsigned(BH * nchunks)), dim3(256), 0, st,
-                     static_cast<const bf16_t*>(a.phi_k), static_cast<const bf16_t*>(a.phi_q),
-                     static_cast<const bf16_t*>(a.v), a.beta, a.lam, static_cast<const bf16_t*>(a.k_prev),
-                     blocks, decay63, a.T, nchunks, a.eps, a.eps_gamma);
-  const int64_t groups = (BH + 7) / 8;
-  hipLaunchKernelGGL(falcon1_chain_kernel, dim3(unsigned(groups * 8 * kSplit)), dim3(kChainThreads), 0, st,
-                     a.S0, blocks, decay63, static_cast<bf16_t*>(a.o), a.S_T, a.T, nchunks, BH, a.spin_limit);
+  const WyLayout L(BH, nchunks);
+  char* ws = static_cast<char*>(a.workspace);
+  int* flags = reinterpret_cast<int*>(ws);
+  float* decay63 = reinterpret_cast<float*>(ws + L.flags_bytes);
+  uint16_t* blocks = reinterpret_cast<uint16_t*>(ws + L.flags_bytes + L.e63_bytes);
+  if (use_two_launch_form()) {
+    hipLaunchKernelGGL(falcon1_wy_kernel, dim3(unsigned(BH * nchunks)), dim3(256), 0, st,
+                       static_cast<const bf16_t*>(a.phi_k), static_cast<const bf16_t*>(a.phi_q),
+                       static_cast<const bf16_t*>(a.v), a.beta, a.lam, static_cast<const bf16_t*>(a.k_prev),
+                       blocks, decay63, a.T, nchunks, a.eps, a.eps_gamma);
+    const int64_t groups = (BH + 7) / 8;
+    hipLaunchKernelGGL(falcon1_chain_kernel, dim3(unsigned(groups * 8 * kSplit)), dim3(kChainThreads), 0, st,
+                       a.S0, blocks, decay63, static_cast<bf16_t*>(a.o), a.S_T, a.T, nchunks, BH, a.spin_limit);
+    return hipGetLastError();
+  }
+  FusedArgs f;
+  f.phi_k = static_cast<const bf16_t*>(a.phi_k);
+  f.phi_q = static_cast<const bf16_t*>(a.phi_q);
+  f.v = static_cast<const bf16_t*>(a.v);
+  f.beta = a.beta;
+  f.lam = a.lam;
+  f.k_prev = static_cast<const bf16_t*>(a.k_prev);
+  f.S0 = a.S0;
+  f.o = static_cast<bf16_t*>(a.o);
+  f.S_T = a.S_T;
+  f.blocks = blocks;
+  f.decay63 = decay63;
+  f.flags = flags;
+  f.T = a.T;
+  f.nchunks = nchunks;
+  f.nflag = int(L.nflag);
+  f.BH = int(BH);
+  f.BHpad = int(L.BHpad);
+  f.spin_limit = a.spin_limit;
+  f.eps = a.eps;
+  f.eps_gamma = a.eps_gamma;
+  const int64_t nflags = L.flags_bytes / 4;
+  hipLaunchKernelGGL(zero_ints_kernel, dim3(unsigned((nflags + 255) / 256)), dim3(256), 0, st, flags, int(nflags));
+  hipLaunchKernelGGL(falcon1_fused_kernel, dim3(unsigned(L.BHpad * (int64_t(nchunks) + 2))), dim3(256), 0, st, f);
   return hipGetLastError();
 }
 

@@ -176,9 +176,9 @@ size_t falcon_workspace_bytes(const falcon_problem* p, int32_t C);
  * library holds on every GPU it runs on until the process ends.  When the
  * problem needs more scratch than that, the sequences are processed in
  * groups that fit, one group after another on `stream`; a problem in which a
- * single sequence needs more returns FALCON_ERR_SCRATCH (for Falcon-1 with
- * bf16 I/O, dk = dv = 64 and C = 64 that is T > 131008 tokens).  The call
- * allocates nothing.
+ * single sequence needs more returns FALCON_ERR_SCRATCH (with bf16 I/O,
+ * dk = dv = 64 and C = 64: Falcon-1 beyond T = 130880 tokens, Falcon-1A
+ * beyond T = 1048064).  The call allocates nothing.
  *
  * The buffer of a GPU is shared by every call on that GPU and keeps the last
  * call's contents; no part of it needs to start at zero.  Calls that overlap

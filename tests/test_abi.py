@@ -332,7 +332,9 @@ def test_noalloc_validation(lib):
     assert call(prob(), C=8) == CHUNK
     assert call(prob(), o=fake(2)) == ALIAS
     assert call(prob(), k=None) == NULL
-    # one Falcon-1 sequence of 2048 chunks needs more than the 64 MiB static buffer
+    # one sequence beyond the 64 MiB static buffer: Falcon-1 with 2048 chunks,
+    # Falcon-1A with 2^21 tokens (4096 tiles of aggregates)
     assert call(prob(B=1, H=1, T=2048 * 64)) == -11
+    assert call(prob(B=1, H=1, T=1 << 21, variant="falcon1a")) == -11
     assert "scratch" in fb.falcon_status_string(-11)
     assert call(prob(T=0), ST=None) == OK                   # nothing to do, nothing launched
