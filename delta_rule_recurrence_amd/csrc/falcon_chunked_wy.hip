@@ -766,27 +766,11 @@ struct FlagOut {
   }
 };
 
-// Chain workgroup of one value-column half of a sequence: waves 0 and 1 hold
-// the state of value columns 16 cb .. 16 cb + 15 (cb = 2 part + wave) and
-// fetch their own H and Ot tiles; waves 2 and 3 stage K and Qt, which both
-// chain waves need, into a double-buffered LDS entry (16 KiB each).
-struct ChainSmemKQ {
-  uint16_t kq[2][8192];
-  int ready[2];                        // chunks stored into entry j so far
-  int freed[2];                        // +1 per chain wave done reading entry j
-  int seen[2];                         // chunks of entry j seen announced so far
-  int abort_flag;
-};
-
-union FusedSmem {
-  WySmem p;
-  ChainSmemKQ c;
-};
-
 // Waits until chunk c is announced by a chunk workgroup on this XCD; `seen`
 // is its flag as read earlier (0 if never), so that a chunk announced in time
-// costs no wait.  A wait that gives up (any wait, with a limit of 0), or a
-// writer on another XCD, sets the workgroup's abort flag.
+// costs no load.  A wait that gives up (any wait, with a limit of 0), or a
+// writer on another XCD, sets the workgroup's abort flag; once it is set,
+// every later wait returns at once.
 __device__ __forceinline__ void wait_chunk(const int* flag, int c, int xcc, int limit, int seen, int* abort_flag) {
   if (__hip_atomic_load(abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) return;
   int v = __builtin_amdgcn_readfirstlane(seen);
@@ -800,201 +784,201 @@ __device__ __forceinline__ void wait_chunk(const int* flag, int c, int xcc, int 
   __hip_atomic_store(abort_flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// K and Qt of a chunk: 16 fragments of 1 KiB, a lane's 16 bytes of each.
-struct KQShare {
-  bf16x8 f[16];
-};
-
-// Staging wave j: chunks j, j + 2, ... into entry j, each read into
-// registers as soon as the previous one is stored.  A chunk is read only
-// after its announcement: an early read would leave stale lines in this CU's
-// L1 for the real read to hit.  The stagers alone poll the flags and pass on
-// what they see through `seen`, so the chain waves wait on LDS only.
-__device__ __forceinline__ void kq_stager(ChainSmemKQ& sm, const FusedArgs& a, int s, int j, int l, int xcc) {
-  const int n = a.nchunks;
-  const int* fl = a.flags + int64_t(s) * a.nflag;
-  const uint16_t* blocks = a.blocks + int64_t(s) * n * kBlockElems + l * 8;
-  int ahead = j < n ? __hip_atomic_load(&fl[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
-  for (int c = j, k = 0; c < n; c += 2, ++k) {
-    wait_chunk(&fl[c], c, xcc, a.spin_limit, ahead, &sm.abort_flag);
-    signal_add(&sm.seen[j], l);                            // the chain waves may now read its tiles
-    KQShare r;
-    const uint16_t* blk = blocks + int64_t(c) * kBlockElems;
-#pragma unroll
-    for (int f = 0; f < 16; ++f) r.f[f] = load_frag(blk + f * 512);
-    if (c + 2 < n) ahead = __hip_atomic_load(&fl[c + 2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // entry j is free once both chain waves have read its previous chunk
-    wait_at_least(&sm.freed[j], 2 * k, &sm.abort_flag, a.spin_limit);
-#pragma unroll
-    for (int f = 0; f < 16; ++f) store_frag(&sm.kq[j][f * 512 + l * 8], r.f[f]);
-    signal_add(&sm.ready[j], l);
-  }
+// A workgroup barrier that orders LDS only: outstanding global loads and
+// stores stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// This wave's H and Ot tiles of a chunk and its decay.
-struct TileShare {
-  uint2 h0, h1, h2, h3, o0, o1, o2, o3;
+// Chain workgroups of a sequence: value columns evolve independently, so
+// the sequence's state is split into column halves, one workgroup each.  In
+// half p, wave w holds rows 16 w .. 16 w + 15 of columns 32 p .. 32 p + 31 in
+// MFMA result registers (S[i]: lane holds S[16w+4g+r][16(2p+i)+c16]).  Per
+// chunk it needs only its share of the block (K and Qt fragments of row block
+// w, H and Ot tiles of row or token block w in its columns), read straight
+// from L2 one chunk ahead.  The bf16 state that every row block multiplies is
+// exchanged through LDS, double-buffered, one barrier a chunk: column j of the
+// half is a row of kSRow bf16 with key 32 m + 16 h + 4 g + r at position
+// 32 m + 8 g + 4 h + r, so that one 16-byte read is a result-compatible
+// fragment (the order frag_acc gives).
+constexpr int kSRow = 72;              // 64 keys + 8 of padding (16-byte reads conflict-free)
+constexpr int kHalfCols = 32;
+
+struct ChainSmemRow {
+  uint16_t s[2][kHalfCols * kSRow];
+  int abort_flag;
+};
+
+union FusedSmem {
+  WySmem p;
+  ChainSmemRow c;
+};
+
+// A wave's share of one chunk's block, and the chunk's decay.
+struct RowTiles {
+  bf16x8 k0, k1, q0, q1;               // K and Qt fragments (row block w, m = 0, 1)
+  uint2 h0, h1;                        // H tiles (column blocks 2p, 2p + 1; row block w)
+  uint2 o0, o1;                        // Ot tiles (column blocks 2p, 2p + 1; token block w)
   float e63;
 };
-__device__ __forceinline__ TileShare load_tiles(const uint16_t* blk, const float* e63, int cb, int l) {
-  TileShare r;
-  const uint2* h = reinterpret_cast<const uint2*>(blk + kOutH + (cb * 4 * 64 + l) * 4);
-  const uint2* o = reinterpret_cast<const uint2*>(blk + kOutOt + (cb * 4 * 64 + l) * 4);
-  r.h0 = h[0];
-  r.h1 = h[64];
-  r.h2 = h[128];
-  r.h3 = h[192];
-  r.o0 = o[0];
-  r.o1 = o[64];
-  r.o2 = o[128];
-  r.o3 = o[192];
+// Loads at a uniform base plus a 32-bit per-lane byte offset (one address
+// register per lane, the base in scalar registers).
+template <class V>
+__device__ __forceinline__ V load_at(const char* base, uint32_t off) {
+  return *reinterpret_cast<const V*>(base + off);
+}
+// blk: the chunk's block; lf = 2 fslot(w, 0, l) and lh = 8 ((8p + w) 64 + l),
+// the lane's byte offsets of its first K fragment and first H tile (tile
+// (cb, w) of H and of Ot sits at element ((cb * 4 + w) * 64 + l) * 4).
+__device__ __forceinline__ RowTiles load_row_tiles(const uint16_t* blk, const float* e63, uint32_t lf, uint32_t lh) {
+  const char* b = reinterpret_cast<const char*>(blk);
+  RowTiles r;
+  r.k0 = load_at<bf16x8>(b + 2 * kOutK, lf);
+  r.k1 = load_at<bf16x8>(b + 2 * kOutK + 1024, lf);
+  r.q0 = load_at<bf16x8>(b + 2 * kOutQt, lf);
+  r.q1 = load_at<bf16x8>(b + 2 * kOutQt + 1024, lf);
+  r.h0 = load_at<uint2>(b + 2 * kOutH, lh);
+  r.h1 = load_at<uint2>(b + 2 * kOutH + 2048, lh);
+  r.o0 = load_at<uint2>(b + 2 * kOutOt, lh);
+  r.o1 = load_at<uint2>(b + 2 * kOutOt + 2048, lh);
   r.e63 = __hip_atomic_load(e63, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return r;
 }
 
-// What a chain wave carries from chunk to chunk.
-struct ChainCtx {
+// What a chain wave carries from chunk to chunk besides its state and tiles.
+struct RowCtx {
+  const int* fl;                       // the sequence's flags
   const uint16_t* blocks;              // the sequence's blocks
   const float* e63;                    // the sequence's decays
   bf16_t* o;                           // the sequence's outputs
-  int cb, l;
+  uint32_t lf, lh, lo;                 // lane byte offsets: K fragment, H tile, output row
+  int p, w, l, xcc, ahead;             // ahead: flag of the next chunk, as read one step earlier
 };
 
-// One chunk of a chain wave: S <- e^{g_63} S + K S + H and O = Qt S + Ot, with
-// the operand roundings of the two-launch chain.  `cur` holds this chunk's H
-// and Ot tiles; the next chunk's are read into `nxt` once it is announced, so
-// their latency hides behind this chunk's work.  Every chunk but the last
-// (kLast) issues the same loads and stores on every path, and the caller
-// alternates two tile sets rather than copying one into the other: the
-// compiler then waits for exactly the loads a step uses, never for the
-// previous chunk's output stores.
-template <bool kLast>
-__device__ __forceinline__ void chain_step(ChainSmemKQ& sm, const FusedArgs& a, ChainCtx& x, int c,
-                                           const TileShare& cur, TileShare& nxt, f32x4 (&S)[4], bf16x8& sb0,
-                                           bf16x8& sb1) {
-  const int l = x.l;
-  if constexpr (!kLast) {
-    wait_at_least(&sm.seen[(c + 1) & 1], ((c + 1) >> 1) + 1, &sm.abort_flag, a.spin_limit);
-    nxt = load_tiles(x.blocks + int64_t(c + 1) * kBlockElems, x.e63 + c + 1, x.cb, l);
-  }
-  const int j = c & 1;
-  wait_at_least(&sm.ready[j], (c >> 1) + 1, &sm.abort_flag, a.spin_limit);
-  const uint16_t* D = sm.kq[j];
-  // O^T tiles from the state at the chunk's start: S^T Qt^T + Ot^T; lane
-  // holds o[c*64+16ib+c16][16cb+4g+r]
+// One chunk of a chain wave: O = Qt S + Ot for token block w and
+// S <- e^{g_63} S + K S + H for row block w, with the operand roundings of the
+// two-launch chain, then the new state's bf16 rows into the other LDS buffer.
+// `cur` holds this chunk's tiles.  A read of a just-written block takes about
+// a microsecond, several chunks' worth of chain work, so tiles are read two
+// chunks ahead, into `dst` (the set of the chunk before this one), once that
+// chunk is announced; near the end the last chunk is read again instead (it
+// is announced, so the read is harmless).  Output rows go through a buffer
+// descriptor that ends at row T, so rows past T are dropped by the hardware.
+// Every step thus issues the same loads and stores, and the caller rotates
+// three tile sets rather than copying them: the compiler then waits for
+// exactly the loads a step uses, never for earlier output stores.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void chain_row_step(ChainSmemRow& sm, const FusedArgs& a, RowCtx& x, int c,
+                                               const RowTiles& cur, RowTiles& dst, f32x4 (&S)[2]) {
+  const int n = a.nchunks, l = x.l, w = x.w;
   const int g = l >> 4, c16 = l & 15;
-  const uint2 oc[4] = {cur.o0, cur.o1, cur.o2, cur.o3};
-#pragma unroll
-  for (int ib = 0; ib < 4; ++ib) {
-    const bf16x8 q0 = load_frag(&D[kOutQt + fslot(ib, 0, l)]);
-    const bf16x8 q1 = load_frag(&D[kOutQt + fslot(ib, 1, l)]);
-    f32x4 acc = mfma32(sb0, q0, unpack_half(oc[ib]));
-    acc = mfma32(sb1, q1, acc);
-    const int tok = c * kC + 16 * ib + c16;
-    if (!kLast || tok < a.T)
-      *reinterpret_cast<uint2*>(x.o + int64_t(tok) * kD + 16 * x.cb + 4 * g) =
-          make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
-  }
-  // S <- e^{g_63} S + K S + H
+  const int ca = c + 2 < n ? c + 2 : n - 1;
+  wait_chunk(&x.fl[ca], ca, x.xcc, a.spin_limit, x.ahead, &sm.abort_flag);
+  // the next flag before the tiles: loads complete in order, so the next
+  // step's look at the flag then waits for nothing issued after it
+  x.ahead = __hip_atomic_load(&x.fl[c + 3 < n ? c + 3 : n - 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  dst = load_row_tiles(x.blocks + int64_t(ca) * kBlockElems, x.e63 + ca, x.lf, x.lh);
+  const uint16_t* Sb = sm.s[c & 1];
+  uint16_t* Sn = sm.s[(c + 1) & 1];
   const float ec = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(cur.e63)));
-  const uint2 hc[4] = {cur.h0, cur.h1, cur.h2, cur.h3};
+  const uint2 hc[2] = {cur.h0, cur.h1};
+  const uint2 oc[2] = {cur.o0, cur.o1};
+  const int rows = a.T - c * kC < kC ? a.T - c * kC : kC;
+  const __amdgpu_buffer_rsrc_t orow =
+      __builtin_amdgcn_make_buffer_rsrc(x.o + int64_t(c) * kC * kD, 0, rows * kD * 2, 0x00020000);
 #pragma unroll
-  for (int fb = 0; fb < 4; ++fb) {
-    const bf16x8 k0 = load_frag(&D[kOutK + fslot(fb, 0, l)]);
-    const bf16x8 k1 = load_frag(&D[kOutK + fslot(fb, 1, l)]);
-    f32x4 acc = S[fb] * ec + unpack_half(hc[fb]);
-    acc = mfma32(k0, sb0, acc);
-    S[fb] = mfma32(k1, sb1, acc);
+  for (int i = 0; i < 2; ++i) {
+    const uint16_t* col = Sb + (16 * i + c16) * kSRow + 8 * g;
+    const bf16x8 f0 = load_frag(col);                      // keys 0..31 of column 16cb+c16
+    const bf16x8 f1 = load_frag(col + 32);                 // keys 32..63
+    // O^T tile: S^T Qt^T + Ot^T; lane holds o[c*64+16w+c16][16cb+4g+r]
+    f32x4 ov = mfma32(f0, cur.q0, unpack_half(oc[i]));
+    ov = mfma32(f1, cur.q1, ov);
+    const u32x2 ob = {pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3])};
+    __builtin_amdgcn_raw_buffer_store_b64(ob, orow, x.lo + 32 * i, 0, 0);
+    // S <- e^{g_63} S + K S + H
+    f32x4 acc = S[i] * ec + unpack_half(hc[i]);
+    acc = mfma32(cur.k0, f0, acc);
+    S[i] = mfma32(cur.k1, f1, acc);
+    *reinterpret_cast<uint2*>(Sn + (16 * i + c16) * kSRow + 32 * (w >> 1) + 8 * g + 4 * (w & 1)) =
+        make_uint2(pack_bf16x2(S[i][0], S[i][1]), pack_bf16x2(S[i][2], S[i][3]));
   }
-  signal_add(&sm.freed[j], l);                             // (its fence waits for the reads above)
-  sb0 = frag_acc(S[0], S[1]);
-  sb1 = frag_acc(S[2], S[3]);
+  lds_barrier();
 }
 
-// Chain wave cw: the state of value columns 16 cb .. 16 cb + 15 in MFMA result
-// registers.  Its H and Ot tiles come straight from L2, K and Qt from the
-// staged LDS entry.  The first chunk is peeled off the loop so that the loop
-// is entered with the loads and stores in flight that its back edge has.
-__device__ __forceinline__ void kq_chain(ChainSmemKQ& sm, const FusedArgs& a, int s, int part, int cw, int l) {
+__device__ __forceinline__ void chain_workgroup(ChainSmemRow& sm, const FusedArgs& a, int s, int p) {
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
   const int g = l >> 4, c16 = l & 15;
   const int n = a.nchunks;
-  ChainCtx x;
+  if (tid == 0) sm.abort_flag = 0;
+  RowCtx x;
+  x.fl = a.flags + int64_t(s) * a.nflag;
   x.blocks = a.blocks + int64_t(s) * n * kBlockElems;
   x.e63 = a.decay63 + int64_t(s) * n;
   x.o = a.o + int64_t(s) * a.T * kD;
-  x.cb = part * 2 + cw;
+  x.p = p;
+  x.w = w;
   x.l = l;
-  f32x4 S[4];                                              // S[fb]: lane holds S[16fb+4g+r][16cb+c16]
-  const float* S0 = a.S0 ? a.S0 + int64_t(s) * kD * kD + 16 * x.cb + c16 : nullptr;
+  x.xcc = xcc_id();
+  x.lf = uint32_t(2 * fslot(w, 0, l));
+  x.lh = uint32_t(8 * ((8 * p + w) * 64 + l));
+  x.lo = uint32_t(2 * ((16 * w + c16) * kD + 32 * p + 4 * g));   // o[16w+c16][32p+4g], within a chunk
+  f32x4 S[2];
+  const float* S0 = a.S0 ? a.S0 + int64_t(s) * kD * kD + (16 * w + 4 * g) * kD + 32 * p + c16 : nullptr;
 #pragma unroll
-  for (int fb = 0; fb < 4; ++fb) {
-    S[fb] = zero4();
+  for (int i = 0; i < 2; ++i) {
+    S[i] = zero4();
     if (S0) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) S[fb][r] = S0[(16 * fb + 4 * g + r) * kD];
+      for (int r = 0; r < 4; ++r) S[i][r] = S0[r * kD + 16 * i];
     }
+    *reinterpret_cast<uint2*>(sm.s[0] + (16 * i + c16) * kSRow + 32 * (w >> 1) + 8 * g + 4 * (w & 1)) =
+        make_uint2(pack_bf16x2(S[i][0], S[i][1]), pack_bf16x2(S[i][2], S[i][3]));
   }
-  bf16x8 sb0 = frag_acc(S[0], S[1]);
-  bf16x8 sb1 = frag_acc(S[2], S[3]);
-  wait_at_least(&sm.seen[0], 1, &sm.abort_flag, a.spin_limit);
-  TileShare ta = load_tiles(x.blocks, x.e63, x.cb, l);
-  TileShare tb{};
-  if (n == 1) {
-    chain_step<true>(sm, a, x, 0, ta, tb, S, sb0, sb1);
-  } else {
-    chain_step<false>(sm, a, x, 0, ta, tb, S, sb0, sb1);
-    int c = 1;
-    for (; c + 2 < n; c += 2) {
-      chain_step<false>(sm, a, x, c, tb, ta, S, sb0, sb1);
-      chain_step<false>(sm, a, x, c + 1, ta, tb, S, sb0, sb1);
-    }
-    if (c + 1 < n) {
-      chain_step<false>(sm, a, x, c, tb, ta, S, sb0, sb1);
-      chain_step<true>(sm, a, x, c + 1, ta, tb, S, sb0, sb1);
-    } else {
-      chain_step<true>(sm, a, x, c, tb, ta, S, sb0, sb1);
-    }
+  __syncthreads();
+  // Tiles of chunks 0 and 1 with the flag of chunk 2 between them, then two
+  // flag loads (values unused): the loop is entered with the loads in flight
+  // after that flag that its back edge has (a set of tiles and two output
+  // stores), so the compiler's wait for the flag at the loop head leaves
+  // them in flight.
+  const int c1 = n > 1 ? 1 : 0;
+  wait_chunk(&x.fl[0], 0, x.xcc, a.spin_limit, 0, &sm.abort_flag);
+  RowTiles t0 = load_row_tiles(x.blocks, x.e63, x.lf, x.lh);
+  wait_chunk(&x.fl[c1], c1, x.xcc, a.spin_limit, 0, &sm.abort_flag);
+  x.ahead = __hip_atomic_load(&x.fl[n > 2 ? 2 : n - 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  RowTiles t1 = load_row_tiles(x.blocks + int64_t(c1) * kBlockElems, x.e63 + c1, x.lf, x.lh);
+  RowTiles t2;
+  int pad = __hip_atomic_load(&x.fl[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  pad |= __hip_atomic_load(&x.fl[c1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // tile set of chunk c is t(c mod 3)
+  int c = 0;
+  for (; c + 3 <= n; c += 3) {
+    chain_row_step(sm, a, x, c, t0, t2, S);
+    chain_row_step(sm, a, x, c + 1, t1, t0, S);
+    chain_row_step(sm, a, x, c + 2, t2, t1, S);
+  }
+  if (c < n) chain_row_step(sm, a, x, c, t0, t2, S);
+  if (c + 1 < n) chain_row_step(sm, a, x, c + 1, t1, t0, S);
+  if (pad == -1) sm.abort_flag = 2;                        // never: flags are never -1; keeps the loads
+  // A wait that gave up anywhere in the workgroup poisons the sequence: its
+  // outputs and final state are NaN.
+  __syncthreads();
+  const bool bad = __hip_atomic_load(&sm.abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0;
+  if (bad) {
+    const uint32_t nan2 = 0x7fc07fc0u;                     // two bf16 NaNs
+    uint4* o4 = reinterpret_cast<uint4*>(x.o);
+    for (int64_t i = tid; i < int64_t(a.T) * 4; i += 256) o4[(i >> 2) * 8 + 4 * p + (i & 3)] = make_uint4(nan2, nan2, nan2, nan2);
   }
   if (a.S_T) {
+    float* st = a.S_T + int64_t(s) * kD * kD + (16 * w + 4 * g) * kD + 32 * p + c16;
 #pragma unroll
-    for (int fb = 0; fb < 4; ++fb)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        a.S_T[(int64_t(s) * kD + 16 * fb + 4 * g + r) * kD + 16 * x.cb + c16] = S[fb][r];
-  }
-}
-
-__device__ __forceinline__ void chain_workgroup(ChainSmemKQ& sm, const FusedArgs& a, int s, int part) {
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
-  if (tid < 2) {
-    sm.ready[tid] = 0;
-    sm.freed[tid] = 0;
-    sm.seen[tid] = 0;
-  }
-  if (tid == 0) sm.abort_flag = 0;
-  __syncthreads();
-  const int xcc = xcc_id();
-  if (wave >= 2) kq_stager(sm, a, s, wave - 2, l, xcc);
-  else kq_chain(sm, a, s, part, wave, l);
-  // Every wave gets here.  A wait that gave up anywhere in the workgroup
-  // poisons this half of the sequence: its outputs and final state are NaN.
-  __syncthreads();
-  if (wave < 2 && __hip_atomic_load(&sm.abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0) {
-    const int cb = part * 2 + wave;
-    const uint16_t nan_bits = 0x7fc0;
-    const uint32_t nan2 = uint32_t(nan_bits) | (uint32_t(nan_bits) << 16);
-    bf16_t* o_s = a.o + int64_t(s) * a.T * kD;
-    for (int tok = l >> 1; tok < a.T; tok += 32)
-      *reinterpret_cast<uint4*>(o_s + int64_t(tok) * kD + 16 * cb + 8 * (l & 1)) = make_uint4(nan2, nan2, nan2, nan2);
-    if (a.S_T) {
-      const int g = l >> 4, c16 = l & 15;
-#pragma unroll
-      for (int fb = 0; fb < 4; ++fb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          a.S_T[(int64_t(s) * kD + 16 * fb + 4 * g + r) * kD + 16 * cb + c16] = __builtin_nanf("");
-    }
+      for (int r = 0; r < 4; ++r) st[r * kD + 16 * i] = bad ? __builtin_nanf("") : S[i][r];
   }
 }
 
@@ -1002,8 +986,8 @@ __global__ void __launch_bounds__(256, 4) falcon1_fused_kernel(FusedArgs a) {
   __shared__ FusedSmem sm;
   const int b = blockIdx.x;
   if (b < 2 * a.BHpad) {
-    const int s = b % a.BHpad, part = b / a.BHpad;
-    if (s < a.BH) chain_workgroup(sm.c, a, s, part);
+    const int s = b % a.BHpad;
+    if (s < a.BH) chain_workgroup(sm.c, a, s, b / a.BHpad);
     return;
   }
   const int j = b - 2 * a.BHpad;
