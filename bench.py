@@ -26,9 +26,10 @@ WORKLOAD = "f1_chunked_8x12x2048_d64"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 FP32_MFMA_PEAK_TFLOPS = 157.3   # MI355X dense fp32 MFMA, published
-# The headline step runs two launches: the chunk-parallel chunk matrices and
-# the per-sequence chain (state passing and outputs).
-STEP_KERNELS = ["falcon1_wy_kernel", "falcon1_chain_kernel"]
+# The headline step runs two launches: a fill of the hand-over flags, then one
+# kernel whose chunk workgroups build the chunk matrices while per-sequence
+# chain workgroups carry the state and write the outputs.
+STEP_KERNELS = ["zero_ints_kernel", "falcon1_fused_kernel"]
 # rocprofv3 counter summaries under profiles/ (<name>_counters.md), each valid
 # while the sources of its kernels hash to the value recorded in it.
 _CSRC = "delta_rule_recurrence_amd/csrc/"
