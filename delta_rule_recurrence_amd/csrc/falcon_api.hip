@@ -15,6 +15,8 @@ namespace {
 
 // Polls a bounded wait makes before giving up (falcon_set_wait_limit).
 std::atomic<int32_t> g_wait_limit{falcon::kDefaultSpinLimit};
+// Form of the Falcon-1 bf16 chunked fast path (falcon_set_f1_launch_form).
+std::atomic<int32_t> g_f1_form{FALCON_F1_ONE_LAUNCH};
 
 using falcon::DecodeArgs;
 using falcon::ProblemArgs;
@@ -97,6 +99,7 @@ falcon_status check_forward(const falcon_problem* p, const void* phi_k, const vo
   out->phi_k = phi_k; out->phi_q = phi_q; out->v = v; out->beta = beta; out->lam = lam;
   out->S0 = S0; out->k_prev = k_prev; out->o = o; out->S_T = S_T;
   out->spin_limit = g_wait_limit.load(std::memory_order_relaxed);
+  out->f1_form = g_f1_form.load(std::memory_order_relaxed);
   return FALCON_OK;
 }
 
@@ -229,6 +232,11 @@ int32_t falcon_abi_version(void) { return FALCON_ABI_VERSION; }
 int32_t falcon_set_wait_limit(int32_t polls) {
   if (polls < 0) return -1;
   return g_wait_limit.exchange(polls, std::memory_order_relaxed);
+}
+
+int32_t falcon_set_f1_launch_form(int32_t form) {
+  if (form != FALCON_F1_ONE_LAUNCH && form != FALCON_F1_TWO_LAUNCH) return -1;
+  return g_f1_form.exchange(form, std::memory_order_relaxed);
 }
 
 const char* falcon_status_string(int32_t s) {

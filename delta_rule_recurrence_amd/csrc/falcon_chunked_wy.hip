@@ -1004,14 +1004,6 @@ __global__ void zero_ints_kernel(int* p, int n) {
   if (i < n) p[i] = 0;
 }
 
-bool use_two_launch_form() {
-  static const bool v = [] {
-    const char* e = getenv("FALCON_F1_TWO_LAUNCH");
-    return e && e[0] == '1';
-  }();
-  return v;
-}
-
 }  // namespace
 
 bool chunked_wy_applies(const ProblemArgs& a) {
@@ -1045,7 +1037,7 @@ hipError_t launch_chunked_wy(const ProblemArgs& a, hipStream_t st) {
   int* flags = reinterpret_cast<int*>(ws);
   float* decay63 = reinterpret_cast<float*>(ws + L.flags_bytes);
   uint16_t* blocks = reinterpret_cast<uint16_t*>(ws + L.flags_bytes + L.e63_bytes);
-  if (use_two_launch_form()) {
+  if (a.f1_form == 1) {
     hipLaunchKernelGGL(falcon1_wy_kernel, dim3(unsigned(BH * nchunks)), dim3(256), 0, st,
                        static_cast<const bf16_t*>(a.phi_k), static_cast<const bf16_t*>(a.phi_q),
                        static_cast<const bf16_t*>(a.v), a.beta, a.lam, static_cast<const bf16_t*>(a.k_prev),

@@ -26,6 +26,7 @@ struct ProblemArgs {
   void* workspace;
   size_t workspace_bytes;
   int spin_limit;        // polls before a bounded wait between waves gives up
+  int f1_form;           // Falcon-1 bf16 fast path: 0 one launch, 1 two launches
 };
 
 // Default number of polls of a bounded wait (each poll sleeps ~64 cycles):

@@ -34,6 +34,7 @@ _P = ctypes.c_void_p
 _SIGNATURES = {
     "falcon_abi_version": (ctypes.c_int32, []),
     "falcon_set_wait_limit": (ctypes.c_int32, [ctypes.c_int32]),
+    "falcon_set_f1_launch_form": (ctypes.c_int32, [ctypes.c_int32]),
     "falcon_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
     "falcon_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(FalconProblem), ctypes.c_int32]),
     "falcon_fwd_recurrent": (ctypes.c_int32, [ctypes.POINTER(FalconProblem), _P, _P, _P, _P, _P,
@@ -88,6 +89,20 @@ def falcon_set_wait_limit(polls: int) -> int:
     prev = int(load_library().falcon_set_wait_limit(int(polls)))
     if prev < 0:
         raise ValueError("the wait limit must be >= 0")
+    return prev
+
+
+F1_ONE_LAUNCH = 0
+F1_TWO_LAUNCH = 1
+
+
+def falcon_set_f1_launch_form(form: int) -> int:
+    """How the Falcon-1 bf16 chunked fast path runs: F1_ONE_LAUNCH (default)
+    or F1_TWO_LAUNCH; returns the previous form (see
+    ``falcon_set_f1_launch_form`` in falcon.h)."""
+    prev = int(load_library().falcon_set_f1_launch_form(int(form)))
+    if prev < 0:
+        raise ValueError("form must be F1_ONE_LAUNCH or F1_TWO_LAUNCH")
     return prev
 
 

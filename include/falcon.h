@@ -33,9 +33,10 @@
  *  - Calls are asynchronous and stream-ordered on `stream` (a hipStream_t;
  *    NULL means the legacy default stream).  The library never synchronises
  *    the device, allocates no device memory in these entry points, and keeps
- *    no global mutable state besides the wait limit of falcon_set_wait_limit,
- *    so concurrent calls on different streams are safe as long as their
- *    output buffers and workspaces do not overlap.
+ *    no global mutable state besides two process-wide settings
+ *    (falcon_set_wait_limit, falcon_set_f1_launch_form), so concurrent calls
+ *    on different streams are safe as long as their output buffers and
+ *    workspaces do not overlap.
  *  - Every argument is validated before anything is launched; on error the
  *    call returns a negative falcon_status and touches no memory.
  *  - Launch failures reported by the HIP runtime return FALCON_ERR_HIP.
@@ -110,7 +111,7 @@ int32_t falcon_abi_version(void);
 const char* falcon_status_string(int32_t status);
 
 /*
- * falcon_set_wait_limit -- the one process-wide setting of the library.  Some
+ * falcon_set_wait_limit -- a process-wide setting of the library.  Some
  * kernels hand data between waves or workgroups through flags in memory;
  * every such wait is bounded and gives up after `polls` polls (default
  * 4194304, about 0.1-0.2 s).  A call in which a wait gave up does not hang:
@@ -121,6 +122,25 @@ const char* falcon_status_string(int32_t status);
  * once.  Returns the previous limit, or -1 (nothing changed) for polls < 0.
  */
 int32_t falcon_set_wait_limit(int32_t polls);
+
+/*
+ * falcon_set_f1_launch_form -- the other process-wide setting: how
+ * falcon_fwd_chunked runs its Falcon-1 fast path (bf16 I/O, dk = dv = 64,
+ * C = 64; every other case ignores it).  Both forms compute the same chunk
+ * form with the same roundings and give bit-identical results (paper,
+ * Section 4.2, chunk-parallel implementation; Eq. 3.3 per chunk):
+ *   FALCON_F1_ONE_LAUNCH (default): one kernel in which chunk workgroups
+ *     build the chunk matrices while per-sequence chain workgroups, started
+ *     first, carry the state through announced chunks (plus a small fill of
+ *     the hand-over flags);
+ *   FALCON_F1_TWO_LAUNCH: the chunk matrices of all chunks, then the chains.
+ * The workspace size is the same for both.  Meant for comparison and
+ * debugging; calls made while it changes use either form.  Returns the
+ * previous form, or -1 (nothing changed) for any other value.
+ */
+#define FALCON_F1_ONE_LAUNCH 0
+#define FALCON_F1_TWO_LAUNCH 1
+int32_t falcon_set_f1_launch_form(int32_t form);
 
 /*
  * falcon_fwd_recurrent -- the recurrent form (paper, Section 4.6 and the

@@ -321,6 +321,19 @@ def test_wait_limit_setting(lib):
     assert fb.falcon_set_wait_limit(prev) == prev
 
 
+def test_f1_launch_form_setting(lib):
+    prev = fb.falcon_set_f1_launch_form(fb.F1_TWO_LAUNCH)
+    try:
+        assert prev == fb.F1_ONE_LAUNCH                        # the default
+        assert lib.falcon_set_f1_launch_form(2) == -1          # rejected, unchanged
+        assert lib.falcon_set_f1_launch_form(-1) == -1
+        assert fb.falcon_set_f1_launch_form(fb.F1_ONE_LAUNCH) == fb.F1_TWO_LAUNCH
+        with pytest.raises(ValueError):
+            fb.falcon_set_f1_launch_form(5)
+    finally:
+        fb.falcon_set_f1_launch_form(prev)
+
+
 def test_noalloc_validation(lib):
     def call(p, C=64, **over):
         a = fwd_args(**over)
