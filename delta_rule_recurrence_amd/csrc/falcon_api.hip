@@ -1,6 +1,8 @@
 // C ABI of the Falcon library: argument validation, status codes and
 // dispatch to the kernels.  Nothing here allocates or synchronises.
 #include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -10,6 +12,16 @@
 
 #include "falcon.h"
 #include "falcon_launch.h"
+
+#ifdef FALCON_BOUNDS_CHECK
+namespace falcon {
+void host_check_failed(const char* cond, const char* file, int line) {
+  fprintf(stderr, "falcon bounds check failed: %s (%s:%d)\n", cond, file, line);
+  fflush(stderr);
+  abort();
+}
+}  // namespace falcon
+#endif
 
 namespace {
 

@@ -1,5 +1,5 @@
 // Chunked-forward dispatch for bf16 I/O with dk = dv = 64 and C = 64: the
-// two-launch WY + chain path for Falcon-1, the chunk-tile path for Falcon-1A,
+// chunk matrices and per-sequence chain for Falcon-1, the chunk-tile path for Falcon-1A,
 // the per-column path for Falcon-2 / 2A; the general float32 kernel for every
 // other case.
 #include "falcon_device.h"

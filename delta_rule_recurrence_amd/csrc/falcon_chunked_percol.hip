@@ -28,6 +28,8 @@
 // 16-column slice); the next chunk's rows are fetched into registers while the
 // current one is solved.
 
+#include <vector>
+
 #include "falcon_device.h"
 #include "falcon_launch.h"
 #include "falcon_mfma_frag.h"
@@ -258,6 +260,15 @@ __device__ __forceinline__ void solve_block(PcSmem& sm, int jl, int li, int t0, 
   gcarry = glast;
 }
 
+// Sequence and first value column of workgroup b: the four 16-column slices
+// of a sequence are workgroups b, b + 8, b + 16, b + 24 (consecutive
+// workgroups go to different XCDs, so the slices share one XCD and its L2).
+// Shared by the kernel and the host-side bounds model.
+__host__ __device__ inline void percol_slice(int b, int64_t& bh, int& j0) {
+  bh = int64_t(b / 32) * 8 + b % 8;
+  j0 = ((b / 8) & 3) * kSlice;
+}
+
 template <bool kReg>
 __global__ void __launch_bounds__(kThreads, 2)
 falcon2_chunked_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restrict__ phi_q,
@@ -270,12 +281,11 @@ falcon2_chunked_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restric
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;   // wave-uniform
   const int g = l >> 4, c16 = l & 15;
   const int jl = 4 * w + g, li = c16;                 // solve layout: column jl of the slice, block row li
-  // the four slices of a sequence are workgroups b, b + 8, b + 16, b + 24:
-  // consecutive workgroups go to different XCDs, so these share one XCD and
-  // its L2, and the keys and queries that every slice reads come from HBM once
-  const int b = blockIdx.x;
-  const int64_t bh = int64_t(b / 32) * 8 + b % 8;
-  const int j0 = ((b / 8) & 3) * kSlice;
+  // the slices of a sequence share one XCD, so the keys and queries that
+  // every slice reads come from HBM once
+  int64_t bh;
+  int j0;
+  percol_slice(blockIdx.x, bh, j0);
   if (bh >= BH) return;
   const bool fresh = (k_prev == nullptr);
   const bf16_t* K = phi_k + bh * T * kD;
@@ -408,7 +418,22 @@ bool chunked_percol_applies(const ProblemArgs& a) {
 
 hipError_t launch_chunked_percol(const ProblemArgs& a, hipStream_t st) {
   const int64_t BH = int64_t(a.B) * a.H;
-  const dim3 grid(unsigned((BH + 7) / 8 * 8 * (kD / kSlice)));
+  const int64_t nwg = (BH + 7) / 8 * 8 * (kD / kSlice);
+  if (kBoundsCheck) {
+    // every (sequence, slice) exactly once, the slices of a sequence on one XCD
+    FALCON_HOST_CHECK(nwg <= INT32_MAX);
+    std::vector<int> seen(size_t(BH) * (kD / kSlice), 0);
+    for (int64_t b = 0; b < nwg; ++b) {
+      int64_t bh;
+      int j0;
+      percol_slice(int(b), bh, j0);
+      FALCON_HOST_CHECK(bh >= 0 && j0 >= 0 && j0 + kSlice <= kD && j0 % kSlice == 0);
+      FALCON_HOST_CHECK(b % 8 == bh % 8);
+      if (bh < BH) ++seen[size_t(bh) * (kD / kSlice) + j0 / kSlice];
+    }
+    for (int v : seen) FALCON_HOST_CHECK(v == 1);
+  }
+  const dim3 grid{unsigned(nwg)};
   if (a.variant == kF2)
     hipLaunchKernelGGL(falcon2_chunked_kernel<true>, grid, dim3(kThreads), 0, st,
                        static_cast<const bf16_t*>(a.phi_k), static_cast<const bf16_t*>(a.phi_q),

@@ -364,6 +364,14 @@ hipError_t launch_chunked_scan(const ProblemArgs& a, hipStream_t st) {
   const int64_t ntiles = BH * nts;
   if (ntiles == 0) return hipSuccess;
   const ScanLayout L(ntiles);
+  // the tiles of a sequence cover its chunks exactly; the grids and the
+  // workspace hold every tile
+  FALCON_HOST_CHECK(ntiles <= INT32_MAX && BH * 4 <= INT32_MAX);
+  FALCON_HOST_CHECK(a.workspace_bytes >= L.total);
+  FALCON_HOST_CHECK((nts - 1) * kTileChunks < (int64_t(a.T) + kC - 1) / kC &&
+                    nts * kTileChunks >= (int64_t(a.T) + kC - 1) / kC);
+  FALCON_HOST_CHECK(L.off_start >= size_t(ntiles) * kStateFloats * 4 && L.off_logd >= 2 * L.off_start &&
+                    L.total >= L.off_logd + 4 * size_t(ntiles));
   char* base = static_cast<char*>(a.workspace);
   ScanWorkspace ws;
   ws.agg = reinterpret_cast<float*>(base);

@@ -1,5 +1,5 @@
-// Chunked Falcon-1 forward in two launches (gfx950, bf16 I/O, dk = dv = 64,
-// chunk C = 64).
+// Chunked Falcon-1 forward (gfx950, bf16 I/O, dk = dv = 64, chunk C = 64),
+// in one launch by default or in two.
 //
 // The chunk form (the log-space renormalisation of Section 4.4 with window 1,
 // applied per chunk; g_i the chunk-local prefix of log gamma):
@@ -12,14 +12,20 @@
 // products that carry S through the chunk.  Substituting R:
 //   S' = e^{g_63} S + K S + H,   K = -Xh^T W,   H = Xh^T U
 //   O  = Qt S + Ot,              Qt = Diag(e^g) Q - M W,   Ot = M U.
-// Launch 1 builds K, H, Qt and Ot for every chunk of every sequence at once
-// (one workgroup per chunk, the whole chip busy) and writes them to the
-// workspace in MFMA operand order.  Launch 2 runs the short sequential part:
-// per chunk, one 64x64x64 product for the state and one for the outputs,
-// streaming the chunk matrices back.  The state is rounded to bf16 only as
-// the operand of K S and Qt S; its decay term stays in float32.
+// Chunk workgroups build K, H, Qt and Ot for every chunk of every sequence at
+// once (one workgroup per chunk) and write them to the workspace in MFMA
+// operand order.  The short sequential part runs per sequence: per chunk, one
+// 64x64x64 product for the state and one for the outputs, reading the chunk
+// matrices back.  In the one-launch form (the default) chain workgroups run
+// beside the chunk workgroups and take each chunk as soon as it is announced;
+// in the two-launch form all chunk matrices come first.  The state is rounded
+// to bf16 only as the operand of K S and Qt S; its decay term stays in
+// float32.
 
+#include <stdint.h>
 #include <stdlib.h>
+
+#include <vector>
 
 #include "falcon_device.h"
 #include "falcon_launch.h"
@@ -205,7 +211,7 @@ __device__ __forceinline__ void build_inverse(WySmem& sm, int l) {
 }
 
 // Fragment slot [b][m] of a 64x64 fragment array.
-__device__ __forceinline__ int fslot(int b, int m, int l) { return ((b * 2 + m) * 64 + l) * 8; }
+__host__ __device__ inline int fslot(int b, int m, int l) { return ((b * 2 + m) * 64 + l) * 8; }
 
 __device__ __forceinline__ bf16x8 ldg_frag(const bf16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
@@ -714,6 +720,30 @@ falcon1_chain_kernel(const float* S0, const uint16_t* __restrict__ blocks, const
 
 constexpr int kTagMask = 0xffffff;
 
+// Role of workgroup b of the one-launch grid: the two chain workgroups of
+// sequence s (value-column half `part`) come first, then chunk c of sequence
+// s.  Shared by the kernel and the host-side bounds model.
+struct FusedRole {
+  bool chain;
+  int s, part, c;
+};
+__host__ __device__ inline FusedRole fused_role(int b, int BHpad) {
+  FusedRole r;
+  r.chain = b < 2 * BHpad;
+  const int j = r.chain ? b : b - 2 * BHpad;
+  r.s = j % BHpad;
+  r.part = r.chain ? j / BHpad : 0;
+  r.c = r.chain ? 0 : j / BHpad;
+  return r;
+}
+// A chain wave's per-lane byte offsets: its first K fragment in a block, its
+// first H (and Ot) tile in a block, its output row within a chunk.
+__host__ __device__ inline uint32_t chain_lf(int w, int l) { return uint32_t(2 * fslot(w, 0, l)); }
+__host__ __device__ inline uint32_t chain_lh(int p, int w, int l) { return uint32_t(8 * ((8 * p + w) * 64 + l)); }
+__host__ __device__ inline uint32_t chain_lo(int p, int w, int l) {
+  return uint32_t(2 * ((16 * w + (l & 15)) * 64 + 32 * p + 4 * (l >> 4)));
+}
+
 struct FusedArgs {
   const bf16_t* phi_k;
   const bf16_t* phi_q;
@@ -924,9 +954,9 @@ __device__ __forceinline__ void chain_workgroup(ChainSmemRow& sm, const FusedArg
   x.w = w;
   x.l = l;
   x.xcc = xcc_id();
-  x.lf = uint32_t(2 * fslot(w, 0, l));
-  x.lh = uint32_t(8 * ((8 * p + w) * 64 + l));
-  x.lo = uint32_t(2 * ((16 * w + c16) * kD + 32 * p + 4 * g));   // o[16w+c16][32p+4g], within a chunk
+  x.lf = chain_lf(w, l);
+  x.lh = chain_lh(p, w, l);
+  x.lo = chain_lo(p, w, l);                                // o[16w+c16][32p+4g], within a chunk
   f32x4 S[2];
   const float* S0 = a.S0 ? a.S0 + int64_t(s) * kD * kD + (16 * w + 4 * g) * kD + 32 * p + c16 : nullptr;
 #pragma unroll
@@ -984,15 +1014,13 @@ __device__ __forceinline__ void chain_workgroup(ChainSmemRow& sm, const FusedArg
 
 __global__ void __launch_bounds__(256, 4) falcon1_fused_kernel(FusedArgs a) {
   __shared__ FusedSmem sm;
-  const int b = blockIdx.x;
-  if (b < 2 * a.BHpad) {
-    const int s = b % a.BHpad;
-    if (s < a.BH) chain_workgroup(sm.c, a, s, b / a.BHpad);
+  const FusedRole r = fused_role(blockIdx.x, a.BHpad);
+  if (r.s >= a.BH) return;
+  if (r.chain) {
+    chain_workgroup(sm.c, a, r.s, r.part);
     return;
   }
-  const int j = b - 2 * a.BHpad;
-  const int s = j % a.BHpad, c = j / a.BHpad;
-  if (s >= a.BH) return;
+  const int s = r.s, c = r.c;
   const int64_t q = int64_t(s) * a.nchunks + c;
   FlagOut out{a.blocks + q * kBlockElems, a.decay63 + q, a.flags + int64_t(s) * a.nflag + c,
               (xcc_id() << 24) | ((c + 1) & kTagMask)};
@@ -1028,6 +1056,57 @@ size_t chunked_wy_workspace_bytes(const ProblemArgs& a) {
   return size_t(WyLayout(int64_t(a.B) * a.H, (int64_t(a.T) + kC - 1) / kC).total);
 }
 
+// The one-launch grid against the workspace layout and the buffers, on the
+// host (bounds-check builds): every workgroup's role and XCD, the block,
+// decay and flag each chunk workgroup writes (each exactly once), the chunks
+// and output rows each chain reads and writes, and a chain lane's reads within
+// a block.
+void check_fused_grid(const ProblemArgs& a, const WyLayout& L, int nchunks) {
+  const int64_t BH = int64_t(a.B) * a.H;
+  const int64_t grid = L.BHpad * (int64_t(nchunks) + 2);
+  FALCON_HOST_CHECK(grid <= INT32_MAX);
+  FALCON_HOST_CHECK(L.BHpad % 8 == 0 && L.BHpad >= BH && L.BHpad < BH + 8);
+  FALCON_HOST_CHECK(L.nflag >= nchunks && L.nflag % 64 == 0);
+  FALCON_HOST_CHECK(int64_t(a.workspace_bytes) >= L.total);
+  FALCON_HOST_CHECK(L.flags_bytes % 256 == 0 && L.e63_bytes % 256 == 0);
+  std::vector<int> chains(size_t(BH) * 2, 0), chunks(size_t(BH) * nchunks, 0);
+  for (int64_t b = 0; b < grid; ++b) {
+    const FusedRole r = fused_role(int(b), int(L.BHpad));
+    FALCON_HOST_CHECK(r.s >= 0 && r.s < L.BHpad);
+    FALCON_HOST_CHECK(b % 8 == r.s % 8);                   // on its sequence's XCD
+    if (r.s >= BH) continue;
+    if (r.chain) {
+      FALCON_HOST_CHECK(r.part == 0 || r.part == 1);
+      ++chains[size_t(r.s) * 2 + r.part];
+      continue;
+    }
+    FALCON_HOST_CHECK(r.c >= 0 && r.c < nchunks);
+    ++chunks[size_t(r.s) * nchunks + r.c];
+    const int64_t q = int64_t(r.s) * nchunks + r.c;
+    FALCON_HOST_CHECK((q + 1) * kBlockElems * 2 <= L.blocks_bytes);
+    FALCON_HOST_CHECK((q + 1) * 4 <= L.e63_bytes);
+    FALCON_HOST_CHECK((int64_t(r.s) * L.nflag + r.c + 1) * 4 <= L.flags_bytes);
+  }
+  for (int v : chains) FALCON_HOST_CHECK(v == 1);
+  for (int v : chunks) FALCON_HOST_CHECK(v == 1);
+  for (int c = 0; c < nchunks; ++c) {
+    const int ca = c + 2 < nchunks ? c + 2 : nchunks - 1;  // chunk read ahead
+    const int cf = c + 3 < nchunks ? c + 3 : nchunks - 1;  // flag read ahead
+    FALCON_HOST_CHECK(ca >= 0 && ca < nchunks && cf >= 0 && cf < nchunks);
+    const int rows = a.T - c * kC < kC ? a.T - c * kC : kC;
+    FALCON_HOST_CHECK(rows > 0 && int64_t(c) * kC + rows <= a.T);
+  }
+  for (int p = 0; p < 2; ++p)
+    for (int w = 0; w < 4; ++w)
+      for (int l = 0; l < 64; ++l) {
+        FALCON_HOST_CHECK(2 * kOutK + chain_lf(w, l) + 1024 + 16 <= 2 * kOutQt);
+        FALCON_HOST_CHECK(2 * kOutQt + chain_lf(w, l) + 1024 + 16 <= 2 * kOutH);
+        FALCON_HOST_CHECK(2 * kOutH + chain_lh(p, w, l) + 2048 + 8 <= 2 * kOutOt);
+        FALCON_HOST_CHECK(2 * kOutOt + chain_lh(p, w, l) + 2048 + 8 <= 2 * kBlockElems);
+        FALCON_HOST_CHECK(chain_lo(p, w, l) + 32 + 8 <= uint32_t(2 * kC * kD));
+      }
+}
+
 hipError_t launch_chunked_wy(const ProblemArgs& a, hipStream_t st) {
   const int64_t BH = int64_t(a.B) * a.H;
   const int nchunks = (a.T + kC - 1) / kC;
@@ -1038,6 +1117,7 @@ hipError_t launch_chunked_wy(const ProblemArgs& a, hipStream_t st) {
   float* decay63 = reinterpret_cast<float*>(ws + L.flags_bytes);
   uint16_t* blocks = reinterpret_cast<uint16_t*>(ws + L.flags_bytes + L.e63_bytes);
   if (a.f1_form == 1) {
+    FALCON_HOST_CHECK(int64_t(a.workspace_bytes) >= L.total && BH * nchunks <= INT32_MAX);
     hipLaunchKernelGGL(falcon1_wy_kernel, dim3(unsigned(BH * nchunks)), dim3(256), 0, st,
                        static_cast<const bf16_t*>(a.phi_k), static_cast<const bf16_t*>(a.phi_q),
                        static_cast<const bf16_t*>(a.v), a.beta, a.lam, static_cast<const bf16_t*>(a.k_prev),
@@ -1069,6 +1149,7 @@ hipError_t launch_chunked_wy(const ProblemArgs& a, hipStream_t st) {
   f.eps = a.eps;
   f.eps_gamma = a.eps_gamma;
   const int64_t nflags = L.flags_bytes / 4;
+  if (kBoundsCheck) check_fused_grid(a, L, nchunks);
   hipLaunchKernelGGL(zero_ints_kernel, dim3(unsigned((nflags + 255) / 256)), dim3(256), 0, st, flags, int(nflags));
   hipLaunchKernelGGL(falcon1_fused_kernel, dim3(unsigned(L.BHpad * (int64_t(nchunks) + 2))), dim3(256), 0, st, f);
   return hipGetLastError();

@@ -8,6 +8,19 @@
 
 namespace falcon {
 
+// Host-side assertions of the launchers' layout and index math.  The
+// bounds-check build (FALCON_BOUNDS_CHECK, with the host sanitizers) compiles
+// them in: a failed one prints the condition and aborts.  Other builds compile
+// them to nothing.
+#ifdef FALCON_BOUNDS_CHECK
+[[noreturn]] void host_check_failed(const char* cond, const char* file, int line);
+#define FALCON_HOST_CHECK(cond) ((cond) ? (void)0 : ::falcon::host_check_failed(#cond, __FILE__, __LINE__))
+constexpr bool kBoundsCheck = true;
+#else
+#define FALCON_HOST_CHECK(cond) ((void)0)
+constexpr bool kBoundsCheck = false;
+#endif
+
 struct ProblemArgs {
   int B, H, T, dk, dv;
   int variant;
