@@ -29,9 +29,25 @@ def oracle_forward(variant, d, *, eps=1e-6, eps_gamma=1e-6, S0=None, k_prev=None
                               k_prev=None if k_prev is None else f(k_prev))
 
 
+def worst_sequence(got, ref):
+    """Largest relative L2 over the (b, h) sequences (leading two axes)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if got.ndim < 3:
+        return rel_l2(got, ref)
+    B, H = got.shape[:2]
+    return max(rel_l2(got[b, h], ref[b, h]) for b in range(B) for h in range(H))
+
+
 def check(o, S_T, O_ref, S_ref, tol, what=""):
-    eo = rel_l2(o.float().cpu().numpy(), O_ref)
-    es = rel_l2(S_T.cpu().numpy(), S_ref)
-    assert np.all(np.isfinite(o.float().cpu().numpy())), f"{what}: non-finite output"
-    assert eo <= tol and es <= tol, f"{what}: rel L2 o={eo:.3e} S_T={es:.3e} tol={tol:.0e}"
+    """The stated tolerance on the whole output and final state and on every
+    sequence's output and final state."""
+    got_o = o.float().cpu().numpy()
+    got_s = S_T.cpu().numpy()
+    assert np.all(np.isfinite(got_o)), f"{what}: non-finite output"
+    assert np.all(np.isfinite(got_s)), f"{what}: non-finite final state"
+    eo, es = rel_l2(got_o, O_ref), rel_l2(got_s, S_ref)
+    wo, ws = worst_sequence(got_o, O_ref), worst_sequence(got_s, S_ref)
+    assert max(eo, es, wo, ws) <= tol, (f"{what}: rel L2 o={eo:.3e} S_T={es:.3e}, worst sequence "
+                                        f"o={wo:.3e} S_T={ws:.3e}, tol={tol:.0e}")
     return eo, es
