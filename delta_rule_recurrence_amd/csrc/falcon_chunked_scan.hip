@@ -39,8 +39,9 @@ using namespace frag;
 constexpr int kC = 64;
 constexpr int kD = 64;
 constexpr int kTileChunks = 8;
-constexpr int kScanThreads = 256;   // a scan block covers 1024 state elements, 4 per thread
-constexpr int kScanDepth = 8;       // tiles of aggregates in flight per scan thread
+constexpr int kScanThreads = 256;   // a scan block covers 256 state elements, one per thread
+constexpr int kScanBlocks = 16;     // scan blocks per sequence (4096 state elements)
+constexpr int kScanDepth = 32;      // tiles of aggregates in flight per scan thread
 constexpr int kStateFloats = kD * kD;
 
 constexpr int kTileThreads = 256;   // four waves per tile
@@ -295,52 +296,37 @@ falcon1a_tile_kernel(TileArgs a, ScanWorkspace ws) {
 }
 
 // ---- launch 2: start state of every tile -------------------------------------
-// Block (bh, part): state elements [part * 1024, part * 1024 + 1024) of
-// sequence bh in register order, 4 per thread.  S_T is written in [dk][dv].
+// Block (bh, part): state elements [part * 256, part * 256 + 256) of sequence
+// bh in register order, one per thread (consecutive threads, consecutive
+// addresses); up to kScanDepth tiles' aggregates are loaded before they are
+// folded, so a sequence of that many tiles costs one round trip to memory.
+// S_T is written in [dk][dv].
 __global__ void __launch_bounds__(kScanThreads)
 falcon1a_tile_scan_kernel(const float* S0, float* S_T, int ntiles_seq, ScanWorkspace ws) {
-  const int64_t bh = blockIdx.x / 4;
-  const int e0 = ((blockIdx.x & 3) * kScanThreads + threadIdx.x) * 4;   // register-order index
-  const int lane = (e0 >> 2) & 63, tcb = e0 >> 8;                      // tile (fb * 4 + cb)
+  const int64_t bh = blockIdx.x / kScanBlocks;
+  const int e = (blockIdx.x % kScanBlocks) * kScanThreads + threadIdx.x;   // register-order index
+  const int r = e & 3, lane = (e >> 2) & 63, tcb = e >> 8;                   // tile (fb * 4 + cb)
   const int fb = tcb >> 2, cb = tcb & 3, g = lane >> 4, c16 = lane & 15;
-  f32x4 s = zero4();
-  if (S0) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) s[r] = S0[(bh * kD + 16 * fb + 4 * g + r) * kD + 16 * cb + c16];
-  }
-  // aggregates are streamed kScanDepth tiles at a time, the next group's
-  // loads in flight while the current group is folded in
+  const int64_t sidx = (bh * kD + 16 * fb + 4 * g + r) * kD + 16 * cb + c16;
+  float s = S0 ? S0[sidx] : 0.0f;
   const int64_t t0 = bh * ntiles_seq;
-  f32x4 cur[kScanDepth], nxt[kScanDepth];
-  float lcur[kScanDepth], lnxt[kScanDepth];
-  auto fetch = [&](int base, f32x4 (&dst)[kScanDepth], float (&ld)[kScanDepth]) {
+  for (int base = 0; base < ntiles_seq; base += kScanDepth) {
+    float ag[kScanDepth], ld[kScanDepth];
 #pragma unroll
     for (int k = 0; k < kScanDepth; ++k) {
       const int tile = base + k < ntiles_seq ? base + k : ntiles_seq - 1;
-      dst[k] = *reinterpret_cast<const f32x4*>(ws.agg + (t0 + tile) * kStateFloats + e0);
+      ag[k] = ws.agg[(t0 + tile) * kStateFloats + e];
       ld[k] = ws.logdecay[t0 + tile];
     }
-  };
-  fetch(0, cur, lcur);
-  for (int base = 0; base < ntiles_seq; base += kScanDepth) {
-    if (base + kScanDepth < ntiles_seq) fetch(base + kScanDepth, nxt, lnxt);
 #pragma unroll
     for (int k = 0; k < kScanDepth; ++k) {
       if (base + k < ntiles_seq) {
-        *reinterpret_cast<f32x4*>(ws.start + (t0 + base + k) * kStateFloats + e0) = s;
-        s = s * __expf(lcur[k]) + cur[k];
+        ws.start[(t0 + base + k) * kStateFloats + e] = s;
+        s = s * __expf(ld[k]) + ag[k];
       }
     }
-#pragma unroll
-    for (int k = 0; k < kScanDepth; ++k) {
-      cur[k] = nxt[k];
-      lcur[k] = lnxt[k];
-    }
   }
-  if (S_T) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) S_T[(bh * kD + 16 * fb + 4 * g + r) * kD + 16 * cb + c16] = s[r];
-  }
+  if (S_T) S_T[sidx] = s;
 }
 
 int64_t scan_tiles_per_seq(const ProblemArgs& a) {
@@ -366,7 +352,8 @@ hipError_t launch_chunked_scan(const ProblemArgs& a, hipStream_t st) {
   const ScanLayout L(ntiles);
   // the tiles of a sequence cover its chunks exactly; the grids and the
   // workspace hold every tile
-  FALCON_HOST_CHECK(ntiles <= INT32_MAX && BH * 4 <= INT32_MAX);
+  FALCON_HOST_CHECK(ntiles <= INT32_MAX && BH * kScanBlocks <= INT32_MAX);
+  FALCON_HOST_CHECK(kScanBlocks * kScanThreads == kStateFloats);
   FALCON_HOST_CHECK(a.workspace_bytes >= L.total);
   FALCON_HOST_CHECK((nts - 1) * kTileChunks < (int64_t(a.T) + kC - 1) / kC &&
                     nts * kTileChunks >= (int64_t(a.T) + kC - 1) / kC);
@@ -390,7 +377,7 @@ hipError_t launch_chunked_scan(const ProblemArgs& a, hipStream_t st) {
   ta.eps = a.eps;
   ta.eps_gamma = a.eps_gamma;
   hipLaunchKernelGGL(falcon1a_tile_kernel<false>, dim3(unsigned(ntiles)), dim3(kTileThreads), 0, st, ta, ws);
-  hipLaunchKernelGGL(falcon1a_tile_scan_kernel, dim3(unsigned(BH * 4)), dim3(kScanThreads), 0, st, a.S0,
+  hipLaunchKernelGGL(falcon1a_tile_scan_kernel, dim3(unsigned(BH * kScanBlocks)), dim3(kScanThreads), 0, st, a.S0,
                      a.S_T, int(nts), ws);
   hipLaunchKernelGGL(falcon1a_tile_kernel<true>, dim3(unsigned(ntiles)), dim3(kTileThreads), 0, st, ta, ws);
   return hipGetLastError();
