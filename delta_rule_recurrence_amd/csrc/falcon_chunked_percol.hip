@@ -44,13 +44,15 @@ constexpr int kC = 64;
 constexpr int kD = 64;
 constexpr int kSlice = 16;                  // value columns per workgroup
 constexpr int kThreads = 256;
-constexpr int kGP = 68;                     // float row pitch of the Gram buffers (16-byte aligned, spreads banks)
+constexpr int kDP = 20;                     // float row pitch of the diagonal Gram blocks (16-byte reads conflict-free)
 
 struct PcSmem {
   uint16_t x[kC * kD];                      // keys phi(k_{t0+r-1}), swizzled rows
   uint16_t q[kC * kD];                      // queries, swizzled rows
-  float kq[kC][kGP];                        // [i][s] = x_i . x_s for s < i, 0 for i <= s < 16(i/16 + 1)
-  float pq[kC][kGP];                        // [i][s] = q_i . x_s for s < i, 0 for i <= s < 16(i/16 + 1)
+  float kqd[4][16][kDP];                    // diagonal blocks: [b][i-16b][s-16b] = x_i . x_s for s < i, else 0
+  float pqd[4][16][kDP];                    // diagonal blocks: [b][i-16b][s-16b] = q_i . x_s for s < i, else 0
+  uint16_t kqf[3][2][64 * 8];               // frag(KQ)[b][m] for b = 1..3, entries s < 16 b only, bf16
+  uint16_t pqf[3][2][64 * 8];               // frag(PQ)[b][m], same
   float xs[kC][kSlice];                     // (X S)_{i,j}
   float qs[kC][kSlice];                     // (Q S)_{i,j}
   float vb[kC][kSlice];                     // v_{i,j}
@@ -140,7 +142,7 @@ __device__ __forceinline__ void stage_chunk(PcSmem& sm, const ChunkRegs& R, int 
 // decay is one exp2.  gcarry holds g at the end of the previous block (0
 // before block 0) and is advanced to the end of this one.
 template <bool kReg, int B>
-__device__ __forceinline__ void solve_block(PcSmem& sm, int jl, int li, int t0, int T, bool fresh, float eps,
+__device__ __forceinline__ void solve_block(PcSmem& sm, int w, int jl, int li, int t0, int T, bool fresh, float eps,
                                             float eps_gamma, float& gcarry) {
   const int i = 16 * B + li;
   const int t = t0 + i;
@@ -166,25 +168,30 @@ __device__ __forceinline__ void solve_block(PcSmem& sm, int jl, int li, int t0, 
   float a = kReg ? eta * (sm.vb[i][jl] - exp2_fast(gprev) * sm.xs[i][jl]) : eta * sm.vb[i][jl];
   float o = exp2_fast(gi) * sm.qs[i][jl];
   if constexpr (B > 0) {
-    float pk0 = 0.f, pk1 = 0.f, pp0 = 0.f, pp1 = 0.f;
-#pragma unroll
-    for (int s4 = 0; s4 < 4 * B; ++s4) {
-      const f32x4 w4 = ld4(&sm.w[jl][4 * s4]);
-      const f32x4 p4 = ld4(&sm.pq[i][4 * s4]);
-      pp0 = fmaf(p4[0], w4[0], pp0);
-      pp1 = fmaf(p4[1], w4[1], pp1);
-      pp0 = fmaf(p4[2], w4[2], pp0);
-      pp1 = fmaf(p4[3], w4[3], pp1);
-      if constexpr (kReg) {
-        const f32x4 k4 = ld4(&sm.kq[i][4 * s4]);
-        pk0 = fmaf(k4[0], w4[0], pk0);
-        pk1 = fmaf(k4[1], w4[1], pk1);
-        pk0 = fmaf(k4[2], w4[2], pk0);
-        pk1 = fmaf(k4[3], w4[3], pk1);
-      }
+    // the earlier blocks on the matrix cores, bf16 operands: D = W' KQ_B^T,
+    // row a of W' the wave's own column 4 w + (a >> 2), so every component of
+    // the lane's result row 4 g + r is EK[16B + li][4 w + g] (and EP likewise):
+    // no value crosses to another wave.  W' rows beyond the solved blocks
+    // meet zero Gram entries.
+    const int g = jl - 4 * w, l = 16 * g + li;
+    const int ja = 4 * w + (li >> 2);
+    const bf16x8 a0 = frag_acc(ld4(&sm.w[ja][4 * g]), ld4(&sm.w[ja][16 + 4 * g]));
+    f32x4 ek4 = zero4(), ep4;
+    if constexpr (kReg) ek4 = mfma32(a0, load_frag(&sm.kqf[B - 1][0][l * 8]), zero4());
+    ep4 = mfma32(a0, load_frag(&sm.pqf[B - 1][0][l * 8]), zero4());
+    if constexpr (B == 3) {
+      const bf16x8 a1 = frag_acc(ld4(&sm.w[ja][32 + 4 * g]), ld4(&sm.w[ja][48 + 4 * g]));
+      if constexpr (kReg) ek4 = mfma32(a1, load_frag(&sm.kqf[2][1][l * 8]), ek4);
+      ep4 = mfma32(a1, load_frag(&sm.pqf[2][1][l * 8]), ep4);
     }
-    if constexpr (kReg) a -= eta * exp2_fast(gprev - gcarry) * (pk0 + pk1);
-    o += exp2_fast(gi - gcarry) * (pp0 + pp1);
+    if constexpr (kReg) a -= eta * exp2_fast(gprev - gcarry) * ek4[0];
+    o += exp2_fast(gi - gcarry) * ep4[0];
+    // The inline-asm DPP chains below write registers the compiler's hazard
+    // checks cannot see.  Reading the products above makes the compiler wait
+    // until the MFMAs are done; no instruction may move above this point, so
+    // no asm write can land in a register an MFMA still reads or will write
+    // (its unused result components are free registers to the allocator).
+    __builtin_amdgcn_sched_barrier(0);
   }
   // in-block decays e^{g_{i-1}-g_s} = gamma_{s+1} ... gamma_{i-1} for
   // s = 16B + sl < i, as a suffix product over sl with gamma_{sl+1} taken from
@@ -208,10 +215,10 @@ __device__ __forceinline__ void solve_block(PcSmem& sm, int jl, int li, int t0, 
   float kr[16], pr[16];
 #pragma unroll
   for (int s4 = 0; s4 < 4; ++s4) {
-    const f32x4 p4 = ld4(&sm.pq[i][16 * B + 4 * s4]);
+    const f32x4 p4 = ld4(&sm.pqd[B][li][4 * s4]);
     pr[4 * s4] = p4[0]; pr[4 * s4 + 1] = p4[1]; pr[4 * s4 + 2] = p4[2]; pr[4 * s4 + 3] = p4[3];
     if constexpr (kReg) {
-      const f32x4 k4 = ld4(&sm.kq[i][16 * B + 4 * s4]);
+      const f32x4 k4 = ld4(&sm.kqd[B][li][4 * s4]);
       kr[4 * s4] = k4[0]; kr[4 * s4 + 1] = k4[1]; kr[4 * s4 + 2] = k4[2]; kr[4 * s4 + 3] = k4[3];
     }
   }
@@ -304,6 +311,9 @@ falcon2_chunked_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restric
       S[fb][r] = (w == 0 && S0) ? S0[(bh * kD + 16 * fb + 4 * g + r) * kD + j0 + c16] : 0.0f;
 
   const int nchunks = (T + kC - 1) / kC;
+  // the earlier-block products read whole rows of w, solved or not: start
+  // them at zero (never NaN), later chunks leave finite values behind
+  for (int e = tid; e < kSlice * kC; e += kThreads) (&sm.w[0][0])[e] = 0.0f;
   ChunkRegs R;
   fetch_chunk(R, K, Q, V, Bt, Lm, kp, T, 0, j0, tid);
   for (int c = 0; c < nchunks; ++c) {
@@ -333,41 +343,64 @@ falcon2_chunked_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restric
         }
       }
     } else {
-      // Gram and read tiles (ib, sb), sb <= ib: lane holds rows i = 16ib+4g+r,
-      // column s = 16sb+c16; waves 1..3 take tiles [0,4), [4,7), [7,10)
-      const int n0 = w == 1 ? 0 : w == 2 ? 4 : 7;
-      const int n1 = w == 1 ? 4 : w == 2 ? 7 : 10;
-      for (int n = n0; n < n1; ++n) {
-        int ib, sb;
-        lower_tile(n, ib, sb);
-        const bf16x8 xs0 = ring_frag_c(sm.x, 16 * sb + c16, 0, g), xs1 = ring_frag_c(sm.x, 16 * sb + c16, 1, g);
-        f32x4 dk = mfma32(ring_frag_c(sm.x, 16 * ib + c16, 0, g), xs0, zero4());
-        dk = mfma32(ring_frag_c(sm.x, 16 * ib + c16, 1, g), xs1, dk);
-        f32x4 dp = mfma32(ring_frag_c(sm.q, 16 * ib + c16, 0, g), xs0, zero4());
-        dp = mfma32(ring_frag_c(sm.q, 16 * ib + c16, 1, g), xs1, dp);
-        // a diagonal tile keeps its strict lower triangle only (the solve
-        // reads it without a mask); its diagonal goes to en and pd
+      // Waves 1..3: the diagonal Gram and read blocks in float32 (lane holds
+      // rows i = 16b+4g+r, column s = 16b+c16; strict lower triangle, the
+      // diagonal to en and pd), and for the earlier-block sums the fragments
+      // frag(KQ)[b][m], frag(PQ)[b][m] of rows 16b.. over s < 16b, built from
+      // tiles T(sb, b) whose lane holds x_{16sb+4g+r} . x_{16b+c16} (and the
+      // same with q_{16b+c16}); tiles with sb >= b are zero.
+      auto diag = [&](int b) {
+        const bf16x8 xs0 = ring_frag_c(sm.x, 16 * b + c16, 0, g), xs1 = ring_frag_c(sm.x, 16 * b + c16, 1, g);
+        f32x4 dk = mfma32(ring_frag_c(sm.x, 16 * b + c16, 0, g), xs0, zero4());
+        dk = mfma32(ring_frag_c(sm.x, 16 * b + c16, 1, g), xs1, dk);
+        f32x4 dp = mfma32(ring_frag_c(sm.q, 16 * b + c16, 0, g), xs0, zero4());
+        dp = mfma32(ring_frag_c(sm.q, 16 * b + c16, 1, g), xs1, dp);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int i = 16 * ib + 4 * g + r;
-          const bool upper = ib == sb && c16 >= 4 * g + r;
-          sm.kq[i][16 * sb + c16] = upper ? 0.0f : dk[r];
-          sm.pq[i][16 * sb + c16] = upper ? 0.0f : dp[r];
-          if (ib == sb && 4 * g + r == c16) {
-            sm.en[i] = dk[r];
-            sm.pd[i] = dp[r];
+          const bool upper = c16 >= 4 * g + r;
+          sm.kqd[b][4 * g + r][c16] = upper ? 0.0f : dk[r];
+          sm.pqd[b][4 * g + r][c16] = upper ? 0.0f : dp[r];
+          if (4 * g + r == c16) {
+            sm.en[16 * b + c16] = dk[r];
+            sm.pd[16 * b + c16] = dp[r];
           }
         }
+      };
+      auto tile = [&](int sb, int b, f32x4& tk, f32x4& tp) {
+        const bf16x8 a0 = ring_frag_c(sm.x, 16 * sb + c16, 0, g), a1 = ring_frag_c(sm.x, 16 * sb + c16, 1, g);
+        tk = mfma32(a0, ring_frag_c(sm.x, 16 * b + c16, 0, g), zero4());
+        tk = mfma32(a1, ring_frag_c(sm.x, 16 * b + c16, 1, g), tk);
+        tp = mfma32(a0, ring_frag_c(sm.q, 16 * b + c16, 0, g), zero4());
+        tp = mfma32(a1, ring_frag_c(sm.q, 16 * b + c16, 1, g), tp);
+      };
+      auto frags = [&](int b, int m, bool two) {
+        f32x4 k0, p0, k1 = zero4(), p1 = zero4();
+        tile(2 * m, b, k0, p0);
+        if (two) tile(2 * m + 1, b, k1, p1);
+        store_frag(&sm.kqf[b - 1][m][l * 8], frag_acc(k0, k1));
+        store_frag(&sm.pqf[b - 1][m][l * 8], frag_acc(p0, p1));
+      };
+      if (w == 1) {
+        diag(0);
+        diag(1);
+        frags(1, 0, false);
+      } else if (w == 2) {
+        diag(2);
+        frags(2, 0, true);
+      } else {
+        diag(3);
+        frags(3, 0, true);
+        frags(3, 1, false);
       }
     }
     __syncthreads();
     // ---- per-column rows, block by block ------------------------------------
     {
       float gcarry = 0.f;
-      solve_block<kReg, 0>(sm, jl, li, t0, T, fresh, eps, eps_gamma, gcarry);
-      solve_block<kReg, 1>(sm, jl, li, t0, T, fresh, eps, eps_gamma, gcarry);
-      solve_block<kReg, 2>(sm, jl, li, t0, T, fresh, eps, eps_gamma, gcarry);
-      solve_block<kReg, 3>(sm, jl, li, t0, T, fresh, eps, eps_gamma, gcarry);
+      solve_block<kReg, 0>(sm, w, jl, li, t0, T, fresh, eps, eps_gamma, gcarry);
+      solve_block<kReg, 1>(sm, w, jl, li, t0, T, fresh, eps, eps_gamma, gcarry);
+      solve_block<kReg, 2>(sm, w, jl, li, t0, T, fresh, eps, eps_gamma, gcarry);
+      solve_block<kReg, 3>(sm, w, jl, li, t0, T, fresh, eps, eps_gamma, gcarry);
       if (li == 0) sm.e63[jl] = exp2_fast(gcarry);
     }
     __syncthreads();
