@@ -1107,6 +1107,13 @@ void check_fused_grid(const ProblemArgs& a, const WyLayout& L, int nchunks) {
       }
 }
 
+// The one-launch form holds two workgroup slots per sequence for its chains
+// for the whole launch (four slots per CU, 128 per XCD), and a chunk
+// workgroup can only run on its sequence's XCD: with more than 64 chains per
+// XCD the chunk workgroups would crowd into too few slots (none at 128, where
+// every chain's wait would give up), so larger batches take two launches.
+constexpr int64_t kMaxOneLaunchSeqs = 256;
+
 hipError_t launch_chunked_wy(const ProblemArgs& a, hipStream_t st) {
   const int64_t BH = int64_t(a.B) * a.H;
   const int nchunks = (a.T + kC - 1) / kC;
@@ -1116,7 +1123,7 @@ hipError_t launch_chunked_wy(const ProblemArgs& a, hipStream_t st) {
   int* flags = reinterpret_cast<int*>(ws);
   float* decay63 = reinterpret_cast<float*>(ws + L.flags_bytes);
   uint16_t* blocks = reinterpret_cast<uint16_t*>(ws + L.flags_bytes + L.e63_bytes);
-  if (a.f1_form == 1) {
+  if (a.f1_form == 1 || L.BHpad > kMaxOneLaunchSeqs) {
     FALCON_HOST_CHECK(int64_t(a.workspace_bytes) >= L.total && BH * nchunks <= INT32_MAX);
     hipLaunchKernelGGL(falcon1_wy_kernel, dim3(unsigned(BH * nchunks)), dim3(256), 0, st,
                        static_cast<const bf16_t*>(a.phi_k), static_cast<const bf16_t*>(a.phi_q),
@@ -1149,6 +1156,7 @@ hipError_t launch_chunked_wy(const ProblemArgs& a, hipStream_t st) {
   f.eps = a.eps;
   f.eps_gamma = a.eps_gamma;
   const int64_t nflags = L.flags_bytes / 4;
+  FALCON_HOST_CHECK(L.BHpad <= kMaxOneLaunchSeqs);
   if (kBoundsCheck) check_fused_grid(a, L, nchunks);
   hipLaunchKernelGGL(zero_ints_kernel, dim3(unsigned((nflags + 255) / 256)), dim3(256), 0, st, flags, int(nflags));
   hipLaunchKernelGGL(falcon1_fused_kernel, dim3(unsigned(L.BHpad * (int64_t(nchunks) + 2))), dim3(256), 0, st, f);

@@ -132,7 +132,9 @@ int32_t falcon_set_wait_limit(int32_t polls);
  *   FALCON_F1_ONE_LAUNCH (default): one kernel in which chunk workgroups
  *     build the chunk matrices while per-sequence chain workgroups, started
  *     first, carry the state through announced chunks (plus a small fill of
- *     the hand-over flags);
+ *     the hand-over flags).  Batches of more than 256 sequences (B H) run the
+ *     two-launch form instead: their chains would hold too many workgroup
+ *     slots;
  *   FALCON_F1_TWO_LAUNCH: the chunk matrices of all chunks, then the chains.
  * The workspace size is the same for both.  Meant for comparison and
  * debugging; calls made while it changes use either form.  Returns the
