@@ -79,12 +79,18 @@ constexpr float kLog2e = 1.4426950408889634f;
 // ratio cancels the rounding of u (Kahan's compensated log1p), so small alpha
 // keeps its relative accuracy; log2 and the reciprocal are the hardware's.
 // Also returns gamma itself (u).
+// Branch-free: both forms are computed and blended by a 0/1 weight (when
+// u rounds to 1 the log is exactly 0 and the ratio finite, so the blend is
+// exact), which keeps the hardware log and reciprocal out of a lane-masked
+// branch.
 __device__ __forceinline__ float log2_gamma(float eta, float lam, float eps_gamma, float& gamma) {
   const float alpha = fminf(eta * lam, 1.0f - eps_gamma);
   const float u = 1.0f - alpha;
   const float d = u - 1.0f;
   gamma = u;
-  return d == 0.0f ? -kLog2e * alpha : __builtin_amdgcn_logf(u) * (-alpha * __builtin_amdgcn_rcpf(d));
+  const float tiny = d == 0.0f ? 1.0f : 0.0f;
+  const float ratio = -alpha * __builtin_amdgcn_rcpf(d - tiny);
+  return __builtin_amdgcn_logf(u) * ratio - kLog2e * alpha * tiny;
 }
 
 // The next chunk's inputs, fetched into registers during the current chunk.
@@ -147,12 +153,15 @@ __device__ __forceinline__ void solve_block(PcSmem& sm, int w, int jl, int li, i
   const int i = 16 * B + li;
   const int t = t0 + i;
   const bool live = t < T;
-  // step size and decay of row i in column jl; g by a scan over the 16 rows
-  const float den = sm.en[i] + sm.lm[i] + eps;
-  const float eta =
-      (live && !(fresh && t == 0) && den != 0.0f) ? sm.bt[i][jl] * __builtin_amdgcn_rcpf(den) : 0.0f;
+  // step size and decay of row i in column jl (branch-free: every operand is
+  // loaded and the reciprocal taken whatever the row); g by a scan over the
+  // 16 rows
+  const float lmi = sm.lm[i], bti = sm.bt[i][jl];
+  const float den = sm.en[i] + lmi + eps;
+  const bool on = live && !(fresh && t == 0) && den != 0.0f;
+  const float eta = on ? bti * __builtin_amdgcn_rcpf(on ? den : 1.0f) : 0.0f;
   float gam;
-  const float lg0 = log2_gamma(eta, sm.lm[i], eps_gamma, gam);
+  const float lg0 = log2_gamma(eta, lmi, eps_gamma, gam);
   const float lg = live ? lg0 : 0.0f;
   gam = live ? gam : 1.0f;
   float gi = lg;
@@ -167,6 +176,10 @@ __device__ __forceinline__ void solve_block(PcSmem& sm, int w, int jl, int li, i
   // earlier blocks, through w_s = e^{g_{16B-1}-g_s} rho_s
   float a = kReg ? eta * (sm.vb[i][jl] - exp2_fast(gprev) * sm.xs[i][jl]) : eta * sm.vb[i][jl];
   float o = exp2_fast(gi) * sm.qs[i][jl];
+  // operands and results of the earlier-block MFMAs, kept live (below) past
+  // every inline-asm statement of the block
+  bf16x8 m_a0 = {}, m_a1 = {}, m_k0 = {}, m_k1 = {}, m_p0 = {}, m_p1 = {};
+  f32x4 ek4 = zero4(), ep4 = zero4();
   if constexpr (B > 0) {
     // the earlier blocks on the matrix cores, bf16 operands: D = W' KQ_B^T,
     // row a of W' the wave's own column 4 w + (a >> 2), so every component of
@@ -175,23 +188,24 @@ __device__ __forceinline__ void solve_block(PcSmem& sm, int w, int jl, int li, i
     // meet zero Gram entries.
     const int g = jl - 4 * w, l = 16 * g + li;
     const int ja = 4 * w + (li >> 2);
-    const bf16x8 a0 = frag_acc(ld4(&sm.w[ja][4 * g]), ld4(&sm.w[ja][16 + 4 * g]));
-    f32x4 ek4 = zero4(), ep4;
-    if constexpr (kReg) ek4 = mfma32(a0, load_frag(&sm.kqf[B - 1][0][l * 8]), zero4());
-    ep4 = mfma32(a0, load_frag(&sm.pqf[B - 1][0][l * 8]), zero4());
+    m_a0 = frag_acc(ld4(&sm.w[ja][4 * g]), ld4(&sm.w[ja][16 + 4 * g]));
+    if constexpr (kReg) {
+      m_k0 = load_frag(&sm.kqf[B - 1][0][l * 8]);
+      ek4 = mfma32(m_a0, m_k0, zero4());
+    }
+    m_p0 = load_frag(&sm.pqf[B - 1][0][l * 8]);
+    ep4 = mfma32(m_a0, m_p0, zero4());
     if constexpr (B == 3) {
-      const bf16x8 a1 = frag_acc(ld4(&sm.w[ja][32 + 4 * g]), ld4(&sm.w[ja][48 + 4 * g]));
-      if constexpr (kReg) ek4 = mfma32(a1, load_frag(&sm.kqf[2][1][l * 8]), ek4);
-      ep4 = mfma32(a1, load_frag(&sm.pqf[2][1][l * 8]), ep4);
+      m_a1 = frag_acc(ld4(&sm.w[ja][32 + 4 * g]), ld4(&sm.w[ja][48 + 4 * g]));
+      if constexpr (kReg) {
+        m_k1 = load_frag(&sm.kqf[2][1][l * 8]);
+        ek4 = mfma32(m_a1, m_k1, ek4);
+      }
+      m_p1 = load_frag(&sm.pqf[2][1][l * 8]);
+      ep4 = mfma32(m_a1, m_p1, ep4);
     }
     if constexpr (kReg) a -= eta * exp2_fast(gprev - gcarry) * ek4[0];
     o += exp2_fast(gi - gcarry) * ep4[0];
-    // The inline-asm DPP chains below write registers the compiler's hazard
-    // checks cannot see.  Reading the products above makes the compiler wait
-    // until the MFMAs are done; no instruction may move above this point, so
-    // no asm write can land in a register an MFMA still reads or will write
-    // (its unused result components are free registers to the allocator).
-    __builtin_amdgcn_sched_barrier(0);
   }
   // in-block decays e^{g_{i-1}-g_s} = gamma_{s+1} ... gamma_{i-1} for
   // s = 16B + sl < i, as a suffix product over sl with gamma_{sl+1} taken from
@@ -255,6 +269,12 @@ __device__ __forceinline__ void solve_block(PcSmem& sm, int w, int jl, int li, i
 #undef FALCON_RD
     o += exp2_fast(lg) * (o0 + o1) + sm.pd[i] * rho;
   }
+  // The inline-asm DPP statements above write registers the compiler's
+  // hazard checks cannot see.  With every operand and result register of the
+  // MFMAs live until here, the allocator cannot give an asm output a register
+  // an MFMA still reads or writes (unused result components would otherwise
+  // be free to it).
+  asm volatile("" ::"v"(m_a0), "v"(m_a1), "v"(m_k0), "v"(m_k1), "v"(m_p0), "v"(m_p1), "v"(ek4), "v"(ep4));
   sm.ob[i][jl] = bf(o);
   // w to the end of this block: earlier entries decay by e^{g_last-g_carry},
   // this block's entries are e^{g_last-g_s} rho_s
