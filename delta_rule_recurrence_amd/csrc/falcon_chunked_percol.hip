@@ -245,7 +245,7 @@ __device__ __forceinline__ void solve_block(PcSmem& sm, int w, int jl, int li, i
     // lane SL of the 16-lane row; the leading s_nop covers the DPP
     // read-after-write hazard on a
 #define FALCON_SUB(SL)                                                                                \
-  asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %0, %1 row_newbcast:" #SL " row_mask:0xf bank_mask:0xf" \
+  asm("s_nop 1\n\tv_fmac_f32_dpp %0, %0, %1 row_newbcast:" #SL " row_mask:0xf bank_mask:0xf" \
                : "+v"(a) : "v"(nc[SL]));
     FALCON_SUB(0) FALCON_SUB(1) FALCON_SUB(2) FALCON_SUB(3) FALCON_SUB(4) FALCON_SUB(5) FALCON_SUB(6)
     FALCON_SUB(7) FALCON_SUB(8) FALCON_SUB(9) FALCON_SUB(10) FALCON_SUB(11) FALCON_SUB(12) FALCON_SUB(13)
@@ -260,7 +260,7 @@ __device__ __forceinline__ void solve_block(PcSmem& sm, int w, int jl, int li, i
 #define FALCON_RD(SL, ACC)                                                                              \
   {                                                                                                     \
     const float cf = ed[SL] * pr[SL];                                                                   \
-    asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_newbcast:" #SL " row_mask:0xf bank_mask:0xf" \
+    asm("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_newbcast:" #SL " row_mask:0xf bank_mask:0xf" \
                  : "+v"(ACC) : "v"(rho), "v"(cf));                                                      \
   }
     FALCON_RD(0, o0) FALCON_RD(1, o1) FALCON_RD(2, o0) FALCON_RD(3, o1) FALCON_RD(4, o0) FALCON_RD(5, o1)
@@ -273,7 +273,10 @@ __device__ __forceinline__ void solve_block(PcSmem& sm, int w, int jl, int li, i
   // hazard checks cannot see.  With every operand and result register of the
   // MFMAs live until here, the allocator cannot give an asm output a register
   // an MFMA still reads or writes (unused result components would otherwise
-  // be free to it).
+  // be free to it).  The substitution and read statements depend on the MFMA
+  // results, so they follow the compiler's wait for them and may be scheduled
+  // freely (not volatile); the decay statements do not, so they stay
+  // volatile and in place before this point.
   asm volatile("" ::"v"(m_a0), "v"(m_a1), "v"(m_k0), "v"(m_k1), "v"(m_p0), "v"(m_p1), "v"(ek4), "v"(ep4));
   sm.ob[i][jl] = bf(o);
   // w to the end of this block: earlier entries decay by e^{g_last-g_carry},
@@ -473,8 +476,9 @@ hipError_t launch_chunked_percol(const ProblemArgs& a, hipStream_t st) {
   const int64_t BH = int64_t(a.B) * a.H;
   const int64_t nwg = (BH + 7) / 8 * 8 * (kD / kSlice);
   if (kBoundsCheck) {
-    // every (sequence, slice) exactly once, the slices of a sequence on one XCD
-    FALCON_HOST_CHECK(nwg <= INT32_MAX);
+    // every (sequence, slice) exactly once, the slices of a sequence on one XCD;
+    // chunk 0 is fetched before the chunk loop, so T > 0
+    FALCON_HOST_CHECK(a.T > 0 && nwg <= INT32_MAX);
     std::vector<int> seen(size_t(BH) * (kD / kSlice), 0);
     for (int64_t b = 0; b < nwg; ++b) {
       int64_t bh;
