@@ -194,6 +194,25 @@ def bench_decode(warmup=5):
     return attach_counters(out, "falcon1_decode_512x12_d128", ms)
 
 
+def warm(step, min_calls, seconds=0.3):
+    """Untimed warm-up of a leg beside the headline: at least min_calls calls
+    and at least `seconds` of wall time, so that the GPU's clocks have ramped
+    again after the host-side work between legs.  Returns the calls made."""
+    import time
+
+    import torch
+
+    n = 0
+    t0 = time.perf_counter()
+    while n < min_calls or time.perf_counter() - t0 < seconds:
+        step()
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
+
+
 def bench_chunked_workload(name, steps=20, warmup=3):
     """Another chunked workload (inputs resident in HBM), timed with HIP events
     on the launch stream; reported beside the headline line."""
@@ -215,9 +234,7 @@ def bench_chunked_workload(name, steps=20, warmup=3):
         fb.falcon_fwd_chunked(d["phi_k"], d["phi_q"], d["v"], d["beta"], d["lam"], variant=w.variant,
                               C=w.C, o=o, S_T=S_T, workspace=ws)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    calls = warm(step, warmup)
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -229,7 +246,8 @@ def bench_chunked_workload(name, steps=20, warmup=3):
     nbytes = algorithmic_bytes(w.B, w.H, w.T, w.dk, w.dv, io_bytes=4 if w.io_dtype == "f32" else 2,
                                per_column_beta=w.variant in ("falcon2", "falcon2a"))
     gbs = nbytes / (ms * 1e-3) / 1e9
-    out = {"workload": name, "variant": w.variant, "io": w.io_dtype, "steps": steps, "us_per_step": ms * 1e3,
+    out = {"workload": name, "variant": w.variant, "io": w.io_dtype, "steps": steps, "warmup_calls": calls,
+           "us_per_step": ms * 1e3,
            "tokens_per_s": w.B * w.T / (ms * 1e-3), "algorithmic_bytes": nbytes,
            "workspace_bytes": int(ws.numel()), "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
     if w.variant in ("falcon2", "falcon2a"):
@@ -282,9 +300,7 @@ def bench_recurrent(name="f1_chunked_8x12x2048_d64", steps=5, warmup=1):
         fb.falcon_fwd_recurrent(d["phi_k"], d["phi_q"], d["v"], d["beta"], d["lam"], variant=w.variant,
                                 o=o, S_T=S_T, eps=w.eps, eps_gamma=w.eps_gamma)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    calls = warm(step, warmup)
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -295,7 +311,8 @@ def bench_recurrent(name="f1_chunked_8x12x2048_d64", steps=5, warmup=1):
     ms = e0.elapsed_time(e1) / steps
     nbytes = algorithmic_bytes(w.B, w.H, w.T, w.dk, w.dv)
     gbs = nbytes / (ms * 1e-3) / 1e9
-    out = {"workload": name, "entry": "falcon_fwd_recurrent", "steps": steps, "us_per_step": ms * 1e3,
+    out = {"workload": name, "entry": "falcon_fwd_recurrent", "steps": steps, "warmup_calls": calls,
+           "us_per_step": ms * 1e3,
            "tokens_per_s": w.B * w.T / (ms * 1e-3), "algorithmic_bytes": nbytes, "hbm_gbs": gbs,
            "hbm_frac": gbs / HBM_PEAK_GBS,
            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -360,9 +377,7 @@ def bench_backward(name="f1_backward_8x12x2048_d64", steps=10, warmup=2):
                               dS_T=cot["dS_T"], eps=w.eps, eps_gamma=w.eps_gamma, grads=grads,
                               workspace=ws)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    calls = warm(step, warmup)
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -379,7 +394,7 @@ def bench_backward(name="f1_backward_8x12x2048_d64", steps=10, warmup=2):
     flops = 2.0 * algorithmic_flops(w.B, w.H, w.T, w.dk, w.dv, 32)
     design = backward_flops(w.B, w.H, w.T, w.dk, w.dv)
     tflops = flops / (ms * 1e-3) / 1e12
-    return {"workload": name, "steps": steps, "us_per_step": ms * 1e3,
+    return {"workload": name, "steps": steps, "warmup_calls": calls, "us_per_step": ms * 1e3,
             "tokens_per_s": w.B * w.T / (ms * 1e-3), "algorithmic_bytes": nbytes,
             "workspace_bytes": int(ws.numel()), "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
             "roofline": {"bound": "mfma", "achieved": tflops, "peak": FP32_MFMA_PEAK_TFLOPS,
@@ -587,8 +602,8 @@ LEGS = {
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
