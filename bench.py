@@ -42,6 +42,7 @@ PROFILE_SOURCES = {
     "falcon1_recurrent_8x12x2048_d64": [_CSRC + "falcon_recurrent.hip"],
     "falcon1_chunked_f32_8x12x2048_d64": [_CSRC + "falcon_generic_kernel.h", _CSRC + "falcon_chunked_generic.hip",
                                           _CSRC + "falcon_chunked_generic_c64.hip"],
+    "falcon1_backward_8x12x2048_d64": [_CSRC + "falcon_backward.hip"],
 }
 
 
@@ -394,7 +395,7 @@ def bench_backward(name="f1_backward_8x12x2048_d64", steps=10, warmup=2):
     flops = 2.0 * algorithmic_flops(w.B, w.H, w.T, w.dk, w.dv, 32)
     design = backward_flops(w.B, w.H, w.T, w.dk, w.dv)
     tflops = flops / (ms * 1e-3) / 1e12
-    return {"workload": name, "steps": steps, "warmup_calls": calls, "us_per_step": ms * 1e3,
+    out = {"workload": name, "steps": steps, "warmup_calls": calls, "us_per_step": ms * 1e3,
             "tokens_per_s": w.B * w.T / (ms * 1e-3), "algorithmic_bytes": nbytes,
             "workspace_bytes": int(ws.numel()), "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
             "roofline": {"bound": "mfma", "achieved": tflops, "peak": FP32_MFMA_PEAK_TFLOPS,
@@ -407,6 +408,7 @@ def bench_backward(name="f1_backward_8x12x2048_d64", steps=10, warmup=2):
             "flops_note": "roofline counts 2x the forward chunk form's algorithmic flops (C = 32); "
                           "design_flops adds the recomputed forward and the chain products the "
                           "implementation runs"}
+    return attach_counters(out, "falcon1_backward_8x12x2048_d64", ms)
 
 
 def oracle_sample(kind, budget_s=3.0):
