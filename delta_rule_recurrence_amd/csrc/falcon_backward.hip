@@ -58,7 +58,7 @@ constexpr int kOffPA = 0, kOffHD = 4096, kOffGD = 8192;
 constexpr int kMapFloats = 12288;
 // Per-chunk forward factors the maps kernel hands to the chunk kernel, row-major:
 // W [32][64], U [32][64], T [32][32], then the gates eta, g, gp, den, lam,
-// flags (int bits) [32] each and G.
+// flags (int bits), glo, gplo [32] each (G is g_31).
 constexpr int kFacW = 0, kFacU = 2048, kFacT = 4096, kFacGates = 5120;
 constexpr int kFacFloats = 5376;
 
@@ -212,14 +212,30 @@ struct __align__(16) ChunkCore {
   float W[kBC][kPW];
   float U[kBC][kPW];
   float KX[kBC][kPN];    // x_i . x_s
-  float AA[kBC][kPN];    // A, strictly lower; then T Diag(eta e^{gp})
+  float AA[kBC][kPN];    // A, strictly lower; then T Diag(eta e^{gp}) (chunk kernel: the pair-term prefixes PT)
   float TT[kBC][kPN];    // T = (I + A)^{-1}
   float MM[kBC][kPN];    // M, lower with the diagonal
   float ZZ[16][20];      // A21 T11
-  float en[kBC], eta[kBC], g[kBC], gp[kBC], lamv[kBC], den[kBC];
+  // log-decay prefixes g_i (through row i) and gp_i = g_{i-1}, each as a
+  // float pair hi + lo, lo the part the float sums dropped; G = g_31
+  float2 g[kBC], gp[kBC], G;
+  float en[kBC], eta[kBC], lamv[kBC], den[kBC];
   int flags[kBC];        // 1: eta from the formula, 2: the clamp binds, 4: live row
-  float G;
 };
+
+// Decays from the compensated prefixes (g = hi + lo, lo the part the float
+// sums dropped): e^{g_r - g_s} as e^{hi_r - hi_s} (1 + lo_r - lo_s), whose
+// hi difference rounds relative to itself, so a decay between nearby rows
+// keeps float accuracy however large the prefixes grow (a binding clamp adds
+// |log eps_gamma| per row); e^{g} likewise.
+__device__ __forceinline__ float dexp(float2 r, float2 s) {
+  const float e = __expf(r.x - s.x);
+  return fmaf(e, r.y - s.y, e);
+}
+__device__ __forceinline__ float eexp(float2 h) {
+  const float e = __expf(h.x);
+  return fmaf(e, h.y, e);
+}
 
 // Eight consecutive elements of a row (16-byte aligned), held as loaded and
 // widened to float only when used, so that every load of a phase can be
@@ -352,33 +368,46 @@ __device__ void chunk_forward(ChunkCore& cc, const BwdArgs& a, int c, int tid, i
       const float den = cc.en[i] + lamv + a.eps;
       const bool on = live && !(fresh && t == 0) && den != 0.0f;
       const float eta = on ? cc.den[i] / den : 0.0f;
+      // a binding clamp gives gamma = eps_gamma exactly (not 1 minus the
+      // float nearest 1 - eps_gamma)
       const float alpha = eta * lamv;
-      const bool clamped = alpha > 1.0f - a.eps_gamma;
-      lg = live ? log1pf(-fminf(alpha, 1.0f - a.eps_gamma)) : 0.0f;
+      const bool clamped = !(1.0f - alpha >= a.eps_gamma);
+      lg = live ? (clamped ? logf(a.eps_gamma) : log1pf(-alpha)) : 0.0f;
       cc.eta[i] = eta;
       cc.den[i] = den;
       cc.flags[i] = (on ? 1 : 0) | (clamped ? 2 : 0) | (live ? 4 : 0);
     }
-    float gi = lg;
+    // inclusive prefix over the chunk, compensated: each partial sum is
+    // carried as gi + ge, the rounding error of every addition (two-sum)
+    // going into ge
+    float gi = lg, ge = 0.f;
 #pragma unroll
     for (int d = 1; d < kBC; d <<= 1) {
-      const float n = __shfl_up(gi, d);
-      if (i >= d) gi += n;
+      const float n = __shfl_up(gi, d), ne = __shfl_up(ge, d);
+      if (i >= d) {
+        const float sum = gi + n;
+        const float nb = sum - gi;
+        const float err = (gi - (sum - nb)) + (n - nb);
+        gi = sum;
+        ge += ne + err;
+      }
     }
-    const float gpv = __shfl_up(gi, 1);
+    const float gpv = __shfl_up(gi, 1), gpe = __shfl_up(ge, 1);
     if (i < kBC) {
-      cc.g[i] = gi;
-      cc.gp[i] = i == 0 ? 0.f : gpv;
-      if (i == kBC - 1) cc.G = gi;
+      cc.g[i] = make_float2(gi, ge);
+      cc.gp[i] = i == 0 ? make_float2(0.f, 0.f) : make_float2(gpv, gpe);
+      if (i == kBC - 1) cc.G = make_float2(gi, ge);
     }
   }
   __syncthreads();
   // A = tril(Diag(eta) K o e^{gp_i - g_s}, -1), M = tril(Q X^T o e^{g_i - g_s})
   fk.store(w, l, [&](int r, int s, float v) {
     cc.KX[r][s] = v;
-    cc.AA[r][s] = s < r ? cc.eta[r] * __expf(cc.gp[r] - cc.g[s]) * v : 0.f;
+    cc.AA[r][s] = s < r ? cc.eta[r] * dexp(cc.gp[r], cc.g[s]) * v : 0.f;
   });
-  fm.store(w, l, [&](int r, int s, float v) { cc.MM[r][s] = s <= r ? __expf(cc.g[r] - cc.g[s]) * v : 0.f; });
+  fm.store(w, l, [&](int r, int s, float v) {
+    cc.MM[r][s] = s <= r ? dexp(cc.g[r], cc.g[s]) * v : 0.f;
+  });
   __syncthreads();
   // T11, T22 by substitution: lane j solves (I + A_bb) t = e_jj, b = j / 16
   if (tid < kBC) {
@@ -426,7 +455,7 @@ __device__ void chunk_factors(ChunkCore& cc, float (*TZ)[kPN], int tid, int w, i
   for (int e = tid; e < kBC * kBC; e += kThreads) {
     const int i = e >> 5, s = e & 31;
     const float t = cc.TT[i][s];
-    cc.AA[i][s] = t * cc.eta[s] * __expf(cc.gp[s]);
+    cc.AA[i][s] = t * cc.eta[s] * eexp(cc.gp[s]);
     TZ[i][s] = t * cc.eta[s];
   }
   __syncthreads();
@@ -503,17 +532,18 @@ falcon1_bwd_maps_kernel(BwdArgs a, int total) {
       const int i = tid >> 3, f = 4 * (tid & 7);
       reinterpret_cast<float4*>(fo + kFacT)[tid] = *reinterpret_cast<const float4*>(&cc.TT[i][f]);
     }
-    if (tid < 193) {
+    {
       const int k = tid >> 5, i = tid & 31;
       float v;
       switch (k) {
         case 0: v = cc.eta[i]; break;
-        case 1: v = cc.g[i]; break;
-        case 2: v = cc.gp[i]; break;
+        case 1: v = cc.g[i].x; break;
+        case 2: v = cc.gp[i].x; break;
         case 3: v = cc.den[i]; break;
         case 4: v = cc.lamv[i]; break;
         case 5: v = __int_as_float(cc.flags[i]); break;
-        default: v = cc.G; break;
+        case 6: v = cc.g[i].y; break;
+        default: v = cc.gp[i].y; break;
       }
       fo[kFacGates + tid] = v;
     }
@@ -524,15 +554,15 @@ falcon1_bwd_maps_kernel(BwdArgs a, int total) {
   static_assert(offsetof(ChunkCore, AA) == offsetof(ChunkCore, KX) + sizeof(cc.KX), "KX, AA not adjacent");
   // Qt = Diag(e^g) Q - M W
   mm<kBC, kD, kBC, false, false>(&cc.MM[0][0], kPN, &cc.W[0][0], kPW, w, l, [&](int r, int s, float v) {
-    QT[r][s] = __expf(cc.g[r]) * cc.Q[r][s] - v;
+    QT[r][s] = eexp(cc.g[r]) * cc.Q[r][s] - v;
   });
   __syncthreads();
   // P^T = e^G I - W^T Diag(e^{G-g}) X, H = X^T Diag(e^{G-g}) U and
   // G^T = dO^T Qt, each written straight from the accumulators: the tile
   // (tm, tn) of a wave is one 1 KiB run of its map.
   float* out = a.maps + int64_t(job) * kMapFloats;
-  const float eG = __expf(cc.G);
-  auto xs = [&](int t) { return __expf(cc.G - cc.g[t]); };
+  const float eG = eexp(cc.G);
+  auto xs = [&](int t) { return dexp(cc.G, cc.g[t]); };
   auto one = [](int) { return 1.f; };
   auto put = [&](float* base, int idx, const f32x4& v) {
     reinterpret_cast<float4*>(base)[idx] = make_float4(v[0], v[1], v[2], v[3]);
@@ -769,7 +799,7 @@ struct __align__(16) GradSmem {
   float DXH[kBC][kPW];   // dXh
   float DM[kBC][kPN];    // T Diag(eta); then dM o D; then D2 = dA o e^{gp_i - g_s}
   float QX[kBC][kPN];    // q_i . x_s
-  float dg[kBC], dgp[kBC], deta[kBC], dgt[kBC];
+  float dg[kBC], dgp[kBC], deta[kBC], dgt[kBC];   // dgt: the Xh terms
   float trp[kWaves3];
 };
 
@@ -780,6 +810,22 @@ __device__ __forceinline__ float sum16(float v) {
   v += __shfl_xor(v, 4);
   v += __shfl_xor(v, 8);
   return v;
+}
+
+// The value of the lane N places lower in the same sixteen-lane DPP row, 0
+// for the first N lanes of the row.
+template <int N>
+__device__ __forceinline__ float row_shr(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x110 + N, 0xf, 0xf, true));
+}
+
+// Exclusive prefix sum over the sixteen lanes of a row.
+__device__ __forceinline__ float excl16(float v) {
+  v += row_shr<1>(v);
+  v += row_shr<2>(v);
+  v += row_shr<4>(v);
+  v += row_shr<8>(v);
+  return row_shr<1>(v);
 }
 
 // This thread's share of one chunk's inputs, held as loaded.  Waves 0-3 take
@@ -838,17 +884,21 @@ __device__ __forceinline__ void grad_store(GradSmem& sm, const GradRegs<IO>& g, 
     *reinterpret_cast<float4*>(&cc.U[i][f]) = g.uf;
     if (w < 4) {
       *reinterpret_cast<float4*>(&cc.TT[u >> 3][4 * (u & 7)]) = g.tf;
-      if (u < 193) {
+      {
         const int k = u >> 5, r = u & 31;
         switch (k) {
           case 0: cc.eta[r] = g.gf; break;
-          case 1: cc.g[r] = g.gf; break;
-          case 2: cc.gp[r] = g.gf; break;
+          case 1: cc.g[r].x = g.gf; break;
+          case 2: cc.gp[r].x = g.gf; break;
           case 3: cc.den[r] = g.gf; break;
           case 4: cc.lamv[r] = g.gf; break;
           case 5: cc.flags[r] = __float_as_int(g.gf); break;
-          default: cc.G = g.gf; break;
+          case 6: cc.g[r].y = g.gf; break;
+          default: cc.gp[r].y = g.gf; break;
         }
+        // g_31 is G
+        if (k == 1 && r == kBC - 1) cc.G.x = g.gf;
+        if (k == 6 && r == kBC - 1) cc.G.y = g.gf;
       }
     }
   }
@@ -919,13 +969,13 @@ __global__ void __launch_bounds__(kThreads3) falcon1_bwd_chunk_kernel(BwdArgs a,
     } else {
       f.store(w & 3, l, [&](int r, int s2, float v) {
         sm.QX[r][s2] = v;
-        cc.MM[r][s2] = s2 <= r ? __expf(cc.g[r] - cc.g[s2]) * v : 0.f;
+        cc.MM[r][s2] = s2 <= r ? dexp(cc.g[r], cc.g[s2]) * v : 0.f;
       });
     }
   }
   __syncthreads();
-  const float eG = __expf(cc.G);
-  auto xs = [&](int i) { return __expf(cc.G - cc.g[i]); };
+  const float eG = eexp(cc.G);
+  auto xs = [&](int i) { return dexp(cc.G, cc.g[i]); };
   {
     // Xh Lam (into DW), dU = Xh Lam + M^T dO, R = U - W S_c, dQt = dO S_c^T
     Mm<kBC, kD, kD, false, false, kWaves3> fxl, fws;
@@ -967,15 +1017,25 @@ __global__ void __launch_bounds__(kThreads3) falcon1_bwd_chunk_kernel(BwdArgs a,
     // dM o D, D_{is} = e^{g_i-g_s} for s <= i
     if (w >= 4)
       fmx.store(w & 3, l, [&](int r, int s, float v) {
-        sm.DM[r][s] = s <= r ? (sm.DM[r][s] + v) * __expf(cc.g[r] - cc.g[s]) : 0.f;
+        sm.DM[r][s] = s <= r ? (sm.DM[r][s] + v) * dexp(cc.g[r], cc.g[s]) : 0.f;
       });
   }
   __syncthreads();
   {
-    // decay terms of M, Qt and Xh (sixteen lanes per row); with M = (Q X^T) o D,
-    // dM o M summed over a row or a column is (dM o D) o (Q X^T)
-    const int i = ri;
-    float qd = 0.f, xd = 0.f, rowm = 0.f, colm = 0.f;
+    // decay terms of M, Qt and Xh (sixteen lanes per row).  The gradient of
+    // the log decay of row i takes, from each decayed product, only the terms
+    // whose decay spans row i, each of which carries gamma_i: from Qt rows
+    // r >= i, from Xh rows r < i, from M (and later A) the pairs s < i <= r.
+    // Summed that way it keeps float accuracy relative to gamma_i, which the
+    // division by gamma_i in the gate step needs; totals of a row minus a
+    // column would cancel O(1) terms.  For M the pair term is
+    // dM o M = (dM o D) o (Q X^T); each row r turns its strictly lower part
+    // into exclusive prefixes along the row, stored transposed in PT (the
+    // chunk kernel leaves A's array unused), so that row i of PT summed over
+    // columns r >= i is the M share of row i.
+    float (*PT)[kPN] = cc.AA;
+    const int i = ri, s0 = 2 * rp;
+    float qd = 0.f, xd = 0.f;
     {
       const float4 q4 = *reinterpret_cast<const float4*>(&cc.Q[i][4 * rp]);
       const float4 t4 = *reinterpret_cast<const float4*>(&sm.DQT[i][4 * rp]);
@@ -984,17 +1044,15 @@ __global__ void __launch_bounds__(kThreads3) falcon1_bwd_chunk_kernel(BwdArgs a,
       qd = q4.x * t4.x + q4.y * t4.y + q4.z * t4.z + q4.w * t4.w;
       xd = x4.x * h4.x + x4.y * h4.y + x4.z * h4.z + x4.w * h4.w;
     }
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int s2 = 2 * rp + k;
-      rowm = fmaf(sm.DM[i][s2], sm.QX[i][s2], rowm);
-      colm = fmaf(sm.DM[s2][i], sm.QX[s2][i], colm);
-    }
-    qd = sum16(qd); xd = sum16(xd); rowm = sum16(rowm); colm = sum16(colm);
+    const float w0 = s0 < i ? sm.DM[i][s0] * sm.QX[i][s0] : 0.f;
+    const float w1 = s0 + 1 < i ? sm.DM[i][s0 + 1] * sm.QX[i][s0 + 1] : 0.f;
+    const float ex = excl16(w0 + w1);
+    PT[s0][i] = ex;
+    PT[s0 + 1][i] = ex + w0;
+    qd = sum16(qd); xd = sum16(xd);
     if (rp == 0) {
-      const float z = xs(i) * xd;
-      sm.dg[i] = __expf(cc.g[i]) * qd + rowm - colm - z;
-      sm.dgt[i] = z;
+      sm.dg[i] = eexp(cc.g[i]) * qd;
+      sm.dgt[i] = xs(i) * xd;
     }
   }
   // dQ = Diag(e^g) dQt + (dM o D) X;  dX = Diag(e^{G-g}) dXh + (dM o D)^T Q
@@ -1007,7 +1065,7 @@ __global__ void __launch_bounds__(kThreads3) falcon1_bwd_chunk_kernel(BwdArgs a,
     fq.run();
     fx.run();
     fq.store(w, l, [&](int r, int s2, float v) {
-      if (t0 + r < T) dq_out[int64_t(t0 + r) * kD + s2] = __expf(cc.g[r]) * sm.DQT[r][s2] + v;
+      if (t0 + r < T) dq_out[int64_t(t0 + r) * kD + s2] = eexp(cc.g[r]) * sm.DQT[r][s2] + v;
     });
     fx.store(w, l, [&](int r, int s2, float v) { sm.RR[r][s2] = xs(r) * sm.DXH[r][s2] + v; });
   }
@@ -1036,7 +1094,7 @@ __global__ void __launch_bounds__(kThreads3) falcon1_bwd_chunk_kernel(BwdArgs a,
     // dV = Diag(eta) dZ, and the eta / gp terms
     {
       const int i = ri, f = 4 * rp;
-      const float egp = __expf(cc.gp[i]), eta = cc.eta[i];
+      const float egp = eexp(cc.gp[i]), eta = cc.eta[i];
       const float4 dy = *reinterpret_cast<const float4*>(&DY[i][f]);
       const float4 dz = *reinterpret_cast<const float4*>(&DZ[i][f]);
       const float4 x = *reinterpret_cast<const float4*>(&cc.X[i][f]);
@@ -1062,25 +1120,29 @@ __global__ void __launch_bounds__(kThreads3) falcon1_bwd_chunk_kernel(BwdArgs a,
     // A_{is} = eta_i e^{gp_i-g_s} k_{is}: D2 = dA o e^{gp_i-g_s} (s < i)
     if (w >= 4)
       fa.store(w & 3, l, [&](int r, int s2, float v) {
-        sm.DM[r][s2] = s2 < r ? (sm.DM[r][s2] - v) * __expf(cc.gp[r] - cc.g[s2]) : 0.f;
+        sm.DM[r][s2] = s2 < r ? (sm.DM[r][s2] - v) * dexp(cc.gp[r], cc.g[s2]) : 0.f;
       });
   }
   __syncthreads();
   {
-    const int i = ri;
-    float row = 0.f, col = 0.f;
+    // eta_i's share of A, and A's pair terms eta_i D2 o K for s < i' < i,
+    // added as exclusive row prefixes into PT (entries s < i)
+    float (*PT)[kPN] = cc.AA;
+    const int i = ri, s0 = 2 * rp;
+    const float eta = cc.eta[i];
+    float row = 0.f, wa[2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const int s2 = 2 * rp + k;
-      row = fmaf(sm.DM[i][s2], cc.KX[i][s2], row);
-      col = fmaf(cc.eta[s2] * sm.DM[s2][i], cc.KX[s2][i], col);
+      const int s2 = s0 + k;
+      const float p = sm.DM[i][s2] * cc.KX[i][s2];
+      row += p;
+      wa[k] = s2 < i ? eta * p : 0.f;
     }
-    row = sum16(row); col = sum16(col);
-    if (rp == 0) {
-      sm.deta[i] += row;
-      sm.dgp[i] += cc.eta[i] * row;
-      sm.dg[i] -= col;
-    }
+    const float ex = excl16(wa[0] + wa[1]);
+    if (s0 < i) PT[s0][i] += ex;
+    if (s0 + 1 < i) PT[s0 + 1][i] += ex + wa[0];
+    row = sum16(row);
+    if (rp == 0) sm.deta[i] += row;
   }
   {
     // dK = Diag(eta) D2 (strictly lower): dX += dK X + dK^T X = Diag(eta) D2 X + D2^T Diag(eta) X
@@ -1097,23 +1159,45 @@ __global__ void __launch_bounds__(kThreads3) falcon1_bwd_chunk_kernel(BwdArgs a,
   // gates: g -> log decay -> (eta, lam); eta -> (beta, lam, ||x||^2)
   if (w == 0) {
     const int i = l;
-    float dgt = 0.f;
+    // the pair terms of M and A spanning row c: row c of PT over the columns
+    // r >= c, lanes c and c + 32 taking columns 0-15 and 16-31
+    float pairs = 0.f;
+    {
+      const int c = l & 31, r0 = (l >> 5) * 16;
+      const float4* pt = reinterpret_cast<const float4*>(&cc.AA[c][r0]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float4 v = pt[k];
+        const int r = r0 + 4 * k;
+        pairs += (r >= c ? v.x : 0.f) + (r + 1 >= c ? v.y : 0.f) + (r + 2 >= c ? v.z : 0.f) +
+                 (r + 3 >= c ? v.w : 0.f);
+      }
+      pairs += __shfl_xor(pairs, 32);
+    }
+    float dgt = 0.f, z = 0.f;
     if (i < kBC) {
       float dG = 0.f;
       if (i == kBC - 1) {
-        float zs = 0.f, tr = 0.f;
-        for (int r = 0; r < kBC; ++r) zs += sm.dgt[r];
+        float tr = 0.f;
         for (int r = 0; r < kWaves3; ++r) tr += sm.trp[r];
-        dG = eG * tr + zs;
+        dG = eG * tr;
       }
       dgt = sm.dg[i] + (i + 1 < kBC ? sm.dgp[i + 1] : 0.f) + dG;
+      z = sm.dgt[i];
     }
-    // suffix sums over the chunk: dlg_i = sum_{r >= i} dgt_r
+    // dlg_i: the Qt, Y and state terms of rows r >= i (suffix sums), the Xh
+    // terms of rows r < i (exclusive prefix sums) and the pair terms
     float dlg = dgt;
 #pragma unroll
     for (int d = 1; d < kBC; d <<= 1) {
       const float n = __shfl_down(dlg, d);
       if (i + d < kBC) dlg += n;
+      const float m = __shfl_up(z, d);
+      if (i >= d) z += m;
+    }
+    {
+      const float zb = __shfl_up(z, 1);
+      dlg += (i == 0 ? 0.f : zb) + pairs;
     }
     if (i < kBC) {
       const int fl = cc.flags[i];

@@ -84,8 +84,11 @@ constexpr float kLog2e = 1.4426950408889634f;
 // exact), which keeps the hardware log and reciprocal out of a lane-masked
 // branch.
 __device__ __forceinline__ float log2_gamma(float eta, float lam, float eps_gamma, float& gamma) {
-  const float alpha = fminf(eta * lam, 1.0f - eps_gamma);
-  const float u = 1.0f - alpha;
+  // a binding clamp takes u = eps_gamma exactly and alpha = 1 - u (ratio 1)
+  const float a = eta * lam;
+  const bool unclamped = 1.0f - a >= eps_gamma;
+  const float u = unclamped ? 1.0f - a : eps_gamma;
+  const float alpha = unclamped ? a : 1.0f - u;
   const float d = u - 1.0f;
   gamma = u;
   const float tiny = d == 0.0f ? 1.0f : 0.0f;

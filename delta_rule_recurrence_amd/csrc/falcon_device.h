@@ -48,14 +48,19 @@ __device__ __forceinline__ float nlms_eta(float beta, float energy, float lam, f
   const float denom = energy + lam + eps;
   return (sentinel || denom == 0.0f) ? 0.0f : beta / denom;
 }
-// alpha = min(eta lam, 1 - eps_gamma); returns gamma = 1 - alpha
-// (Section 4.3 "Decay positivity").
+// gamma = 1 - min(eta lam, 1 - eps_gamma) (Section 4.3 "Decay positivity"),
+// formed as max(1 - eta lam, eps_gamma): the same number, but a binding
+// clamp yields eps_gamma itself, where 1 minus the float nearest 1 - eps_gamma
+// would be off by up to 5 % at eps_gamma = 1e-6 (1 - alpha is exact for
+// alpha in [0.5, 2]).
 __device__ __forceinline__ float clamped_gamma(float eta, float lam, float eps_gamma) {
-  return 1.0f - fminf(eta * lam, 1.0f - eps_gamma);
+  return fmaxf(1.0f - eta * lam, eps_gamma);
 }
-// log gamma in float32 as log1p(-alpha) (Section 4.3).
+// log gamma in float32: log1p(-alpha), or log eps_gamma where the clamp binds
+// (Section 4.3).
 __device__ __forceinline__ float clamped_log_gamma(float eta, float lam, float eps_gamma) {
-  return log1pf(-fminf(eta * lam, 1.0f - eps_gamma));
+  const float a = eta * lam;
+  return 1.0f - a >= eps_gamma ? log1pf(-a) : logf(eps_gamma);
 }
 
 }  // namespace falcon

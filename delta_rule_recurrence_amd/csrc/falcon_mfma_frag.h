@@ -129,8 +129,12 @@ __device__ __forceinline__ void lower_tile(int n, int& ib, int& sb) {
 // keeps its relative accuracy; ln is the hardware log2 times ln 2, and the
 // division a hardware reciprocal (a few ulp in all).
 __device__ __forceinline__ float fast_log_gamma(float eta, float lam, float eps_gamma) {
-  const float alpha = fminf(eta * lam, 1.0f - eps_gamma);
-  const float u = 1.0f - alpha;
+  // a binding clamp takes u = eps_gamma exactly and alpha = 1 - u, so that
+  // the ratio below is 1 and the result log eps_gamma
+  const float a = eta * lam;
+  const bool unclamped = 1.0f - a >= eps_gamma;
+  const float u = unclamped ? 1.0f - a : eps_gamma;
+  const float alpha = unclamped ? a : 1.0f - u;
   const float d = u - 1.0f;
   return d == 0.0f ? -alpha
                    : __builtin_amdgcn_logf(u) * 0.6931471805599453f * (-alpha * __builtin_amdgcn_rcpf(d));
