@@ -35,14 +35,16 @@ STEP_KERNELS = ["zero_ints_kernel", "falcon1_fused_kernel"]
 _CSRC = "delta_rule_recurrence_amd/csrc/"
 PROFILE_SOURCES = {
     "falcon1_chunked_8x12x2048_d64": [_CSRC + "falcon_chunked_wy.hip", _CSRC + "falcon_mfma_frag.h",
-                                      _CSRC + "falcon_chunked.hip"],
-    "falcon1a_chunked_2x12x16384_d64": [_CSRC + "falcon_chunked_scan.hip", _CSRC + "falcon_mfma_frag.h"],
-    "falcon2_chunked_8x12x2048_d64": [_CSRC + "falcon_chunked_percol.hip", _CSRC + "falcon_mfma_frag.h"],
-    "falcon1_decode_512x12_d128": [_CSRC + "falcon_recurrent.hip"],
-    "falcon1_recurrent_8x12x2048_d64": [_CSRC + "falcon_recurrent.hip"],
+                                      _CSRC + "falcon_chunked.hip", _CSRC + "falcon_device.h"],
+    "falcon1a_chunked_2x12x16384_d64": [_CSRC + "falcon_chunked_scan.hip", _CSRC + "falcon_mfma_frag.h",
+                                        _CSRC + "falcon_device.h"],
+    "falcon2_chunked_8x12x2048_d64": [_CSRC + "falcon_chunked_percol.hip", _CSRC + "falcon_mfma_frag.h",
+                                      _CSRC + "falcon_device.h"],
+    "falcon1_decode_512x12_d128": [_CSRC + "falcon_recurrent.hip", _CSRC + "falcon_device.h"],
+    "falcon1_recurrent_8x12x2048_d64": [_CSRC + "falcon_recurrent.hip", _CSRC + "falcon_device.h"],
     "falcon1_chunked_f32_8x12x2048_d64": [_CSRC + "falcon_generic_kernel.h", _CSRC + "falcon_chunked_generic.hip",
-                                          _CSRC + "falcon_chunked_generic_c64.hip"],
-    "falcon1_backward_8x12x2048_d64": [_CSRC + "falcon_backward.hip"],
+                                          _CSRC + "falcon_chunked_generic_c64.hip", _CSRC + "falcon_device.h"],
+    "falcon1_backward_8x12x2048_d64": [_CSRC + "falcon_backward.hip", _CSRC + "falcon_device.h"],
 }
 
 
