@@ -45,6 +45,10 @@ constexpr int kD = 64;
 constexpr int kSlice = 16;                  // value columns per workgroup
 constexpr int kThreads = 256;
 constexpr int kDP = 20;                     // float row pitch of the diagonal Gram blocks (16-byte reads conflict-free)
+// Float pitch of the per-column arrays, stored column by column: a solve
+// read of row 16B + li in column 4w + g lands in bank 16g + li (+ const),
+// so the 64 lanes of a wave hit 64 distinct banks.
+constexpr int kWP = kC + 16;
 
 struct PcSmem {
   uint16_t x[kC * kD];                      // keys phi(k_{t0+r-1}), swizzled rows
@@ -53,14 +57,14 @@ struct PcSmem {
   float pqd[4][16][kDP];                    // diagonal blocks: [b][i-16b][s-16b] = q_i . x_s for s < i, else 0
   uint16_t kqf[3][2][64 * 8];               // frag(KQ)[b][m] for b = 1..3, entries s < 16 b only, bf16
   uint16_t pqf[3][2][64 * 8];               // frag(PQ)[b][m], same
-  float xs[kC][kSlice];                     // (X S)_{i,j}
-  float qs[kC][kSlice];                     // (Q S)_{i,j}
-  float vb[kC][kSlice];                     // v_{i,j}
-  float bt[kC][kSlice];                     // beta_{i,j}
+  float xs[kSlice][kWP];                    // (X S)_{i,j} at [j][i]
+  float qs[kSlice][kWP];                    // (Q S)_{i,j} at [j][i]
+  float vb[kSlice][kWP];                    // v_{i,j} at [j][i]
+  float bt[kSlice][kWP];                    // beta_{i,j} at [j][i]
   float lm[kC];                             // lam_i
   float en[kC];                             // ||x_i||^2
   float pd[kC];                             // q_i . x_i
-  float w[kSlice][kC];                      // per column: e^{g_b-g_s} rho_s, b = end of the last solved block
+  float w[kSlice][kWP];                     // per column: e^{g_b-g_s} rho_s, b = end of the last solved block
   float e63[kSlice];                        // e^{g_63} per column
   uint16_t ob[kC][kSlice];                  // outputs of the chunk, bf16
 };
@@ -140,9 +144,15 @@ __device__ __forceinline__ void stage_chunk(PcSmem& sm, const ChunkRegs& R, int 
   if (tid < 128) {
     const int r = tid >> 1;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sm.vb[r][8 * (tid & 1) + e] = static_cast<float>(R.v[e]);
+    for (int e = 0; e < 8; ++e) sm.vb[8 * (tid & 1) + e][r] = static_cast<float>(R.v[e]);
   }
-  *reinterpret_cast<float4*>(&sm.bt[tid >> 2][4 * (tid & 3)]) = R.bt;
+  {
+    const int r = tid >> 2, j = 4 * (tid & 3);
+    sm.bt[j][r] = R.bt.x;
+    sm.bt[j + 1][r] = R.bt.y;
+    sm.bt[j + 2][r] = R.bt.z;
+    sm.bt[j + 3][r] = R.bt.w;
+  }
   if (tid < 64) sm.lm[tid] = R.lm;
 }
 
@@ -159,7 +169,7 @@ __device__ __forceinline__ void solve_block(PcSmem& sm, int w, int jl, int li, i
   // step size and decay of row i in column jl (branch-free: every operand is
   // loaded and the reciprocal taken whatever the row); g by a scan over the
   // 16 rows
-  const float lmi = sm.lm[i], bti = sm.bt[i][jl];
+  const float lmi = sm.lm[i], bti = sm.bt[jl][i];
   const float den = sm.en[i] + lmi + eps;
   const bool on = live && !(fresh && t == 0) && den != 0.0f;
   const float eta = on ? bti * __builtin_amdgcn_rcpf(on ? den : 1.0f) : 0.0f;
@@ -177,8 +187,8 @@ __device__ __forceinline__ void solve_block(PcSmem& sm, int w, int jl, int li, i
   const float gprev = li == 0 ? gcarry : gsh;
   const float glast = row_bcast<15>(gi);
   // earlier blocks, through w_s = e^{g_{16B-1}-g_s} rho_s
-  float a = kReg ? eta * (sm.vb[i][jl] - exp2_fast(gprev) * sm.xs[i][jl]) : eta * sm.vb[i][jl];
-  float o = exp2_fast(gi) * sm.qs[i][jl];
+  float a = kReg ? eta * (sm.vb[jl][i] - exp2_fast(gprev) * sm.xs[jl][i]) : eta * sm.vb[jl][i];
+  float o = exp2_fast(gi) * sm.qs[jl][i];
   // operands and results of the earlier-block MFMAs, kept live (below) past
   // every inline-asm statement of the block
   bf16x8 m_a0 = {}, m_a1 = {}, m_k0 = {}, m_k1 = {}, m_p0 = {}, m_p1 = {};
@@ -339,14 +349,13 @@ falcon2_chunked_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restric
   const int nchunks = (T + kC - 1) / kC;
   // the earlier-block products read whole rows of w, solved or not: start
   // them at zero (never NaN), later chunks leave finite values behind
-  for (int e = tid; e < kSlice * kC; e += kThreads) (&sm.w[0][0])[e] = 0.0f;
+  for (int e = tid; e < kSlice * kWP; e += kThreads) (&sm.w[0][0])[e] = 0.0f;
   ChunkRegs R;
   fetch_chunk(R, K, Q, V, Bt, Lm, kp, T, 0, j0, tid);
   for (int c = 0; c < nchunks; ++c) {
     const int t0 = c * kC;
     stage_chunk(sm, R, tid);
     __syncthreads();
-    if (c + 1 < nchunks) fetch_chunk(R, K, Q, V, Bt, Lm, kp, T, t0 + kC, j0, tid);
     // ---- products shared by all columns, on the matrix cores ---------------
     if (w == 0) {
       // X S and Q S for the slice: lane holds rows 16ib+4g+r, column j0+c16
@@ -362,11 +371,9 @@ falcon2_chunked_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restric
           ax = mfma32(ring_frag_p(sm.x, i, 0, g), s0, ax);
           ax = mfma32(ring_frag_p(sm.x, i, 1, g), s1, ax);
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          sm.qs[16 * ib + 4 * g + r][c16] = aq[r];
-          if (kReg) sm.xs[16 * ib + 4 * g + r][c16] = ax[r];
-        }
+        // rows 16ib+4g .. +3 of column c16 are contiguous: one 16-byte store each
+        *reinterpret_cast<f32x4*>(&sm.qs[c16][16 * ib + 4 * g]) = aq;
+        if (kReg) *reinterpret_cast<f32x4*>(&sm.xs[c16][16 * ib + 4 * g]) = ax;
       }
     } else {
       // Waves 1..3: the diagonal Gram and read blocks in float32 (lane holds
@@ -424,6 +431,10 @@ falcon2_chunked_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restric
     {
       float gcarry = 0.f;
       solve_block<kReg, 0>(sm, w, jl, li, t0, T, fresh, eps, eps_gamma, gcarry);
+      // the next chunk's rows: issued here, among the solve's dependent
+      // chains, rather than beside the products, where the four waves' loads
+      // queue for the memory pipeline at once
+      if (c + 1 < nchunks) fetch_chunk(R, K, Q, V, Bt, Lm, kp, T, t0 + kC, j0, tid);
       solve_block<kReg, 1>(sm, w, jl, li, t0, T, fresh, eps, eps_gamma, gcarry);
       solve_block<kReg, 2>(sm, w, jl, li, t0, T, fresh, eps, eps_gamma, gcarry);
       solve_block<kReg, 3>(sm, w, jl, li, t0, T, fresh, eps, eps_gamma, gcarry);
