@@ -45,28 +45,30 @@ constexpr int kD = 64;
 constexpr int kSlice = 16;                  // value columns per workgroup
 constexpr int kThreads = 256;
 constexpr int kDP = 20;                     // float row pitch of the diagonal Gram blocks (16-byte reads conflict-free)
-// Float pitch of the per-column arrays, stored column by column: a solve
-// read of row 16B + li in column 4w + g lands in bank 16g + li (+ const),
-// so the 64 lanes of a wave hit 64 distinct banks.
-constexpr int kWP = kC + 16;
+constexpr int kSbP = 72;                    // bf16 pitch of the state copy sb
+
+// Per-column arrays hold kSlice columns of kC rows, column by column, row i
+// of column j at j kC + (i ^ 16 (j & 3)): a solve read of row 16B + li in
+// column 4w + g lands in bank 16 (B ^ g) + li, so the 64 lanes of a wave hit
+// 64 distinct banks, and every aligned run of four rows stays contiguous.
+__device__ __forceinline__ int cix(int j, int i) { return j * kC + (i ^ ((j & 3) << 4)); }
 
 struct PcSmem {
-  uint16_t x[kC * kD];                      // keys phi(k_{t0+r-1}), swizzled rows
-  uint16_t q[kC * kD];                      // queries, swizzled rows
+  uint16_t x[2][kC * kD];                   // keys phi(k_{t0+r-1}), swizzled rows, of two chunks
+  uint16_t q[2][kC * kD];                   // queries, swizzled rows, of two chunks
   float kqd[4][16][kDP];                    // diagonal blocks: [b][i-16b][s-16b] = x_i . x_s for s < i, else 0
   float pqd[4][16][kDP];                    // diagonal blocks: [b][i-16b][s-16b] = q_i . x_s for s < i, else 0
   uint16_t kqf[3][2][64 * 8];               // frag(KQ)[b][m] for b = 1..3, entries s < 16 b only, bf16
   uint16_t pqf[3][2][64 * 8];               // frag(PQ)[b][m], same
-  float xs[kSlice][kWP];                    // (X S)_{i,j} at [j][i]
-  float qs[kSlice][kWP];                    // (Q S)_{i,j} at [j][i]
-  float vb[kSlice][kWP];                    // v_{i,j} at [j][i]
-  float bt[kSlice][kWP];                    // beta_{i,j} at [j][i]
+  float vb[kSlice * kC];                    // v_{i,j} at cix(j, i)
+  float bt[kSlice * kC];                    // beta_{i,j} at cix(j, i)
   float lm[kC];                             // lam_i
   float en[kC];                             // ||x_i||^2
   float pd[kC];                             // q_i . x_i
-  float w[kSlice][kWP];                     // per column: e^{g_b-g_s} rho_s, b = end of the last solved block
+  float w[kSlice * kC];                     // per column j: e^{g_b-g_s} rho_s at cix(j, s), b = end of the last solved block
   float e63[kSlice];                        // e^{g_63} per column
   uint16_t ob[kC][kSlice];                  // outputs of the chunk, bf16
+  uint16_t sb[kSlice][kSbP];                // the slice's state in bf16, column by column: sb[j][k] = S[k][j0 + j]
 };
 
 // Lane N of the lane's 16-lane row (DPP row_newbcast; every lane has a
@@ -133,25 +135,30 @@ __device__ __forceinline__ void fetch_chunk(ChunkRegs& R, const bf16_t* K, const
   if (tid < 64) R.lm = Lm[t0 + tid < T ? t0 + tid : T - 1];
 }
 
-__device__ __forceinline__ void stage_chunk(PcSmem& sm, const ChunkRegs& R, int tid) {
+// A chunk's keys and queries into one of the two row buffers.
+__device__ __forceinline__ void stage_xq(uint16_t* xb, uint16_t* qb, const ChunkRegs& R, int tid) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int r = 32 * j + (tid >> 3);
     const int off = r * kD + 8 * seg_pos(r, tid & 7);
-    *reinterpret_cast<bf16x8*>(sm.x + off) = R.x[j];
-    *reinterpret_cast<bf16x8*>(sm.q + off) = R.q[j];
+    *reinterpret_cast<bf16x8*>(xb + off) = R.x[j];
+    *reinterpret_cast<bf16x8*>(qb + off) = R.q[j];
   }
+}
+
+// A chunk's values, beta and lam.
+__device__ __forceinline__ void stage_gates(PcSmem& sm, const ChunkRegs& R, int tid) {
   if (tid < 128) {
     const int r = tid >> 1;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sm.vb[8 * (tid & 1) + e][r] = static_cast<float>(R.v[e]);
+    for (int e = 0; e < 8; ++e) sm.vb[cix(8 * (tid & 1) + e, r)] = static_cast<float>(R.v[e]);
   }
   {
     const int r = tid >> 2, j = 4 * (tid & 3);
-    sm.bt[j][r] = R.bt.x;
-    sm.bt[j + 1][r] = R.bt.y;
-    sm.bt[j + 2][r] = R.bt.z;
-    sm.bt[j + 3][r] = R.bt.w;
+    sm.bt[cix(j, r)] = R.bt.x;
+    sm.bt[cix(j + 1, r)] = R.bt.y;
+    sm.bt[cix(j + 2, r)] = R.bt.z;
+    sm.bt[cix(j + 3, r)] = R.bt.w;
   }
   if (tid < 64) sm.lm[tid] = R.lm;
 }
@@ -161,15 +168,32 @@ __device__ __forceinline__ void stage_chunk(PcSmem& sm, const ChunkRegs& R, int 
 // decay is one exp2.  gcarry holds g at the end of the previous block (0
 // before block 0) and is advanced to the end of this one.
 template <bool kReg, int B>
-__device__ __forceinline__ void solve_block(PcSmem& sm, int w, int jl, int li, int t0, int T, bool fresh, float eps,
-                                            float eps_gamma, float& gcarry) {
+__device__ __forceinline__ void solve_block(PcSmem& sm, const uint16_t* xb, const uint16_t* qb, const bf16x8& sa0,
+                                            const bf16x8& sa1, int w, int jl, int li, int t0, int T, bool fresh,
+                                            float eps, float eps_gamma, float& gcarry) {
   const int i = 16 * B + li;
   const int t = t0 + i;
   const bool live = t < T;
+  const int g = jl - 4 * w;
+  // (X S)_{i,jl} and (Q S)_{i,jl} on the matrix cores: A's row a is the
+  // state's column 4w + (a & 3) (sa0, sa1), B's column li is row i of X (of
+  // Q), so every result row of lane (g, li) is row i, and component g holds
+  // column 4w + g, the lane's own column
+  bf16x8 m_x0 = {}, m_x1 = {};
+  const bf16x8 m_q0 = ring_frag_c(qb, i, 0, g), m_q1 = ring_frag_c(qb, i, 1, g);
+  f32x4 m_qs = mfma32(sa0, m_q0, zero4());
+  m_qs = mfma32(sa1, m_q1, m_qs);
+  f32x4 m_xs = zero4();
+  if constexpr (kReg) {
+    m_x0 = ring_frag_c(xb, i, 0, g);
+    m_x1 = ring_frag_c(xb, i, 1, g);
+    m_xs = mfma32(sa0, m_x0, zero4());
+    m_xs = mfma32(sa1, m_x1, m_xs);
+  }
   // step size and decay of row i in column jl (branch-free: every operand is
   // loaded and the reciprocal taken whatever the row); g by a scan over the
   // 16 rows
-  const float lmi = sm.lm[i], bti = sm.bt[jl][i];
+  const float lmi = sm.lm[i], bti = sm.bt[cix(jl, i)];
   const float den = sm.en[i] + lmi + eps;
   const bool on = live && !(fresh && t == 0) && den != 0.0f;
   const float eta = on ? bti * __builtin_amdgcn_rcpf(on ? den : 1.0f) : 0.0f;
@@ -187,8 +211,10 @@ __device__ __forceinline__ void solve_block(PcSmem& sm, int w, int jl, int li, i
   const float gprev = li == 0 ? gcarry : gsh;
   const float glast = row_bcast<15>(gi);
   // earlier blocks, through w_s = e^{g_{16B-1}-g_s} rho_s
-  float a = kReg ? eta * (sm.vb[jl][i] - exp2_fast(gprev) * sm.xs[jl][i]) : eta * sm.vb[jl][i];
-  float o = exp2_fast(gi) * sm.qs[jl][i];
+  const float qsv = g == 0 ? m_qs[0] : g == 1 ? m_qs[1] : g == 2 ? m_qs[2] : m_qs[3];
+  const float xsv = g == 0 ? m_xs[0] : g == 1 ? m_xs[1] : g == 2 ? m_xs[2] : m_xs[3];
+  float a = kReg ? eta * (sm.vb[cix(jl, i)] - exp2_fast(gprev) * xsv) : eta * sm.vb[cix(jl, i)];
+  float o = exp2_fast(gi) * qsv;
   // operands and results of the earlier-block MFMAs, kept live (below) past
   // every inline-asm statement of the block
   bf16x8 m_a0 = {}, m_a1 = {}, m_k0 = {}, m_k1 = {}, m_p0 = {}, m_p1 = {};
@@ -199,9 +225,9 @@ __device__ __forceinline__ void solve_block(PcSmem& sm, int w, int jl, int li, i
     // the lane's result row 4 g + r is EK[16B + li][4 w + g] (and EP likewise):
     // no value crosses to another wave.  W' rows beyond the solved blocks
     // meet zero Gram entries.
-    const int g = jl - 4 * w, l = 16 * g + li;
+    const int l = 16 * g + li;
     const int ja = 4 * w + (li >> 2);
-    m_a0 = frag_acc(ld4(&sm.w[ja][4 * g]), ld4(&sm.w[ja][16 + 4 * g]));
+    m_a0 = frag_acc(ld4(&sm.w[cix(ja, 4 * g)]), ld4(&sm.w[cix(ja, 16 + 4 * g)]));
     if constexpr (kReg) {
       m_k0 = load_frag(&sm.kqf[B - 1][0][l * 8]);
       ek4 = mfma32(m_a0, m_k0, zero4());
@@ -209,7 +235,7 @@ __device__ __forceinline__ void solve_block(PcSmem& sm, int w, int jl, int li, i
     m_p0 = load_frag(&sm.pqf[B - 1][0][l * 8]);
     ep4 = mfma32(m_a0, m_p0, zero4());
     if constexpr (B == 3) {
-      m_a1 = frag_acc(ld4(&sm.w[ja][32 + 4 * g]), ld4(&sm.w[ja][48 + 4 * g]));
+      m_a1 = frag_acc(ld4(&sm.w[cix(ja, 32 + 4 * g)]), ld4(&sm.w[cix(ja, 48 + 4 * g)]));
       if constexpr (kReg) {
         m_k1 = load_frag(&sm.kqf[2][1][l * 8]);
         ek4 = mfma32(m_a1, m_k1, ek4);
@@ -291,14 +317,15 @@ __device__ __forceinline__ void solve_block(PcSmem& sm, int w, int jl, int li, i
   // freely (not volatile); the decay statements do not, so they stay
   // volatile and in place before this point.
   asm volatile("" ::"v"(m_a0), "v"(m_a1), "v"(m_k0), "v"(m_k1), "v"(m_p0), "v"(m_p1), "v"(ek4), "v"(ep4));
+  asm volatile("" ::"v"(m_q0), "v"(m_q1), "v"(m_x0), "v"(m_x1), "v"(m_qs), "v"(m_xs), "v"(sa0), "v"(sa1));
   sm.ob[i][jl] = bf(o);
   // w to the end of this block: earlier entries decay by e^{g_last-g_carry},
   // this block's entries are e^{g_last-g_s} rho_s
   {
     const float blk = exp2_fast(glast - gcarry);
 #pragma unroll
-    for (int k = 0; k < B; ++k) sm.w[jl][16 * k + li] *= blk;
-    sm.w[jl][i] = exp2_fast(glast - gi) * rho;
+    for (int k = 0; k < B; ++k) sm.w[cix(jl, 16 * k + li)] *= blk;
+    sm.w[cix(jl, i)] = exp2_fast(glast - gi) * rho;
   }
   gcarry = glast;
 }
@@ -338,106 +365,111 @@ falcon2_chunked_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restric
   const float* Lm = lam + bh * T;
   const bf16_t* kp = k_prev ? k_prev + bh * kD : nullptr;
 
-  // wave 0 holds the state of the slice: S[fb], lane holds S[16fb+4g+r][j0+c16]
-  f32x4 S[4];
+  // wave w holds rows 16w..16w+15 of the slice's state: lane holds S[16w+4g+r][j0+c16]
+  f32x4 S;
 #pragma unroll
-  for (int fb = 0; fb < 4; ++fb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      S[fb][r] = (w == 0 && S0) ? S0[(bh * kD + 16 * fb + 4 * g + r) * kD + j0 + c16] : 0.0f;
+  for (int r = 0; r < 4; ++r) S[r] = S0 ? S0[(bh * kD + 16 * w + 4 * g + r) * kD + j0 + c16] : 0.0f;
 
   const int nchunks = (T + kC - 1) / kC;
-  // the earlier-block products read whole rows of w, solved or not: start
+  // the earlier-block products read whole columns of w, solved or not: start
   // them at zero (never NaN), later chunks leave finite values behind
-  for (int e = tid; e < kSlice * kWP; e += kThreads) (&sm.w[0][0])[e] = 0.0f;
-  ChunkRegs R;
-  fetch_chunk(R, K, Q, V, Bt, Lm, kp, T, 0, j0, tid);
-  for (int c = 0; c < nchunks; ++c) {
-    const int t0 = c * kC;
-    stage_chunk(sm, R, tid);
-    __syncthreads();
-    // ---- products shared by all columns, on the matrix cores ---------------
-    if (w == 0) {
-      // X S and Q S for the slice: lane holds rows 16ib+4g+r, column j0+c16
-      const bf16x8 s0 = frag_acc(S[0], S[1]);
-      const bf16x8 s1 = frag_acc(S[2], S[3]);
+  for (int e = tid; e < kSlice * kC; e += kThreads) sm.w[e] = 0.0f;
+
+  // ---- products shared by all columns, on the matrix cores ------------------
+  // Diagonal Gram and read block b in float32 (lane holds rows i = 16b+4g+r,
+  // column s = 16b+c16; strict lower triangle, the diagonal to en and pd).
+  auto diag = [&](const uint16_t* xb, const uint16_t* qb, int b) {
+    const bf16x8 xs0 = ring_frag_c(xb, 16 * b + c16, 0, g), xs1 = ring_frag_c(xb, 16 * b + c16, 1, g);
+    f32x4 dk = mfma32(xs0, xs0, zero4());
+    dk = mfma32(xs1, xs1, dk);
+    f32x4 dp = mfma32(ring_frag_c(qb, 16 * b + c16, 0, g), xs0, zero4());
+    dp = mfma32(ring_frag_c(qb, 16 * b + c16, 1, g), xs1, dp);
 #pragma unroll
-      for (int ib = 0; ib < 4; ++ib) {
-        const int i = 16 * ib + c16;
-        f32x4 aq = mfma32(ring_frag_p(sm.q, i, 0, g), s0, zero4());
-        aq = mfma32(ring_frag_p(sm.q, i, 1, g), s1, aq);
-        f32x4 ax = zero4();
-        if (kReg) {
-          ax = mfma32(ring_frag_p(sm.x, i, 0, g), s0, ax);
-          ax = mfma32(ring_frag_p(sm.x, i, 1, g), s1, ax);
-        }
-        // rows 16ib+4g .. +3 of column c16 are contiguous: one 16-byte store each
-        *reinterpret_cast<f32x4*>(&sm.qs[c16][16 * ib + 4 * g]) = aq;
-        if (kReg) *reinterpret_cast<f32x4*>(&sm.xs[c16][16 * ib + 4 * g]) = ax;
-      }
-    } else {
-      // Waves 1..3: the diagonal Gram and read blocks in float32 (lane holds
-      // rows i = 16b+4g+r, column s = 16b+c16; strict lower triangle, the
-      // diagonal to en and pd), and for the earlier-block sums the fragments
-      // frag(KQ)[b][m], frag(PQ)[b][m] of rows 16b.. over s < 16b, built from
-      // tiles T(sb, b) whose lane holds x_{16sb+4g+r} . x_{16b+c16} (and the
-      // same with q_{16b+c16}); tiles with sb >= b are zero.
-      auto diag = [&](int b) {
-        const bf16x8 xs0 = ring_frag_c(sm.x, 16 * b + c16, 0, g), xs1 = ring_frag_c(sm.x, 16 * b + c16, 1, g);
-        f32x4 dk = mfma32(ring_frag_c(sm.x, 16 * b + c16, 0, g), xs0, zero4());
-        dk = mfma32(ring_frag_c(sm.x, 16 * b + c16, 1, g), xs1, dk);
-        f32x4 dp = mfma32(ring_frag_c(sm.q, 16 * b + c16, 0, g), xs0, zero4());
-        dp = mfma32(ring_frag_c(sm.q, 16 * b + c16, 1, g), xs1, dp);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool upper = c16 >= 4 * g + r;
-          sm.kqd[b][4 * g + r][c16] = upper ? 0.0f : dk[r];
-          sm.pqd[b][4 * g + r][c16] = upper ? 0.0f : dp[r];
-          if (4 * g + r == c16) {
-            sm.en[16 * b + c16] = dk[r];
-            sm.pd[16 * b + c16] = dp[r];
-          }
-        }
-      };
-      auto tile = [&](int sb, int b, f32x4& tk, f32x4& tp) {
-        const bf16x8 a0 = ring_frag_c(sm.x, 16 * sb + c16, 0, g), a1 = ring_frag_c(sm.x, 16 * sb + c16, 1, g);
-        tk = mfma32(a0, ring_frag_c(sm.x, 16 * b + c16, 0, g), zero4());
-        tk = mfma32(a1, ring_frag_c(sm.x, 16 * b + c16, 1, g), tk);
-        tp = mfma32(a0, ring_frag_c(sm.q, 16 * b + c16, 0, g), zero4());
-        tp = mfma32(a1, ring_frag_c(sm.q, 16 * b + c16, 1, g), tp);
-      };
-      auto frags = [&](int b, int m, bool two) {
-        f32x4 k0, p0, k1 = zero4(), p1 = zero4();
-        tile(2 * m, b, k0, p0);
-        if (two) tile(2 * m + 1, b, k1, p1);
-        store_frag(&sm.kqf[b - 1][m][l * 8], frag_acc(k0, k1));
-        store_frag(&sm.pqf[b - 1][m][l * 8], frag_acc(p0, p1));
-      };
-      if (w == 1) {
-        diag(0);
-        diag(1);
-        frags(1, 0, false);
-      } else if (w == 2) {
-        diag(2);
-        frags(2, 0, true);
-      } else {
-        diag(3);
-        frags(3, 0, true);
-        frags(3, 1, false);
+    for (int r = 0; r < 4; ++r) {
+      const bool upper = c16 >= 4 * g + r;
+      sm.kqd[b][4 * g + r][c16] = upper ? 0.0f : dk[r];
+      sm.pqd[b][4 * g + r][c16] = upper ? 0.0f : dp[r];
+      if (4 * g + r == c16) {
+        sm.en[16 * b + c16] = dk[r];
+        sm.pd[16 * b + c16] = dp[r];
       }
     }
-    __syncthreads();
+  };
+  // For the earlier-block sums, the fragments frag(KQ)[b][m], frag(PQ)[b][m]
+  // of rows 16b.. over s < 16b, built from tiles T(sb, b) whose lane holds
+  // x_{16sb+4g+r} . x_{16b+c16} (and the same with q_{16b+c16}); tiles with
+  // sb >= b are zero.
+  auto tile = [&](const uint16_t* xb, const uint16_t* qb, int sb, int b, f32x4& tk, f32x4& tp) {
+    const bf16x8 a0 = ring_frag_c(xb, 16 * sb + c16, 0, g), a1 = ring_frag_c(xb, 16 * sb + c16, 1, g);
+    tk = mfma32(a0, ring_frag_c(xb, 16 * b + c16, 0, g), zero4());
+    tk = mfma32(a1, ring_frag_c(xb, 16 * b + c16, 1, g), tk);
+    tp = mfma32(a0, ring_frag_c(qb, 16 * b + c16, 0, g), zero4());
+    tp = mfma32(a1, ring_frag_c(qb, 16 * b + c16, 1, g), tp);
+  };
+  auto frags = [&](const uint16_t* xb, const uint16_t* qb, int b, int m, bool two) {
+    f32x4 k0, p0, k1 = zero4(), p1 = zero4();
+    tile(xb, qb, 2 * m, b, k0, p0);
+    if (two) tile(xb, qb, 2 * m + 1, b, k1, p1);
+    store_frag(&sm.kqf[b - 1][m][l * 8], frag_acc(k0, k1));
+    store_frag(&sm.pqf[b - 1][m][l * 8], frag_acc(p0, p1));
+  };
+  // the wave's share of the fragments (four, six, eight and eight products)
+  auto gram_frags = [&](const uint16_t* xb, const uint16_t* qb) {
+    if (w == 0) frags(xb, qb, 3, 1, false);
+    else if (w == 1) frags(xb, qb, 1, 0, false);
+    else if (w == 2) frags(xb, qb, 2, 0, true);
+    else frags(xb, qb, 3, 0, true);
+  };
+  // the state's bf16 copy, column by column, for the X S and Q S products
+  auto put_state = [&]() { store_half(&sm.sb[c16][16 * w + 4 * g], S); };
+  // rows 16w.. of the state: S <- e^{g_63} S + X^T W, X^T's rows from
+  // products with a selection matrix
+  auto state_update = [&](const uint16_t* xb) {
+    const float dec = sm.e63[c16];
+    // frag(W^T): lane holds w_{c16, 32m + kperm(g, e)}
+    bf16x8 u[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) u[m] = frag_acc(ld4(&sm.w[cix(c16, 32 * m + 4 * g)]), ld4(&sm.w[cix(c16, 32 * m + 16 + 4 * g)]));
+    const bf16x8 sel = select_frag(w & 1, g, c16);
+    f32x4 d[4];
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) d[sb] = mfma32(ring_frag_c(xb, 16 * sb + c16, w >> 1, g), sel, zero4());
+    f32x4 acc = S * dec;
+    acc = mfma32(frag_acc(d[0], d[1]), u[0], acc);
+    S = mfma32(frag_acc(d[2], d[3]), u[1], acc);
+  };
+
+  // Chunk c keeps its rows in buffer c & 1.  Per chunk: the solve (which
+  // forms X S and Q S block by block from the bf16 state, and during which
+  // the next chunk's rows are staged into the other buffer), then the
+  // outputs, the state update and the next chunk's Gram products.  The next
+  // chunk's rows are fetched into registers a chunk ahead.
+  ChunkRegs R;
+  fetch_chunk(R, K, Q, V, Bt, Lm, kp, T, 0, j0, tid);
+  stage_xq(sm.x[0], sm.q[0], R, tid);
+  stage_gates(sm, R, tid);
+  put_state();
+  if (nchunks > 1) fetch_chunk(R, K, Q, V, Bt, Lm, kp, T, kC, j0, tid);
+  __syncthreads();
+  diag(sm.x[0], sm.q[0], w);
+  gram_frags(sm.x[0], sm.q[0]);
+  __syncthreads();
+  for (int c = 0; c < nchunks; ++c) {
+    const int t0 = c * kC, buf = c & 1, nb = buf ^ 1;
+    const bool more = c + 1 < nchunks;
     // ---- per-column rows, block by block ------------------------------------
     {
+      // the state's columns 4w + (li & 3) as A fragments of the X S, Q S products
+      const bf16x8 sa0 = load_frag(&sm.sb[4 * w + (li & 3)][8 * g]);
+      const bf16x8 sa1 = load_frag(&sm.sb[4 * w + (li & 3)][32 + 8 * g]);
+      const uint16_t* xb = sm.x[buf];
+      const uint16_t* qb = sm.q[buf];
       float gcarry = 0.f;
-      solve_block<kReg, 0>(sm, w, jl, li, t0, T, fresh, eps, eps_gamma, gcarry);
-      // the next chunk's rows: issued here, among the solve's dependent
-      // chains, rather than beside the products, where the four waves' loads
-      // queue for the memory pipeline at once
-      if (c + 1 < nchunks) fetch_chunk(R, K, Q, V, Bt, Lm, kp, T, t0 + kC, j0, tid);
-      solve_block<kReg, 1>(sm, w, jl, li, t0, T, fresh, eps, eps_gamma, gcarry);
-      solve_block<kReg, 2>(sm, w, jl, li, t0, T, fresh, eps, eps_gamma, gcarry);
-      solve_block<kReg, 3>(sm, w, jl, li, t0, T, fresh, eps, eps_gamma, gcarry);
+      solve_block<kReg, 0>(sm, xb, qb, sa0, sa1, w, jl, li, t0, T, fresh, eps, eps_gamma, gcarry);
+      if (more) stage_xq(sm.x[nb], sm.q[nb], R, tid);
+      solve_block<kReg, 1>(sm, xb, qb, sa0, sa1, w, jl, li, t0, T, fresh, eps, eps_gamma, gcarry);
+      solve_block<kReg, 2>(sm, xb, qb, sa0, sa1, w, jl, li, t0, T, fresh, eps, eps_gamma, gcarry);
+      solve_block<kReg, 3>(sm, xb, qb, sa0, sa1, w, jl, li, t0, T, fresh, eps, eps_gamma, gcarry);
       if (li == 0) sm.e63[jl] = exp2_fast(gcarry);
     }
     __syncthreads();
@@ -448,35 +480,22 @@ falcon2_chunked_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restric
         *reinterpret_cast<uint4*>(o + (bh * T + t0 + r) * kD + j0 + 8 * (tid & 1)) =
             *reinterpret_cast<const uint4*>(&sm.ob[r][8 * (tid & 1)]);
     }
-    // ---- state update (wave 0): S <- e^{g_63} S + X^T W ------------------------
-    if (w == 0) {
-      const float dec = sm.e63[c16];
-      // frag(W^T): lane holds w_{c16, 32m + kperm(g, e)}
-      bf16x8 u[2];
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const f32x4 lo = ld4(&sm.w[c16][32 * m + 4 * g]);
-        const f32x4 hi = ld4(&sm.w[c16][32 * m + 16 + 4 * g]);
-        u[m] = frag_acc(lo, hi);
-      }
-#pragma unroll
-      for (int fb = 0; fb < 4; ++fb) {
-        const bf16x8 sel = select_frag(fb & 1, g, c16);
-        f32x4 d[4];
-#pragma unroll
-        for (int sb = 0; sb < 4; ++sb) d[sb] = mfma32(ring_frag_c(sm.x, 16 * sb + c16, fb >> 1, g), sel, zero4());
-        f32x4 acc = S[fb] * dec;
-        acc = mfma32(frag_acc(d[0], d[1]), u[0], acc);
-        S[fb] = mfma32(frag_acc(d[2], d[3]), u[1], acc);
-      }
+    if (more) {
+      stage_gates(sm, R, tid);
+      if (c + 2 < nchunks) fetch_chunk(R, K, Q, V, Bt, Lm, kp, T, t0 + 2 * kC, j0, tid);
+    }
+    // ---- state update, the next chunk's Gram products ------------------------
+    state_update(sm.x[buf]);
+    put_state();
+    if (more) {
+      diag(sm.x[nb], sm.q[nb], w);
+      gram_frags(sm.x[nb], sm.q[nb]);
     }
     __syncthreads();
   }
-  if (w == 0 && S_T) {
+  if (S_T) {
 #pragma unroll
-    for (int fb = 0; fb < 4; ++fb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) S_T[(bh * kD + 16 * fb + 4 * g + r) * kD + j0 + c16] = S[fb][r];
+    for (int r = 0; r < 4; ++r) S_T[(bh * kD + 16 * w + 4 * g + r) * kD + j0 + c16] = S[r];
   }
 }
 
