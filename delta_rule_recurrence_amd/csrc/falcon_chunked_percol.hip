@@ -176,9 +176,9 @@ __device__ __forceinline__ void solve_block(PcSmem& sm, const uint16_t* xb, cons
   const bool live = t < T;
   const int g = jl - 4 * w;
   // (X S)_{i,jl} and (Q S)_{i,jl} on the matrix cores: A's row a is the
-  // state's column 4w + (a & 3) (sa0, sa1), B's column li is row i of X (of
-  // Q), so every result row of lane (g, li) is row i, and component g holds
-  // column 4w + g, the lane's own column
+  // state's column 4w + (a >> 2) (sa0, sa1), B's column li is row i of X (of
+  // Q), so the result rows 4g..4g+3 of lane (g, li) are all row i of the
+  // lane's own column 4w + g
   bf16x8 m_x0 = {}, m_x1 = {};
   const bf16x8 m_q0 = ring_frag_c(qb, i, 0, g), m_q1 = ring_frag_c(qb, i, 1, g);
   f32x4 m_qs = mfma32(sa0, m_q0, zero4());
@@ -211,8 +211,7 @@ __device__ __forceinline__ void solve_block(PcSmem& sm, const uint16_t* xb, cons
   const float gprev = li == 0 ? gcarry : gsh;
   const float glast = row_bcast<15>(gi);
   // earlier blocks, through w_s = e^{g_{16B-1}-g_s} rho_s
-  const float qsv = g == 0 ? m_qs[0] : g == 1 ? m_qs[1] : g == 2 ? m_qs[2] : m_qs[3];
-  const float xsv = g == 0 ? m_xs[0] : g == 1 ? m_xs[1] : g == 2 ? m_xs[2] : m_xs[3];
+  const float qsv = m_qs[0], xsv = m_xs[0];
   float a = kReg ? eta * (sm.vb[cix(jl, i)] - exp2_fast(gprev) * xsv) : eta * sm.vb[cix(jl, i)];
   float o = exp2_fast(gi) * qsv;
   // operands and results of the earlier-block MFMAs, kept live (below) past
@@ -459,9 +458,9 @@ falcon2_chunked_kernel(const bf16_t* __restrict__ phi_k, const bf16_t* __restric
     const bool more = c + 1 < nchunks;
     // ---- per-column rows, block by block ------------------------------------
     {
-      // the state's columns 4w + (li & 3) as A fragments of the X S, Q S products
-      const bf16x8 sa0 = load_frag(&sm.sb[4 * w + (li & 3)][8 * g]);
-      const bf16x8 sa1 = load_frag(&sm.sb[4 * w + (li & 3)][32 + 8 * g]);
+      // the state's columns 4w + (li >> 2) as A fragments of the X S, Q S products
+      const bf16x8 sa0 = load_frag(&sm.sb[4 * w + (li >> 2)][8 * g]);
+      const bf16x8 sa1 = load_frag(&sm.sb[4 * w + (li >> 2)][32 + 8 * g]);
       const uint16_t* xb = sm.x[buf];
       const uint16_t* qb = sm.q[buf];
       float gcarry = 0.f;
