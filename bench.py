@@ -718,13 +718,13 @@ def main():
         line["decode"] = bench_decode()
     if not args.no_extra:
         line["f1a_chunked"] = bench_chunked_workload("f1a_chunked_2x12x16384_d64")
-        line["f2_chunked"] = bench_chunked_workload("f2_chunked_8x12x2048_d64", steps=5, warmup=1)
+        line["f2_chunked"] = bench_chunked_workload("f2_chunked_8x12x2048_d64", steps=100, warmup=1)
         line["f1_backward"] = bench_backward()
         rb = line["f1_backward"]["roofline"]
         if peaks:
             rb["frac_of_measured_fp32_gemm"] = rb["achieved"] / peaks["fp32_gemm_tflops"]
-        line["f1_recurrent"] = bench_recurrent()
-        line["f1_chunked_f32"] = bench_chunked_workload("f1_chunked_f32_8x12x2048_d64", steps=5, warmup=1)
+        line["f1_recurrent"] = bench_recurrent(steps=20)
+        line["f1_chunked_f32"] = bench_chunked_workload("f1_chunked_f32_8x12x2048_d64", steps=20, warmup=1)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(d, w, o, S_T, pool, nproc)
         pool.close()
