@@ -819,6 +819,13 @@ __device__ __forceinline__ float row_shr(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x110 + N, 0xf, 0xf, true));
 }
 
+// The value of the lane N places higher in the same sixteen-lane DPP row, 0
+// for the last N lanes of the row.
+template <int N>
+__device__ __forceinline__ float row_shl(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x100 + N, 0xf, 0xf, true));
+}
+
 // Exclusive prefix sum over the sixteen lanes of a row.
 __device__ __forceinline__ float excl16(float v) {
   v += row_shr<1>(v);
@@ -1156,66 +1163,66 @@ __global__ void __launch_bounds__(kThreads3) falcon1_bwd_chunk_kernel(BwdArgs a,
     f2.store(w, l, [&](int r, int s2, float v) { sm.RR[r][s2] += v; });
   }
   __syncthreads();
-  // gates: g -> log decay -> (eta, lam); eta -> (beta, lam, ||x||^2)
+  // gates: g -> log decay -> (eta, lam); eta -> (beta, lam, ||x||^2).  One
+  // wave; every operand is loaded first and the sums run on DPP lane moves,
+  // since the other seven waves wait for this step.
   if (w == 0) {
-    const int i = l;
+    const int i = l, ic = l & 31;
     // the pair terms of M and A spanning row c: row c of PT over the columns
     // r >= c, lanes c and c + 32 taking columns 0-15 and 16-31
+    const int c = ic, r0 = (l >> 5) * 16;
+    const float4* pt = reinterpret_cast<const float4*>(&cc.AA[c][r0]);
+    float4 pv[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) pv[k] = pt[k];
+    const float dgi = sm.dg[ic], dgpn = ic + 1 < kBC ? sm.dgp[ic + 1] : 0.f, zi = sm.dgt[ic];
+    float tr = 0.f;
+#pragma unroll
+    for (int r = 0; r < kWaves3; ++r) tr += sm.trp[r];
+    const int fl = cc.flags[ic];
+    const float eta = cc.eta[ic], lamv = cc.lamv[ic], den = cc.den[ic], detai = sm.deta[ic];
     float pairs = 0.f;
-    {
-      const int c = l & 31, r0 = (l >> 5) * 16;
-      const float4* pt = reinterpret_cast<const float4*>(&cc.AA[c][r0]);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float4 v = pt[k];
-        const int r = r0 + 4 * k;
-        pairs += (r >= c ? v.x : 0.f) + (r + 1 >= c ? v.y : 0.f) + (r + 2 >= c ? v.z : 0.f) +
-                 (r + 3 >= c ? v.w : 0.f);
-      }
-      pairs += __shfl_xor(pairs, 32);
+    for (int k = 0; k < 4; ++k) {
+      const int r = r0 + 4 * k;
+      pairs += (r >= c ? pv[k].x : 0.f) + (r + 1 >= c ? pv[k].y : 0.f) + (r + 2 >= c ? pv[k].z : 0.f) +
+               (r + 3 >= c ? pv[k].w : 0.f);
     }
-    float dgt = 0.f, z = 0.f;
-    if (i < kBC) {
-      float dG = 0.f;
-      if (i == kBC - 1) {
-        float tr = 0.f;
-        for (int r = 0; r < kWaves3; ++r) tr += sm.trp[r];
-        dG = eG * tr;
-      }
-      dgt = sm.dg[i] + (i + 1 < kBC ? sm.dgp[i + 1] : 0.f) + dG;
-      z = sm.dgt[i];
-    }
+    pairs += __shfl_xor(pairs, 32);   // lanes l and l ^ 32 hold the two halves
     // dlg_i: the Qt, Y and state terms of rows r >= i (suffix sums), the Xh
-    // terms of rows r < i (exclusive prefix sums) and the pair terms
-    float dlg = dgt;
-#pragma unroll
-    for (int d = 1; d < kBC; d <<= 1) {
-      const float n = __shfl_down(dlg, d);
-      if (i + d < kBC) dlg += n;
-      const float m = __shfl_up(z, d);
-      if (i >= d) z += m;
-    }
-    {
-      const float zb = __shfl_up(z, 1);
-      dlg += (i == 0 ? 0.f : zb) + pairs;
-    }
+    // terms of rows r < i (exclusive prefix sums) and the pair terms; the
+    // scans run within 16-lane rows, then row 0 takes row 1's total (suffix)
+    // and row 1 takes row 0's (prefix)
+    float dlg = dgi + dgpn + (ic == kBC - 1 ? eG * tr : 0.f);
+    dlg += row_shl<1>(dlg);
+    dlg += row_shl<2>(dlg);
+    dlg += row_shl<4>(dlg);
+    dlg += row_shl<8>(dlg);
+    float z = zi;
+    z += row_shr<1>(z);
+    z += row_shr<2>(z);
+    z += row_shr<4>(z);
+    z += row_shr<8>(z);
+    const float up = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dlg), 16));
+    const float lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), 15));
+    dlg += ic < 16 ? up : 0.f;
+    z += ic >= 16 ? lo : 0.f;
+    // exclusive: the lane below's inclusive prefix (0 at each row start, where
+    // lane 16 adds row 0's total).  The lane move runs in every lane, outside
+    // any select: a DPP read from a lane switched off by a branch yields 0.
+    const float zb = row_shr<1>(z) + (ic == 16 ? lo : 0.f);
+    dlg += zb + pairs;
     if (i < kBC) {
-      const int fl = cc.flags[i];
-      const float eta = cc.eta[i], lamv = cc.lamv[i];
-      float deta = sm.deta[i], dlam = 0.f;
-      if ((fl & 4) && !(fl & 2)) {
-        const float dalpha = -dlg / (1.0f - eta * lamv);
-        deta += dalpha * lamv;
-        dlam += dalpha * eta;
-      }
-      float dbeta = 0.f, dE = 0.f;
-      if (fl & 1) {
-        const float den = cc.den[i];
-        dbeta = deta / den;
-        const float dden = -deta * eta / den;
-        dlam += dden;
-        dE = dden;
-      }
+      // decay path where the clamp does not bind (alpha = eta lam, gamma = 1 - alpha)
+      const bool decay = (fl & 4) && !(fl & 2);
+      const float dalpha = decay ? -dlg * __builtin_amdgcn_rcpf(decay ? 1.0f - eta * lamv : 1.0f) : 0.f;
+      const float deta = detai + dalpha * lamv;
+      // step size eta = beta / den where it comes from the formula
+      const bool onr = fl & 1;
+      const float rden = __builtin_amdgcn_rcpf(onr ? den : 1.0f);
+      const float dbeta = onr ? deta * rden : 0.f;
+      const float dE = onr ? -deta * eta * rden : 0.f;
+      const float dlam = dalpha * eta + dE;
       const int t = t0 + i;
       if (t < T) {
         a.dbeta[bh * T + t] = dbeta;

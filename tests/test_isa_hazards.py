@@ -7,6 +7,13 @@ compiled to such a region (s_and_saveexec ... s_or_b64 exec) and, unless
 the region is skipped with s_cbranch_execz, silently changes the result.
 This test compiles every HIP source to assembly and fails on any MFMA in a
 masked region that is not skipped.
+
+DPP lane moves have the opposite problem: a lane reading a neighbour that
+the mask switched off receives 0 (or its own old value), not the
+neighbour's data.  Every lane move in these kernels is written for a full
+wave, so the test also fails on any DPP instruction inside a region where
+EXEC was narrowed (a select the compiler turned into a branch around a
+lane move once cost the backward its cross-row scan).
 """
 
 import os
@@ -51,6 +58,25 @@ def _masked_mfmas(asm: str):
     return bad
 
 
+def _masked_dpp(asm: str):
+    """DPP instructions between an EXEC-narrowing instruction (a saveexec, or
+    a move or AND into exec) and the s_or_b64 that restores it."""
+    bad, masked, fn = [], False, "?"
+    for i, line in enumerate(asm.split("\n")):
+        if re.match(r"^_Z\S+:", line):
+            fn = line.split(":")[0]
+            masked = False
+        s = line.strip()
+        if re.match(r"s_(and|andn2|xor|or)_saveexec_b64", s) or s.startswith("s_mov_b64 exec, s") or \
+                s.startswith("s_and_b64 exec"):
+            masked = True
+        elif s.startswith("s_or_b64 exec, exec"):
+            masked = False
+        elif masked and "_dpp" in s.split(" ")[0]:
+            bad.append(f"{fn} line {i + 1}: {s}")
+    return bad
+
+
 def _hipcc():
     try:
         return B.hipcc()
@@ -65,5 +91,8 @@ def test_no_mfma_under_exec_mask(src, tmp_path):
     cmd = [B.hipcc(), *B.HIPCC_FLAGS, "--cuda-device-only", "-S", os.path.join(B.CSRC, src), "-o", str(out)]
     res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr[-2000:]
-    bad = _masked_mfmas(out.read_text())
+    asm = out.read_text()
+    bad = _masked_mfmas(asm)
     assert not bad, "MFMA inside an EXEC-masked region:\n" + "\n".join(bad[:10])
+    bad = _masked_dpp(asm)
+    assert not bad, "DPP lane move inside an EXEC-narrowed region:\n" + "\n".join(bad[:10])
