@@ -171,12 +171,20 @@ __device__ __forceinline__ void mm(const float* A, int pa, const float* B, int p
   f.store(w, l, epi);
 }
 
+// v plus its value in the lane a DPP move (control CTRL) names: quad_perm
+// [1,0,3,2] (0xb1) and [2,3,0,1] (0x4e) pair lanes l ^ 1 and l ^ 2, the
+// half-row mirror (0x141) pairs the two quads of eight lanes and the row
+// mirror (0x140) the two halves of sixteen.  Called by every lane.
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
 // Sum over the eight consecutive lanes that share a row.
 __device__ __forceinline__ float sum8(float v) {
-  v += __shfl_xor(v, 1);
-  v += __shfl_xor(v, 2);
-  v += __shfl_xor(v, 4);
-  return v;
+  v = dpp_add<0xb1>(v);
+  v = dpp_add<0x4e>(v);
+  return dpp_add<0x141>(v);
 }
 
 struct BwdArgs {
@@ -805,11 +813,7 @@ struct __align__(16) GradSmem {
 
 // Sum over the sixteen consecutive lanes that share a row.
 __device__ __forceinline__ float sum16(float v) {
-  v += __shfl_xor(v, 1);
-  v += __shfl_xor(v, 2);
-  v += __shfl_xor(v, 4);
-  v += __shfl_xor(v, 8);
-  return v;
+  return dpp_add<0x140>(sum8(v));
 }
 
 // The value of the lane N places lower in the same sixteen-lane DPP row, 0
@@ -961,9 +965,13 @@ __global__ void __launch_bounds__(kThreads3) falcon1_bwd_chunk_kernel(BwdArgs a,
       const float4 y = *reinterpret_cast<const float4*>(&sm.SC[rr][cl]);
       trace = fmaf(x.x, y.x, fmaf(x.y, y.y, fmaf(x.z, y.z, fmaf(x.w, y.w, trace))));
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) trace += __shfl_xor(trace, off);
-    if (l == 0) sm.trp[w] = trace;
+    // the wave's sum: sixteen-lane sums, then the four rows' totals
+    trace = sum16(trace);
+    const float tw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(trace), 0)) +
+                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(trace), 16)) +
+                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(trace), 32)) +
+                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(trace), 48));
+    if (l == 0) sm.trp[w] = tw;
   }
   {
     // Gram (waves 0-3) and Q X^T (waves 4-7); M = tril(Q X^T) o D.  The gates,
