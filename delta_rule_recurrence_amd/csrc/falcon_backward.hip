@@ -180,6 +180,20 @@ __device__ __forceinline__ float dpp_add(float v) {
   return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
 }
 
+// The value of the lane N places lower in the same sixteen-lane DPP row, 0
+// for the first N lanes of the row.
+template <int N>
+__device__ __forceinline__ float row_shr(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x110 + N, 0xf, 0xf, true));
+}
+
+// The value of the lane N places higher in the same sixteen-lane DPP row, 0
+// for the last N lanes of the row.
+template <int N>
+__device__ __forceinline__ float row_shl(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x100 + N, 0xf, 0xf, true));
+}
+
 // Sum over the eight consecutive lanes that share a row.
 __device__ __forceinline__ float sum8(float v) {
   v = dpp_add<0xb1>(v);
@@ -388,19 +402,27 @@ __device__ void chunk_forward(ChunkCore& cc, const BwdArgs& a, int c, int tid, i
     // inclusive prefix over the chunk, compensated: each partial sum is
     // carried as gi + ge, the rounding error of every addition (two-sum)
     // going into ge
+    // (within 16-lane rows on DPP shifts, whose 0 past a row start adds
+    // exactly; then row 1 adds row 0's total)
     float gi = lg, ge = 0.f;
-#pragma unroll
-    for (int d = 1; d < kBC; d <<= 1) {
-      const float n = __shfl_up(gi, d), ne = __shfl_up(ge, d);
-      if (i >= d) {
-        const float sum = gi + n;
-        const float nb = sum - gi;
-        const float err = (gi - (sum - nb)) + (n - nb);
-        gi = sum;
-        ge += ne + err;
-      }
-    }
-    const float gpv = __shfl_up(gi, 1), gpe = __shfl_up(ge, 1);
+    auto add2 = [&](float n, float ne) {
+      const float sum = gi + n;
+      const float nb = sum - gi;
+      const float err = (gi - (sum - nb)) + (n - nb);
+      gi = sum;
+      ge += ne + err;
+    };
+    add2(row_shr<1>(gi), row_shr<1>(ge));
+    add2(row_shr<2>(gi), row_shr<2>(ge));
+    add2(row_shr<4>(gi), row_shr<4>(ge));
+    add2(row_shr<8>(gi), row_shr<8>(ge));
+    const float g15 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gi), 15));
+    const float e15 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ge), 15));
+    const bool row1 = (i & 31) >= 16;
+    add2(row1 ? g15 : 0.f, row1 ? e15 : 0.f);
+    // exclusive: the lane below's value (lane 16 takes lane 15's)
+    const float gpv = row_shr<1>(gi) + ((i & 31) == 16 ? g15 : 0.f);
+    const float gpe = row_shr<1>(ge) + ((i & 31) == 16 ? e15 : 0.f);
     if (i < kBC) {
       cc.g[i] = make_float2(gi, ge);
       cc.gp[i] = i == 0 ? make_float2(0.f, 0.f) : make_float2(gpv, gpe);
@@ -816,19 +838,6 @@ __device__ __forceinline__ float sum16(float v) {
   return dpp_add<0x140>(sum8(v));
 }
 
-// The value of the lane N places lower in the same sixteen-lane DPP row, 0
-// for the first N lanes of the row.
-template <int N>
-__device__ __forceinline__ float row_shr(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x110 + N, 0xf, 0xf, true));
-}
-
-// The value of the lane N places higher in the same sixteen-lane DPP row, 0
-// for the last N lanes of the row.
-template <int N>
-__device__ __forceinline__ float row_shl(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x100 + N, 0xf, 0xf, true));
-}
 
 // Exclusive prefix sum over the sixteen lanes of a row.
 __device__ __forceinline__ float excl16(float v) {
