@@ -8,7 +8,8 @@ tensors and every sequence), repeats its results bit for bit, and the two
 agree bit for bit, on shapes with one chunk, odd and even chunk counts with
 ragged tails, a carried state and key, a sequence count that is not a
 multiple of the eight XCDs, batches at and past the 256 sequences up to which
-the default runs in one launch, and the full workload shape.  The bit
+the default runs in one launch, long sequences (256 chunks, and a ragged 6001
+tokens) and the full workload shape.  The bit
 agreement pins the hand-over of the one-launch form against the other,
 independently scheduled form."""
 
@@ -32,6 +33,8 @@ CASES = {
     "256_sequences": (16, 16, 100, False),
     "264_sequences": (8, 33, 128, True),
     "workload_carry": (8, 12, 2048, True),
+    "long_16384_carry": (1, 2, 16384, True),
+    "long_ragged": (2, 3, 6001, False),
 }
 FORMS = {"one_launch": fb.F1_ONE_LAUNCH, "two_launch": fb.F1_TWO_LAUNCH}
 
