@@ -23,10 +23,13 @@
 //    -c_{i,s} rho_s to every later row, rho_s broadcast from lane s by a DPP
 //    row broadcast (row_newbcast), 15 dependent steps per block.
 //  * The products shared by all columns (x_i.x_s, q_i.x_s, X S, Q S and the
-//    state update) run on the matrix cores.
+//    state update) run on the matrix cores; each solve block forms its own
+//    rows of X S and Q S from a bf16 copy of the state.
 // One workgroup (four waves, four value columns each) per (batch, head,
-// 16-column slice); the next chunk's rows are fetched into registers while the
-// current one is solved.
+// 16-column slice).  Per chunk two phases: the solve (during which the next
+// chunk's rows go into the second LDS row buffer), then the outputs, the
+// state update (wave w owns state rows 16w..16w+15) and the next chunk's Gram
+// products.  Rows are fetched into registers a chunk ahead.
 
 #include <vector>
 
