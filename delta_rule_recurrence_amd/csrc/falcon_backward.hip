@@ -641,10 +641,15 @@ falcon1_bwd_maps_kernel(BwdArgs a, int total) {
 // are loaded kRing chunks ahead of their use.  The four groups
 // of a (chain, sequence) are placed on one XCD (workgroups go round-robin over
 // the eight XCDs), so P is fetched from HBM once per XCD L2.
-struct ChainSmem {
-  float Bt[16][kPW];     // state chain: S[:, 16cg .. 16cg+15] transposed (Bt[c][k] = S[k][16cg + c])
-  float L[16][kPW];      // adjoint chain: Lam^T[16cg .. 16cg+15][:]
-  float P[kD][kPW];      // adjoint chain: this chunk's P
+// Double-buffered by the parity of the step, so one barrier per step
+// suffices: a step writes the buffers the step before last read, and every
+// wave has passed the last step's barrier after those reads.
+union ChainSmem {
+  float Bt[2][16][kPW];  // state chain: S[:, 16cg .. 16cg+15] transposed (Bt[c][k] = S[k][16cg + c])
+  struct {
+    float L[2][16][kPW]; // adjoint chain: Lam^T[16cg .. 16cg+15][:]
+    float P[2][kD][kPW]; // adjoint chain: this chunk's P
+  } j;
 };
 
 constexpr int kRing = 3;   // chunks of operands in flight per chain
@@ -671,7 +676,8 @@ __device__ __forceinline__ void chain_state(const BwdArgs& a, ChainSmem& sm, int
   };
   auto step = [&](int c, const float4 (&p4)[4], const float4& h) __attribute__((always_inline)) {
     // S (entering chunk c) to LDS and to the checkpoint, then S <- P S + H
-    *reinterpret_cast<float4*>(&sm.Bt[c16][16 * w + 4 * g]) = make_float4(S[0], S[1], S[2], S[3]);
+    float (*Bt)[kPW] = sm.Bt[c & 1];
+    *reinterpret_cast<float4*>(&Bt[c16][16 * w + 4 * g]) = make_float4(S[0], S[1], S[2], S[3]);
     float* ck = a.ckpt + (bh * n + c) * kD * kD;
     reinterpret_cast<float4*>(ck)[(cg * 4 + w) * 64 + l] = make_float4(S[0], S[1], S[2], S[3]);
     __syncthreads();
@@ -679,7 +685,7 @@ __device__ __forceinline__ void chain_state(const BwdArgs& a, ChainSmem& sm, int
     // MFMA chains interleave
     float4 b4[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) b4[m] = *reinterpret_cast<const float4*>(&sm.Bt[c16][16 * m + 4 * g]);
+    for (int m = 0; m < 4; ++m) b4[m] = *reinterpret_cast<const float4*>(&Bt[c16][16 * m + 4 * g]);
     f32x4 acc[4] = {{h.x, h.y, h.z, h.w}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(p4[m].x, b4[m].x, acc[m], 0, 0, 0);
@@ -690,7 +696,6 @@ __device__ __forceinline__ void chain_state(const BwdArgs& a, ChainSmem& sm, int
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(p4[m].w, b4[m].w, acc[m], 0, 0, 0);
     S = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-    __syncthreads();
   };
   // the ring slots are named explicitly (slot d holds chunk c0 + d), so they
   // stay in registers
@@ -733,8 +738,10 @@ __device__ __forceinline__ void chain_adjoint(const BwdArgs& a, ChainSmem& sm, i
     // Lam^T (at the end of chunk c) to LDS and to the adjoint store, then
     // Lam^T <- Lam^T P + G^T
     const int c = n - 1 - s;
+    float (*L)[kPW] = sm.j.L[s & 1];
+    float (*P)[kPW] = sm.j.P[s & 1];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sm.L[4 * g + r][16 * w + c16] = Lt[r];
+    for (int r = 0; r < 4; ++r) L[4 * g + r][16 * w + c16] = Lt[r];
     // this wave's rows 16w..16w+15 of P (PA order) into LDS; the product below
     // reads P's column block w
     // (stored component-wise: a 16-byte store of the slot itself makes the
@@ -742,7 +749,7 @@ __device__ __forceinline__ void chain_adjoint(const BwdArgs& a, ChainSmem& sm, i
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const float4 q = p4[m];
-      float* dst = &sm.P[16 * w + c16][16 * m + 4 * g];
+      float* dst = &P[16 * w + c16][16 * m + 4 * g];
       dst[0] = q.x; dst[1] = q.y; dst[2] = q.z; dst[3] = q.w;
     }
     float* ad = a.adj + (bh * n + c) * kD * kD;
@@ -752,9 +759,9 @@ __device__ __forceinline__ void chain_adjoint(const BwdArgs& a, ChainSmem& sm, i
     float4 a4[4], b4[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      a4[m] = *reinterpret_cast<const float4*>(&sm.L[c16][16 * m + 4 * g]);
-      b4[m] = make_float4(sm.P[16 * m + 4 * g + 0][16 * w + c16], sm.P[16 * m + 4 * g + 1][16 * w + c16],
-                          sm.P[16 * m + 4 * g + 2][16 * w + c16], sm.P[16 * m + 4 * g + 3][16 * w + c16]);
+      a4[m] = *reinterpret_cast<const float4*>(&L[c16][16 * m + 4 * g]);
+      b4[m] = make_float4(P[16 * m + 4 * g + 0][16 * w + c16], P[16 * m + 4 * g + 1][16 * w + c16],
+                          P[16 * m + 4 * g + 2][16 * w + c16], P[16 * m + 4 * g + 3][16 * w + c16]);
     }
     f32x4 acc[4] = {{g4.x, g4.y, g4.z, g4.w}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
@@ -766,7 +773,6 @@ __device__ __forceinline__ void chain_adjoint(const BwdArgs& a, ChainSmem& sm, i
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[m].w, b4[m].w, acc[m], 0, 0, 0);
     Lt = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-    __syncthreads();
   };
   load(0, pb[0], gd[0]);
   load(1, pb[1], gd[1]);
