@@ -25,8 +25,10 @@
 //        dY = T^T dW,  dZ = T^T dU,  dA = -dY W^T - dZ U^T,
 //      then the Gram, the decays and the gates (eta, the clamped log decay,
 //      the prefix sums) by the chain rule, and the key shift x_t = phi(k_{t-1}).
-// Every product runs on the matrix cores in float32 (v_mfma_f32_16x16x4f32)
-// with operands in LDS.  T comes from a blocked inverse: the two 16 x 16
+// Every product runs on the matrix cores with operands in LDS: in float32
+// (v_mfma_f32_16x16x4f32), or, where both operands are bf16 inputs, on the
+// bf16 matrix cores, whose products of bf16 numbers are exact and whose
+// sums are float32.  T comes from a blocked inverse: the two 16 x 16
 // diagonal blocks by substitution (a column per lane), the off-diagonal
 // block as -T22 A21 T11.
 
@@ -34,6 +36,7 @@
 
 #include "falcon_device.h"
 #include "falcon_launch.h"
+#include "falcon_mfma_frag.h"
 
 namespace falcon {
 
@@ -161,6 +164,68 @@ struct Mm {
     }
   }
 };
+
+// The same product with TB and no scales, for operands whose values are
+// bfloat16 numbers held as floats (the bf16 inputs: keys and queries): the
+// bf16 matrix cores (v_mfma_f32_16x16x32_bf16) form every product exactly
+// and accumulate in float32, with an eighth of the instructions.  Lane
+// group g supplies k = 32m + kperm(g, e) of its row, so both operands are
+// read as two 16-byte runs per 32-wide block; results sit in the lanes as
+// in Mm.
+template <int M, int N, int K, int NW = 4>
+struct MmBf {
+  static constexpr int TN = N / 16, TM = M / 16, IT = TM * TN / NW, KB = K / 32;
+  static_assert(K % 32 == 0, "K must be a multiple of 32");
+  static_assert(TM * TN % NW == 0 && NW % TN == 0, "tiles must split evenly over the waves");
+  frag::bf16x8 bv[KB];
+  frag::bf16x8 av[IT][KB];
+  f32x4 acc[IT];
+
+  // the eight bf16 values of k = k0 .. k0 + 3 and k0 + 16 .. k0 + 19 of a
+  // float row (exact: the floats are bf16 numbers)
+  static __device__ __forceinline__ frag::bf16x8 pack(const float* row, int k0) {
+    const uint4 lo = *reinterpret_cast<const uint4*>(row + k0);
+    const uint4 hi = *reinterpret_cast<const uint4*>(row + k0 + 16);
+    const uint4 v = make_uint4((lo.x >> 16) | (lo.y & 0xffff0000u), (lo.z >> 16) | (lo.w & 0xffff0000u),
+                               (hi.x >> 16) | (hi.y & 0xffff0000u), (hi.z >> 16) | (hi.w & 0xffff0000u));
+    return __builtin_bit_cast(frag::bf16x8, v);
+  }
+  __device__ __forceinline__ void load(const float* A, int pa, const float* B, int pb, int w, int l) {
+    const int g = l >> 4, c16 = l & 15;
+    const int tn = w % TN;
+#pragma unroll
+    for (int m = 0; m < KB; ++m) {
+      const int k0 = 32 * m + 4 * g;
+      bv[m] = pack(B + (16 * tn + c16) * pb, k0);
+#pragma unroll
+      for (int it = 0; it < IT; ++it) av[it][m] = pack(A + (16 * ((w + NW * it) / TN) + c16) * pa, k0);
+    }
+  }
+  __device__ __forceinline__ void run() {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) acc[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < KB; ++m)
+#pragma unroll
+      for (int it = 0; it < IT; ++it) acc[it] = frag::mfma32(av[it][m], bv[m], acc[it]);
+  }
+  template <typename Epi>
+  __device__ __forceinline__ void store(int w, int l, Epi epi) const {
+    const int g = l >> 4, c16 = l & 15;
+    const int tn = w % TN;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int tm = (w + NW * it) / TN;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) epi(16 * tm + 4 * g + r, 16 * tn + c16, acc[it][r]);
+    }
+  }
+};
+
+// Products of two input matrices (x_i . x_s, q_i . x_s): on the bf16 matrix
+// cores when the inputs are bf16, in float32 otherwise.
+template <typename IO> struct InputGram { using type = Mm<kBC, kBC, kD, false, true>; };
+template <> struct InputGram<bf16_t> { using type = MmBf<kBC, kBC, kD>; };
 
 // One product: load, run, store.
 template <int M, int N, int K, bool TA, bool TB, typename Epi>
@@ -370,11 +435,12 @@ __device__ __forceinline__ void chunk_store(ChunkCore& cc, const ChunkRegs<IO>& 
 // issued first; wave 0 forms the gates while its products run, and the
 // decays are applied from the registers after the barrier.  Ends with a
 // barrier.
+template <typename IO>
 __device__ void chunk_forward(ChunkCore& cc, const BwdArgs& a, int c, int tid, int w, int l) {
   const int T = a.T;
   const int t0 = c * kBC;
   const bool fresh = (a.k_prev == nullptr);
-  Mm<kBC, kBC, kD, false, true> fk, fm;
+  typename InputGram<IO>::type fk, fm;
   fk.load(&cc.X[0][0], kPW, &cc.X[0][0], kPW, w, l);
   fm.load(&cc.Q[0][0], kPW, &cc.X[0][0], kPW, w, l);
   fk.run();
@@ -548,7 +614,7 @@ falcon1_bwd_maps_kernel(BwdArgs a, int total) {
   __syncthreads();
   // the next chunk's inputs (this chunk's again after the last one)
   map_load<IO>(in, a, job + int(gridDim.x) < total ? job + int(gridDim.x) : job, tid);
-  chunk_forward(cc, a, c, tid, w, l);
+  chunk_forward<IO>(cc, a, c, tid, w, l);
   chunk_factors(cc, TZ, tid, w, l);
   {
     // W, U, T and the gates for the chunk kernel
@@ -991,7 +1057,7 @@ __global__ void __launch_bounds__(kThreads3) falcon1_bwd_chunk_kernel(BwdArgs a,
   {
     // Gram (waves 0-3) and Q X^T (waves 4-7); M = tril(Q X^T) o D.  The gates,
     // T, W and U come from the maps kernel.
-    Mm<kBC, kBC, kD, false, true> f;
+    typename InputGram<IO>::type f;
     f.load(w < 4 ? &cc.X[0][0] : &cc.Q[0][0], kPW, &cc.X[0][0], kPW, w & 3, l);
     f.run();
     if (w < 4) {
