@@ -134,6 +134,11 @@ struct Mm {
   __device__ __forceinline__ void load(const float* A, int pa, const float* B, int pb, int w, int l) {
     load(A, pa, B, pb, w, l, [](int) { return 1.f; }, [](int) { return 1.f; });
   }
+  // with a scale ks(k) along the contraction index (applied to B's rows)
+  template <typename KScale>
+  __device__ __forceinline__ void load_k(const float* A, int pa, const float* B, int pb, int w, int l, KScale ks) {
+    load(A, pa, B, pb, w, l, [](int) { return 1.f; }, ks);
+  }
   // acc = op(A) op(B), or init + op(A) op(B)
   __device__ __forceinline__ void run() {
 #pragma unroll
@@ -221,6 +226,118 @@ struct MmBf {
     }
   }
 };
+
+// op(A) op(B) with one operand a bf16 input held as floats and the other any
+// float matrix, on the bf16 matrix cores: the float operand (A when SA,
+// else B), after its scale ks(k) along the contraction index, is split into
+// three bf16 parts hi + mid + lo that sum to it exactly (each part takes the
+// next eight significant bits; only values below the smallest normal float
+// lose bits), so each of the three products is exact and the result is the
+// float32 product up to the order of its float32 sums, in three bf16 MFMAs
+// per 32-wide block of k where float32 takes eight.  Layouts as in Mm
+// (A is M x K, stored K x M when TA; B is K x N, stored N x K when TB).
+template <int M, int N, int K, bool TA, bool TB, bool SA, int NW = 4>
+struct MmX3 {
+  static constexpr int TN = N / 16, TM = M / 16, IT = TM * TN / NW, KB = K / 32;
+  static_assert(K % 32 == 0, "K must be a multiple of 32");
+  static_assert(TM * TN % NW == 0 && NW % TN == 0, "tiles must split evenly over the waves");
+  frag::bf16x8 ar[SA ? 1 : IT][KB], br[SA ? KB : 1];   // the bf16 operand
+  frag::bf16x8 as[SA ? IT : 1][KB][3], bs[SA ? 1 : KB][3];   // the split operand
+  f32x4 acc[IT];
+
+  // k = 32m + kperm(g, e) of row r of a matrix stored with k contiguous
+  // (tr = false) or of column r of one stored with k as its row index
+  static __device__ __forceinline__ void read8(const float* X, int p, int r, int kb, int g, bool tr, float (&v)[8]) {
+    if (!tr) {
+      const float4 lo = *reinterpret_cast<const float4*>(X + r * p + kb + 4 * g);
+      const float4 hi = *reinterpret_cast<const float4*>(X + r * p + kb + 16 + 4 * g);
+      v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w; v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = X[(kb + (e < 4 ? 4 * g + e : 12 + 4 * g + e)) * p + r];
+    }
+  }
+  static __device__ __forceinline__ frag::bf16x8 exact(const float (&v)[8]) {
+    uint32_t u[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) u[q] = (__float_as_uint(v[2 * q]) >> 16) | (__float_as_uint(v[2 * q + 1]) & 0xffff0000u);
+    return __builtin_bit_cast(frag::bf16x8, make_uint4(u[0], u[1], u[2], u[3]));
+  }
+  template <typename KScale>
+  static __device__ __forceinline__ void split(float (&v)[8], int kb, int g, KScale ks, frag::bf16x8 (&d)[3]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = v[e] * ks(kb + (e < 4 ? 4 * g + e : 12 + 4 * g + e));
+      const __bf16 h = static_cast<__bf16>(x);
+      const float r1 = x - static_cast<float>(h);
+      const __bf16 m = static_cast<__bf16>(r1);
+      const float r2 = r1 - static_cast<float>(m);
+      d[2][e] = h;
+      d[1][e] = m;
+      d[0][e] = static_cast<__bf16>(r2);
+    }
+  }
+  template <typename KScale>
+  __device__ __forceinline__ void load(const float* A, int pa, const float* B, int pb, int w, int l, KScale ks) {
+    const int g = l >> 4, c16 = l & 15;
+    const int tn = w % TN;
+#pragma unroll
+    for (int m = 0; m < KB; ++m) {
+      float v[8];
+      read8(B, pb, 16 * tn + c16, 32 * m, g, !TB, v);
+      if (SA) br[SA ? m : 0] = exact(v);
+      else split(v, 32 * m, g, ks, bs[SA ? 0 : m]);
+#pragma unroll
+      for (int it = 0; it < IT; ++it) {
+        read8(A, pa, 16 * ((w + NW * it) / TN) + c16, 32 * m, g, TA, v);
+        if (SA) split(v, 32 * m, g, ks, as[SA ? it : 0][m]);
+        else ar[SA ? 0 : it][m] = exact(v);
+      }
+    }
+  }
+  __device__ __forceinline__ void load(const float* A, int pa, const float* B, int pb, int w, int l) {
+    load(A, pa, B, pb, w, l, [](int) { return 1.f; });
+  }
+  template <typename KScale>
+  __device__ __forceinline__ void load_k(const float* A, int pa, const float* B, int pb, int w, int l, KScale ks) {
+    load(A, pa, B, pb, w, l, ks);
+  }
+  __device__ __forceinline__ void run() {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) acc[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+    mac();
+  }
+  // the small parts first, so the float32 sums meet them before the large
+  __device__ __forceinline__ void mac() {
+#pragma unroll
+    for (int m = 0; m < KB; ++m)
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+#pragma unroll
+        for (int it = 0; it < IT; ++it)
+          acc[it] = SA ? frag::mfma32(as[SA ? it : 0][m][j], br[SA ? m : 0], acc[it])
+                       : frag::mfma32(ar[SA ? 0 : it][m], bs[SA ? 0 : m][j], acc[it]);
+  }
+  template <typename Epi>
+  __device__ __forceinline__ void store(int w, int l, Epi epi) const {
+    const int g = l >> 4, c16 = l & 15;
+    const int tn = w % TN;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int tm = (w + NW * it) / TN;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) epi(16 * tm + 4 * g + r, 16 * tn + c16, acc[it][r]);
+    }
+  }
+};
+
+// op(A) op(B) with the bf16 input operand on the side named by SA's
+// complement: bf16 matrix cores with a three-way split when the inputs are
+// bf16, Mm in float32 otherwise.  ks scales the other operand along k.
+template <typename IO, int M, int N, int K, bool TA, bool TB, bool SA, int NW = 4>
+struct InputProduct { using type = MmX3<M, N, K, TA, TB, SA, NW>; };
+template <int M, int N, int K, bool TA, bool TB, bool SA, int NW>
+struct InputProduct<float, M, N, K, TA, TB, SA, NW> { using type = Mm<M, N, K, TA, TB, NW>; };
 
 // Products of two input matrices (x_i . x_s, q_i . x_s): on the bf16 matrix
 // cores when the inputs are bf16, in float32 otherwise.
@@ -547,6 +664,7 @@ __device__ void chunk_forward(ChunkCore& cc, const BwdArgs& a, int c, int tid, i
 
 // W = T Diag(eta e^{gp}) X and U = T Diag(eta) V, with TZ = T Diag(eta) in
 // the caller's 32 x 36 scratch; AA becomes T Diag(eta e^{gp}).  Ends with a barrier.
+template <typename IO>
 __device__ void chunk_factors(ChunkCore& cc, float (*TZ)[kPN], int tid, int w, int l) {
   for (int e = tid; e < kBC * kBC; e += kThreads) {
     const int i = e >> 5, s = e & 31;
@@ -555,7 +673,7 @@ __device__ void chunk_factors(ChunkCore& cc, float (*TZ)[kPN], int tid, int w, i
     TZ[i][s] = t * cc.eta[s];
   }
   __syncthreads();
-  Mm<kBC, kD, kBC, false, false> fw, fu;
+  typename InputProduct<IO, kBC, kD, kBC, false, false, true>::type fw, fu;
   fw.load(&cc.AA[0][0], kPN, &cc.X[0][0], kPW, w, l);
   fu.load(&TZ[0][0], kPN, &cc.V[0][0], kPW, w, l);
   fw.run();
@@ -615,7 +733,7 @@ falcon1_bwd_maps_kernel(BwdArgs a, int total) {
   // the next chunk's inputs (this chunk's again after the last one)
   map_load<IO>(in, a, job + int(gridDim.x) < total ? job + int(gridDim.x) : job, tid);
   chunk_forward<IO>(cc, a, c, tid, w, l);
-  chunk_factors(cc, TZ, tid, w, l);
+  chunk_factors<IO>(cc, TZ, tid, w, l);
   {
     // W, U, T and the gates for the chunk kernel
     float* fo = a.fac + int64_t(job) * kFacFloats;
@@ -659,14 +777,13 @@ falcon1_bwd_maps_kernel(BwdArgs a, int total) {
   float* out = a.maps + int64_t(job) * kMapFloats;
   const float eG = eexp(cc.G);
   auto xs = [&](int t) { return dexp(cc.G, cc.g[t]); };
-  auto one = [](int) { return 1.f; };
   auto put = [&](float* base, int idx, const f32x4& v) {
     reinterpret_cast<float4*>(base)[idx] = make_float4(v[0], v[1], v[2], v[3]);
   };
   const int g4 = 4 * (l >> 4), c16 = l & 15;
   {
-    Mm<kD, kD, kBC, true, false> fpt;
-    fpt.load(&cc.W[0][0], kPW, &cc.X[0][0], kPW, w, l, one, xs);
+    typename InputProduct<IO, kD, kD, kBC, true, false, true>::type fpt;
+    fpt.load_k(&cc.W[0][0], kPW, &cc.X[0][0], kPW, w, l, xs);
     fpt.run();
 #pragma unroll
     for (int it = 0; it < fpt.IT; ++it) {
@@ -681,8 +798,8 @@ falcon1_bwd_maps_kernel(BwdArgs a, int total) {
     }
   }
   {
-    Mm<kD, kD, kBC, true, false> fh, fg;
-    fh.load(&cc.X[0][0], kPW, &cc.U[0][0], kPW, w, l, one, xs);
+    typename InputProduct<IO, kD, kD, kBC, true, false, false>::type fh, fg;
+    fh.load_k(&cc.X[0][0], kPW, &cc.U[0][0], kPW, w, l, xs);
     fg.load(&DO[0][0], kPW, &QT[0][0], kPW, w, l);
     fh.run();
     fg.run();
