@@ -338,7 +338,9 @@ def backward_bytes(B, H, T, dk, dv, io_bytes=2):
 
 def backward_flops(B, H, T, dk=64, dv=64, C=32):
     """Matrix-core flops of the Falcon-1 backward as designed (32-token
-    chunks, every product in fp32 MFMA), per chunk:
+    chunks; the products the design forms, counted once whichever matrix
+    cores run them: float32, bf16 for products of two bf16 inputs, or bf16
+    on a float operand split into three exact parts), per chunk:
       maps:  Gram and M (2 C^2 d), W and U (C^2 (dk + dv)), P, H and G
              (3 C dk dv, dk^2 C for P), Q~ (C^2 dk)
       chains: P S and Lam^T P (2 dk^2 dv)

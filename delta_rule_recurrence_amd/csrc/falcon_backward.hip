@@ -231,10 +231,11 @@ struct MmBf {
 // float matrix, on the bf16 matrix cores: the float operand (A when SA,
 // else B), after its scale ks(k) along the contraction index, is split into
 // three bf16 parts hi + mid + lo that sum to it exactly (each part takes the
-// next eight significant bits; only values below the smallest normal float
-// lose bits), so each of the three products is exact and the result is the
-// float32 product up to the order of its float32 sums, in three bf16 MFMAs
-// per 32-wide block of k where float32 takes eight.  Layouts as in Mm
+// next eight significant bits; only values within a factor 2^16 of the
+// smallest normal float lose bits), so each of the three products is exact
+// and the result is the float32 product up to the order of its float32
+// sums, in three bf16 MFMAs per 32-wide block of k where float32 takes
+// eight.  Layouts as in Mm
 // (A is M x K, stored K x M when TA; B is K x N, stored N x K when TB).
 template <int M, int N, int K, bool TA, bool TB, bool SA, int NW = 4>
 struct MmX3 {
