@@ -231,8 +231,8 @@ struct MmBf {
 // float matrix, on the bf16 matrix cores: the float operand (A when SA,
 // else B), after its scale ks(k) along the contraction index, is split into
 // three bf16 parts hi + mid + lo that sum to it exactly (each part takes the
-// next eight significant bits; only values within a factor 2^16 of the
-// smallest normal float lose bits), so each of the three products is exact
+// next eight significant bits of the 24; only values within a factor 2^16 of
+// the smallest normal float lose bits), so each of the three products is exact
 // and the result is the float32 product up to the order of its float32
 // sums, in three bf16 MFMAs per 32-wide block of k where float32 takes
 // eight.  Layouts as in Mm
@@ -264,18 +264,30 @@ struct MmX3 {
     for (int q = 0; q < 4; ++q) u[q] = (__float_as_uint(v[2 * q]) >> 16) | (__float_as_uint(v[2 * q + 1]) & 0xffff0000u);
     return __builtin_bit_cast(frag::bf16x8, make_uint4(u[0], u[1], u[2], u[3]));
   }
+  // The parts by truncation: hi keeps the top eight significant bits of x,
+  // x - hi (exact) has at most sixteen, mid keeps its top eight, and the
+  // exact remainder lo has at most eight, so every part is a bf16 number
+  // and the sixteen-bit halves are the parts' bf16 encodings.
   template <typename KScale>
   static __device__ __forceinline__ void split(float (&v)[8], int kb, int g, KScale ks, frag::bf16x8 (&d)[3]) {
+    uint32_t p[3][8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float x = v[e] * ks(kb + (e < 4 ? 4 * g + e : 12 + 4 * g + e));
-      const __bf16 h = static_cast<__bf16>(x);
-      const float r1 = x - static_cast<float>(h);
-      const __bf16 m = static_cast<__bf16>(r1);
-      const float r2 = r1 - static_cast<float>(m);
-      d[2][e] = h;
-      d[1][e] = m;
-      d[0][e] = static_cast<__bf16>(r2);
+      const uint32_t hb = __float_as_uint(x) & 0xffff0000u;
+      const float r1 = x - __uint_as_float(hb);
+      const uint32_t mb = __float_as_uint(r1) & 0xffff0000u;
+      const float r2 = r1 - __uint_as_float(mb);
+      p[2][e] = hb;
+      p[1][e] = mb;
+      p[0][e] = __float_as_uint(r2);
+    }
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      uint32_t u[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) u[q] = (p[j][2 * q] >> 16) | (p[j][2 * q + 1] & 0xffff0000u);
+      d[j] = __builtin_bit_cast(frag::bf16x8, make_uint4(u[0], u[1], u[2], u[3]));
     }
   }
   template <typename KScale>
