@@ -1050,27 +1050,41 @@ __device__ __forceinline__ float excl16(float v) {
   return row_shr<1>(v);
 }
 
-// This thread's share of one chunk's inputs, held as loaded.  Waves 0-3 take
-// the keys, queries and values, waves 4-7 dO, all eight the state, the
-// adjoint and W, U; the first 256 threads T and the gates.
+// This thread's share of one chunk's inputs, held as loaded.  Every wave
+// issues the same loads from addresses chosen without a branch (a branch
+// between different loads made the compiler copy the loaded registers, and
+// so wait for the loads, right after issuing them): waves 0-3 take the keys
+// and queries, waves 4-7 the values and dO, all eight the state, the
+// adjoint and W, U; T and the gates go to every 256 threads.
 template <typename IO>
 struct GradRegs {
-  ChunkRegs<IO> r;
-  Raw8<IO> odr;
+  Raw8<IO> m0, m1;     // waves 0-3: x, q; waves 4-7: v, dO (row (tid & 255) >> 3, columns 8 (tid & 7) ..)
+  bool live0, live1;   // the rows' masks (x: a live row with a key; q, v, dO: a live row)
   float4 s4[2], l4[2];
   float4 wf, uf, tf;   // W, U (all threads), T (threads < 256)
   float gf;            // gates (threads < 256)
-  bool olive;
 };
 
 template <typename IO>
 __device__ __forceinline__ void grad_load(GradRegs<IO>& g, const BwdArgs& a, int64_t bh, int c, int tid, int w) {
   const int T = a.T;
   const int u = tid & 255;
-  const int orow = c * kBC + (u >> 3);
-  g.olive = orow < T;
-  if (w < 4) chunk_load<IO>(g.r, a, bh, c, u);
-  else g.odr.load(static_cast<const IO*>(a.dO) + (bh * T + (orow < T ? orow : T - 1)) * kD + (u & 7) * 8);
+  const int i = u >> 3, f0 = (u & 7) * 8;
+  const int t = c * kBC + i;
+  const bool live = t < T;
+  const int tc = live ? t : T - 1;
+  const bool lo = w < 4;
+  const IO* K = static_cast<const IO*>(a.phi_k) + bh * T * kD;
+  const IO* kp = a.k_prev ? static_cast<const IO*>(a.k_prev) + bh * kD : K;
+  // key row t - 1 for a live row t >= 1; any other row reads row 0 (T >= 1)
+  const IO* xr = t == 0 ? kp : K + int64_t(live ? t - 1 : 0) * kD;
+  const IO* vr = static_cast<const IO*>(a.v) + (bh * T + tc) * kD;
+  const IO* qr = static_cast<const IO*>(a.phi_q) + (bh * T + tc) * kD;
+  const IO* dr = static_cast<const IO*>(a.dO) + (bh * T + tc) * kD;
+  g.m0.load((lo ? xr : vr) + f0);
+  g.m1.load((lo ? qr : dr) + f0);
+  g.live0 = lo ? live && (t >= 1 || a.k_prev != nullptr) : live;
+  g.live1 = live;
   const float4* ck = reinterpret_cast<const float4*>(a.ckpt + (bh * a.nchunks + c) * kD * kD);
   const float4* ad = reinterpret_cast<const float4*>(a.adj + (bh * a.nchunks + c) * kD * kD);
 #pragma unroll
@@ -1088,16 +1102,22 @@ __device__ __forceinline__ void grad_load(GradRegs<IO>& g, const BwdArgs& a, int
 template <typename IO>
 __device__ __forceinline__ void grad_store(GradSmem& sm, const GradRegs<IO>& g, int tid, int w) {
   const int u = tid & 255;
-  if (w < 4) {
-    chunk_store<IO>(sm.cc, g.r, u, false);   // the gates come with the factors
-  } else {
+  {
     const int i = u >> 3, f0 = (u & 7) * 8;
-    float od[8];
-    g.odr.get(od);
+    float m0[8], m1[8];
+    g.m0.get(m0);
+    g.m1.get(m1);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) od[k] = g.olive ? od[k] : 0.f;
-    *reinterpret_cast<float4*>(&sm.DO[i][f0]) = make_float4(od[0], od[1], od[2], od[3]);
-    *reinterpret_cast<float4*>(&sm.DO[i][f0 + 4]) = make_float4(od[4], od[5], od[6], od[7]);
+    for (int k = 0; k < 8; ++k) {
+      m0[k] = g.live0 ? m0[k] : 0.f;
+      m1[k] = g.live1 ? m1[k] : 0.f;
+    }
+    float* d0 = w < 4 ? &sm.cc.X[i][f0] : &sm.cc.V[i][f0];
+    float* d1 = w < 4 ? &sm.cc.Q[i][f0] : &sm.DO[i][f0];
+    *reinterpret_cast<float4*>(d0) = make_float4(m0[0], m0[1], m0[2], m0[3]);
+    *reinterpret_cast<float4*>(d0 + 4) = make_float4(m0[4], m0[5], m0[6], m0[7]);
+    *reinterpret_cast<float4*>(d1) = make_float4(m1[0], m1[1], m1[2], m1[3]);
+    *reinterpret_cast<float4*>(d1 + 4) = make_float4(m1[4], m1[5], m1[6], m1[7]);
   }
   {
     ChunkCore& cc = sm.cc;
