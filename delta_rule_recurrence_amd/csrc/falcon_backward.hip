@@ -63,7 +63,7 @@ constexpr int kMapFloats = 12288;
 // W [32][64], U [32][64], T [32][32], then the gates eta, g, gp, den, lam,
 // flags (int bits), glo, gplo [32] each (G is g_31).
 constexpr int kFacW = 0, kFacU = 2048, kFacT = 4096, kFacGates = 5120;
-constexpr int kFacFloats = 5376;
+constexpr int kFacFloats = 5408;   // the gates, then gamma [32]
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -437,6 +437,7 @@ struct __align__(16) ChunkCore {
   // float pair hi + lo, lo the part the float sums dropped; G = g_31
   float2 g[kBC], gp[kBC], G;
   float en[kBC], eta[kBC], lamv[kBC], den[kBC];
+  float gam[kBC];        // gamma_i = 1 - eta_i lam_i, or eps_gamma where the clamp binds
   int flags[kBC];        // 1: eta from the formula, 2: the clamp binds, 4: live row
 };
 
@@ -582,17 +583,33 @@ __device__ void chunk_forward(ChunkCore& cc, const BwdArgs& a, int c, int tid, i
     float lg = 0.f;
     if (i < kBC) {
       const bool live = t < T;
-      const float lamv = cc.lamv[i];
-      const float den = cc.en[i] + lamv + a.eps;
-      const bool on = live && !(fresh && t == 0) && den != 0.0f;
-      const float eta = on ? cc.den[i] / den : 0.0f;
-      // a binding clamp gives gamma = eps_gamma exactly (not 1 minus the
-      // float nearest 1 - eps_gamma)
-      const float alpha = eta * lamv;
-      const bool clamped = !(1.0f - alpha >= a.eps_gamma);
-      lg = live ? (clamped ? logf(a.eps_gamma) : log1pf(-alpha)) : 0.0f;
+      const float lamv = cc.lamv[i], beta = cc.den[i];
+      // gamma = 1 - beta lam / den = (den - beta lam) / den cancels down to
+      // gamma wherever the decay is small, so the energy, the denominator
+      // and gamma are formed in double precision (the row's key is exact in
+      // float): float sums would leave gamma a relative error of about
+      // 1e-7 / gamma, which the gradient of the log decay, divided by gamma,
+      // would carry (beta in (1, 2) puts gamma anywhere in (0, 1))
+      double e0 = 0.0, e1 = 0.0;
+#pragma unroll
+      for (int k = 0; k < kD; k += 4) {
+        const float4 xv = *reinterpret_cast<const float4*>(&cc.X[i][k]);
+        e0 = fma(double(xv.x), double(xv.x), e0);
+        e1 = fma(double(xv.y), double(xv.y), e1);
+        e0 = fma(double(xv.z), double(xv.z), e0);
+        e1 = fma(double(xv.w), double(xv.w), e1);
+      }
+      const double den64 = (e0 + e1) + double(lamv) + double(a.eps);
+      const bool on = live && !(fresh && t == 0) && den64 != 0.0;
+      const float den = float(den64);
+      const float eta = on ? float(double(beta) / den64) : 0.0f;
+      const double gam64 = on ? (den64 - double(beta) * double(lamv)) / den64 : 1.0;
+      // a binding clamp gives gamma = eps_gamma exactly
+      const bool clamped = !(gam64 >= double(a.eps_gamma));
+      lg = live ? (clamped ? logf(a.eps_gamma) : float(log(gam64))) : 0.0f;
       cc.eta[i] = eta;
       cc.den[i] = den;
+      cc.gam[i] = clamped ? a.eps_gamma : float(gam64);
       cc.flags[i] = (on ? 1 : 0) | (clamped ? 2 : 0) | (live ? 4 : 0);
     }
     // inclusive prefix over the chunk, compensated: each partial sum is
@@ -773,6 +790,7 @@ falcon1_bwd_maps_kernel(BwdArgs a, int total) {
         default: v = cc.gp[i].y; break;
       }
       fo[kFacGates + tid] = v;
+      if (tid < kBC) fo[kFacGates + 256 + tid] = cc.gam[tid];
     }
   }
   // KX and AA (two adjacent 32 x 36 arrays, dead after the factors) hold Qt.
@@ -1062,7 +1080,7 @@ struct GradRegs {
   bool live0, live1;   // the rows' masks (x: a live row with a key; q, v, dO: a live row)
   float4 s4[2], l4[2];
   float4 wf, uf, tf;   // W, U (all threads), T (threads < 256)
-  float gf;            // gates (threads < 256)
+  float gf;            // gates (threads < 256), gamma (threads 256..)
 };
 
 template <typename IO>
@@ -1096,7 +1114,8 @@ __device__ __forceinline__ void grad_load(GradRegs<IO>& g, const BwdArgs& a, int
   g.wf = reinterpret_cast<const float4*>(fo + kFacW)[tid];
   g.uf = reinterpret_cast<const float4*>(fo + kFacU)[tid];
   g.tf = reinterpret_cast<const float4*>(fo + kFacT)[u];
-  g.gf = fo[kFacGates + u];
+  // threads 256.. take gamma (row tid & 31)
+  g.gf = fo[kFacGates + (tid < 256 ? tid : 256 + (tid & 31))];
 }
 
 template <typename IO>
@@ -1142,6 +1161,8 @@ __device__ __forceinline__ void grad_store(GradSmem& sm, const GradRegs<IO>& g, 
         if (k == 1 && r == kBC - 1) cc.G.x = g.gf;
         if (k == 6 && r == kBC - 1) cc.G.y = g.gf;
       }
+    } else if (tid < 256 + kBC) {
+      cc.gam[tid & 31] = g.gf;
     }
   }
 #pragma unroll
@@ -1454,7 +1475,7 @@ __global__ void __launch_bounds__(kThreads3) falcon1_bwd_chunk_kernel(BwdArgs a,
     if (i < kBC) {
       // decay path where the clamp does not bind (alpha = eta lam, gamma = 1 - alpha)
       const bool decay = (fl & 4) && !(fl & 2);
-      const float dalpha = decay ? -dlg * __builtin_amdgcn_rcpf(decay ? 1.0f - eta * lamv : 1.0f) : 0.f;
+      const float dalpha = decay ? -dlg * __builtin_amdgcn_rcpf(decay ? cc.gam[ic] : 1.0f) : 0.f;
       const float deta = detai + dalpha * lamv;
       // step size eta = beta / den where it comes from the formula
       const bool onr = fl & 1;

@@ -66,3 +66,31 @@ def test_backward_random_sweep_against_oracle():
             errs[n] = rel_l2(got[n], ref[n])
         bad = {n: e for n, e in errs.items() if e > BWD_TOL}
         assert not bad, f"case {i} ({c['what']}): " + ", ".join(f"{n}={e:.2e}" for n, e in bad.items())
+
+
+
+
+def test_backward_decay_just_above_the_clamp():
+    """A row whose decay gamma = 1 - eta lam sits just above eps_gamma (beta in
+    (1, 2) with small keys, "Fast Weight Attention for Continual Learning",
+    Section 3.1 and Section 4.3): on these seeded inputs (float32 I/O, keys
+    scaled to 0.02, beta scaled by 1.95, a carried state and previous key)
+    sequence 3 has gamma = 5.8e-6 at token 8, the difference of two nearly
+    equal terms.  Formed in float arithmetic, gamma kept about two digits
+    there, and the gradient of beta, which takes the log decay's gradient
+    divided by gamma, missed the bar (5.1e-5 relative L2)."""
+    B, H, T, seed = 2, 2, 208, 935896980
+    d = I.make_inputs(B, H, T, 64, 64, seed=seed, io_dtype="f32", feature_scale=0.02)
+    d["beta"] = d["beta"] * 1.95
+    cot = I.make_cotangents(B, H, T, 64, seed=seed + 1, io_dtype="f32", with_state=False)
+    rng = np.random.default_rng(seed + 2)
+    S0 = torch.from_numpy((0.1 * rng.standard_normal((B, H, 64, 64))).astype(np.float32))
+    kp = torch.from_numpy((0.02 * rng.standard_normal((B, H, 64))).astype(np.float32))
+    kw = dict(S0=S0, k_prev=kp, eps=1e-6, eps_gamma=1e-6)
+    ref = oracle_grads(d, cot, **kw)
+    got = gpu_grads(d, cot, **kw)
+    for n in NAMES:
+        if ref[n] is None:
+            continue
+        e = rel_l2(got[n], ref[n])
+        assert e <= BWD_TOL, f"{n}: rel L2 {e:.2e}"
