@@ -533,20 +533,26 @@ __device__ __forceinline__ void chunk_load(ChunkRegs<IO>& r, const BwdArgs& a, i
 }
 
 template <typename IO>
-__device__ __forceinline__ void chunk_store(ChunkCore& cc, const ChunkRegs<IO>& r, int tid, bool gate_inputs = true) {
+// enp: the thread's partial key energy, in double precision (the eight
+// partials of row i at enp[8i ..]).
+__device__ __forceinline__ void chunk_store(ChunkCore& cc, const ChunkRegs<IO>& r, int tid, double* enp,
+                                            bool gate_inputs = true) {
   const int i = tid >> 3, f0 = (tid & 7) * 8;
   float x[8], q[8], v[8];
   r.x.get(x);
   r.q.get(q);
   r.v.get(v);
   float e = 0.f;
+  double ed = 0.0;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     x[k] = r.xlive ? x[k] : 0.f;
     q[k] = r.live ? q[k] : 0.f;
     v[k] = r.live ? v[k] : 0.f;
     e = fmaf(x[k], x[k], e);
+    ed = fma(double(x[k]), double(x[k]), ed);
   }
+  enp[tid] = ed;
 #pragma unroll
   for (int k = 0; k < 8; k += 4) {
     *reinterpret_cast<float4*>(&cc.X[i][f0 + k]) = make_float4(x[k], x[k + 1], x[k + 2], x[k + 3]);
@@ -567,7 +573,7 @@ __device__ __forceinline__ void chunk_store(ChunkCore& cc, const ChunkRegs<IO>& 
 // decays are applied from the registers after the barrier.  Ends with a
 // barrier.
 template <typename IO>
-__device__ void chunk_forward(ChunkCore& cc, const BwdArgs& a, int c, int tid, int w, int l) {
+__device__ void chunk_forward(ChunkCore& cc, const BwdArgs& a, int c, int tid, int w, int l, const double* enp) {
   const int T = a.T;
   const int t0 = c * kBC;
   const bool fresh = (a.k_prev == nullptr);
@@ -586,30 +592,26 @@ __device__ void chunk_forward(ChunkCore& cc, const BwdArgs& a, int c, int tid, i
       const float lamv = cc.lamv[i], beta = cc.den[i];
       // gamma = 1 - beta lam / den = (den - beta lam) / den cancels down to
       // gamma wherever the decay is small, so the energy, the denominator
-      // and gamma are formed in double precision (the row's key is exact in
-      // float): float sums would leave gamma a relative error of about
-      // 1e-7 / gamma, which the gradient of the log decay, divided by gamma,
-      // would carry (beta in (1, 2) puts gamma anywhere in (0, 1))
-      double e0 = 0.0, e1 = 0.0;
+      // and the numerator den - beta lam are formed in double precision (the
+      // row's key is exact in float): float sums would leave gamma a
+      // relative error of about 1e-7 / gamma, which the gradient of the log
+      // decay, divided by gamma, would carry (beta in (1, 2) puts gamma
+      // anywhere in (0, 1))
+      double e64 = 0.0;
 #pragma unroll
-      for (int k = 0; k < kD; k += 4) {
-        const float4 xv = *reinterpret_cast<const float4*>(&cc.X[i][k]);
-        e0 = fma(double(xv.x), double(xv.x), e0);
-        e1 = fma(double(xv.y), double(xv.y), e1);
-        e0 = fma(double(xv.z), double(xv.z), e0);
-        e1 = fma(double(xv.w), double(xv.w), e1);
-      }
-      const double den64 = (e0 + e1) + double(lamv) + double(a.eps);
+      for (int k = 0; k < 8; ++k) e64 += enp[8 * i + k];
+      const double den64 = e64 + double(lamv) + double(a.eps);
+      const double num64 = fma(-double(beta), double(lamv), den64);
       const bool on = live && !(fresh && t == 0) && den64 != 0.0;
       const float den = float(den64);
-      const float eta = on ? float(double(beta) / den64) : 0.0f;
-      const double gam64 = on ? (den64 - double(beta) * double(lamv)) / den64 : 1.0;
+      const float eta = on ? beta / den : 0.0f;
+      const float gam = on ? float(num64) / den : 1.0f;
       // a binding clamp gives gamma = eps_gamma exactly
-      const bool clamped = !(gam64 >= double(a.eps_gamma));
-      lg = live ? (clamped ? logf(a.eps_gamma) : float(log(gam64))) : 0.0f;
+      const bool clamped = on && !(num64 >= double(a.eps_gamma) * den64);
+      lg = live ? (clamped ? logf(a.eps_gamma) : logf(gam)) : 0.0f;
       cc.eta[i] = eta;
       cc.den[i] = den;
-      cc.gam[i] = clamped ? a.eps_gamma : float(gam64);
+      cc.gam[i] = clamped ? a.eps_gamma : gam;
       cc.flags[i] = (on ? 1 : 0) | (clamped ? 2 : 0) | (live ? 4 : 0);
     }
     // inclusive prefix over the chunk, compensated: each partial sum is
@@ -741,6 +743,7 @@ falcon1_bwd_maps_kernel(BwdArgs a, int total) {
   __shared__ ChunkCore cc;
   __shared__ float TZ[kBC][kPN];
   __shared__ __align__(16) float DO[kBC][kPW];
+  __shared__ double ENP[kBC * 8];
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;   // wave-uniform
   const int first = blockIdx.x;
@@ -750,7 +753,7 @@ falcon1_bwd_maps_kernel(BwdArgs a, int total) {
   for (int job = first; job < total; job += gridDim.x) {
   const int c = job % a.nchunks;
   {
-    chunk_store<IO>(cc, in.r, tid);
+    chunk_store<IO>(cc, in.r, tid, ENP);
     float od[8];
     in.odr.get(od);
 #pragma unroll
@@ -762,7 +765,7 @@ falcon1_bwd_maps_kernel(BwdArgs a, int total) {
   __syncthreads();
   // the next chunk's inputs (this chunk's again after the last one)
   map_load<IO>(in, a, job + int(gridDim.x) < total ? job + int(gridDim.x) : job, tid);
-  chunk_forward<IO>(cc, a, c, tid, w, l);
+  chunk_forward<IO>(cc, a, c, tid, w, l, ENP);
   chunk_factors<IO>(cc, TZ, tid, w, l);
   {
     // W, U, T and the gates for the chunk kernel
