@@ -172,8 +172,12 @@ def call_bwd(lib, p, ws=None, wsb=0, **over):
 
 def test_backward_validation(lib):
     need = fb.falcon_bwd_workspace_bytes(prob())
-    # 101 KiB per 32-token chunk per (b, h): T = 40 -> 2 chunks, B*H = 6
-    assert need == 6 * 2 * 101 * 1024
+    # per 32-token chunk per (b, h), in floats: the maps (P, H, G: 3 x 64 x 64),
+    # the saved state and adjoint (2 x 64 x 64) and the forward factors (W, U:
+    # 2 x 32 x 64, T: 32 x 32, eight gate rows and gamma: 9 x 32); T = 40 -> 2
+    # chunks, B*H = 6
+    per_chunk = 3 * 4096 + 2 * 4096 + (2 * 2048 + 1024 + 9 * 32)
+    assert need == 6 * 2 * per_chunk * 4
     ws = fake(20)
     assert call_bwd(lib, None) == NULL
     assert call_bwd(lib, prob(variant="falcon1a"), ws, need) == VARIANT
