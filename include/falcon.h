@@ -273,8 +273,8 @@ falcon_status falcon_decode_step(const falcon_problem* p,
  *  workspace : device scratch of at least falcon_bwd_workspace_bytes(p)
  *              bytes, 16-byte aligned (per 32-token chunk per (b, h): the
  *              chunk maps, the state entering the chunk, the adjoint
- *              leaving it and the forward factors W, U, T and the gates;
- *              101 KiB).
+ *              leaving it, the forward factors W, U, T, the gates and
+ *              each row's decay gamma; 103,552 bytes).
  */
 falcon_status falcon_bwd_chunked(const falcon_problem* p,
                                  const void* phi_k, const void* phi_q, const void* v,
